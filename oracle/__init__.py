@@ -1,0 +1,11 @@
+"""CPU oracle for the HARD-KV decode step.
+
+Test infrastructure only: imported by the test-suite, by the package
+``smoke()`` check and by the benchmark's ``cpu_baseline`` leg, never by the
+product path.  It shares no code with the HIP library.
+"""
+from .hardkv_oracle import (  # noqa: F401
+    METRIC_QK, METRIC_L2, aged_count, score_head, calibrate_head, topp_head,
+    condense, attend_head, full_attention, step_head, step, HeadState,
+    init_state, lifecycle_step,
+)

@@ -1,0 +1,432 @@
+"""Plain CPU oracle for the HARD-KV decode step (test infrastructure only).
+
+This module is test infrastructure.  Only the test-suite, the package's
+``smoke()`` self-check and the ``cpu_baseline`` leg of the benchmark may
+import it.  The product path (the HIP library and its Python binding) never
+calls it, and it shares no code with that path.
+
+What it computes follows "HARD-KV: Head-Adaptive Regularization for
+Decoding-time KV Compression" (gist.science technical summary, section 2,
+"Methodology"; arXiv abstract on the mlsanity.com page).  The pages give no
+formulas, so the readings taken where they are silent are written next to
+each function.  Every step is the plain definition: float64 arithmetic from
+the exact input values, a full sort, a cumulative sum, direct gathers and a
+direct softmax.  No blocking, fusion or reordering.
+
+Precision of decisions.  The token ranking is an integer decision taken from
+floating point, so it is taken in the precision the GPU kernels keep their
+ranking keys in: the score of every candidate (and the calibrated value) is
+rounded once to float32, and the probability masses built from those float32
+keys are float64.  Attention runs entirely in float64.
+
+Parity pins (tests/test_oracle_pins.py): closed forms for the score
+(Hadamard keys) and the key norm (integer triples), a hand-derived
+calibration example, brute force over all subsets for the top-p set, uniform
+and two-level closed forms, reductions to full softmax attention (p = 1,
+chunk size 1, chunk-constant keys and values, window covering the context),
+and the lifecycle invariants of the Cascade Cache.  The rule chosen for
+calibrating a non-logit metric (moment matching, see ``calibrate_head``) is a
+reading of the pages; its implementation is pinned by a hand-worked example
+and invariants, the rule itself is not fixed by the pages.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+METRIC_QK = 0   # max-over-GQA-group q.k logit
+METRIC_L2 = 1   # key L2 norm
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening of float32 / bfloat16-valued inputs to float64."""
+    return np.asarray(x, dtype=np.float64)
+
+
+def _check_finite(*arrays):
+    # Inputs must be finite: NaN or Inf in q, K or V has no defined ranking.
+    for a in arrays:
+        if a is not None and not np.all(np.isfinite(a)):
+            raise ValueError("oracle inputs must be finite")
+
+
+# ---------------------------------------------------------------------------
+# Tiers of the Cascade Cache (technical summary, section 2.A: Tier 1 dense,
+# Tier 2 sparse, Tier 3 condensed).
+# ---------------------------------------------------------------------------
+def aged_count(T: int, W: int) -> int:
+    """Number of tokens that have left the dense window.
+
+    Tier 1 buffers the most recent tokens; a token that ages out of that
+    window becomes a candidate for Tier 2 (section 2.A).  Reading: the dense
+    window is the last W tokens, the current token included, so the aged
+    candidates are positions [0, T - W).
+    """
+    if T < 1:
+        raise ValueError("context length must be >= 1")
+    if W < 0:
+        raise ValueError("dense window must be >= 0")
+    return max(T - W, 0)
+
+
+# ---------------------------------------------------------------------------
+# Importance scores (section 2.B, "Goal": max-pooled logits are one of the
+# importance metrics the calibration normalises).
+# ---------------------------------------------------------------------------
+def score_head(q_group, K):
+    """Importance scores of the candidate keys of one KV head.
+
+    q_group: [G, d] query rows of the heads sharing this KV head.
+    K:       [n, d] candidate key rows.
+    Returns (ell, s) as float32 arrays of length n:
+      ell_t = max_g (q_g . k_t) / sqrt(d)   -- the "max-pooled logits"
+              (section 2.B); pooling is read as the max over the GQA group,
+              with no pooling across positions,
+      s_t   = ||k_t||_2                      -- the key-norm metric.
+    Both are computed in float64 from the exact inputs and rounded once to
+    float32, the precision in which the ranking decision is taken.
+    """
+    q = _f64(q_group)
+    k = _f64(K)
+    _check_finite(q, k)
+    d = q.shape[1]
+    if k.shape[0] == 0:
+        return np.zeros(0, np.float32), np.zeros(0, np.float32)
+    dots = k @ q.T                                  # [n, G], exact for bf16 data
+    ell = dots.max(axis=1) * (1.0 / math.sqrt(d))
+    s = np.sqrt(np.einsum("nd,nd->n", k, k))
+    return ell.astype(np.float32), s.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Logits Calibration (section 2.B "Mechanism"; section 3, second
+# contribution).
+# ---------------------------------------------------------------------------
+@dataclass
+class Calibration:
+    shift: float      # c = fl32((x - shift) * scale)
+    scale: float
+    c: np.ndarray     # calibrated value per candidate, float32
+    m: float          # max of c
+    w: np.ndarray     # exp(c - m), float64
+    Z: float          # sum of w
+
+
+def calibrate_head(ell, s, metric: int) -> Calibration:
+    """Map one head's importance scores into a softmax probability space.
+
+    The pages state that calibration maps a selection metric onto a
+    normalised softmax by adjusting the temperature, keeps the metric's
+    order, and maps onto the raw attention distribution.  Reading:
+      * QK heads: temperature 1, c = ell.  The calibrated distribution is the
+        raw attention distribution over the candidates.
+      * key-norm heads: a temperature chosen so the metric's spread equals
+        the head's raw-logit spread:  c = (s - mu_s) * sigma_ell / sigma_s,
+        population moments over the candidates.  A zero spread gives c = 0.
+    The softmax domain is the candidate set only (dense-tier tokens are kept
+    by rule).  Weights w = exp(c - max c), Z = sum w, float64.
+    """
+    ell = np.asarray(ell, dtype=np.float32)
+    s = np.asarray(s, dtype=np.float32)
+    n = ell.shape[0]
+    if metric == METRIC_QK:
+        shift, scale = 0.0, 1.0
+        c = ell.copy()
+    elif metric == METRIC_L2:
+        if n == 0:
+            shift, scale = 0.0, 0.0
+            c = np.zeros(0, np.float32)
+        else:
+            s64 = _f64(s)
+            l64 = _f64(ell)
+            mu_s = float(np.mean(s64))
+            sd_s = float(np.sqrt(np.mean((s64 - mu_s) ** 2)))
+            mu_l = float(np.mean(l64))
+            sd_l = float(np.sqrt(np.mean((l64 - mu_l) ** 2)))
+            if sd_s == 0.0 or sd_l == 0.0:
+                shift, scale = 0.0, 0.0
+                c = np.zeros(n, np.float32)
+            else:
+                shift, scale = mu_s, sd_l / sd_s
+                c = ((s64 - shift) * scale).astype(np.float32)
+    else:
+        raise ValueError(f"unknown metric {metric}")
+    if n == 0:
+        return Calibration(shift, scale, c, 0.0, np.zeros(0), 0.0)
+    c64 = _f64(c)
+    m = float(c64.max())
+    w = np.exp(c64 - m)
+    Z = math.fsum(w)
+    return Calibration(shift, scale, c, m, w, Z)
+
+
+# ---------------------------------------------------------------------------
+# Calibrated Top-p selection (section 2.A, Tier 2; section 2.B "Outcome").
+# ---------------------------------------------------------------------------
+@dataclass
+class Selection:
+    order: np.ndarray      # candidate indices in rank order (c desc, position asc)
+    k: int                 # size of the selected set
+    selected: np.ndarray   # selected candidate indices, ascending
+    prefix_excl: np.ndarray  # exclusive prefix mass / Z in rank order
+    w_sorted: np.ndarray   # weights in rank order
+
+
+def topp_head(c, w, Z, p, positions=None) -> Selection:
+    """Smallest candidate set whose calibrated mass reaches p.
+
+    Reading: Top-p here is a deterministic nucleus, not random sampling.
+    Candidates are ranked by calibrated value, highest first, equal values by
+    lower original position first.  k is the smallest k >= 1 with
+    sum_{i<k} w_(i) >= p * Z, p taken as float32 and widened exactly.
+    p >= 1 keeps every candidate; an empty candidate set selects nothing.
+    """
+    c = np.asarray(c, dtype=np.float32)
+    n = c.shape[0]
+    pos = np.arange(n) if positions is None else np.asarray(positions)
+    p32 = float(np.float32(p))
+    if p32 <= 0.0:
+        raise ValueError("top_p must be > 0")
+    if n == 0:
+        e = np.zeros(0, np.int64)
+        return Selection(e, 0, e, np.zeros(0), np.zeros(0))
+    order = np.lexsort((pos, -_f64(c)))          # primary: c desc, then position asc
+    ws = np.asarray(w, dtype=np.float64)[order]
+    prefix = np.cumsum(ws)
+    prefix_excl = np.concatenate(([0.0], prefix[:-1])) / Z
+    if p32 >= 1.0:
+        k = n
+    else:
+        target = p32 * Z
+        hits = np.nonzero(prefix >= target)[0]
+        k = int(hits[0]) + 1 if hits.size else n
+    selected = np.sort(order[:k])
+    return Selection(order, k, selected, prefix_excl, ws)
+
+
+# ---------------------------------------------------------------------------
+# Condensed tier (section 2.A, Tier 3: oldest blocks compressed into
+# constant-size storage by eviction or weighted merging).
+# ---------------------------------------------------------------------------
+def condense(K, V, evicted, positions, C: int, nchunks: int):
+    """Mean-pool storage of evicted tokens.
+
+    Reading: chunks are position-aligned, chunk j holds the evicted tokens
+    with position in [jC, (j+1)C).  The stored form is the float64 sum of
+    keys, the sum of values and the token count; the pooled key and value
+    are sum / count.  A chunk with no evicted token has count 0.
+    """
+    d = K.shape[1]
+    ksum = np.zeros((nchunks, d))
+    vsum = np.zeros((nchunks, d))
+    cnt = np.zeros(nchunks, np.int64)
+    k64 = _f64(K)
+    v64 = _f64(V)
+    for i in evicted:
+        j = int(positions[i]) // C
+        ksum[j] += k64[i]
+        vsum[j] += v64[i]
+        cnt[j] += 1
+    return ksum, vsum, cnt
+
+
+# ---------------------------------------------------------------------------
+# Decode attention over the three tiers.
+# ---------------------------------------------------------------------------
+def attend_head(q_group, dense_K, dense_V, sparse_K, sparse_V, ksum, vsum, cnt):
+    """Softmax attention of each query row over dense, sparse and condensed.
+
+    Dense and sparse entries use logit q.k / sqrt(d) and value v.  A non-empty
+    chunk with count n enters once with key ksum/n and value vsum/n; reading:
+    its logit carries + ln n, so that a chunk of n identical tokens weighs
+    exactly as those n tokens would.  float64, max-subtracted.
+    Returns [G, d] float64.
+    """
+    q = _f64(q_group)
+    d = q.shape[1]
+    scale = 1.0 / math.sqrt(d)
+    keys = [_f64(dense_K), _f64(sparse_K)]
+    vals = [_f64(dense_V), _f64(sparse_V)]
+    bias = [np.zeros(len(dense_K)), np.zeros(len(sparse_K))]
+    nz = np.nonzero(np.asarray(cnt) > 0)[0]
+    if nz.size:
+        n = np.asarray(cnt, dtype=np.float64)[nz]
+        keys.append(np.asarray(ksum, np.float64)[nz] / n[:, None])
+        vals.append(np.asarray(vsum, np.float64)[nz] / n[:, None])
+        bias.append(np.log(n))
+    Kall = np.concatenate(keys, axis=0).reshape(-1, d)
+    Vall = np.concatenate(vals, axis=0).reshape(-1, d)
+    ball = np.concatenate(bias)
+    if Kall.shape[0] == 0:
+        return np.zeros_like(q)
+    logits = (q @ Kall.T) * scale + ball[None, :]
+    logits -= logits.max(axis=1, keepdims=True)
+    e = np.exp(logits)
+    return (e @ Vall) / e.sum(axis=1, keepdims=True)
+
+
+def full_attention(q_group, K, V):
+    """Plain softmax attention of each query row over all rows of K/V."""
+    q = _f64(q_group)
+    d = q.shape[1]
+    logits = (q @ _f64(K).T) / math.sqrt(d)
+    logits -= logits.max(axis=1, keepdims=True)
+    e = np.exp(logits)
+    return (e @ _f64(V)) / e.sum(axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# One decode step for one (sequence, KV head): the four-step pipeline of
+# section 2.A (append, calibrate + top-p -> sparse mask, index
+# regularisation, eviction / merging).
+# ---------------------------------------------------------------------------
+@dataclass
+class HeadResult:
+    A: int
+    ell: np.ndarray
+    s: np.ndarray
+    cal: Calibration
+    sel: Selection
+    mask: np.ndarray       # uint8 [A]
+    pos: np.ndarray        # compacted positions (ascending)
+    Kc: np.ndarray         # compacted keys, bit copies of the input rows
+    Vc: np.ndarray
+    ksum: np.ndarray
+    vsum: np.ndarray
+    cnt: np.ndarray
+    out: np.ndarray        # [G, d] float64
+    extra: dict = field(default_factory=dict)
+
+
+def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int) -> HeadResult:
+    """Single-step compression + attention of one KV head.
+
+    K, V: [>=T, d] rows of this head's cache in position order (exact
+    input values, any float dtype).  The dense tier is [A, T), the candidates
+    are [0, A), A = max(T - W, 0).
+    Rewrite: the selected rows are copied, in ascending position order, into
+    contiguous slots 0..k-1 (Rewrite Cache + Flatten Index to the maximum
+    length, section 2.C).
+    """
+    A = aged_count(T, W)
+    cand_K = K[:A]
+    ell, s = score_head(q_group, cand_K)
+    cal = calibrate_head(ell, s, metric)
+    sel = topp_head(cal.c, cal.w, cal.Z, p)
+    mask = np.zeros(A, np.uint8)
+    mask[sel.selected] = 1
+    evicted = np.nonzero(mask == 0)[0]
+    nchunks = -(-A // C) if A else 0
+    ksum, vsum, cnt = condense(K, V, evicted, np.arange(A), C, nchunks)
+    Kc = np.asarray(K)[sel.selected]
+    Vc = np.asarray(V)[sel.selected]
+    out = attend_head(q_group, K[A:T], V[A:T], Kc, Vc, ksum, vsum, cnt)
+    return HeadResult(A, ell, s, cal, sel, mask, sel.selected.copy(), Kc, Vc,
+                      ksum, vsum, cnt, out)
+
+
+def step(q, k_rows, v_rows, ctx_len, W, C, p, metric):
+    """Whole batch: q [B, Hq, d]; k_rows(b, h) / v_rows(b, h) return the
+    [T_b, d] position-ordered rows of head h of sequence b; metric [Hkv].
+    Query head g belongs to KV head g // G.  Returns {(b, h): HeadResult}.
+    """
+    q = np.asarray(q)
+    B, Hq, d = q.shape
+    Hkv = len(metric)
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    G = Hq // Hkv
+    res = {}
+    for b in range(B):
+        T = int(ctx_len[b])
+        for h in range(Hkv):
+            res[(b, h)] = step_head(q[b, h * G:(h + 1) * G], k_rows(b, h), v_rows(b, h),
+                                    T, W, C, p, int(metric[h]))
+    return res
+
+
+# ---------------------------------------------------------------------------
+# Multi-step lifecycle with in-place tiers (section 2.A: tokens move dense ->
+# sparse -> condensed as they age; the sparse tier is re-selected each step).
+# ---------------------------------------------------------------------------
+@dataclass
+class HeadState:
+    """Tiers of one (layer, sequence, KV head) between decode steps.
+
+    ring_K/ring_V: [W, d] dense window, the token at position t lives in slot
+    t mod W.  pool_K/pool_V/pool_pos: the sparse tier, positions ascending.
+    ksum/vsum/cnt: condensed chunks (running sums).
+    """
+    W: int
+    C: int
+    ring_K: np.ndarray
+    ring_V: np.ndarray
+    pool_K: np.ndarray
+    pool_V: np.ndarray
+    pool_pos: np.ndarray
+    ksum: np.ndarray
+    vsum: np.ndarray
+    cnt: np.ndarray
+    T: int                 # tokens seen so far (positions 0..T-1)
+
+
+def init_state(K, V, T0: int, W: int, C: int, nchunks: int) -> HeadState:
+    """Initial tiers after a prefill of T0 tokens: dense = last W tokens,
+    sparse pool = every older token, condensed = empty."""
+    if T0 < W:
+        raise ValueError("the multi-step lifecycle starts with a full window")
+    d = K.shape[1]
+    ring_K = np.zeros((W, d), K.dtype)
+    ring_V = np.zeros((W, d), V.dtype)
+    for t in range(T0 - W, T0):
+        ring_K[t % W] = K[t]
+        ring_V[t % W] = V[t]
+    A = T0 - W
+    return HeadState(W, C, ring_K, ring_V, np.array(K[:A]), np.array(V[:A]),
+                     np.arange(A), np.zeros((nchunks, d)), np.zeros((nchunks, d)),
+                     np.zeros(nchunks, np.int64), T0)
+
+
+def lifecycle_step(st: HeadState, q_group, k_new, v_new, p: float, metric: int):
+    """One decode step of one head.
+
+    (1) Append: the new token at position P = T goes into ring slot P mod W;
+        the token it replaces (position P - W) leaves the window and is
+        appended to the end of the sparse pool.
+    (2) Score, calibrate and select top-p over the pool.
+    (3) Rewrite: the kept pool rows are compacted, positions ascending.
+    (4) Merge: every dropped pool token is added to the running sums of its
+        position-aligned chunk; it never returns to another tier.
+    Then attention over the ring, the rewritten pool and the chunks.
+    Returns (out [G, d] float64, HeadResult-like dict of the step).
+    """
+    W, C = st.W, st.C
+    P = st.T
+    slot = P % W
+    aged_pos = P - W
+    st.pool_K = np.concatenate([st.pool_K, st.ring_K[slot][None]], axis=0)
+    st.pool_V = np.concatenate([st.pool_V, st.ring_V[slot][None]], axis=0)
+    st.pool_pos = np.concatenate([st.pool_pos, [aged_pos]])
+    st.ring_K[slot] = k_new
+    st.ring_V[slot] = v_new
+    st.T = P + 1
+    ell, s = score_head(q_group, st.pool_K)
+    cal = calibrate_head(ell, s, metric)
+    sel = topp_head(cal.c, cal.w, cal.Z, p, positions=st.pool_pos)
+    keep = np.zeros(len(st.pool_pos), bool)
+    keep[sel.selected] = True
+    evicted = np.nonzero(~keep)[0]
+    ks, vs, cn = condense(st.pool_K, st.pool_V, evicted, st.pool_pos, C, len(st.cnt))
+    st.ksum += ks
+    st.vsum += vs
+    st.cnt += cn
+    n_before = len(st.pool_pos)
+    st.pool_K = st.pool_K[keep]
+    st.pool_V = st.pool_V[keep]
+    st.pool_pos = st.pool_pos[keep]
+    out = attend_head(q_group, st.ring_K, st.ring_V, st.pool_K, st.pool_V,
+                      st.ksum, st.vsum, st.cnt)
+    return out, {"n_candidates": n_before, "k": sel.k, "ell": ell, "s": s,
+                 "cal": cal, "sel": sel}
