@@ -1,0 +1,401 @@
+// C ABI of the HARD-KV decode-step library: argument validation, workspace
+// layout and the launch sequences.  Declarations and contracts: hardkv.h.
+#include <math.h>
+#include <string.h>
+
+#include "internal.h"
+
+using namespace hk;
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+int log2i(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+int max_aged(const hardkv_desc* d) { return d->ctx_cap > d->dense_window ? d->ctx_cap - d->dense_window : 0; }
+
+int validate(const hardkv_desc* d) {
+  if (!d) return HARDKV_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1) return HARDKV_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads) return HARDKV_ERR_INVALID_ARG;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return HARDKV_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return HARDKV_ERR_UNSUPPORTED;
+  if (d->dtype != HARDKV_F32 && d->dtype != HARDKV_BF16) return HARDKV_ERR_UNSUPPORTED;
+  if (d->dense_window < 0 || d->chunk < 1 || d->block_size < 0 || d->ctx_cap < 1)
+    return HARDKV_ERR_INVALID_ARG;
+  if (d->block_size > 0) {
+    if (d->block_size & (d->block_size - 1)) return HARDKV_ERR_UNSUPPORTED;
+    if (d->max_blocks < 1 || (int64_t)d->max_blocks * d->block_size < d->ctx_cap)
+      return HARDKV_ERR_INVALID_ARG;
+  }
+  if (!(d->top_p > 0.0f && d->top_p <= 1.0f)) return HARDKV_ERR_INVALID_ARG;  // NaN fails too
+  if (d->sparse_cap < 0 || d->chunk_cap < 0) return HARDKV_ERR_INVALID_ARG;
+  const int A = max_aged(d);
+  if (d->sparse_cap < A) return HARDKV_ERR_CAPACITY;
+  if ((int64_t)d->chunk_cap * d->chunk < A) return HARDKV_ERR_CAPACITY;
+  // every element offset must fit comfortably in 63 bits
+  const double elems = (double)d->batch * d->num_kv_heads *
+                       ((double)d->sparse_cap + d->ctx_cap + d->chunk_cap) * d->head_dim * 8.0;
+  if (elems > 4.0e18) return HARDKV_ERR_INVALID_ARG;
+  return HARDKV_OK;
+}
+
+struct Layout {
+  size_t q64, logit, l2, stats, mask, count, part, total;
+  int max_tiles;
+};
+
+Layout layout(const hardkv_desc* d) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t B = d->batch, Hq = d->num_q_heads, Hkv = d->num_kv_heads, D = d->head_dim;
+  const size_t G = Hq / Hkv, cap = d->sparse_cap;
+  L.q64 = take(B * Hq * D * 8);
+  L.logit = take(B * Hkv * cap * 4);
+  L.l2 = take(B * Hkv * cap * 4);
+  L.stats = take(B * Hkv * 4 * 8);
+  L.mask = take(B * Hkv * cap);
+  L.count = take(B * Hkv * 4);
+  L.max_tiles = attn_max_tiles(d->dense_window, d->sparse_cap, d->chunk_cap);
+  L.part = take(B * Hkv * (size_t)L.max_tiles * G * (D + 2) * 4);
+  L.total = off;
+  return L;
+}
+
+Rows cache_rows(const hardkv_desc* d, const void* base, const int32_t* table) {
+  Rows r{};
+  r.base = (const char*)base;
+  r.table = d->block_size > 0 ? table : nullptr;
+  r.region = d->ctx_cap;
+  r.hkv = d->num_kv_heads;
+  r.lbs = d->block_size > 0 ? log2i(d->block_size) : 0;
+  r.max_blocks = d->max_blocks;
+  r.row_bytes = d->head_dim * (d->dtype == HARDKV_F32 ? 4 : 2);
+  return r;
+}
+
+Rows region_rows(const hardkv_desc* d, const void* base, int64_t region) {
+  Rows r{};
+  r.base = (const char*)base;
+  r.table = nullptr;
+  r.region = region;
+  r.hkv = d->num_kv_heads;
+  r.row_bytes = d->head_dim * (d->dtype == HARDKV_F32 ? 4 : 2);
+  return r;
+}
+
+Cand aged_cand(const hardkv_desc* d, const int32_t* ctx_len) {
+  return Cand{ctx_len, nullptr, d->dense_window, d->ctx_cap, max_aged(d), d->num_kv_heads};
+}
+
+int launched() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? HARDKV_OK : HARDKV_ERR_HIP;
+}
+
+// ---------------------------------------------------------- launch steps --
+void do_score(const hardkv_desc* d, const Layout& L, char* ws, const void* q, const Rows& rows,
+              const Cand& cand, int max_cand, const int8_t* metric, float* logit, float* l2,
+              hipStream_t st) {
+  ScoreArgs a{};
+  a.dtype = d->dtype;
+  a.D = d->head_dim;
+  a.G = d->num_q_heads / d->num_kv_heads;
+  a.B = d->batch;
+  a.hq = d->num_q_heads;
+  a.q = q;
+  a.q64 = (double*)(ws + L.q64);
+  a.rows = rows;
+  a.cand = cand;
+  a.max_cand = max_cand;
+  a.metric = metric;
+  a.logit = logit;
+  a.l2 = l2;
+  a.cap_stride = d->sparse_cap;
+  a.scale = 1.0 / sqrt((double)d->head_dim);
+  launch_score(a, st);
+}
+
+SelectArgs select_args(const hardkv_desc* d, const Cand& cand, const int8_t* metric,
+                       const float* logit, const float* l2, double* stats, uint8_t* mask,
+                       int32_t* count) {
+  SelectArgs a{};
+  a.B = d->batch;
+  a.hkv = d->num_kv_heads;
+  a.cand = cand;
+  a.metric = metric;
+  a.logit = logit;
+  a.l2 = l2;
+  a.cap_stride = d->sparse_cap;
+  a.stats = stats;
+  a.top_p = d->top_p;
+  a.mask = mask;
+  a.count = count;
+  return a;
+}
+
+CompactArgs compact_args(const hardkv_desc* d, const Layout& L, char* ws, const Rows& kr,
+                         const Rows& vr, const Cand& cand, int max_cand, const uint8_t* mask,
+                         const hardkv_tiers* t) {
+  CompactArgs a{};
+  a.dtype = d->dtype;
+  a.D = d->head_dim;
+  a.B = d->batch;
+  a.hkv = d->num_kv_heads;
+  a.C = d->chunk;
+  a.krows = kr;
+  a.vrows = vr;
+  a.cand = cand;
+  a.max_cand = max_cand;
+  a.mask = mask;
+  a.cap_stride = d->sparse_cap;
+  a.out_k = (char*)t->k;
+  a.out_v = (char*)t->v;
+  a.out_pos = t->pos;
+  a.out_count = t->count;
+  a.ksum = t->ksum;
+  a.vsum = t->vsum;
+  a.ccount = t->ccount;
+  a.chunk_stride = d->chunk_cap;
+  return a;
+}
+
+AttnArgs attn_args(const hardkv_desc* d, const Layout& L, char* ws, const void* q,
+                   const hardkv_tiers* t, float* out) {
+  AttnArgs a{};
+  a.dtype = d->dtype;
+  a.D = d->head_dim;
+  a.G = d->num_q_heads / d->num_kv_heads;
+  a.B = d->batch;
+  a.hkv = d->num_kv_heads;
+  a.hq = d->num_q_heads;
+  a.q = q;
+  a.ctx_cap = d->ctx_cap;
+  a.W = d->dense_window;
+  a.sk = region_rows(d, t->k, d->sparse_cap);
+  a.sv = region_rows(d, t->v, d->sparse_cap);
+  a.count = t->count;
+  a.sparse_cap = d->sparse_cap;
+  a.ksum = t->ksum;
+  a.vsum = t->vsum;
+  a.ccount = t->ccount;
+  a.chunk_cap = d->chunk_cap;
+  a.C = d->chunk;
+  a.part = (float*)(ws + L.part);
+  a.max_tiles = L.max_tiles;
+  a.out = out;
+  a.scale = 1.0 / sqrt((double)d->head_dim);
+  return a;
+}
+
+bool tiers_ok(const hardkv_tiers* t) {
+  return t && t->k && t->v && t->pos && t->count && t->ksum && t->vsum && t->ccount;
+}
+bool cache_ok(const hardkv_desc* d, const hardkv_cache* c) {
+  return c && c->k && c->v && c->ctx_len && (d->block_size == 0 || c->block_table);
+}
+
+int common_checks(const hardkv_desc* d, void* ws, size_t ws_bytes) {
+  const int rc = validate(d);
+  if (rc != HARDKV_OK) return rc;
+  if (!ws || ws_bytes < layout(d).total) return HARDKV_ERR_WORKSPACE;
+  return HARDKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hardkv_version(void) { return kVersion; }
+
+const char* hardkv_strerror(int code) {
+  switch (code) {
+    case HARDKV_OK: return "ok";
+    case HARDKV_ERR_INVALID_ARG: return "invalid argument";
+    case HARDKV_ERR_UNSUPPORTED: return "unsupported head_dim, dtype or GQA group size";
+    case HARDKV_ERR_CAPACITY: return "sparse_cap or chunk_cap below the aged capacity";
+    case HARDKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case HARDKV_ERR_HIP: return "HIP launch failure";
+    default: return "unknown error";
+  }
+}
+
+int hardkv_validate(const hardkv_desc* desc) { return validate(desc); }
+
+size_t hardkv_workspace_size(const hardkv_desc* desc) {
+  if (validate(desc) != HARDKV_OK) return 0;
+  return layout(desc).total;
+}
+
+int hardkv_score(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
+                 const int8_t* metric, float* logit, float* l2, void* ws, size_t ws_bytes,
+                 hardkv_stream_t stream) {
+  int rc = common_checks(d, ws, ws_bytes);
+  if (rc) return rc;
+  if (!q || !cache_ok(d, cache) || !logit || (metric && !l2)) return HARDKV_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  hipGetLastError();
+  do_score(d, L, (char*)ws, q, cache_rows(d, cache->k, cache->block_table),
+           aged_cand(d, cache->ctx_len), max_aged(d), metric, logit, l2, (hipStream_t)stream);
+  return launched();
+}
+
+int hardkv_calibrate(const hardkv_desc* d, const int32_t* ctx_len, const int8_t* metric,
+                     const float* logit, const float* l2, double* stats, void* ws,
+                     size_t ws_bytes, hardkv_stream_t stream) {
+  int rc = common_checks(d, ws, ws_bytes);
+  if (rc) return rc;
+  if (!ctx_len || !logit || !stats || (metric && !l2)) return HARDKV_ERR_INVALID_ARG;
+  hipGetLastError();
+  launch_calibrate(select_args(d, aged_cand(d, ctx_len), metric, logit, l2, stats, nullptr, nullptr),
+                   (hipStream_t)stream);
+  return launched();
+}
+
+int hardkv_topp_select(const hardkv_desc* d, const int32_t* ctx_len, const int8_t* metric,
+                       const float* logit, const float* l2, const double* stats, uint8_t* mask,
+                       int32_t* count, void* ws, size_t ws_bytes, hardkv_stream_t stream) {
+  int rc = common_checks(d, ws, ws_bytes);
+  if (rc) return rc;
+  if (!ctx_len || !logit || !stats || !mask || !count || (metric && !l2))
+    return HARDKV_ERR_INVALID_ARG;
+  hipGetLastError();
+  launch_select(select_args(d, aged_cand(d, ctx_len), metric, logit, l2, (double*)stats, mask,
+                            count),
+                (hipStream_t)stream);
+  return launched();
+}
+
+int hardkv_compact(const hardkv_desc* d, const hardkv_cache* cache, const uint8_t* mask,
+                   const hardkv_tiers* out, void* ws, size_t ws_bytes, hardkv_stream_t stream) {
+  int rc = common_checks(d, ws, ws_bytes);
+  if (rc) return rc;
+  if (!cache_ok(d, cache) || !mask || !tiers_ok(out)) return HARDKV_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  hipGetLastError();
+  launch_compact(compact_args(d, L, (char*)ws, cache_rows(d, cache->k, cache->block_table),
+                              cache_rows(d, cache->v, cache->block_table),
+                              aged_cand(d, cache->ctx_len), max_aged(d), mask, out),
+                 (hipStream_t)stream);
+  return launched();
+}
+
+int hardkv_decode_attn(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
+                       const hardkv_tiers* tiers, float* out, void* ws, size_t ws_bytes,
+                       hardkv_stream_t stream) {
+  int rc = common_checks(d, ws, ws_bytes);
+  if (rc) return rc;
+  if (!q || !cache_ok(d, cache) || !tiers_ok(tiers) || !out) return HARDKV_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  AttnArgs a = attn_args(d, L, (char*)ws, q, tiers, out);
+  a.dk = cache_rows(d, cache->k, cache->block_table);
+  a.dv = cache_rows(d, cache->v, cache->block_table);
+  a.ctx_len = cache->ctx_len;
+  a.ring = false;
+  hipGetLastError();
+  launch_attn(a, (hipStream_t)stream);
+  return launched();
+}
+
+int hardkv_step(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
+                const int8_t* metric, const hardkv_tiers* tiers, float* out, void* ws,
+                size_t ws_bytes, hardkv_stream_t stream) {
+  int rc = common_checks(d, ws, ws_bytes);
+  if (rc) return rc;
+  if (!q || !cache_ok(d, cache) || !tiers_ok(tiers) || !out) return HARDKV_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  char* w = (char*)ws;
+  hipStream_t st = (hipStream_t)stream;
+  const Rows kr = cache_rows(d, cache->k, cache->block_table);
+  const Rows vr = cache_rows(d, cache->v, cache->block_table);
+  const Cand cand = aged_cand(d, cache->ctx_len);
+  float* logit = (float*)(w + L.logit);
+  float* l2 = (float*)(w + L.l2);
+  double* stats = (double*)(w + L.stats);
+  uint8_t* mask = (uint8_t*)(w + L.mask);
+  int32_t* count = (int32_t*)(w + L.count);
+  hipGetLastError();
+  do_score(d, L, w, q, kr, cand, max_aged(d), metric, logit, l2, st);
+  const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
+  launch_calibrate(sa, st);
+  launch_select(sa, st);
+  launch_compact(compact_args(d, L, w, kr, vr, cand, max_aged(d), mask, tiers), st);
+  AttnArgs a = attn_args(d, L, w, q, tiers, out);
+  a.dk = kr;
+  a.dv = vr;
+  a.ctx_len = cache->ctx_len;
+  a.ring = false;
+  launch_attn(a, st);
+  return launched();
+}
+
+int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
+                        const void* v_new, const int8_t* metric, const hardkv_state* s,
+                        float* out, void* ws, size_t ws_bytes, hardkv_stream_t stream) {
+  int rc = common_checks(d, ws, ws_bytes);
+  if (rc) return rc;
+  if (d->block_size != 0 || d->dense_window < 1) return HARDKV_ERR_INVALID_ARG;
+  if (!q || !k_new || !v_new || !s || !s->ring_k || !s->ring_v || !s->seq_len ||
+      !tiers_ok(&s->tiers) || !out)
+    return HARDKV_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  char* w = (char*)ws;
+  hipStream_t st = (hipStream_t)stream;
+  const hardkv_tiers* t = &s->tiers;
+  hipGetLastError();
+
+  AppendArgs ap{};
+  ap.dtype = d->dtype;
+  ap.D = d->head_dim;
+  ap.B = d->batch;
+  ap.hkv = d->num_kv_heads;
+  ap.W = d->dense_window;
+  ap.sparse_cap = d->sparse_cap;
+  ap.ctx_cap = d->ctx_cap;
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.ring_k = (char*)s->ring_k;
+  ap.ring_v = (char*)s->ring_v;
+  ap.pool_k = (char*)t->k;
+  ap.pool_v = (char*)t->v;
+  ap.pool_pos = t->pos;
+  ap.pool_count = t->count;
+  ap.seq_len = s->seq_len;
+  launch_append(ap, st);
+
+  const Cand cand{nullptr, t->count, d->dense_window, d->ctx_cap, d->sparse_cap,
+                  d->num_kv_heads};
+  const Rows pk = region_rows(d, t->k, d->sparse_cap);
+  const Rows pv = region_rows(d, t->v, d->sparse_cap);
+  float* logit = (float*)(w + L.logit);
+  float* l2 = (float*)(w + L.l2);
+  double* stats = (double*)(w + L.stats);
+  uint8_t* mask = (uint8_t*)(w + L.mask);
+  int32_t* count = (int32_t*)(w + L.count);
+  do_score(d, L, w, q, pk, cand, d->sparse_cap, metric, logit, l2, st);
+  const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
+  launch_calibrate(sa, st);
+  launch_select(sa, st);
+  launch_compact_inplace(compact_args(d, L, w, pk, pv, cand, d->sparse_cap, mask, t), st);
+  AttnArgs a = attn_args(d, L, w, q, t, out);
+  a.dk = region_rows(d, s->ring_k, d->dense_window);
+  a.dv = region_rows(d, s->ring_v, d->dense_window);
+  a.ctx_len = s->seq_len;
+  a.ring = true;
+  launch_attn(a, st);
+  launch_advance(s->seq_len, d->batch, st);
+  return launched();
+}
+
+}  // extern "C"

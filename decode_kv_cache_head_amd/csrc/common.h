@@ -1,0 +1,166 @@
+// Device helpers shared by the HARD-KV gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hardkv.h"
+
+namespace hk {
+
+// ---------------------------------------------------------------- elements --
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct Elt;
+template <>
+struct Elt<float> {
+  static constexpr int kPer16 = 4;  // elements per 16-byte piece
+  __device__ static inline void unpack(const uint4& v, float (&f)[4]) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ static inline float load1(const float* p) { return *p; }
+};
+template <>
+struct Elt<bf16_t> {
+  static constexpr int kPer16 = 8;
+  // bf16 -> f32 is exact: the 16 bits are the high half of the f32 pattern.
+  __device__ static inline void unpack(const uint4& v, float (&f)[8]) {
+    f[0] = __uint_as_float(v.x << 16);
+    f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16);
+    f[3] = __uint_as_float(v.y & 0xffff0000u);
+    f[4] = __uint_as_float(v.z << 16);
+    f[5] = __uint_as_float(v.z & 0xffff0000u);
+    f[6] = __uint_as_float(v.w << 16);
+    f[7] = __uint_as_float(v.w & 0xffff0000u);
+  }
+  __device__ static inline float load1(const bf16_t* p) {
+    return __uint_as_float(((uint32_t)p->bits) << 16);
+  }
+};
+
+// ------------------------------------------------------------ row sources --
+// Where the rows of one tensor live for every (sequence b, KV head h).
+//   contiguous: row(b, h, t) = base + ((b * Hkv + h) * region + t) * row_bytes
+//   paged:      row(b, h, t) = base + ((table[b][t >> lbs] * Hkv + h) * bs + (t & (bs-1))) * row_bytes
+struct Rows {
+  const char* base;
+  const int32_t* table;
+  int64_t region;
+  int32_t hkv;
+  int32_t lbs;  // log2(block size) when paged
+  int32_t max_blocks;
+  int32_t row_bytes;
+  __device__ inline const char* row(int b, int h, int t) const {
+    if (table) {
+      const int blk = table[(int64_t)b * max_blocks + (t >> lbs)];
+      return base + ((((int64_t)blk * hkv + h) << lbs) + (t & ((1 << lbs) - 1))) * row_bytes;
+    }
+    return base + (((int64_t)b * hkv + h) * region + t) * row_bytes;
+  }
+};
+
+// Number of candidate (aged / pool) tokens of (b, h).
+//   single step: clamp(ctx_len[b], 0, ctx_cap) - W, clamped to [0, cap]
+//   lifecycle:   count[b * Hkv + h], clamped to [0, cap]
+struct Cand {
+  const int32_t* ctx_len;
+  const int32_t* count;
+  int32_t W;
+  int32_t ctx_cap;
+  int32_t cap;
+  int32_t hkv;
+  __device__ inline int n(int b, int h) const {
+    int v;
+    if (count) {
+      v = count[b * hkv + h];
+    } else {
+      int T = ctx_len[b];
+      T = T < 0 ? 0 : (T > ctx_cap ? ctx_cap : T);
+      v = T - W;
+    }
+    v = v < 0 ? 0 : v;
+    return v > cap ? cap : v;
+  }
+};
+
+// ------------------------------------------------------------- ordering ---
+// Order-preserving key of a float: larger value -> larger key, -0 == +0.
+__device__ inline uint32_t okey(float c) {
+  c = c + 0.0f;  // -0 + +0 = +0
+  const uint32_t u = __float_as_uint(c);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float okey_inv(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Calibrated value c = fl32((x - shift) * scale).  For shift 0 and scale 1
+// (QK heads) this is x itself.
+__device__ inline float cval(float x, double shift, double scale) {
+  return (float)(((double)x - shift) * scale);
+}
+
+// Fixed-point weight round(exp(c - m) * 2^47); exp(c - m) <= 1.
+__device__ inline uint64_t wfix(float c, double m) {
+  const double w = exp((double)c - m);
+  return (uint64_t)__double2ull_rn(w * 140737488355328.0);
+}
+
+// ------------------------------------------------------- wave reductions --
+__device__ inline double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum over aligned groups of LPR lanes (LPR in {4, 8, 16, 32, 64}); every
+// lane of the group receives the group's sum.  Within 16-lane DPP rows the
+// exchanges use DPP moves; larger groups finish with lane shuffles.
+template <int LPR>
+__device__ inline float group_sum(float v) {
+  // quad butterfly: xor 1, xor 2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if constexpr (LPR == 8) {
+    // row_half_mirror: lane i <-> 7 - i within each half row; after the quad
+    // step this adds the other quad of the 8-lane group.
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  } else if constexpr (LPR >= 16) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+    if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (LPR >= 64) v += __shfl_xor(v, 32, 64);
+  }
+  return v;
+}
+
+// Lanes l and l ^ o for o >= LPR hold different rows; reduce across them.
+template <int LPR>
+__device__ inline float across_groups_max(float v) {
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+template <int LPR>
+__device__ inline float across_groups_sum(float v) {
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+}  // namespace hk

@@ -1,0 +1,123 @@
+// Host-side launch interfaces between the C ABI and the kernels.
+#pragma once
+
+#include "common.h"
+
+namespace hk {
+
+// Dispatch on element type, head dim and GQA group size (compile-time
+// specialisations for every supported combination).
+#define HK_DISPATCH_G(T, D, G, FN, ...)               \
+  do {                                                \
+    switch (G) {                                      \
+      case 1: FN<T, D, 1>(__VA_ARGS__); break;        \
+      case 2: FN<T, D, 2>(__VA_ARGS__); break;        \
+      case 4: FN<T, D, 4>(__VA_ARGS__); break;        \
+      default: FN<T, D, 8>(__VA_ARGS__); break;       \
+    }                                                 \
+  } while (0)
+#define HK_DISPATCH_D(T, D, G, FN, ...)                       \
+  do {                                                        \
+    if ((D) == 64) HK_DISPATCH_G(T, 64, G, FN, __VA_ARGS__);  \
+    else HK_DISPATCH_G(T, 128, G, FN, __VA_ARGS__);           \
+  } while (0)
+#define HK_DISPATCH(DT, D, G, FN, ...)                                  \
+  do {                                                                  \
+    if ((DT) == HARDKV_F32) HK_DISPATCH_D(float, D, G, FN, __VA_ARGS__); \
+    else HK_DISPATCH_D(bf16_t, D, G, FN, __VA_ARGS__);                  \
+  } while (0)
+
+struct ScoreArgs {
+  int dtype, D, G, B, hq;
+  const void* q;
+  double* q64;        // workspace [B][Hq][D]
+  Rows rows;          // candidate key rows
+  Cand cand;
+  int max_cand;       // upper bound of any (b, h)'s candidate count
+  const int8_t* metric;
+  float* logit;
+  float* l2;
+  int64_t cap_stride; // elements per (b, h) in logit / l2
+  double scale;       // 1 / sqrt(D)
+};
+void launch_score(const ScoreArgs& a, hipStream_t st);
+
+struct SelectArgs {
+  int B, hkv;
+  Cand cand;
+  const int8_t* metric;
+  const float* logit;
+  const float* l2;
+  int64_t cap_stride;
+  double* stats;        // [B][Hkv][4] {shift, scale, max, Z}
+  float top_p;
+  uint8_t* mask;        // [B][Hkv][cap_stride]
+  int32_t* count;       // [B][Hkv]
+};
+void launch_calibrate(const SelectArgs& a, hipStream_t st);
+void launch_select(const SelectArgs& a, hipStream_t st);
+
+// Tile of the single-step compaction: whole chunks, about 1024 tokens
+// (one chunk when a chunk is longer), processed in 64-row sub-tiles.
+inline int compact_tile(int C) { return C >= 1024 ? C : C * (1024 / C); }
+
+struct CompactArgs {
+  int dtype, D, B, hkv, C;
+  Rows krows, vrows;    // candidate rows
+  Cand cand;
+  int max_cand;
+  const uint8_t* mask;
+  int64_t cap_stride;   // mask / tier slots per (b, h)
+  char* out_k;          // [B][Hkv][cap_stride][D]
+  char* out_v;
+  int32_t* out_pos;
+  int32_t* out_count;
+  float* ksum;          // [B][Hkv][chunk_stride][D]
+  float* vsum;
+  int32_t* ccount;
+  int chunk_stride;
+};
+void launch_compact(const CompactArgs& a, hipStream_t st);
+void launch_compact_inplace(const CompactArgs& a, hipStream_t st);
+
+struct AttnArgs {
+  int dtype, D, G, B, hkv, hq;
+  const void* q;
+  // dense tier: single step = cache positions [A_b, T_b); lifecycle = ring of W slots
+  Rows dk, dv;
+  const int32_t* ctx_len;  // single step
+  int ctx_cap, W;
+  bool ring;
+  // sparse tier
+  Rows sk, sv;
+  const int32_t* count;
+  int sparse_cap;
+  // condensed tier
+  const float* ksum;
+  const float* vsum;
+  const int32_t* ccount;
+  int chunk_cap, C;
+  float* part;             // workspace partials
+  int max_tiles;
+  float* out;
+  double scale;
+};
+int attn_max_tiles(int W, int sparse_cap, int chunk_cap);
+void launch_attn(const AttnArgs& a, hipStream_t st);
+
+struct AppendArgs {
+  int dtype, D, B, hkv, W, sparse_cap, ctx_cap;
+  const void* k_new;
+  const void* v_new;
+  char* ring_k;
+  char* ring_v;
+  char* pool_k;
+  char* pool_v;
+  int32_t* pool_pos;
+  int32_t* pool_count;
+  const int32_t* seq_len;
+};
+void launch_append(const AppendArgs& a, hipStream_t st);
+void launch_advance(int32_t* seq_len, int B, hipStream_t st);
+
+}  // namespace hk

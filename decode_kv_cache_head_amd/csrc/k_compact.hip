@@ -1,0 +1,256 @@
+// Index Regularization (HARD-KV, gist.science technical summary, section
+// 2.C: Rewrite Cache moves the selected tokens into contiguous ranges,
+// Flatten Index pads every head to the maximum length) and the condensed
+// tier (section 2.A, Tier 3: evicted tokens merged into constant-size
+// storage).
+//
+// Single step: a tile is a whole number of position-aligned chunks (about
+// 1024 tokens, or one chunk when chunks are longer), processed in 64-row
+// sub-tiles.  A workgroup finds its first destination slot by counting the
+// kept tokens before its tile in the mask (one byte per token, L2-resident),
+// so tiles are independent and the rewrite is one launch.  Rows are staged
+// through LDS with 16-byte coalesced loads; kept rows are stored to their
+// slots as bit copies, evicted rows are summed into per-chunk float32 sums by
+// one thread per (tensor, dim), in ascending position order.  Sequences with
+// no candidate tokens write count = 0 from the first tile slot.
+//
+// Lifecycle (in place): k_compact_inplace runs one workgroup per (b, h) that
+// sweeps its pool in 64-row sub-tiles in order.  Every sub-tile is read
+// completely into LDS before any of its rows is written back, and a kept row
+// only moves to a slot at or below its own, so the left compaction never
+// overwrites a row that has not been read.  Evicted rows are added to the
+// running sums of chunk pos / C.
+#include "internal.h"
+
+namespace hk {
+
+__device__ inline int block_excl_scan_256(int v, int* sh, int& total) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (l >= o) incl += u;
+  }
+  __syncthreads();
+  if (l == 63) sh[w] = incl;
+  __syncthreads();
+  int off = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < w) off += sh[i];
+    total += sh[i];
+  }
+  return off + incl - v;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
+  constexpr int RB = D * (int)sizeof(T);
+  constexpr int CPR = RB / 16;
+  constexpr int PIECES = 2 * 64 * CPR;     // K and V pieces of one 64-row sub-tile
+  constexpr int PER = PIECES / 256;
+  __shared__ __attribute__((aligned(16))) unsigned char sk[64 * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char sv[64 * RB];
+  __shared__ int s_rank[64];
+  __shared__ int s_sel[64];
+  __shared__ int s_base;
+  __shared__ int s_scan[4];
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int n = a.cand.n(b, h);
+  const int t0 = j * TT;
+  const int64_t bh = (int64_t)b * a.hkv + h;
+  if (t0 >= n) {
+    if (j == 0 && tid == 0) a.out_count[bh] = 0;
+    return;
+  }
+  const int tend = min(t0 + TT, n);
+  const uint8_t* mk = a.mask + bh * a.cap_stride;
+  char* ok = a.out_k + bh * a.cap_stride * RB;
+  char* ov = a.out_v + bh * a.cap_stride * RB;
+  int32_t* pos = a.out_pos + bh * a.cap_stride;
+  // first destination slot of this tile: kept tokens before t0
+  int base;
+  {
+    int c = 0;
+#pragma unroll 8
+    for (int t = tid; t < t0; t += 256) c += mk[t] != 0;
+    int total;
+    block_excl_scan_256(c, s_scan, total);
+    base = total;
+  }
+
+  const bool summer = tid < 2 * D;
+  const int tensor = tid / D, dim = tid % D;
+  float acc = 0.f;
+  int cnt = 0;
+  int cur = t0 / a.C;
+  auto flush = [&](int ch) {
+    float* dst = (tensor ? a.vsum : a.ksum) + (bh * a.chunk_stride + ch) * D + dim;
+    *dst = acc;
+    if (tid == 0) a.ccount[bh * a.chunk_stride + ch] = cnt;
+  };
+
+  for (int s0 = t0; s0 < tend; s0 += 64) {
+    const int nr = min(64, tend - s0);
+    if (tid < 64) {
+      const bool sel = tid < nr && mk[s0 + tid] != 0;
+      const unsigned long long bal = __ballot(sel);
+      const int rk = base + __popcll(bal & ((1ull << tid) - 1ull));
+      s_sel[tid] = sel;
+      s_rank[tid] = rk;
+      if (sel) pos[rk] = s0 + tid;
+      if (tid == 0) s_base = base + __popcll(bal);
+    }
+    uint4 buf[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
+      // rows past the sub-tile re-read its last row (in bounds, never stored)
+      const int t = s0 + min(r, nr - 1);
+      const char* src = tsr ? a.vrows.row(b, h, t) : a.krows.row(b, h, t);
+      buf[k] = *(const uint4*)(src + c * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
+      *(uint4*)((tsr ? sv : sk) + r * RB + c * 16) = buf[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
+      if (r < nr && s_sel[r])
+        *(uint4*)((tsr ? ov : ok) + (int64_t)s_rank[r] * RB + c * 16) =
+            *(const uint4*)((tsr ? sv : sk) + r * RB + c * 16);
+    }
+    if (summer) {
+      const T* src = (const T*)(tensor ? sv : sk);
+      for (int r = 0; r < nr; ++r) {
+        const int ch = (s0 + r) / a.C;
+        if (ch != cur) {
+          flush(cur);
+          cur = ch;
+          acc = 0.f;
+          cnt = 0;
+        }
+        if (!s_sel[r]) {
+          acc += Elt<T>::load1(src + r * D + dim);
+          ++cnt;
+        }
+      }
+    }
+    base = s_base;
+    __syncthreads();
+  }
+  if (summer) flush(cur);
+  if (tid == 0 && tend == n) a.out_count[bh] = base;
+}
+
+template <typename T, int D, int G_unused>
+static void launch_compact_t(const CompactArgs& a, hipStream_t st) {
+  const int TT = compact_tile(a.C);
+  const int nt = max(1, ceil_div(a.max_cand, TT));  // tile 0 also writes count = 0
+  hipLaunchKernelGGL((k_compact<T, D>), dim3(nt, a.hkv, a.B), dim3(256), 0, st, a, TT);
+}
+
+void launch_compact(const CompactArgs& a, hipStream_t st) {
+  HK_DISPATCH(a.dtype, a.D, 1, launch_compact_t, a, st);
+}
+
+// ------------------------------------------------------------ in place ----
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_compact_inplace(CompactArgs a) {
+  constexpr int RB = D * (int)sizeof(T);
+  constexpr int CPR = RB / 16;
+  constexpr int PIECES = 2 * 64 * CPR;
+  constexpr int PER = PIECES / 256;
+  __shared__ __attribute__((aligned(16))) unsigned char sk[64 * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char sv[64 * RB];
+  __shared__ int s_rank[64];
+  __shared__ int s_sel[64];
+  __shared__ int s_pos[64];
+  __shared__ int s_base;
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int n = a.cand.n(b, h);
+  const int64_t bh = (int64_t)b * a.hkv + h;
+  const uint8_t* mk = a.mask + bh * a.cap_stride;
+  char* pk = a.out_k + bh * a.cap_stride * RB;   // pool rows (read and written)
+  char* pv = a.out_v + bh * a.cap_stride * RB;
+  int32_t* pos = a.out_pos + bh * a.cap_stride;
+  const bool summer = tid < 2 * D;
+  const int tensor = tid / D, dim = tid % D;
+  float acc = 0.f;
+  int cnt = 0;
+  int cur = -1;
+  auto flush = [&]() {
+    if (cur < 0 || cur >= a.chunk_stride) return;  // positions outside the chunk capacity
+    float* dst = (tensor ? a.vsum : a.ksum) + (bh * a.chunk_stride + cur) * D + dim;
+    *dst += acc;
+    if (tid == 0) a.ccount[bh * a.chunk_stride + cur] += cnt;
+  };
+  int base = 0;
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int nr = min(64, n - s0);
+    if (tid < 64) {
+      const bool sel = tid < nr && mk[s0 + tid] != 0;
+      const unsigned long long bal = __ballot(sel);
+      s_sel[tid] = sel;
+      s_rank[tid] = base + __popcll(bal & ((1ull << tid) - 1ull));
+      s_pos[tid] = tid < nr ? pos[s0 + tid] : 0;
+      if (tid == 0) s_base = base + __popcll(bal);
+    }
+    uint4 buf[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
+      buf[k] = *(const uint4*)((tsr ? pv : pk) + (int64_t)(s0 + min(r, nr - 1)) * RB + c * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
+      if (r < nr) *(uint4*)((tsr ? sv : sk) + r * RB + c * 16) = buf[k];
+    }
+    __syncthreads();  // the whole sub-tile (rows, positions, ranks) is read
+    // write kept rows to their (lower or equal) slots
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
+      if (r < nr && s_sel[r] && s_rank[r] != s0 + r)
+        *(uint4*)((tsr ? pv : pk) + (int64_t)s_rank[r] * RB + c * 16) =
+            *(const uint4*)((tsr ? sv : sk) + r * RB + c * 16);
+    }
+    if (tid < nr && s_sel[tid]) pos[s_rank[tid]] = s_pos[tid];
+    if (summer) {
+      const T* src = (const T*)(tensor ? sv : sk);
+      for (int r = 0; r < nr; ++r) {
+        if (s_sel[r]) continue;
+        const int ch = s_pos[r] / a.C;
+        if (ch != cur) {
+          flush();
+          cur = ch;
+          acc = 0.f;
+          cnt = 0;
+        }
+        acc += Elt<T>::load1(src + r * D + dim);
+        ++cnt;
+      }
+    }
+    base = s_base;
+    __syncthreads();
+  }
+  if (summer) flush();
+  if (tid == 0) a.out_count[bh] = base;
+}
+
+template <typename T, int D, int G_unused>
+static void launch_compact_inplace_t(const CompactArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_compact_inplace<T, D>), dim3(a.hkv, a.B), dim3(256), 0, st, a);
+}
+
+void launch_compact_inplace(const CompactArgs& a, hipStream_t st) {
+  HK_DISPATCH(a.dtype, a.D, 1, launch_compact_inplace_t, a, st);
+}
+
+}  // namespace hk

@@ -1,0 +1,297 @@
+// Logits Calibration and Calibrated Top-p selection (HARD-KV, gist.science
+// technical summary, section 2.B "Mechanism"/"Outcome" and section 2.A,
+// Tier 2).
+//
+// calibrate: one workgroup per (b, h).  Deterministic float64 block
+//   reductions (fixed lane/wave order, no atomics): moments for key-norm
+//   heads, then m = max c and Z = sum exp(c - m).
+// select: one 1024-thread workgroup per (b, h).  Radix select by MASS on the
+//   order-preserving 32-bit key of the float32 calibrated value: 11/11/10-bit
+//   passes, each accumulating per-bin mass in LDS as 2^-47 fixed point
+//   (integer atomics, so the result does not depend on the order of the
+//   additions).  The cutoff key K* is the bin where the mass accumulated from
+//   the top first reaches ceil(p * Z); the tokens tied at K* are taken lowest
+//   position first, as many as needed.  A final ordered pass writes the mask.
+#include "internal.h"
+
+namespace hk {
+
+template <int NW>
+__device__ inline double block_sum_f64(double v, double* sh) {
+  v = wave_sum_f64(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) sh[w] = v;
+  __syncthreads();
+  double r = sh[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r += sh[i];
+  return r;
+}
+
+template <int NW>
+__device__ inline float block_max_f32(float v, float* sh) {
+  v = wave_max_f32(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) sh[w] = v;
+  __syncthreads();
+  float r = sh[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, sh[i]);
+  return r;
+}
+
+// ------------------------------------------------------------ calibrate ---
+__global__ __launch_bounds__(256) void k_calibrate(Cand cand, const int8_t* __restrict__ metric,
+                                                   const float* __restrict__ logit,
+                                                   const float* __restrict__ l2,
+                                                   int64_t cap_stride, double* __restrict__ stats) {
+  __shared__ double shd[4];
+  __shared__ float shf[4];
+  const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
+  const int n = cand.n(b, h);
+  const int64_t bh = (int64_t)b * hkv + h;
+  const float* x = logit + bh * cap_stride;
+  const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
+  double shift = 0.0, scale = 1.0;
+  if (is_l2) {
+    const float* s = l2 + bh * cap_stride;
+    double sx = 0.0, sy = 0.0;
+    for (int t = tid; t < n; t += 256) {
+      sx += (double)x[t];
+      sy += (double)s[t];
+    }
+    sx = block_sum_f64<4>(sx, shd);
+    sy = block_sum_f64<4>(sy, shd);
+    const double mux = n ? sx / n : 0.0, mus = n ? sy / n : 0.0;
+    double vx = 0.0, vy = 0.0;
+    for (int t = tid; t < n; t += 256) {
+      const double dx = (double)x[t] - mux, dy = (double)s[t] - mus;
+      vx += dx * dx;
+      vy += dy * dy;
+    }
+    vx = block_sum_f64<4>(vx, shd);
+    vy = block_sum_f64<4>(vy, shd);
+    const double sdx = n ? sqrt(vx / n) : 0.0, sds = n ? sqrt(vy / n) : 0.0;
+    if (sdx == 0.0 || sds == 0.0) {
+      shift = 0.0;
+      scale = 0.0;
+    } else {
+      shift = mus;
+      scale = sdx / sds;
+    }
+    x = s;
+  }
+  float m = -INFINITY;
+  for (int t = tid; t < n; t += 256) m = fmaxf(m, is_l2 ? cval(x[t], shift, scale) : x[t]);
+  m = block_max_f32<4>(m, shf);
+  double Z = 0.0;
+  for (int t = tid; t < n; t += 256) {
+    const float c = is_l2 ? cval(x[t], shift, scale) : x[t];
+    Z += exp((double)c - (double)m);
+  }
+  Z = block_sum_f64<4>(Z, shd);
+  if (tid == 0) {
+    double* o = stats + bh * 4;
+    o[0] = shift;
+    o[1] = scale;
+    o[2] = n ? (double)m : 0.0;
+    o[3] = n ? Z : 0.0;
+  }
+}
+
+// --------------------------------------------------------------- select ---
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+
+// ceil(p * Z) exactly, p a float in (0, 1), Z < 2^63.
+__device__ inline uint64_t ceil_mul(float p, uint64_t Z) {
+  int ex;
+  const float f = frexpf(p, &ex);                      // p = f * 2^ex, f in [0.5, 1)
+  const uint64_t mant = (uint64_t)(f * 16777216.0f);   // exact 24-bit significand
+  const int sh = 24 - ex;                              // p = mant * 2^-sh, sh >= 24
+  const unsigned __int128 prod = (unsigned __int128)mant * Z;
+  if (sh >= 120) return prod ? 1 : 0;
+  const unsigned __int128 one = 1;
+  return (uint64_t)((prod + ((one << sh) - 1)) >> sh);
+}
+
+struct SelShared {
+  unsigned long long hist[2048];
+  unsigned long long target;
+  unsigned long long above;
+  uint32_t bin;
+  int wc[kSelWaves];
+  int red[kSelWaves];
+};
+
+// Run by wave 0: the largest bin whose suffix mass (bins at or above it)
+// reaches `target`; records the bin and the mass strictly above it.  With
+// from_total, the target is first set to max(ceil(p * total), 1).
+template <int NB>
+__device__ inline void find_bin(SelShared& S, bool from_total, float p) {
+  const int lane = threadIdx.x;
+  constexpr int PER = NB / 64;
+  unsigned long long s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s += S.hist[lane * PER + i];
+  unsigned long long suf = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long v = __shfl_down(suf, o, 64);
+    if (lane + o < 64) suf += v;
+  }
+  unsigned long long target;
+  if (from_total) {
+    const unsigned long long total = __shfl(suf, 0, 64);
+    target = ceil_mul(p, total);
+    if (target < 1) target = 1;
+  } else {
+    target = S.target;
+  }
+  const unsigned long long ok = __ballot(suf >= target);
+  const int L = __popcll(ok) - 1;
+  if (lane == L) {
+    unsigned long long run = suf - s;
+    for (int i = PER - 1; i >= 0; --i) {
+      const unsigned long long hv = S.hist[lane * PER + i];
+      if (run + hv >= target) {
+        S.bin = lane * PER + i;
+        S.above = run;
+        break;
+      }
+      run += hv;
+    }
+  }
+  if (from_total && lane == 0) S.target = target;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t* __restrict__ metric,
+                                                        const float* __restrict__ logit,
+                                                        const float* __restrict__ l2,
+                                                        int64_t cap_stride,
+                                                        const double* __restrict__ stats,
+                                                        float top_p, uint8_t* __restrict__ mask,
+                                                        int32_t* __restrict__ count) {
+  __shared__ SelShared S;
+  const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
+  const int n = cand.n(b, h);
+  const int64_t bh = (int64_t)b * hkv + h;
+  uint8_t* mk = mask + bh * cap_stride;
+  if (n == 0) {
+    if (tid == 0) count[bh] = 0;
+    return;
+  }
+  if (!(top_p < 1.0f)) {
+    for (int t = tid; t < n; t += kSelThreads) mk[t] = 1;
+    if (tid == 0) count[bh] = n;
+    return;
+  }
+  const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
+  const float* x = (is_l2 ? l2 : logit) + bh * cap_stride;
+  const double shift = stats[bh * 4 + 0], scale = stats[bh * 4 + 1], m = stats[bh * 4 + 2];
+  auto cv = [&](int t) -> float { return is_l2 ? cval(x[t], shift, scale) : x[t]; };
+
+  // pass 1: top 11 bits of the key
+  for (int i = tid; i < 2048; i += kSelThreads) S.hist[i] = 0;
+  __syncthreads();
+  for (int t = tid; t < n; t += kSelThreads) {
+    const float c = cv(t);
+    const uint64_t w = wfix(c, m);
+    if (w) atomicAdd(&S.hist[okey(c) >> 21], (unsigned long long)w);
+  }
+  __syncthreads();
+  if (tid < 64) find_bin<2048>(S, true, top_p);
+  __syncthreads();
+  const unsigned long long target = S.target;
+  const uint32_t b1 = S.bin;
+  unsigned long long above = S.above;
+  __syncthreads();
+
+  // pass 2: next 11 bits inside bin b1
+  for (int i = tid; i < 2048; i += kSelThreads) S.hist[i] = 0;
+  if (tid == 0) S.target = target - above;
+  __syncthreads();
+  for (int t = tid; t < n; t += kSelThreads) {
+    const float c = cv(t);
+    const uint32_t k = okey(c);
+    if ((k >> 21) == b1) atomicAdd(&S.hist[(k >> 10) & 2047u], (unsigned long long)wfix(c, m));
+  }
+  __syncthreads();
+  if (tid < 64) find_bin<2048>(S, false, top_p);
+  __syncthreads();
+  const uint32_t b2 = S.bin;
+  above += S.above;
+  const unsigned long long t2 = S.target;
+  __syncthreads();
+
+  // pass 3: last 10 bits inside (b1, b2)
+  for (int i = tid; i < 1024; i += kSelThreads) S.hist[i] = 0;
+  if (tid == 0) S.target = t2 - S.above;
+  __syncthreads();
+  const uint32_t pre = (b1 << 11) | b2;
+  for (int t = tid; t < n; t += kSelThreads) {
+    const float c = cv(t);
+    const uint32_t k = okey(c);
+    if ((k >> 10) == pre) atomicAdd(&S.hist[k & 1023u], (unsigned long long)wfix(c, m));
+  }
+  __syncthreads();
+  if (tid < 64) find_bin<1024>(S, false, top_p);
+  __syncthreads();
+  const uint32_t kstar = (pre << 10) | S.bin;
+  above += S.above;
+  // all tokens tied at K* carry the same weight; take r of them
+  const unsigned long long wstar = wfix(okey_inv(kstar), m);
+  const unsigned long long need = target - above;
+  const unsigned long long r = (need + wstar - 1) / wstar;
+
+  // pass 4: mask, ties by ascending position
+  const int wv = tid >> 6, ln = tid & 63;
+  unsigned long long carried = 0;
+  int nsel = 0;
+  for (int t0 = 0; t0 < n; t0 += kSelThreads) {
+    const int t = t0 + tid;
+    const bool valid = t < n;
+    const uint32_t k = valid ? okey(cv(t)) : 0u;
+    const bool tie = valid && k == kstar;
+    const int ntie = __syncthreads_count(tie);
+    unsigned long long rank = 0;
+    if (ntie) {
+      const unsigned long long bal = __ballot(tie);
+      if (ln == 0) S.wc[wv] = __popcll(bal);
+      __syncthreads();
+      int off = 0;
+      for (int i = 0; i < wv; ++i) off += S.wc[i];
+      __syncthreads();
+      rank = carried + off + __popcll(bal & ((1ull << ln) - 1ull));
+      carried += ntie;
+    }
+    const bool sel = valid && (k > kstar || (tie && rank < r));
+    if (valid) mk[t] = sel ? 1 : 0;
+    nsel += sel;
+  }
+  // block sum of nsel
+  int v = nsel;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (ln == 0) S.red[wv] = v;
+  __syncthreads();
+  if (tid == 0) {
+    int tot = 0;
+    for (int i = 0; i < kSelWaves; ++i) tot += S.red[i];
+    count[bh] = tot;
+  }
+}
+
+void launch_calibrate(const SelectArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_calibrate, dim3(a.hkv, a.B), dim3(256), 0, st, a.cand, a.metric, a.logit,
+                     a.l2, a.cap_stride, a.stats);
+}
+
+void launch_select(const SelectArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_select, dim3(a.hkv, a.B), dim3(kSelThreads), 0, st, a.cand, a.metric,
+                     a.logit, a.l2, a.cap_stride, (const double*)a.stats, a.top_p, a.mask, a.count);
+}
+
+}  // namespace hk

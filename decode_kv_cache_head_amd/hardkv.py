@@ -1,0 +1,234 @@
+"""ctypes binding of libhardkv.so (the HIP library).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels behind the C ABI declared in include/hardkv.h.  Tensors are torch
+tensors on the GPU; their data pointers and the current HIP stream are passed
+through.  A missing library raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhardkv.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+METRIC_QK, METRIC_L2 = 0, 1
+
+_lib = None
+
+
+class HardKVError(RuntimeError):
+    def __init__(self, code, fn):
+        self.code = code
+        msg = _lib.hardkv_strerror(code).decode() if _lib else str(code)
+        super().__init__(f"{fn}: {msg} ({code})")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("dense_window", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("ctx_cap", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("sparse_cap", ctypes.c_int32), ("chunk_cap", ctypes.c_int32),
+                ("top_p", ctypes.c_float)]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("ctx_len", ctypes.c_void_p)]
+
+
+class TiersC(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("count", ctypes.c_void_p), ("ksum", ctypes.c_void_p),
+                ("vsum", ctypes.c_void_p), ("ccount", ctypes.c_void_p)]
+
+
+class StateC(ctypes.Structure):
+    _fields_ = [("ring_k", ctypes.c_void_p), ("ring_v", ctypes.c_void_p),
+                ("tiers", TiersC), ("seq_len", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "hardkv_version": ([], ctypes.c_int),
+    "hardkv_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "hardkv_validate": ([ctypes.POINTER(Desc)], ctypes.c_int),
+    "hardkv_workspace_size": ([ctypes.POINTER(Desc)], ctypes.c_size_t),
+    "hardkv_score": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(Cache), _P, _P, _P, _P,
+                      ctypes.c_size_t, _P], ctypes.c_int),
+    "hardkv_calibrate": ([ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+                         ctypes.c_int),
+    "hardkv_topp_select": ([ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P, _P, _P,
+                            ctypes.c_size_t, _P], ctypes.c_int),
+    "hardkv_compact": ([ctypes.POINTER(Desc), ctypes.POINTER(Cache), _P, ctypes.POINTER(TiersC),
+                        _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hardkv_decode_attn": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(Cache),
+                            ctypes.POINTER(TiersC), _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hardkv_step": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(Cache), _P,
+                     ctypes.POINTER(TiersC), _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hardkv_step_inplace": ([ctypes.POINTER(Desc), _P, _P, _P, _P, ctypes.POINTER(StateC), _P,
+                             _P, ctypes.c_size_t, _P], ctypes.c_int),
+}
+EXPORTS = tuple(_SIGS)
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with python -m decode_kv_cache_head_amd.build")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(rc, fn):
+    if rc != OK:
+        raise HardKVError(rc, fn)
+
+
+def make_desc(B, Hq, Hkv, d, dtype, W, C, top_p, ctx_cap, block_size=0, max_blocks=0,
+              sparse_cap=None, chunk_cap=None) -> Desc:
+    A = max(ctx_cap - W, 0)
+    if sparse_cap is None:
+        sparse_cap = A
+    if chunk_cap is None:
+        chunk_cap = -(-A // C) if C > 0 else 0
+    return Desc(B, Hq, Hkv, d, dtype, W, C, block_size, ctx_cap, max_blocks, sparse_cap,
+                chunk_cap, float(top_p))
+
+
+def validate(desc: Desc) -> int:
+    return load().hardkv_validate(ctypes.byref(desc))
+
+
+def workspace_size(desc: Desc) -> int:
+    return load().hardkv_workspace_size(ctypes.byref(desc))
+
+
+def alloc_workspace(desc: Desc, device="cuda"):
+    n = workspace_size(desc)
+    if n == 0:
+        _check(validate(desc), "workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+@dataclass
+class Tiers:
+    k: torch.Tensor
+    v: torch.Tensor
+    pos: torch.Tensor
+    count: torch.Tensor
+    ksum: torch.Tensor
+    vsum: torch.Tensor
+    ccount: torch.Tensor
+
+    def c(self) -> TiersC:
+        return TiersC(*(ctypes.c_void_p(t.data_ptr()) for t in
+                        (self.k, self.v, self.pos, self.count, self.ksum, self.vsum, self.ccount)))
+
+
+def alloc_tiers(desc: Desc, device="cuda", zero=False) -> Tiers:
+    B, Hkv, d = desc.batch, desc.num_kv_heads, desc.head_dim
+    dt = torch.float32 if desc.dtype == F32 else torch.bfloat16
+    mk = torch.zeros if zero else torch.empty
+    cap, ccap = desc.sparse_cap, desc.chunk_cap
+    return Tiers(mk((B, Hkv, cap, d), dtype=dt, device=device),
+                 mk((B, Hkv, cap, d), dtype=dt, device=device),
+                 mk((B, Hkv, cap), dtype=torch.int32, device=device),
+                 mk((B, Hkv), dtype=torch.int32, device=device),
+                 mk((B, Hkv, ccap, d), dtype=torch.float32, device=device),
+                 mk((B, Hkv, ccap, d), dtype=torch.float32, device=device),
+                 mk((B, Hkv, ccap), dtype=torch.int32, device=device))
+
+
+def cache_struct(k, v, ctx_len, block_table=None) -> Cache:
+    return Cache(_p(k), _p(v), _p(block_table), _p(ctx_len))
+
+
+def score(desc, q, cache: Cache, metric, logit, l2, ws, stream=None):
+    rc = load().hardkv_score(ctypes.byref(desc), _p(q), ctypes.byref(cache), _p(metric),
+                             _p(logit), _p(l2), _p(ws), ws.numel(), _stream(stream))
+    _check(rc, "hardkv_score")
+
+
+def calibrate(desc, ctx_len, metric, logit, l2, stats, ws, stream=None):
+    rc = load().hardkv_calibrate(ctypes.byref(desc), _p(ctx_len), _p(metric), _p(logit), _p(l2),
+                                 _p(stats), _p(ws), ws.numel(), _stream(stream))
+    _check(rc, "hardkv_calibrate")
+
+
+def topp_select(desc, ctx_len, metric, logit, l2, stats, mask, count, ws, stream=None):
+    rc = load().hardkv_topp_select(ctypes.byref(desc), _p(ctx_len), _p(metric), _p(logit),
+                                   _p(l2), _p(stats), _p(mask), _p(count), _p(ws), ws.numel(),
+                                   _stream(stream))
+    _check(rc, "hardkv_topp_select")
+
+
+def compact(desc, cache: Cache, mask, tiers: Tiers, ws, stream=None):
+    tc = tiers.c()
+    rc = load().hardkv_compact(ctypes.byref(desc), ctypes.byref(cache), _p(mask), ctypes.byref(tc),
+                               _p(ws), ws.numel(), _stream(stream))
+    _check(rc, "hardkv_compact")
+
+
+def decode_attn(desc, q, cache: Cache, tiers: Tiers, out, ws, stream=None):
+    tc = tiers.c()
+    rc = load().hardkv_decode_attn(ctypes.byref(desc), _p(q), ctypes.byref(cache),
+                                   ctypes.byref(tc), _p(out), _p(ws), ws.numel(), _stream(stream))
+    _check(rc, "hardkv_decode_attn")
+
+
+def step(desc, q, cache: Cache, metric, tiers: Tiers, out, ws, stream=None):
+    tc = tiers.c()
+    rc = load().hardkv_step(ctypes.byref(desc), _p(q), ctypes.byref(cache), _p(metric),
+                            ctypes.byref(tc), _p(out), _p(ws), ws.numel(), _stream(stream))
+    _check(rc, "hardkv_step")
+
+
+@dataclass
+class State:
+    ring_k: torch.Tensor
+    ring_v: torch.Tensor
+    tiers: Tiers
+    seq_len: torch.Tensor
+
+    def c(self) -> StateC:
+        return StateC(_p(self.ring_k), _p(self.ring_v), self.tiers.c(), _p(self.seq_len))
+
+
+def step_inplace(desc, q, k_new, v_new, metric, state: State, out, ws, stream=None):
+    sc = state.c()
+    rc = load().hardkv_step_inplace(ctypes.byref(desc), _p(q), _p(k_new), _p(v_new), _p(metric),
+                                    ctypes.byref(sc), _p(out), _p(ws), ws.numel(),
+                                    _stream(stream))
+    _check(rc, "hardkv_step_inplace")
+
+
+def scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

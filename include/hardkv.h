@@ -1,0 +1,228 @@
+/*
+ * hardkv.h -- C ABI of the HARD-KV decode-step library for MI355X (gfx950).
+ *
+ * The method is "HARD-KV: Head-Adaptive Regularization for Decoding-time KV
+ * Compression" (arXiv abstract on mlsanity.com; gist.science technical
+ * summary, section 2 "Methodology").  Per KV head, one decode step:
+ *   score      q.K importance of every aged token            (section 2.B, Goal)
+ *   calibrate  per-head softmax into one probability space  (section 2.B, Mechanism)
+ *   top-p      smallest calibrated set with mass >= p       (section 2.A, Tier 2)
+ *   compact    rewrite the selection into contiguous slots  (section 2.C, Rewrite
+ *              Cache + Flatten Index) and pool the evicted
+ *              tokens into condensed chunks                 (section 2.A, Tier 3)
+ *   attention  over dense + sparse + condensed tiers        (abstract; section 3)
+ * hardkv_step chains all of them; hardkv_step_inplace runs the multi-step
+ * token lifecycle (section 2.A four-step pipeline) on persistent tiers.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a caller-owned DEVICE pointer unless it is a
+ *     `const hardkv_*` descriptor struct, which lives in HOST memory and is
+ *     read only during the call.  The library never allocates, frees or
+ *     retains caller memory; kernels use the buffers until they complete on
+ *     the given stream.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work: no host synchronisation, no device-to-host reads, no
+ *     allocation, so every call can be captured into a HIP graph.
+ *   - Every argument is validated on the host before the first launch; a call
+ *     that returns an error has enqueued nothing.  Faults inside kernels show
+ *     up at the caller's next synchronisation of the stream.  No C++
+ *     exception crosses the ABI.
+ *   - Device-resident sizes (ctx_len, counts) are clamped by the kernels to
+ *     the capacities in the descriptor, so a bad value cannot make a kernel
+ *     read or write out of bounds.
+ *   - Shapes: B sequences, Hq query heads, Hkv KV heads, G = Hq / Hkv query
+ *     heads per KV head (query head g belongs to KV head g / G), d head dim,
+ *     T_b context length of sequence b (current token included), W dense
+ *     window, C chunk size, A_b = max(T_b - W, 0) aged tokens.
+ *   - Thread safety: no global mutable state; calls on distinct streams with
+ *     distinct buffers may run concurrently.
+ */
+#ifndef HARDKV_H
+#define HARDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hardkv_stream_t; /* same type as hipStream_t */
+
+/* Return codes. */
+#define HARDKV_OK 0
+#define HARDKV_ERR_INVALID_ARG -1  /* null pointer, Hq % Hkv != 0, top_p not in (0,1], W < 0, C < 1, ... */
+#define HARDKV_ERR_UNSUPPORTED -2  /* head_dim not 64/128, dtype, G not in {1,2,4,8} */
+#define HARDKV_ERR_CAPACITY -3     /* sparse_cap / chunk_cap smaller than the aged capacity */
+#define HARDKV_ERR_WORKSPACE -4    /* workspace missing or smaller than hardkv_workspace_size() */
+#define HARDKV_ERR_HIP -5          /* a kernel launch failed (hipGetLastError) */
+
+/* Element types of q, K and V (the compacted K/V use the cache's type). */
+#define HARDKV_F32 0
+#define HARDKV_BF16 1
+
+/* Importance metric per KV head. */
+#define HARDKV_METRIC_QK 0 /* max over the GQA group of q.k / sqrt(d) ("max-pooled logits") */
+#define HARDKV_METRIC_L2 1 /* key L2 norm, calibrated onto the head's logit spread */
+
+/* Shapes and policy of one decode step (host memory). */
+typedef struct hardkv_desc {
+  int32_t batch;        /* B >= 1 */
+  int32_t num_q_heads;  /* Hq, a multiple of Hkv */
+  int32_t num_kv_heads; /* Hkv >= 1; G = Hq / Hkv must be 1, 2, 4 or 8 */
+  int32_t head_dim;     /* d: 64 or 128 */
+  int32_t dtype;        /* HARDKV_F32 or HARDKV_BF16 for q, K, V and the compacted tier */
+  int32_t dense_window; /* W >= 0: the last W tokens form the dense tier */
+  int32_t chunk;        /* C >= 1: condensed chunk j pools evicted positions [jC, (j+1)C) */
+  int32_t block_size;   /* 0: contiguous cache; > 0: paged cache with this many tokens per block */
+  int32_t ctx_cap;      /* largest allowed T_b; contiguous: token stride of the cache per (b, h) */
+  int32_t max_blocks;   /* paged: entries per block-table row; ctx_cap <= max_blocks * block_size */
+  int32_t sparse_cap;   /* sparse slots per (b, h); >= max(ctx_cap - W, 0) */
+  int32_t chunk_cap;    /* chunk slots per (b, h); >= ceil(max(ctx_cap - W, 0) / C) */
+  float top_p;          /* p in (0, 1]; p = 1 keeps every aged token */
+} hardkv_desc;
+
+/* The KV cache of one layer.
+ *   contiguous: k, v = [B][Hkv][ctx_cap][d]
+ *   paged:      k, v = [num_blocks][Hkv][block_size][d]; token t of sequence b,
+ *               head h is row (t % block_size) of block block_table[b][t / block_size]
+ *   ctx_len:    [B] int32, 1 <= T_b <= ctx_cap (clamped on the device). */
+typedef struct hardkv_cache {
+  const void* k;
+  const void* v;
+  const int32_t* block_table; /* [B][max_blocks]; NULL for a contiguous cache */
+  const int32_t* ctx_len;
+} hardkv_cache;
+
+/* Sparse (rewritten) and condensed tiers.
+ *   k, v:   [B][Hkv][sparse_cap][d] in the cache dtype; slots 0..count-1 hold the
+ *           selected tokens as bit copies, ascending position; later slots unspecified
+ *   pos:    [B][Hkv][sparse_cap] int32 original positions of those slots
+ *   count:  [B][Hkv] int32 selected tokens (the head's budget k_{b,h})
+ *   ksum, vsum: [B][Hkv][chunk_cap][d] float32 sums of the evicted keys / values
+ *   ccount: [B][Hkv][chunk_cap] int32 evicted tokens per chunk (0 = empty chunk)
+ * Single-step calls write chunk slots [0, ceil(A_b / C)); the rest is unspecified. */
+typedef struct hardkv_tiers {
+  void* k;
+  void* v;
+  int32_t* pos;
+  int32_t* count;
+  float* ksum;
+  float* vsum;
+  int32_t* ccount;
+} hardkv_tiers;
+
+/* Persistent state of the multi-step lifecycle (one layer).
+ *   ring_k, ring_v: [B][Hkv][W][d] dense window; position t lives in slot t % W
+ *   tiers: sparse pool (positions ascending, `count` residents) and running chunk sums
+ *   seq_len: [B] int32 tokens seen so far; must be >= W; advanced by one per step */
+typedef struct hardkv_state {
+  void* ring_k;
+  void* ring_v;
+  hardkv_tiers tiers;
+  int32_t* seq_len;
+} hardkv_state;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int hardkv_version(void);
+
+/* Static text for a return code. */
+const char* hardkv_strerror(int code);
+
+/* Checks a descriptor.  Returns HARDKV_OK or the error any entry point would
+ * return for it. */
+int hardkv_validate(const hardkv_desc* desc);
+
+/* Bytes of device workspace every entry point below needs for `desc`
+ * (one buffer serves all of them).  0 if the descriptor is invalid.
+ * The workspace is scratch: its contents are not preserved between calls,
+ * and two calls that run at the same time need separate workspaces. */
+size_t hardkv_workspace_size(const hardkv_desc* desc);
+
+/* Importance scores of the aged tokens [0, A_b) of every (b, h)
+ * (section 2.B, Goal: max-pooled logits and other similarity metrics).
+ *   q:      [B][Hq][d] in desc->dtype
+ *   metric: [Hkv] int8 HARDKV_METRIC_*, NULL = all QK
+ *   logit:  [B][Hkv][sparse_cap] float32, logit[t] = fl32(max_g q_g.k_t / sqrt(d)),
+ *           the dot product accumulated in float64
+ *   l2:     [B][Hkv][sparse_cap] float32 key norms, written for HARDKV_METRIC_L2 heads
+ *           only; must be non-NULL whenever metric is non-NULL
+ * Entries at t >= A_b are unspecified. */
+int hardkv_score(const hardkv_desc* desc, const void* q, const hardkv_cache* cache,
+                 const int8_t* metric, float* logit, float* l2, void* ws, size_t ws_bytes,
+                 hardkv_stream_t stream);
+
+/* Logits Calibration (section 2.B, Mechanism; section 3, second contribution).
+ * For each (b, h) maps the aged tokens' metric x into calibrated values
+ *   c_t = fl32((x_t - shift) * scale)
+ * QK heads: x = logit, shift 0, scale 1 (the raw attention distribution).
+ * L2 heads: x = l2, shift = mean(l2), scale = std(logit) / std(l2) (population
+ * moments over the aged tokens; 0 if either spread is 0).
+ *   stats: [B][Hkv][4] float64 {shift, scale, m = max c, Z = sum exp(c - m)}. */
+int hardkv_calibrate(const hardkv_desc* desc, const int32_t* ctx_len, const int8_t* metric,
+                     const float* logit, const float* l2, double* stats, void* ws,
+                     size_t ws_bytes, hardkv_stream_t stream);
+
+/* Calibrated Top-p selection (section 2.A, Tier 2; section 2.B, Outcome).
+ * Ranks the aged tokens by c (highest first, equal values lower position first)
+ * and keeps the smallest prefix whose mass sum exp(c - m) reaches top_p * Z.
+ * Masses are accumulated exactly in 2^-47 fixed point.
+ *   mask:  [B][Hkv][sparse_cap] uint8, 1 = kept, for t < A_b (later bytes unspecified)
+ *   count: [B][Hkv] int32 kept tokens. */
+int hardkv_topp_select(const hardkv_desc* desc, const int32_t* ctx_len, const int8_t* metric,
+                       const float* logit, const float* l2, const double* stats,
+                       uint8_t* mask, int32_t* count, void* ws, size_t ws_bytes,
+                       hardkv_stream_t stream);
+
+/* Index Regularization (section 2.C: Rewrite Cache, Flatten Index to the
+ * maximum length) and the condensed tier (section 2.A, Tier 3).  For every
+ * (b, h): the tokens t < A_b with mask[t] = 1 are copied bit for bit into
+ * out->k / out->v slots 0..count-1 in ascending position order with their
+ * positions; every other aged token is added to the float32 sums of chunk
+ * t / C.  Writes every field of *out (count = number of mask bytes set).
+ * The tiers must not alias the cache. */
+int hardkv_compact(const hardkv_desc* desc, const hardkv_cache* cache, const uint8_t* mask,
+                   const hardkv_tiers* out, void* ws, size_t ws_bytes,
+                   hardkv_stream_t stream);
+
+/* Decode attention over the three tiers (abstract; section 3, third
+ * contribution).  For every query head g of (b, h = g / G): softmax over
+ *   dense tokens [A_b, T_b) of the cache      logit q.k / sqrt(d), value v
+ *   sparse slots 0..count-1 of the tiers      logit q.k / sqrt(d), value v
+ *   chunks j < ceil(A_b / C) with n = ccount > 0: logit q.(ksum / n) / sqrt(d) + ln n,
+ *                                             value vsum / n
+ *   out: [B][Hq][d] float32.  Split-K partials live in the workspace. */
+int hardkv_decode_attn(const hardkv_desc* desc, const void* q, const hardkv_cache* cache,
+                       const hardkv_tiers* tiers, float* out, void* ws, size_t ws_bytes,
+                       hardkv_stream_t stream);
+
+/* One complete decode step (section 2.A four-step pipeline for a single
+ * step): score -> calibrate -> top-p -> compact -> attention, on one stream,
+ * with intermediate scores, statistics and masks in the workspace.
+ *   metric: as in hardkv_score; tiers: written as by hardkv_compact;
+ *   out: [B][Hq][d] float32 attention output. */
+int hardkv_step(const hardkv_desc* desc, const void* q, const hardkv_cache* cache,
+                const int8_t* metric, const hardkv_tiers* tiers, float* out, void* ws,
+                size_t ws_bytes, hardkv_stream_t stream);
+
+/* One decode step of the multi-step token lifecycle on persistent tiers
+ * (section 2.A: tokens move dense -> sparse -> condensed as they age; the
+ * sparse tier is re-selected every step).  For every (b, h), with P = seq_len[b]:
+ *   1. append: the token in ring slot P % W (position P - W) moves to the end of
+ *      the sparse pool; k_new / v_new ([B][Hkv][d]) take its ring slot;
+ *   2. score, calibrate and top-p over the pool residents;
+ *   3. the kept residents are compacted in place (stable, positions ascending);
+ *   4. every dropped resident is added to the running sums of chunk pos / C;
+ *   5. attention over the ring, the pool and the chunks -> out [B][Hq][d] f32;
+ *   6. seq_len[b] += 1.
+ * desc->block_size must be 0; ctx_cap bounds P + 1 and sizes the pool
+ * (sparse_cap >= ctx_cap - W) and the chunks (chunk_cap >= ceil((ctx_cap - W) / C)). */
+int hardkv_step_inplace(const hardkv_desc* desc, const void* q, const void* k_new,
+                        const void* v_new, const int8_t* metric, const hardkv_state* state,
+                        float* out, void* ws, size_t ws_bytes, hardkv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HARDKV_H */

@@ -1,0 +1,131 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point include/hardkv.h declares, and rejects bad arguments with the
+documented codes before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_kv_cache_head_amd import hardkv as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hardkv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hardkv_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = H.load()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(H.EXPORTS)
+
+
+def test_version_and_strerror():
+    lib = H.load()
+    assert lib.hardkv_version() == 10000
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.hardkv_strerror(code)
+    assert lib.hardkv_strerror(99) == b"unknown error"
+
+
+def base_desc(**kw):
+    d = dict(B=2, Hq=8, Hkv=2, d=128, dtype=H.BF16, W=64, C=32, top_p=0.9, ctx_cap=1000)
+    d.update(kw)
+    return H.make_desc(d["B"], d["Hq"], d["Hkv"], d["d"], d["dtype"], d["W"], d["C"], d["top_p"],
+                       d["ctx_cap"], d.get("block_size", 0), d.get("max_blocks", 0),
+                       d.get("sparse_cap"), d.get("chunk_cap"))
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, H.OK),
+    (dict(Hq=7), H.ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=2), H.ERR_UNSUPPORTED),      # G = 3
+    (dict(Hq=32, Hkv=2), H.ERR_UNSUPPORTED),     # G = 16
+    (dict(d=96), H.ERR_UNSUPPORTED),
+    (dict(dtype=7), H.ERR_UNSUPPORTED),
+    (dict(W=-1), H.ERR_INVALID_ARG),
+    (dict(C=0), H.ERR_INVALID_ARG),
+    (dict(top_p=0.0), H.ERR_INVALID_ARG),
+    (dict(top_p=1.5), H.ERR_INVALID_ARG),
+    (dict(top_p=float("nan")), H.ERR_INVALID_ARG),
+    (dict(top_p=1.0), H.OK),
+    (dict(sparse_cap=935), H.ERR_CAPACITY),
+    (dict(chunk_cap=29), H.ERR_CAPACITY),
+    (dict(chunk_cap=30), H.OK),
+    (dict(block_size=16, max_blocks=63), H.OK),
+    (dict(block_size=16, max_blocks=62), H.ERR_INVALID_ARG),
+    (dict(block_size=12, max_blocks=100), H.ERR_UNSUPPORTED),
+    (dict(B=0), H.ERR_INVALID_ARG),
+    (dict(ctx_cap=0), H.ERR_INVALID_ARG),
+    (dict(W=2000), H.OK),                          # everything dense
+])
+def test_validate_codes(kw, code):
+    assert H.validate(base_desc(**kw)) == code
+
+
+def test_workspace_size():
+    d = base_desc()
+    n = H.workspace_size(d)
+    assert n > 0 and n % 256 == 0
+    assert H.workspace_size(base_desc(Hq=7)) == 0
+    big = base_desc(ctx_cap=4000)
+    assert H.workspace_size(big) > n
+
+
+def _call_all(desc, ws_bytes, null_q=False):
+    """Calls every entry point with fake (never dereferenced) device
+    pointers; each must fail validation before any launch."""
+    lib = H.load()
+    fake = ctypes.c_void_p(0x1000)
+    cache = H.Cache(fake, fake, None, fake)
+    tiers = H.TiersC(*([fake] * 7))
+    state = H.StateC(fake, fake, tiers, fake)
+    q = None if null_q else fake
+    d = ctypes.byref(desc)
+    st = ctypes.c_void_p(0)
+    return [
+        lib.hardkv_score(d, q, ctypes.byref(cache), None, fake, None, fake, ws_bytes, st),
+        lib.hardkv_calibrate(d, fake, None, fake, None, fake, fake, ws_bytes, st),
+        lib.hardkv_topp_select(d, fake, None, fake, None, fake, fake, fake, fake, ws_bytes, st),
+        lib.hardkv_compact(d, ctypes.byref(cache), fake, ctypes.byref(tiers), fake, ws_bytes, st),
+        lib.hardkv_decode_attn(d, q, ctypes.byref(cache), ctypes.byref(tiers), fake, fake,
+                               ws_bytes, st),
+        lib.hardkv_step(d, q, ctypes.byref(cache), None, ctypes.byref(tiers), fake, fake,
+                        ws_bytes, st),
+        lib.hardkv_step_inplace(d, q, fake, fake, None, ctypes.byref(state), fake, fake,
+                                ws_bytes, st),
+    ]
+
+
+def test_errors_before_launch():
+    desc = base_desc()
+    need = H.workspace_size(desc)
+    assert _call_all(desc, need - 1) == [H.ERR_WORKSPACE] * 7
+    assert _call_all(base_desc(d=96), need) == [H.ERR_UNSUPPORTED] * 7
+    assert _call_all(base_desc(top_p=2.0), need) == [H.ERR_INVALID_ARG] * 7
+    assert _call_all(base_desc(sparse_cap=10), need) == [H.ERR_CAPACITY] * 7
+    rc = _call_all(desc, need, null_q=True)
+    assert rc[0] == rc[4] == rc[5] == rc[6] == H.ERR_INVALID_ARG
+    # the lifecycle needs a contiguous layout and a window
+    paged = base_desc(block_size=16, max_blocks=63)
+    assert _call_all(paged, H.workspace_size(paged))[6] == H.ERR_INVALID_ARG
+    lib = H.load()
+    assert lib.hardkv_validate(None) == H.ERR_INVALID_ARG
+    assert lib.hardkv_workspace_size(None) == 0
+
+
+def test_l2_buffer_required_with_metric():
+    desc = base_desc()
+    lib = H.load()
+    fake = ctypes.c_void_p(0x1000)
+    cache = H.Cache(fake, fake, None, fake)
+    rc = lib.hardkv_score(ctypes.byref(desc), fake, ctypes.byref(cache), fake, fake, None, fake,
+                          H.workspace_size(desc), ctypes.c_void_p(0))
+    assert rc == H.ERR_INVALID_ARG

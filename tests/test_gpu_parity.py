@@ -1,0 +1,222 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases check every (b, h) and every stage; the full-size workloads
+check sampled heads against the oracle and cheap invariants on all heads.
+Comparison rules: tests/parity.py.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decode_kv_cache_head_amd import hardkv as H
+from decode_kv_cache_head_amd import synth as S
+
+from parity import (check_all_heads_invariants, check_case, desc_for, run_stages, run_step)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def small(name, **kw):
+    base = dict(name=name, B=3, Hq=8, Hkv=2, d=128, T=(2100, 777, 40), dtype=S.DT_BF16, W=64,
+                C=64, p=0.9)
+    base.update(kw)
+    return S.Workload(**base)
+
+
+def test_tiny_workload(gpu):
+    w = S.workload("tiny")
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    say("tiny", w)
+    g = run_stages(case, desc)
+    rep = check_case(case, g, w.p)
+    say(rep)
+    assert rep["heads"] == 2 and rep["selected"] > 0
+    # the planted heavy keys are kept
+    for h in range(w.Hkv):
+        kept = set(g["tiers"].pos[0, h, :int(g["tiers"].count[0, h])].tolist())
+        assert set(case.extra[("planted", 0, h)]) <= kept
+
+
+GRID = [
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.9),
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.5, block_size=16),
+    dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=8, C=32, p=0.95),
+    dict(dtype=S.DT_F32, d=128, Hq=4, Hkv=2, C=7, p=0.8),
+    dict(dtype=S.DT_F32, d=64, Hq=16, Hkv=2, C=100, p=0.99, block_size=32),
+    dict(dtype=S.DT_BF16, d=128, Hq=16, Hkv=2, C=1, p=0.7, metric=(S.METRIC_QK, S.METRIC_L2)),
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=4, C=64, p=0.9,
+         metric=(S.METRIC_L2, S.METRIC_QK, S.METRIC_L2, S.METRIC_L2), block_size=16),
+]
+
+
+@pytest.mark.parametrize("i", range(len(GRID)))
+def test_small_grid_all_heads_all_stages(gpu, i):
+    w = small(f"grid{i}", **GRID[i])
+    say("grid", i, w)
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_stages(case, desc)
+    rep = check_case(case, g, w.p)
+    say(rep)
+    check_all_heads_invariants(case, desc, g)
+    # the fused step gives the same bits as the stage-by-stage calls
+    s = run_step(case, desc)
+    for f in ("k", "v", "pos", "count"):
+        a, b = getattr(s["tiers"], f), getattr(g["tiers"], f)
+        if f in ("k", "v", "pos"):
+            for bb in range(w.B):
+                for hh in range(w.Hkv):
+                    n = int(g["tiers"].count[bb, hh])
+                    assert torch.equal(a[bb, hh, :n], b[bb, hh, :n])
+        else:
+            assert torch.equal(a, b)
+    assert torch.equal(s["out"], g["out"])
+
+
+def test_p_one_is_full_attention(gpu):
+    w = small("pone", p=1.0, T=(1500, 300, 65))
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_step(case, desc)
+    for b in range(w.B):
+        assert torch.equal(g["tiers"].count[b].long(),
+                           torch.full((w.Hkv,), max(w.T[b] - w.W, 0), device=gpu))
+        for h in range(w.Hkv):
+            G = w.G
+            q = case.q[b, h * G:(h + 1) * G].double().cpu()
+            K = S.head_rows(case, b, h, "k").double().cpu()
+            V = S.head_rows(case, b, h, "v").double().cpu()
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[None, :, None], K[None, None].expand(1, G, -1, -1).contiguous(),
+                V[None, None].expand(1, G, -1, -1).contiguous())[0, :, 0]
+            o = g["out"][b, h * G:(h + 1) * G].double().cpu()
+            err = ((o - ref).abs().amax(1) / ref.abs().amax(1)).max().item()
+            assert err <= 2e-3, err
+
+
+def test_edge_cases(gpu):
+    # every sequence shorter than the window, a single-token context, and a
+    # context exactly one token past the window
+    w = small("edge", T=(1, 64, 65, 63), B=4, p=0.6)
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_stages(case, desc)
+    rep = check_case(case, g, w.p)
+    assert rep["candidates"] == 2  # only the 65-token sequence ages one token (x2 heads)
+    # a window of zero: everything is a candidate
+    w0 = small("w0", T=(300, 129), B=2, W=0, C=16, p=0.9)
+    c0 = S.make_case(w0, gpu)
+    check_case(c0, run_stages(c0, desc_for(c0)), w0.p)
+
+
+def test_capacity_larger_than_needed(gpu):
+    w = small("cap", T=(900, 500), B=2)
+    case = S.make_case(w, gpu)
+    desc = desc_for(case, sparse_cap=2000, chunk_cap=64)
+    g = run_stages(case, desc)
+    check_case(case, g, w.p)
+
+
+def test_determinism(gpu):
+    w = small("det", T=(3000, 2500, 1999), metric=(S.METRIC_QK, S.METRIC_L2))
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    a = run_stages(case, desc)
+    b = run_stages(case, desc)
+    for f in ("logit", "stats", "mask", "count"):
+        x, y = a[f], b[f]
+        if f == "mask":
+            for bb in range(w.B):
+                A = max(w.T[bb] - w.W, 0)
+                assert torch.equal(x[bb, :, :A], y[bb, :, :A])
+        elif f == "logit":
+            for bb in range(w.B):
+                A = max(w.T[bb] - w.W, 0)
+                assert torch.equal(x[bb, :, :A], y[bb, :, :A])
+        else:
+            assert torch.equal(x, y)
+    for f in ("ksum", "vsum", "ccount"):
+        for bb in range(w.B):
+            nch = -(-max(w.T[bb] - w.W, 0) // w.C)
+            assert torch.equal(getattr(a["tiers"], f)[bb, :, :nch], getattr(b["tiers"], f)[bb, :, :nch])
+    assert torch.equal(a["out"], b["out"])
+
+
+def test_budget_adapts_per_head_qwen8b_b1_16k(gpu):
+    """Single-layer Qwen3-8B shape, batch 1, 16k context, per-head query
+    temperature in [0.5, 4]: every head against the oracle."""
+    w = S.workload("qwen8b_b1_16k")
+    say(w)
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_stages(case, desc)
+    rep = check_case(case, g, w.p)
+    say(rep)
+    budgets = g["tiers"].count[0].float() / (w.T[0] - w.W)
+    assert budgets.max() - budgets.min() > 0.15   # head-adaptive
+
+
+def _sample_heads(w, n, seed):
+    rng = np.random.default_rng(seed)
+    heads = {(0, 0), (w.B - 1, w.Hkv - 1)}
+    while len(heads) < n:
+        heads.add((int(rng.integers(w.B)), int(rng.integers(w.Hkv))))
+    return sorted(heads)
+
+
+def test_headline_b32_16k_paged(gpu):
+    """The headline workload at full size: sampled heads against the oracle
+    through hardkv_step, invariants on every head."""
+    w = S.workload("qwen8b_b32_16k_paged")
+    say(w.name)
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_step(case, desc)
+    check_all_heads_invariants(case, desc, g)
+    rep = check_case(case, g, w.p, heads=_sample_heads(w, 10, 1), stages=False)
+    say(rep)
+
+
+def test_ragged_b32_paged(gpu):
+    w = S.workload("qwen8b_b32_ragged_paged")
+    say(w.name, w.T[:4])
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_stages(case, desc)
+    check_all_heads_invariants(case, desc, g)
+    rep = check_case(case, g, w.p, heads=_sample_heads(w, 8, 2))
+    say(rep)
+
+
+def test_mixed_metric_64k_p_sweep(gpu):
+    w = S.workload("qwen8b_b8_64k_mixed")
+    say(w.name)
+    case = S.make_case(w, gpu)
+    prev = None
+    heads = [(0, 0), (0, 4), (3, 1), (5, 6), (7, 0), (7, 4)]
+    for p in (0.8, 0.9, 0.99):
+        desc = desc_for(case, top_p=p)
+        g = run_stages(case, desc)
+        check_all_heads_invariants(case, desc, g)
+        rep = check_case(case, g, p, heads=heads)
+        say(p, rep)
+        A = w.T[0] - w.W
+        m = g["mask"][:, :, :A].bool()
+        if prev is not None:
+            assert not torch.any(prev & ~m)      # S(p1) is inside S(p2)
+        prev = m
+        cnt = g["tiers"].count.float() / A
+        # peaked heads keep far fewer tokens than flat heads
+        if p < 0.95:
+            assert cnt[:, 0].max() < 0.01 and cnt[:, 4].max() < 0.01
+        assert cnt[:, [0, 4]].max() < 0.5 * cnt[:, [1, 2, 3, 5, 6, 7]].min()
+        del g
