@@ -1,0 +1,181 @@
+"""GPU parity of the multi-step token lifecycle (hardkv_step_inplace):
+dense ring -> sparse pool (re-selected every step, compacted in place) ->
+condensed running chunk sums, against the oracle's lifecycle step by step.
+
+Per step and head: pool positions equal (borderline tokens allowed, counted,
+and the oracle then re-synchronised from the GPU state, as a staged check),
+pool rows bit copies of the source tokens, chunk counts exact, chunk sums
+within 1e-5 * n * max|x|, ring contents exact, attention within 2e-3.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decode_kv_cache_head_amd import hardkv as H
+
+from parity import ATTN_TOL, borderline_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Run:
+    """Seeded lifecycle inputs and the GPU state for one layer."""
+
+    def __init__(self, dev, seed, B, Hq, Hkv, d, T0, W, C, p, steps, dtype=torch.bfloat16):
+        g = torch.Generator(device=dev).manual_seed(seed)
+        self.B, self.Hq, self.Hkv, self.d, self.T0, self.W, self.C, self.p = B, Hq, Hkv, d, T0, W, C, p
+        self.G = Hq // Hkv
+        self.dt = dtype
+        Tmax = T0 + steps
+        self.K = torch.randn((B, Hkv, T0, d), generator=g, device=dev).to(dtype)
+        self.V = torch.randn((B, Hkv, T0, d), generator=g, device=dev).to(dtype)
+        self.knew = torch.randn((steps, B, Hkv, d), generator=g, device=dev).to(dtype)
+        self.vnew = torch.randn((steps, B, Hkv, d), generator=g, device=dev).to(dtype)
+        self.q = (torch.randn((steps, B, Hq, d), generator=g, device=dev) * 1.5).to(dtype)
+        self.desc = H.make_desc(B, Hq, Hkv, d, H.BF16 if dtype == torch.bfloat16 else H.F32,
+                                W, C, p, Tmax)
+        A = T0 - W
+        tiers = H.alloc_tiers(self.desc, dev, zero=True)
+        tiers.k[:, :, :A] = self.K[:, :, :A]
+        tiers.v[:, :, :A] = self.V[:, :, :A]
+        tiers.pos[:, :, :A] = torch.arange(A, dtype=torch.int32, device=dev)
+        tiers.count.fill_(A)
+        ring_k = torch.empty((B, Hkv, W, d), dtype=dtype, device=dev)
+        ring_v = torch.empty_like(ring_k)
+        for t in range(T0 - W, T0):
+            ring_k[:, :, t % W] = self.K[:, :, t]
+            ring_v[:, :, t % W] = self.V[:, :, t]
+        self.state = H.State(ring_k, ring_v, tiers,
+                             torch.full((B,), T0, dtype=torch.int32, device=dev))
+        self.ws = H.alloc_workspace(self.desc, dev)
+        self.out = torch.empty((B, Hq, d), device=dev)
+
+    def oracle_state(self, b, h):
+        K = self.K[b, h].float().cpu().numpy()
+        V = self.V[b, h].float().cpu().numpy()
+        return O.init_state(K, V, self.T0, self.W, self.C, self.desc.chunk_cap)
+
+    def gpu_step(self, s):
+        H.step_inplace(self.desc, self.q[s], self.knew[s], self.vnew[s], None, self.state,
+                       self.out, self.ws)
+        torch.cuda.synchronize()
+
+
+def resync(st, run, b, h):
+    """Oracle state of (b, h) from the GPU tiers (staged comparison)."""
+    t = run.state.tiers
+    n = int(t.count[b, h])
+    st.pool_K = t.k[b, h, :n].float().cpu().numpy()
+    st.pool_V = t.v[b, h, :n].float().cpu().numpy()
+    st.pool_pos = t.pos[b, h, :n].cpu().numpy().astype(np.int64)
+    st.ksum = t.ksum[b, h].double().cpu().numpy()
+    st.vsum = t.vsum[b, h].double().cpu().numpy()
+    st.cnt = t.ccount[b, h].cpu().numpy().astype(np.int64)
+
+
+def check_step(run, states, s, rep):
+    t = run.state.tiers
+    G, W = run.G, run.W
+    P = run.T0 + s
+    assert torch.all(run.state.seq_len == P + 1)
+    for (b, h), st in states.items():
+        pool_before = st.pool_pos.copy()
+        q = run.q[s, b, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
+        kn = run.knew[s, b, h].float().cpu().numpy()
+        vn = run.vnew[s, b, h].float().cpu().numpy()
+        out_ref, info = O.lifecycle_step(st, q, kn, vn, run.p, O.METRIC_QK)
+        n = int(t.count[b, h])
+        pos = t.pos[b, h, :n].cpu().numpy().astype(np.int64)
+        diff = np.setxor1d(pos, st.pool_pos)
+        rep["selected"] += n
+        rep["candidates"] += info["n_candidates"]
+        if diff.size:
+            # rank the differing tokens in the oracle's own selection
+            cand_pos = np.concatenate([pool_before, [P - W]])
+            idx = np.searchsorted(cand_pos, diff)
+            ref = O.HeadResult(len(cand_pos), None, None, info["cal"], info["sel"], None, None,
+                               None, None, None, None, None, None)
+            assert borderline_tokens(ref, run.p, idx).all(), (s, b, h, diff[:8])
+            rep["borderline"] += int(diff.size)
+            resync(st, run, b, h)
+            rep["resyncs"] += 1
+        # pool rows are bit copies of the tokens at their positions
+        src_k = np.concatenate([run.K[b, h].float().cpu().numpy(),
+                                run.knew[:s + 1, b, h].float().cpu().numpy()])
+        assert np.array_equal(t.k[b, h, :n].float().cpu().numpy(), src_k[pos])
+        assert np.array_equal(t.pos[b, h, :n].cpu().numpy(), st.pool_pos)
+        cc = t.ccount[b, h].cpu().numpy()
+        assert np.array_equal(cc, st.cnt)
+        bound = 1e-5 * np.maximum(cc, 1)[:, None] * 6.0 + 1e-30
+        assert np.all(np.abs(t.ksum[b, h].double().cpu().numpy() - st.ksum) <= bound)
+        assert np.all(np.abs(t.vsum[b, h].double().cpu().numpy() - st.vsum) <= bound)
+        rk = run.state.ring_k[b, h].float().cpu().numpy()
+        assert np.array_equal(rk, st.ring_K)
+        o = run.out[b, h * G:(h + 1) * G].double().cpu().numpy()
+        if diff.size:
+            out_ref = O.attend_head(q, st.ring_K, st.ring_V, st.pool_K, st.pool_V, st.ksum,
+                                    st.vsum, st.cnt)
+        err = np.abs(o - out_ref).max(axis=1) / np.abs(out_ref).max(axis=1)
+        assert np.all(err <= ATTN_TOL), (s, b, h, err.max())
+        rep["max_attn_err"] = max(rep["max_attn_err"], float(err.max()))
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(B=2, Hq=16, Hkv=2, d=128, T0=1500, W=512, C=64, p=0.95, steps=12),
+    dict(B=3, Hq=8, Hkv=4, d=64, T0=700, W=100, C=7, p=0.8, steps=9),
+    dict(B=1, Hq=4, Hkv=4, d=128, T0=300, W=64, C=1, p=0.5, steps=6, dtype=torch.float32),
+])
+def test_lifecycle_matches_oracle(gpu, cfg):
+    steps = cfg.pop("steps")
+    run = Run(gpu, 11, steps=steps, **cfg)
+    say("lifecycle", cfg, "steps", steps)
+    states = {(b, h): run.oracle_state(b, h) for b in range(run.B) for h in range(run.Hkv)}
+    rep = dict(selected=0, candidates=0, borderline=0, resyncs=0, max_attn_err=0.0)
+    for s in range(steps):
+        run.gpu_step(s)
+        check_step(run, states, s, rep)
+    say(rep)
+    # tokens keep flowing dense -> sparse -> condensed
+    assert int(run.state.tiers.ccount.sum()) > 0
+
+
+def test_lifecycle_p_one_keeps_everything(gpu):
+    run = Run(gpu, 12, B=2, Hq=8, Hkv=2, d=128, T0=600, W=128, C=32, p=1.0, steps=5)
+    for s in range(5):
+        run.gpu_step(s)
+    assert torch.all(run.state.tiers.count == 600 - 128 + 5)
+    assert int(run.state.tiers.ccount.sum()) == 0
+
+
+def test_first_lifecycle_step_equals_single_step(gpu):
+    """Step 1 on the raw prefill equals hardkv_step on the cache that holds
+    the new token: same kept set, same compacted rows, same attention."""
+    run = Run(gpu, 13, B=2, Hq=16, Hkv=2, d=128, T0=2000, W=256, C=64, p=0.9, steps=1)
+    run.gpu_step(0)
+    T = run.T0 + 1
+    k = torch.cat([run.K, run.knew[0][:, :, None]], dim=2).contiguous()
+    v = torch.cat([run.V, run.vnew[0][:, :, None]], dim=2).contiguous()
+    ctx = torch.full((run.B,), T, dtype=torch.int32, device=gpu)
+    desc = H.make_desc(run.B, run.Hq, run.Hkv, run.d, H.BF16, run.W, run.C, run.p, T)
+    tiers = H.alloc_tiers(desc, gpu)
+    out = torch.empty_like(run.out)
+    H.step(desc, run.q[0], H.cache_struct(k, v, ctx), None, tiers, out, H.alloc_workspace(desc, gpu))
+    torch.cuda.synchronize()
+    st = run.state.tiers
+    assert torch.equal(st.count, tiers.count)
+    for b in range(run.B):
+        for h in range(run.Hkv):
+            n = int(tiers.count[b, h])
+            assert torch.equal(st.pos[b, h, :n], tiers.pos[b, h, :n])
+            assert torch.equal(st.k[b, h, :n], tiers.k[b, h, :n])
+            nch = -(-(T - run.W) // run.C)
+            assert torch.equal(st.ccount[b, h, :nch], tiers.ccount[b, h, :nch])
+    err = ((out - run.out).abs().amax(-1) / out.abs().amax(-1)).max().item()
+    assert err < 1e-5
