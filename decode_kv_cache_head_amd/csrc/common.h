@@ -9,6 +9,10 @@
 namespace hk {
 
 // ---------------------------------------------------------------- elements --
+// 16-byte piece as a native vector: loads and stores stay single
+// instructions and register arrays of pieces are promoted to VGPRs.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
 struct bf16_t {
   uint16_t bits;
 };
@@ -18,7 +22,7 @@ struct Elt;
 template <>
 struct Elt<float> {
   static constexpr int kPer16 = 4;  // elements per 16-byte piece
-  __device__ static inline void unpack(const uint4& v, float (&f)[4]) {
+  __device__ static inline void unpack(const v4u& v, float (&f)[4]) {
     f[0] = __uint_as_float(v.x);
     f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z);
@@ -30,7 +34,7 @@ template <>
 struct Elt<bf16_t> {
   static constexpr int kPer16 = 8;
   // bf16 -> f32 is exact: the 16 bits are the high half of the f32 pattern.
-  __device__ static inline void unpack(const uint4& v, float (&f)[8]) {
+  __device__ static inline void unpack(const v4u& v, float (&f)[8]) {
     f[0] = __uint_as_float(v.x << 16);
     f[1] = __uint_as_float(v.x & 0xffff0000u);
     f[2] = __uint_as_float(v.y << 16);
@@ -57,12 +61,16 @@ struct Rows {
   int32_t lbs;  // log2(block size) when paged
   int32_t max_blocks;
   int32_t row_bytes;
+  // PAGED is a compile-time property of the launch, so the unrolled loads of
+  // a tile stay in one basic block.
+  template <bool PAGED>
   __device__ inline const char* row(int b, int h, int t) const {
-    if (table) {
+    if constexpr (PAGED) {
       const int blk = table[(int64_t)b * max_blocks + (t >> lbs)];
       return base + ((((int64_t)blk * hkv + h) << lbs) + (t & ((1 << lbs) - 1))) * row_bytes;
+    } else {
+      return base + (((int64_t)b * hkv + h) * region + t) * row_bytes;
     }
-    return base + (((int64_t)b * hkv + h) * region + t) * row_bytes;
   }
 };
 

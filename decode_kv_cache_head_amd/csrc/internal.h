@@ -26,6 +26,31 @@ namespace hk {
     if ((DT) == HARDKV_F32) HK_DISPATCH_D(float, D, G, FN, __VA_ARGS__); \
     else HK_DISPATCH_D(bf16_t, D, G, FN, __VA_ARGS__);                  \
   } while (0)
+// ... and on the cache layout (paged or contiguous rows) as a fourth parameter.
+#define HK_DISPATCH_GP(T, D, G, P, FN, ...)                  \
+  do {                                                       \
+    switch (G) {                                             \
+      case 1: FN<T, D, 1, P>(__VA_ARGS__); break;            \
+      case 2: FN<T, D, 2, P>(__VA_ARGS__); break;            \
+      case 4: FN<T, D, 4, P>(__VA_ARGS__); break;            \
+      default: FN<T, D, 8, P>(__VA_ARGS__); break;           \
+    }                                                        \
+  } while (0)
+#define HK_DISPATCH_DP(T, D, G, P, FN, ...)                              \
+  do {                                                                   \
+    if ((D) == 64) HK_DISPATCH_GP(T, 64, G, P, FN, __VA_ARGS__);         \
+    else HK_DISPATCH_GP(T, 128, G, P, FN, __VA_ARGS__);                  \
+  } while (0)
+#define HK_DISPATCH_TP(T, D, G, PAGED, FN, ...)                            \
+  do {                                                                     \
+    if (PAGED) HK_DISPATCH_DP(T, D, G, true, FN, __VA_ARGS__);             \
+    else HK_DISPATCH_DP(T, D, G, false, FN, __VA_ARGS__);                  \
+  } while (0)
+#define HK_DISPATCH_P(DT, D, G, PAGED, FN, ...)                                   \
+  do {                                                                          \
+    if ((DT) == HARDKV_F32) HK_DISPATCH_TP(float, D, G, PAGED, FN, __VA_ARGS__); \
+    else HK_DISPATCH_TP(bf16_t, D, G, PAGED, FN, __VA_ARGS__);                  \
+  } while (0)
 
 struct ScoreArgs {
   int dtype, D, G, B, hq;

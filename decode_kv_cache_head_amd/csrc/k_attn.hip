@@ -54,97 +54,129 @@ __device__ inline TileCounts tile_counts(const AttnArgs& a, int b, int h) {
   return t;
 }
 
-// One wave, up to 64 entries starting at row r0 of `kr`/`vr` (rows r0 + i
-// map to row index r0 + i + roff of the source).  CHUNK: float32 sums with
-// counts.  Writes the wave's max m, sum l and numerator o (lanes 0..LPR-1
-// hold the full numerator, EPL elements each).
-template <typename E, int D, int G, typename QT, bool CHUNK>
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Takes the word by value: bit-casting an ext-vector element in place
+// (__builtin_bit_cast(T, v.y)) is compiled as a cast of element 0.
+__device__ __forceinline__ bf16x2_t as_bf2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+// q.k partial over one lane's 16-byte piece.  bf16 rows with bf16 queries use
+// the packed dot (v_dot2c_f32_bf16, products exact, float32 accumulation);
+// float rows use float FMAs.
+template <typename E, typename QT, int EPL>
+struct QPiece {
+  float f[EPL];
+  __device__ inline void load(const QT* q) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) f[e] = Elt<QT>::load1(q + e);
+  }
+  __device__ inline float dot(const v4u& raw) const {
+    float k[EPL];
+    Elt<E>::unpack(raw, k);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s = fmaf(f[e], k[e], s);
+    return s;
+  }
+};
+template <>
+struct QPiece<bf16_t, bf16_t, 8> {
+  uint32_t w[4];
+  __device__ inline void load(const bf16_t* q) {
+    const v4u v = *(const v4u*)q;
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+    w[3] = v.w;
+  }
+  __device__ inline float dot(const v4u& raw) const {
+    float s = 0.f;
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[0]), as_bf2(raw.x), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[1]), as_bf2(raw.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[2]), as_bf2(raw.z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[3]), as_bf2(raw.w), s, false);
+    return s;
+  }
+};
+
+// One wave, up to 64 entries starting at row r0 of `kr`/`vr`, in rounds of
+// 8 iterations x RPI rows.  Each round issues the K and the V loads of all
+// its rows first, then scores, then rescales the running (m, l, o) to the
+// new maximum and accumulates p * v.  CHUNK: float32 sums with counts.
+// Lanes 0..LPR-1 end with the full numerator (EPL elements each).
+template <typename E, int D, int G, typename QT, bool CHUNK, bool P>
 __device__ inline void wave_attn(const QT* __restrict__ qg, const Rows& kr, const Rows& vr, int b,
                                  int h, int r0, int wn, const int32_t* __restrict__ cc, float scale,
-                                 float* s_sc, float (&m)[G], float (&l)[G],
-                                 float (&o)[G][Lay<E, D>::EPL]) {
+                                 float (&m)[G], float (&l)[G], float (&o)[G][Lay<E, D>::EPL]) {
   using L = Lay<E, D>;
-  constexpr int LPR = L::LPR, EPL = L::EPL, RPI = L::RPI, IT = L::IT;
+  constexpr int LPR = L::LPR, EPL = L::EPL, RPI = L::RPI;
+  constexpr int IT = 8;
+  constexpr int RR = IT * RPI;  // rows per round
   const int lane = threadIdx.x & 63;
   const int grp = lane / LPR, piece = lane % LPR;
-  float qf[G][EPL];
+  QPiece<E, QT, EPL> qp[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[g][e] = Elt<QT>::load1(qg + g * D + piece * EPL + e);
-
-  uint4 kb[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int r = it * RPI + grp;
-    kb[it] = make_uint4(0, 0, 0, 0);
-    if (r < wn) kb[it] = *(const uint4*)(kr.row(b, h, r0 + r) + piece * 16);
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) m[g] = -INFINITY;
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int r = it * RPI + grp;
-    float f[EPL];
-    Elt<E>::unpack(kb[it], f);
-    float dot[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s = fmaf(qf[g][e], f[e], s);
-      dot[g] = group_sum<LPR>(s);
-    }
-    bool valid = r < wn;
-    float bias = 0.f, inv = 1.f;
-    if (CHUNK) {
-      const int cnt = valid ? cc[r0 + r] : 0;
-      valid = valid && cnt > 0;
-      inv = valid ? 1.f / (float)cnt : 0.f;
-      bias = valid ? __logf((float)cnt) : 0.f;
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float sc = valid ? dot[g] * inv * scale + bias : -INFINITY;
-      m[g] = fmaxf(m[g], sc);
-      if (piece == 0) s_sc[r * G + g] = sc;
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) m[g] = across_groups_max<LPR>(m[g]);
-
-  uint4 vb[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int r = it * RPI + grp;
-    vb[it] = make_uint4(0, 0, 0, 0);
-    if (r < wn) vb[it] = *(const uint4*)(vr.row(b, h, r0 + r) + piece * 16);
-  }
+  for (int g = 0; g < G; ++g) qp[g].load(qg + g * D + piece * EPL);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
     l[g] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
   }
-  __builtin_amdgcn_wave_barrier();
+  for (int base = 0; base < wn; base += RR) {
+    v4u kb[IT], vb[IT];
+    int cnt[IT];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int r = it * RPI + grp;
-    float f[EPL];
-    Elt<E>::unpack(vb[it], f);
-    float inv = 1.f;
-    if (CHUNK) {
-      const int cnt = r < wn ? cc[r0 + r] : 0;
-      inv = cnt > 0 ? 1.f / (float)cnt : 0.f;
+    for (int it = 0; it < IT; ++it) {
+      const int r = min(base + it * RPI + grp, wn - 1);  // in bounds; masked below
+      kb[it] = *(const v4u*)(kr.template row<P>(b, h, r0 + r) + piece * 16);
+      vb[it] = *(const v4u*)(vr.template row<P>(b, h, r0 + r) + piece * 16);
+      if (CHUNK) cnt[it] = cc[r0 + r];
+    }
+    float s[IT][G];
+    float mr[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) mr[g] = -INFINITY;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const bool valid = base + it * RPI + grp < wn && (!CHUNK || cnt[it] > 0);
+      float inv = 1.f, bias = 0.f;
+      if (CHUNK) {
+        inv = valid ? 1.f / (float)cnt[it] : 0.f;
+        bias = valid ? __logf((float)cnt[it]) : 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float dot = group_sum<LPR>(qp[g].dot(kb[it]));
+        s[it][g] = valid ? dot * inv * scale + bias : -INFINITY;
+        mr[g] = fmaxf(mr[g], s[it][g]);
+      }
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float sc = s_sc[r * G + g];
-      const float p = (r < wn && sc != -INFINITY) ? __expf(sc - m[g]) : 0.f;
-      l[g] += p;
-      const float pv = CHUNK ? p * inv : p;
+      mr[g] = across_groups_max<LPR>(mr[g]);
+      const float mn = fmaxf(m[g], mr[g]);
+      const float alpha = (m[g] == -INFINITY) ? 0.f : __expf(m[g] - mn);
+      l[g] *= alpha;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(pv, f[e], o[g][e]);
+      for (int e = 0; e < EPL; ++e) o[g][e] *= alpha;
+      m[g] = mn;
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      float f[EPL];
+      Elt<E>::unpack(vb[it], f);
+      float inv = 1.f;
+      if (CHUNK) inv = cnt[it] > 0 ? 1.f / (float)cnt[it] : 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = s[it][g] == -INFINITY ? 0.f : __expf(s[it][g] - m[g]);
+        l[g] += p;
+        const float pv = CHUNK ? p * inv : p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(pv, f[e], o[g][e]);
+      }
     }
   }
 #pragma unroll
@@ -155,17 +187,17 @@ __device__ inline void wave_attn(const QT* __restrict__ qg, const Rows& kr, cons
   }
 }
 
-template <typename E, int D, int G, typename QT, bool CHUNK>
+template <typename E, int D, int G, typename QT, bool CHUNK, bool P>
 __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr, const Rows& vr,
-                                 int b, int h, int r0, int nrows, const int32_t* cc, float* s_sc,
-                                 float* s_m, float* s_l, float* s_o, float* part_out) {
+                                 int b, int h, int r0, int nrows, const int32_t* cc, float* s_m,
+                                 float* s_l, float* s_o, float* part_out) {
   using L = Lay<E, D>;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int wn = nrows - w * 64;
   wn = wn < 0 ? 0 : (wn > 64 ? 64 : wn);
   float m[G], l[G], o[G][L::EPL];
-  wave_attn<E, D, G, QT, CHUNK>(qg, kr, vr, b, h, r0 + w * 64, wn, cc, (float)a.scale,
-                                s_sc + w * 64 * G, m, l, o);
+  wave_attn<E, D, G, QT, CHUNK, P>(qg, kr, vr, b, h, r0 + w * 64, wn, cc, (float)a.scale, m, l,
+                                o);
   if (lane < L::LPR) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -206,9 +238,8 @@ __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr
   }
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool P>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-  __shared__ float s_sc[kAttnTile * G];
   __shared__ float s_m[4 * G], s_l[4 * G];
   __shared__ float s_o[4 * G * D];
   const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -222,19 +253,19 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     T_ = T_ < 0 ? 0 : (T_ > a.ctx_cap ? a.ctx_cap : T_);
     const int roff = a.ring ? 0 : (T_ > a.W ? T_ - a.W : 0);
     const int r0 = x * kAttnTile;
-    tile_attn<T, D, G, T, false>(a, qg, a.dk, a.dv, b, h, roff + r0,
-                                 min(kAttnTile, tc.nd - r0), nullptr, s_sc, s_m, s_l, s_o,
+    tile_attn<T, D, G, T, false, P>(a, qg, a.dk, a.dv, b, h, roff + r0,
+                                 min(kAttnTile, tc.nd - r0), nullptr, s_m, s_l, s_o,
                                  part_out);
   } else if (x < tc.ntd + tc.nts) {
     const int r0 = (x - tc.ntd) * kAttnTile;
-    tile_attn<T, D, G, T, false>(a, qg, a.sk, a.sv, b, h, r0, min(kAttnTile, tc.ns - r0),
-                                 nullptr, s_sc, s_m, s_l, s_o, part_out);
+    tile_attn<T, D, G, T, false, false>(a, qg, a.sk, a.sv, b, h, r0, min(kAttnTile, tc.ns - r0),
+                                 nullptr, s_m, s_l, s_o, part_out);
   } else {
     const int r0 = (x - tc.ntd - tc.nts) * kAttnTile;
     Rows ck{(const char*)a.ksum, nullptr, a.chunk_cap, a.hkv, 0, 0, D * 4};
     Rows cv{(const char*)a.vsum, nullptr, a.chunk_cap, a.hkv, 0, 0, D * 4};
-    tile_attn<float, D, G, T, true>(a, qg, ck, cv, b, h, r0, min(kAttnTile, tc.nc - r0),
-                                    a.ccount + bh * a.chunk_cap, s_sc, s_m, s_l, s_o, part_out);
+    tile_attn<float, D, G, T, true, false>(a, qg, ck, cv, b, h, r0, min(kAttnTile, tc.nc - r0),
+                                    a.ccount + bh * a.chunk_cap, s_m, s_l, s_o, part_out);
   }
 }
 
@@ -251,17 +282,30 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   float M = -INFINITY, S = 0.f, O[PE];
 #pragma unroll
   for (int e = 0; e < PE; ++e) O[e] = 0.f;
-  for (int x = 0; x < nt; ++x) {
-    const float* p = a.part + ((bh * a.max_tiles + x) * G + g) * (D + 2);
-    const float mx = p[0];
-    if (mx == -INFINITY) continue;
-    const float nm = fmaxf(M, mx);
-    const float fa = M == -INFINITY ? 0.f : __expf(M - nm);
-    const float fb = __expf(mx - nm);
-    S = S * fa + p[1] * fb;
+  constexpr int U = 8;  // partials fetched per round, loads issued together
+  for (int x0 = 0; x0 < nt; x0 += U) {
+    float pm[U], pl[U], po[U][PE];
 #pragma unroll
-    for (int e = 0; e < PE; ++e) O[e] = O[e] * fa + p[2 + lane * PE + e] * fb;
-    M = nm;
+    for (int u = 0; u < U; ++u) {
+      const int x = min(x0 + u, nt - 1);
+      const float* p = a.part + ((bh * a.max_tiles + x) * G + g) * (D + 2);
+      pm[u] = x0 + u < nt ? p[0] : -INFINITY;
+      pl[u] = p[1];
+#pragma unroll
+      for (int e = 0; e < PE; ++e) po[u][e] = p[2 + lane * PE + e];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float mx = pm[u];
+      if (mx == -INFINITY) continue;
+      const float nm = fmaxf(M, mx);
+      const float fa = M == -INFINITY ? 0.f : __expf(M - nm);
+      const float fb = __expf(mx - nm);
+      S = S * fa + pl[u] * fb;
+#pragma unroll
+      for (int e = 0; e < PE; ++e) O[e] = O[e] * fa + po[u][e] * fb;
+      M = nm;
+    }
   }
   float* out = a.out + ((int64_t)b * a.hq + qh) * D;
 #pragma unroll
@@ -272,16 +316,16 @@ int attn_max_tiles(int W, int sparse_cap, int chunk_cap) {
   return ceil_div(W, kAttnTile) + ceil_div(sparse_cap, kAttnTile) + ceil_div(chunk_cap, kAttnTile);
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool P>
 static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
   if (a.max_tiles > 0)
-    hipLaunchKernelGGL((k_attn<T, D, G>), dim3(a.max_tiles, a.hkv, a.B), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_attn<T, D, G, P>), dim3(a.max_tiles, a.hkv, a.B), dim3(256), 0, st, a);
   hipLaunchKernelGGL((k_attn_merge<T, D, G>), dim3(ceil_div((int64_t)a.B * a.hq, 4)), dim3(256),
                      0, st, a);
 }
 
 void launch_attn(const AttnArgs& a, hipStream_t st) {
-  HK_DISPATCH(a.dtype, a.D, a.G, launch_attn_t, a, st);
+  HK_DISPATCH_P(a.dtype, a.D, a.G, a.dk.table != nullptr, launch_attn_t, a, st);
 }
 
 }  // namespace hk

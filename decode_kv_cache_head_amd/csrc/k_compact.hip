@@ -45,7 +45,7 @@ __device__ inline int block_excl_scan_256(int v, int* sh, int& total) {
   return off + incl - v;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool P>
 __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
   constexpr int RB = D * (int)sizeof(T);
   constexpr int CPR = RB / 16;
@@ -103,27 +103,27 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
       if (sel) pos[rk] = s0 + tid;
       if (tid == 0) s_base = base + __popcll(bal);
     }
-    uint4 buf[PER];
+    v4u buf[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
       // rows past the sub-tile re-read its last row (in bounds, never stored)
       const int t = s0 + min(r, nr - 1);
-      const char* src = tsr ? a.vrows.row(b, h, t) : a.krows.row(b, h, t);
-      buf[k] = *(const uint4*)(src + c * 16);
+      const char* src = tsr ? a.vrows.template row<P>(b, h, t) : a.krows.template row<P>(b, h, t);
+      buf[k] = *(const v4u*)(src + c * 16);
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
-      *(uint4*)((tsr ? sv : sk) + r * RB + c * 16) = buf[k];
+      *(v4u*)((tsr ? sv : sk) + r * RB + c * 16) = buf[k];
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
       if (r < nr && s_sel[r])
-        *(uint4*)((tsr ? ov : ok) + (int64_t)s_rank[r] * RB + c * 16) =
-            *(const uint4*)((tsr ? sv : sk) + r * RB + c * 16);
+        *(v4u*)((tsr ? ov : ok) + (int64_t)s_rank[r] * RB + c * 16) =
+            *(const v4u*)((tsr ? sv : sk) + r * RB + c * 16);
     }
     if (summer) {
       const T* src = (const T*)(tensor ? sv : sk);
@@ -148,15 +148,184 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
   if (tid == 0 && tend == n) a.out_count[bh] = base;
 }
 
-template <typename T, int D, int G_unused>
+// Fast path for chunks that are whole multiples of 64 rows.  One tile
+// (<= 1024 rows, whole chunks) per workgroup: the ranks of all its rows are
+// computed once (block scan of the mask), then 64-row sub-tiles stream
+// through registers with the next sub-tile's loads issued before the current
+// one is stored (ping-pong buffers).  Thread (rg, c) owns 16-byte piece c of
+// rows rg, rg + RG, ...; kept pieces go straight to their slot, evicted ones
+// are added to per-thread float32 partial sums.  At the end of each chunk
+// the partials are reduced across row groups (lane shuffles, then the four
+// waves in a fixed order through LDS): deterministic.
+template <typename T, int D, bool P>
+__global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
+  constexpr int RB = D * (int)sizeof(T);
+  constexpr int CPR = RB / 16;        // pieces per row
+  constexpr int EPC = Elt<T>::kPer16;  // elements per piece
+  constexpr int RG = 256 / CPR;       // row groups per sub-tile
+  constexpr int RPT = 64 / RG;        // rows per thread per sub-tile
+  constexpr int NB = 2 * RPT;         // pieces per thread per sub-tile (K and V)
+  __shared__ int s_rank[1024];
+  __shared__ float s_red[4][2][D];
+  __shared__ int s_scan[4];
+  __shared__ int s_ev;
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int n = a.cand.n(b, h);
+  const int t0 = j * TT;
+  const int64_t bh = (int64_t)b * a.hkv + h;
+  if (t0 >= n) {
+    if (j == 0 && tid == 0) a.out_count[bh] = 0;
+    return;
+  }
+  const int nrows = min(TT, n - t0);
+  const uint8_t* mk = a.mask + bh * a.cap_stride;
+  char* ok = a.out_k + bh * a.cap_stride * RB;
+  char* ov = a.out_v + bh * a.cap_stride * RB;
+  int32_t* pos = a.out_pos + bh * a.cap_stride;
+
+  // kept tokens before the tile
+  int base;
+  {
+    int c = 0;
+#pragma unroll 8
+    for (int t = tid; t < t0; t += 256) c += mk[t] != 0;
+    int total;
+    block_excl_scan_256(c, s_scan, total);
+    base = total;
+  }
+  // ranks of the tile's rows (rows 4 tid .. 4 tid + 3); -1 = evicted
+  {
+    int c4 = 0, flags = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 4 * tid + q;
+      const bool sel = r < nrows && mk[t0 + r] != 0;
+      flags |= (int)sel << q;
+      c4 += sel;
+    }
+    int total;
+    int rk = base + block_excl_scan_256(c4, s_scan, total);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 4 * tid + q;
+      if (r < nrows) {
+        if ((flags >> q) & 1) {
+          s_rank[r] = rk;
+          pos[rk] = t0 + r;
+          ++rk;
+        } else {
+          s_rank[r] = -1;
+        }
+      }
+    }
+    if (tid == 0) s_ev = 0;
+    if (t0 + nrows == n && tid == 255) a.out_count[bh] = rk;
+  }
+  __syncthreads();
+
+  const int c = tid % CPR, rg = tid / CPR;
+  const int w = tid >> 6, lane = tid & 63;
+  const int nsub = (nrows + 63) / 64;
+  float acc[2][EPC];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[q][e] = 0.f;
+
+  auto load = [&](v4u (&buf)[NB], int s) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = min(s * 64 + rg + RG * i, nrows - 1);
+      buf[i] = *(const v4u*)(a.krows.template row<P>(b, h, t0 + r) + c * 16);
+      buf[RPT + i] = *(const v4u*)(a.vrows.template row<P>(b, h, t0 + r) + c * 16);
+    }
+  };
+  auto process = [&](const v4u (&buf)[NB], int s) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = s * 64 + rg + RG * i;
+      if (r < nrows) {
+        const int rk = s_rank[r];
+        if (rk >= 0) {
+          *(v4u*)(ok + (int64_t)rk * RB + c * 16) = buf[i];
+          *(v4u*)(ov + (int64_t)rk * RB + c * 16) = buf[RPT + i];
+        } else {
+          float f[EPC];
+          Elt<T>::unpack(buf[i], f);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[0][e] += f[e];
+          Elt<T>::unpack(buf[RPT + i], f);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[1][e] += f[e];
+        }
+      }
+    }
+    // end of a chunk: reduce and store its sums and count
+    const int rows_done = min((s + 1) * 64, nrows);
+    if (rows_done % a.C == 0 || rows_done == nrows) {
+      const int ch = (t0 + s * 64) / a.C;
+      const int cs = ch * a.C - t0;  // chunk's first row in the tile (>= 0)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          float v = acc[q][e];
+#pragma unroll
+          for (int o = CPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+          acc[q][e] = v;
+        }
+      if (lane < CPR) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) s_red[w][q][c * EPC + e] = acc[q][e];
+      }
+      // evicted rows of the chunk
+      int ev = 0;
+      for (int r = cs + tid; r < rows_done; r += 256) ev += s_rank[r] < 0;
+      if (ev) atomicAdd(&s_ev, ev);
+      __syncthreads();
+      if (tid < 2 * D) {
+        const int q = tid / D, dim = tid % D;
+        const float v = ((s_red[0][q][dim] + s_red[1][q][dim]) + s_red[2][q][dim]) + s_red[3][q][dim];
+        (q ? a.vsum : a.ksum)[(bh * a.chunk_stride + ch) * D + dim] = v;
+      }
+      if (tid == 0) {
+        a.ccount[bh * a.chunk_stride + ch] = s_ev;
+        s_ev = 0;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[q][e] = 0.f;
+      __syncthreads();
+    }
+  };
+
+  v4u A_[NB], B_[NB];
+  load(A_, 0);
+  for (int s = 0; s < nsub; s += 2) {
+    if (s + 1 < nsub) load(B_, s + 1);
+    process(A_, s);
+    if (s + 1 < nsub) {
+      if (s + 2 < nsub) load(A_, s + 2);
+      process(B_, s + 1);
+    }
+  }
+}
+
+template <typename T, int D, int G_unused, bool P>
 static void launch_compact_t(const CompactArgs& a, hipStream_t st) {
   const int TT = compact_tile(a.C);
   const int nt = max(1, ceil_div(a.max_cand, TT));  // tile 0 also writes count = 0
-  hipLaunchKernelGGL((k_compact<T, D>), dim3(nt, a.hkv, a.B), dim3(256), 0, st, a, TT);
+  if (a.C % 64 == 0 && TT <= 1024)
+    hipLaunchKernelGGL((k_compact_fast<T, D, P>), dim3(nt, a.hkv, a.B), dim3(256), 0, st, a, TT);
+  else
+    hipLaunchKernelGGL((k_compact<T, D, P>), dim3(nt, a.hkv, a.B), dim3(256), 0, st, a, TT);
 }
 
 void launch_compact(const CompactArgs& a, hipStream_t st) {
-  HK_DISPATCH(a.dtype, a.D, 1, launch_compact_t, a, st);
+  HK_DISPATCH_P(a.dtype, a.D, 1, a.krows.table != nullptr, launch_compact_t, a, st);
 }
 
 // ------------------------------------------------------------ in place ----
@@ -201,16 +370,16 @@ __global__ __launch_bounds__(256) void k_compact_inplace(CompactArgs a) {
       s_pos[tid] = tid < nr ? pos[s0 + tid] : 0;
       if (tid == 0) s_base = base + __popcll(bal);
     }
-    uint4 buf[PER];
+    v4u buf[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
-      buf[k] = *(const uint4*)((tsr ? pv : pk) + (int64_t)(s0 + min(r, nr - 1)) * RB + c * 16);
+      buf[k] = *(const v4u*)((tsr ? pv : pk) + (int64_t)(s0 + min(r, nr - 1)) * RB + c * 16);
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
-      if (r < nr) *(uint4*)((tsr ? sv : sk) + r * RB + c * 16) = buf[k];
+      if (r < nr) *(v4u*)((tsr ? sv : sk) + r * RB + c * 16) = buf[k];
     }
     __syncthreads();  // the whole sub-tile (rows, positions, ranks) is read
     // write kept rows to their (lower or equal) slots
@@ -218,8 +387,8 @@ __global__ __launch_bounds__(256) void k_compact_inplace(CompactArgs a) {
     for (int k = 0; k < PER; ++k) {
       const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
       if (r < nr && s_sel[r] && s_rank[r] != s0 + r)
-        *(uint4*)((tsr ? pv : pk) + (int64_t)s_rank[r] * RB + c * 16) =
-            *(const uint4*)((tsr ? sv : sk) + r * RB + c * 16);
+        *(v4u*)((tsr ? pv : pk) + (int64_t)s_rank[r] * RB + c * 16) =
+            *(const v4u*)((tsr ? sv : sk) + r * RB + c * 16);
     }
     if (tid < nr && s_sel[tid]) pos[s_rank[tid]] = s_pos[tid];
     if (summer) {

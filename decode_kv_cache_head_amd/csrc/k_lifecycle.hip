@@ -22,9 +22,9 @@ __global__ __launch_bounds__(64) void k_append(AppendArgs a) {
   for (int i = tid; i < 2 * CPR; i += 64) {
     const int tsr = i / CPR, c = i % CPR;
     char* ring = (tsr ? a.ring_v : a.ring_k) + (bh * a.W + slot) * RB + c * 16;
-    const uint4 old = *(const uint4*)ring;
-    if (room) *(uint4*)((tsr ? a.pool_v : a.pool_k) + (bh * a.sparse_cap + cnt) * RB + c * 16) = old;
-    *(uint4*)ring = *(const uint4*)((const char*)(tsr ? a.v_new : a.k_new) + bh * RB + c * 16);
+    const v4u old = *(const v4u*)ring;
+    if (room) *(v4u*)((tsr ? a.pool_v : a.pool_k) + (bh * a.sparse_cap + cnt) * RB + c * 16) = old;
+    *(v4u*)ring = *(const v4u*)((const char*)(tsr ? a.v_new : a.k_new) + bh * RB + c * 16);
   }
   if (tid == 0 && room) {
     a.pool_pos[bh * a.sparse_cap + cnt] = P - a.W;

@@ -1,8 +1,10 @@
 // Importance scores of aged tokens (HARD-KV, gist.science technical summary,
 // section 2.B "Goal": max-pooled logits; key-norm metric alongside).
 //
-// HBM-bound stream over the aged keys.  Each workgroup stages a 256-token
-// tile of one (b, h) into LDS with coalesced 16-byte loads, then every lane
+// HBM-bound stream over the aged keys.  Each workgroup takes up to four
+// consecutive 256-token tiles of one (b, h); a tile is staged into LDS with
+// coalesced 16-byte loads, and the next tile's loads are issued before the
+// current one is scored, so HBM traffic overlaps the arithmetic.  Every lane
 // scores one token: the G query rows of the head's GQA group are read as
 // float64 from wave-uniform addresses (scalar loads, SGPR operands), the
 // token's key is widened exactly to float64 and the G dot products are
@@ -20,6 +22,7 @@ __global__ __launch_bounds__(256) void k_q_to_f64(const T* __restrict__ q, doubl
 }
 
 constexpr int kScoreTile = 256;
+constexpr int kScoreTiles = 4;  // tiles per workgroup
 
 template <typename T, int D, int G, bool L2>
 __device__ inline void score_row(const unsigned char* row, const double* __restrict__ qg,
@@ -29,7 +32,7 @@ __device__ inline void score_row(const unsigned char* row, const double* __restr
   constexpr int EPC = Elt<T>::kPer16;
 #pragma unroll
   for (int c = 0; c < CPR; ++c) {
-    const uint4 raw = *(const uint4*)(row + c * 16);
+    const v4u raw = *(const v4u*)(row + c * 16);
     float f[EPC];
     Elt<T>::unpack(raw, f);
 #pragma unroll
@@ -42,7 +45,52 @@ __device__ inline void score_row(const unsigned char* row, const double* __restr
   }
 }
 
+// Coalesced 16-byte loads of a 256-token tile; rows past the end re-read the
+// last valid row (always in bounds, their scores are never written).
+template <int CPR, bool P>
+__device__ __forceinline__ void load_tile(v4u (&buf)[CPR], const Rows& rows, int b, int h,
+                                          int t0, int n, int tid) {
+#pragma unroll
+  for (int j = 0; j < CPR; ++j) {
+    const int idx = j * kScoreTile + tid;
+    const int r = idx / CPR, c = idx % CPR;
+    buf[j] = *(const v4u*)(rows.template row<P>(b, h, min(t0 + r, n - 1)) + c * 16);
+  }
+}
+
+template <int CPR, int PAD>
+__device__ __forceinline__ void store_tile(const v4u (&buf)[CPR], unsigned char* lds, int tid) {
+#pragma unroll
+  for (int j = 0; j < CPR; ++j) {
+    const int idx = j * kScoreTile + tid;
+    const int r = idx / CPR, c = idx % CPR;
+    *(v4u*)(lds + r * PAD + c * 16) = buf[j];
+  }
+}
+
+// One lane scores token t from its LDS row.
 template <typename T, int D, int G>
+__device__ __forceinline__ void score_lane(const unsigned char* row, const double* __restrict__ qg,
+                                           bool is_l2, int t, int n, float* __restrict__ logit,
+                                           float* __restrict__ l2, int64_t obase, double scale) {
+  double acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = 0.0;
+  double ss = 0.0;
+  if (is_l2)
+    score_row<T, D, G, true>(row, qg, acc, ss);
+  else
+    score_row<T, D, G, false>(row, qg, acc, ss);
+  double mx = acc[0];
+#pragma unroll
+  for (int g = 1; g < G; ++g) mx = fmax(mx, acc[g]);
+  if (t < n) {
+    logit[obase + t] = (float)(mx * scale);
+    if (is_l2) l2[obase + t] = (float)sqrt(ss);
+  }
+}
+
+template <typename T, int D, int G, bool P>
 __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, int hq, Rows rows,
                                                Cand cand, const int8_t* __restrict__ metric,
                                                float* __restrict__ logit, float* __restrict__ l2,
@@ -53,62 +101,45 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
   __shared__ __attribute__((aligned(16))) unsigned char lds[kScoreTile * PAD];
   const int b = blockIdx.z, h = blockIdx.y, hkv = gridDim.y;
   const int n = cand.n(b, h);
-  const int t0 = blockIdx.x * kScoreTile;
-  if (t0 >= n) return;
   const int tid = threadIdx.x;
-
-  // Rows past the end re-read the last valid row (always in bounds); their
-  // scores are never written.
-  uint4 buf[CPR];
-#pragma unroll
-  for (int j = 0; j < CPR; ++j) {
-    const int idx = j * kScoreTile + tid;
-    const int r = idx / CPR, c = idx % CPR;
-    const int t = min(t0 + r, n - 1);
-    buf[j] = *(const uint4*)(rows.row(b, h, t) + c * 16);
-  }
-#pragma unroll
-  for (int j = 0; j < CPR; ++j) {
-    const int idx = j * kScoreTile + tid;
-    const int r = idx / CPR, c = idx % CPR;
-    *(uint4*)(lds + r * PAD + c * 16) = buf[j];
-  }
-  __syncthreads();
-
-  const int t = t0 + tid;
-  if (t >= n) return;
+  // this workgroup's tiles: kScoreTiles consecutive 256-token tiles
+  const int tfirst = blockIdx.x * kScoreTiles;
+  const int ntiles = min(kScoreTiles, (n + kScoreTile - 1) / kScoreTile - tfirst);
+  if (ntiles <= 0) return;
   const double* __restrict__ qg = q64 + ((int64_t)b * hq + (int64_t)h * G) * D;
   const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
-  double acc[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) acc[g] = 0.0;
-  double ss = 0.0;
-  const unsigned char* row = lds + tid * PAD;
-  if (is_l2)
-    score_row<T, D, G, true>(row, qg, acc, ss);
-  else
-    score_row<T, D, G, false>(row, qg, acc, ss);
-  double mx = acc[0];
-#pragma unroll
-  for (int g = 1; g < G; ++g) mx = fmax(mx, acc[g]);
-  const int64_t o = ((int64_t)b * hkv + h) * cap_stride + t;
-  logit[o] = (float)(mx * scale);
-  if (is_l2) l2[o] = (float)sqrt(ss);
+  const int64_t obase = ((int64_t)b * hkv + h) * cap_stride;
+
+  v4u buf[CPR];
+  load_tile<CPR, P>(buf, rows, b, h, tfirst * kScoreTile, n, tid);
+  // steady state: the next tile's loads are in flight while this one is scored
+  for (int tile = 0; tile + 1 < ntiles; ++tile) {
+    store_tile<CPR, PAD>(buf, lds, tid);
+    __syncthreads();
+    load_tile<CPR, P>(buf, rows, b, h, (tfirst + tile + 1) * kScoreTile, n, tid);
+    score_lane<T, D, G>(lds + tid * PAD, qg, is_l2, (tfirst + tile) * kScoreTile + tid, n, logit,
+                        l2, obase, scale);
+    __syncthreads();
+  }
+  store_tile<CPR, PAD>(buf, lds, tid);
+  __syncthreads();
+  score_lane<T, D, G>(lds + tid * PAD, qg, is_l2, (tfirst + ntiles - 1) * kScoreTile + tid, n,
+                      logit, l2, obase, scale);
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool P>
 static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   const int64_t nq = (int64_t)a.B * a.hq * D;
   hipLaunchKernelGGL(k_q_to_f64<T>, dim3(ceil_div(nq, 256)), dim3(256), 0, st, (const T*)a.q,
                      a.q64, nq);
-  dim3 grid(ceil_div(a.max_cand, kScoreTile), a.rows.hkv, a.B);
+  dim3 grid(ceil_div(a.max_cand, kScoreTile * kScoreTiles), a.rows.hkv, a.B);
   if (grid.x == 0) return;
-  hipLaunchKernelGGL((k_score<T, D, G>), grid, dim3(256), 0, st, a.q64, a.hq, a.rows, a.cand,
+  hipLaunchKernelGGL((k_score<T, D, G, P>), grid, dim3(256), 0, st, a.q64, a.hq, a.rows, a.cand,
                      a.metric, a.logit, a.l2, a.cap_stride, a.scale);
 }
 
 void launch_score(const ScoreArgs& a, hipStream_t st) {
-  HK_DISPATCH(a.dtype, a.D, a.G, launch_score_t, a, st);
+  HK_DISPATCH_P(a.dtype, a.D, a.G, a.rows.table != nullptr, launch_score_t, a, st);
 }
 
 }  // namespace hk

@@ -55,6 +55,10 @@ GRID = [
     dict(dtype=S.DT_BF16, d=128, Hq=16, Hkv=2, C=1, p=0.7, metric=(S.METRIC_QK, S.METRIC_L2)),
     dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=4, C=64, p=0.9,
          metric=(S.METRIC_L2, S.METRIC_QK, S.METRIC_L2, S.METRIC_L2), block_size=16),
+    dict(dtype=S.DT_F32, d=128, Hq=8, Hkv=2, C=128, p=0.9, T=(3000, 1100, 200)),
+    dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=1, C=64, p=0.85, block_size=64),
+    dict(dtype=S.DT_F32, d=64, Hq=4, Hkv=4, C=192, p=0.6, T=(2500, 1000, 70)),
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=1024, p=0.9, T=(2600, 1300, 1090)),
 ]
 
 
