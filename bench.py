@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="override the cache layout (0 = contiguous)")
     return ap.parse_args()
 
 
@@ -155,6 +157,9 @@ def main():
     H.load()
     dev = torch.device("cuda:0")
     w = S.workload(args.workload)
+    if args.block_size is not None:
+        from dataclasses import replace
+        w = replace(w, block_size=args.block_size)
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     case = S.make_case(w, dev)
     desc = H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.W, w.C, w.p, case.ctx_cap,
@@ -225,6 +230,22 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
+
+    # reference: a plain device-to-device copy of 2 GiB (read + write), the
+    # bandwidth a streaming kernel can reach on this machine
+    src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 31) * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
 
     A = np.maximum(np.array(w.T)[:, None] - w.W, 0) * np.ones((1, w.Hkv), np.int64)
     k = tiers.count.cpu().numpy().astype(np.int64)
@@ -252,6 +273,7 @@ def main():
         "stage_hbm_gbs": {s: round(v, 1) for s, v in gbs.items()},
         "stage_peak_frac": {s: round(v / HBM_PEAK_GBS, 4) for s, v in gbs.items()},
         "fused_step_ms": round(fused_ms, 4),
+        "device_copy_gbs": round(copy_gbs, 1),
         "fused_tokens_s": round(w.B / (fused_ms * 1e-3), 1),
         "kept_fraction": round(float(k.sum() / max(A.sum(), 1)), 4),
         "dtype_note": "bf16 q/K/V in HBM; float64 score accumulation, 2^-47 fixed-point "

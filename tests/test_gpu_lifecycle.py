@@ -179,3 +179,106 @@ def test_first_lifecycle_step_equals_single_step(gpu):
             assert torch.equal(st.ccount[b, h, :nch], tiers.ccount[b, h, :nch])
     err = ((out - run.out).abs().amax(-1) / out.abs().amax(-1)).max().item()
     assert err < 1e-5
+
+
+def test_lifecycle_qwen32b_64_layers_256_steps(gpu):
+    """Full-size lifecycle: Qwen3-32B attention shape (64 query heads, 8 KV
+    heads, d=128), 64 layers with their own caches, 64 sequences starting at
+    12288 tokens, 256 decode steps, window 512, chunk 64, p = 0.95.  Sampled
+    (layer, sequence, head) triples follow the oracle step by step; every
+    head is checked for the token-count invariant at several steps."""
+    L, B, Hq, Hkv, d, T0, W, C, p, steps = 64, 64, 64, 8, 128, 12288, 512, 64, 0.95, 256
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    need = L * B * Hkv * ((T0 + steps - W) * d * 4 + W * d * 4 + 188 * d * 8) * 1.02
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} free")
+    desc = H.make_desc(B, Hq, Hkv, d, H.BF16, W, C, p, T0 + steps)
+    A = T0 - W
+    ws = H.alloc_workspace(desc, gpu)
+    out = torch.empty((B, Hq, d), device=gpu)
+    layers = []
+    for layer in range(L):
+        g = torch.Generator(device=gpu).manual_seed(1000 + layer)
+        t = H.alloc_tiers(desc, gpu)
+        for i in range(0, B, 8):   # draw in slices to bound the float32 temporaries
+            t.k[i:i + 8, :, :A] = torch.randn((8, Hkv, A, d), generator=g, device=gpu).to(torch.bfloat16)
+            t.v[i:i + 8, :, :A] = torch.randn((8, Hkv, A, d), generator=g, device=gpu).to(torch.bfloat16)
+        t.pos[:, :, :A] = torch.arange(A, dtype=torch.int32, device=gpu)
+        t.count.fill_(A)
+        t.ksum.zero_()
+        t.vsum.zero_()
+        t.ccount.zero_()
+        rk = torch.randn((B, Hkv, W, d), generator=g, device=gpu).to(torch.bfloat16)
+        rv = torch.randn((B, Hkv, W, d), generator=g, device=gpu).to(torch.bfloat16)
+        layers.append(H.State(rk, rv, t, torch.full((B,), T0, dtype=torch.int32, device=gpu)))
+    say("allocated", L, "layers")
+    samples = [(0, 0, 0), (17, 33, 5), (63, 63, 7)]
+    states = {}
+    for (layer, b, h) in samples:
+        st = layers[layer]
+        pk = st.tiers.k[b, h, :A].float().cpu().numpy()
+        pv = st.tiers.v[b, h, :A].float().cpu().numpy()
+        o = O.HeadState(W, C, st.ring_k[b, h].float().cpu().numpy(), st.ring_v[b, h].float().cpu().numpy(),
+                        pk, pv, np.arange(A), np.zeros((desc.chunk_cap, d)), np.zeros((desc.chunk_cap, d)),
+                        np.zeros(desc.chunk_cap, np.int64), T0)
+        states[(layer, b, h)] = o
+    rep = dict(borderline=0, resyncs=0, max_attn_err=0.0)
+    gq = torch.Generator(device=gpu).manual_seed(7)
+    G = Hq // Hkv
+    for s in range(steps):
+        for layer in range(L):
+            q = (torch.randn((B, Hq, d), generator=gq, device=gpu)).to(torch.bfloat16)
+            kn = torch.randn((B, Hkv, d), generator=gq, device=gpu).to(torch.bfloat16)
+            vn = torch.randn((B, Hkv, d), generator=gq, device=gpu).to(torch.bfloat16)
+            H.step_inplace(desc, q, kn, vn, None, layers[layer], out, ws)
+            for (ly, b, h), st in states.items():
+                if ly != layer:
+                    continue
+                torch.cuda.synchronize()
+                qh = q[b, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
+                pool_before = st.pool_pos.copy()
+                o_ref, info = O.lifecycle_step(st, qh, kn[b, h].float().cpu().numpy(),
+                                               vn[b, h].float().cpu().numpy(), p, O.METRIC_QK)
+                t = layers[layer].tiers
+                n = int(t.count[b, h])
+                pos = t.pos[b, h, :n].cpu().numpy().astype(np.int64)
+                diff = np.setxor1d(pos, st.pool_pos)
+                if diff.size:
+                    P = T0 + s
+                    cand = np.concatenate([pool_before, [P - W]])
+                    ref = O.HeadResult(len(cand), None, None, info["cal"], info["sel"], None, None,
+                                       None, None, None, None, None, None)
+                    assert borderline_tokens(ref, p, np.searchsorted(cand, diff)).all()
+                    rep["borderline"] += int(diff.size)
+                    st.pool_K = t.k[b, h, :n].float().cpu().numpy()
+                    st.pool_V = t.v[b, h, :n].float().cpu().numpy()
+                    st.pool_pos = pos
+                    st.ksum = t.ksum[b, h].double().cpu().numpy()
+                    st.vsum = t.vsum[b, h].double().cpu().numpy()
+                    st.cnt = t.ccount[b, h].cpu().numpy().astype(np.int64)
+                    o_ref = O.attend_head(qh, st.ring_K, st.ring_V, st.pool_K, st.pool_V, st.ksum,
+                                          st.vsum, st.cnt)
+                    rep["resyncs"] += 1
+                assert np.array_equal(t.ccount[b, h].cpu().numpy(), st.cnt)
+                if s % 32 == 0 or s == steps - 1:
+                    assert np.array_equal(t.k[b, h, :n].float().cpu().numpy(), st.pool_K)
+                    bound = 1e-5 * np.maximum(st.cnt, 1)[:, None] * 6.0
+                    assert np.all(np.abs(t.ksum[b, h].double().cpu().numpy() - st.ksum) <= bound)
+                og = out[b, h * G:(h + 1) * G].double().cpu().numpy()
+                err = np.abs(og - o_ref).max(axis=1) / np.abs(o_ref).max(axis=1)
+                assert np.all(err <= ATTN_TOL), (s, layer, b, h, err.max())
+                rep["max_attn_err"] = max(rep["max_attn_err"], float(err.max()))
+        if s in (0, 1, 9, 19, 49, steps - 1):
+            torch.cuda.synchronize()
+            P1 = T0 + s + 1
+            for layer in (0, 31, 63):
+                t = layers[layer].tiers
+                tot = t.count.long() + t.ccount.long().sum(-1) + W
+                assert torch.all(tot == P1), (s, layer)
+                assert torch.all(layers[layer].seq_len == P1)
+            pool = layers[0].tiers.count.float().mean().item()
+            say(f"step {s + 1}: mean pool size {pool:.0f} (layer 0)", rep)
+    say(rep)
+    del layers, ws
+    torch.cuda.empty_cache()
