@@ -1,16 +1,18 @@
 """Decode-step benchmark of the HARD-KV hot path on one MI355X.
 
 One step = one pass of the whole path over one batch: score -> calibrate ->
-top-p select -> compact (rewrite + condense) -> three-tier attention, for
-every (sequence, KV head) of one layer.  Default workload: Qwen3-8B attention
-shape (32 query heads, 8 KV heads, head_dim 128), batch 32, 16384-token
-contexts in a paged bf16 cache (16-token blocks), dense window 256, chunk 64,
-top-p 0.95.  Inputs are synthetic N(0, 1) and resident in HBM before timing.
+top-p select -> compact (rewrite + condense, with attention over the kept
+rows folded in) -> dense/condensed attention -> merge, for every (sequence,
+KV head) of one layer, through the C ABI's hardkv_step.  Default workload:
+Qwen3-8B attention shape (32 query heads, 8 KV heads, head_dim 128), batch
+32, 16384-token contexts in a paged bf16 cache (16-token blocks), dense
+window 256, chunk 64, top-p 0.95.  Inputs are synthetic N(0, 1) and resident
+in HBM before timing.
 
-Prints one JSON line (rank 0).  The timed region runs the five ABI calls of
-the path back to back on one stream with HIP events between them, so every
-stage's average duration is measured live; the fused hardkv_step over the
-same inputs is timed separately and reported next to it.
+Prints one JSON line.  In the timed region the library's launch observer
+records a HIP event on the launch stream before every kernel, so each
+kernel's average duration is measured live; the same loop without the
+observer is timed as a cross-check.
 """
 from __future__ import annotations
 
@@ -27,10 +29,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s + HBM GB/s (% of peak), Qwen3-8B shape, 16k ctx, batch 32"
 HBM_PEAK_GBS = 8000.0
-KERNEL_OF_STAGE = {"score": "k_score", "calibrate": "k_calibrate", "select": "k_select",
-                   "compact": "k_compact", "attn": "k_attn"}
-STAGE_SOURCES = {"score": "k_score.hip", "calibrate": "k_select.hip", "select": "k_select.hip",
-                 "compact": "k_compact.hip", "attn": "k_attn.hip"}
+KERNEL_SOURCES = {"k_q_to_f64": "k_score.hip", "k_score": "k_score.hip",
+                  "k_calibrate": "k_select.hip", "k_select": "k_select.hip",
+                  "k_compact_attn": "k_compact.hip", "k_compact_fast": "k_compact.hip",
+                  "k_compact": "k_compact.hip", "k_attn": "k_attn.hip",
+                  "k_attn_merge": "k_attn.hip"}
 
 
 def parse():
@@ -48,18 +51,18 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(w, A, k, stage):
-    """Bytes the method must move per step (sums over every (b, h)).
+def kernel_bytes(w, A, k, kernel, fused):
+    """Bytes the method must move per launch (sums over every (b, h)).
 
-    A[b, h]: aged candidates, k[b, h]: kept tokens (numpy int arrays).
-    row = d * element size.  Per (b, h):
-      score     A*row (keys) + 4A (logits)            [+ 4A norms on L2 heads]
-      calibrate 4A (read scores)                      [+ 4A on L2 heads]
-      select    4A (read scores) + A (mask)           [+ 4A on L2 heads]
-      compact   2A*row (K, V) + A (mask) + 2k*row + 4k (rows, positions)
-                + nch*(8d + 4) (chunk sums and counts)
-      attn      2(k + W')*row + nch*(8d + 4), W' = dense rows
-    plus q (and o for attention) once per query head.
+    A[b, h]: aged candidates, k[b, h]: kept tokens (numpy int arrays);
+    row = d * element size, nch = ceil(A / C), W' = dense rows.  Per (b, h):
+      k_score        A*row (keys) + 4A (logits)         [+ 4A norms, L2 heads]
+      k_calibrate    4A (scores)                         [+ 4A]
+      k_select       4A (scores) + A (mask)              [+ 4A]
+      k_compact*     2A*row (K, V) + A (mask) + 2k*row + 4k (rows, positions)
+                     + nch*(8d + 4) (chunk sums, counts)
+      k_attn         fused: 2W'*row + nch*(8d + 4); unfused: + 2k*row
+    plus q once per query head (score, attention) and o (attention).
     """
     import numpy as np
     d = w.d
@@ -70,34 +73,41 @@ def algorithmic_bytes(w, A, k, stage):
     nch = -(-A // w.C)
     dense = np.minimum(T, w.W) + 0 * A
     q_bytes = w.B * w.Hq * d * es
-    if stage == "score":
-        return int((A * row + 4 * A + 4 * A * l2).sum() + q_bytes)
-    if stage == "calibrate":
+    o_bytes = w.B * w.Hq * d * 4
+    if kernel == "k_q_to_f64":
+        return q_bytes + w.B * w.Hq * d * 8
+    if kernel == "k_score":
+        return int((A * row + 4 * A + 4 * A * l2).sum() + w.B * w.Hq * d * 8)
+    if kernel == "k_calibrate":
         return int((4 * A + 4 * A * l2).sum())
-    if stage == "select":
+    if kernel == "k_select":
         return int((4 * A + A + 4 * A * l2).sum())
-    if stage == "compact":
-        return int((2 * A * row + A + 2 * k * row + 4 * k + nch * (8 * d + 4)).sum())
-    if stage == "attn":
-        return int((2 * (k + dense) * row + nch * (8 * d + 4)).sum() + q_bytes + w.B * w.Hq * d * 4)
-    raise KeyError(stage)
+    if kernel in ("k_compact", "k_compact_fast", "k_compact_attn"):
+        extra = q_bytes if kernel == "k_compact_attn" else 0
+        return int((2 * A * row + A + 2 * k * row + 4 * k + nch * (8 * d + 4)).sum() + extra)
+    if kernel == "k_attn":
+        sparse = 0 if fused else 2 * k * row
+        return int((2 * dense * row + sparse + nch * (8 * d + 4)).sum() + q_bytes)
+    if kernel == "k_attn_merge":
+        return o_bytes
+    return 0
 
 
-def source_hash(stage):
+def source_hash(kernel):
     h = hashlib.sha256()
-    for f in (STAGE_SOURCES[stage], "common.h", "internal.h"):
+    for f in (KERNEL_SOURCES[kernel], "common.h", "internal.h"):
         h.update(open(os.path.join(ROOT, "decode_kv_cache_head_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(stage, workload):
+def traffic_from_profile(kernel, workload):
     """HBM bytes per launch from committed counter runs, if they were taken on
     the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{KERNEL_OF_STAGE[stage]}_{workload}.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(p):
         return None
     t = json.load(open(p))
-    if t.get("source_hash") != source_hash(stage):
+    if t.get("source_hash") != source_hash(kernel):
         return None
     return int(t["fetch_bytes"] * t["fetch_scale"] + t["write_bytes"] * t["write_scale"])
 
@@ -166,64 +176,41 @@ def main():
                        w.block_size, case.max_blocks)
     ws = H.alloc_workspace(desc, dev)
     cache = H.cache_struct(case.k, case.v, case.ctx_len, case.block_table)
-    cap = desc.sparse_cap
-    logit = torch.empty((w.B, w.Hkv, cap), device=dev)
-    l2 = torch.empty((w.B, w.Hkv, cap), device=dev)
-    stats = torch.empty((w.B, w.Hkv, 4), dtype=torch.float64, device=dev)
-    mask = torch.empty((w.B, w.Hkv, cap), dtype=torch.uint8, device=dev)
-    count = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
     tiers = H.alloc_tiers(desc, dev)
     out = torch.empty((w.B, w.Hq, w.d), device=dev)
     stream = torch.cuda.current_stream()
 
-    stages = ["score", "calibrate", "select", "compact", "attn"]
-
-    def one_pass(ev=None):
-        if ev:
-            ev[0].record(stream)
-        H.score(desc, case.q, cache, case.metric, logit, l2, ws)
-        if ev:
-            ev[1].record(stream)
-        H.calibrate(desc, case.ctx_len, case.metric, logit, l2, stats, ws)
-        if ev:
-            ev[2].record(stream)
-        H.topp_select(desc, case.ctx_len, case.metric, logit, l2, stats, mask, count, ws)
-        if ev:
-            ev[3].record(stream)
-        H.compact(desc, cache, mask, tiers, ws)
-        if ev:
-            ev[4].record(stream)
-        H.decode_attn(desc, case.q, cache, tiers, out, ws)
-        if ev:
-            ev[5].record(stream)
-
-    for _ in range(args.warmup):
-        one_pass()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_pass(evs[i])
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / args.steps
-    stage_ms = {s: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
-                for j, s in enumerate(stages)}
-    ms_per_step = float(np.mean([evs[i][0].elapsed_time(evs[i][5]) for i in range(args.steps)]))
-    print(f"[bench] staged step {ms_per_step:.3f} ms (wall {wall * 1e3:.3f} ms) {stage_ms}",
-          file=sys.stderr, flush=True)
-
-    # the fused entry point over the same inputs
-    for _ in range(args.warmup):
+    def step():
         H.step(desc, case.q, cache, case.metric, tiers, out, ws)
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
+    # timed region: every kernel bracketed by events on the launch stream
+    with H.KernelTimer() as kt:
+        for _ in range(args.steps):
+            kt.mark(stream)
+            step()
+        kt.mark(stream)
+    torch.cuda.synchronize()
+    marks = [i for i, (n, _) in enumerate(kt.events) if n is None]
+    step_ms = [kt.events[a][1].elapsed_time(kt.events[b][1]) for a, b in zip(marks, marks[1:])]
+    ms_per_step = float(np.mean(step_ms))
+    per_kernel = {}
+    for name, ms in kt.durations():
+        per_kernel.setdefault(name, []).append(ms)
+    kernel_ms = {n: float(np.mean(v)) for n, v in per_kernel.items()}
+    launches = {n: len(v) // args.steps for n, v in per_kernel.items()}
+    print(f"[bench] step {ms_per_step:.3f} ms {kernel_ms}", file=sys.stderr, flush=True)
+
+    # the same loop without the observer (cross-check of the step time)
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     f0.record(stream)
     for _ in range(args.steps):
-        H.step(desc, case.q, cache, case.metric, tiers, out, ws)
+        step()
     f1.record(stream)
     torch.cuda.synchronize()
-    fused_ms = f0.elapsed_time(f1) / args.steps
+    plain_ms = f0.elapsed_time(f1) / args.steps
 
     if args.copy_calib:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -232,8 +219,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # reference: a plain device-to-device copy of 2 GiB (read + write), the
-    # bandwidth a streaming kernel can reach on this machine
+    # reference: a plain device-to-device copy of 2 GiB (read + write)
     src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for _ in range(2):
@@ -249,15 +235,17 @@ def main():
 
     A = np.maximum(np.array(w.T)[:, None] - w.W, 0) * np.ones((1, w.Hkv), np.int64)
     k = tiers.count.cpu().numpy().astype(np.int64)
-    alg = {s: algorithmic_bytes(w, A, k, s) for s in stages}
-    gbs = {s: alg[s] / (stage_ms[s] * 1e-3) / 1e9 for s in stages}
-    dom = max(stages, key=lambda s: stage_ms[s])
+    fused = "k_compact_attn" in kernel_ms
+    alg = {n: kernel_bytes(w, A, k, n, fused) for n in kernel_ms}
+    gbs = {n: alg[n] / (kernel_ms[n] * 1e-3) / 1e9 for n in kernel_ms}
+    dom = max(kernel_ms, key=lambda n: kernel_ms[n])
     traffic = traffic_from_profile(dom, w.name)
-    roof = {"bound": "hbm", "kernel": KERNEL_OF_STAGE[dom],
+    roof = {"bound": "hbm", "kernel": dom,
             "achieved": round(gbs[dom], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs[dom] / HBM_PEAK_GBS, 4),
             "traffic": traffic, "algorithmic_bytes": alg[dom],
-            "avg_launch_ms": round(stage_ms[dom], 4)}
+            "avg_launch_ms": round(kernel_ms[dom], 4)}
+    step_bytes = sum(alg.values())
     tok_s = w.B / (ms_per_step * 1e-3)
     res = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -269,12 +257,14 @@ def main():
                    "layout": f"paged{w.block_size}" if w.block_size else "contiguous",
                    "dense_window": w.W, "chunk": w.C, "top_p": w.p, "layers": 1},
         "roofline": roof,
-        "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
-        "stage_hbm_gbs": {s: round(v, 1) for s, v in gbs.items()},
-        "stage_peak_frac": {s: round(v / HBM_PEAK_GBS, 4) for s, v in gbs.items()},
-        "fused_step_ms": round(fused_ms, 4),
+        "kernel_ms": {n: round(v, 4) for n, v in kernel_ms.items()},
+        "kernel_launches_per_step": launches,
+        "kernel_hbm_gbs": {n: round(v, 1) for n, v in gbs.items()},
+        "kernel_peak_frac": {n: round(v / HBM_PEAK_GBS, 4) for n, v in gbs.items()},
+        "step_algorithmic_gb": round(step_bytes / 1e9, 4),
+        "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_ms_without_observer": round(plain_ms, 4),
         "device_copy_gbs": round(copy_gbs, 1),
-        "fused_tokens_s": round(w.B / (fused_ms * 1e-3), 1),
         "kept_fraction": round(float(k.sum() / max(A.sum(), 1)), 4),
         "dtype_note": "bf16 q/K/V in HBM; float64 score accumulation, 2^-47 fixed-point "
                       "top-p masses, float32 attention",

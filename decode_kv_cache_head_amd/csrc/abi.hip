@@ -8,6 +8,15 @@
 using namespace hk;
 
 namespace {
+hardkv_launch_observer g_observer = nullptr;
+void* g_observer_user = nullptr;
+}  // namespace
+
+void hk::observe(const char* kernel, hipStream_t st) {
+  if (g_observer) g_observer(kernel, (hardkv_stream_t)st, g_observer_user);
+}
+
+namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
 
@@ -168,6 +177,12 @@ CompactArgs compact_args(const hardkv_desc* d, const Layout& L, char* ws, const 
   a.vsum = t->vsum;
   a.ccount = t->ccount;
   a.chunk_stride = d->chunk_cap;
+  a.G = d->num_q_heads / d->num_kv_heads;
+  a.hq = d->num_q_heads;
+  a.q = nullptr;
+  a.part = (float*)(ws + L.part);
+  a.max_tiles = L.max_tiles;
+  a.scale = (float)(1.0 / sqrt((double)d->head_dim));
   return a;
 }
 
@@ -196,6 +211,7 @@ AttnArgs attn_args(const hardkv_desc* d, const Layout& L, char* ws, const void* 
   a.max_tiles = L.max_tiles;
   a.out = out;
   a.scale = 1.0 / sqrt((double)d->head_dim);
+  a.fused_tt = 0;
   return a;
 }
 
@@ -232,6 +248,11 @@ const char* hardkv_strerror(int code) {
 }
 
 int hardkv_validate(const hardkv_desc* desc) { return validate(desc); }
+
+void hardkv_set_launch_observer(hardkv_launch_observer fn, void* user) {
+  g_observer = fn;
+  g_observer_user = user;
+}
 
 size_t hardkv_workspace_size(const hardkv_desc* desc) {
   if (validate(desc) != HARDKV_OK) return 0;
@@ -330,12 +351,21 @@ int hardkv_step(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
   const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
   launch_calibrate(sa, st);
   launch_select(sa, st);
-  launch_compact(compact_args(d, L, w, kr, vr, cand, max_aged(d), mask, tiers), st);
+  CompactArgs ca = compact_args(d, L, w, kr, vr, cand, max_aged(d), mask, tiers);
   AttnArgs a = attn_args(d, L, w, q, tiers, out);
   a.dk = kr;
   a.dv = vr;
   a.ctx_len = cache->ctx_len;
   a.ring = false;
+  if (compact_fusable(d->chunk)) {
+    // attention over the kept rows happens inside the compaction pass; the
+    // attention launch then covers the dense and condensed tiers only
+    ca.q = q;
+    launch_compact_attn(ca, st);
+    a.fused_tt = compact_tile(d->chunk);
+  } else {
+    launch_compact(ca, st);
+  }
   launch_attn(a, st);
   return launched();
 }

@@ -169,6 +169,51 @@ __device__ inline float across_groups_sum(float v) {
   return v;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Takes the word by value: bit-casting an ext-vector element in place
+// (__builtin_bit_cast(T, v.y)) is compiled as a cast of element 0.
+__device__ __forceinline__ bf16x2_t as_bf2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+// q.k partial over one lane's 16-byte piece.  bf16 rows with bf16 queries use
+// the packed dot (v_dot2c_f32_bf16, products exact, float32 accumulation);
+// float rows use float FMAs.
+template <typename E, typename QT, int EPL>
+struct QPiece {
+  float f[EPL];
+  __device__ inline void load(const QT* q) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) f[e] = Elt<QT>::load1(q + e);
+  }
+  __device__ inline float dot(const v4u& raw) const {
+    float k[EPL];
+    Elt<E>::unpack(raw, k);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s = fmaf(f[e], k[e], s);
+    return s;
+  }
+};
+template <>
+struct QPiece<bf16_t, bf16_t, 8> {
+  uint32_t w[4];
+  __device__ inline void load(const bf16_t* q) {
+    const v4u v = *(const v4u*)q;
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+    w[3] = v.w;
+  }
+  __device__ inline float dot(const v4u& raw) const {
+    float s = 0.f;
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[0]), as_bf2(raw.x), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[1]), as_bf2(raw.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[2]), as_bf2(raw.z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[3]), as_bf2(raw.w), s, false);
+    return s;
+  }
+};
+
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 }  // namespace hk

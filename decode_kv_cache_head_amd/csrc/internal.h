@@ -52,6 +52,10 @@ namespace hk {
     else HK_DISPATCH_TP(bf16_t, D, G, PAGED, FN, __VA_ARGS__);                  \
   } while (0)
 
+// Profiling hook: reports every kernel launch (name, stream) just before it
+// is enqueued when an observer is installed through the C ABI.
+void observe(const char* kernel, hipStream_t st);
+
 struct ScoreArgs {
   int dtype, D, G, B, hq;
   const void* q;
@@ -85,6 +89,9 @@ void launch_select(const SelectArgs& a, hipStream_t st);
 // Tile of the single-step compaction: whole chunks, about 1024 tokens
 // (one chunk when a chunk is longer), processed in 64-row sub-tiles.
 inline int compact_tile(int C) { return C >= 1024 ? C : C * (1024 / C); }
+// Chunks of whole 64-row sub-tiles take the register-streaming compaction,
+// which can also fold attention over the kept rows into the same pass.
+inline bool compact_fusable(int C) { return C % 64 == 0 && compact_tile(C) <= 1024; }
 
 struct CompactArgs {
   int dtype, D, B, hkv, C;
@@ -101,8 +108,15 @@ struct CompactArgs {
   float* vsum;
   int32_t* ccount;
   int chunk_stride;
+  // fused attention over the kept rows (launch_compact_attn only)
+  int G, hq;
+  const void* q;        // [B][Hq][D]
+  float* part;          // partials [B][Hkv][max_tiles][G][D + 2]; tile j -> slot j
+  int max_tiles;
+  float scale;
 };
 void launch_compact(const CompactArgs& a, hipStream_t st);
+void launch_compact_attn(const CompactArgs& a, hipStream_t st);
 void launch_compact_inplace(const CompactArgs& a, hipStream_t st);
 
 struct AttnArgs {
@@ -126,6 +140,9 @@ struct AttnArgs {
   int max_tiles;
   float* out;
   double scale;
+  // > 0: the sparse tier was attended by the fused compaction (its tiles of
+  // fused_tt candidates own partial slots 0..); only dense and chunk tiles here
+  int fused_tt;
 };
 int attn_max_tiles(int W, int sparse_cap, int chunk_cap);
 void launch_attn(const AttnArgs& a, hipStream_t st);

@@ -31,6 +31,7 @@ struct Lay {
 
 struct TileCounts {
   int nd, ns, nc, ntd, nts, ntc;
+  int first;  // partial slots taken by the fused compaction's tiles
 };
 
 __device__ inline TileCounts tile_counts(const AttnArgs& a, int b, int h) {
@@ -51,53 +52,14 @@ __device__ inline TileCounts tile_counts(const AttnArgs& a, int b, int h) {
   t.ntd = (t.nd + kAttnTile - 1) / kAttnTile;
   t.nts = (t.ns + kAttnTile - 1) / kAttnTile;
   t.ntc = (t.nc + kAttnTile - 1) / kAttnTile;
+  t.first = 0;
+  if (a.fused_tt > 0) {
+    int n = A > a.sparse_cap ? a.sparse_cap : A;
+    t.first = (n + a.fused_tt - 1) / a.fused_tt;
+    t.nts = 0;
+  }
   return t;
 }
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// Takes the word by value: bit-casting an ext-vector element in place
-// (__builtin_bit_cast(T, v.y)) is compiled as a cast of element 0.
-__device__ __forceinline__ bf16x2_t as_bf2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
-
-// q.k partial over one lane's 16-byte piece.  bf16 rows with bf16 queries use
-// the packed dot (v_dot2c_f32_bf16, products exact, float32 accumulation);
-// float rows use float FMAs.
-template <typename E, typename QT, int EPL>
-struct QPiece {
-  float f[EPL];
-  __device__ inline void load(const QT* q) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) f[e] = Elt<QT>::load1(q + e);
-  }
-  __device__ inline float dot(const v4u& raw) const {
-    float k[EPL];
-    Elt<E>::unpack(raw, k);
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) s = fmaf(f[e], k[e], s);
-    return s;
-  }
-};
-template <>
-struct QPiece<bf16_t, bf16_t, 8> {
-  uint32_t w[4];
-  __device__ inline void load(const bf16_t* q) {
-    const v4u v = *(const v4u*)q;
-    w[0] = v.x;
-    w[1] = v.y;
-    w[2] = v.z;
-    w[3] = v.w;
-  }
-  __device__ inline float dot(const v4u& raw) const {
-    float s = 0.f;
-    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[0]), as_bf2(raw.x), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[1]), as_bf2(raw.y), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[2]), as_bf2(raw.z), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[3]), as_bf2(raw.w), s, false);
-    return s;
-  }
-};
 
 // One wave, up to 64 entries starting at row r0 of `kr`/`vr`, in rounds of
 // 8 iterations x RPI rows.  Each round issues the K and the V loads of all
@@ -247,7 +209,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   if (x >= tc.ntd + tc.nts + tc.ntc) return;
   const int64_t bh = (int64_t)b * a.hkv + h;
   const T* qg = (const T*)a.q + ((int64_t)b * a.hq + (int64_t)h * G) * D;
-  float* part_out = a.part + (bh * a.max_tiles + x) * G * (D + 2);
+  float* part_out = a.part + (bh * a.max_tiles + tc.first + x) * G * (D + 2);
   if (x < tc.ntd) {
     int T_ = a.ctx_len ? a.ctx_len[b] : 0;
     T_ = T_ < 0 ? 0 : (T_ > a.ctx_cap ? a.ctx_cap : T_);
@@ -276,7 +238,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   if (wid >= a.B * a.hq) return;
   const int b = wid / a.hq, qh = wid % a.hq, h = qh / G, g = qh % G;
   const TileCounts tc = tile_counts(a, b, h);
-  const int nt = tc.ntd + tc.nts + tc.ntc;
+  const int nt = tc.first + tc.ntd + tc.nts + tc.ntc;
   const int64_t bh = (int64_t)b * a.hkv + h;
   constexpr int PE = D / 64;  // elements per lane
   float M = -INFINITY, S = 0.f, O[PE];
@@ -318,8 +280,13 @@ int attn_max_tiles(int W, int sparse_cap, int chunk_cap) {
 
 template <typename T, int D, int G, bool P>
 static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
-  if (a.max_tiles > 0)
-    hipLaunchKernelGGL((k_attn<T, D, G, P>), dim3(a.max_tiles, a.hkv, a.B), dim3(256), 0, st, a);
+  const int gx = a.fused_tt > 0 ? ceil_div(a.W, kAttnTile) + ceil_div(a.chunk_cap, kAttnTile)
+                                : a.max_tiles;
+  if (gx > 0) {
+    observe("k_attn", st);
+    hipLaunchKernelGGL((k_attn<T, D, G, P>), dim3(gx, a.hkv, a.B), dim3(256), 0, st, a);
+  }
+  observe("k_attn_merge", st);
   hipLaunchKernelGGL((k_attn_merge<T, D, G>), dim3(ceil_div((int64_t)a.B * a.hq, 4)), dim3(256),
                      0, st, a);
 }

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
 // are added to per-thread float32 partial sums.  At the end of each chunk
 // the partials are reduced across row groups (lane shuffles, then the four
 // waves in a fixed order through LDS): deterministic.
-template <typename T, int D, bool P>
+template <typename T, int D, int G, bool P, bool ATTN>
 __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   constexpr int RB = D * (int)sizeof(T);
   constexpr int CPR = RB / 16;        // pieces per row
@@ -165,10 +165,13 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   constexpr int RG = 256 / CPR;       // row groups per sub-tile
   constexpr int RPT = 64 / RG;        // rows per thread per sub-tile
   constexpr int NB = 2 * RPT;         // pieces per thread per sub-tile (K and V)
+  constexpr int GA = ATTN ? G : 1;
   __shared__ int s_rank[1024];
   __shared__ float s_red[4][2][D];
   __shared__ int s_scan[4];
   __shared__ int s_ev;
+  __shared__ float s_am[4][GA], s_al[4][GA];
+  __shared__ float s_ao[ATTN ? 4 * G * D : 1];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int n = a.cand.n(b, h);
   const int t0 = j * TT;
@@ -231,6 +234,21 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[q][e] = 0.f;
+  // attention over the kept rows (fused): running max, sum and numerator of
+  // this lane's row group for every query head of the GQA group
+  QPiece<T, T, EPC> qp[GA];
+  float am[GA], al[GA], ao[GA][EPC];
+  if constexpr (ATTN) {
+    const T* qg = (const T*)a.q + ((int64_t)b * a.hq + (int64_t)h * G) * D;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      qp[g].load(qg + g * D + c * EPC);
+      am[g] = -INFINITY;
+      al[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) ao[g][e] = 0.f;
+    }
+  }
 
   auto load = [&](v4u (&buf)[NB], int s) {
 #pragma unroll
@@ -241,6 +259,43 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
     }
   };
   auto process = [&](const v4u (&buf)[NB], int s) {
+    if constexpr (ATTN) {
+      float sc[RPT][G], mr[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) mr[g] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int r = s * 64 + rg + RG * i;
+        const bool kept = r < nrows && s_rank[min(r, nrows - 1)] >= 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float dot = group_sum<CPR>(qp[g].dot(buf[i]));
+          sc[i][g] = kept ? dot * a.scale : -INFINITY;
+          mr[g] = fmaxf(mr[g], sc[i][g]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mn = fmaxf(am[g], mr[g]);
+        const float alpha = am[g] == -INFINITY ? 0.f : __expf(am[g] - mn);
+        al[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) ao[g][e] *= alpha;
+        am[g] = mn;
+      }
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        float f[EPC];
+        Elt<T>::unpack(buf[RPT + i], f);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float pr = sc[i][g] == -INFINITY ? 0.f : __expf(sc[i][g] - am[g]);
+          al[g] += pr;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) ao[g][e] = fmaf(pr, f[e], ao[g][e]);
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = s * 64 + rg + RG * i;
@@ -312,20 +367,88 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
       process(B_, s + 1);
     }
   }
+  if constexpr (ATTN) {
+    // join the row groups of each wave, then the four waves; one partial
+    // (max, sum, numerator) per query head for this tile
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mw = across_groups_max<CPR>(am[g]);
+      const float f = am[g] == -INFINITY ? 0.f : __expf(am[g] - mw);
+      al[g] = across_groups_sum<CPR>(al[g] * f);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) ao[g][e] = across_groups_sum<CPR>(ao[g][e] * f);
+      am[g] = mw;
+    }
+    if (lane < CPR) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s_ao[(w * G + g) * D + lane * EPC + e] = ao[g][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        s_am[w][g] = am[g];
+        s_al[w][g] = al[g];
+      }
+    }
+    __syncthreads();
+    float* part_out = a.part + (bh * a.max_tiles + j) * G * (D + 2);
+    for (int i = tid; i < G * D; i += 256) {
+      const int g = i / D, e = i % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) M = fmaxf(M, s_am[v][g]);
+      float O = 0.f, S = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (s_am[v][g] != -INFINITY) {
+            const float f = __expf(s_am[v][g] - M);
+            O = fmaf(f, s_ao[(v * G + g) * D + e], O);
+            S = fmaf(f, s_al[v][g], S);
+          }
+        }
+      }
+      float* pp = part_out + g * (D + 2);
+      pp[2 + e] = O;
+      if (e == 0) {
+        pp[0] = M;
+        pp[1] = S;
+      }
+    }
+  }
 }
 
 template <typename T, int D, int G_unused, bool P>
 static void launch_compact_t(const CompactArgs& a, hipStream_t st) {
   const int TT = compact_tile(a.C);
   const int nt = max(1, ceil_div(a.max_cand, TT));  // tile 0 also writes count = 0
-  if (a.C % 64 == 0 && TT <= 1024)
-    hipLaunchKernelGGL((k_compact_fast<T, D, P>), dim3(nt, a.hkv, a.B), dim3(256), 0, st, a, TT);
-  else
+  if (compact_fusable(a.C)) {
+    observe("k_compact_fast", st);
+    hipLaunchKernelGGL((k_compact_fast<T, D, 1, P, false>), dim3(nt, a.hkv, a.B), dim3(256), 0, st,
+                       a, TT);
+  } else {
+    observe("k_compact", st);
     hipLaunchKernelGGL((k_compact<T, D, P>), dim3(nt, a.hkv, a.B), dim3(256), 0, st, a, TT);
+  }
 }
 
 void launch_compact(const CompactArgs& a, hipStream_t st) {
   HK_DISPATCH_P(a.dtype, a.D, 1, a.krows.table != nullptr, launch_compact_t, a, st);
+}
+
+template <typename T, int D, int G, bool P>
+static void launch_compact_attn_t(const CompactArgs& a, hipStream_t st) {
+  const int TT = compact_tile(a.C);
+  const int nt = max(1, ceil_div(a.max_cand, TT));
+  observe("k_compact_attn", st);
+  hipLaunchKernelGGL((k_compact_fast<T, D, G, P, true>), dim3(nt, a.hkv, a.B), dim3(256), 0, st,
+                     a, TT);
+}
+
+void launch_compact_attn(const CompactArgs& a, hipStream_t st) {
+  HK_DISPATCH_P(a.dtype, a.D, a.G, a.krows.table != nullptr, launch_compact_attn_t, a, st);
 }
 
 // ------------------------------------------------------------ in place ----
@@ -415,6 +538,7 @@ __global__ __launch_bounds__(256) void k_compact_inplace(CompactArgs a) {
 
 template <typename T, int D, int G_unused>
 static void launch_compact_inplace_t(const CompactArgs& a, hipStream_t st) {
+  observe("k_compact_inplace", st);
   hipLaunchKernelGGL((k_compact_inplace<T, D>), dim3(a.hkv, a.B), dim3(256), 0, st, a);
 }
 

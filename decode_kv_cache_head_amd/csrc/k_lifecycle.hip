@@ -39,6 +39,7 @@ __global__ void k_advance(int32_t* seq_len, int B) {
 
 template <typename T, int D, int G_unused>
 static void launch_append_t(const AppendArgs& a, hipStream_t st) {
+  observe("k_append", st);
   hipLaunchKernelGGL((k_append<T, D>), dim3(a.hkv, a.B), dim3(64), 0, st, a);
 }
 
@@ -47,6 +48,7 @@ void launch_append(const AppendArgs& a, hipStream_t st) {
 }
 
 void launch_advance(int32_t* seq_len, int B, hipStream_t st) {
+  observe("k_advance", st);
   hipLaunchKernelGGL(k_advance, dim3(ceil_div(B, 256)), dim3(256), 0, st, seq_len, B);
 }
 

@@ -130,10 +130,12 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
 template <typename T, int D, int G, bool P>
 static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   const int64_t nq = (int64_t)a.B * a.hq * D;
+  observe("k_q_to_f64", st);
   hipLaunchKernelGGL(k_q_to_f64<T>, dim3(ceil_div(nq, 256)), dim3(256), 0, st, (const T*)a.q,
                      a.q64, nq);
   dim3 grid(ceil_div(a.max_cand, kScoreTile * kScoreTiles), a.rows.hkv, a.B);
   if (grid.x == 0) return;
+  observe("k_score", st);
   hipLaunchKernelGGL((k_score<T, D, G, P>), grid, dim3(256), 0, st, a.q64, a.hq, a.rows, a.cand,
                      a.metric, a.logit, a.l2, a.cap_stride, a.scale);
 }

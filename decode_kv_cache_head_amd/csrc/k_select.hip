@@ -285,11 +285,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
 }
 
 void launch_calibrate(const SelectArgs& a, hipStream_t st) {
+  observe("k_calibrate", st);
   hipLaunchKernelGGL(k_calibrate, dim3(a.hkv, a.B), dim3(256), 0, st, a.cand, a.metric, a.logit,
                      a.l2, a.cap_stride, a.stats);
 }
 
 void launch_select(const SelectArgs& a, hipStream_t st) {
+  observe("k_select", st);
   hipLaunchKernelGGL(k_select, dim3(a.hkv, a.B), dim3(kSelThreads), 0, st, a.cand, a.metric,
                      a.logit, a.l2, a.cap_stride, (const double*)a.stats, a.top_p, a.mask, a.count);
 }

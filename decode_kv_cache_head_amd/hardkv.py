@@ -58,7 +58,9 @@ class StateC(ctypes.Structure):
 
 
 _P = ctypes.c_void_p
+OBSERVER = ctypes.CFUNCTYPE(None, ctypes.c_char_p, ctypes.c_void_p, ctypes.c_void_p)
 _SIGS = {
+    "hardkv_set_launch_observer": ([OBSERVER, _P], None),
     "hardkv_version": ([], ctypes.c_int),
     "hardkv_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "hardkv_validate": ([ctypes.POINTER(Desc)], ctypes.c_int),
@@ -228,6 +230,43 @@ def step_inplace(desc, q, k_new, v_new, metric, state: State, out, ws, stream=No
                                     ctypes.byref(sc), _p(out), _p(ws), ws.numel(),
                                     _stream(stream))
     _check(rc, "hardkv_step_inplace")
+
+
+class KernelTimer:
+    """Records a CUDA event on the launch stream before every kernel the
+    library enqueues (through the launch observer), so the duration of each
+    kernel is the gap between consecutive events.  Use as a context manager;
+    call mark() after the last library call to close the last kernel."""
+
+    def __init__(self):
+        self.events = []   # (kernel name or None, event)
+        self._cb = OBSERVER(self._on_launch)
+
+    def _on_launch(self, name, stream, user):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(torch.cuda.ExternalStream(stream) if stream else torch.cuda.default_stream())
+        self.events.append((name.decode(), ev))
+
+    def mark(self, stream=None):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream or torch.cuda.current_stream())
+        self.events.append((None, ev))
+
+    def __enter__(self):
+        load().hardkv_set_launch_observer(self._cb, None)
+        return self
+
+    def __exit__(self, *exc):
+        load().hardkv_set_launch_observer(OBSERVER(), None)
+        return False
+
+    def durations(self):
+        """[(kernel, ms)] for every launch followed by an event."""
+        out = []
+        for (name, e0), (_, e1) in zip(self.events, self.events[1:]):
+            if name is not None:
+                out.append((name, e0.elapsed_time(e1)))
+        return out
 
 
 def scale(d: int) -> float:

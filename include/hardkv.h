@@ -34,8 +34,8 @@
  *     heads per KV head (query head g belongs to KV head g / G), d head dim,
  *     T_b context length of sequence b (current token included), W dense
  *     window, C chunk size, A_b = max(T_b - W, 0) aged tokens.
- *   - Thread safety: no global mutable state; calls on distinct streams with
- *     distinct buffers may run concurrently.
+ *   - Thread safety: the only global state is the optional launch observer;
+ *     calls on distinct streams with distinct buffers may run concurrently.
  */
 #ifndef HARDKV_H
 #define HARDKV_H
@@ -126,6 +126,15 @@ typedef struct hardkv_state {
 /* Library version (major * 10000 + minor * 100 + patch). */
 int hardkv_version(void);
 
+/* Profiling hook.  When installed, `fn` is called on the calling thread right
+ * before every kernel launch the library makes, with the kernel's name, the
+ * stream it goes to and `user`, so a profiler can record stream events
+ * between launches (per-kernel durations of one hardkv_step, say).  NULL
+ * (the default) disables it.  The observer is process-wide: install or
+ * remove it while no other thread is calling the library. */
+typedef void (*hardkv_launch_observer)(const char* kernel, hardkv_stream_t stream, void* user);
+void hardkv_set_launch_observer(hardkv_launch_observer fn, void* user);
+
 /* Static text for a return code. */
 const char* hardkv_strerror(int code);
 
@@ -198,7 +207,11 @@ int hardkv_decode_attn(const hardkv_desc* desc, const void* q, const hardkv_cach
 
 /* One complete decode step (section 2.A four-step pipeline for a single
  * step): score -> calibrate -> top-p -> compact -> attention, on one stream,
- * with intermediate scores, statistics and masks in the workspace.
+ * with intermediate scores, statistics and masks in the workspace.  When C
+ * is a multiple of 64, attention over the rewritten rows is folded into the
+ * compaction pass (the rows are attended while they are copied), so the
+ * sparse tier is not read back; results equal hardkv_compact followed by
+ * hardkv_decode_attn up to float32 summation order in the attention.
  *   metric: as in hardkv_score; tiers: written as by hardkv_compact;
  *   out: [B][Hq][d] float32 attention output. */
 int hardkv_step(const hardkv_desc* desc, const void* q, const hardkv_cache* cache,
