@@ -31,6 +31,7 @@ METRIC = "decode tokens/s + HBM GB/s (% of peak), Qwen3-8B shape, 16k ctx, batch
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = {"k_q_to_f64": "k_score.hip", "k_score": "k_score.hip",
                   "k_calibrate": "k_select.hip", "k_select": "k_select.hip",
+                  "k_calsel": "k_select.hip",
                   "k_compact_attn": "k_compact.hip", "k_compact_fast": "k_compact.hip",
                   "k_compact": "k_compact.hip", "k_attn": "k_attn.hip",
                   "k_attn_merge": "k_attn.hip"}
@@ -59,6 +60,7 @@ def kernel_bytes(w, A, k, kernel, fused):
       k_score        A*row (keys) + 4A (logits)         [+ 4A norms, L2 heads]
       k_calibrate    4A (scores)                         [+ 4A]
       k_select       4A (scores) + A (mask)              [+ 4A]
+      k_calsel       4A (scores) + A (mask)              [+ 4A] (both in one)
       k_compact*     2A*row (K, V) + A (mask) + 2k*row + 4k (rows, positions)
                      + nch*(8d + 4) (chunk sums, counts)
       k_attn         fused: 2W'*row + nch*(8d + 4); unfused: + 2k*row
@@ -81,6 +83,8 @@ def kernel_bytes(w, A, k, kernel, fused):
     if kernel == "k_calibrate":
         return int((4 * A + 4 * A * l2).sum())
     if kernel == "k_select":
+        return int((4 * A + A + 4 * A * l2).sum())
+    if kernel == "k_calsel":
         return int((4 * A + A + 4 * A * l2).sum())
     if kernel in ("k_compact", "k_compact_fast", "k_compact_attn"):
         extra = q_bytes if kernel == "k_compact_attn" else 0

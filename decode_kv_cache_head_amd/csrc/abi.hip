@@ -349,8 +349,12 @@ int hardkv_step(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
   hipGetLastError();
   do_score(d, L, w, q, kr, cand, max_aged(d), metric, logit, l2, st);
   const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
-  launch_calibrate(sa, st);
-  launch_select(sa, st);
+  if (calsel_fits(max_aged(d))) {
+    launch_calsel(sa, max_aged(d), st);
+  } else {
+    launch_calibrate(sa, st);
+    launch_select(sa, st);
+  }
   CompactArgs ca = compact_args(d, L, w, kr, vr, cand, max_aged(d), mask, tiers);
   AttnArgs a = attn_args(d, L, w, q, tiers, out);
   a.dk = kr;

@@ -85,6 +85,9 @@ struct SelectArgs {
 };
 void launch_calibrate(const SelectArgs& a, hipStream_t st);
 void launch_select(const SelectArgs& a, hipStream_t st);
+// calibrate + select in one launch, scores in registers (max_cand <= 16384)
+bool calsel_fits(int max_cand);
+void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st);
 
 // Tile of the single-step compaction: whole chunks, about 1024 tokens
 // (one chunk when a chunk is longer), processed in 64-row sub-tiles.

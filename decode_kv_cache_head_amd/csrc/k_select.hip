@@ -284,6 +284,211 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   }
 }
 
+// ------------------------------------------------ calibrate + select -----
+// Both steps for one (b, h) in one 1024-thread workgroup, with the head's
+// scores held in registers (NPT per thread, token t = tid + 1024 i), so every
+// pass after the first load runs from registers.  Same rules as k_calibrate
+// and k_select; the float64 reductions run over 1024 threads instead of 256,
+// so the diagnostic statistics may differ in their last bits.
+template <int NPT>
+__global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t* __restrict__ metric,
+                                                        const float* __restrict__ logit,
+                                                        const float* __restrict__ l2,
+                                                        int64_t cap_stride,
+                                                        double* __restrict__ stats, float top_p,
+                                                        uint8_t* __restrict__ mask,
+                                                        int32_t* __restrict__ count) {
+  __shared__ SelShared S;
+  __shared__ double shd[kSelWaves];
+  __shared__ float shf[kSelWaves];
+  const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
+  const int n = cand.n(b, h);
+  const int64_t bh = (int64_t)b * hkv + h;
+  uint8_t* mk = mask + bh * cap_stride;
+  const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
+  if (n == 0) {
+    if (tid == 0) {
+      double* o = stats + bh * 4;
+      o[0] = 0.0;
+      o[1] = is_l2 ? 0.0 : 1.0;
+      o[2] = 0.0;
+      o[3] = 0.0;
+      count[bh] = 0;
+    }
+    return;
+  }
+  const float* xs = logit + bh * cap_stride;
+  float c[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int t = tid + kSelThreads * i;
+    c[i] = t < n ? xs[t] : 0.f;
+  }
+  double shift = 0.0, scale = 1.0;
+  if (is_l2) {
+    const float* ss = l2 + bh * cap_stride;
+    float sv[NPT];
+    double sx = 0.0, sy = 0.0;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int t = tid + kSelThreads * i;
+      sv[i] = t < n ? ss[t] : 0.f;
+      sx += (double)c[i];
+      sy += (double)sv[i];
+    }
+    sx = block_sum_f64<kSelWaves>(sx, shd);
+    sy = block_sum_f64<kSelWaves>(sy, shd);
+    const double mux = sx / n, mus = sy / n;
+    double vx = 0.0, vy = 0.0;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      if (tid + kSelThreads * i < n) {
+        const double dx = (double)c[i] - mux, dy = (double)sv[i] - mus;
+        vx += dx * dx;
+        vy += dy * dy;
+      }
+    }
+    vx = block_sum_f64<kSelWaves>(vx, shd);
+    vy = block_sum_f64<kSelWaves>(vy, shd);
+    const double sdx = sqrt(vx / n), sds = sqrt(vy / n);
+    if (sdx == 0.0 || sds == 0.0) {
+      shift = 0.0;
+      scale = 0.0;
+    } else {
+      shift = mus;
+      scale = sdx / sds;
+    }
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) c[i] = cval(sv[i], shift, scale);
+  }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i)
+    if (tid + kSelThreads * i < n) mloc = fmaxf(mloc, c[i]);
+  const double m = (double)block_max_f32<kSelWaves>(mloc, shf);
+
+  // pass 1: weights, Z, and the histogram of the top 11 key bits
+  for (int i = tid; i < 2048; i += kSelThreads) S.hist[i] = 0;
+  __syncthreads();
+  double Z = 0.0;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    if (tid + kSelThreads * i < n) {
+      const double wd = exp((double)c[i] - m);
+      Z += wd;
+      const uint64_t w = (uint64_t)__double2ull_rn(wd * 140737488355328.0);
+      if (w) atomicAdd(&S.hist[okey(c[i]) >> 21], (unsigned long long)w);
+    }
+  }
+  Z = block_sum_f64<kSelWaves>(Z, shd);  // contains the barrier before find_bin
+  if (tid == 0) {
+    double* o = stats + bh * 4;
+    o[0] = shift;
+    o[1] = scale;
+    o[2] = m;
+    o[3] = Z;
+  }
+  if (!(top_p < 1.0f)) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i)
+      if (tid + kSelThreads * i < n) mk[tid + kSelThreads * i] = 1;
+    if (tid == 0) count[bh] = n;
+    return;
+  }
+  if (tid < 64) find_bin<2048>(S, true, top_p);
+  __syncthreads();
+  const unsigned long long target = S.target;
+  const uint32_t b1 = S.bin;
+  unsigned long long above = S.above;
+  __syncthreads();
+
+  for (int i = tid; i < 2048; i += kSelThreads) S.hist[i] = 0;
+  if (tid == 0) S.target = target - above;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const uint32_t k = okey(c[i]);
+    if (tid + kSelThreads * i < n && (k >> 21) == b1)
+      atomicAdd(&S.hist[(k >> 10) & 2047u], (unsigned long long)wfix(c[i], m));
+  }
+  __syncthreads();
+  if (tid < 64) find_bin<2048>(S, false, top_p);
+  __syncthreads();
+  const uint32_t b2 = S.bin;
+  above += S.above;
+  const unsigned long long t2 = S.target;
+  __syncthreads();
+
+  for (int i = tid; i < 1024; i += kSelThreads) S.hist[i] = 0;
+  if (tid == 0) S.target = t2 - S.above;
+  __syncthreads();
+  const uint32_t pre = (b1 << 11) | b2;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const uint32_t k = okey(c[i]);
+    if (tid + kSelThreads * i < n && (k >> 10) == pre)
+      atomicAdd(&S.hist[k & 1023u], (unsigned long long)wfix(c[i], m));
+  }
+  __syncthreads();
+  if (tid < 64) find_bin<1024>(S, false, top_p);
+  __syncthreads();
+  const uint32_t kstar = (pre << 10) | S.bin;
+  above += S.above;
+  const unsigned long long wstar = wfix(okey_inv(kstar), m);
+  const unsigned long long need = target - above;
+  const unsigned long long r = (need + wstar - 1) / wstar;
+
+  const int wv = tid >> 6, ln = tid & 63;
+  unsigned long long carried = 0;
+  int nsel = 0;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    if (kSelThreads * i >= n) break;  // uniform
+    const int t = tid + kSelThreads * i;
+    const bool valid = t < n;
+    const uint32_t k = valid ? okey(c[i]) : 0u;
+    const bool tie = valid && k == kstar;
+    const int ntie = __syncthreads_count(tie);
+    unsigned long long rank = 0;
+    if (ntie) {
+      const unsigned long long bal = __ballot(tie);
+      if (ln == 0) S.wc[wv] = __popcll(bal);
+      __syncthreads();
+      int off = 0;
+      for (int j = 0; j < wv; ++j) off += S.wc[j];
+      __syncthreads();
+      rank = carried + off + __popcll(bal & ((1ull << ln) - 1ull));
+      carried += ntie;
+    }
+    const bool sel = valid && (k > kstar || (tie && rank < r));
+    if (valid) mk[t] = sel ? 1 : 0;
+    nsel += sel;
+  }
+  int v = nsel;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (ln == 0) S.red[wv] = v;
+  __syncthreads();
+  if (tid == 0) {
+    int tot = 0;
+    for (int j = 0; j < kSelWaves; ++j) tot += S.red[j];
+    count[bh] = tot;
+  }
+}
+
+bool calsel_fits(int max_cand) { return max_cand <= 16 * kSelThreads; }
+
+void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st) {
+  observe("k_calsel", st);
+  const dim3 grid(a.hkv, a.B), blk(kSelThreads);
+  if (max_cand <= 4 * kSelThreads)
+    hipLaunchKernelGGL(k_calsel<4>, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2,
+                       a.cap_stride, a.stats, a.top_p, a.mask, a.count);
+  else
+    hipLaunchKernelGGL(k_calsel<16>, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2,
+                       a.cap_stride, a.stats, a.top_p, a.mask, a.count);
+}
+
 void launch_calibrate(const SelectArgs& a, hipStream_t st) {
   observe("k_calibrate", st);
   hipLaunchKernelGGL(k_calibrate, dim3(a.hkv, a.B), dim3(256), 0, st, a.cand, a.metric, a.logit,

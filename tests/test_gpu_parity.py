@@ -72,24 +72,11 @@ def test_small_grid_all_heads_all_stages(gpu, i):
     rep = check_case(case, g, w.p)
     say(rep)
     check_all_heads_invariants(case, desc, g)
-    # the fused step gives the same tiers as the stage-by-stage calls, and
-    # the same attention up to float32 summation order
+    # the fused hardkv_step (its own launches) against the oracle too
     s = run_step(case, desc)
-    for f in ("k", "v", "pos", "count"):
-        a, b = getattr(s["tiers"], f), getattr(g["tiers"], f)
-        if f in ("k", "v", "pos"):
-            for bb in range(w.B):
-                for hh in range(w.Hkv):
-                    n = int(g["tiers"].count[bb, hh])
-                    assert torch.equal(a[bb, hh, :n], b[bb, hh, :n])
-        else:
-            assert torch.equal(a, b)
-    err = ((s["out"] - g["out"]).abs().amax(-1) / g["out"].abs().amax(-1).clamp_min(1e-30)).max()
-    assert err.item() < 1e-5, err.item()
-    for f in ("ksum", "vsum", "ccount"):
-        for bb in range(w.B):
-            nch = -(-max(w.T[bb] - w.W, 0) // w.C)
-            assert torch.equal(getattr(s["tiers"], f)[bb, :, :nch], getattr(g["tiers"], f)[bb, :, :nch])
+    check_all_heads_invariants(case, desc, s)
+    rep2 = check_case(case, s, w.p, stages=False)
+    say("step", rep2)
 
 
 def test_p_one_is_full_attention(gpu):
