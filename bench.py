@@ -207,6 +207,29 @@ def main():
     launches = {n: len(v) // args.steps for n, v in per_kernel.items()}
     print(f"[bench] step {ms_per_step:.3f} ms {kernel_ms}", file=sys.stderr, flush=True)
 
+    # the step captured once into a HIP graph and replayed (static shapes,
+    # no host synchronisation or allocation inside the step)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    del graph
+
     # the same loop without the observer (cross-check of the step time)
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     f0.record(stream)
@@ -268,6 +291,7 @@ def main():
         "step_algorithmic_gb": round(step_bytes / 1e9, 4),
         "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "step_ms_without_observer": round(plain_ms, 4),
+        "graph_replay_ms_per_step": round(graph_ms, 4),
         "device_copy_gbs": round(copy_gbs, 1),
         "kept_fraction": round(float(k.sum() / max(A.sum(), 1)), 4),
         "dtype_note": "bf16 q/K/V in HBM; float64 score accumulation, 2^-47 fixed-point "
