@@ -28,6 +28,15 @@ and the lifecycle invariants of the Cascade Cache.  The rule chosen for
 calibrating a non-logit metric (moment matching, see ``calibrate_head``) is a
 reading of the pages; its implementation is pinned by a hand-worked example
 and invariants, the rule itself is not fixed by the pages.
+
+The rewrite-versus-sparse-loading policy (``mti_head``, ``plan_head``) and
+the reuse of a selection over later steps (``reuse_head``) are readings of
+section 2.C, "Techniques" and "Trade-off Management", which name the
+Memory-Time Integral and the thresholds L_lower / L_upper without a formula
+(tests/test_oracle_policy.py: a worked example, a break-even closed form
+derived from the integral, degenerate cases, threshold precedence, and
+reductions of reuse attention to full softmax attention).  The integral's
+cost model itself is this reading, not the pages'.
 """
 from __future__ import annotations
 
@@ -430,3 +439,93 @@ def lifecycle_step(st: HeadState, q_group, k_new, v_new, p: float, metric: int):
                       st.ksum, st.vsum, st.cnt)
     return out, {"n_candidates": n_before, "k": sel.k, "ell": ell, "s": s,
                  "cal": cal, "sel": sel}
+
+
+# ---------------------------------------------------------------------------
+# Rewrite versus Sparse Loading (section 2.C, "Techniques" and "Trade-off
+# Management"): a selection is either rewritten into contiguous slots or
+# left in place and loaded through its index; a Memory-Time Integral, with
+# the budget thresholds L_lower and L_upper, decides per head.
+# ---------------------------------------------------------------------------
+POLICY_REWRITE = 0   # every head rewritten
+POLICY_SPARSE = 1    # every head sparse-loaded
+POLICY_MTI = 2       # thresholds, then the memory-time integral
+
+MODE_REWRITE = 0
+MODE_SPARSE = 1
+
+
+def mti_head(A: int, k: int, W: int, horizon: int):
+    """Memory-time integrals of serving one selection for `horizon` steps.
+
+    The pages name the metric and what it balances (the one-off cost of the
+    rewrite against the per-step gain) but give no formula.  Reading: the
+    integral of the head's KV footprint over the time the steps take, both in
+    units of one K or V row (the path is bandwidth-bound, so a step takes time
+    in proportion to the rows it moves).  A horizon of N steps is the
+    selection step plus N - 1 steps that reuse its tiers.
+
+      footprint, sparse loading : A + W   every aged row stays where it is
+      footprint, rewritten      : k + W   the kept rows only (the originals of
+                                          the aged rows can be released)
+      selection step, either    : 3A + 2W rows read (K to score, K and V to
+                                          pool, the window's K and V)
+      the rewrite's own cost    : 2k      rows written (K and V of each kept token)
+      reuse step, either        : 2(k + W) rows read
+
+    While the rewrite runs both copies of the kept rows exist (footprint
+    A + W + k).  The window's growth during the horizon is the same in both
+    modes and is left out.  Exact integers: (mti_rewrite, mti_sparse).
+    """
+    if min(A, k, W) < 0 or k > A or horizon < 1:
+        raise ValueError("need 0 <= k <= A, W >= 0, horizon >= 1")
+    foot_sparse = A + W
+    foot_rewrite = k + W
+    select_rows = 3 * A + 2 * W
+    rewrite_rows = 2 * k
+    reuse_rows = 2 * (k + W)
+    mti_sparse = foot_sparse * select_rows + (horizon - 1) * foot_sparse * reuse_rows
+    mti_rewrite = ((foot_sparse + k) * (select_rows + rewrite_rows)
+                   + (horizon - 1) * foot_rewrite * reuse_rows)
+    return mti_rewrite, mti_sparse
+
+
+def plan_head(A: int, k: int, W: int, policy: int, horizon: int = 1,
+              l_lower: int = 0, l_upper: int = 2 ** 31 - 1) -> int:
+    """Rewrite (0) or sparse loading (1) for one head's selection.
+
+    Reading of the budget thresholds: a budget k at or below L_lower is
+    always rewritten (small, cheap to move, frees the most memory); one at or
+    above L_upper is always loaded in place (a near-complete selection gains
+    little from moving); in between the smaller memory-time integral wins,
+    a tie going to sparse loading (nothing is moved).
+    """
+    if policy == POLICY_REWRITE:
+        return MODE_REWRITE
+    if policy == POLICY_SPARSE:
+        return MODE_SPARSE
+    if policy != POLICY_MTI:
+        raise ValueError("unknown policy")
+    if k <= l_lower:
+        return MODE_REWRITE
+    if k >= l_upper:
+        return MODE_SPARSE
+    mr, ms = mti_head(A, k, W, horizon)
+    return MODE_REWRITE if mr < ms else MODE_SPARSE
+
+
+def reuse_head(q_group, K, V, T_now: int, sel: HeadResult):
+    """Attention at a later decode step that reuses an earlier selection.
+
+    Reading: the tiers of the selection step serve the following steps
+    unchanged; the tokens that left the W-window after the selection are
+    not yet scored and stay dense, so at context length T_now the dense tier
+    is [A_sel, T_now).  The kept rows are the cache rows at the selection's
+    positions -- rewritten copies or, with sparse loading, the originals,
+    which hold the same values.
+    """
+    if T_now < sel.A:
+        raise ValueError("the context only grows")
+    return attend_head(q_group, K[sel.A:T_now], V[sel.A:T_now],
+                       np.asarray(K)[sel.pos], np.asarray(V)[sel.pos],
+                       sel.ksum, sel.vsum, sel.cnt)
