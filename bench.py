@@ -49,6 +49,8 @@ def parse():
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--block-size", type=int, default=None,
                     help="override the cache layout (0 = contiguous)")
+    ap.add_argument("--no-amortization", action="store_true",
+                    help="skip the selection-reuse timings")
     return ap.parse_args()
 
 
@@ -154,6 +156,89 @@ def cpu_baseline(case, w, seconds):
                       f"over all {len(heads)} heads of the same workload, {spent:.1f} s of "
                       f"single-thread oracle time; input copies to host not timed",
             "ms_per_step": round(step_s * 1e3, 1)}
+
+
+def time_ms(fn, steps, warmup=2):
+    import torch
+    for _ in range(warmup):
+        fn()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def amortization(w, case, steps, horizons=(1, 2, 4, 8, 16, 32)):
+    """Serving one selection over several decode steps (section 2.C,
+    "Trade-off Management"; section 4, "Scalability": the rewrite's cost is
+    amortized within a few steps).  Times, per step of one layer:
+      select  hardkv_step (every head rewritten) / hardkv_step_policy with
+              every head sparse-loaded;
+      reuse   hardkv_decode_attn over those tiers (window W: the cost of a
+              reuse step up to one more dense row per step since the selection);
+      dense   hardkv_decode_attn over the whole context with no selection
+              (window = context), the uncompressed reference;
+    and the average step time over a horizon of N steps (one selection, N - 1
+    reuses), the first N where it beats dense attention, and how many heads
+    the memory-time-integral policy sends to each mode."""
+    import numpy as np
+    import torch
+    from decode_kv_cache_head_amd import hardkv as H
+    dev = case.q.device
+    desc = H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.W, w.C, w.p, case.ctx_cap,
+                       w.block_size, case.max_blocks)
+    ws = H.alloc_workspace(desc, dev)
+    cache = H.cache_struct(case.k, case.v, case.ctx_len, case.block_table)
+    out = torch.empty((w.B, w.Hq, w.d), device=dev)
+    t_rw = H.alloc_tiers(desc, dev, mode=True)
+    t_sp = H.alloc_tiers(desc, dev, mode=True)
+    sparse = H.policy(H.POLICY_SPARSE)
+    sel_rw = time_ms(lambda: H.step(desc, case.q, cache, case.metric, t_rw, out, ws), steps)
+    sel_sp = time_ms(lambda: H.step_policy(desc, sparse, case.q, cache, case.metric, t_sp, out,
+                                           ws), steps)
+    reuse_rw = time_ms(lambda: H.decode_attn(desc, case.q, cache, t_rw, out, ws), steps)
+    reuse_sp = time_ms(lambda: H.decode_attn(desc, case.q, cache, t_sp, out, ws), steps)
+    d_dense = H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, case.ctx_cap, w.C, w.p, case.ctx_cap,
+                          w.block_size, case.max_blocks, desc.sparse_cap, desc.chunk_cap)
+    ws_dense = H.alloc_workspace(d_dense, dev)
+    t_none = H.Tiers(t_rw.k, t_rw.v, t_rw.pos, torch.zeros_like(t_rw.count), t_rw.ksum,
+                     t_rw.vsum, t_rw.ccount)
+    dense = time_ms(lambda: H.decode_attn(d_dense, case.q, cache, t_none, out, ws_dense), steps)
+    A = np.maximum(np.array(w.T) - w.W, 0)
+    k = t_rw.count.cpu().numpy()
+
+    def avg(sel, reuse, n):
+        return (sel + (n - 1) * reuse) / n
+
+    def breakeven(sel, reuse):
+        if reuse >= dense:
+            return None
+        return int(math.floor((sel - dense) / (dense - reuse))) + 2 if sel > dense else 1
+
+    mti = {}
+    t_mti = H.alloc_tiers(desc, dev, mode=True)
+    for n in horizons:
+        H.step_policy(desc, H.policy(H.POLICY_MTI, n), case.q, cache, case.metric, t_mti, out, ws)
+        torch.cuda.synchronize()
+        mti[str(n)] = int(t_mti.mode.sum().item())
+    return {
+        "kept_fraction": round(float(k.sum() / max(int(A.sum()) * w.Hkv, 1)), 4),
+        "median_kept_tokens": int(np.median(k)),
+        "select_ms": {"rewrite": round(sel_rw, 4), "sparse": round(sel_sp, 4)},
+        "reuse_ms": {"rewrite": round(reuse_rw, 4), "sparse": round(reuse_sp, 4)},
+        "dense_attention_ms": round(dense, 4),
+        "avg_step_ms": {str(n): {"rewrite": round(avg(sel_rw, reuse_rw, n), 4),
+                                 "sparse": round(avg(sel_sp, reuse_sp, n), 4)}
+                        for n in horizons},
+        "breakeven_horizon_vs_dense": {"rewrite": breakeven(sel_rw, reuse_rw),
+                                       "sparse": breakeven(sel_sp, reuse_sp)},
+        "mti_sparse_heads_by_horizon": mti,
+        "heads": int(w.B * w.Hkv),
+    }
 
 
 def main():
@@ -297,6 +382,14 @@ def main():
         "dtype_note": "bf16 q/K/V in HBM; float64 score accumulation, 2^-47 fixed-point "
                       "top-p masses, float32 attention",
     }
+    if not args.no_amortization:
+        print("[bench] selection reuse", file=sys.stderr, flush=True)
+        am = {w.name: amortization(w, case, args.steps)}
+        if args.workload == "qwen8b_b32_16k_paged" and args.block_size is None:
+            wp = S.workload("qwen8b_b32_16k_paged_peaked")
+            am[wp.name] = amortization(wp, S.make_case(wp, dev), args.steps)
+            torch.cuda.empty_cache()
+        res["amortization"] = am
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(case, w, args.cpu_seconds)

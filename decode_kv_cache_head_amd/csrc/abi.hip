@@ -18,7 +18,7 @@ void hk::observe(const char* kernel, hipStream_t st) {
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0
 
 int log2i(int v) {
   int l = 0;
@@ -151,6 +151,8 @@ SelectArgs select_args(const hardkv_desc* d, const Cand& cand, const int8_t* met
   a.top_p = d->top_p;
   a.mask = mask;
   a.count = count;
+  a.mode = nullptr;
+  a.policy = hardkv_policy{HARDKV_POLICY_REWRITE, 1, 0, 0};
   return a;
 }
 
@@ -177,6 +179,7 @@ CompactArgs compact_args(const hardkv_desc* d, const Layout& L, char* ws, const 
   a.vsum = t->vsum;
   a.ccount = t->ccount;
   a.chunk_stride = d->chunk_cap;
+  a.mode = t->mode;
   a.G = d->num_q_heads / d->num_kv_heads;
   a.hq = d->num_q_heads;
   a.q = nullptr;
@@ -202,6 +205,8 @@ AttnArgs attn_args(const hardkv_desc* d, const Layout& L, char* ws, const void* 
   a.sv = region_rows(d, t->v, d->sparse_cap);
   a.count = t->count;
   a.sparse_cap = d->sparse_cap;
+  a.mode = t->mode;
+  a.pos = t->pos;
   a.ksum = t->ksum;
   a.vsum = t->vsum;
   a.ccount = t->ccount;
@@ -222,11 +227,63 @@ bool cache_ok(const hardkv_desc* d, const hardkv_cache* c) {
   return c && c->k && c->v && c->ctx_len && (d->block_size == 0 || c->block_table);
 }
 
+bool policy_ok(const hardkv_policy* p) {
+  return p && (p->kind == HARDKV_POLICY_REWRITE || p->kind == HARDKV_POLICY_SPARSE ||
+               p->kind == HARDKV_POLICY_MTI) &&
+         p->horizon >= 1;
+}
+
 int common_checks(const hardkv_desc* d, void* ws, size_t ws_bytes) {
   const int rc = validate(d);
   if (rc != HARDKV_OK) return rc;
   if (!ws || ws_bytes < layout(d).total) return HARDKV_ERR_WORKSPACE;
   return HARDKV_OK;
+}
+
+// score -> calibrate + select (+ plan) -> compact (+ attention over the kept
+// rows) -> attention.  Each head's choice goes to tiers->mode when that is
+// given.
+void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
+              const hardkv_cache* cache, const int8_t* metric, const hardkv_tiers* tiers,
+              float* out, void* ws, hipStream_t st) {
+  const Layout L = layout(d);
+  char* w = (char*)ws;
+  const hardkv_tiers& t = *tiers;
+  const Rows kr = cache_rows(d, cache->k, cache->block_table);
+  const Rows vr = cache_rows(d, cache->v, cache->block_table);
+  const Cand cand = aged_cand(d, cache->ctx_len);
+  float* logit = (float*)(w + L.logit);
+  float* l2 = (float*)(w + L.l2);
+  double* stats = (double*)(w + L.stats);
+  uint8_t* mask = (uint8_t*)(w + L.mask);
+  int32_t* count = (int32_t*)(w + L.count);
+  hipGetLastError();
+  do_score(d, L, w, q, kr, cand, max_aged(d), metric, logit, l2, st);
+  SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
+  sa.mode = t.mode;
+  sa.policy = *policy;
+  if (calsel_fits(max_aged(d))) {
+    launch_calsel(sa, max_aged(d), st);
+  } else {
+    launch_calibrate(sa, st);
+    launch_select(sa, st);
+  }
+  CompactArgs ca = compact_args(d, L, w, kr, vr, cand, max_aged(d), mask, &t);
+  AttnArgs a = attn_args(d, L, w, q, &t, out);
+  a.dk = kr;
+  a.dv = vr;
+  a.ctx_len = cache->ctx_len;
+  a.ring = false;
+  if (compact_fusable(d->chunk)) {
+    // attention over the kept rows happens inside the compaction pass; the
+    // attention launch then covers the dense and condensed tiers only
+    ca.q = q;
+    launch_compact_attn(ca, st);
+    a.fused_tt = compact_tile(d->chunk);
+  } else {
+    launch_compact(ca, st);
+  }
+  launch_attn(a, st);
 }
 
 }  // namespace
@@ -329,48 +386,41 @@ int hardkv_decode_attn(const hardkv_desc* d, const void* q, const hardkv_cache* 
   return launched();
 }
 
+int hardkv_plan(const hardkv_desc* d, const hardkv_policy* policy, const int32_t* ctx_len,
+                const int32_t* count, uint8_t* mode, hardkv_stream_t stream) {
+  const int rc = validate(d);
+  if (rc) return rc;
+  if (!policy_ok(policy) || !ctx_len || !count || !mode) return HARDKV_ERR_INVALID_ARG;
+  SelectArgs a = select_args(d, aged_cand(d, ctx_len), nullptr, nullptr, nullptr, nullptr,
+                             nullptr, (int32_t*)count);
+  a.mode = mode;
+  a.policy = *policy;
+  hipGetLastError();
+  launch_plan(a, (hipStream_t)stream);
+  return launched();
+}
+
 int hardkv_step(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
                 const int8_t* metric, const hardkv_tiers* tiers, float* out, void* ws,
                 size_t ws_bytes, hardkv_stream_t stream) {
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
   if (!q || !cache_ok(d, cache) || !tiers_ok(tiers) || !out) return HARDKV_ERR_INVALID_ARG;
-  const Layout L = layout(d);
-  char* w = (char*)ws;
-  hipStream_t st = (hipStream_t)stream;
-  const Rows kr = cache_rows(d, cache->k, cache->block_table);
-  const Rows vr = cache_rows(d, cache->v, cache->block_table);
-  const Cand cand = aged_cand(d, cache->ctx_len);
-  float* logit = (float*)(w + L.logit);
-  float* l2 = (float*)(w + L.l2);
-  double* stats = (double*)(w + L.stats);
-  uint8_t* mask = (uint8_t*)(w + L.mask);
-  int32_t* count = (int32_t*)(w + L.count);
-  hipGetLastError();
-  do_score(d, L, w, q, kr, cand, max_aged(d), metric, logit, l2, st);
-  const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
-  if (calsel_fits(max_aged(d))) {
-    launch_calsel(sa, max_aged(d), st);
-  } else {
-    launch_calibrate(sa, st);
-    launch_select(sa, st);
-  }
-  CompactArgs ca = compact_args(d, L, w, kr, vr, cand, max_aged(d), mask, tiers);
-  AttnArgs a = attn_args(d, L, w, q, tiers, out);
-  a.dk = kr;
-  a.dv = vr;
-  a.ctx_len = cache->ctx_len;
-  a.ring = false;
-  if (compact_fusable(d->chunk)) {
-    // attention over the kept rows happens inside the compaction pass; the
-    // attention launch then covers the dense and condensed tiers only
-    ca.q = q;
-    launch_compact_attn(ca, st);
-    a.fused_tt = compact_tile(d->chunk);
-  } else {
-    launch_compact(ca, st);
-  }
-  launch_attn(a, st);
+  const hardkv_policy rewrite_all{HARDKV_POLICY_REWRITE, 1, 0, 0};
+  run_step(d, &rewrite_all, q, cache, metric, tiers, out, ws, (hipStream_t)stream);
+  return launched();
+}
+
+int hardkv_step_policy(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
+                       const hardkv_cache* cache, const int8_t* metric,
+                       const hardkv_tiers* tiers, float* out, void* ws, size_t ws_bytes,
+                       hardkv_stream_t stream) {
+  int rc = common_checks(d, ws, ws_bytes);
+  if (rc) return rc;
+  if (!policy_ok(policy) || !q || !cache_ok(d, cache) || !tiers_ok(tiers) || !tiers->mode ||
+      !out)
+    return HARDKV_ERR_INVALID_ARG;
+  run_step(d, policy, q, cache, metric, tiers, out, ws, (hipStream_t)stream);
   return launched();
 }
 
@@ -381,7 +431,7 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   if (rc) return rc;
   if (d->block_size != 0 || d->dense_window < 1) return HARDKV_ERR_INVALID_ARG;
   if (!q || !k_new || !v_new || !s || !s->ring_k || !s->ring_v || !s->seq_len ||
-      !tiers_ok(&s->tiers) || !out)
+      !tiers_ok(&s->tiers) || s->tiers.mode || !out)
     return HARDKV_ERR_INVALID_ARG;
   const Layout L = layout(d);
   char* w = (char*)ws;

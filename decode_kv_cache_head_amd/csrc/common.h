@@ -214,6 +214,27 @@ struct QPiece<bf16_t, bf16_t, 8> {
   }
 };
 
+// ------------------------------------------------------------ policy -----
+// Rewrite (0) or sparse loading (1) for a head with A aged tokens, k kept,
+// window W: budget thresholds first, then the smaller memory-time integral
+// over the horizon, in K/V rows, in exact 128-bit integers (the formulas
+// are documented with hardkv_policy).
+__host__ __device__ inline uint8_t plan_mode(const hardkv_policy& p, int A, int k, int W) {
+  if (p.kind == HARDKV_POLICY_REWRITE) return HARDKV_MODE_REWRITE;
+  if (p.kind == HARDKV_POLICY_SPARSE) return HARDKV_MODE_SPARSE;
+  if (k <= p.l_lower) return HARDKV_MODE_REWRITE;
+  if (k >= p.l_upper) return HARDKV_MODE_SPARSE;
+  typedef unsigned __int128 u128;
+  const u128 a = (u128)(uint32_t)A, kk = (u128)(uint32_t)k, w = (u128)(uint32_t)W;
+  const u128 reuse = (u128)(uint32_t)(p.horizon - 1);
+  const u128 foot_sparse = a + w, foot_rewrite = kk + w;
+  const u128 select_rows = 3 * a + 2 * w, rewrite_rows = 2 * kk, reuse_rows = 2 * (kk + w);
+  const u128 mti_sparse = foot_sparse * select_rows + reuse * foot_sparse * reuse_rows;
+  const u128 mti_rewrite =
+      (foot_sparse + kk) * (select_rows + rewrite_rows) + reuse * foot_rewrite * reuse_rows;
+  return mti_rewrite < mti_sparse ? HARDKV_MODE_REWRITE : HARDKV_MODE_SPARSE;
+}
+
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 }  // namespace hk

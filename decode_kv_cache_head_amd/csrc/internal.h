@@ -82,12 +82,16 @@ struct SelectArgs {
   float top_p;
   uint8_t* mask;        // [B][Hkv][cap_stride]
   int32_t* count;       // [B][Hkv]
+  uint8_t* mode;        // [B][Hkv] rewrite / sparse choice, written with count; may be null
+  hardkv_policy policy;
 };
 void launch_calibrate(const SelectArgs& a, hipStream_t st);
 void launch_select(const SelectArgs& a, hipStream_t st);
 // calibrate + select in one launch, scores in registers (max_cand <= 16384)
 bool calsel_fits(int max_cand);
 void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st);
+// mode[b][h] from count[b][h] and the candidate count
+void launch_plan(const SelectArgs& a, hipStream_t st);
 
 // Tile of the single-step compaction: whole chunks, about 1024 tokens
 // (one chunk when a chunk is longer), processed in 64-row sub-tiles.
@@ -111,6 +115,7 @@ struct CompactArgs {
   float* vsum;
   int32_t* ccount;
   int chunk_stride;
+  const uint8_t* mode;  // [B][Hkv]; HARDKV_MODE_SPARSE heads skip the row copies; may be null
   // fused attention over the kept rows (launch_compact_attn only)
   int G, hq;
   const void* q;        // [B][Hq][D]
@@ -134,6 +139,10 @@ struct AttnArgs {
   Rows sk, sv;
   const int32_t* count;
   int sparse_cap;
+  // sparse loading: heads whose mode byte is HARDKV_MODE_SPARSE read their
+  // kept rows from the dense-tier rows (the cache) at pos; may be null
+  const uint8_t* mode;
+  const int32_t* pos;
   // condensed tier
   const float* ksum;
   const float* vsum;

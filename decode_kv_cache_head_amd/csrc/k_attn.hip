@@ -12,6 +12,10 @@
 // partial (max, sum, numerator) per query head; k_attn_merge joins the
 // partials of every tile.
 //
+// Heads served by sparse loading (mode byte HARDKV_MODE_SPARSE) read their
+// sparse entries from the cache rows at the tier's positions instead of the
+// rewritten slots (section 2.C, "Techniques").
+//
 // Condensed entries hold float32 sums and a count n: their logit is
 // q.(ksum / n) / sqrt(d) + ln n and their value vsum / n.
 #include "internal.h"
@@ -66,9 +70,12 @@ __device__ inline TileCounts tile_counts(const AttnArgs& a, int b, int h) {
 // its rows first, then scores, then rescales the running (m, l, o) to the
 // new maximum and accumulates p * v.  CHUNK: float32 sums with counts.
 // Lanes 0..LPR-1 end with the full numerator (EPL elements each).
-template <typename E, int D, int G, typename QT, bool CHUNK, bool P>
+// IDX: entry r is row idx[r0 + r] of kr / vr (clamped to [0, idx_max]) --
+// sparse loading of kept rows from the cache.
+template <typename E, int D, int G, typename QT, bool CHUNK, bool P, bool IDX>
 __device__ inline void wave_attn(const QT* __restrict__ qg, const Rows& kr, const Rows& vr, int b,
-                                 int h, int r0, int wn, const int32_t* __restrict__ cc, float scale,
+                                 int h, int r0, int wn, const int32_t* __restrict__ cc,
+                                 const int32_t* __restrict__ idx, int idx_max, float scale,
                                  float (&m)[G], float (&l)[G], float (&o)[G][Lay<E, D>::EPL]) {
   using L = Lay<E, D>;
   constexpr int LPR = L::LPR, EPL = L::EPL, RPI = L::RPI;
@@ -88,13 +95,22 @@ __device__ inline void wave_attn(const QT* __restrict__ qg, const Rows& kr, cons
   }
   for (int base = 0; base < wn; base += RR) {
     v4u kb[IT], vb[IT];
-    int cnt[IT];
+    int cnt[IT], row[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int r = min(base + it * RPI + grp, wn - 1);  // in bounds; masked below
-      kb[it] = *(const v4u*)(kr.template row<P>(b, h, r0 + r) + piece * 16);
-      vb[it] = *(const v4u*)(vr.template row<P>(b, h, r0 + r) + piece * 16);
-      if (CHUNK) cnt[it] = cc[r0 + r];
+      if (IDX) {
+        const int t = idx[r0 + r];
+        row[it] = t < 0 ? 0 : (t > idx_max ? idx_max : t);
+      } else {
+        row[it] = r0 + r;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      kb[it] = *(const v4u*)(kr.template row<P>(b, h, row[it]) + piece * 16);
+      vb[it] = *(const v4u*)(vr.template row<P>(b, h, row[it]) + piece * 16);
+      if (CHUNK) cnt[it] = cc[row[it]];
     }
     float s[IT][G];
     float mr[G];
@@ -149,17 +165,18 @@ __device__ inline void wave_attn(const QT* __restrict__ qg, const Rows& kr, cons
   }
 }
 
-template <typename E, int D, int G, typename QT, bool CHUNK, bool P>
+template <typename E, int D, int G, typename QT, bool CHUNK, bool P, bool IDX = false>
 __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr, const Rows& vr,
                                  int b, int h, int r0, int nrows, const int32_t* cc, float* s_m,
-                                 float* s_l, float* s_o, float* part_out) {
+                                 float* s_l, float* s_o, float* part_out,
+                                 const int32_t* idx = nullptr, int idx_max = 0) {
   using L = Lay<E, D>;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int wn = nrows - w * 64;
   wn = wn < 0 ? 0 : (wn > 64 ? 64 : wn);
   float m[G], l[G], o[G][L::EPL];
-  wave_attn<E, D, G, QT, CHUNK, P>(qg, kr, vr, b, h, r0 + w * 64, wn, cc, (float)a.scale, m, l,
-                                o);
+  wave_attn<E, D, G, QT, CHUNK, P, IDX>(qg, kr, vr, b, h, r0 + w * 64, wn, cc, idx, idx_max,
+                                        (float)a.scale, m, l, o);
   if (lane < L::LPR) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -220,8 +237,16 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
                                  part_out);
   } else if (x < tc.ntd + tc.nts) {
     const int r0 = (x - tc.ntd) * kAttnTile;
-    tile_attn<T, D, G, T, false, false>(a, qg, a.sk, a.sv, b, h, r0, min(kAttnTile, tc.ns - r0),
-                                 nullptr, s_m, s_l, s_o, part_out);
+    if (a.mode && a.mode[bh] == HARDKV_MODE_SPARSE) {
+      // sparse loading: the kept rows stay in the cache, found through pos
+      tile_attn<T, D, G, T, false, P, true>(a, qg, a.dk, a.dv, b, h, r0,
+                                            min(kAttnTile, tc.ns - r0), nullptr, s_m, s_l, s_o,
+                                            part_out, a.pos + bh * a.sparse_cap, a.ctx_cap - 1);
+    } else {
+      tile_attn<T, D, G, T, false, false>(a, qg, a.sk, a.sv, b, h, r0,
+                                          min(kAttnTile, tc.ns - r0), nullptr, s_m, s_l, s_o,
+                                          part_out);
+    }
   } else {
     const int r0 = (x - tc.ntd - tc.nts) * kAttnTile;
     Rows ck{(const char*)a.ksum, nullptr, a.chunk_cap, a.hkv, 0, 0, D * 4};

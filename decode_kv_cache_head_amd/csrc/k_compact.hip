@@ -14,6 +14,10 @@
 // one thread per (tensor, dim), in ascending position order.  Sequences with
 // no candidate tokens write count = 0 from the first tile slot.
 //
+// Sparse Loading (section 2.C, "Techniques"): a head whose mode byte says
+// HARDKV_MODE_SPARSE gets its positions, count and chunks but no row copies;
+// attention later loads its kept rows from the cache through the positions.
+//
 // Lifecycle (in place): k_compact_inplace runs one workgroup per (b, h) that
 // sweeps its pool in 64-row sub-tiles in order.  Every sub-tile is read
 // completely into LDS before any of its rows is written back, and a kept row
@@ -66,6 +70,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
     return;
   }
   const int tend = min(t0 + TT, n);
+  const bool copy_rows = a.mode == nullptr || a.mode[bh] == HARDKV_MODE_REWRITE;
   const uint8_t* mk = a.mask + bh * a.cap_stride;
   char* ok = a.out_k + bh * a.cap_stride * RB;
   char* ov = a.out_v + bh * a.cap_stride * RB;
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
-      if (r < nr && s_sel[r])
+      if (copy_rows && r < nr && s_sel[r])
         *(v4u*)((tsr ? ov : ok) + (int64_t)s_rank[r] * RB + c * 16) =
             *(const v4u*)((tsr ? sv : sk) + r * RB + c * 16);
     }
@@ -181,6 +186,7 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
     return;
   }
   const int nrows = min(TT, n - t0);
+  const bool copy_rows = a.mode == nullptr || a.mode[bh] == HARDKV_MODE_REWRITE;
   const uint8_t* mk = a.mask + bh * a.cap_stride;
   char* ok = a.out_k + bh * a.cap_stride * RB;
   char* ov = a.out_v + bh * a.cap_stride * RB;
@@ -302,8 +308,10 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
       if (r < nrows) {
         const int rk = s_rank[r];
         if (rk >= 0) {
-          *(v4u*)(ok + (int64_t)rk * RB + c * 16) = buf[i];
-          *(v4u*)(ov + (int64_t)rk * RB + c * 16) = buf[RPT + i];
+          if (copy_rows) {
+            *(v4u*)(ok + (int64_t)rk * RB + c * 16) = buf[i];
+            *(v4u*)(ov + (int64_t)rk * RB + c * 16) = buf[RPT + i];
+          }
         } else {
           float f[EPC];
           Elt<T>::unpack(buf[i], f);

@@ -167,25 +167,38 @@ __device__ inline void find_bin(SelShared& S, bool from_total, float p) {
   if (from_total && lane == 0) S.target = target;
 }
 
+// Where a selection's size goes: count[bh] = k and, when a mode array is
+// given, the head's rewrite / sparse-loading choice for (A = n, k).
+struct CountOut {
+  int32_t* count;
+  uint8_t* mode;
+  hardkv_policy pol;
+  int W;
+  __device__ inline void put(int64_t bh, int n, int k) const {
+    count[bh] = k;
+    if (mode) mode[bh] = plan_mode(pol, n, k, W);
+  }
+};
+
 __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t* __restrict__ metric,
                                                         const float* __restrict__ logit,
                                                         const float* __restrict__ l2,
                                                         int64_t cap_stride,
                                                         const double* __restrict__ stats,
                                                         float top_p, uint8_t* __restrict__ mask,
-                                                        int32_t* __restrict__ count) {
+                                                        CountOut co) {
   __shared__ SelShared S;
   const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
   const int n = cand.n(b, h);
   const int64_t bh = (int64_t)b * hkv + h;
   uint8_t* mk = mask + bh * cap_stride;
   if (n == 0) {
-    if (tid == 0) count[bh] = 0;
+    if (tid == 0) co.put(bh, n, 0);
     return;
   }
   if (!(top_p < 1.0f)) {
     for (int t = tid; t < n; t += kSelThreads) mk[t] = 1;
-    if (tid == 0) count[bh] = n;
+    if (tid == 0) co.put(bh, n, n);
     return;
   }
   const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
@@ -280,7 +293,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   if (tid == 0) {
     int tot = 0;
     for (int i = 0; i < kSelWaves; ++i) tot += S.red[i];
-    count[bh] = tot;
+    co.put(bh, n, tot);
   }
 }
 
@@ -297,7 +310,7 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
                                                         int64_t cap_stride,
                                                         double* __restrict__ stats, float top_p,
                                                         uint8_t* __restrict__ mask,
-                                                        int32_t* __restrict__ count) {
+                                                        CountOut co) {
   __shared__ SelShared S;
   __shared__ double shd[kSelWaves];
   __shared__ float shf[kSelWaves];
@@ -313,7 +326,7 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
       o[1] = is_l2 ? 0.0 : 1.0;
       o[2] = 0.0;
       o[3] = 0.0;
-      count[bh] = 0;
+      co.put(bh, n, 0);
     }
     return;
   }
@@ -392,7 +405,7 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
 #pragma unroll
     for (int i = 0; i < NPT; ++i)
       if (tid + kSelThreads * i < n) mk[tid + kSelThreads * i] = 1;
-    if (tid == 0) count[bh] = n;
+    if (tid == 0) co.put(bh, n, n);
     return;
   }
   if (tid < 64) find_bin<2048>(S, true, top_p);
@@ -472,8 +485,26 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   if (tid == 0) {
     int tot = 0;
     for (int j = 0; j < kSelWaves; ++j) tot += S.red[j];
-    count[bh] = tot;
+    co.put(bh, n, tot);
   }
+}
+
+static CountOut count_out(const SelectArgs& a) { return CountOut{a.count, a.mode, a.policy, a.cand.W}; }
+
+__global__ __launch_bounds__(256) void k_plan(Cand cand, int B, const int32_t* __restrict__ count,
+                                              uint8_t* __restrict__ mode, hardkv_policy pol) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * cand.hkv) return;
+  const int n = cand.n(i / cand.hkv, i % cand.hkv);
+  int k = count[i];
+  k = k < 0 ? 0 : (k > n ? n : k);
+  mode[i] = plan_mode(pol, n, k, cand.W);
+}
+
+void launch_plan(const SelectArgs& a, hipStream_t st) {
+  observe("k_plan", st);
+  hipLaunchKernelGGL(k_plan, dim3(ceil_div((int64_t)a.B * a.hkv, 256)), dim3(256), 0, st, a.cand,
+                     a.B, a.count, a.mode, a.policy);
 }
 
 bool calsel_fits(int max_cand) { return max_cand <= 16 * kSelThreads; }
@@ -483,10 +514,10 @@ void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st) {
   const dim3 grid(a.hkv, a.B), blk(kSelThreads);
   if (max_cand <= 4 * kSelThreads)
     hipLaunchKernelGGL(k_calsel<4>, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2,
-                       a.cap_stride, a.stats, a.top_p, a.mask, a.count);
+                       a.cap_stride, a.stats, a.top_p, a.mask, count_out(a));
   else
     hipLaunchKernelGGL(k_calsel<16>, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2,
-                       a.cap_stride, a.stats, a.top_p, a.mask, a.count);
+                       a.cap_stride, a.stats, a.top_p, a.mask, count_out(a));
 }
 
 void launch_calibrate(const SelectArgs& a, hipStream_t st) {
@@ -498,7 +529,7 @@ void launch_calibrate(const SelectArgs& a, hipStream_t st) {
 void launch_select(const SelectArgs& a, hipStream_t st) {
   observe("k_select", st);
   hipLaunchKernelGGL(k_select, dim3(a.hkv, a.B), dim3(kSelThreads), 0, st, a.cand, a.metric,
-                     a.logit, a.l2, a.cap_stride, (const double*)a.stats, a.top_p, a.mask, a.count);
+                     a.logit, a.l2, a.cap_stride, (const double*)a.stats, a.top_p, a.mask, count_out(a));
 }
 
 }  // namespace hk

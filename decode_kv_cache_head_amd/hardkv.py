@@ -20,6 +20,9 @@ LIB_PATH = os.path.join(HERE, "libhardkv.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 METRIC_QK, METRIC_L2 = 0, 1
+MODE_REWRITE, MODE_SPARSE = 0, 1
+POLICY_REWRITE, POLICY_SPARSE, POLICY_MTI = 0, 1, 2
+INT32_MAX = 2 ** 31 - 1
 
 _lib = None
 
@@ -49,7 +52,13 @@ class Cache(ctypes.Structure):
 class TiersC(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
                 ("count", ctypes.c_void_p), ("ksum", ctypes.c_void_p),
-                ("vsum", ctypes.c_void_p), ("ccount", ctypes.c_void_p)]
+                ("vsum", ctypes.c_void_p), ("ccount", ctypes.c_void_p),
+                ("mode", ctypes.c_void_p)]
+
+
+class Policy(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("horizon", ctypes.c_int32),
+                ("l_lower", ctypes.c_int32), ("l_upper", ctypes.c_int32)]
 
 
 class StateC(ctypes.Structure):
@@ -77,6 +86,11 @@ _SIGS = {
                             ctypes.POINTER(TiersC), _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "hardkv_step": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(Cache), _P,
                      ctypes.POINTER(TiersC), _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hardkv_plan": ([ctypes.POINTER(Desc), ctypes.POINTER(Policy), _P, _P, _P, _P],
+                    ctypes.c_int),
+    "hardkv_step_policy": ([ctypes.POINTER(Desc), ctypes.POINTER(Policy), _P,
+                            ctypes.POINTER(Cache), _P, ctypes.POINTER(TiersC), _P, _P,
+                            ctypes.c_size_t, _P], ctypes.c_int),
     "hardkv_step_inplace": ([ctypes.POINTER(Desc), _P, _P, _P, _P, ctypes.POINTER(StateC), _P,
                              _P, ctypes.c_size_t, _P], ctypes.c_int),
 }
@@ -149,13 +163,15 @@ class Tiers:
     ksum: torch.Tensor
     vsum: torch.Tensor
     ccount: torch.Tensor
+    mode: torch.Tensor | None = None   # [B][Hkv] uint8, None = every head rewritten
 
     def c(self) -> TiersC:
         return TiersC(*(ctypes.c_void_p(t.data_ptr()) for t in
-                        (self.k, self.v, self.pos, self.count, self.ksum, self.vsum, self.ccount)))
+                        (self.k, self.v, self.pos, self.count, self.ksum, self.vsum, self.ccount)),
+                      _p(self.mode))
 
 
-def alloc_tiers(desc: Desc, device="cuda", zero=False) -> Tiers:
+def alloc_tiers(desc: Desc, device="cuda", zero=False, mode=False) -> Tiers:
     B, Hkv, d = desc.batch, desc.num_kv_heads, desc.head_dim
     dt = torch.float32 if desc.dtype == F32 else torch.bfloat16
     mk = torch.zeros if zero else torch.empty
@@ -166,7 +182,12 @@ def alloc_tiers(desc: Desc, device="cuda", zero=False) -> Tiers:
                  mk((B, Hkv), dtype=torch.int32, device=device),
                  mk((B, Hkv, ccap, d), dtype=torch.float32, device=device),
                  mk((B, Hkv, ccap, d), dtype=torch.float32, device=device),
-                 mk((B, Hkv, ccap), dtype=torch.int32, device=device))
+                 mk((B, Hkv, ccap), dtype=torch.int32, device=device),
+                 torch.zeros((B, Hkv), dtype=torch.uint8, device=device) if mode else None)
+
+
+def policy(kind=POLICY_MTI, horizon=1, l_lower=0, l_upper=INT32_MAX) -> Policy:
+    return Policy(kind, horizon, l_lower, l_upper)
 
 
 def cache_struct(k, v, ctx_len, block_table=None) -> Cache:
@@ -211,6 +232,20 @@ def step(desc, q, cache: Cache, metric, tiers: Tiers, out, ws, stream=None):
     rc = load().hardkv_step(ctypes.byref(desc), _p(q), ctypes.byref(cache), _p(metric),
                             ctypes.byref(tc), _p(out), _p(ws), ws.numel(), _stream(stream))
     _check(rc, "hardkv_step")
+
+
+def plan(desc, pol: Policy, ctx_len, count, mode, stream=None):
+    rc = load().hardkv_plan(ctypes.byref(desc), ctypes.byref(pol), _p(ctx_len), _p(count),
+                            _p(mode), _stream(stream))
+    _check(rc, "hardkv_plan")
+
+
+def step_policy(desc, pol: Policy, q, cache: Cache, metric, tiers: Tiers, out, ws, stream=None):
+    tc = tiers.c()
+    rc = load().hardkv_step_policy(ctypes.byref(desc), ctypes.byref(pol), _p(q),
+                                   ctypes.byref(cache), _p(metric), ctypes.byref(tc), _p(out),
+                                   _p(ws), ws.numel(), _stream(stream))
+    _check(rc, "hardkv_step_policy")
 
 
 @dataclass

@@ -62,7 +62,8 @@ def _ragged(B, lo, hi, seed):
 
 def workload(name: str, **over) -> Workload:
     """The named workloads (tiny fp32 check, Qwen3-8B-shaped single layer,
-    batched paged 16k headline, ragged paged batch, mixed-metric 64k)."""
+    batched paged 16k headline and its all-peaked variant, ragged paged
+    batch, mixed-metric 64k)."""
     if name == "tiny":
         w = Workload("tiny", 1, 4, 2, 64, (512,), DT_F32, 64, 32, 0.9, planted=8)
     elif name == "qwen8b_b1_16k":
@@ -71,6 +72,11 @@ def workload(name: str, **over) -> Workload:
     elif name == "qwen8b_b32_16k_paged":
         w = Workload("qwen8b_b32_16k_paged", 32, 32, 8, 128, (16384,) * 32, DT_BF16,
                      256, 64, 0.95, block_size=16)
+    elif name == "qwen8b_b32_16k_paged_peaked":
+        # the headline shape with every KV head peaked (Zipf-planted keys),
+        # the concentrated attention for which a selection keeps few tokens
+        w = Workload("qwen8b_b32_16k_paged_peaked", 32, 32, 8, 128, (16384,) * 32, DT_BF16,
+                     256, 64, 0.95, block_size=16, peaked_heads=tuple(range(8)))
     elif name == "qwen8b_b32_ragged_paged":
         w = Workload("qwen8b_b32_ragged_paged", 32, 32, 8, 128,
                      _ragged(32, 8192, 32768, 20260627 + 3), DT_BF16, 256, 64, 0.95,
@@ -175,7 +181,7 @@ def make_case(w: Workload, device="cpu") -> Case:
             L_r = w.peaked_top - w.peaked_zipf * torch.log(r)
             keys = (L_r * math.sqrt(d) / qh.norm())[:, None] * (qh / qh.norm())[None, :]
             pos = torch.randperm(A, generator=_gen(w, "cpu", "peak", b, h))[:w.peaked_m]
-            kb[h, pos.to(device)] = keys
+            kb[h, pos.to(device)] = keys[:len(pos)]
             extra[("peaked", b, h)] = [int(x) for x in pos]
         kb = kb.to(dt)
         vb = vb.to(dt)

@@ -13,6 +13,9 @@
  *   attention  over dense + sparse + condensed tiers        (abstract; section 3)
  * hardkv_step chains all of them; hardkv_step_inplace runs the multi-step
  * token lifecycle (section 2.A four-step pipeline) on persistent tiers.
+ * hardkv_plan and hardkv_step_policy choose per head between rewriting the
+ * selection and loading it in place (section 2.C: Sparse Loading, and the
+ * Memory-Time Integral with budget thresholds under "Trade-off Management").
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is a caller-owned DEVICE pointer unless it is a
@@ -65,6 +68,30 @@ typedef struct ihipStream_t* hardkv_stream_t; /* same type as hipStream_t */
 #define HARDKV_METRIC_QK 0 /* max over the GQA group of q.k / sqrt(d) ("max-pooled logits") */
 #define HARDKV_METRIC_L2 1 /* key L2 norm, calibrated onto the head's logit spread */
 
+/* How a head's selection is served (per head, device byte). */
+#define HARDKV_MODE_REWRITE 0 /* kept rows copied into the tier's contiguous slots */
+#define HARDKV_MODE_SPARSE 1  /* kept rows left in the cache, loaded through the tier's positions */
+
+/* Policy kinds (hardkv_policy.kind). */
+#define HARDKV_POLICY_REWRITE 0 /* every head rewritten */
+#define HARDKV_POLICY_SPARSE 1  /* every head sparse-loaded */
+#define HARDKV_POLICY_MTI 2     /* budget thresholds, then the memory-time integral */
+
+/* Rewrite-versus-sparse-loading policy (host memory; section 2.C, "Trade-off
+ * Management").  For a head with A aged tokens of which k are kept, window W:
+ *   k <= l_lower -> rewrite; else k >= l_upper -> sparse loading; else the
+ *   smaller memory-time integral over `horizon` steps (the selection step
+ *   and horizon - 1 steps that reuse its tiers), in units of K/V rows:
+ *     sparse  = (A + W)(3A + 2W) + (horizon - 1)(A + W) * 2(k + W)
+ *     rewrite = (A + W + k)(3A + 2W + 2k) + (horizon - 1)(k + W) * 2(k + W)
+ *   rewrite only if strictly smaller; computed in exact 128-bit integers. */
+typedef struct hardkv_policy {
+  int32_t kind;    /* HARDKV_POLICY_* */
+  int32_t horizon; /* >= 1 */
+  int32_t l_lower; /* budgets k <= l_lower are rewritten (e.g. 0) */
+  int32_t l_upper; /* budgets k >= l_upper are sparse-loaded (e.g. INT32_MAX) */
+} hardkv_policy;
+
 /* Shapes and policy of one decode step (host memory). */
 typedef struct hardkv_desc {
   int32_t batch;        /* B >= 1 */
@@ -101,6 +128,10 @@ typedef struct hardkv_cache {
  *   count:  [B][Hkv] int32 selected tokens (the head's budget k_{b,h})
  *   ksum, vsum: [B][Hkv][chunk_cap][d] float32 sums of the evicted keys / values
  *   ccount: [B][Hkv][chunk_cap] int32 evicted tokens per chunk (0 = empty chunk)
+ *   mode:   [B][Hkv] uint8 HARDKV_MODE_* per head, or NULL (every head rewritten).
+ *           A HARDKV_MODE_SPARSE head's k / v slots are neither written nor read:
+ *           attention loads its kept rows from the cache at pos (Sparse Loading,
+ *           section 2.C), so that cache must stay unchanged while the tiers are used.
  * Single-step calls write chunk slots [0, ceil(A_b / C)); the rest is unspecified. */
 typedef struct hardkv_tiers {
   void* k;
@@ -110,11 +141,13 @@ typedef struct hardkv_tiers {
   float* ksum;
   float* vsum;
   int32_t* ccount;
+  uint8_t* mode;
 } hardkv_tiers;
 
 /* Persistent state of the multi-step lifecycle (one layer).
  *   ring_k, ring_v: [B][Hkv][W][d] dense window; position t lives in slot t % W
- *   tiers: sparse pool (positions ascending, `count` residents) and running chunk sums
+ *   tiers: sparse pool (positions ascending, `count` residents) and running chunk sums;
+ *          tiers.mode must be NULL (the pool is always compacted in place)
  *   seq_len: [B] int32 tokens seen so far; must be >= W; advanced by one per step */
 typedef struct hardkv_state {
   void* ring_k;
@@ -188,7 +221,9 @@ int hardkv_topp_select(const hardkv_desc* desc, const int32_t* ctx_len, const in
  * (b, h): the tokens t < A_b with mask[t] = 1 are copied bit for bit into
  * out->k / out->v slots 0..count-1 in ascending position order with their
  * positions; every other aged token is added to the float32 sums of chunk
- * t / C.  Writes every field of *out (count = number of mask bytes set).
+ * t / C.  Writes every field of *out (count = number of mask bytes set),
+ * except the k / v slots of heads whose out->mode byte is HARDKV_MODE_SPARSE
+ * (out->mode is read, e.g. as written by hardkv_plan).
  * The tiers must not alias the cache. */
 int hardkv_compact(const hardkv_desc* desc, const hardkv_cache* cache, const uint8_t* mask,
                    const hardkv_tiers* out, void* ws, size_t ws_bytes,
@@ -198,9 +233,14 @@ int hardkv_compact(const hardkv_desc* desc, const hardkv_cache* cache, const uin
  * contribution).  For every query head g of (b, h = g / G): softmax over
  *   dense tokens [A_b, T_b) of the cache      logit q.k / sqrt(d), value v
  *   sparse slots 0..count-1 of the tiers      logit q.k / sqrt(d), value v
+ *     (HARDKV_MODE_SPARSE heads: cache rows at pos[0..count-1] instead)
  *   chunks j < ceil(A_b / C) with n = ccount > 0: logit q.(ksum / n) / sqrt(d) + ln n,
  *                                             value vsum / n
- *   out: [B][Hq][d] float32.  Split-K partials live in the workspace. */
+ *   out: [B][Hq][d] float32.  Split-K partials live in the workspace.
+ * Reusing a selection on later steps: after a step at length T with window W
+ * wrote the tiers, a call with ctx_len T + i and dense_window W + i attends
+ * the same sparse and condensed tiers plus every token that aged since,
+ * densely (A_b stays that of the selection). */
 int hardkv_decode_attn(const hardkv_desc* desc, const void* q, const hardkv_cache* cache,
                        const hardkv_tiers* tiers, float* out, void* ws, size_t ws_bytes,
                        hardkv_stream_t stream);
@@ -212,11 +252,29 @@ int hardkv_decode_attn(const hardkv_desc* desc, const void* q, const hardkv_cach
  * compaction pass (the rows are attended while they are copied), so the
  * sparse tier is not read back; results equal hardkv_compact followed by
  * hardkv_decode_attn up to float32 summation order in the attention.
- *   metric: as in hardkv_score; tiers: written as by hardkv_compact;
+ *   metric: as in hardkv_score; tiers: written as by hardkv_compact, every
+ *   head rewritten (tiers->mode, when given, is set to HARDKV_MODE_REWRITE);
  *   out: [B][Hq][d] float32 attention output. */
 int hardkv_step(const hardkv_desc* desc, const void* q, const hardkv_cache* cache,
                 const int8_t* metric, const hardkv_tiers* tiers, float* out, void* ws,
                 size_t ws_bytes, hardkv_stream_t stream);
+
+/* Rewrite or sparse loading per head (section 2.C, "Trade-off Management"):
+ *   count: [B][Hkv] int32 kept tokens k (as written by hardkv_topp_select)
+ *   mode:  [B][Hkv] uint8 output, HARDKV_MODE_* from *policy with A = A_b. */
+int hardkv_plan(const hardkv_desc* desc, const hardkv_policy* policy, const int32_t* ctx_len,
+                const int32_t* count, uint8_t* mode, hardkv_stream_t stream);
+
+/* hardkv_step with a per-head choice between rewriting the selection and
+ * loading it in place: the policy is evaluated right after the top-p
+ * selection, tiers->mode (required) receives each head's choice, and
+ * HARDKV_MODE_SPARSE heads skip the row copies.  The attention output is
+ * the same function of the inputs for every choice (the selection, the
+ * chunks and the positions do not depend on it). */
+int hardkv_step_policy(const hardkv_desc* desc, const hardkv_policy* policy, const void* q,
+                       const hardkv_cache* cache, const int8_t* metric,
+                       const hardkv_tiers* tiers, float* out, void* ws, size_t ws_bytes,
+                       hardkv_stream_t stream);
 
 /* One decode step of the multi-step token lifecycle on persistent tiers
  * (section 2.A: tokens move dense -> sparse -> condensed as they age; the

@@ -110,8 +110,9 @@ def borderline_tokens(ref: O.HeadResult, p: float, tokens) -> np.ndarray:
     return np.array(ok, bool)
 
 
-def check_head(case, b, h, gpu, p, report, stages=True, desc=None):
-    """Compare every stage of (b, h) with the oracle; returns mismatch count."""
+def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=False):
+    """Compare every stage of (b, h) with the oracle; returns mismatch count.
+    skip_slots: the head is sparse-loaded, its k / v slots hold no rows."""
     w = case.w
     q, K, V, ref = oracle_head(case, b, h, p)
     A = ref.A
@@ -151,7 +152,9 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None):
     report["selected"] += k_gpu
     report["candidates"] += A
     # rewritten rows are bit copies of the source rows
-    kt = tiers.k[b, h, :k_gpu]
+    if skip_slots:
+        report["sparse_heads"] += 1
+    kt = tiers.k[b, h, :0 if skip_slots else k_gpu]
     vt = tiers.v[b, h, :k_gpu]
     src_k = S.head_rows(case, b, h, "k")[torch.as_tensor(pos_gpu, device=kt.device).long()]
     src_v = S.head_rows(case, b, h, "v")[torch.as_tensor(pos_gpu, device=kt.device).long()]
@@ -190,16 +193,18 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None):
 
 def new_report():
     return dict(logit_1ulp=0, l2_1ulp=0, borderline=0, selected=0, candidates=0, staged_attn=0,
-                max_attn_err=0.0, heads=0)
+                max_attn_err=0.0, heads=0, sparse_heads=0)
 
 
-def check_case(case, gpu, p, heads=None, stages=True):
+def check_case(case, gpu, p, heads=None, stages=True, skip_slots=None):
+    """skip_slots: optional [B][Hkv] array, non-zero = sparse-loaded head."""
     rep = new_report()
     w = case.w
     if heads is None:
         heads = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     for b, h in heads:
-        check_head(case, b, h, gpu, p, rep, stages)
+        check_head(case, b, h, gpu, p, rep, stages,
+                   skip_slots=skip_slots is not None and bool(skip_slots[b, h]))
         rep["heads"] += 1
     return rep
 

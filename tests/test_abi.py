@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = H.load()
-    assert lib.hardkv_version() == 10000
+    assert lib.hardkv_version() == 10100
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.hardkv_strerror(code)
     assert lib.hardkv_strerror(99) == b"unknown error"
@@ -85,8 +85,9 @@ def _call_all(desc, ws_bytes, null_q=False):
     lib = H.load()
     fake = ctypes.c_void_p(0x1000)
     cache = H.Cache(fake, fake, None, fake)
-    tiers = H.TiersC(*([fake] * 7))
-    state = H.StateC(fake, fake, tiers, fake)
+    tiers = H.TiersC(*([fake] * 8))
+    state = H.StateC(fake, fake, H.TiersC(*([fake] * 7)), fake)
+    pol = H.policy(H.POLICY_MTI, 4)
     q = None if null_q else fake
     d = ctypes.byref(desc)
     st = ctypes.c_void_p(0)
@@ -101,18 +102,20 @@ def _call_all(desc, ws_bytes, null_q=False):
                         ws_bytes, st),
         lib.hardkv_step_inplace(d, q, fake, fake, None, ctypes.byref(state), fake, fake,
                                 ws_bytes, st),
+        lib.hardkv_step_policy(d, ctypes.byref(pol), q, ctypes.byref(cache), None,
+                               ctypes.byref(tiers), fake, fake, ws_bytes, st),
     ]
 
 
 def test_errors_before_launch():
     desc = base_desc()
     need = H.workspace_size(desc)
-    assert _call_all(desc, need - 1) == [H.ERR_WORKSPACE] * 7
-    assert _call_all(base_desc(d=96), need) == [H.ERR_UNSUPPORTED] * 7
-    assert _call_all(base_desc(top_p=2.0), need) == [H.ERR_INVALID_ARG] * 7
-    assert _call_all(base_desc(sparse_cap=10), need) == [H.ERR_CAPACITY] * 7
+    assert _call_all(desc, need - 1) == [H.ERR_WORKSPACE] * 8
+    assert _call_all(base_desc(d=96), need) == [H.ERR_UNSUPPORTED] * 8
+    assert _call_all(base_desc(top_p=2.0), need) == [H.ERR_INVALID_ARG] * 8
+    assert _call_all(base_desc(sparse_cap=10), need) == [H.ERR_CAPACITY] * 8
     rc = _call_all(desc, need, null_q=True)
-    assert rc[0] == rc[4] == rc[5] == rc[6] == H.ERR_INVALID_ARG
+    assert rc[0] == rc[4] == rc[5] == rc[6] == rc[7] == H.ERR_INVALID_ARG
     # the lifecycle needs a contiguous layout and a window
     paged = base_desc(block_size=16, max_blocks=63)
     assert _call_all(paged, H.workspace_size(paged))[6] == H.ERR_INVALID_ARG
@@ -129,3 +132,46 @@ def test_l2_buffer_required_with_metric():
     rc = lib.hardkv_score(ctypes.byref(desc), fake, ctypes.byref(cache), fake, fake, None, fake,
                           H.workspace_size(desc), ctypes.c_void_p(0))
     assert rc == H.ERR_INVALID_ARG
+
+
+def test_policy_errors_before_launch():
+    lib = H.load()
+    desc = base_desc()
+    ws_bytes = H.workspace_size(desc)
+    fake = ctypes.c_void_p(0x1000)
+    cache = H.Cache(fake, fake, None, fake)
+    st = ctypes.c_void_p(0)
+    d = ctypes.byref(desc)
+    with_mode = H.TiersC(*([fake] * 8))
+    no_mode = H.TiersC(*([fake] * 7))
+
+    def step_policy(pol, tiers):
+        return lib.hardkv_step_policy(d, pol, fake, ctypes.byref(cache), None,
+                                      ctypes.byref(tiers), fake, fake, ws_bytes, st)
+
+    for bad in (H.policy(3), H.policy(-1), H.policy(H.POLICY_MTI, 0)):
+        assert step_policy(ctypes.byref(bad), with_mode) == H.ERR_INVALID_ARG
+        assert lib.hardkv_plan(d, ctypes.byref(bad), fake, fake, fake, st) == H.ERR_INVALID_ARG
+    assert step_policy(None, with_mode) == H.ERR_INVALID_ARG
+    # the policy's choice needs somewhere to go
+    assert step_policy(ctypes.byref(H.policy()), no_mode) == H.ERR_INVALID_ARG
+    good = ctypes.byref(H.policy(H.POLICY_MTI, 8, 16, 1 << 20))
+    for args in ((None, fake, fake), (fake, None, fake), (fake, fake, None)):
+        assert lib.hardkv_plan(d, good, *args, st) == H.ERR_INVALID_ARG
+    assert lib.hardkv_plan(ctypes.byref(base_desc(d=96)), good, fake, fake, fake, st) == \
+        H.ERR_UNSUPPORTED
+    # the lifecycle compacts in place: no per-head mode
+    state = H.StateC(fake, fake, with_mode, fake)
+    assert lib.hardkv_step_inplace(d, fake, fake, fake, None, ctypes.byref(state), fake, fake,
+                                   ws_bytes, st) == H.ERR_INVALID_ARG
+
+
+def test_host_plan_matches_oracle_reading():
+    """The memory-time integrals documented with hardkv_policy in
+    include/hardkv.h, evaluated in Python integers, agree with the oracle's."""
+    import oracle as O
+    for A, k, W, N in [(10, 2, 2, 3), (10, 2, 2, 2), (16128, 13548, 256, 22),
+                       (16128, 13548, 256, 23), (16128, 60, 256, 2), (0, 0, 256, 5)]:
+        sparse = (A + W) * (3 * A + 2 * W) + (N - 1) * (A + W) * 2 * (k + W)
+        rewrite = (A + W + k) * (3 * A + 2 * W + 2 * k) + (N - 1) * (k + W) * 2 * (k + W)
+        assert (rewrite, sparse) == O.mti_head(A, k, W, N)
