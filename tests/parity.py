@@ -151,17 +151,19 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
         assert k_gpu == ref.sel.k
     report["selected"] += k_gpu
     report["candidates"] += A
-    # rewritten rows are bit copies of the source rows
+    # rewritten rows are bit copies of the source rows (a sparse-loaded head
+    # has no rows in its slots)
     if skip_slots:
         report["sparse_heads"] += 1
-    kt = tiers.k[b, h, :0 if skip_slots else k_gpu]
-    vt = tiers.v[b, h, :k_gpu]
-    src_k = S.head_rows(case, b, h, "k")[torch.as_tensor(pos_gpu, device=kt.device).long()]
-    src_v = S.head_rows(case, b, h, "v")[torch.as_tensor(pos_gpu, device=kt.device).long()]
-    assert torch.equal(kt.view(torch.int16) if kt.dtype == torch.bfloat16 else kt.view(torch.int32),
-                       src_k.view(torch.int16) if kt.dtype == torch.bfloat16 else src_k.view(torch.int32))
-    assert torch.equal(vt.view(torch.int16) if vt.dtype == torch.bfloat16 else vt.view(torch.int32),
-                       src_v.view(torch.int16) if vt.dtype == torch.bfloat16 else src_v.view(torch.int32))
+    else:
+        kt = tiers.k[b, h, :k_gpu]
+        vt = tiers.v[b, h, :k_gpu]
+        idx = torch.as_tensor(pos_gpu, device=kt.device).long()
+        src_k = S.head_rows(case, b, h, "k")[idx]
+        src_v = S.head_rows(case, b, h, "v")[idx]
+        bits = torch.int16 if kt.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(kt.view(bits), src_k.view(bits))
+        assert torch.equal(vt.view(bits), src_v.view(bits))
     # condensed tier
     nch = -(-A // w.C) if A else 0
     cc = tiers.ccount[b, h, :nch].cpu().numpy()
