@@ -8,5 +8,6 @@ from .hardkv_oracle import (  # noqa: F401
     METRIC_QK, METRIC_L2, aged_count, score_head, calibrate_head, topp_head,
     condense, attend_head, full_attention, step_head, step, HeadState,
     init_state, lifecycle_step, POLICY_REWRITE, POLICY_SPARSE, POLICY_MTI,
-    MODE_REWRITE, MODE_SPARSE, mti_head, plan_head, reuse_head,
+    MODE_REWRITE, MODE_SPARSE, mti_head, plan_head, reuse_head, MERGE_MEAN,
+    MERGE_WEIGHTED, MERGE_FLOOR, merge_weights, candidate_range, dense_positions,
 )

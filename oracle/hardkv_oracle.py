@@ -37,6 +37,13 @@ Memory-Time Integral and the thresholds L_lower / L_upper without a formula
 derived from the integral, degenerate cases, threshold precedence, and
 reductions of reuse attention to full softmax attention).  The integral's
 cost model itself is this reading, not the pages'.
+
+Attention-sink tokens in the dense tier and attention-weighted merging in
+the condensed tier (``candidate_range``, ``merge_weights``, ``condense``)
+read section 2.A, Tier 1 and Tier 3 (tests/test_oracle_merge.py: a
+hand-worked weighted chunk, scale invariance and the weight floor, the tier
+partition and chunk alignment with sinks, and reductions to full softmax
+attention).
 """
 from __future__ import annotations
 
@@ -219,25 +226,54 @@ def topp_head(c, w, Z, p, positions=None) -> Selection:
 # Condensed tier (section 2.A, Tier 3: oldest blocks compressed into
 # constant-size storage by eviction or weighted merging).
 # ---------------------------------------------------------------------------
-def condense(K, V, evicted, positions, C: int, nchunks: int):
-    """Mean-pool storage of evicted tokens.
+MERGE_MEAN = 0       # chunk = plain mean of its evicted tokens
+MERGE_WEIGHTED = 1   # chunk = attention-weighted mean of its evicted tokens
+MERGE_FLOOR = -80.0  # log-weight floor of a token in weighted merging
 
-    Reading: chunks are position-aligned, chunk j holds the evicted tokens
-    with position in [jC, (j+1)C).  The stored form is the float64 sum of
-    keys, the sum of values and the token count; the pooled key and value
-    are sum / count.  A chunk with no evicted token has count 0.
+
+def merge_weights(c, m):
+    """Weights of evicted tokens for attention-weighted merging.
+
+    Reading of "weighted merging" (section 2.A, Tier 3): a token enters its
+    chunk with its calibrated attention weight exp(c - m), the quantity the
+    top-p selection ranked it by.  A weight below e^-80 of the head's largest
+    counts as e^-80, so a chunk never has zero total weight (float32 on the
+    GPU keeps e^-80 as a normal number).
+    """
+    return np.exp(np.maximum(_f64(c) - float(m), MERGE_FLOOR))
+
+
+def condense(K, V, evicted, positions, C: int, nchunks: int, weights=None, origin: int = 0):
+    """Storage of evicted tokens in the condensed tier.
+
+    Reading: chunks are aligned to the candidate range, chunk j holds the
+    evicted tokens with position in [origin + jC, origin + (j+1)C) (origin =
+    the first candidate position: 0, or the number of sink tokens).  Stored
+    per chunk: the token count n and key / value sums such that sum / n is
+    the chunk's representative key / value:
+      mean merging (weights None): the plain sums;
+      weighted merging: n * (sum_t a_t x_t) / (sum_t a_t), the weighted mean
+      scaled by n, so both forms enter attention the same way.
+    A chunk with no evicted token has count 0.
     """
     d = K.shape[1]
     ksum = np.zeros((nchunks, d))
     vsum = np.zeros((nchunks, d))
+    wsum = np.zeros(nchunks)
     cnt = np.zeros(nchunks, np.int64)
     k64 = _f64(K)
     v64 = _f64(V)
-    for i in evicted:
-        j = int(positions[i]) // C
-        ksum[j] += k64[i]
-        vsum[j] += v64[i]
+    for n_i, i in enumerate(evicted):
+        j = (int(positions[i]) - origin) // C
+        a = 1.0 if weights is None else float(weights[n_i])
+        ksum[j] += a * k64[i]
+        vsum[j] += a * v64[i]
+        wsum[j] += a
         cnt[j] += 1
+    if weights is not None:
+        nz = cnt > 0
+        ksum[nz] *= (cnt[nz] / wsum[nz])[:, None]
+        vsum[nz] *= (cnt[nz] / wsum[nz])[:, None]
     return ksum, vsum, cnt
 
 
@@ -307,20 +343,43 @@ class HeadResult:
     cnt: np.ndarray
     out: np.ndarray        # [G, d] float64
     extra: dict = field(default_factory=dict)
+    sinks: int = 0         # leading positions held in the dense tier
 
 
-def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int) -> HeadResult:
+def candidate_range(T: int, W: int, sinks: int = 0):
+    """(first candidate position, number of candidates) of one step.
+
+    Tier 1 keeps the last W tokens and, reading its mention of attention
+    sinks (section 2.A, Tier 1) as the usual leading tokens, the first
+    `sinks` positions; everything in between is a candidate for Tier 2:
+    [S, T - W), empty when T <= S + W.
+    """
+    if sinks < 0:
+        raise ValueError("sinks must be >= 0")
+    A = aged_count(T, W)
+    return sinks, max(A - sinks, 0)
+
+
+def dense_positions(T: int, S: int, A: int) -> np.ndarray:
+    """Positions of the dense tier: [0, T) without the candidates [S, S + A)."""
+    return np.concatenate([np.arange(0, S if A else T), np.arange(S + A, T) if A else []]).astype(np.int64)
+
+
+def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
+              sinks: int = 0, merge: int = MERGE_MEAN) -> HeadResult:
     """Single-step compression + attention of one KV head.
 
     K, V: [>=T, d] rows of this head's cache in position order (exact
-    input values, any float dtype).  The dense tier is [A, T), the candidates
-    are [0, A), A = max(T - W, 0).
+    input values, any float dtype).  Candidates are [S, S + A) with
+    (S, A) = candidate_range(T, W, sinks); the dense tier is every other
+    position below T.
     Rewrite: the selected rows are copied, in ascending position order, into
     contiguous slots 0..k-1 (Rewrite Cache + Flatten Index to the maximum
-    length, section 2.C).
+    length, section 2.C).  Evicted candidates go to the condensed tier, mean-
+    or attention-weighted-merged (``condense``).
     """
-    A = aged_count(T, W)
-    cand_K = K[:A]
+    S, A = candidate_range(T, W, sinks)
+    cand_K = K[S:S + A]
     ell, s = score_head(q_group, cand_K)
     cal = calibrate_head(ell, s, metric)
     sel = topp_head(cal.c, cal.w, cal.Z, p)
@@ -328,15 +387,22 @@ def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int) -> H
     mask[sel.selected] = 1
     evicted = np.nonzero(mask == 0)[0]
     nchunks = -(-A // C) if A else 0
-    ksum, vsum, cnt = condense(K, V, evicted, np.arange(A), C, nchunks)
-    Kc = np.asarray(K)[sel.selected]
-    Vc = np.asarray(V)[sel.selected]
-    out = attend_head(q_group, K[A:T], V[A:T], Kc, Vc, ksum, vsum, cnt)
-    return HeadResult(A, ell, s, cal, sel, mask, sel.selected.copy(), Kc, Vc,
-                      ksum, vsum, cnt, out)
+    if merge == MERGE_MEAN:
+        weights = None
+    elif merge == MERGE_WEIGHTED:
+        weights = merge_weights(cal.c[evicted], cal.m)
+    else:
+        raise ValueError("unknown merge rule")
+    ksum, vsum, cnt = condense(K, V, S + evicted, np.arange(T), C, nchunks, weights, origin=S)
+    pos = S + sel.selected
+    Kc = np.asarray(K)[pos]
+    Vc = np.asarray(V)[pos]
+    dense = dense_positions(T, S, A)
+    out = attend_head(q_group, np.asarray(K)[dense], np.asarray(V)[dense], Kc, Vc, ksum, vsum, cnt)
+    return HeadResult(A, ell, s, cal, sel, mask, pos, Kc, Vc, ksum, vsum, cnt, out, sinks=S)
 
 
-def step(q, k_rows, v_rows, ctx_len, W, C, p, metric):
+def step(q, k_rows, v_rows, ctx_len, W, C, p, metric, sinks=0, merge=MERGE_MEAN):
     """Whole batch: q [B, Hq, d]; k_rows(b, h) / v_rows(b, h) return the
     [T_b, d] position-ordered rows of head h of sequence b; metric [Hkv].
     Query head g belongs to KV head g // G.  Returns {(b, h): HeadResult}.
@@ -352,7 +418,7 @@ def step(q, k_rows, v_rows, ctx_len, W, C, p, metric):
         T = int(ctx_len[b])
         for h in range(Hkv):
             res[(b, h)] = step_head(q[b, h * G:(h + 1) * G], k_rows(b, h), v_rows(b, h),
-                                    T, W, C, p, int(metric[h]))
+                                    T, W, C, p, int(metric[h]), sinks, merge)
     return res
 
 
@@ -524,8 +590,9 @@ def reuse_head(q_group, K, V, T_now: int, sel: HeadResult):
     positions -- rewritten copies or, with sparse loading, the originals,
     which hold the same values.
     """
-    if T_now < sel.A:
+    if T_now < sel.sinks + sel.A:
         raise ValueError("the context only grows")
-    return attend_head(q_group, K[sel.A:T_now], V[sel.A:T_now],
+    dense = dense_positions(T_now, sel.sinks, sel.A)
+    return attend_head(q_group, np.asarray(K)[dense], np.asarray(V)[dense],
                        np.asarray(K)[sel.pos], np.asarray(V)[sel.pos],
                        sel.ksum, sel.vsum, sel.cnt)
