@@ -228,7 +228,7 @@ def topp_head(c, w, Z, p, positions=None) -> Selection:
 # ---------------------------------------------------------------------------
 MERGE_MEAN = 0       # chunk = plain mean of its evicted tokens
 MERGE_WEIGHTED = 1   # chunk = attention-weighted mean of its evicted tokens
-MERGE_FLOOR = -80.0  # log-weight floor of a token in weighted merging
+MERGE_FLOOR = -60.0  # log-weight floor of a token in weighted merging
 
 
 def merge_weights(c, m):
@@ -236,9 +236,9 @@ def merge_weights(c, m):
 
     Reading of "weighted merging" (section 2.A, Tier 3): a token enters its
     chunk with its calibrated attention weight exp(c - m), the quantity the
-    top-p selection ranked it by.  A weight below e^-80 of the head's largest
-    counts as e^-80, so a chunk never has zero total weight (float32 on the
-    GPU keeps e^-80 as a normal number).
+    top-p selection ranked it by.  A weight below e^-60 of the head's largest
+    counts as e^-60, so a chunk never has zero total weight, and float32
+    products of such weights with the cache's values stay normal numbers.
     """
     return np.exp(np.maximum(_f64(c) - float(m), MERGE_FLOOR))
 
