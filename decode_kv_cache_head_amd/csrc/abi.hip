@@ -18,7 +18,7 @@ void hk::observe(const char* kernel, hipStream_t st) {
 
 namespace {
 
-constexpr int kVersion = 10100;  // 1.1.0
+constexpr int kVersion = 10200;  // 1.2.0
 
 int log2i(int v) {
   int l = 0;
@@ -26,7 +26,11 @@ int log2i(int v) {
   return l;
 }
 
-int max_aged(const hardkv_desc* d) { return d->ctx_cap > d->dense_window ? d->ctx_cap - d->dense_window : 0; }
+// candidates per (b, h) at most: positions [S, ctx_cap - W)
+int max_aged(const hardkv_desc* d) {
+  const int64_t a = (int64_t)d->ctx_cap - d->dense_window - d->sinks;
+  return a > 0 ? (int)a : 0;
+}
 
 int validate(const hardkv_desc* d) {
   if (!d) return HARDKV_ERR_INVALID_ARG;
@@ -44,6 +48,9 @@ int validate(const hardkv_desc* d) {
       return HARDKV_ERR_INVALID_ARG;
   }
   if (!(d->top_p > 0.0f && d->top_p <= 1.0f)) return HARDKV_ERR_INVALID_ARG;  // NaN fails too
+  if (d->sinks < 0 || (d->merge != HARDKV_MERGE_MEAN && d->merge != HARDKV_MERGE_WEIGHTED))
+    return HARDKV_ERR_INVALID_ARG;
+  if ((int64_t)d->dense_window + d->sinks > INT32_MAX / 2) return HARDKV_ERR_INVALID_ARG;
   if (d->sparse_cap < 0 || d->chunk_cap < 0) return HARDKV_ERR_INVALID_ARG;
   const int A = max_aged(d);
   if (d->sparse_cap < A) return HARDKV_ERR_CAPACITY;
@@ -76,7 +83,7 @@ Layout layout(const hardkv_desc* d) {
   L.stats = take(B * Hkv * 4 * 8);
   L.mask = take(B * Hkv * cap);
   L.count = take(B * Hkv * 4);
-  L.max_tiles = attn_max_tiles(d->dense_window, d->sparse_cap, d->chunk_cap);
+  L.max_tiles = attn_max_tiles(d->dense_window + d->sinks, d->sparse_cap, d->chunk_cap);
   L.part = take(B * Hkv * (size_t)L.max_tiles * G * (D + 2) * 4);
   L.total = off;
   return L;
@@ -94,6 +101,13 @@ Rows cache_rows(const hardkv_desc* d, const void* base, const int32_t* table) {
   return r;
 }
 
+// candidate rows: position t of the candidates is cache position sinks + t
+Rows cand_rows(const hardkv_desc* d, const void* base, const int32_t* table) {
+  Rows r = cache_rows(d, base, table);
+  r.off = d->sinks;
+  return r;
+}
+
 Rows region_rows(const hardkv_desc* d, const void* base, int64_t region) {
   Rows r{};
   r.base = (const char*)base;
@@ -105,7 +119,8 @@ Rows region_rows(const hardkv_desc* d, const void* base, int64_t region) {
 }
 
 Cand aged_cand(const hardkv_desc* d, const int32_t* ctx_len) {
-  return Cand{ctx_len, nullptr, d->dense_window, d->ctx_cap, max_aged(d), d->num_kv_heads};
+  return Cand{ctx_len, nullptr, d->dense_window, d->ctx_cap, max_aged(d), d->num_kv_heads,
+              d->sinks};
 }
 
 int launched() {
@@ -180,6 +195,8 @@ CompactArgs compact_args(const hardkv_desc* d, const Layout& L, char* ws, const 
   a.ccount = t->ccount;
   a.chunk_stride = d->chunk_cap;
   a.mode = t->mode;
+  a.pos_off = d->sinks;
+  a.merge = d->merge;
   a.G = d->num_q_heads / d->num_kv_heads;
   a.hq = d->num_q_heads;
   a.q = nullptr;
@@ -201,6 +218,7 @@ AttnArgs attn_args(const hardkv_desc* d, const Layout& L, char* ws, const void* 
   a.q = q;
   a.ctx_cap = d->ctx_cap;
   a.W = d->dense_window;
+  a.sinks = d->sinks;
   a.sk = region_rows(d, t->k, d->sparse_cap);
   a.sv = region_rows(d, t->v, d->sparse_cap);
   a.count = t->count;
@@ -249,8 +267,8 @@ void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
   const Layout L = layout(d);
   char* w = (char*)ws;
   const hardkv_tiers& t = *tiers;
-  const Rows kr = cache_rows(d, cache->k, cache->block_table);
-  const Rows vr = cache_rows(d, cache->v, cache->block_table);
+  const Rows kr = cand_rows(d, cache->k, cache->block_table);
+  const Rows vr = cand_rows(d, cache->v, cache->block_table);
   const Cand cand = aged_cand(d, cache->ctx_len);
   float* logit = (float*)(w + L.logit);
   float* l2 = (float*)(w + L.l2);
@@ -269,9 +287,13 @@ void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
     launch_select(sa, st);
   }
   CompactArgs ca = compact_args(d, L, w, kr, vr, cand, max_aged(d), mask, &t);
+  ca.metric = metric;
+  ca.logit = logit;
+  ca.l2 = l2;
+  ca.stats = stats;
   AttnArgs a = attn_args(d, L, w, q, &t, out);
-  a.dk = kr;
-  a.dv = vr;
+  a.dk = cache_rows(d, cache->k, cache->block_table);
+  a.dv = cache_rows(d, cache->v, cache->block_table);
   a.ctx_len = cache->ctx_len;
   a.ring = false;
   if (compact_fusable(d->chunk)) {
@@ -324,7 +346,7 @@ int hardkv_score(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
   if (!q || !cache_ok(d, cache) || !logit || (metric && !l2)) return HARDKV_ERR_INVALID_ARG;
   const Layout L = layout(d);
   hipGetLastError();
-  do_score(d, L, (char*)ws, q, cache_rows(d, cache->k, cache->block_table),
+  do_score(d, L, (char*)ws, q, cand_rows(d, cache->k, cache->block_table),
            aged_cand(d, cache->ctx_len), max_aged(d), metric, logit, l2, (hipStream_t)stream);
   return launched();
 }
@@ -355,18 +377,35 @@ int hardkv_topp_select(const hardkv_desc* d, const int32_t* ctx_len, const int8_
   return launched();
 }
 
-int hardkv_compact(const hardkv_desc* d, const hardkv_cache* cache, const uint8_t* mask,
-                   const hardkv_tiers* out, void* ws, size_t ws_bytes, hardkv_stream_t stream) {
+int hardkv_compact_scored(const hardkv_desc* d, const hardkv_cache* cache,
+                          const int8_t* metric, const float* logit, const float* l2,
+                          const double* stats, const uint8_t* mask, const hardkv_tiers* out,
+                          void* ws, size_t ws_bytes, hardkv_stream_t stream) {
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
   if (!cache_ok(d, cache) || !mask || !tiers_ok(out)) return HARDKV_ERR_INVALID_ARG;
+  if (d->merge == HARDKV_MERGE_WEIGHTED && (!logit || !stats || (metric && !l2)))
+    return HARDKV_ERR_INVALID_ARG;
   const Layout L = layout(d);
+  CompactArgs a = compact_args(d, L, (char*)ws, cand_rows(d, cache->k, cache->block_table),
+                               cand_rows(d, cache->v, cache->block_table),
+                               aged_cand(d, cache->ctx_len), max_aged(d), mask, out);
+  a.metric = metric;
+  a.logit = logit;
+  a.l2 = l2;
+  a.stats = stats;
   hipGetLastError();
-  launch_compact(compact_args(d, L, (char*)ws, cache_rows(d, cache->k, cache->block_table),
-                              cache_rows(d, cache->v, cache->block_table),
-                              aged_cand(d, cache->ctx_len), max_aged(d), mask, out),
-                 (hipStream_t)stream);
+  launch_compact(a, (hipStream_t)stream);
   return launched();
+}
+
+int hardkv_compact(const hardkv_desc* d, const hardkv_cache* cache, const uint8_t* mask,
+                   const hardkv_tiers* out, void* ws, size_t ws_bytes, hardkv_stream_t stream) {
+  const int rc = validate(d);
+  if (rc) return rc;
+  if (d->merge != HARDKV_MERGE_MEAN) return HARDKV_ERR_INVALID_ARG;
+  return hardkv_compact_scored(d, cache, nullptr, nullptr, nullptr, nullptr, mask, out, ws,
+                               ws_bytes, stream);
 }
 
 int hardkv_decode_attn(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
@@ -429,7 +468,9 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
                         float* out, void* ws, size_t ws_bytes, hardkv_stream_t stream) {
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
-  if (d->block_size != 0 || d->dense_window < 1) return HARDKV_ERR_INVALID_ARG;
+  if (d->block_size != 0 || d->dense_window < 1 || d->sinks != 0 ||
+      d->merge != HARDKV_MERGE_MEAN)
+    return HARDKV_ERR_INVALID_ARG;
   if (!q || !k_new || !v_new || !s || !s->ring_k || !s->ring_v || !s->seq_len ||
       !tiers_ok(&s->tiers) || s->tiers.mode || !out)
     return HARDKV_ERR_INVALID_ARG;

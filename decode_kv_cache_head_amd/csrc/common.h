@@ -61,10 +61,12 @@ struct Rows {
   int32_t lbs;  // log2(block size) when paged
   int32_t max_blocks;
   int32_t row_bytes;
+  int32_t off;  // added to every position (the first candidate position)
   // PAGED is a compile-time property of the launch, so the unrolled loads of
   // a tile stay in one basic block.
   template <bool PAGED>
   __device__ inline const char* row(int b, int h, int t) const {
+    t += off;
     if constexpr (PAGED) {
       const int blk = table[(int64_t)b * max_blocks + (t >> lbs)];
       return base + ((((int64_t)blk * hkv + h) << lbs) + (t & ((1 << lbs) - 1))) * row_bytes;
@@ -75,7 +77,7 @@ struct Rows {
 };
 
 // Number of candidate (aged / pool) tokens of (b, h).
-//   single step: clamp(ctx_len[b], 0, ctx_cap) - W, clamped to [0, cap]
+//   single step: clamp(ctx_len[b], 0, ctx_cap) - W - sinks, clamped to [0, cap]
 //   lifecycle:   count[b * Hkv + h], clamped to [0, cap]
 struct Cand {
   const int32_t* ctx_len;
@@ -84,6 +86,7 @@ struct Cand {
   int32_t ctx_cap;
   int32_t cap;
   int32_t hkv;
+  int32_t sinks;
   __device__ inline int n(int b, int h) const {
     int v;
     if (count) {
@@ -91,7 +94,7 @@ struct Cand {
     } else {
       int T = ctx_len[b];
       T = T < 0 ? 0 : (T > ctx_cap ? ctx_cap : T);
-      v = T - W;
+      v = T - W - sinks;
     }
     v = v < 0 ? 0 : v;
     return v > cap ? cap : v;
@@ -213,6 +216,10 @@ struct QPiece<bf16_t, bf16_t, 8> {
     return s;
   }
 };
+
+// Weight of an evicted token in attention-weighted merging: its calibrated
+// attention weight relative to the head's largest, floored at e^-60.
+__device__ inline float merge_weight(float c, float m) { return __expf(fmaxf(c - m, -60.f)); }
 
 // ------------------------------------------------------------ policy -----
 // Rewrite (0) or sparse loading (1) for a head with A aged tokens, k kept,

@@ -116,6 +116,14 @@ struct CompactArgs {
   int32_t* ccount;
   int chunk_stride;
   const uint8_t* mode;  // [B][Hkv]; HARDKV_MODE_SPARSE heads skip the row copies; may be null
+  int pos_off;          // position of candidate 0 (the sink count)
+  // weighted merging (merge == HARDKV_MERGE_WEIGHTED): per-token weights from
+  // the selection's scores and statistics
+  int merge;
+  const int8_t* metric;
+  const float* logit;
+  const float* l2;
+  const double* stats;  // [B][Hkv][4] {shift, scale, max, Z}
   // fused attention over the kept rows (launch_compact_attn only)
   int G, hq;
   const void* q;        // [B][Hq][D]
@@ -134,6 +142,7 @@ struct AttnArgs {
   Rows dk, dv;
   const int32_t* ctx_len;  // single step
   int ctx_cap, W;
+  int sinks;               // single step: dense = [0, sinks) and [sinks + A, T)
   bool ring;
   // sparse tier
   Rows sk, sv;

@@ -35,14 +35,18 @@ struct Lay {
 
 struct TileCounts {
   int nd, ns, nc, ntd, nts, ntc;
-  int first;  // partial slots taken by the fused compaction's tiles
+  int first;     // partial slots taken by the fused compaction's tiles
+  int gap_at;    // dense entry r is position r, or r + gap_len from gap_at on
+  int gap_len;
 };
 
 __device__ inline TileCounts tile_counts(const AttnArgs& a, int b, int h) {
   TileCounts t;
   int T = a.ctx_len ? a.ctx_len[b] : 0;
   T = T < 0 ? 0 : (T > a.ctx_cap ? a.ctx_cap : T);
-  const int A = T > a.W ? T - a.W : 0;
+  const int A = T > a.W + a.sinks ? T - a.W - a.sinks : 0;  // candidates [S, S + A)
+  t.gap_at = a.sinks;
+  t.gap_len = a.ring ? 0 : A;
   if (a.ring) {
     t.nd = a.W;
     t.nc = a.chunk_cap;
@@ -71,12 +75,15 @@ __device__ inline TileCounts tile_counts(const AttnArgs& a, int b, int h) {
 // new maximum and accumulates p * v.  CHUNK: float32 sums with counts.
 // Lanes 0..LPR-1 end with the full numerator (EPL elements each).
 // IDX: entry r is row idx[r0 + r] of kr / vr (clamped to [0, idx_max]) --
-// sparse loading of kept rows from the cache.
+// sparse loading of kept rows from the cache.  Otherwise entry r is row
+// r0 + r, moved up by gap_len from row gap_at on (the dense tier skips the
+// candidate range).
 template <typename E, int D, int G, typename QT, bool CHUNK, bool P, bool IDX>
 __device__ inline void wave_attn(const QT* __restrict__ qg, const Rows& kr, const Rows& vr, int b,
                                  int h, int r0, int wn, const int32_t* __restrict__ cc,
-                                 const int32_t* __restrict__ idx, int idx_max, float scale,
-                                 float (&m)[G], float (&l)[G], float (&o)[G][Lay<E, D>::EPL]) {
+                                 const int32_t* __restrict__ idx, int idx_max, int gap_at,
+                                 int gap_len, float scale, float (&m)[G], float (&l)[G],
+                                 float (&o)[G][Lay<E, D>::EPL]) {
   using L = Lay<E, D>;
   constexpr int LPR = L::LPR, EPL = L::EPL, RPI = L::RPI;
   constexpr int IT = 8;
@@ -104,6 +111,7 @@ __device__ inline void wave_attn(const QT* __restrict__ qg, const Rows& kr, cons
         row[it] = t < 0 ? 0 : (t > idx_max ? idx_max : t);
       } else {
         row[it] = r0 + r;
+        if (row[it] >= gap_at) row[it] += gap_len;
       }
     }
 #pragma unroll
@@ -169,14 +177,15 @@ template <typename E, int D, int G, typename QT, bool CHUNK, bool P, bool IDX = 
 __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr, const Rows& vr,
                                  int b, int h, int r0, int nrows, const int32_t* cc, float* s_m,
                                  float* s_l, float* s_o, float* part_out,
-                                 const int32_t* idx = nullptr, int idx_max = 0) {
+                                 const int32_t* idx = nullptr, int idx_max = 0,
+                                 int gap_at = 0, int gap_len = 0) {
   using L = Lay<E, D>;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int wn = nrows - w * 64;
   wn = wn < 0 ? 0 : (wn > 64 ? 64 : wn);
   float m[G], l[G], o[G][L::EPL];
   wave_attn<E, D, G, QT, CHUNK, P, IDX>(qg, kr, vr, b, h, r0 + w * 64, wn, cc, idx, idx_max,
-                                        (float)a.scale, m, l, o);
+                                        gap_at, gap_len, (float)a.scale, m, l, o);
   if (lane < L::LPR) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -228,13 +237,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const T* qg = (const T*)a.q + ((int64_t)b * a.hq + (int64_t)h * G) * D;
   float* part_out = a.part + (bh * a.max_tiles + tc.first + x) * G * (D + 2);
   if (x < tc.ntd) {
-    int T_ = a.ctx_len ? a.ctx_len[b] : 0;
-    T_ = T_ < 0 ? 0 : (T_ > a.ctx_cap ? a.ctx_cap : T_);
-    const int roff = a.ring ? 0 : (T_ > a.W ? T_ - a.W : 0);
+    // dense entries: sinks [0, S), then the window from S + A (ring: slots)
     const int r0 = x * kAttnTile;
-    tile_attn<T, D, G, T, false, P>(a, qg, a.dk, a.dv, b, h, roff + r0,
-                                 min(kAttnTile, tc.nd - r0), nullptr, s_m, s_l, s_o,
-                                 part_out);
+    tile_attn<T, D, G, T, false, P>(a, qg, a.dk, a.dv, b, h, r0, min(kAttnTile, tc.nd - r0),
+                                    nullptr, s_m, s_l, s_o, part_out, nullptr, 0, tc.gap_at,
+                                    tc.gap_len);
   } else if (x < tc.ntd + tc.nts) {
     const int r0 = (x - tc.ntd) * kAttnTile;
     if (a.mode && a.mode[bh] == HARDKV_MODE_SPARSE) {
@@ -299,14 +306,16 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   for (int e = 0; e < PE; ++e) out[lane * PE + e] = S > 0.f ? O[e] / S : 0.f;
 }
 
+// W: dense rows at most (window plus sinks)
 int attn_max_tiles(int W, int sparse_cap, int chunk_cap) {
   return ceil_div(W, kAttnTile) + ceil_div(sparse_cap, kAttnTile) + ceil_div(chunk_cap, kAttnTile);
 }
 
 template <typename T, int D, int G, bool P>
 static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
-  const int gx = a.fused_tt > 0 ? ceil_div(a.W, kAttnTile) + ceil_div(a.chunk_cap, kAttnTile)
-                                : a.max_tiles;
+  const int gx = a.fused_tt > 0
+                     ? ceil_div(a.W + a.sinks, kAttnTile) + ceil_div(a.chunk_cap, kAttnTile)
+                     : a.max_tiles;
   if (gx > 0) {
     observe("k_attn", st);
     hipLaunchKernelGGL((k_attn<T, D, G, P>), dim3(gx, a.hkv, a.B), dim3(256), 0, st, a);

@@ -28,6 +28,30 @@
 
 namespace hk {
 
+// Per-token weights of attention-weighted merging for one (b, h): the
+// token's calibrated value c from the selection's scores and statistics.
+struct MergeW {
+  const float* x;
+  double shift, scale;
+  float m;
+  bool on;
+  __device__ inline float at(int t) const { return merge_weight(cval(x[t], shift, scale), m); }
+};
+
+__device__ inline MergeW merge_w(const CompactArgs& a, int h, int64_t bh) {
+  MergeW r{};
+  r.on = a.merge == HARDKV_MERGE_WEIGHTED;
+  if (r.on) {
+    const bool l2 = a.metric != nullptr && a.metric[h] == HARDKV_METRIC_L2;
+    r.x = (l2 ? a.l2 : a.logit) + bh * a.cap_stride;
+    const double* st = a.stats + bh * 4;
+    r.shift = st[0];
+    r.scale = st[1];
+    r.m = (float)st[2];
+  }
+  return r;
+}
+
 __device__ inline int block_excl_scan_256(int v, int* sh, int& total) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   int incl = v;
@@ -59,6 +83,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
   __shared__ __attribute__((aligned(16))) unsigned char sv[64 * RB];
   __shared__ int s_rank[64];
   __shared__ int s_sel[64];
+  __shared__ float s_w[64];
   __shared__ int s_base;
   __shared__ int s_scan[4];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -88,12 +113,13 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
 
   const bool summer = tid < 2 * D;
   const int tensor = tid / D, dim = tid % D;
-  float acc = 0.f;
+  const MergeW mw = merge_w(a, h, bh);
+  float acc = 0.f, wsum = 0.f;
   int cnt = 0;
   int cur = t0 / a.C;
   auto flush = [&](int ch) {
     float* dst = (tensor ? a.vsum : a.ksum) + (bh * a.chunk_stride + ch) * D + dim;
-    *dst = acc;
+    *dst = mw.on ? (cnt > 0 ? acc * ((float)cnt / wsum) : 0.f) : acc;
     if (tid == 0) a.ccount[bh * a.chunk_stride + ch] = cnt;
   };
 
@@ -105,7 +131,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
       const int rk = base + __popcll(bal & ((1ull << tid) - 1ull));
       s_sel[tid] = sel;
       s_rank[tid] = rk;
-      if (sel) pos[rk] = s0 + tid;
+      if (sel) pos[rk] = a.pos_off + s0 + tid;
+      if (mw.on) s_w[tid] = tid < nr ? mw.at(s0 + tid) : 0.f;
       if (tid == 0) s_base = base + __popcll(bal);
     }
     v4u buf[PER];
@@ -138,10 +165,17 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
           flush(cur);
           cur = ch;
           acc = 0.f;
+          wsum = 0.f;
           cnt = 0;
         }
         if (!s_sel[r]) {
-          acc += Elt<T>::load1(src + r * D + dim);
+          const float x = Elt<T>::load1(src + r * D + dim);
+          if (mw.on) {
+            acc = fmaf(s_w[r], x, acc);
+            wsum += s_w[r];
+          } else {
+            acc += x;
+          }
           ++cnt;
         }
       }
@@ -162,7 +196,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
 // are added to per-thread float32 partial sums.  At the end of each chunk
 // the partials are reduced across row groups (lane shuffles, then the four
 // waves in a fixed order through LDS): deterministic.
-template <typename T, int D, int G, bool P, bool ATTN>
+template <typename T, int D, int G, bool P, bool ATTN, bool WMERGE>
 __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   constexpr int RB = D * (int)sizeof(T);
   constexpr int CPR = RB / 16;        // pieces per row
@@ -173,8 +207,9 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   constexpr int GA = ATTN ? G : 1;
   __shared__ int s_rank[1024];
   __shared__ float s_red[4][2][D];
+  __shared__ float s_wred[4];
   __shared__ int s_scan[4];
-  __shared__ int s_ev;
+  __shared__ int s_ev[2];  // evicted rows of the current chunk (alternating per chunk)
   __shared__ float s_am[4][GA], s_al[4][GA];
   __shared__ float s_ao[ATTN ? 4 * G * D : 1];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -220,14 +255,14 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
       if (r < nrows) {
         if ((flags >> q) & 1) {
           s_rank[r] = rk;
-          pos[rk] = t0 + r;
+          pos[rk] = a.pos_off + t0 + r;
           ++rk;
         } else {
           s_rank[r] = -1;
         }
       }
     }
-    if (tid == 0) s_ev = 0;
+    if (tid == 0) s_ev[0] = s_ev[1] = 0;
     if (t0 + nrows == n && tid == 255) a.out_count[bh] = rk;
   }
   __syncthreads();
@@ -235,7 +270,11 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   const int c = tid % CPR, rg = tid / CPR;
   const int w = tid >> 6, lane = tid & 63;
   const int nsub = (nrows + 63) / 64;
+  MergeW mw{};
+  if constexpr (WMERGE) mw = merge_w(a, h, bh);
   float acc[2][EPC];
+  float wacc = 0.f;  // weighted merging: sum of this thread's evicted rows' weights
+  int nflush = 0;
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -312,6 +351,16 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
             *(v4u*)(ok + (int64_t)rk * RB + c * 16) = buf[i];
             *(v4u*)(ov + (int64_t)rk * RB + c * 16) = buf[RPT + i];
           }
+        } else if (WMERGE) {
+          const float wt = mw.at(t0 + r);
+          wacc += wt;
+          float f[EPC];
+          Elt<T>::unpack(buf[i], f);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[0][e] = fmaf(wt, f[e], acc[0][e]);
+          Elt<T>::unpack(buf[RPT + i], f);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[1][e] = fmaf(wt, f[e], acc[1][e]);
         } else {
           float f[EPC];
           Elt<T>::unpack(buf[i], f);
@@ -343,20 +392,34 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
 #pragma unroll
           for (int e = 0; e < EPC; ++e) s_red[w][q][c * EPC + e] = acc[q][e];
       }
+      if (WMERGE) {
+        float v = wacc;
+#pragma unroll
+        for (int o = CPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0) s_wred[w] = v;
+      }
       // evicted rows of the chunk
+      const int par = nflush & 1;
       int ev = 0;
       for (int r = cs + tid; r < rows_done; r += 256) ev += s_rank[r] < 0;
-      if (ev) atomicAdd(&s_ev, ev);
+      if (ev) atomicAdd(&s_ev[par], ev);
       __syncthreads();
+      const int nev = s_ev[par];
       if (tid < 2 * D) {
         const int q = tid / D, dim = tid % D;
-        const float v = ((s_red[0][q][dim] + s_red[1][q][dim]) + s_red[2][q][dim]) + s_red[3][q][dim];
+        float v = ((s_red[0][q][dim] + s_red[1][q][dim]) + s_red[2][q][dim]) + s_red[3][q][dim];
+        if (WMERGE) {
+          const float wt = ((s_wred[0] + s_wred[1]) + s_wred[2]) + s_wred[3];
+          v = nev > 0 ? v * ((float)nev / wt) : 0.f;
+        }
         (q ? a.vsum : a.ksum)[(bh * a.chunk_stride + ch) * D + dim] = v;
       }
       if (tid == 0) {
-        a.ccount[bh * a.chunk_stride + ch] = s_ev;
-        s_ev = 0;
+        a.ccount[bh * a.chunk_stride + ch] = nev;
+        s_ev[par ^ 1] = 0;  // the next chunk's counter; its last reader passed a barrier
       }
+      ++nflush;
+      wacc = 0.f;
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -434,8 +497,12 @@ static void launch_compact_t(const CompactArgs& a, hipStream_t st) {
   const int nt = max(1, ceil_div(a.max_cand, TT));  // tile 0 also writes count = 0
   if (compact_fusable(a.C)) {
     observe("k_compact_fast", st);
-    hipLaunchKernelGGL((k_compact_fast<T, D, 1, P, false>), dim3(nt, a.hkv, a.B), dim3(256), 0, st,
-                       a, TT);
+    if (a.merge == HARDKV_MERGE_WEIGHTED)
+      hipLaunchKernelGGL((k_compact_fast<T, D, 1, P, false, true>), dim3(nt, a.hkv, a.B),
+                         dim3(256), 0, st, a, TT);
+    else
+      hipLaunchKernelGGL((k_compact_fast<T, D, 1, P, false, false>), dim3(nt, a.hkv, a.B),
+                         dim3(256), 0, st, a, TT);
   } else {
     observe("k_compact", st);
     hipLaunchKernelGGL((k_compact<T, D, P>), dim3(nt, a.hkv, a.B), dim3(256), 0, st, a, TT);
@@ -451,8 +518,12 @@ static void launch_compact_attn_t(const CompactArgs& a, hipStream_t st) {
   const int TT = compact_tile(a.C);
   const int nt = max(1, ceil_div(a.max_cand, TT));
   observe("k_compact_attn", st);
-  hipLaunchKernelGGL((k_compact_fast<T, D, G, P, true>), dim3(nt, a.hkv, a.B), dim3(256), 0, st,
-                     a, TT);
+  if (a.merge == HARDKV_MERGE_WEIGHTED)
+    hipLaunchKernelGGL((k_compact_fast<T, D, G, P, true, true>), dim3(nt, a.hkv, a.B),
+                       dim3(256), 0, st, a, TT);
+  else
+    hipLaunchKernelGGL((k_compact_fast<T, D, G, P, true, false>), dim3(nt, a.hkv, a.B),
+                       dim3(256), 0, st, a, TT);
 }
 
 void launch_compact_attn(const CompactArgs& a, hipStream_t st) {

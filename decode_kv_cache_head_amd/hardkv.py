@@ -21,6 +21,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = 0, 
 F32, BF16 = 0, 1
 METRIC_QK, METRIC_L2 = 0, 1
 MODE_REWRITE, MODE_SPARSE = 0, 1
+MERGE_MEAN, MERGE_WEIGHTED = 0, 1
 POLICY_REWRITE, POLICY_SPARSE, POLICY_MTI = 0, 1, 2
 INT32_MAX = 2 ** 31 - 1
 
@@ -41,7 +42,7 @@ class Desc(ctypes.Structure):
                 ("chunk", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("ctx_cap", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
                 ("sparse_cap", ctypes.c_int32), ("chunk_cap", ctypes.c_int32),
-                ("top_p", ctypes.c_float)]
+                ("top_p", ctypes.c_float), ("sinks", ctypes.c_int32), ("merge", ctypes.c_int32)]
 
 
 class Cache(ctypes.Structure):
@@ -82,6 +83,8 @@ _SIGS = {
                             ctypes.c_size_t, _P], ctypes.c_int),
     "hardkv_compact": ([ctypes.POINTER(Desc), ctypes.POINTER(Cache), _P, ctypes.POINTER(TiersC),
                         _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hardkv_compact_scored": ([ctypes.POINTER(Desc), ctypes.POINTER(Cache), _P, _P, _P, _P, _P,
+                               ctypes.POINTER(TiersC), _P, ctypes.c_size_t, _P], ctypes.c_int),
     "hardkv_decode_attn": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(Cache),
                             ctypes.POINTER(TiersC), _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "hardkv_step": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(Cache), _P,
@@ -129,14 +132,14 @@ def _check(rc, fn):
 
 
 def make_desc(B, Hq, Hkv, d, dtype, W, C, top_p, ctx_cap, block_size=0, max_blocks=0,
-              sparse_cap=None, chunk_cap=None) -> Desc:
-    A = max(ctx_cap - W, 0)
+              sparse_cap=None, chunk_cap=None, sinks=0, merge=MERGE_MEAN) -> Desc:
+    A = max(ctx_cap - W - sinks, 0)
     if sparse_cap is None:
         sparse_cap = A
     if chunk_cap is None:
         chunk_cap = -(-A // C) if C > 0 else 0
     return Desc(B, Hq, Hkv, d, dtype, W, C, block_size, ctx_cap, max_blocks, sparse_cap,
-                chunk_cap, float(top_p))
+                chunk_cap, float(top_p), sinks, merge)
 
 
 def validate(desc: Desc) -> int:
@@ -218,6 +221,15 @@ def compact(desc, cache: Cache, mask, tiers: Tiers, ws, stream=None):
     rc = load().hardkv_compact(ctypes.byref(desc), ctypes.byref(cache), _p(mask), ctypes.byref(tc),
                                _p(ws), ws.numel(), _stream(stream))
     _check(rc, "hardkv_compact")
+
+
+def compact_scored(desc, cache: Cache, metric, logit, l2, stats, mask, tiers: Tiers, ws,
+                   stream=None):
+    tc = tiers.c()
+    rc = load().hardkv_compact_scored(ctypes.byref(desc), ctypes.byref(cache), _p(metric),
+                                      _p(logit), _p(l2), _p(stats), _p(mask), ctypes.byref(tc),
+                                      _p(ws), ws.numel(), _stream(stream))
+    _check(rc, "hardkv_compact_scored")
 
 
 def decode_attn(desc, q, cache: Cache, tiers: Tiers, out, ws, stream=None):

@@ -45,6 +45,8 @@ class Workload:
     peaked_zipf: float = 1.2
     peaked_top: float = 24.0
     seed: int = 20260627
+    sinks: int = 0       # leading positions kept in the dense tier
+    merge: int = 0       # 0 mean, 1 attention-weighted merging of evicted tokens
 
     @property
     def G(self):

@@ -36,7 +36,8 @@
  *   - Shapes: B sequences, Hq query heads, Hkv KV heads, G = Hq / Hkv query
  *     heads per KV head (query head g belongs to KV head g / G), d head dim,
  *     T_b context length of sequence b (current token included), W dense
- *     window, C chunk size, A_b = max(T_b - W, 0) aged tokens.
+ *     window, S sink tokens, C chunk size, A_b = max(T_b - W - S, 0) aged
+ *     tokens (the candidates, positions [S, S + A_b)).
  *   - Thread safety: the only global state is the optional launch observer;
  *     calls on distinct streams with distinct buffers may run concurrently.
  */
@@ -67,6 +68,10 @@ typedef struct ihipStream_t* hardkv_stream_t; /* same type as hipStream_t */
 /* Importance metric per KV head. */
 #define HARDKV_METRIC_QK 0 /* max over the GQA group of q.k / sqrt(d) ("max-pooled logits") */
 #define HARDKV_METRIC_L2 1 /* key L2 norm, calibrated onto the head's logit spread */
+
+/* How evicted tokens are merged into a condensed chunk (hardkv_desc.merge). */
+#define HARDKV_MERGE_MEAN 0     /* plain mean of the chunk's evicted tokens */
+#define HARDKV_MERGE_WEIGHTED 1 /* mean weighted by each token's calibrated attention weight */
 
 /* How a head's selection is served (per head, device byte). */
 #define HARDKV_MODE_REWRITE 0 /* kept rows copied into the tier's contiguous slots */
@@ -104,9 +109,16 @@ typedef struct hardkv_desc {
   int32_t block_size;   /* 0: contiguous cache; > 0: paged cache with this many tokens per block */
   int32_t ctx_cap;      /* largest allowed T_b; contiguous: token stride of the cache per (b, h) */
   int32_t max_blocks;   /* paged: entries per block-table row; ctx_cap <= max_blocks * block_size */
-  int32_t sparse_cap;   /* sparse slots per (b, h); >= max(ctx_cap - W, 0) */
-  int32_t chunk_cap;    /* chunk slots per (b, h); >= ceil(max(ctx_cap - W, 0) / C) */
+  int32_t sparse_cap;   /* sparse slots per (b, h); >= max(ctx_cap - W - S, 0) */
+  int32_t chunk_cap;    /* chunk slots per (b, h); >= ceil(max(ctx_cap - W - S, 0) / C) */
   float top_p;          /* p in (0, 1]; p = 1 keeps every aged token */
+  int32_t sinks;        /* S >= 0: positions [0, S) stay in the dense tier (attention sinks,
+                           section 2.A Tier 1); candidates are [S, T - W) and chunk j pools
+                           evicted positions [S + jC, S + (j+1)C).  0 = none */
+  int32_t merge;        /* HARDKV_MERGE_*: condensed chunks (section 2.A Tier 3) store
+                           n times the mean of their evicted keys / values, plain or weighted
+                           by a = exp(max(c - m, -60)), c the token's calibrated value and m
+                           the head's largest (float32); attention uses sum / n either way */
 } hardkv_desc;
 
 /* The KV cache of one layer.
@@ -224,14 +236,23 @@ int hardkv_topp_select(const hardkv_desc* desc, const int32_t* ctx_len, const in
  * t / C.  Writes every field of *out (count = number of mask bytes set),
  * except the k / v slots of heads whose out->mode byte is HARDKV_MODE_SPARSE
  * (out->mode is read, e.g. as written by hardkv_plan).
- * The tiers must not alias the cache. */
+ * The tiers must not alias the cache.  desc->merge must be HARDKV_MERGE_MEAN
+ * (weighted merging needs the scores: hardkv_compact_scored). */
 int hardkv_compact(const hardkv_desc* desc, const hardkv_cache* cache, const uint8_t* mask,
                    const hardkv_tiers* out, void* ws, size_t ws_bytes,
                    hardkv_stream_t stream);
 
+/* hardkv_compact with the scores and statistics of the selection at hand
+ * (as written by hardkv_score and hardkv_calibrate), which weighted merging
+ * needs; for HARDKV_MERGE_MEAN it equals hardkv_compact. */
+int hardkv_compact_scored(const hardkv_desc* desc, const hardkv_cache* cache,
+                          const int8_t* metric, const float* logit, const float* l2,
+                          const double* stats, const uint8_t* mask, const hardkv_tiers* out,
+                          void* ws, size_t ws_bytes, hardkv_stream_t stream);
+
 /* Decode attention over the three tiers (abstract; section 3, third
  * contribution).  For every query head g of (b, h = g / G): softmax over
- *   dense tokens [A_b, T_b) of the cache      logit q.k / sqrt(d), value v
+ *   dense tokens [0, S) and [S + A_b, T_b)    logit q.k / sqrt(d), value v
  *   sparse slots 0..count-1 of the tiers      logit q.k / sqrt(d), value v
  *     (HARDKV_MODE_SPARSE heads: cache rows at pos[0..count-1] instead)
  *   chunks j < ceil(A_b / C) with n = ccount > 0: logit q.(ksum / n) / sqrt(d) + ln n,
@@ -286,7 +307,7 @@ int hardkv_step_policy(const hardkv_desc* desc, const hardkv_policy* policy, con
  *   4. every dropped resident is added to the running sums of chunk pos / C;
  *   5. attention over the ring, the pool and the chunks -> out [B][Hq][d] f32;
  *   6. seq_len[b] += 1.
- * desc->block_size must be 0; ctx_cap bounds P + 1 and sizes the pool
+ * desc->block_size, desc->sinks and desc->merge must be 0; ctx_cap bounds P + 1 and sizes the pool
  * (sparse_cap >= ctx_cap - W) and the chunks (chunk_cap >= ceil((ctx_cap - W) / C)). */
 int hardkv_step_inplace(const hardkv_desc* desc, const void* q, const void* k_new,
                         const void* v_new, const int8_t* metric, const hardkv_state* state,

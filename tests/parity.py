@@ -34,7 +34,7 @@ def desc_for(case: S.Case, top_p=None, sparse_cap=None, chunk_cap=None) -> H.Des
     w = case.w
     return H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.W, w.C,
                        w.p if top_p is None else top_p, case.ctx_cap, w.block_size,
-                       case.max_blocks, sparse_cap, chunk_cap)
+                       case.max_blocks, sparse_cap, chunk_cap, w.sinks, w.merge)
 
 
 def cache_of(case: S.Case) -> H.Cache:
@@ -58,7 +58,7 @@ def run_stages(case: S.Case, desc: H.Desc):
     H.score(desc, case.q, cache, case.metric, logit, l2, ws)
     H.calibrate(desc, case.ctx_len, case.metric, logit, l2, stats, ws)
     H.topp_select(desc, case.ctx_len, case.metric, logit, l2, stats, mask, count, ws)
-    H.compact(desc, cache, mask, tiers, ws)
+    H.compact_scored(desc, cache, case.metric, logit, l2, stats, mask, tiers, ws)
     H.decode_attn(desc, case.q, cache, tiers, out, ws)
     torch.cuda.synchronize()
     return dict(logit=logit, l2=l2, stats=stats, mask=mask, count=count, tiers=tiers, out=out)
@@ -81,7 +81,7 @@ def oracle_head(case: S.Case, b: int, h: int, p: float):
     q = case.q[b, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
     K = S.head_rows(case, b, h, "k").float().cpu().numpy()
     V = S.head_rows(case, b, h, "v").float().cpu().numpy()
-    ref = O.step_head(q, K, V, w.T[b], w.W, w.C, p, int(w.metrics[h]))
+    ref = O.step_head(q, K, V, w.T[b], w.W, w.C, p, int(w.metrics[h]), w.sinks, w.merge)
     return q, K, V, ref
 
 
@@ -92,6 +92,7 @@ def _ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 
 
 def borderline_tokens(ref: O.HeadResult, p: float, tokens) -> np.ndarray:
+    """tokens: candidate indices (position - sinks)."""
     sel = ref.sel
     A = ref.A
     p32 = float(np.float32(p))
@@ -116,6 +117,7 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
     w = case.w
     q, K, V, ref = oracle_head(case, b, h, p)
     A = ref.A
+    S = ref.sinks
     G, d = w.G, w.d
     is_l2 = int(w.metrics[h]) == O.METRIC_L2
     if stages:
@@ -139,12 +141,12 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
     tiers = gpu["tiers"]
     k_gpu = int(tiers.count[b, h])
     pos_gpu = tiers.pos[b, h, :k_gpu].cpu().numpy().astype(np.int64)
-    assert np.all(np.diff(pos_gpu) > 0) and (k_gpu == 0 or (pos_gpu[0] >= 0 and pos_gpu[-1] < A))
+    assert np.all(np.diff(pos_gpu) > 0) and (k_gpu == 0 or (pos_gpu[0] >= S and pos_gpu[-1] < S + A))
     if stages:
-        assert np.array_equal(pos_gpu, np.nonzero(gm)[0])
-    diff = np.setxor1d(pos_gpu, ref.sel.selected)
+        assert np.array_equal(pos_gpu, S + np.nonzero(gm)[0])
+    diff = np.setxor1d(pos_gpu, ref.pos)
     if diff.size:
-        bl = borderline_tokens(ref, p, diff)
+        bl = borderline_tokens(ref, p, diff - S)
         assert bl.all(), f"non-borderline set mismatch at ({b},{h}): {diff[~bl][:10]}"
         report["borderline"] += int(diff.size)
     else:
@@ -169,13 +171,18 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
     cc = tiers.ccount[b, h, :nch].cpu().numpy()
     ks = tiers.ksum[b, h, :nch].double().cpu().numpy()
     vs = tiers.vsum[b, h, :nch].double().cpu().numpy()
-    evicted_gpu = np.setdiff1d(np.arange(A), pos_gpu)
+    evicted_gpu = np.setdiff1d(S + np.arange(A), pos_gpu)
+    wts = None
+    if w.merge == O.MERGE_WEIGHTED:
+        wts = O.merge_weights(ref.cal.c[evicted_gpu - S], ref.cal.m)
+    allpos = np.arange(w.T[b])
     if diff.size:
-        ek, ev, ec = O.condense(K, V, evicted_gpu, np.arange(A), w.C, nch)
+        ek, ev, ec = O.condense(K, V, evicted_gpu, allpos, w.C, nch, wts, origin=S)
     else:
         ek, ev, ec = ref.ksum, ref.vsum, ref.cnt
     assert np.array_equal(cc, ec)
-    ak, av, _ = O.condense(np.abs(K), np.abs(V), evicted_gpu, np.arange(A), w.C, nch)
+    # bound: SUM_TOL times the same merge of |x| (n * weighted mean of |x|)
+    ak, av, _ = O.condense(np.abs(K), np.abs(V), evicted_gpu, allpos, w.C, nch, wts, origin=S)
     assert np.all(np.abs(ks - ek) <= SUM_TOL * ak + 1e-30)
     assert np.all(np.abs(vs - ev) <= SUM_TOL * av + 1e-30)
     # attention
@@ -183,7 +190,8 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
     if diff.size:
         Kc = K[pos_gpu]
         Vc = V[pos_gpu]
-        o_ref = O.attend_head(q, K[A:w.T[b]], V[A:w.T[b]], Kc, Vc, ks, vs, cc)
+        dense = O.dense_positions(w.T[b], S, A)
+        o_ref = O.attend_head(q, K[dense], V[dense], Kc, Vc, ks, vs, cc)
         report["staged_attn"] += 1
     else:
         o_ref = ref.out
@@ -216,7 +224,7 @@ def check_all_heads_invariants(case, desc, gpu):
     evicted = aged, counts within capacity, positions strictly increasing."""
     w = case.w
     t = gpu["tiers"]
-    A = torch.clamp(case.ctx_len.long() - w.W, min=0)
+    A = torch.clamp(case.ctx_len.long() - w.W - w.sinks, min=0)
     cnt = t.count.long()
     assert torch.all(cnt >= 0) and torch.all(cnt <= A[:, None])
     nch_max = desc.chunk_cap
@@ -229,3 +237,5 @@ def check_all_heads_invariants(case, desc, gpu):
     slot = torch.arange(desc.sparse_cap, device=pos.device)
     live = slot[None, None, 1:] < cnt[..., None]
     assert torch.all((pos[..., 1:] > pos[..., :-1]) | ~live)
+    # sink positions never leave the dense tier
+    assert torch.all((pos >= w.sinks) | ~(slot[None, None, :] < cnt[..., None]))

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = H.load()
-    assert lib.hardkv_version() == 10100
+    assert lib.hardkv_version() == 10200
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.hardkv_strerror(code)
     assert lib.hardkv_strerror(99) == b"unknown error"
@@ -40,7 +40,8 @@ def base_desc(**kw):
     d.update(kw)
     return H.make_desc(d["B"], d["Hq"], d["Hkv"], d["d"], d["dtype"], d["W"], d["C"], d["top_p"],
                        d["ctx_cap"], d.get("block_size", 0), d.get("max_blocks", 0),
-                       d.get("sparse_cap"), d.get("chunk_cap"))
+                       d.get("sparse_cap"), d.get("chunk_cap"), d.get("sinks", 0),
+                       d.get("merge", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -65,6 +66,13 @@ def base_desc(**kw):
     (dict(B=0), H.ERR_INVALID_ARG),
     (dict(ctx_cap=0), H.ERR_INVALID_ARG),
     (dict(W=2000), H.OK),                          # everything dense
+    (dict(sinks=4), H.OK),
+    (dict(sinks=-1), H.ERR_INVALID_ARG),
+    (dict(sinks=100, sparse_cap=835), H.ERR_CAPACITY),  # 1000 - 64 - 100 = 836 candidates
+    (dict(sinks=100, sparse_cap=836), H.OK),
+    (dict(sinks=2000), H.OK),                      # sinks and window cover everything
+    (dict(merge=1), H.OK),
+    (dict(merge=2), H.ERR_INVALID_ARG),
 ])
 def test_validate_codes(kw, code):
     assert H.validate(base_desc(**kw)) == code
@@ -175,3 +183,32 @@ def test_host_plan_matches_oracle_reading():
         sparse = (A + W) * (3 * A + 2 * W) + (N - 1) * (A + W) * 2 * (k + W)
         rewrite = (A + W + k) * (3 * A + 2 * W + 2 * k) + (N - 1) * (k + W) * 2 * (k + W)
         assert (rewrite, sparse) == O.mti_head(A, k, W, N)
+
+
+def test_sinks_and_merge_errors_before_launch():
+    lib = H.load()
+    fake = ctypes.c_void_p(0x1000)
+    cache = H.Cache(fake, fake, None, fake)
+    tiers = H.TiersC(*([fake] * 7))
+    st = ctypes.c_void_p(0)
+    weighted = base_desc(merge=H.MERGE_WEIGHTED)
+    need = H.workspace_size(weighted)
+    d = ctypes.byref(weighted)
+    # weighted merging needs the scores: plain hardkv_compact refuses it
+    assert lib.hardkv_compact(d, ctypes.byref(cache), fake, ctypes.byref(tiers), fake, need,
+                              st) == H.ERR_INVALID_ARG
+    for args in ((None, None, fake, fake), (None, fake, fake, None), (fake, fake, None, fake)):
+        metric, logit, l2, stats = args
+        assert lib.hardkv_compact_scored(d, ctypes.byref(cache), metric, logit, l2, stats, fake,
+                                         ctypes.byref(tiers), fake, need, st) == H.ERR_INVALID_ARG
+    assert lib.hardkv_compact_scored(d, ctypes.byref(cache), None, fake, None, fake, fake,
+                                     ctypes.byref(tiers), fake, need - 1, st) == H.ERR_WORKSPACE
+    # the lifecycle has neither sinks nor weighted merging
+    for desc in (base_desc(sinks=8), weighted):
+        state = H.StateC(fake, fake, tiers, fake)
+        assert lib.hardkv_step_inplace(ctypes.byref(desc), fake, fake, fake, None,
+                                       ctypes.byref(state), fake, fake, H.workspace_size(desc),
+                                       st) == H.ERR_INVALID_ARG
+    # sinks add dense tiles: at equal capacities the workspace grows with them
+    assert H.workspace_size(base_desc(sinks=300, sparse_cap=936, chunk_cap=30)) > \
+        H.workspace_size(base_desc())

@@ -59,6 +59,14 @@ GRID = [
     dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=1, C=64, p=0.85, block_size=64),
     dict(dtype=S.DT_F32, d=64, Hq=4, Hkv=4, C=192, p=0.6, T=(2500, 1000, 70)),
     dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=1024, p=0.9, T=(2600, 1300, 1090)),
+    # attention sinks and attention-weighted merging
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.9, sinks=4, merge=1, block_size=16),
+    dict(dtype=S.DT_F32, d=64, Hq=4, Hkv=2, C=7, p=0.8, sinks=37, merge=1),
+    dict(dtype=S.DT_BF16, d=128, Hq=16, Hkv=2, C=128, p=0.7, sinks=300,
+         metric=(S.METRIC_QK, S.METRIC_L2)),
+    dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=4, C=64, p=0.95, sinks=1, merge=1,
+         metric=(S.METRIC_L2, S.METRIC_QK, S.METRIC_L2, S.METRIC_QK)),
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=192, p=0.6, merge=1, T=(2500, 1000, 400)),
 ]
 
 
@@ -180,6 +188,19 @@ def test_headline_b32_16k_paged(gpu):
     g = run_step(case, desc)
     check_all_heads_invariants(case, desc, g)
     rep = check_case(case, g, w.p, heads=_sample_heads(w, 10, 1), stages=False)
+    say(rep)
+
+
+def test_headline_with_sinks_and_weighted_merging(gpu):
+    """The headline shape with 4 sink tokens and attention-weighted merging:
+    sampled heads against the oracle, invariants on every head."""
+    w = S.workload("qwen8b_b32_16k_paged", sinks=4, merge=1)
+    say(w.name, "sinks", w.sinks, "merge", w.merge)
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_step(case, desc)
+    check_all_heads_invariants(case, desc, g)
+    rep = check_case(case, g, w.p, heads=_sample_heads(w, 6, 2), stages=False)
     say(rep)
 
 

@@ -43,7 +43,7 @@ def oracle_modes(case, desc, count, pol):
     w = case.w
     modes = np.empty((w.B, w.Hkv), np.uint8)
     for b in range(w.B):
-        A = min(max(int(case.ctx_len[b]) - desc.dense_window, 0), desc.sparse_cap)
+        A = min(max(int(case.ctx_len[b]) - desc.dense_window - desc.sinks, 0), desc.sparse_cap)
         for h in range(w.Hkv):
             modes[b, h] = O.plan_head(A, int(count[b, h]), desc.dense_window, pol.kind,
                                       pol.horizon, pol.l_lower, pol.l_upper)
@@ -133,6 +133,8 @@ GRID = [
     dict(dtype=S.DT_F32, d=64, Hq=16, Hkv=2, C=100, p=0.99, block_size=32),
     dict(dtype=S.DT_BF16, d=128, Hq=16, Hkv=4, C=64, p=0.9, peaked_heads=(0, 2),
          metric=(S.METRIC_QK, S.METRIC_QK, S.METRIC_L2, S.METRIC_L2), block_size=16),
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.8, sinks=4, merge=1, block_size=16),
+    dict(dtype=S.DT_F32, d=64, Hq=8, Hkv=2, C=7, p=0.9, sinks=33, merge=1),
 ]
 
 
@@ -209,7 +211,8 @@ def _reuse_check(case, desc, g, T_sel, steps, report, oracle_sel):
     for i in steps:
         ctx = (T_sel + i).to(torch.int32)
         d_i = H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.W + i, w.C, w.p, case.ctx_cap,
-                          w.block_size, case.max_blocks, desc.sparse_cap, desc.chunk_cap)
+                          w.block_size, case.max_blocks, desc.sparse_cap, desc.chunk_cap,
+                          w.sinks, w.merge)
         ws = H.alloc_workspace(d_i, dev)
         qn = S._randn((w.B, w.Hq, w.d), w, dev, "reuse_q", i).to(case.q.dtype)
         out = torch.full((w.B, w.Hq, w.d), float("nan"), device=dev)
@@ -219,7 +222,8 @@ def _reuse_check(case, desc, g, T_sel, steps, report, oracle_sel):
         for b in range(w.B):
             Ts = int(T_sel[b])
             Tn = int(ctx[b])
-            A = max(Ts - w.W, 0)
+            A = max(Ts - w.W - w.sinks, 0)
+            dense = O.dense_positions(Tn, w.sinks, A)
             for h in range(w.Hkv):
                 K = S.head_rows(case, b, h, "k").float().cpu().numpy()
                 V = S.head_rows(case, b, h, "v").float().cpu().numpy()
@@ -232,7 +236,7 @@ def _reuse_check(case, desc, g, T_sel, steps, report, oracle_sel):
                     report["oracle_reuse"] += 1
                 else:
                     nch = -(-A // w.C) if A else 0
-                    o_ref = O.attend_head(q, K[A:Tn], V[A:Tn], K[pos], V[pos],
+                    o_ref = O.attend_head(q, K[dense], V[dense], K[pos], V[pos],
                                           tiers.ksum[b, h, :nch].double().cpu().numpy(),
                                           tiers.vsum[b, h, :nch].double().cpu().numpy(),
                                           tiers.ccount[b, h, :nch].cpu().numpy())
@@ -245,7 +249,8 @@ def _reuse_check(case, desc, g, T_sel, steps, report, oracle_sel):
 
 
 @pytest.mark.parametrize("kw", [dict(C=64, block_size=16), dict(C=7, dtype=S.DT_F32),
-                                dict(C=64, peaked_heads=(1,), W=128)])
+                                dict(C=64, peaked_heads=(1,), W=128),
+                                dict(C=64, block_size=16, sinks=5, merge=1)])
 def test_reuse_steps(gpu, kw):
     # sequences long enough to grow by 40 tokens past the selection
     R = 40
@@ -266,7 +271,7 @@ def test_reuse_steps(gpu, kw):
             K = S.head_rows(case, b, h, "k").float().cpu().numpy()
             V = S.head_rows(case, b, h, "v").float().cpu().numpy()
             oracle_sel[(b, h)] = O.step_head(q, K, V, wsel.T[b], w.W, w.C, w.p,
-                                             int(w.metrics[h]))
+                                             int(w.metrics[h]), w.sinks, w.merge)
     rep = new_report()
     rep["oracle_reuse"] = 0
     full = S.Case(w, case.q, case.k, case.v, case.ctx_len, case.block_table, case.metric,
