@@ -117,7 +117,7 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
     w = case.w
     q, K, V, ref = oracle_head(case, b, h, p)
     A = ref.A
-    S = ref.sinks
+    s0 = ref.sinks  # sink count: candidate index i is position s0 + i
     G, d = w.G, w.d
     is_l2 = int(w.metrics[h]) == O.METRIC_L2
     if stages:
@@ -141,12 +141,12 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
     tiers = gpu["tiers"]
     k_gpu = int(tiers.count[b, h])
     pos_gpu = tiers.pos[b, h, :k_gpu].cpu().numpy().astype(np.int64)
-    assert np.all(np.diff(pos_gpu) > 0) and (k_gpu == 0 or (pos_gpu[0] >= S and pos_gpu[-1] < S + A))
+    assert np.all(np.diff(pos_gpu) > 0) and (k_gpu == 0 or (pos_gpu[0] >= s0 and pos_gpu[-1] < s0 + A))
     if stages:
-        assert np.array_equal(pos_gpu, S + np.nonzero(gm)[0])
+        assert np.array_equal(pos_gpu, s0 + np.nonzero(gm)[0])
     diff = np.setxor1d(pos_gpu, ref.pos)
     if diff.size:
-        bl = borderline_tokens(ref, p, diff - S)
+        bl = borderline_tokens(ref, p, diff - s0)
         assert bl.all(), f"non-borderline set mismatch at ({b},{h}): {diff[~bl][:10]}"
         report["borderline"] += int(diff.size)
     else:
@@ -171,18 +171,18 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
     cc = tiers.ccount[b, h, :nch].cpu().numpy()
     ks = tiers.ksum[b, h, :nch].double().cpu().numpy()
     vs = tiers.vsum[b, h, :nch].double().cpu().numpy()
-    evicted_gpu = np.setdiff1d(S + np.arange(A), pos_gpu)
+    evicted_gpu = np.setdiff1d(s0 + np.arange(A), pos_gpu)
     wts = None
     if w.merge == O.MERGE_WEIGHTED:
-        wts = O.merge_weights(ref.cal.c[evicted_gpu - S], ref.cal.m)
+        wts = O.merge_weights(ref.cal.c[evicted_gpu - s0], ref.cal.m)
     allpos = np.arange(w.T[b])
     if diff.size:
-        ek, ev, ec = O.condense(K, V, evicted_gpu, allpos, w.C, nch, wts, origin=S)
+        ek, ev, ec = O.condense(K, V, evicted_gpu, allpos, w.C, nch, wts, origin=s0)
     else:
         ek, ev, ec = ref.ksum, ref.vsum, ref.cnt
     assert np.array_equal(cc, ec)
     # bound: SUM_TOL times the same merge of |x| (n * weighted mean of |x|)
-    ak, av, _ = O.condense(np.abs(K), np.abs(V), evicted_gpu, allpos, w.C, nch, wts, origin=S)
+    ak, av, _ = O.condense(np.abs(K), np.abs(V), evicted_gpu, allpos, w.C, nch, wts, origin=s0)
     assert np.all(np.abs(ks - ek) <= SUM_TOL * ak + 1e-30)
     assert np.all(np.abs(vs - ev) <= SUM_TOL * av + 1e-30)
     # attention
@@ -190,7 +190,7 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
     if diff.size:
         Kc = K[pos_gpu]
         Vc = V[pos_gpu]
-        dense = O.dense_positions(w.T[b], S, A)
+        dense = O.dense_positions(w.T[b], s0, A)
         o_ref = O.attend_head(q, K[dense], V[dense], Kc, Vc, ks, vs, cc)
         report["staged_attn"] += 1
     else:
