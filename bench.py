@@ -382,6 +382,18 @@ def main():
         "dtype_note": "bf16 q/K/V in HBM; float64 score accumulation, 2^-47 fixed-point "
                       "top-p masses, float32 attention",
     }
+    if not args.no_amortization and args.block_size is None:
+        # the step with attention sinks and / or attention-weighted merging
+        var = {}
+        for tag, kw in (("sinks4", dict(sinks=4)), ("weighted_merge", dict(merge=1)),
+                        ("sinks4_weighted_merge", dict(sinks=4, merge=1))):
+            dv = H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.W, w.C, w.p, case.ctx_cap,
+                             w.block_size, case.max_blocks, desc.sparse_cap, desc.chunk_cap,
+                             **kw)
+            wsv = H.alloc_workspace(dv, dev)
+            var[tag] = round(time_ms(lambda: H.step(dv, case.q, cache, case.metric, tiers, out,
+                                                    wsv), args.steps), 4)
+        res["variant_step_ms"] = var
     if not args.no_amortization:
         print("[bench] selection reuse", file=sys.stderr, flush=True)
         am = {w.name: amortization(w, case, args.steps)}
