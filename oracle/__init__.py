@@ -10,4 +10,5 @@ from .hardkv_oracle import (  # noqa: F401
     init_state, lifecycle_step, POLICY_REWRITE, POLICY_SPARSE, POLICY_MTI,
     MODE_REWRITE, MODE_SPARSE, mti_head, plan_head, reuse_head, MERGE_MEAN,
     MERGE_WEIGHTED, MERGE_FLOOR, merge_weights, candidate_range, dense_positions,
+    pack_heads,
 )

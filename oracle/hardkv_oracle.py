@@ -596,3 +596,35 @@ def reuse_head(q_group, K, V, T_now: int, sel: HeadResult):
     return attend_head(q_group, np.asarray(K)[dense], np.asarray(V)[dense],
                        np.asarray(K)[sel.pos], np.asarray(V)[sel.pos],
                        sel.ksum, sel.vsum, sel.cnt)
+
+
+# ---------------------------------------------------------------------------
+# Head-wise allocation of the rewritten tier (section 2.C, "Metadata": a
+# head-wise block manager for head-adaptive allocation under static shapes;
+# "Techniques": Flatten Index to the maximum length or to the sum).
+# ---------------------------------------------------------------------------
+def pack_heads(counts, modes, packed_rows: int):
+    """Offsets of every head's rewritten rows in one shared region.
+
+    Reading of the "sum" form of the Flatten Index: instead of a region of
+    the maximum length per head, the heads' kept rows are laid end to end in
+    one region of `packed_rows` rows, in (sequence, KV head) order.  A
+    rewritten head needs k rows, a sparse-loaded head none; head i starts at
+    the sum of the needs of the heads before it.  A rewritten head whose rows
+    would end past the region is served by sparse loading instead (its rows
+    stay in the cache), so every head's attention is unchanged.
+    counts, modes: [B][Hkv].  Returns (offsets int64 [B][Hkv], modes uint8).
+    """
+    counts = np.asarray(counts, np.int64)
+    modes = np.asarray(modes, np.uint8).copy()
+    flat_k = counts.ravel()
+    flat_m = modes.ravel()
+    offsets = np.zeros(flat_k.size, np.int64)
+    run = 0
+    for i in range(flat_k.size):
+        need = int(flat_k[i]) if flat_m[i] == MODE_REWRITE else 0
+        offsets[i] = run
+        if run + need > packed_rows:
+            flat_m[i] = MODE_SPARSE
+        run += need
+    return offsets.reshape(counts.shape), flat_m.reshape(modes.shape)

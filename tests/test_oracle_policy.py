@@ -160,3 +160,41 @@ def test_reuse_dense_tier_grows():
                            rtol=1e-12, atol=1e-13)
     with pytest.raises(ValueError):
         O.reuse_head(q, K, V, A - 1, r)
+
+
+# ------------------------------------------------------ packed region -------
+def test_pack_heads_worked_example():
+    # four heads, budgets 3, 5, 2, 4; the second is sparse-loaded
+    counts = np.array([[3, 5], [2, 4]])
+    modes = np.array([[0, 1], [0, 0]], np.uint8)
+    off, m = O.pack_heads(counts, modes, 100)
+    assert off.tolist() == [[0, 3], [3, 5]] and m.tolist() == modes.tolist()
+    # a region of 8 rows: heads 0 and 2 fit (rows 0-2, 3-4), head 3 (rows 5-8) does not
+    off, m = O.pack_heads(counts, modes, 8)
+    assert off.tolist() == [[0, 3], [3, 5]] and m.tolist() == [[0, 1], [0, 1]]
+    # exactly full
+    off, m = O.pack_heads(counts, modes, 9)
+    assert m.tolist() == [[0, 1], [0, 0]]
+
+
+def test_pack_heads_brute_force():
+    # against a direct enumeration of which prefix of rewritten heads fits
+    rng = np.random.default_rng(9)
+    for _ in range(300):
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        counts = rng.integers(0, 20, (B, H))
+        modes = (rng.random((B, H)) < 0.3).astype(np.uint8)
+        cap = int(rng.integers(0, 60))
+        off, m = O.pack_heads(counts, modes, cap)
+        k, md = counts.ravel(), modes.ravel()
+        for i in range(k.size):
+            before = sum(int(k[j]) for j in range(i) if md[j] == 0)
+            assert off.ravel()[i] == before
+            fits = md[i] == 0 and before + int(k[i]) <= cap
+            assert m.ravel()[i] == (0 if fits else 1)
+        # rewritten heads never overlap and stay inside the region
+        used = [(int(off.ravel()[i]), int(k[i])) for i in range(k.size) if m.ravel()[i] == 0]
+        for a, (o, n) in enumerate(used):
+            assert o + n <= cap
+            for o2, n2 in used[a + 1:]:
+                assert o + n <= o2 or o2 + n2 <= o
