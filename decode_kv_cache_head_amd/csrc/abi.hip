@@ -18,7 +18,7 @@ void hk::observe(const char* kernel, hipStream_t st) {
 
 namespace {
 
-constexpr int kVersion = 10200;  // 1.2.0
+constexpr int kVersion = 10300;  // 1.3.0
 
 int log2i(int v) {
   int l = 0;
@@ -51,6 +51,10 @@ int validate(const hardkv_desc* d) {
   if (d->sinks < 0 || (d->merge != HARDKV_MERGE_MEAN && d->merge != HARDKV_MERGE_WEIGHTED))
     return HARDKV_ERR_INVALID_ARG;
   if ((int64_t)d->dense_window + d->sinks > INT32_MAX / 2) return HARDKV_ERR_INVALID_ARG;
+  if (d->packed_rows < 0) return HARDKV_ERR_INVALID_ARG;
+  if (d->packed_rows > 0 &&
+      (int64_t)d->batch * d->num_kv_heads * (int64_t)d->sparse_cap >= ((int64_t)1 << 31))
+    return HARDKV_ERR_INVALID_ARG;
   if (d->sparse_cap < 0 || d->chunk_cap < 0) return HARDKV_ERR_INVALID_ARG;
   const int A = max_aged(d);
   if (d->sparse_cap < A) return HARDKV_ERR_CAPACITY;
@@ -195,6 +199,7 @@ CompactArgs compact_args(const hardkv_desc* d, const Layout& L, char* ws, const 
   a.ccount = t->ccount;
   a.chunk_stride = d->chunk_cap;
   a.mode = t->mode;
+  a.offset = d->packed_rows > 0 ? t->offset : nullptr;
   a.pos_off = d->sinks;
   a.merge = d->merge;
   a.G = d->num_q_heads / d->num_kv_heads;
@@ -225,6 +230,7 @@ AttnArgs attn_args(const hardkv_desc* d, const Layout& L, char* ws, const void* 
   a.sparse_cap = d->sparse_cap;
   a.mode = t->mode;
   a.pos = t->pos;
+  a.offset = d->packed_rows > 0 ? t->offset : nullptr;
   a.ksum = t->ksum;
   a.vsum = t->vsum;
   a.ccount = t->ccount;
@@ -240,6 +246,10 @@ AttnArgs attn_args(const hardkv_desc* d, const Layout& L, char* ws, const void* 
 
 bool tiers_ok(const hardkv_tiers* t) {
   return t && t->k && t->v && t->pos && t->count && t->ksum && t->vsum && t->ccount;
+}
+// ... and, for a packed rewritten tier, the offsets and the per-head modes
+bool tiers_ok(const hardkv_desc* d, const hardkv_tiers* t) {
+  return tiers_ok(t) && (d->packed_rows == 0 || (t->mode && t->offset));
 }
 bool cache_ok(const hardkv_desc* d, const hardkv_cache* c) {
   return c && c->k && c->v && c->ctx_len && (d->block_size == 0 || c->block_table);
@@ -286,6 +296,9 @@ void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
     launch_calibrate(sa, st);
     launch_select(sa, st);
   }
+  if (d->packed_rows > 0)
+    launch_pack(d->batch * d->num_kv_heads, count, max_aged(d), t.mode, t.offset,
+                d->packed_rows, st);
   CompactArgs ca = compact_args(d, L, w, kr, vr, cand, max_aged(d), mask, &t);
   ca.metric = metric;
   ca.logit = logit;
@@ -383,7 +396,7 @@ int hardkv_compact_scored(const hardkv_desc* d, const hardkv_cache* cache,
                           void* ws, size_t ws_bytes, hardkv_stream_t stream) {
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
-  if (!cache_ok(d, cache) || !mask || !tiers_ok(out)) return HARDKV_ERR_INVALID_ARG;
+  if (!cache_ok(d, cache) || !mask || !tiers_ok(d, out)) return HARDKV_ERR_INVALID_ARG;
   if (d->merge == HARDKV_MERGE_WEIGHTED && (!logit || !stats || (metric && !l2)))
     return HARDKV_ERR_INVALID_ARG;
   const Layout L = layout(d);
@@ -413,7 +426,7 @@ int hardkv_decode_attn(const hardkv_desc* d, const void* q, const hardkv_cache* 
                        hardkv_stream_t stream) {
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
-  if (!q || !cache_ok(d, cache) || !tiers_ok(tiers) || !out) return HARDKV_ERR_INVALID_ARG;
+  if (!q || !cache_ok(d, cache) || !tiers_ok(d, tiers) || !out) return HARDKV_ERR_INVALID_ARG;
   const Layout L = layout(d);
   AttnArgs a = attn_args(d, L, (char*)ws, q, tiers, out);
   a.dk = cache_rows(d, cache->k, cache->block_table);
@@ -439,12 +452,24 @@ int hardkv_plan(const hardkv_desc* d, const hardkv_policy* policy, const int32_t
   return launched();
 }
 
+int hardkv_pack(const hardkv_desc* d, const int32_t* count, const hardkv_tiers* tiers,
+                hardkv_stream_t stream) {
+  const int rc = validate(d);
+  if (rc) return rc;
+  if (d->packed_rows == 0 || !count || !tiers || !tiers->mode || !tiers->offset)
+    return HARDKV_ERR_INVALID_ARG;
+  hipGetLastError();
+  launch_pack(d->batch * d->num_kv_heads, count, max_aged(d), tiers->mode, tiers->offset,
+              d->packed_rows, (hipStream_t)stream);
+  return launched();
+}
+
 int hardkv_step(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
                 const int8_t* metric, const hardkv_tiers* tiers, float* out, void* ws,
                 size_t ws_bytes, hardkv_stream_t stream) {
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
-  if (!q || !cache_ok(d, cache) || !tiers_ok(tiers) || !out) return HARDKV_ERR_INVALID_ARG;
+  if (!q || !cache_ok(d, cache) || !tiers_ok(d, tiers) || !out) return HARDKV_ERR_INVALID_ARG;
   const hardkv_policy rewrite_all{HARDKV_POLICY_REWRITE, 1, 0, 0};
   run_step(d, &rewrite_all, q, cache, metric, tiers, out, ws, (hipStream_t)stream);
   return launched();
@@ -456,7 +481,7 @@ int hardkv_step_policy(const hardkv_desc* d, const hardkv_policy* policy, const 
                        hardkv_stream_t stream) {
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
-  if (!policy_ok(policy) || !q || !cache_ok(d, cache) || !tiers_ok(tiers) || !tiers->mode ||
+  if (!policy_ok(policy) || !q || !cache_ok(d, cache) || !tiers_ok(d, tiers) || !tiers->mode ||
       !out)
     return HARDKV_ERR_INVALID_ARG;
   run_step(d, policy, q, cache, metric, tiers, out, ws, (hipStream_t)stream);
@@ -469,7 +494,7 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
   if (d->block_size != 0 || d->dense_window < 1 || d->sinks != 0 ||
-      d->merge != HARDKV_MERGE_MEAN)
+      d->merge != HARDKV_MERGE_MEAN || d->packed_rows != 0)
     return HARDKV_ERR_INVALID_ARG;
   if (!q || !k_new || !v_new || !s || !s->ring_k || !s->ring_v || !s->seq_len ||
       !tiers_ok(&s->tiers) || s->tiers.mode || !out)

@@ -92,6 +92,9 @@ bool calsel_fits(int max_cand);
 void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st);
 // mode[b][h] from count[b][h] and the candidate count
 void launch_plan(const SelectArgs& a, hipStream_t st);
+// offsets of the packed rewritten tier (and overflow -> sparse loading)
+void launch_pack(int n_heads, const int32_t* count, int cap, uint8_t* mode, int32_t* offset,
+                 int packed_rows, hipStream_t st);
 
 // Tile of the single-step compaction: whole chunks, about 1024 tokens
 // (one chunk when a chunk is longer), processed in 64-row sub-tiles.
@@ -116,6 +119,7 @@ struct CompactArgs {
   int32_t* ccount;
   int chunk_stride;
   const uint8_t* mode;  // [B][Hkv]; HARDKV_MODE_SPARSE heads skip the row copies; may be null
+  const int32_t* offset;  // packed tier: head (b, h)'s slot 0 is row offset[b][h]; may be null
   int pos_off;          // position of candidate 0 (the sink count)
   // weighted merging (merge == HARDKV_MERGE_WEIGHTED): per-token weights from
   // the selection's scores and statistics
@@ -152,6 +156,7 @@ struct AttnArgs {
   // kept rows from the dense-tier rows (the cache) at pos; may be null
   const uint8_t* mode;
   const int32_t* pos;
+  const int32_t* offset;   // packed tier (see CompactArgs); may be null
   // condensed tier
   const float* ksum;
   const float* vsum;

@@ -249,6 +249,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       tile_attn<T, D, G, T, false, P, true>(a, qg, a.dk, a.dv, b, h, r0,
                                             min(kAttnTile, tc.ns - r0), nullptr, s_m, s_l, s_o,
                                             part_out, a.pos + bh * a.sparse_cap, a.ctx_cap - 1);
+    } else if (a.offset) {
+      // packed tier: this head's slots start at row offset[b][h]
+      Rows sk = a.sk, sv = a.sv;
+      sk.base += (int64_t)a.offset[bh] * sk.row_bytes;
+      sv.base += (int64_t)a.offset[bh] * sv.row_bytes;
+      sk.region = sv.region = 0;
+      tile_attn<T, D, G, T, false, false>(a, qg, sk, sv, b, h, r0, min(kAttnTile, tc.ns - r0),
+                                          nullptr, s_m, s_l, s_o, part_out);
     } else {
       tile_attn<T, D, G, T, false, false>(a, qg, a.sk, a.sv, b, h, r0,
                                           min(kAttnTile, tc.ns - r0), nullptr, s_m, s_l, s_o,

@@ -97,8 +97,9 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
   const int tend = min(t0 + TT, n);
   const bool copy_rows = a.mode == nullptr || a.mode[bh] == HARDKV_MODE_REWRITE;
   const uint8_t* mk = a.mask + bh * a.cap_stride;
-  char* ok = a.out_k + bh * a.cap_stride * RB;
-  char* ov = a.out_v + bh * a.cap_stride * RB;
+  const int64_t slot0 = a.offset ? (int64_t)a.offset[bh] : bh * a.cap_stride;
+  char* ok = a.out_k + slot0 * RB;
+  char* ov = a.out_v + slot0 * RB;
   int32_t* pos = a.out_pos + bh * a.cap_stride;
   // first destination slot of this tile: kept tokens before t0
   int base;
@@ -223,8 +224,9 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   const int nrows = min(TT, n - t0);
   const bool copy_rows = a.mode == nullptr || a.mode[bh] == HARDKV_MODE_REWRITE;
   const uint8_t* mk = a.mask + bh * a.cap_stride;
-  char* ok = a.out_k + bh * a.cap_stride * RB;
-  char* ov = a.out_v + bh * a.cap_stride * RB;
+  const int64_t slot0 = a.offset ? (int64_t)a.offset[bh] : bh * a.cap_stride;
+  char* ok = a.out_k + slot0 * RB;
+  char* ov = a.out_v + slot0 * RB;
   int32_t* pos = a.out_pos + bh * a.cap_stride;
 
   // kept tokens before the tile

@@ -507,6 +507,53 @@ void launch_plan(const SelectArgs& a, hipStream_t st) {
                      a.B, a.count, a.mode, a.policy);
 }
 
+// Exclusive scan of the rewritten heads' row needs in (b, h) order, one
+// workgroup, 1024 heads per round with the running total carried.
+__global__ __launch_bounds__(kSelThreads) void k_pack(int n_heads, const int32_t* __restrict__ count,
+                                                      int cap, uint8_t* __restrict__ mode,
+                                                      int32_t* __restrict__ offset,
+                                                      int packed_rows) {
+  __shared__ long long s_w[kSelWaves];
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+  long long run = 0;
+  for (int base = 0; base < n_heads; base += kSelThreads) {
+    const int i = base + tid;
+    const bool rw = i < n_heads && mode[i] == HARDKV_MODE_REWRITE;
+    int need = 0;
+    if (rw) {
+      const int k = count[i];
+      need = k < 0 ? 0 : (k > cap ? cap : k);
+    }
+    long long incl = need;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long u = __shfl_up(incl, o, 64);
+      if (ln >= o) incl += u;
+    }
+    if (ln == 63) s_w[wv] = incl;
+    __syncthreads();
+    long long before = run, total = run;
+    for (int j = 0; j < kSelWaves; ++j) {
+      if (j < wv) before += s_w[j];
+      total += s_w[j];
+    }
+    const long long off = before + incl - need;
+    if (i < n_heads) {
+      offset[i] = (int32_t)off;
+      if (rw && off + need > packed_rows) mode[i] = HARDKV_MODE_SPARSE;
+    }
+    run = total;
+    __syncthreads();
+  }
+}
+
+void launch_pack(int n_heads, const int32_t* count, int cap, uint8_t* mode, int32_t* offset,
+                 int packed_rows, hipStream_t st) {
+  observe("k_pack", st);
+  hipLaunchKernelGGL(k_pack, dim3(1), dim3(kSelThreads), 0, st, n_heads, count, cap, mode, offset,
+                     packed_rows);
+}
+
 bool calsel_fits(int max_cand) { return max_cand <= 16 * kSelThreads; }
 
 void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st) {

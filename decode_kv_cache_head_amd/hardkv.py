@@ -42,7 +42,8 @@ class Desc(ctypes.Structure):
                 ("chunk", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("ctx_cap", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
                 ("sparse_cap", ctypes.c_int32), ("chunk_cap", ctypes.c_int32),
-                ("top_p", ctypes.c_float), ("sinks", ctypes.c_int32), ("merge", ctypes.c_int32)]
+                ("top_p", ctypes.c_float), ("sinks", ctypes.c_int32), ("merge", ctypes.c_int32),
+                ("packed_rows", ctypes.c_int32)]
 
 
 class Cache(ctypes.Structure):
@@ -54,7 +55,7 @@ class TiersC(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
                 ("count", ctypes.c_void_p), ("ksum", ctypes.c_void_p),
                 ("vsum", ctypes.c_void_p), ("ccount", ctypes.c_void_p),
-                ("mode", ctypes.c_void_p)]
+                ("mode", ctypes.c_void_p), ("offset", ctypes.c_void_p)]
 
 
 class Policy(ctypes.Structure):
@@ -91,6 +92,7 @@ _SIGS = {
                      ctypes.POINTER(TiersC), _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "hardkv_plan": ([ctypes.POINTER(Desc), ctypes.POINTER(Policy), _P, _P, _P, _P],
                     ctypes.c_int),
+    "hardkv_pack": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(TiersC), _P], ctypes.c_int),
     "hardkv_step_policy": ([ctypes.POINTER(Desc), ctypes.POINTER(Policy), _P,
                             ctypes.POINTER(Cache), _P, ctypes.POINTER(TiersC), _P, _P,
                             ctypes.c_size_t, _P], ctypes.c_int),
@@ -132,14 +134,15 @@ def _check(rc, fn):
 
 
 def make_desc(B, Hq, Hkv, d, dtype, W, C, top_p, ctx_cap, block_size=0, max_blocks=0,
-              sparse_cap=None, chunk_cap=None, sinks=0, merge=MERGE_MEAN) -> Desc:
+              sparse_cap=None, chunk_cap=None, sinks=0, merge=MERGE_MEAN,
+              packed_rows=0) -> Desc:
     A = max(ctx_cap - W - sinks, 0)
     if sparse_cap is None:
         sparse_cap = A
     if chunk_cap is None:
         chunk_cap = -(-A // C) if C > 0 else 0
     return Desc(B, Hq, Hkv, d, dtype, W, C, block_size, ctx_cap, max_blocks, sparse_cap,
-                chunk_cap, float(top_p), sinks, merge)
+                chunk_cap, float(top_p), sinks, merge, packed_rows)
 
 
 def validate(desc: Desc) -> int:
@@ -167,26 +170,42 @@ class Tiers:
     vsum: torch.Tensor
     ccount: torch.Tensor
     mode: torch.Tensor | None = None   # [B][Hkv] uint8, None = every head rewritten
+    offset: torch.Tensor | None = None  # [B][Hkv] int32, packed tier only
 
     def c(self) -> TiersC:
         return TiersC(*(ctypes.c_void_p(t.data_ptr()) for t in
                         (self.k, self.v, self.pos, self.count, self.ksum, self.vsum, self.ccount)),
-                      _p(self.mode))
+                      _p(self.mode), _p(self.offset))
+
+    def slots(self, b, h, which="k"):
+        """Head (b, h)'s rewritten slots 0..count-1 (either layout)."""
+        src = self.k if which == "k" else self.v
+        n = int(self.count[b, h])
+        if self.offset is None:
+            return src[b, h, :n]
+        o = int(self.offset[b, h])
+        return src[o:o + n]
 
 
 def alloc_tiers(desc: Desc, device="cuda", zero=False, mode=False) -> Tiers:
+    """Tiers for `desc`; a packed desc (packed_rows > 0) gets one [packed_rows][d]
+    region for K and for V plus the offsets and modes it needs."""
     B, Hkv, d = desc.batch, desc.num_kv_heads, desc.head_dim
     dt = torch.float32 if desc.dtype == F32 else torch.bfloat16
     mk = torch.zeros if zero else torch.empty
     cap, ccap = desc.sparse_cap, desc.chunk_cap
-    return Tiers(mk((B, Hkv, cap, d), dtype=dt, device=device),
-                 mk((B, Hkv, cap, d), dtype=dt, device=device),
+    packed = desc.packed_rows > 0
+    rows = (desc.packed_rows, d) if packed else (B, Hkv, cap, d)
+    return Tiers(mk(rows, dtype=dt, device=device),
+                 mk(rows, dtype=dt, device=device),
                  mk((B, Hkv, cap), dtype=torch.int32, device=device),
                  mk((B, Hkv), dtype=torch.int32, device=device),
                  mk((B, Hkv, ccap, d), dtype=torch.float32, device=device),
                  mk((B, Hkv, ccap, d), dtype=torch.float32, device=device),
                  mk((B, Hkv, ccap), dtype=torch.int32, device=device),
-                 torch.zeros((B, Hkv), dtype=torch.uint8, device=device) if mode else None)
+                 torch.zeros((B, Hkv), dtype=torch.uint8, device=device)
+                 if (mode or packed) else None,
+                 torch.zeros((B, Hkv), dtype=torch.int32, device=device) if packed else None)
 
 
 def policy(kind=POLICY_MTI, horizon=1, l_lower=0, l_upper=INT32_MAX) -> Policy:
@@ -250,6 +269,12 @@ def plan(desc, pol: Policy, ctx_len, count, mode, stream=None):
     rc = load().hardkv_plan(ctypes.byref(desc), ctypes.byref(pol), _p(ctx_len), _p(count),
                             _p(mode), _stream(stream))
     _check(rc, "hardkv_plan")
+
+
+def pack(desc, count, tiers: Tiers, stream=None):
+    tc = tiers.c()
+    rc = load().hardkv_pack(ctypes.byref(desc), _p(count), ctypes.byref(tc), _stream(stream))
+    _check(rc, "hardkv_pack")
 
 
 def step_policy(desc, pol: Policy, q, cache: Cache, metric, tiers: Tiers, out, ws, stream=None):

@@ -119,6 +119,12 @@ typedef struct hardkv_desc {
                            n times the mean of their evicted keys / values, plain or weighted
                            by a = exp(max(c - m, -60)), c the token's calibrated value and m
                            the head's largest (float32); attention uses sum / n either way */
+  int32_t packed_rows;  /* 0: the rewritten tier has a region of sparse_cap rows per head
+                           (Flatten Index to the maximum length).  > 0: one region of this many
+                           rows shared by all heads, laid end to end in (b, h) order (Flatten
+                           Index to the sum; section 2.C, head-wise allocation under static
+                           shapes); needs tiers->offset and tiers->mode, and
+                           B * Hkv * sparse_cap < 2^31 */
 } hardkv_desc;
 
 /* The KV cache of one layer.
@@ -144,6 +150,9 @@ typedef struct hardkv_cache {
  *           A HARDKV_MODE_SPARSE head's k / v slots are neither written nor read:
  *           attention loads its kept rows from the cache at pos (Sparse Loading,
  *           section 2.C), so that cache must stay unchanged while the tiers are used.
+ *   offset: [B][Hkv] int32, packed layout only (desc->packed_rows > 0; else may be
+ *           NULL): k, v are then [packed_rows][d] and slot j of head (b, h) is row
+ *           offset[b][h] + j (hardkv_pack).
  * Single-step calls write chunk slots [0, ceil(A_b / C)); the rest is unspecified. */
 typedef struct hardkv_tiers {
   void* k;
@@ -154,6 +163,7 @@ typedef struct hardkv_tiers {
   float* vsum;
   int32_t* ccount;
   uint8_t* mode;
+  int32_t* offset;
 } hardkv_tiers;
 
 /* Persistent state of the multi-step lifecycle (one layer).
@@ -274,7 +284,8 @@ int hardkv_decode_attn(const hardkv_desc* desc, const void* q, const hardkv_cach
  * sparse tier is not read back; results equal hardkv_compact followed by
  * hardkv_decode_attn up to float32 summation order in the attention.
  *   metric: as in hardkv_score; tiers: written as by hardkv_compact, every
- *   head rewritten (tiers->mode, when given, is set to HARDKV_MODE_REWRITE);
+ *   head rewritten (tiers->mode, when given, is set to HARDKV_MODE_REWRITE;
+ *   with a packed tier, heads that do not fit are sparse-loaded, hardkv_pack);
  *   out: [B][Hq][d] float32 attention output. */
 int hardkv_step(const hardkv_desc* desc, const void* q, const hardkv_cache* cache,
                 const int8_t* metric, const hardkv_tiers* tiers, float* out, void* ws,
@@ -285,6 +296,17 @@ int hardkv_step(const hardkv_desc* desc, const void* q, const hardkv_cache* cach
  *   mode:  [B][Hkv] uint8 output, HARDKV_MODE_* from *policy with A = A_b. */
 int hardkv_plan(const hardkv_desc* desc, const hardkv_policy* policy, const int32_t* ctx_len,
                 const int32_t* count, uint8_t* mode, hardkv_stream_t stream);
+
+/* Head-wise allocation of the packed rewritten tier (desc->packed_rows > 0;
+ * section 2.C, "Metadata" and Flatten Index to the sum).  With need = count
+ * for a HARDKV_MODE_REWRITE head and 0 for a sparse-loaded one, head i in
+ * (b, h) order gets tiers->offset[i] = the sum of the needs before it; a
+ * rewritten head whose rows would end past packed_rows is switched to
+ * HARDKV_MODE_SPARSE (its attention is unchanged, its rows stay in the cache).
+ * Reads count and tiers->mode, writes tiers->offset and tiers->mode.  Run it
+ * after hardkv_plan and before hardkv_compact; the steps run it themselves. */
+int hardkv_pack(const hardkv_desc* desc, const int32_t* count, const hardkv_tiers* tiers,
+                hardkv_stream_t stream);
 
 /* hardkv_step with a per-head choice between rewriting the selection and
  * loading it in place: the policy is evaluated right after the top-p
@@ -307,7 +329,7 @@ int hardkv_step_policy(const hardkv_desc* desc, const hardkv_policy* policy, con
  *   4. every dropped resident is added to the running sums of chunk pos / C;
  *   5. attention over the ring, the pool and the chunks -> out [B][Hq][d] f32;
  *   6. seq_len[b] += 1.
- * desc->block_size, desc->sinks and desc->merge must be 0; ctx_cap bounds P + 1 and sizes the pool
+ * desc->block_size, desc->sinks, desc->merge and desc->packed_rows must be 0; ctx_cap bounds P + 1 and sizes the pool
  * (sparse_cap >= ctx_cap - W) and the chunks (chunk_cap >= ceil((ctx_cap - W) / C)). */
 int hardkv_step_inplace(const hardkv_desc* desc, const void* q, const void* k_new,
                         const void* v_new, const int8_t* metric, const hardkv_state* state,

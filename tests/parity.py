@@ -158,8 +158,8 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
     if skip_slots:
         report["sparse_heads"] += 1
     else:
-        kt = tiers.k[b, h, :k_gpu]
-        vt = tiers.v[b, h, :k_gpu]
+        kt = tiers.slots(b, h, "k")
+        vt = tiers.slots(b, h, "v")
         idx = torch.as_tensor(pos_gpu, device=kt.device).long()
         src_k = S.head_rows(case, b, h, "k")[idx]
         src_v = S.head_rows(case, b, h, "v")[idx]

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = H.load()
-    assert lib.hardkv_version() == 10200
+    assert lib.hardkv_version() == 10300
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.hardkv_strerror(code)
     assert lib.hardkv_strerror(99) == b"unknown error"
@@ -41,7 +41,7 @@ def base_desc(**kw):
     return H.make_desc(d["B"], d["Hq"], d["Hkv"], d["d"], d["dtype"], d["W"], d["C"], d["top_p"],
                        d["ctx_cap"], d.get("block_size", 0), d.get("max_blocks", 0),
                        d.get("sparse_cap"), d.get("chunk_cap"), d.get("sinks", 0),
-                       d.get("merge", 0))
+                       d.get("merge", 0), d.get("packed_rows", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -73,6 +73,9 @@ def base_desc(**kw):
     (dict(sinks=2000), H.OK),                      # sinks and window cover everything
     (dict(merge=1), H.OK),
     (dict(merge=2), H.ERR_INVALID_ARG),
+    (dict(packed_rows=100), H.OK),
+    (dict(packed_rows=-1), H.ERR_INVALID_ARG),
+    (dict(B=1 << 18, Hkv=16, Hq=16, packed_rows=1), H.ERR_INVALID_ARG),  # offsets past int32
 ])
 def test_validate_codes(kw, code):
     assert H.validate(base_desc(**kw)) == code
@@ -93,7 +96,7 @@ def _call_all(desc, ws_bytes, null_q=False):
     lib = H.load()
     fake = ctypes.c_void_p(0x1000)
     cache = H.Cache(fake, fake, None, fake)
-    tiers = H.TiersC(*([fake] * 8))
+    tiers = H.TiersC(*([fake] * 9))
     state = H.StateC(fake, fake, H.TiersC(*([fake] * 7)), fake)
     pol = H.policy(H.POLICY_MTI, 4)
     q = None if null_q else fake
@@ -212,3 +215,33 @@ def test_sinks_and_merge_errors_before_launch():
     # sinks add dense tiles: at equal capacities the workspace grows with them
     assert H.workspace_size(base_desc(sinks=300, sparse_cap=936, chunk_cap=30)) > \
         H.workspace_size(base_desc())
+
+
+def test_packed_tier_errors_before_launch():
+    lib = H.load()
+    fake = ctypes.c_void_p(0x1000)
+    cache = H.Cache(fake, fake, None, fake)
+    st = ctypes.c_void_p(0)
+    packed = base_desc(packed_rows=500)
+    need = H.workspace_size(packed)
+    d = ctypes.byref(packed)
+    full = H.TiersC(*([fake] * 9))
+    no_offset = H.TiersC(*([fake] * 8))
+    no_mode = H.TiersC(*([fake] * 7), None, fake)
+    for t in (no_offset, no_mode):
+        tb = ctypes.byref(t)
+        assert lib.hardkv_step(d, fake, ctypes.byref(cache), None, tb, fake, fake, need, st) == \
+            H.ERR_INVALID_ARG
+        assert lib.hardkv_compact(d, ctypes.byref(cache), fake, tb, fake, need, st) == \
+            H.ERR_INVALID_ARG
+        assert lib.hardkv_decode_attn(d, fake, ctypes.byref(cache), tb, fake, fake, need, st) == \
+            H.ERR_INVALID_ARG
+        assert lib.hardkv_pack(d, fake, tb, st) == H.ERR_INVALID_ARG
+    assert lib.hardkv_pack(d, None, ctypes.byref(full), st) == H.ERR_INVALID_ARG
+    # hardkv_pack needs a packed descriptor
+    assert lib.hardkv_pack(ctypes.byref(base_desc()), fake, ctypes.byref(full), st) == \
+        H.ERR_INVALID_ARG
+    # the lifecycle keeps per-head pools
+    state = H.StateC(fake, fake, H.TiersC(*([fake] * 7)), fake)
+    assert lib.hardkv_step_inplace(d, fake, fake, fake, None, ctypes.byref(state), fake, fake,
+                                   need, st) == H.ERR_INVALID_ARG
