@@ -219,6 +219,16 @@ def amortization(w, case, steps, horizons=(1, 2, 4, 8, 16, 32)):
             return None
         return int(math.floor((sel - dense) / (dense - reuse))) + 2 if sel > dense else 1
 
+    # the packed rewritten tier (one region sized to the kept rows, Flatten
+    # Index to the sum) against the per-head regions of the maximum length
+    kept_rows = int(t_rw.count.sum().item())
+    d_pack = H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.W, w.C, w.p, case.ctx_cap,
+                         w.block_size, case.max_blocks, packed_rows=max(kept_rows, 1))
+    t_pack = H.alloc_tiers(d_pack, dev)
+    sel_pack = time_ms(lambda: H.step(d_pack, case.q, cache, case.metric, t_pack, out, ws), steps)
+    reuse_pack = time_ms(lambda: H.decode_attn(d_pack, case.q, cache, t_pack, out, ws), steps)
+    row_bytes = w.d * (4 if w.dtype == 0 else 2)
+    del t_pack
     mti = {}
     t_mti = H.alloc_tiers(desc, dev, mode=True)
     for n in horizons:
@@ -238,6 +248,9 @@ def amortization(w, case, steps, horizons=(1, 2, 4, 8, 16, 32)):
                                        "sparse": breakeven(sel_sp, reuse_sp)},
         "mti_sparse_heads_by_horizon": mti,
         "heads": int(w.B * w.Hkv),
+        "packed_tier": {"select_ms": round(sel_pack, 4), "reuse_ms": round(reuse_pack, 4),
+                        "kv_bytes": 2 * kept_rows * row_bytes,
+                        "per_head_regions_kv_bytes": 2 * w.B * w.Hkv * desc.sparse_cap * row_bytes},
     }
 
 

@@ -190,27 +190,35 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
 
 // Fast path for chunks that are whole multiples of 64 rows.  One tile
 // (<= 1024 rows, whole chunks) per workgroup: the ranks of all its rows are
-// computed once (block scan of the mask), then 64-row sub-tiles stream
-// through registers with the next sub-tile's loads issued before the current
-// one is stored (ping-pong buffers).  Thread (rg, c) owns 16-byte piece c of
-// rows rg, rg + RG, ...; kept pieces go straight to their slot, evicted ones
-// are added to per-thread float32 partial sums.  At the end of each chunk
-// the partials are reduced across row groups (lane shuffles, then the four
-// waves in a fixed order through LDS): deterministic.
+// computed once (block scan of the mask), then every wave streams whole
+// 64-row units of the tile (wave w takes units w, w + 4, ...) through
+// registers in steps of 4 KB per tensor, the next step's loads issued before
+// the current one is processed (ping-pong buffers), with no workgroup
+// barrier until the tile ends.  Lane (g, c) of a wave owns 16-byte piece c
+// of rows g, g + RGW, ... of a step; kept pieces go straight to their slot,
+// evicted ones are added to per-lane float32 partial sums.  At the end of a
+// unit the wave reduces its partials across its row groups (lane shuffles)
+// into LDS; at the end of the tile the units of each chunk are added in unit
+// order and stored: deterministic, and one barrier per tile instead of two
+// per 64 rows.
 template <typename T, int D, int G, bool P, bool ATTN, bool WMERGE>
 __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   constexpr int RB = D * (int)sizeof(T);
-  constexpr int CPR = RB / 16;        // pieces per row
+  constexpr int CPR = RB / 16;         // pieces per row
   constexpr int EPC = Elt<T>::kPer16;  // elements per piece
-  constexpr int RG = 256 / CPR;       // row groups per sub-tile
-  constexpr int RPT = 64 / RG;        // rows per thread per sub-tile
-  constexpr int NB = 2 * RPT;         // pieces per thread per sub-tile (K and V)
+  constexpr int RGW = 64 / CPR;        // row groups per wave
+  constexpr int RPT = 4;               // rows per lane per step
+  constexpr int SR = RPT * RGW;        // rows per step (4 KB of each tensor)
+  constexpr int SPU = 64 / SR;         // steps per 64-row unit
+  constexpr int NB = 2 * RPT;          // pieces per lane per step (K and V)
+  constexpr int MAXU = 16;             // units per tile (TT <= 1024)
   constexpr int GA = ATTN ? G : 1;
   __shared__ int s_rank[1024];
-  __shared__ float s_red[4][2][D];
-  __shared__ float s_wred[4];
+  __shared__ float s_unit[MAXU][2][D];  // per-unit sums of the evicted rows
+  __shared__ float s_unitw[WMERGE ? MAXU : 1];
+  __shared__ int s_evc[MAXU];           // evicted rows per chunk of the tile
   __shared__ int s_scan[4];
-  __shared__ int s_ev[2];  // evicted rows of the current chunk (alternating per chunk)
+  __shared__ unsigned s_kept_sub;       // bit u: unit u holds a kept row
   __shared__ float s_am[4][GA], s_al[4][GA];
   __shared__ float s_ao[ATTN ? 4 * G * D : 1];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -228,6 +236,8 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   char* ok = a.out_k + slot0 * RB;
   char* ov = a.out_v + slot0 * RB;
   int32_t* pos = a.out_pos + bh * a.cap_stride;
+  if (tid < MAXU) s_evc[tid] = 0;
+  if (tid == 0) s_kept_sub = 0u;
 
   // kept tokens before the tile
   int base;
@@ -239,15 +249,16 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
     block_excl_scan_256(c, s_scan, total);
     base = total;
   }
-  // ranks of the tile's rows (rows 4 tid .. 4 tid + 3); -1 = evicted
+  // ranks of the tile's rows (rows 4 tid .. 4 tid + 3, one unit); -1 = evicted
   {
-    int c4 = 0, flags = 0;
+    int c4 = 0, ev4 = 0, flags = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 4 * tid + q;
       const bool sel = r < nrows && mk[t0 + r] != 0;
       flags |= (int)sel << q;
       c4 += sel;
+      ev4 += r < nrows && !sel;
     }
     int total;
     int rk = base + block_excl_scan_256(c4, s_scan, total);
@@ -264,19 +275,21 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
         }
       }
     }
-    if (tid == 0) s_ev[0] = s_ev[1] = 0;
+    if (c4) atomicOr(&s_kept_sub, 1u << (tid >> 4));  // unit of rows 4 tid..
+    if (ev4) atomicAdd(&s_evc[(4 * tid) / a.C], ev4);
     if (t0 + nrows == n && tid == 255) a.out_count[bh] = rk;
   }
   __syncthreads();
 
-  const int c = tid % CPR, rg = tid / CPR;
   const int w = tid >> 6, lane = tid & 63;
-  const int nsub = (nrows + 63) / 64;
+  const int c = lane % CPR, rg = lane / CPR;
+  const int nunits = (nrows + 63) / 64;
+  const int my_units = nunits > w ? (nunits - w + 3) / 4 : 0;
+  const int nsteps = my_units * SPU;
   MergeW mw{};
   if constexpr (WMERGE) mw = merge_w(a, h, bh);
   float acc[2][EPC];
-  float wacc = 0.f;  // weighted merging: sum of this thread's evicted rows' weights
-  int nflush = 0;
+  float wacc = 0.f;  // weighted merging: sum of this lane's evicted rows' weights
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -297,22 +310,28 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
     }
   }
 
-  auto load = [&](v4u (&buf)[NB], int s) {
+  // step k of this wave: unit w + 4 (k / SPU), rows (k % SPU) * SR + rg + RGW i
+  auto first_row = [&](int k) { return (w + 4 * (k / SPU)) * 64 + (k % SPU) * SR + rg; };
+  auto load = [&](v4u (&buf)[NB], int k) {
+    const int r0 = first_row(k);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = min(s * 64 + rg + RG * i, nrows - 1);
+      const int r = min(r0 + RGW * i, nrows - 1);
       buf[i] = *(const v4u*)(a.krows.template row<P>(b, h, t0 + r) + c * 16);
       buf[RPT + i] = *(const v4u*)(a.vrows.template row<P>(b, h, t0 + r) + c * 16);
     }
   };
-  auto process = [&](const v4u (&buf)[NB], int s) {
-    if constexpr (ATTN) {
+  auto process = [&](const v4u (&buf)[NB], int k) {
+    const int u = w + 4 * (k / SPU);
+    const int r0 = first_row(k);
+    // attention only where the unit holds a kept row (uniform branch)
+    if constexpr (ATTN) if ((s_kept_sub >> u) & 1u) {
       float sc[RPT][G], mr[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) mr[g] = -INFINITY;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const int r = s * 64 + rg + RG * i;
+        const int r = r0 + RGW * i;
         const bool kept = r < nrows && s_rank[min(r, nrows - 1)] >= 0;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -345,7 +364,7 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = s * 64 + rg + RG * i;
+      const int r = r0 + RGW * i;
       if (r < nrows) {
         const int rk = s_rank[r];
         if (rk >= 0) {
@@ -374,11 +393,8 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
         }
       }
     }
-    // end of a chunk: reduce and store its sums and count
-    const int rows_done = min((s + 1) * 64, nrows);
-    if (rows_done % a.C == 0 || rows_done == nrows) {
-      const int ch = (t0 + s * 64) / a.C;
-      const int cs = ch * a.C - t0;  // chunk's first row in the tile (>= 0)
+    // end of the unit: its sums across this wave's row groups go to LDS
+    if (k % SPU == SPU - 1) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -386,58 +402,27 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
           float v = acc[q][e];
 #pragma unroll
           for (int o = CPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-          acc[q][e] = v;
+          acc[q][e] = 0.f;
+          if (lane < CPR) s_unit[u][q][c * EPC + e] = v;
         }
-      if (lane < CPR) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) s_red[w][q][c * EPC + e] = acc[q][e];
-      }
       if (WMERGE) {
         float v = wacc;
 #pragma unroll
         for (int o = CPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-        if (lane == 0) s_wred[w] = v;
+        if (lane == 0) s_unitw[u] = v;
+        wacc = 0.f;
       }
-      // evicted rows of the chunk
-      const int par = nflush & 1;
-      int ev = 0;
-      for (int r = cs + tid; r < rows_done; r += 256) ev += s_rank[r] < 0;
-      if (ev) atomicAdd(&s_ev[par], ev);
-      __syncthreads();
-      const int nev = s_ev[par];
-      if (tid < 2 * D) {
-        const int q = tid / D, dim = tid % D;
-        float v = ((s_red[0][q][dim] + s_red[1][q][dim]) + s_red[2][q][dim]) + s_red[3][q][dim];
-        if (WMERGE) {
-          const float wt = ((s_wred[0] + s_wred[1]) + s_wred[2]) + s_wred[3];
-          v = nev > 0 ? v * ((float)nev / wt) : 0.f;
-        }
-        (q ? a.vsum : a.ksum)[(bh * a.chunk_stride + ch) * D + dim] = v;
-      }
-      if (tid == 0) {
-        a.ccount[bh * a.chunk_stride + ch] = nev;
-        s_ev[par ^ 1] = 0;  // the next chunk's counter; its last reader passed a barrier
-      }
-      ++nflush;
-      wacc = 0.f;
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[q][e] = 0.f;
-      __syncthreads();
     }
   };
 
   v4u A_[NB], B_[NB];
-  load(A_, 0);
-  for (int s = 0; s < nsub; s += 2) {
-    if (s + 1 < nsub) load(B_, s + 1);
-    process(A_, s);
-    if (s + 1 < nsub) {
-      if (s + 2 < nsub) load(A_, s + 2);
-      process(B_, s + 1);
+  if (nsteps > 0) load(A_, 0);
+  for (int k = 0; k < nsteps; k += 2) {
+    if (k + 1 < nsteps) load(B_, k + 1);
+    process(A_, k);
+    if (k + 1 < nsteps) {
+      if (k + 2 < nsteps) load(A_, k + 2);
+      process(B_, k + 1);
     }
   }
   if constexpr (ATTN) {
@@ -445,12 +430,12 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
     // (max, sum, numerator) per query head for this tile
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float mw = across_groups_max<CPR>(am[g]);
-      const float f = am[g] == -INFINITY ? 0.f : __expf(am[g] - mw);
+      const float mw_ = across_groups_max<CPR>(am[g]);
+      const float f = am[g] == -INFINITY ? 0.f : __expf(am[g] - mw_);
       al[g] = across_groups_sum<CPR>(al[g] * f);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) ao[g][e] = across_groups_sum<CPR>(ao[g][e] * f);
-      am[g] = mw;
+      am[g] = mw_;
     }
     if (lane < CPR) {
 #pragma unroll
@@ -465,7 +450,30 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
         s_al[w][g] = al[g];
       }
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  // chunks of the tile: units added in unit order
+  {
+    const int ch0 = t0 / a.C;
+    const int upc = a.C / 64;
+    const int nch = (nrows + a.C - 1) / a.C;
+    for (int idx = tid; idx < nch * 2 * D; idx += 256) {
+      const int cl = idx / (2 * D), q = (idx / D) & 1, dim = idx % D;
+      const int u1 = min((cl + 1) * upc, nunits);
+      float v = 0.f, wt = 0.f;
+      for (int u = cl * upc; u < u1; ++u) {
+        v += s_unit[u][q][dim];
+        if (WMERGE) wt += s_unitw[u];
+      }
+      if (WMERGE) {
+        const int ne = s_evc[cl];
+        v = ne > 0 ? v * ((float)ne / wt) : 0.f;
+      }
+      (q ? a.vsum : a.ksum)[(bh * a.chunk_stride + ch0 + cl) * D + dim] = v;
+    }
+    if (tid < nch) a.ccount[bh * a.chunk_stride + ch0 + tid] = s_evc[tid];
+  }
+  if constexpr (ATTN) {
     float* part_out = a.part + (bh * a.max_tiles + j) * G * (D + 2);
     for (int i = tid; i < G * D; i += 256) {
       const int g = i / D, e = i % D;
