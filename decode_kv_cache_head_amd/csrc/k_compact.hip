@@ -24,6 +24,8 @@
 // only moves to a slot at or below its own, so the left compaction never
 // overwrites a row that has not been read.  Evicted rows are added to the
 // running sums of chunk pos / C.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace hk {
@@ -200,7 +202,10 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
 // unit the wave reduces its partials across its row groups (lane shuffles)
 // into LDS; at the end of the tile the units of each chunk are added in unit
 // order and stored: deterministic, and one barrier per tile instead of two
-// per 64 rows.
+// per 64 rows.  In the fused step, tiles that keep under 1/8 of their rows
+// run a copy of the streaming loop that skips the attention arithmetic of
+// units without a kept row; denser tiles run the copy without that branch
+// (it costs them more than it saves).
 template <typename T, int D, int G, bool P, bool ATTN, bool WMERGE>
 __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   constexpr int RB = D * (int)sizeof(T);
@@ -219,6 +224,7 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   __shared__ int s_evc[MAXU];           // evicted rows per chunk of the tile
   __shared__ int s_scan[4];
   __shared__ unsigned s_kept_sub;       // bit u: unit u holds a kept row
+  __shared__ int s_kept_tile;           // kept rows in the tile
   __shared__ float s_am[4][GA], s_al[4][GA];
   __shared__ float s_ao[ATTN ? 4 * G * D : 1];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -262,6 +268,7 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
     }
     int total;
     int rk = base + block_excl_scan_256(c4, s_scan, total);
+    if (tid == 0) s_kept_tile = total;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 4 * tid + q;
@@ -321,11 +328,11 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
       buf[RPT + i] = *(const v4u*)(a.vrows.template row<P>(b, h, t0 + r) + c * 16);
     }
   };
-  auto process = [&](const v4u (&buf)[NB], int k) {
+  auto process = [&](const v4u (&buf)[NB], int k, auto skip) {
     const int u = w + 4 * (k / SPU);
     const int r0 = first_row(k);
-    // attention only where the unit holds a kept row (uniform branch)
-    if constexpr (ATTN) if ((s_kept_sub >> u) & 1u) {
+    // attention over the unit's rows; sparse tiles skip units with no kept row
+    if constexpr (ATTN) if (!decltype(skip)::value || ((s_kept_sub >> u) & 1u)) {
       float sc[RPT][G], mr[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) mr[g] = -INFINITY;
@@ -415,16 +422,22 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
     }
   };
 
-  v4u A_[NB], B_[NB];
-  if (nsteps > 0) load(A_, 0);
-  for (int k = 0; k < nsteps; k += 2) {
-    if (k + 1 < nsteps) load(B_, k + 1);
-    process(A_, k);
-    if (k + 1 < nsteps) {
-      if (k + 2 < nsteps) load(A_, k + 2);
-      process(B_, k + 1);
+  auto stream = [&](auto skip) {
+    v4u A_[NB], B_[NB];
+    if (nsteps > 0) load(A_, 0);
+    for (int k = 0; k < nsteps; k += 2) {
+      if (k + 1 < nsteps) load(B_, k + 1);
+      process(A_, k, skip);
+      if (k + 1 < nsteps) {
+        if (k + 2 < nsteps) load(A_, k + 2);
+        process(B_, k + 1, skip);
+      }
     }
-  }
+  };
+  if (!ATTN || 8 * s_kept_tile >= nrows)
+    stream(std::false_type{});
+  else
+    stream(std::true_type{});
   if constexpr (ATTN) {
     // join the row groups of each wave, then the four waves; one partial
     // (max, sum, numerator) per query head for this tile
