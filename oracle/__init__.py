@@ -5,7 +5,7 @@ Test infrastructure only: imported by the test-suite, by the package
 product path.  It shares no code with the HIP library.
 """
 from .hardkv_oracle import (  # noqa: F401
-    METRIC_QK, METRIC_L2, aged_count, score_head, calibrate_head, topp_head,
+    METRIC_QK, METRIC_L2, METRIC_WINDOW, window_score_head, aged_count, score_head, calibrate_head, topp_head,
     condense, attend_head, full_attention, step_head, step, HeadState,
     init_state, lifecycle_step, POLICY_REWRITE, POLICY_SPARSE, POLICY_MTI,
     MODE_REWRITE, MODE_SPARSE, mti_head, plan_head, reuse_head, MERGE_MEAN,

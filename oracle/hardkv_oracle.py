@@ -44,6 +44,12 @@ read section 2.A, Tier 1 and Tier 3 (tests/test_oracle_merge.py: a
 hand-worked weighted chunk, scale invariance and the weight floor, the tier
 partition and chunk alignment with sinks, and reductions to full softmax
 attention).
+
+The observation-window metric (``window_score_head``; section 2.B) is pinned
+in tests/test_oracle_window.py by a Hadamard closed form over several window
+queries, scipy's maximum filter for the pooling, the one-query reduction to
+the raw logits and the uniform closed form of a pooling radius that covers
+the candidates.
 """
 from __future__ import annotations
 
@@ -52,8 +58,9 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-METRIC_QK = 0   # max-over-GQA-group q.k logit
-METRIC_L2 = 1   # key L2 norm
+METRIC_QK = 0      # max-over-GQA-group q.k logit
+METRIC_L2 = 1      # key L2 norm
+METRIC_WINDOW = 2  # observation-window, position-pooled max logit
 
 
 def _f64(x) -> np.ndarray:
@@ -116,6 +123,34 @@ def score_head(q_group, K):
     return ell.astype(np.float32), s.astype(np.float32)
 
 
+def window_score_head(q_window, K, radius: int):
+    """Observation-window metric with positional pooling (section 2.B: the
+    calibration maps metrics of selection strategies such as SnapKV onto one
+    probability space; "Goal": max-pooled logits).
+
+    Reading: SnapKV scores a token by the attention the last few queries (an
+    observation window) pay it, pooled over neighbouring positions so that
+    the neighbours of an important token are kept with it.  In logit form:
+      x_t  = max over the window's queries and the GQA group of q . k_t / sqrt(d)
+             (float64 dots, rounded once to float32),
+      x'_t = max of x_u over positions u in [t - r, t + r] inside the candidates.
+    q_window: [w, G, d], row 0 the current query.  Returns x' float32 [n].
+    """
+    q = _f64(q_window)
+    k = _f64(K)
+    _check_finite(q, k)
+    w, G, d = q.shape
+    n = k.shape[0]
+    if n == 0:
+        return np.zeros(0, np.float32)
+    dots = k @ q.reshape(w * G, d).T                # [n, w G]
+    x = (dots.max(axis=1) * (1.0 / math.sqrt(d))).astype(np.float32)
+    pooled = np.empty(n, np.float32)
+    for t in range(n):
+        pooled[t] = x[max(0, t - radius):min(n, t + radius + 1)].max()
+    return pooled
+
+
 # ---------------------------------------------------------------------------
 # Logits Calibration (section 2.B "Mechanism"; section 3, second
 # contribution).
@@ -138,9 +173,11 @@ def calibrate_head(ell, s, metric: int) -> Calibration:
     order, and maps onto the raw attention distribution.  Reading:
       * QK heads: temperature 1, c = ell.  The calibrated distribution is the
         raw attention distribution over the candidates.
-      * key-norm heads: a temperature chosen so the metric's spread equals
-        the head's raw-logit spread:  c = (s - mu_s) * sigma_ell / sigma_s,
-        population moments over the candidates.  A zero spread gives c = 0.
+      * key-norm and observation-window heads (s = the metric): a temperature
+        chosen so the metric's spread equals the head's raw-logit spread:
+        c = (s - mu_s) * sigma_ell / sigma_s, population moments over the
+        candidates (the shift does not change the softmax).  A zero spread
+        gives c = 0.
     The softmax domain is the candidate set only (dense-tier tokens are kept
     by rule).  Weights w = exp(c - max c), Z = sum w, float64.
     """
@@ -150,7 +187,7 @@ def calibrate_head(ell, s, metric: int) -> Calibration:
     if metric == METRIC_QK:
         shift, scale = 0.0, 1.0
         c = ell.copy()
-    elif metric == METRIC_L2:
+    elif metric in (METRIC_L2, METRIC_WINDOW):
         if n == 0:
             shift, scale = 0.0, 0.0
             c = np.zeros(0, np.float32)
@@ -366,13 +403,15 @@ def dense_positions(T: int, S: int, A: int) -> np.ndarray:
 
 
 def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
-              sinks: int = 0, merge: int = MERGE_MEAN) -> HeadResult:
+              sinks: int = 0, merge: int = MERGE_MEAN, q_hist=None,
+              radius: int = 0) -> HeadResult:
     """Single-step compression + attention of one KV head.
 
     K, V: [>=T, d] rows of this head's cache in position order (exact
     input values, any float dtype).  Candidates are [S, S + A) with
     (S, A) = candidate_range(T, W, sinks); the dense tier is every other
-    position below T.
+    position below T.  metric METRIC_WINDOW scores with ``window_score_head``
+    over this query and q_hist (the previous queries, most recent first).
     Rewrite: the selected rows are copied, in ascending position order, into
     contiguous slots 0..k-1 (Rewrite Cache + Flatten Index to the maximum
     length, section 2.C).  Evicted candidates go to the condensed tier, mean-
@@ -381,6 +420,12 @@ def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
     S, A = candidate_range(T, W, sinks)
     cand_K = K[S:S + A]
     ell, s = score_head(q_group, cand_K)
+    if metric == METRIC_WINDOW:
+        # the window: this step's query, then the previous ones (q_hist [w-1, G, d])
+        qw = [np.asarray(q_group)[None]]
+        if q_hist is not None and len(q_hist):
+            qw.append(np.asarray(q_hist))
+        s = window_score_head(np.concatenate(qw, axis=0), cand_K, radius)
     cal = calibrate_head(ell, s, metric)
     sel = topp_head(cal.c, cal.w, cal.Z, p)
     mask = np.zeros(A, np.uint8)
