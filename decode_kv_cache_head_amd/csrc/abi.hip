@@ -18,7 +18,7 @@ void hk::observe(const char* kernel, hipStream_t st) {
 
 namespace {
 
-constexpr int kVersion = 10300;  // 1.3.0
+constexpr int kVersion = 10400;  // 1.4.0
 
 int log2i(int v) {
   int l = 0;
@@ -52,6 +52,8 @@ int validate(const hardkv_desc* d) {
     return HARDKV_ERR_INVALID_ARG;
   if ((int64_t)d->dense_window + d->sinks > INT32_MAX / 2) return HARDKV_ERR_INVALID_ARG;
   if (d->packed_rows < 0) return HARDKV_ERR_INVALID_ARG;
+  if (d->obs_window < 0 || d->obs_window > 64 || d->pool_radius < 0 || d->pool_radius > 512)
+    return HARDKV_ERR_INVALID_ARG;
   if (d->packed_rows > 0 &&
       (int64_t)d->batch * d->num_kv_heads * (int64_t)d->sparse_cap >= ((int64_t)1 << 31))
     return HARDKV_ERR_INVALID_ARG;
@@ -67,9 +69,12 @@ int validate(const hardkv_desc* d) {
 }
 
 struct Layout {
-  size_t q64, logit, l2, stats, mask, count, part, total;
+  size_t q64, logit, l2, wx, stats, mask, count, part, total;
   int max_tiles;
 };
+
+// queries in the observation window (0 and 1 both mean this step's only)
+int window_of(const hardkv_desc* d) { return d->obs_window > 1 ? d->obs_window : 1; }
 
 Layout layout(const hardkv_desc* d) {
   Layout L{};
@@ -81,9 +86,10 @@ Layout layout(const hardkv_desc* d) {
   };
   const size_t B = d->batch, Hq = d->num_q_heads, Hkv = d->num_kv_heads, D = d->head_dim;
   const size_t G = Hq / Hkv, cap = d->sparse_cap;
-  L.q64 = take(B * Hq * D * 8);
+  L.q64 = take(B * (size_t)window_of(d) * Hq * D * 8);
   L.logit = take(B * Hkv * cap * 4);
   L.l2 = take(B * Hkv * cap * 4);
+  L.wx = take(d->pool_radius > 0 ? B * Hkv * cap * 4 : 0);
   L.stats = take(B * Hkv * 4 * 8);
   L.mask = take(B * Hkv * cap);
   L.count = take(B * Hkv * 4);
@@ -133,9 +139,9 @@ int launched() {
 }
 
 // ---------------------------------------------------------- launch steps --
-void do_score(const hardkv_desc* d, const Layout& L, char* ws, const void* q, const Rows& rows,
-              const Cand& cand, int max_cand, const int8_t* metric, float* logit, float* l2,
-              hipStream_t st) {
+void do_score(const hardkv_desc* d, const Layout& L, char* ws, const void* q, const void* q_hist,
+              const Rows& rows, const Cand& cand, int max_cand, const int8_t* metric,
+              float* logit, float* l2, hipStream_t st) {
   ScoreArgs a{};
   a.dtype = d->dtype;
   a.D = d->head_dim;
@@ -143,6 +149,10 @@ void do_score(const hardkv_desc* d, const Layout& L, char* ws, const void* q, co
   a.B = d->batch;
   a.hq = d->num_q_heads;
   a.q = q;
+  a.q_hist = q_hist;
+  a.window = window_of(d);
+  a.radius = d->pool_radius;
+  a.wx = (float*)(ws + L.wx);
   a.q64 = (double*)(ws + L.q64);
   a.rows = rows;
   a.cand = cand;
@@ -254,6 +264,10 @@ bool tiers_ok(const hardkv_desc* d, const hardkv_tiers* t) {
 bool cache_ok(const hardkv_desc* d, const hardkv_cache* c) {
   return c && c->k && c->v && c->ctx_len && (d->block_size == 0 || c->block_table);
 }
+// ... and, when the window metric looks back, the earlier queries
+bool scored_cache_ok(const hardkv_desc* d, const hardkv_cache* c) {
+  return cache_ok(d, c) && (window_of(d) == 1 || c->q_hist);
+}
 
 bool policy_ok(const hardkv_policy* p) {
   return p && (p->kind == HARDKV_POLICY_REWRITE || p->kind == HARDKV_POLICY_SPARSE ||
@@ -286,7 +300,7 @@ void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
   uint8_t* mask = (uint8_t*)(w + L.mask);
   int32_t* count = (int32_t*)(w + L.count);
   hipGetLastError();
-  do_score(d, L, w, q, kr, cand, max_aged(d), metric, logit, l2, st);
+  do_score(d, L, w, q, cache->q_hist, kr, cand, max_aged(d), metric, logit, l2, st);
   SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
   sa.mode = t.mode;
   sa.policy = *policy;
@@ -356,10 +370,10 @@ int hardkv_score(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
                  hardkv_stream_t stream) {
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
-  if (!q || !cache_ok(d, cache) || !logit || (metric && !l2)) return HARDKV_ERR_INVALID_ARG;
+  if (!q || !scored_cache_ok(d, cache) || !logit || (metric && !l2)) return HARDKV_ERR_INVALID_ARG;
   const Layout L = layout(d);
   hipGetLastError();
-  do_score(d, L, (char*)ws, q, cand_rows(d, cache->k, cache->block_table),
+  do_score(d, L, (char*)ws, q, cache->q_hist, cand_rows(d, cache->k, cache->block_table),
            aged_cand(d, cache->ctx_len), max_aged(d), metric, logit, l2, (hipStream_t)stream);
   return launched();
 }
@@ -469,7 +483,8 @@ int hardkv_step(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
                 size_t ws_bytes, hardkv_stream_t stream) {
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
-  if (!q || !cache_ok(d, cache) || !tiers_ok(d, tiers) || !out) return HARDKV_ERR_INVALID_ARG;
+  if (!q || !scored_cache_ok(d, cache) || !tiers_ok(d, tiers) || !out)
+    return HARDKV_ERR_INVALID_ARG;
   const hardkv_policy rewrite_all{HARDKV_POLICY_REWRITE, 1, 0, 0};
   run_step(d, &rewrite_all, q, cache, metric, tiers, out, ws, (hipStream_t)stream);
   return launched();
@@ -481,7 +496,7 @@ int hardkv_step_policy(const hardkv_desc* d, const hardkv_policy* policy, const 
                        hardkv_stream_t stream) {
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
-  if (!policy_ok(policy) || !q || !cache_ok(d, cache) || !tiers_ok(d, tiers) || !tiers->mode ||
+  if (!policy_ok(policy) || !q || !scored_cache_ok(d, cache) || !tiers_ok(d, tiers) || !tiers->mode ||
       !out)
     return HARDKV_ERR_INVALID_ARG;
   run_step(d, policy, q, cache, metric, tiers, out, ws, (hipStream_t)stream);
@@ -494,7 +509,8 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
   if (d->block_size != 0 || d->dense_window < 1 || d->sinks != 0 ||
-      d->merge != HARDKV_MERGE_MEAN || d->packed_rows != 0)
+      d->merge != HARDKV_MERGE_MEAN || d->packed_rows != 0 || window_of(d) != 1 ||
+      d->pool_radius != 0)
     return HARDKV_ERR_INVALID_ARG;
   if (!q || !k_new || !v_new || !s || !s->ring_k || !s->ring_v || !s->seq_len ||
       !tiers_ok(&s->tiers) || s->tiers.mode || !out)
@@ -533,7 +549,7 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   double* stats = (double*)(w + L.stats);
   uint8_t* mask = (uint8_t*)(w + L.mask);
   int32_t* count = (int32_t*)(w + L.count);
-  do_score(d, L, w, q, pk, cand, d->sparse_cap, metric, logit, l2, st);
+  do_score(d, L, w, q, nullptr, pk, cand, d->sparse_cap, metric, logit, l2, st);
   const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
   launch_calibrate(sa, st);
   launch_select(sa, st);

@@ -113,6 +113,12 @@ __device__ inline float okey_inv(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// Heads whose ranking metric is the second score array (key norm or the
+// pooled window metric) rather than the raw logit.
+__device__ inline bool aux_metric(const int8_t* metric, int h) {
+  return metric != nullptr && metric[h] != HARDKV_METRIC_QK;
+}
+
 // Calibrated value c = fl32((x - shift) * scale).  For shift 0 and scale 1
 // (QK heads) this is x itself.
 __device__ inline float cval(float x, double shift, double scale) {

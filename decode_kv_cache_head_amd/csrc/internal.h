@@ -59,7 +59,11 @@ void observe(const char* kernel, hipStream_t st);
 struct ScoreArgs {
   int dtype, D, G, B, hq;
   const void* q;
-  double* q64;        // workspace [B][Hq][D]
+  const void* q_hist;  // [B][window - 1][Hq][D] previous queries (window metric)
+  int window;          // queries in the observation window (>= 1)
+  int radius;          // max-pooling radius of the window metric
+  float* wx;           // workspace [B][Hkv][cap_stride]: window metric before pooling
+  double* q64;        // workspace [B][window][Hq][D]
   Rows rows;          // candidate key rows
   Cand cand;
   int max_cand;       // upper bound of any (b, h)'s candidate count

@@ -44,7 +44,7 @@ __device__ inline MergeW merge_w(const CompactArgs& a, int h, int64_t bh) {
   MergeW r{};
   r.on = a.merge == HARDKV_MERGE_WEIGHTED;
   if (r.on) {
-    const bool l2 = a.metric != nullptr && a.metric[h] == HARDKV_METRIC_L2;
+    const bool l2 = aux_metric(a.metric, h);
     r.x = (l2 ? a.l2 : a.logit) + bh * a.cap_stride;
     const double* st = a.stats + bh * 4;
     r.shift = st[0];

@@ -1,6 +1,10 @@
 // Importance scores of aged tokens (HARD-KV, gist.science technical summary,
 // section 2.B "Goal": max-pooled logits; key-norm metric alongside).
 //
+// Observation-window heads (section 2.B: SnapKV-style strategies) also take
+// the max over the earlier queries of the window, then a max-pooling pass
+// over neighbouring positions (k_pool).
+//
 // HBM-bound stream over the aged keys.  Each workgroup takes up to four
 // consecutive 256-token tiles of one (b, h); a tile is staged into LDS with
 // coalesced 16-byte loads, and the next tile's loads are issued before the
@@ -14,17 +18,27 @@
 
 namespace hk {
 
+// q64[b][i][:] = this step's query (i = 0) or the i-th previous one (q_hist)
 template <typename T>
-__global__ __launch_bounds__(256) void k_q_to_f64(const T* __restrict__ q, double* __restrict__ q64,
+__global__ __launch_bounds__(256) void k_q_to_f64(const T* __restrict__ q,
+                                                   const T* __restrict__ q_hist, int window,
+                                                   int64_t per_q, double* __restrict__ q64,
                                                    int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) q64[i] = (double)Elt<T>::load1(q + i);
+  if (i >= n) return;
+  const int64_t b = i / (window * per_q), rest = i % (window * per_q);
+  const int64_t wi = rest / per_q, e = rest % per_q;
+  const T* src = wi == 0 ? q + b * per_q + e : q_hist + (b * (window - 1) + wi - 1) * per_q + e;
+  q64[i] = (double)Elt<T>::load1(src);
 }
 
 constexpr int kScoreTile = 256;
 constexpr int kScoreTiles = 4;  // tiles per workgroup
 
-template <typename T, int D, int G, bool L2>
+// RELOAD: read the row again from LDS (volatile) rather than keep its
+// float64 widening live across calls -- the window loop scores one row
+// against several queries.
+template <typename T, int D, int G, bool L2, bool RELOAD = false>
 __device__ inline void score_row(const unsigned char* row, const double* __restrict__ qg,
                                  double (&acc)[G], double& ss) {
   constexpr int RB = D * (int)sizeof(T);
@@ -32,7 +46,11 @@ __device__ inline void score_row(const unsigned char* row, const double* __restr
   constexpr int EPC = Elt<T>::kPer16;
 #pragma unroll
   for (int c = 0; c < CPR; ++c) {
-    const v4u raw = *(const v4u*)(row + c * 16);
+    v4u raw;
+    if constexpr (RELOAD)
+      raw = *(const volatile v4u*)(row + c * 16);
+    else
+      raw = *(const v4u*)(row + c * 16);
     float f[EPC];
     Elt<T>::unpack(raw, f);
 #pragma unroll
@@ -68,11 +86,21 @@ __device__ __forceinline__ void store_tile(const v4u (&buf)[CPR], unsigned char*
   }
 }
 
-// One lane scores token t from its LDS row.
-template <typename T, int D, int G>
+// One lane scores token t from its LDS row.  Window heads (WIN: more than
+// one query in the window) also take the max over the earlier queries,
+// whose float64 rows follow at a stride of qstride.
+struct WinOut {
+  bool on;           // this head uses the window metric
+  float* dst;        // window metric (before pooling) or the pooled array itself
+  int window;
+  int64_t qstride;   // elements between consecutive window queries in q64
+};
+
+template <typename T, int D, int G, bool WIN>
 __device__ __forceinline__ void score_lane(const unsigned char* row, const double* __restrict__ qg,
-                                           bool is_l2, int t, int n, float* __restrict__ logit,
-                                           float* __restrict__ l2, int64_t obase, double scale) {
+                                           bool is_l2, const WinOut& wo, int t, int n,
+                                           float* __restrict__ logit, float* __restrict__ l2,
+                                           int64_t obase, double scale) {
   double acc[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g] = 0.0;
@@ -84,16 +112,31 @@ __device__ __forceinline__ void score_lane(const unsigned char* row, const doubl
   double mx = acc[0];
 #pragma unroll
   for (int g = 1; g < G; ++g) mx = fmax(mx, acc[g]);
+  double mw = mx;
+  if constexpr (WIN) {
+    if (wo.on) {
+#pragma unroll 1
+      for (int i = 1; i < wo.window; ++i) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = 0.0;
+        score_row<T, D, G, false, true>(row, qg + i * wo.qstride, acc, ss);
+#pragma unroll
+        for (int g = 0; g < G; ++g) mw = fmax(mw, acc[g]);
+      }
+    }
+  }
   if (t < n) {
     logit[obase + t] = (float)(mx * scale);
     if (is_l2) l2[obase + t] = (float)sqrt(ss);
+    if (wo.on) wo.dst[obase + t] = (float)(mw * scale);
   }
 }
 
-template <typename T, int D, int G, bool P>
+template <typename T, int D, int G, bool P, bool WIN>
 __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, int hq, Rows rows,
                                                Cand cand, const int8_t* __restrict__ metric,
                                                float* __restrict__ logit, float* __restrict__ l2,
+                                               float* __restrict__ wdst, int window,
                                                int64_t cap_stride, double scale) {
   constexpr int RB = D * (int)sizeof(T);
   constexpr int CPR = RB / 16;
@@ -106,8 +149,10 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
   const int tfirst = blockIdx.x * kScoreTiles;
   const int ntiles = min(kScoreTiles, (n + kScoreTile - 1) / kScoreTile - tfirst);
   if (ntiles <= 0) return;
-  const double* __restrict__ qg = q64 + ((int64_t)b * hq + (int64_t)h * G) * D;
+  const double* __restrict__ qg = q64 + ((int64_t)b * window * hq + (int64_t)h * G) * D;
   const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
+  const WinOut wo{metric != nullptr && metric[h] == HARDKV_METRIC_WINDOW, wdst, window,
+                  (int64_t)hq * D};
   const int64_t obase = ((int64_t)b * hkv + h) * cap_stride;
 
   v4u buf[CPR];
@@ -117,27 +162,82 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
     store_tile<CPR, PAD>(buf, lds, tid);
     __syncthreads();
     load_tile<CPR, P>(buf, rows, b, h, (tfirst + tile + 1) * kScoreTile, n, tid);
-    score_lane<T, D, G>(lds + tid * PAD, qg, is_l2, (tfirst + tile) * kScoreTile + tid, n, logit,
-                        l2, obase, scale);
+    score_lane<T, D, G, WIN>(lds + tid * PAD, qg, is_l2, wo, (tfirst + tile) * kScoreTile + tid,
+                             n, logit, l2, obase, scale);
     __syncthreads();
   }
   store_tile<CPR, PAD>(buf, lds, tid);
   __syncthreads();
-  score_lane<T, D, G>(lds + tid * PAD, qg, is_l2, (tfirst + ntiles - 1) * kScoreTile + tid, n,
-                      logit, l2, obase, scale);
+  score_lane<T, D, G, WIN>(lds + tid * PAD, qg, is_l2, wo, (tfirst + ntiles - 1) * kScoreTile + tid,
+                           n, logit, l2, obase, scale);
+}
+
+// Max-pooling of the window metric over positions [t - r, t + r] inside the
+// candidates, for window heads: a 1024-token tile plus r on each side in
+// LDS, then doubling passes (M_{2p}[i] = max(M_p[i], M_p[i + p])) and one
+// query of two overlapping power-of-two windows per token.  Exact (max).
+constexpr int kPoolTile = 1024;
+constexpr int kPoolMaxR = 512;
+
+__global__ __launch_bounds__(256) void k_pool(Cand cand, const int8_t* __restrict__ metric,
+                                              const float* __restrict__ src,
+                                              float* __restrict__ dst, int64_t cap_stride,
+                                              int r) {
+  __shared__ float s_a[kPoolTile + 2 * kPoolMaxR], s_b[kPoolTile + 2 * kPoolMaxR];
+  const int b = blockIdx.z, h = blockIdx.y, hkv = gridDim.y, tid = threadIdx.x;
+  if (metric == nullptr || metric[h] != HARDKV_METRIC_WINDOW) return;
+  const int n = cand.n(b, h);
+  const int t0 = blockIdx.x * kPoolTile;
+  if (t0 >= n) return;
+  const int64_t base = ((int64_t)b * hkv + h) * cap_stride;
+  const int L = kPoolTile + 2 * r;  // s_a[i] holds position t0 - r + i
+  for (int i = tid; i < L; i += 256) {
+    const int t = t0 - r + i;
+    s_a[i] = (t >= 0 && t < n) ? src[base + t] : -INFINITY;
+  }
+  __syncthreads();
+  int K = 1;
+  float* cur = s_a;
+  float* nxt = s_b;
+  while (2 * K <= 2 * r + 1) {
+    for (int i = tid; i < L; i += 256) nxt[i] = i + K < L ? fmaxf(cur[i], cur[i + K]) : cur[i];
+    __syncthreads();
+    float* tmp = cur;
+    cur = nxt;
+    nxt = tmp;
+    K *= 2;
+  }
+  // cur[i] = max over positions [t0 - r + i, t0 - r + i + K); token j needs
+  // [j - r, j + r] = windows starting at j - r and j + r + 1 - K
+  for (int j = tid; j < kPoolTile; j += 256) {
+    const int t = t0 + j;
+    if (t < n) dst[base + t] = fmaxf(cur[j], cur[j + 2 * r + 1 - K]);
+  }
 }
 
 template <typename T, int D, int G, bool P>
 static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
-  const int64_t nq = (int64_t)a.B * a.hq * D;
+  const int64_t per_q = (int64_t)a.hq * D;
+  const int64_t nq = (int64_t)a.B * a.window * per_q;
   observe("k_q_to_f64", st);
   hipLaunchKernelGGL(k_q_to_f64<T>, dim3(ceil_div(nq, 256)), dim3(256), 0, st, (const T*)a.q,
-                     a.q64, nq);
+                     (const T*)a.q_hist, a.window, per_q, a.q64, nq);
   dim3 grid(ceil_div(a.max_cand, kScoreTile * kScoreTiles), a.rows.hkv, a.B);
   if (grid.x == 0) return;
+  // window heads: the metric goes straight to l2 unless it is pooled
+  float* wdst = a.radius > 0 ? a.wx : a.l2;
   observe("k_score", st);
-  hipLaunchKernelGGL((k_score<T, D, G, P>), grid, dim3(256), 0, st, a.q64, a.hq, a.rows, a.cand,
-                     a.metric, a.logit, a.l2, a.cap_stride, a.scale);
+  if (a.window > 1)
+    hipLaunchKernelGGL((k_score<T, D, G, P, true>), grid, dim3(256), 0, st, a.q64, a.hq, a.rows,
+                       a.cand, a.metric, a.logit, a.l2, wdst, a.window, a.cap_stride, a.scale);
+  else
+    hipLaunchKernelGGL((k_score<T, D, G, P, false>), grid, dim3(256), 0, st, a.q64, a.hq, a.rows,
+                       a.cand, a.metric, a.logit, a.l2, wdst, a.window, a.cap_stride, a.scale);
+  if (a.radius > 0 && a.metric != nullptr) {
+    observe("k_pool", st);
+    hipLaunchKernelGGL(k_pool, dim3(ceil_div(a.max_cand, kPoolTile), a.rows.hkv, a.B), dim3(256),
+                       0, st, a.cand, a.metric, (const float*)a.wx, a.l2, a.cap_stride, a.radius);
+  }
 }
 
 void launch_score(const ScoreArgs& a, hipStream_t st) {

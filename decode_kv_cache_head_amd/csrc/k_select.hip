@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void k_calibrate(Cand cand, const int8_t* __re
   const int n = cand.n(b, h);
   const int64_t bh = (int64_t)b * hkv + h;
   const float* x = logit + bh * cap_stride;
-  const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
+  const bool is_l2 = aux_metric(metric, h);  // second score array
   double shift = 0.0, scale = 1.0;
   if (is_l2) {
     const float* s = l2 + bh * cap_stride;
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
     if (tid == 0) co.put(bh, n, n);
     return;
   }
-  const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
+  const bool is_l2 = aux_metric(metric, h);  // second score array
   const float* x = (is_l2 ? l2 : logit) + bh * cap_stride;
   const double shift = stats[bh * 4 + 0], scale = stats[bh * 4 + 1], m = stats[bh * 4 + 2];
   auto cv = [&](int t) -> float { return is_l2 ? cval(x[t], shift, scale) : x[t]; };
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   const int n = cand.n(b, h);
   const int64_t bh = (int64_t)b * hkv + h;
   uint8_t* mk = mask + bh * cap_stride;
-  const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
+  const bool is_l2 = aux_metric(metric, h);  // second score array
   if (n == 0) {
     if (tid == 0) {
       double* o = stats + bh * 4;

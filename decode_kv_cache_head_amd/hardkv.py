@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libhardkv.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
-METRIC_QK, METRIC_L2 = 0, 1
+METRIC_QK, METRIC_L2, METRIC_WINDOW = 0, 1, 2
 MODE_REWRITE, MODE_SPARSE = 0, 1
 MERGE_MEAN, MERGE_WEIGHTED = 0, 1
 POLICY_REWRITE, POLICY_SPARSE, POLICY_MTI = 0, 1, 2
@@ -43,12 +43,14 @@ class Desc(ctypes.Structure):
                 ("ctx_cap", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
                 ("sparse_cap", ctypes.c_int32), ("chunk_cap", ctypes.c_int32),
                 ("top_p", ctypes.c_float), ("sinks", ctypes.c_int32), ("merge", ctypes.c_int32),
-                ("packed_rows", ctypes.c_int32)]
+                ("packed_rows", ctypes.c_int32), ("obs_window", ctypes.c_int32),
+                ("pool_radius", ctypes.c_int32)]
 
 
 class Cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("block_table", ctypes.c_void_p), ("ctx_len", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("ctx_len", ctypes.c_void_p),
+                ("q_hist", ctypes.c_void_p)]
 
 
 class TiersC(ctypes.Structure):
@@ -135,14 +137,14 @@ def _check(rc, fn):
 
 def make_desc(B, Hq, Hkv, d, dtype, W, C, top_p, ctx_cap, block_size=0, max_blocks=0,
               sparse_cap=None, chunk_cap=None, sinks=0, merge=MERGE_MEAN,
-              packed_rows=0) -> Desc:
+              packed_rows=0, obs_window=1, pool_radius=0) -> Desc:
     A = max(ctx_cap - W - sinks, 0)
     if sparse_cap is None:
         sparse_cap = A
     if chunk_cap is None:
         chunk_cap = -(-A // C) if C > 0 else 0
     return Desc(B, Hq, Hkv, d, dtype, W, C, block_size, ctx_cap, max_blocks, sparse_cap,
-                chunk_cap, float(top_p), sinks, merge, packed_rows)
+                chunk_cap, float(top_p), sinks, merge, packed_rows, obs_window, pool_radius)
 
 
 def validate(desc: Desc) -> int:
@@ -212,8 +214,8 @@ def policy(kind=POLICY_MTI, horizon=1, l_lower=0, l_upper=INT32_MAX) -> Policy:
     return Policy(kind, horizon, l_lower, l_upper)
 
 
-def cache_struct(k, v, ctx_len, block_table=None) -> Cache:
-    return Cache(_p(k), _p(v), _p(block_table), _p(ctx_len))
+def cache_struct(k, v, ctx_len, block_table=None, q_hist=None) -> Cache:
+    return Cache(_p(k), _p(v), _p(block_table), _p(ctx_len), _p(q_hist))
 
 
 def score(desc, q, cache: Cache, metric, logit, l2, ws, stream=None):

@@ -22,6 +22,7 @@ DT_F32 = 0
 DT_BF16 = 1
 METRIC_QK = 0
 METRIC_L2 = 1
+METRIC_WINDOW = 2
 
 
 @dataclass(frozen=True)
@@ -47,6 +48,8 @@ class Workload:
     seed: int = 20260627
     sinks: int = 0       # leading positions kept in the dense tier
     merge: int = 0       # 0 mean, 1 attention-weighted merging of evicted tokens
+    obs_window: int = 1  # queries in the observation window (window-metric heads)
+    pool_radius: int = 0  # max-pooling radius of the window metric
 
     @property
     def G(self):
@@ -126,6 +129,7 @@ class Case:
     ctx_cap: int
     max_blocks: int
     extra: dict = field(default_factory=dict)
+    q_hist: torch.Tensor | None = None  # [B][obs_window - 1][Hq][d] earlier queries
 
 
 def make_case(w: Workload, device="cpu") -> Case:
@@ -198,7 +202,11 @@ def make_case(w: Workload, device="cpu") -> Case:
     metric = torch.tensor(w.metrics, dtype=torch.int8, device=device)
     if table is not None:
         table = table.to(device)
-    return Case(w, q, k, v, ctx_len, table, metric, ctx_cap, max_blocks, extra)
+    q_hist = None
+    if w.obs_window > 1:
+        # earlier decode queries of the observation window, most recent first
+        q_hist = _randn((B, w.obs_window - 1, Hq, d), w, device, "q_hist").to(dt)
+    return Case(w, q, k, v, ctx_len, table, metric, ctx_cap, max_blocks, extra, q_hist)
 
 
 def head_rows(case: Case, b: int, h: int, which: str = "k", upto: int | None = None):

@@ -68,6 +68,10 @@ typedef struct ihipStream_t* hardkv_stream_t; /* same type as hipStream_t */
 /* Importance metric per KV head. */
 #define HARDKV_METRIC_QK 0 /* max over the GQA group of q.k / sqrt(d) ("max-pooled logits") */
 #define HARDKV_METRIC_L2 1 /* key L2 norm, calibrated onto the head's logit spread */
+#define HARDKV_METRIC_WINDOW 2 /* observation window: max over the last obs_window queries and
+                                  the GQA group of q.k / sqrt(d), max-pooled over positions
+                                  [t - pool_radius, t + pool_radius]; calibrated like L2
+                                  (section 2.B: SnapKV-style strategies) */
 
 /* How evicted tokens are merged into a condensed chunk (hardkv_desc.merge). */
 #define HARDKV_MERGE_MEAN 0     /* plain mean of the chunk's evicted tokens */
@@ -125,6 +129,9 @@ typedef struct hardkv_desc {
                            Index to the sum; section 2.C, head-wise allocation under static
                            shapes); needs tiers->offset and tiers->mode, and
                            B * Hkv * sparse_cap < 2^31 */
+  int32_t obs_window;   /* HARDKV_METRIC_WINDOW heads: queries in the observation window,
+                           0..64 (0 or 1 = this step's query only; > 1 needs cache->q_hist) */
+  int32_t pool_radius;  /* HARDKV_METRIC_WINDOW heads: max-pooling radius, 0..512 */
 } hardkv_desc;
 
 /* The KV cache of one layer.
@@ -137,6 +144,8 @@ typedef struct hardkv_cache {
   const void* v;
   const int32_t* block_table; /* [B][max_blocks]; NULL for a contiguous cache */
   const int32_t* ctx_len;
+  const void* q_hist;         /* [B][obs_window - 1][Hq][d] in desc->dtype: the previous
+                                 decode queries, most recent first; NULL if obs_window <= 1 */
 } hardkv_cache;
 
 /* Sparse (rewritten) and condensed tiers.
@@ -209,8 +218,10 @@ size_t hardkv_workspace_size(const hardkv_desc* desc);
  *   metric: [Hkv] int8 HARDKV_METRIC_*, NULL = all QK
  *   logit:  [B][Hkv][sparse_cap] float32, logit[t] = fl32(max_g q_g.k_t / sqrt(d)),
  *           the dot product accumulated in float64
- *   l2:     [B][Hkv][sparse_cap] float32 key norms, written for HARDKV_METRIC_L2 heads
- *           only; must be non-NULL whenever metric is non-NULL
+ *   l2:     [B][Hkv][sparse_cap] float32 second metric: key norms for HARDKV_METRIC_L2
+ *           heads, the pooled window metric for HARDKV_METRIC_WINDOW heads (float64
+ *           dots, one rounding, exact max-pooling); must be non-NULL whenever metric is
+ *           non-NULL
  * Entries at t >= A_b are unspecified. */
 int hardkv_score(const hardkv_desc* desc, const void* q, const hardkv_cache* cache,
                  const int8_t* metric, float* logit, float* l2, void* ws, size_t ws_bytes,
@@ -220,8 +231,8 @@ int hardkv_score(const hardkv_desc* desc, const void* q, const hardkv_cache* cac
  * For each (b, h) maps the aged tokens' metric x into calibrated values
  *   c_t = fl32((x_t - shift) * scale)
  * QK heads: x = logit, shift 0, scale 1 (the raw attention distribution).
- * L2 heads: x = l2, shift = mean(l2), scale = std(logit) / std(l2) (population
- * moments over the aged tokens; 0 if either spread is 0).
+ * L2 and window heads: x = l2, shift = mean(l2), scale = std(logit) / std(l2)
+ * (population moments over the aged tokens; 0 if either spread is 0).
  *   stats: [B][Hkv][4] float64 {shift, scale, m = max c, Z = sum exp(c - m)}. */
 int hardkv_calibrate(const hardkv_desc* desc, const int32_t* ctx_len, const int8_t* metric,
                      const float* logit, const float* l2, double* stats, void* ws,
@@ -329,7 +340,8 @@ int hardkv_step_policy(const hardkv_desc* desc, const hardkv_policy* policy, con
  *   4. every dropped resident is added to the running sums of chunk pos / C;
  *   5. attention over the ring, the pool and the chunks -> out [B][Hq][d] f32;
  *   6. seq_len[b] += 1.
- * desc->block_size, desc->sinks, desc->merge and desc->packed_rows must be 0; ctx_cap bounds P + 1 and sizes the pool
+ * desc->block_size, sinks, merge, packed_rows and pool_radius must be 0 and obs_window
+ * at most 1 (the pool has no position-ordered neighbours to pool or old queries to keep); ctx_cap bounds P + 1 and sizes the pool
  * (sparse_cap >= ctx_cap - W) and the chunks (chunk_cap >= ceil((ctx_cap - W) / C)). */
 int hardkv_step_inplace(const hardkv_desc* desc, const void* q, const void* k_new,
                         const void* v_new, const int8_t* metric, const hardkv_state* state,

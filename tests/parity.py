@@ -34,11 +34,12 @@ def desc_for(case: S.Case, top_p=None, sparse_cap=None, chunk_cap=None) -> H.Des
     w = case.w
     return H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.W, w.C,
                        w.p if top_p is None else top_p, case.ctx_cap, w.block_size,
-                       case.max_blocks, sparse_cap, chunk_cap, w.sinks, w.merge)
+                       case.max_blocks, sparse_cap, chunk_cap, w.sinks, w.merge,
+                       obs_window=w.obs_window, pool_radius=w.pool_radius)
 
 
 def cache_of(case: S.Case) -> H.Cache:
-    return H.cache_struct(case.k, case.v, case.ctx_len, case.block_table)
+    return H.cache_struct(case.k, case.v, case.ctx_len, case.block_table, case.q_hist)
 
 
 def run_stages(case: S.Case, desc: H.Desc):
@@ -81,7 +82,11 @@ def oracle_head(case: S.Case, b: int, h: int, p: float):
     q = case.q[b, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
     K = S.head_rows(case, b, h, "k").float().cpu().numpy()
     V = S.head_rows(case, b, h, "v").float().cpu().numpy()
-    ref = O.step_head(q, K, V, w.T[b], w.W, w.C, p, int(w.metrics[h]), w.sinks, w.merge)
+    hist = None
+    if case.q_hist is not None:
+        hist = case.q_hist[b, :, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
+    ref = O.step_head(q, K, V, w.T[b], w.W, w.C, p, int(w.metrics[h]), w.sinks, w.merge,
+                      q_hist=hist, radius=w.pool_radius)
     return q, K, V, ref
 
 
@@ -119,7 +124,7 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
     A = ref.A
     s0 = ref.sinks  # sink count: candidate index i is position s0 + i
     G, d = w.G, w.d
-    is_l2 = int(w.metrics[h]) == O.METRIC_L2
+    is_l2 = int(w.metrics[h]) != O.METRIC_QK  # the second score array holds the metric
     if stages:
         lg = gpu["logit"][b, h, :A].cpu().numpy()
         u = _ulp_diff(lg, ref.ell)

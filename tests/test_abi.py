@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = H.load()
-    assert lib.hardkv_version() == 10300
+    assert lib.hardkv_version() == 10400
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.hardkv_strerror(code)
     assert lib.hardkv_strerror(99) == b"unknown error"
@@ -41,7 +41,8 @@ def base_desc(**kw):
     return H.make_desc(d["B"], d["Hq"], d["Hkv"], d["d"], d["dtype"], d["W"], d["C"], d["top_p"],
                        d["ctx_cap"], d.get("block_size", 0), d.get("max_blocks", 0),
                        d.get("sparse_cap"), d.get("chunk_cap"), d.get("sinks", 0),
-                       d.get("merge", 0), d.get("packed_rows", 0))
+                       d.get("merge", 0), d.get("packed_rows", 0), d.get("obs_window", 1),
+                       d.get("pool_radius", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -76,6 +77,11 @@ def base_desc(**kw):
     (dict(packed_rows=100), H.OK),
     (dict(packed_rows=-1), H.ERR_INVALID_ARG),
     (dict(B=1 << 18, Hkv=16, Hq=16, packed_rows=1), H.ERR_INVALID_ARG),  # offsets past int32
+    (dict(obs_window=0), H.OK),
+    (dict(obs_window=64, pool_radius=512), H.OK),
+    (dict(obs_window=65), H.ERR_INVALID_ARG),
+    (dict(pool_radius=513), H.ERR_INVALID_ARG),
+    (dict(pool_radius=-1), H.ERR_INVALID_ARG),
 ])
 def test_validate_codes(kw, code):
     assert H.validate(base_desc(**kw)) == code
@@ -243,5 +249,28 @@ def test_packed_tier_errors_before_launch():
         H.ERR_INVALID_ARG
     # the lifecycle keeps per-head pools
     state = H.StateC(fake, fake, H.TiersC(*([fake] * 7)), fake)
+    assert lib.hardkv_step_inplace(d, fake, fake, fake, None, ctypes.byref(state), fake, fake,
+                                   need, st) == H.ERR_INVALID_ARG
+
+
+def test_window_metric_needs_the_query_history():
+    lib = H.load()
+    fake = ctypes.c_void_p(0x1000)
+    no_hist = H.Cache(fake, fake, None, fake, None)
+    with_hist = H.Cache(fake, fake, None, fake, fake)
+    tiers = H.TiersC(*([fake] * 7))
+    st = ctypes.c_void_p(0)
+    win = base_desc(obs_window=4, pool_radius=3)
+    need = H.workspace_size(win)
+    assert need > H.workspace_size(base_desc())   # float64 window queries + pre-pool metric
+    d = ctypes.byref(win)
+    assert lib.hardkv_score(d, fake, ctypes.byref(no_hist), fake, fake, fake, fake, need, st) == \
+        H.ERR_INVALID_ARG
+    assert lib.hardkv_step(d, fake, ctypes.byref(no_hist), fake, ctypes.byref(tiers), fake, fake,
+                           need, st) == H.ERR_INVALID_ARG
+    assert lib.hardkv_score(d, fake, ctypes.byref(with_hist), fake, fake, fake, fake, need - 1,
+                            st) == H.ERR_WORKSPACE
+    # the lifecycle has no window metric
+    state = H.StateC(fake, fake, tiers, fake)
     assert lib.hardkv_step_inplace(d, fake, fake, fake, None, ctypes.byref(state), fake, fake,
                                    need, st) == H.ERR_INVALID_ARG

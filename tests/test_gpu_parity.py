@@ -67,6 +67,16 @@ GRID = [
     dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=4, C=64, p=0.95, sinks=1, merge=1,
          metric=(S.METRIC_L2, S.METRIC_QK, S.METRIC_L2, S.METRIC_QK)),
     dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=192, p=0.6, merge=1, T=(2500, 1000, 400)),
+    # observation-window metric (pooled max over earlier queries)
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.9, block_size=16,
+         metric=(S.METRIC_WINDOW, S.METRIC_QK), obs_window=4, pool_radius=3),
+    dict(dtype=S.DT_F32, d=64, Hq=8, Hkv=4, C=7, p=0.8, obs_window=2,
+         metric=(S.METRIC_WINDOW, S.METRIC_L2, S.METRIC_WINDOW, S.METRIC_QK)),
+    dict(dtype=S.DT_BF16, d=128, Hq=16, Hkv=2, C=128, p=0.95, pool_radius=5,
+         metric=(S.METRIC_WINDOW, S.METRIC_WINDOW)),
+    dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=1, C=64, p=0.7, obs_window=8, pool_radius=64, merge=1,
+         sinks=3, metric=(S.METRIC_WINDOW,)),
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.9, metric=(S.METRIC_WINDOW, S.METRIC_QK)),
 ]
 
 
@@ -201,6 +211,21 @@ def test_headline_with_sinks_and_weighted_merging(gpu):
     g = run_step(case, desc)
     check_all_heads_invariants(case, desc, g)
     rep = check_case(case, g, w.p, heads=_sample_heads(w, 6, 2), stages=False)
+    say(rep)
+
+
+def test_headline_with_window_metric(gpu):
+    """The headline shape with every KV head on the observation-window
+    metric (4 queries, pooling radius 3): sampled heads against the oracle,
+    invariants on every head."""
+    w = S.workload("qwen8b_b32_16k_paged", metric=(S.METRIC_WINDOW,) * 8, obs_window=4,
+                   pool_radius=3)
+    say(w.name, "window", w.obs_window, "radius", w.pool_radius)
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_step(case, desc)
+    check_all_heads_invariants(case, desc, g)
+    rep = check_case(case, g, w.p, heads=_sample_heads(w, 4, 3), stages=False)
     say(rep)
 
 
