@@ -406,6 +406,16 @@ def main():
             wsv = H.alloc_workspace(dv, dev)
             var[tag] = round(time_ms(lambda: H.step(dv, case.q, cache, case.metric, tiers, out,
                                                     wsv), args.steps), 4)
+        # every head on the observation-window metric: 4 queries, pooling radius 3
+        dv = H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.W, w.C, w.p, case.ctx_cap,
+                         w.block_size, case.max_blocks, desc.sparse_cap, desc.chunk_cap,
+                         obs_window=4, pool_radius=3)
+        wsv = H.alloc_workspace(dv, dev)
+        q_hist = torch.randn((w.B, 3, w.Hq, w.d), device=dev).to(case.q.dtype)
+        cache_w = H.cache_struct(case.k, case.v, case.ctx_len, case.block_table, q_hist)
+        metric_w = torch.full((w.Hkv,), H.METRIC_WINDOW, dtype=torch.int8, device=dev)
+        var["window4_pool3"] = round(time_ms(lambda: H.step(dv, case.q, cache_w, metric_w, tiers,
+                                                            out, wsv), args.steps), 4)
         res["variant_step_ms"] = var
     if not args.no_amortization:
         print("[bench] selection reuse", file=sys.stderr, flush=True)
