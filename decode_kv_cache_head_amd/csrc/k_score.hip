@@ -5,13 +5,11 @@
 // the max over the earlier queries of the window, then a max-pooling pass
 // over neighbouring positions (k_pool).
 //
-// HBM-bound stream over the aged keys.  Each workgroup takes up to four
-// consecutive 256-token tiles of one (b, h); a tile is staged into LDS with
-// coalesced 16-byte loads, and the next tile's loads are issued before the
-// current one is scored, so HBM traffic overlaps the arithmetic.  Every lane
-// scores one token: the G query rows of the head's GQA group are read as
-// float64 from wave-uniform addresses (scalar loads, SGPR operands), the
-// token's key is widened exactly to float64 and the G dot products are
+// HBM-bound stream over the aged keys.  Each workgroup stages one 128-token
+// tile of one (b, h) in LDS; two lanes score each token, one per half of the
+// head dimension, with the G query rows of the head's GQA group read as
+// float64 from wave-uniform addresses (scalar loads, SGPR operands).  The
+// token's key is widened exactly to float64 and the dot products are
 // accumulated in float64, so the only rounding the ranking key sees is the
 // final fl32().
 #include "internal.h"
@@ -32,25 +30,20 @@ __global__ __launch_bounds__(256) void k_q_to_f64(const T* __restrict__ q,
   q64[i] = (double)Elt<T>::load1(src);
 }
 
-constexpr int kScoreTile = 256;
-constexpr int kScoreTiles = 4;  // tiles per workgroup
+constexpr int kScoreTile = 128;  // tokens per workgroup
 
-// RELOAD: read the row again from LDS (volatile) rather than keep its
-// float64 widening live across calls -- the window loop scores one row
-// against several queries.
-template <typename T, int D, int G, bool L2, bool RELOAD = false>
-__device__ inline void score_row(const unsigned char* row, const double* __restrict__ qg,
-                                 double (&acc)[G], double& ss) {
-  constexpr int RB = D * (int)sizeof(T);
-  constexpr int CPR = RB / 16;
+// Partial q.k over one split of the row: `row` points at the split's first
+// byte, `qg` at the split's first query element; float64 from exact inputs.
+template <typename T, int D, int G, int PCS, bool L2>
+__device__ __forceinline__ void split_dot(const unsigned char* row, const double* __restrict__ qg,
+                                          double (&acc)[G], double& ss) {
   constexpr int EPC = Elt<T>::kPer16;
 #pragma unroll
-  for (int c = 0; c < CPR; ++c) {
-    v4u raw;
-    if constexpr (RELOAD)
-      raw = *(const volatile v4u*)(row + c * 16);
-    else
-      raw = *(const v4u*)(row + c * 16);
+  for (int g = 0; g < G; ++g) acc[g] = 0.0;
+  ss = 0.0;
+#pragma unroll
+  for (int c = 0; c < PCS; ++c) {
+    const v4u raw = *(const v4u*)(row + c * 16);
     float f[EPC];
     Elt<T>::unpack(raw, f);
 #pragma unroll
@@ -63,75 +56,15 @@ __device__ inline void score_row(const unsigned char* row, const double* __restr
   }
 }
 
-// Coalesced 16-byte loads of a 256-token tile; rows past the end re-read the
-// last valid row (always in bounds, their scores are never written).
-template <int CPR, bool P>
-__device__ __forceinline__ void load_tile(v4u (&buf)[CPR], const Rows& rows, int b, int h,
-                                          int t0, int n, int tid) {
-#pragma unroll
-  for (int j = 0; j < CPR; ++j) {
-    const int idx = j * kScoreTile + tid;
-    const int r = idx / CPR, c = idx % CPR;
-    buf[j] = *(const v4u*)(rows.template row<P>(b, h, min(t0 + r, n - 1)) + c * 16);
-  }
-}
-
-template <int CPR, int PAD>
-__device__ __forceinline__ void store_tile(const v4u (&buf)[CPR], unsigned char* lds, int tid) {
-#pragma unroll
-  for (int j = 0; j < CPR; ++j) {
-    const int idx = j * kScoreTile + tid;
-    const int r = idx / CPR, c = idx % CPR;
-    *(v4u*)(lds + r * PAD + c * 16) = buf[j];
-  }
-}
-
-// One lane scores token t from its LDS row.  Window heads (WIN: more than
-// one query in the window) also take the max over the earlier queries,
-// whose float64 rows follow at a stride of qstride.
-struct WinOut {
-  bool on;           // this head uses the window metric
-  float* dst;        // window metric (before pooling) or the pooled array itself
-  int window;
-  int64_t qstride;   // elements between consecutive window queries in q64
-};
-
-template <typename T, int D, int G, bool WIN>
-__device__ __forceinline__ void score_lane(const unsigned char* row, const double* __restrict__ qg,
-                                           bool is_l2, const WinOut& wo, int t, int n,
-                                           float* __restrict__ logit, float* __restrict__ l2,
-                                           int64_t obase, double scale) {
-  double acc[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) acc[g] = 0.0;
-  double ss = 0.0;
-  if (is_l2)
-    score_row<T, D, G, true>(row, qg, acc, ss);
-  else
-    score_row<T, D, G, false>(row, qg, acc, ss);
-  double mx = acc[0];
-#pragma unroll
-  for (int g = 1; g < G; ++g) mx = fmax(mx, acc[g]);
-  double mw = mx;
-  if constexpr (WIN) {
-    if (wo.on) {
-#pragma unroll 1
-      for (int i = 1; i < wo.window; ++i) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) acc[g] = 0.0;
-        score_row<T, D, G, false, true>(row, qg + i * wo.qstride, acc, ss);
-#pragma unroll
-        for (int g = 0; g < G; ++g) mw = fmax(mw, acc[g]);
-      }
-    }
-  }
-  if (t < n) {
-    logit[obase + t] = (float)(mx * scale);
-    if (is_l2) l2[obase + t] = (float)sqrt(ss);
-    if (wo.on) wo.dst[obase + t] = (float)(mw * scale);
-  }
-}
-
+// One 128-token tile of one (b, h) per 256-thread workgroup.  The tile is
+// staged into LDS with coalesced 16-byte loads; then every token is scored
+// by two lanes in different waves, one per half of the head dimension:
+// waves 0-1 take the first half of tokens 0-63 / 64-127, waves 2-3 the
+// second half.  The half index is wave-uniform, so the float64 query
+// elements stay scalar loads (SGPR operands of v_fma_f64); the second half's
+// partial sums reach the first through LDS.  Small register and LDS
+// footprints (four workgroups per CU) let the waves of other workgroups
+// cover the loads, instead of a register prefetch inside one workgroup.
 template <typename T, int D, int G, bool P, bool WIN>
 __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, int hq, Rows rows,
                                                Cand cand, const int8_t* __restrict__ metric,
@@ -139,37 +72,82 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
                                                float* __restrict__ wdst, int window,
                                                int64_t cap_stride, double scale) {
   constexpr int RB = D * (int)sizeof(T);
-  constexpr int CPR = RB / 16;
-  constexpr int PAD = RB + 16;  // keeps per-lane row reads conflict free
+  constexpr int CPR = RB / 16;             // 16-byte pieces per row
+  constexpr int PCS = CPR / 2;             // pieces per half row
+  constexpr int PAD = RB + 16;             // conflict-free per-lane row reads
+  constexpr int LOADS = kScoreTile * CPR / 256;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kScoreTile * PAD];
-  const int b = blockIdx.z, h = blockIdx.y, hkv = gridDim.y;
+  __shared__ double s_part[G + 1][kScoreTile];  // second half's dots and squared norm
+  const int b = blockIdx.z, h = blockIdx.y, hkv = gridDim.y, tid = threadIdx.x;
   const int n = cand.n(b, h);
-  const int tid = threadIdx.x;
-  // this workgroup's tiles: kScoreTiles consecutive 256-token tiles
-  const int tfirst = blockIdx.x * kScoreTiles;
-  const int ntiles = min(kScoreTiles, (n + kScoreTile - 1) / kScoreTile - tfirst);
-  if (ntiles <= 0) return;
-  const double* __restrict__ qg = q64 + ((int64_t)b * window * hq + (int64_t)h * G) * D;
-  const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
-  const WinOut wo{metric != nullptr && metric[h] == HARDKV_METRIC_WINDOW, wdst, window,
-                  (int64_t)hq * D};
-  const int64_t obase = ((int64_t)b * hkv + h) * cap_stride;
-
-  v4u buf[CPR];
-  load_tile<CPR, P>(buf, rows, b, h, tfirst * kScoreTile, n, tid);
-  // steady state: the next tile's loads are in flight while this one is scored
-  for (int tile = 0; tile + 1 < ntiles; ++tile) {
-    store_tile<CPR, PAD>(buf, lds, tid);
-    __syncthreads();
-    load_tile<CPR, P>(buf, rows, b, h, (tfirst + tile + 1) * kScoreTile, n, tid);
-    score_lane<T, D, G, WIN>(lds + tid * PAD, qg, is_l2, wo, (tfirst + tile) * kScoreTile + tid,
-                             n, logit, l2, obase, scale);
-    __syncthreads();
+  const int t0 = blockIdx.x * kScoreTile;
+  if (t0 >= n) return;
+  const int w = tid >> 6, lane = tid & 63;
+  const int half = __builtin_amdgcn_readfirstlane(w >> 1);
+  const int tok = (w & 1) * 64 + lane;
+  {
+    v4u buf[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int idx = j * 256 + tid, r = idx / CPR, c = idx % CPR;
+      buf[j] = *(const v4u*)(rows.template row<P>(b, h, min(t0 + r, n - 1)) + c * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int idx = j * 256 + tid, r = idx / CPR, c = idx % CPR;
+      *(v4u*)(lds + r * PAD + c * 16) = buf[j];
+    }
   }
-  store_tile<CPR, PAD>(buf, lds, tid);
   __syncthreads();
-  score_lane<T, D, G, WIN>(lds + tid * PAD, qg, is_l2, wo, (tfirst + ntiles - 1) * kScoreTile + tid,
-                           n, logit, l2, obase, scale);
+  const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
+  const bool is_win = metric != nullptr && metric[h] == HARDKV_METRIC_WINDOW;
+  const double* __restrict__ qg =
+      q64 + ((int64_t)b * window * hq + (int64_t)h * G) * D + half * (D / 2);
+  const unsigned char* row = lds + tok * PAD + half * (RB / 2);
+  const int t = t0 + tok;
+  const int64_t obase = ((int64_t)b * hkv + h) * cap_stride;
+  double acc[G], ss;
+  if (is_l2)
+    split_dot<T, D, G, PCS, true>(row, qg, acc, ss);
+  else
+    split_dot<T, D, G, PCS, false>(row, qg, acc, ss);
+  if (half) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) s_part[g][tok] = acc[g];
+    s_part[G][tok] = ss;
+  }
+  __syncthreads();
+  double mx = -INFINITY;
+  if (!half) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) mx = fmax(mx, acc[g] + s_part[g][tok]);
+    if (t < n) {
+      logit[obase + t] = (float)(mx * scale);
+      if (is_l2) l2[obase + t] = (float)sqrt(ss + s_part[G][tok]);
+    }
+  }
+  if (is_win) {
+    // observation window: the earlier queries of the window, one partial
+    // exchange each (a wave-uniform branch: the whole workgroup takes it)
+    double mw = mx;
+    if constexpr (WIN) {
+#pragma unroll 1
+      for (int i = 1; i < window; ++i) {
+        split_dot<T, D, G, PCS, false>(row, qg + (int64_t)i * hq * D, acc, ss);
+        __syncthreads();  // the previous exchange has been read
+        if (half) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) s_part[g][tok] = acc[g];
+        }
+        __syncthreads();
+        if (!half) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) mw = fmax(mw, acc[g] + s_part[g][tok]);
+        }
+      }
+    }
+    if (!half && t < n) wdst[obase + t] = (float)(mw * scale);
+  }
 }
 
 // Max-pooling of the window metric over positions [t - r, t + r] inside the
@@ -222,7 +200,7 @@ static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   observe("k_q_to_f64", st);
   hipLaunchKernelGGL(k_q_to_f64<T>, dim3(ceil_div(nq, 256)), dim3(256), 0, st, (const T*)a.q,
                      (const T*)a.q_hist, a.window, per_q, a.q64, nq);
-  dim3 grid(ceil_div(a.max_cand, kScoreTile * kScoreTiles), a.rows.hkv, a.B);
+  dim3 grid(ceil_div(a.max_cand, kScoreTile), a.rows.hkv, a.B);
   if (grid.x == 0) return;
   // window heads: the metric goes straight to l2 unless it is pooled
   float* wdst = a.radius > 0 ? a.wx : a.l2;
