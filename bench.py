@@ -254,6 +254,84 @@ def amortization(w, case, steps, horizons=(1, 2, 4, 8, 16, 32)):
     }
 
 
+def lifecycle(dev, reps=5, steady_steps=48):
+    """The multi-step lifecycle (hardkv_step_inplace) of one layer at the
+    Qwen3-32B attention shape: 64 sequences, 64 query / 8 KV heads, d = 128,
+    12288-token prefill, window 512, chunk 64, p = 0.95, fresh N(0, 1) query,
+    key and value every step.  Step 1 re-selects over the whole aged pool
+    (restored from a copy before each timed repetition); later steps run on
+    the pool that the selections left."""
+    import torch
+    from decode_kv_cache_head_amd import hardkv as H
+    B, Hq, Hkv, d, T0, W, C, p = 64, 64, 8, 128, 12288, 512, 64, 0.95
+    steps_cap = 1 + steady_steps + 8
+    desc = H.make_desc(B, Hq, Hkv, d, H.BF16, W, C, p, T0 + steps_cap)
+    A = T0 - W
+    ws = H.alloc_workspace(desc, dev)
+    out = torch.empty((B, Hq, d), device=dev)
+    g = torch.Generator(device=dev).manual_seed(4242)
+    t = H.alloc_tiers(desc, dev)
+    for i in range(0, B, 8):
+        t.k[i:i + 8, :, :A] = torch.randn((8, Hkv, A, d), generator=g, device=dev).to(torch.bfloat16)
+        t.v[i:i + 8, :, :A] = torch.randn((8, Hkv, A, d), generator=g, device=dev).to(torch.bfloat16)
+    t.pos[:, :, :A] = torch.arange(A, dtype=torch.int32, device=dev)
+    ring_k = torch.randn((B, Hkv, W, d), generator=g, device=dev).to(torch.bfloat16)
+    ring_v = torch.randn((B, Hkv, W, d), generator=g, device=dev).to(torch.bfloat16)
+    k0, v0 = t.k[:, :, :A].clone(), t.v[:, :, :A].clone()
+    r0k, r0v = ring_k.clone(), ring_v.clone()
+    seq = torch.full((B,), T0, dtype=torch.int32, device=dev)
+    st = H.State(ring_k, ring_v, t, seq)
+    qs = [torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(4)]
+    kn = torch.randn((B, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((B, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+
+    def reset():
+        t.k[:, :, :A].copy_(k0)
+        t.v[:, :, :A].copy_(v0)
+        t.pos[:, :, :A] = torch.arange(A, dtype=torch.int32, device=dev)
+        t.count.fill_(A)
+        t.ksum.zero_()
+        t.vsum.zero_()
+        t.ccount.zero_()
+        ring_k.copy_(r0k)
+        ring_v.copy_(r0v)
+        seq.fill_(T0)
+
+    s1 = []
+    for r in range(reps + 1):
+        reset()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        H.step_inplace(desc, qs[0], kn, vn, None, st, out, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if r:
+            s1.append(e0.elapsed_time(e1))
+    pool1 = int(t.count.float().median().item())
+    for i in range(steady_steps - 8):
+        H.step_inplace(desc, qs[i % 4], kn, vn, None, st, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(8):
+        H.step_inplace(desc, qs[i % 4], kn, vn, None, st, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    steady = e0.elapsed_time(e1) / 8
+    step1 = sum(s1) / len(s1)
+    res = {"shape": "qwen3-32b attention, B=64, T0=12288, W=512, C=64, p=0.95, one layer",
+           "step1_ms": round(step1, 4), "step1_pool_median_after": pool1,
+           "aged_pool_before_step1": A, "steady_ms": round(steady, 4),
+           "steady_after_steps": steady_steps,
+           "steady_pool_median": int(t.count.float().median().item()),
+           "step1_tokens_per_s": round(B / (step1 * 1e-3), 1),
+           "steady_tokens_per_s": round(B / (steady * 1e-3), 1)}
+    del t, k0, v0, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -425,6 +503,8 @@ def main():
             am[wp.name] = amortization(wp, S.make_case(wp, dev), args.steps)
             torch.cuda.empty_cache()
         res["amortization"] = am
+        print("[bench] lifecycle", file=sys.stderr, flush=True)
+        res["lifecycle"] = lifecycle(dev)
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(case, w, args.cpu_seconds)
