@@ -86,7 +86,7 @@ __device__ inline void wave_attn(const QT* __restrict__ qg, const Rows& kr, cons
                                  float (&o)[G][Lay<E, D>::EPL]) {
   using L = Lay<E, D>;
   constexpr int LPR = L::LPR, EPL = L::EPL, RPI = L::RPI;
-  constexpr int IT = 8;
+  constexpr int IT = G >= 8 ? 4 : 8;  // G = 8: smaller rounds keep two waves per SIMD
   constexpr int RR = IT * RPI;  // rows per round
   const int lane = threadIdx.x & 63;
   const int grp = lane / LPR, piece = lane % LPR;

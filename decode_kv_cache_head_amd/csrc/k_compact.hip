@@ -19,8 +19,8 @@
 // attention later loads its kept rows from the cache through the positions.
 //
 // Lifecycle (in place): k_compact_inplace runs one workgroup per (b, h) that
-// sweeps its pool in 64-row sub-tiles in order.  Every sub-tile is read
-// completely into LDS before any of its rows is written back, and a kept row
+// sweeps its pool in sub-tiles in order, reading each sub-tile before any of
+// its rows is written back and the next one while it is written.  A kept row
 // only moves to a slot at or below its own, so the left compaction never
 // overwrites a row that has not been read.  Evicted rows are added to the
 // running sums of chunk pos / C.
@@ -554,85 +554,133 @@ void launch_compact_attn(const CompactArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------ in place ----
+// One workgroup of 512 threads per (b, h) sweeps the pool in order, in
+// sub-tiles of 32 KB per tensor (128 rows of bf16 d = 128).  A sub-tile is
+// staged in LDS; while its kept rows are written to their slots and its
+// evicted rows are summed, the next sub-tile is already being loaded into
+// registers.  Reading ahead is safe: a kept row only moves to a slot at or
+// below its own, so every slot written while sub-tile s is processed lies
+// below the rows of sub-tile s + 1.  Evicted rows are added to the running
+// sums of chunk pos / C in ascending position order, one thread per (tensor,
+// dimension); a chunk's old sums are loaded when its first evicted row is
+// met and stored back when the next chunk starts.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_compact_inplace(CompactArgs a) {
+__global__ __launch_bounds__(512) void k_compact_inplace(CompactArgs a) {
+  constexpr int NT = 512;
   constexpr int RB = D * (int)sizeof(T);
-  constexpr int CPR = RB / 16;
-  constexpr int PIECES = 2 * 64 * CPR;
-  constexpr int PER = PIECES / 256;
-  __shared__ __attribute__((aligned(16))) unsigned char sk[64 * RB];
-  __shared__ __attribute__((aligned(16))) unsigned char sv[64 * RB];
-  __shared__ int s_rank[64];
-  __shared__ int s_sel[64];
-  __shared__ int s_pos[64];
-  __shared__ int s_base;
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  constexpr int CPR = RB / 16;        // 16-byte pieces per row
+  constexpr int SUB = 32768 / RB;     // rows per sub-tile
+  constexpr int NW = SUB / 64;        // 64-row words of mask bits
+  constexpr int PER = 2 * SUB * CPR / NT;  // pieces per thread (K then V)
+  static_assert(NW >= 1 && NW * 64 <= NT && PER % 2 == 0, "sub-tile shape");
+  __shared__ __attribute__((aligned(16))) unsigned char sk[SUB * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char sv[SUB * RB];
+  __shared__ unsigned long long s_bal[NW];
+  __shared__ int s_pos[SUB];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, w = tid >> 6;
   const int n = a.cand.n(b, h);
   const int64_t bh = (int64_t)b * a.hkv + h;
   const uint8_t* mk = a.mask + bh * a.cap_stride;
   char* pk = a.out_k + bh * a.cap_stride * RB;   // pool rows (read and written)
   char* pv = a.out_v + bh * a.cap_stride * RB;
   int32_t* pos = a.out_pos + bh * a.cap_stride;
+
+  v4u buf[PER];
+  bool sel = false;
+  int mypos = 0;
+  auto fetch = [&](int s0) {
+    const int nr = min(SUB, n - s0);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = (k % (PER / 2)) * NT + tid, r = idx / CPR, c = idx % CPR;
+      buf[k] = *(const v4u*)((k < PER / 2 ? pk : pv) + (int64_t)(s0 + min(r, nr - 1)) * RB + c * 16);
+    }
+    if (tid < SUB) {
+      sel = tid < nr && mk[s0 + tid] != 0;
+      mypos = tid < nr ? pos[s0 + tid] : 0;
+    }
+  };
+  auto kept = [&](int r) { return ((s_bal[r >> 6] >> (r & 63)) & 1ull) != 0; };
+
+  // running chunk sums of thread (tensor, dim)
   const bool summer = tid < 2 * D;
   const int tensor = tid / D, dim = tid % D;
-  float acc = 0.f;
-  int cnt = 0;
-  int cur = -1;
+  float* sums = (tensor ? a.vsum : a.ksum) + bh * a.chunk_stride * D + dim;
+  int32_t* cc = a.ccount + bh * a.chunk_stride;
+  float acc = 0.f, old = 0.f;
+  int cnt = 0, oldc = 0, cur = -1;
   auto flush = [&]() {
     if (cur < 0 || cur >= a.chunk_stride) return;  // positions outside the chunk capacity
-    float* dst = (tensor ? a.vsum : a.ksum) + (bh * a.chunk_stride + cur) * D + dim;
-    *dst += acc;
-    if (tid == 0) a.ccount[bh * a.chunk_stride + cur] += cnt;
+    sums[(int64_t)cur * D] = old + acc;
+    if (tid == 0) cc[cur] = oldc + cnt;
   };
+
   int base = 0;
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    const int nr = min(64, n - s0);
-    if (tid < 64) {
-      const bool sel = tid < nr && mk[s0 + tid] != 0;
+  if (n > 0) fetch(0);
+  for (int s0 = 0; s0 < n; s0 += SUB) {
+    const int nr = min(SUB, n - s0);
+    if (w < NW) {
       const unsigned long long bal = __ballot(sel);
-      s_sel[tid] = sel;
-      s_rank[tid] = base + __popcll(bal & ((1ull << tid) - 1ull));
-      s_pos[tid] = tid < nr ? pos[s0 + tid] : 0;
-      if (tid == 0) s_base = base + __popcll(bal);
-    }
-    v4u buf[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
-      buf[k] = *(const v4u*)((tsr ? pv : pk) + (int64_t)(s0 + min(r, nr - 1)) * RB + c * 16);
+      if ((tid & 63) == 0) s_bal[w] = bal;
+      s_pos[tid] = mypos;
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
-      if (r < nr) *(v4u*)((tsr ? sv : sk) + r * RB + c * 16) = buf[k];
+      const int idx = (k % (PER / 2)) * NT + tid, r = idx / CPR, c = idx % CPR;
+      if (r < nr) *(v4u*)((k < PER / 2 ? sk : sv) + r * RB + c * 16) = buf[k];
     }
-    __syncthreads();  // the whole sub-tile (rows, positions, ranks) is read
-    // write kept rows to their (lower or equal) slots
+    __syncthreads();  // the sub-tile, its positions and mask bits are in LDS
+    int total = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) total += __popcll(s_bal[v]);
+    auto rank = [&](int r) {
+      int rk = base;
+#pragma unroll
+      for (int v = 0; v < NW; ++v)
+        if (v < (r >> 6)) rk += __popcll(s_bal[v]);
+      return rk + __popcll(s_bal[r >> 6] & ((1ull << (r & 63)) - 1ull));
+    };
+    if (s0 + SUB < n) fetch(s0 + SUB);  // in flight during the writes below
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
-      if (r < nr && s_sel[r] && s_rank[r] != s0 + r)
-        *(v4u*)((tsr ? pv : pk) + (int64_t)s_rank[r] * RB + c * 16) =
-            *(const v4u*)((tsr ? sv : sk) + r * RB + c * 16);
-    }
-    if (tid < nr && s_sel[tid]) pos[s_rank[tid]] = s_pos[tid];
-    if (summer) {
-      const T* src = (const T*)(tensor ? sv : sk);
-      for (int r = 0; r < nr; ++r) {
-        if (s_sel[r]) continue;
-        const int ch = s_pos[r] / a.C;
-        if (ch != cur) {
-          flush();
-          cur = ch;
-          acc = 0.f;
-          cnt = 0;
-        }
-        acc += Elt<T>::load1(src + r * D + dim);
-        ++cnt;
+      const int idx = (k % (PER / 2)) * NT + tid, r = idx / CPR, c = idx % CPR;
+      if (r < nr && kept(r)) {
+        const int rk = rank(r);
+        if (rk != s0 + r)
+          *(v4u*)((k < PER / 2 ? pk : pv) + (int64_t)rk * RB + c * 16) =
+              *(const v4u*)((k < PER / 2 ? sk : sv) + r * RB + c * 16);
       }
     }
-    base = s_base;
-    __syncthreads();
+    if (tid < nr && kept(tid)) pos[rank(tid)] = s_pos[tid];
+    if (summer) {
+      const T* src = (const T*)(tensor ? sv : sk) + dim;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const int lo = v * 64;
+        if (lo >= nr) break;
+        unsigned long long ev = ~s_bal[v];
+        if (nr - lo < 64) ev &= (1ull << (nr - lo)) - 1ull;
+        while (ev) {
+          const int r = lo + __ffsll((long long)ev) - 1;
+          ev &= ev - 1ull;
+          const int ch = s_pos[r] / a.C;
+          if (ch != cur) {
+            flush();
+            cur = ch;
+            acc = 0.f;
+            cnt = 0;
+            if (cur < a.chunk_stride) {
+              old = sums[(int64_t)cur * D];
+              if (tid == 0) oldc = cc[cur];
+            }
+          }
+          acc += Elt<T>::load1(src + r * D);
+          ++cnt;
+        }
+      }
+    }
+    base += total;
+    __syncthreads();  // LDS is read before the next sub-tile is stored
   }
   if (summer) flush();
   if (tid == 0) a.out_count[bh] = base;
@@ -641,7 +689,7 @@ __global__ __launch_bounds__(256) void k_compact_inplace(CompactArgs a) {
 template <typename T, int D, int G_unused>
 static void launch_compact_inplace_t(const CompactArgs& a, hipStream_t st) {
   observe("k_compact_inplace", st);
-  hipLaunchKernelGGL((k_compact_inplace<T, D>), dim3(a.hkv, a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_compact_inplace<T, D>), dim3(a.hkv, a.B), dim3(512), 0, st, a);
 }
 
 void launch_compact_inplace(const CompactArgs& a, hipStream_t st) {
