@@ -131,6 +131,20 @@ __device__ inline uint64_t wfix(float c, double m) {
   return (uint64_t)__double2ull_rn(w * 140737488355328.0);
 }
 
+// ------------------------------------------------------ XCD placement ----
+// The chip's 8 XCDs (each with its own L2 and scalar caches) receive the
+// workgroups of a launch round-robin by linear id.  xcd_contiguous renumbers
+// linear id L of N so that each XCD works through one contiguous range of
+// the logical order instead: consecutive tiles of a head then run on the
+// same XCD and share its caches (a bijection on [0, N)).
+__device__ inline int xcd_contiguous(int L, int N) {
+  constexpr int X = 8;
+  const int per = (N + X - 1) / X;
+  const int tall = N % X == 0 ? X : N % X;  // XCDs that receive `per` workgroups
+  const int xcd = L % X, local = L / X;
+  return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+}
+
 // ------------------------------------------------------- wave reductions --
 __device__ inline double wave_sum_f64(double v) {
 #pragma unroll

@@ -78,9 +78,14 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
   constexpr int LOADS = kScoreTile * CPR / 256;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kScoreTile * PAD];
   __shared__ double s_part[G + 1][kScoreTile];  // second half's dots and squared norm
-  const int b = blockIdx.z, h = blockIdx.y, hkv = gridDim.y, tid = threadIdx.x;
+  // logical (tile, h, b), tile fastest, spread XCD-contiguously
+  const int hkv = gridDim.y, tid = threadIdx.x;
+  const int nwg = gridDim.x * gridDim.y * gridDim.z;
+  const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int id = xcd_contiguous(L, nwg);
+  const int tile = id % gridDim.x, h = (id / gridDim.x) % hkv, b = id / (gridDim.x * hkv);
   const int n = cand.n(b, h);
-  const int t0 = blockIdx.x * kScoreTile;
+  const int t0 = tile * kScoreTile;
   if (t0 >= n) return;
   const int w = tid >> 6, lane = tid & 63;
   const int half = __builtin_amdgcn_readfirstlane(w >> 1);
