@@ -50,6 +50,12 @@ in tests/test_oracle_window.py by a Hadamard closed form over several window
 queries, scipy's maximum filter for the pooling, the one-query reduction to
 the raw logits and the uniform closed form of a pooling radius that covers
 the candidates.
+
+The entropy-matched calibration rule (``entropy_temperature``; sections 2.A
+and 2.B: a temperature, the raw attention distribution, budgets from
+attention entropy) is pinned in tests/test_oracle_entropy.py by the
+proportional-logit closed form, an independent root of the same equation
+(scipy's brentq), exact power-of-two rescaling and the bisection's limits.
 """
 from __future__ import annotations
 
@@ -61,6 +67,12 @@ import numpy as np
 METRIC_QK = 0      # max-over-GQA-group q.k logit
 METRIC_L2 = 1      # key L2 norm
 METRIC_WINDOW = 2  # observation-window, position-pooled max logit
+
+# Calibration rule for heads whose metric is not the raw logit
+CALIB_SPREAD = 0   # temperature that matches the raw-logit spread (moments)
+CALIB_ENTROPY = 1  # temperature that matches the raw-attention entropy
+ENTROPY_STEPS = 32      # bisection halvings of the inverse-temperature bracket
+ENTROPY_SPAN = 1024.0   # bracket [0, ENTROPY_SPAN / (max s - min s)]
 
 
 def _f64(x) -> np.ndarray:
@@ -165,7 +177,47 @@ class Calibration:
     Z: float          # sum of w
 
 
-def calibrate_head(ell, s, metric: int) -> Calibration:
+def softmax_entropy(x) -> float:
+    """Entropy in nats of softmax(x) over the entries of x (float64):
+    ln Z - sum(w * d) / Z with d = x - max x, w = exp(d), Z = sum w."""
+    x64 = _f64(x)
+    d = x64 - x64.max()
+    w = np.exp(d)
+    Z = math.fsum(w)
+    return math.log(Z) - math.fsum(w * d) / Z
+
+
+def entropy_temperature(ell, s) -> float:
+    """Inverse temperature beta >= 0 for which softmax(beta * s) has the
+    entropy of softmax(ell), the head's raw attention over the candidates.
+
+    The entropy of softmax(beta * s) falls monotonically from ln n at
+    beta = 0 towards ln(number of maxima of s).  The root is bracketed in
+    [0, ENTROPY_SPAN / (max s - min s)] (at the upper end every
+    non-maximal token weighs below e^-1024 of the top) and the bracket is
+    halved ENTROPY_STEPS times: the midpoint's entropy above the target
+    moves the lower end up, otherwise the upper end down; the result is the
+    final midpoint.  A target beyond the bracket ends at its nearer end.
+    Requires max s > min s."""
+    s64 = _f64(s)
+    target = softmax_entropy(ell)
+    smax = float(s64.max())
+    R = smax - float(s64.min())
+    d = s64 - smax
+    lo, hi = 0.0, ENTROPY_SPAN / R
+    for _ in range(ENTROPY_STEPS):
+        mid = 0.5 * (lo + hi)
+        w = np.exp(mid * d)
+        Z = math.fsum(w)
+        H = math.log(Z) - mid * math.fsum(w * d) / Z
+        if H > target:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def calibrate_head(ell, s, metric: int, calib: int = CALIB_SPREAD) -> Calibration:
     """Map one head's importance scores into a softmax probability space.
 
     The pages state that calibration maps a selection metric onto a
@@ -178,6 +230,11 @@ def calibrate_head(ell, s, metric: int) -> Calibration:
         c = (s - mu_s) * sigma_ell / sigma_s, population moments over the
         candidates (the shift does not change the softmax).  A zero spread
         gives c = 0.
+      * with calib = CALIB_ENTROPY instead, the temperature that gives the
+        metric's softmax the entropy of the raw attention distribution (the
+        pages tie Tier-2 budgets to attention entropy, section 2.A):
+        c = (s - max s) * beta with beta from ``entropy_temperature``.  A
+        metric with no spread gives c = 0.
     The softmax domain is the candidate set only (dense-tier tokens are kept
     by rule).  Weights w = exp(c - max c), Z = sum w, float64.
     """
@@ -187,7 +244,17 @@ def calibrate_head(ell, s, metric: int) -> Calibration:
     if metric == METRIC_QK:
         shift, scale = 0.0, 1.0
         c = ell.copy()
+    elif metric in (METRIC_L2, METRIC_WINDOW) and calib == CALIB_ENTROPY:
+        s64 = _f64(s)
+        if n == 0 or s64.max() == s64.min():
+            shift, scale = 0.0, 0.0
+            c = np.zeros(n, np.float32)
+        else:
+            shift, scale = float(s64.max()), entropy_temperature(ell, s)
+            c = ((s64 - shift) * scale).astype(np.float32)
     elif metric in (METRIC_L2, METRIC_WINDOW):
+        if calib != CALIB_SPREAD:
+            raise ValueError(f"unknown calibration rule {calib}")
         if n == 0:
             shift, scale = 0.0, 0.0
             c = np.zeros(0, np.float32)
@@ -404,7 +471,7 @@ def dense_positions(T: int, S: int, A: int) -> np.ndarray:
 
 def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
               sinks: int = 0, merge: int = MERGE_MEAN, q_hist=None,
-              radius: int = 0) -> HeadResult:
+              radius: int = 0, calib: int = CALIB_SPREAD) -> HeadResult:
     """Single-step compression + attention of one KV head.
 
     K, V: [>=T, d] rows of this head's cache in position order (exact
@@ -426,7 +493,7 @@ def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
         if q_hist is not None and len(q_hist):
             qw.append(np.asarray(q_hist))
         s = window_score_head(np.concatenate(qw, axis=0), cand_K, radius)
-    cal = calibrate_head(ell, s, metric)
+    cal = calibrate_head(ell, s, metric, calib)
     sel = topp_head(cal.c, cal.w, cal.Z, p)
     mask = np.zeros(A, np.uint8)
     mask[sel.selected] = 1
