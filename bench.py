@@ -494,6 +494,15 @@ def main():
         metric_w = torch.full((w.Hkv,), H.METRIC_WINDOW, dtype=torch.int8, device=dev)
         var["window4_pool3"] = round(time_ms(lambda: H.step(dv, case.q, cache_w, metric_w, tiers,
                                                             out, wsv), args.steps), 4)
+        # every head on the key norm, calibrated by the spread or the entropy rule
+        metric_n = torch.full((w.Hkv,), H.METRIC_L2, dtype=torch.int8, device=dev)
+        for tag, rule in (("keynorm_spread", H.CALIB_SPREAD), ("keynorm_entropy", H.CALIB_ENTROPY)):
+            dv = H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.W, w.C, w.p, case.ctx_cap,
+                             w.block_size, case.max_blocks, desc.sparse_cap, desc.chunk_cap,
+                             calibration=rule)
+            wsv = H.alloc_workspace(dv, dev)
+            var[tag] = round(time_ms(lambda: H.step(dv, case.q, cache, metric_n, tiers, out, wsv),
+                                     args.steps), 4)
         res["variant_step_ms"] = var
     if not args.no_amortization:
         print("[bench] selection reuse", file=sys.stderr, flush=True)

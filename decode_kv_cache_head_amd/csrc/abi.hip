@@ -18,7 +18,7 @@ void hk::observe(const char* kernel, hipStream_t st) {
 
 namespace {
 
-constexpr int kVersion = 10400;  // 1.4.0
+constexpr int kVersion = 10500;  // 1.5.0
 
 int log2i(int v) {
   int l = 0;
@@ -53,6 +53,8 @@ int validate(const hardkv_desc* d) {
   if ((int64_t)d->dense_window + d->sinks > INT32_MAX / 2) return HARDKV_ERR_INVALID_ARG;
   if (d->packed_rows < 0) return HARDKV_ERR_INVALID_ARG;
   if (d->obs_window < 0 || d->obs_window > 64 || d->pool_radius < 0 || d->pool_radius > 512)
+    return HARDKV_ERR_INVALID_ARG;
+  if (d->calibration != HARDKV_CALIB_SPREAD && d->calibration != HARDKV_CALIB_ENTROPY)
     return HARDKV_ERR_INVALID_ARG;
   if (d->packed_rows > 0 &&
       (int64_t)d->batch * d->num_kv_heads * (int64_t)d->sparse_cap >= ((int64_t)1 << 31))
@@ -182,6 +184,7 @@ SelectArgs select_args(const hardkv_desc* d, const Cand& cand, const int8_t* met
   a.count = count;
   a.mode = nullptr;
   a.policy = hardkv_policy{HARDKV_POLICY_REWRITE, 1, 0, 0};
+  a.calib = d->calibration;
   return a;
 }
 
@@ -510,7 +513,7 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   if (rc) return rc;
   if (d->block_size != 0 || d->dense_window < 1 || d->sinks != 0 ||
       d->merge != HARDKV_MERGE_MEAN || d->packed_rows != 0 || window_of(d) != 1 ||
-      d->pool_radius != 0)
+      d->pool_radius != 0 || d->calibration != HARDKV_CALIB_SPREAD)
     return HARDKV_ERR_INVALID_ARG;
   if (!q || !k_new || !v_new || !s || !s->ring_k || !s->ring_v || !s->seq_len ||
       !tiers_ok(&s->tiers) || s->tiers.mode || !out)

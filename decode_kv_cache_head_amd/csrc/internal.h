@@ -88,6 +88,7 @@ struct SelectArgs {
   int32_t* count;       // [B][Hkv]
   uint8_t* mode;        // [B][Hkv] rewrite / sparse choice, written with count; may be null
   hardkv_policy policy;
+  int calib;            // HARDKV_CALIB_* for heads on the second score array
 };
 void launch_calibrate(const SelectArgs& a, hipStream_t st);
 void launch_select(const SelectArgs& a, hipStream_t st);

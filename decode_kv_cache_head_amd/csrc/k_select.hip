@@ -42,12 +42,91 @@ __device__ inline float block_max_f32(float v, float* sh) {
   return r;
 }
 
+template <int NW>
+__device__ inline void block_sum2_f64(double& a, double& b, double* sh) {
+  a = wave_sum_f64(a);
+  b = wave_sum_f64(b);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) {
+    sh[2 * w] = a;
+    sh[2 * w + 1] = b;
+  }
+  __syncthreads();
+  a = sh[0];
+  b = sh[1];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    a += sh[2 * i];
+    b += sh[2 * i + 1];
+  }
+}
+
+// Entropy-matched temperature (HARDKV_CALIB_ENTROPY) of one head, run by the
+// whole workgroup.  each_logit(f) / each_metric(f) call f on every logit /
+// metric value this thread holds.  Target: the entropy of softmax(logit),
+// ln Z - sum(w d) / Z with d = x - max x, w = exp(d).  The inverse
+// temperature beta in [0, 1024 / (max s - min s)] is bisected 32 times on the
+// entropy of softmax(beta s) (a midpoint entropy above the target raises the
+// lower end); c = (s - max s) * beta.  Every decision is taken on block sums
+// that all threads read in the same order, so the branch is uniform.
+constexpr int kEntropySteps = 32;
+constexpr double kEntropySpan = 1024.0;
+
+template <int NW, typename EachLogit, typename EachMetric>
+__device__ inline void entropy_temperature(EachLogit each_logit, EachMetric each_metric,
+                                           double* sh2, float* shf, double& shift,
+                                           double& scale) {
+  float lm = -INFINITY;
+  each_logit([&](float x) { lm = fmaxf(lm, x); });
+  const double lmax = (double)block_max_f32<NW>(lm, shf);
+  double z = 0.0, zd = 0.0;
+  each_logit([&](float x) {
+    const double d = (double)x - lmax, w = exp(d);
+    z += w;
+    zd += w * d;
+  });
+  block_sum2_f64<NW>(z, zd, sh2);
+  const double target = log(z) - zd / z;
+  float smx = -INFINITY, smn = -INFINITY;
+  each_metric([&](float x) {
+    smx = fmaxf(smx, x);
+    smn = fmaxf(smn, -x);
+  });
+  const double smax = (double)block_max_f32<NW>(smx, shf);
+  const double smin = -(double)block_max_f32<NW>(smn, shf);
+  if (smax == smin) {
+    shift = 0.0;
+    scale = 0.0;
+    return;
+  }
+  double lo = 0.0, hi = kEntropySpan / (smax - smin);
+  for (int it = 0; it < kEntropySteps; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    double zb = 0.0, zbd = 0.0;
+    each_metric([&](float x) {
+      const double d = (double)x - smax, w = exp(mid * d);
+      zb += w;
+      zbd += w * d;
+    });
+    block_sum2_f64<NW>(zb, zbd, sh2);
+    const double H = log(zb) - mid * zbd / zb;
+    if (H > target)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  shift = smax;
+  scale = 0.5 * (lo + hi);
+}
+
 // ------------------------------------------------------------ calibrate ---
 __global__ __launch_bounds__(256) void k_calibrate(Cand cand, const int8_t* __restrict__ metric,
                                                    const float* __restrict__ logit,
                                                    const float* __restrict__ l2,
-                                                   int64_t cap_stride, double* __restrict__ stats) {
-  __shared__ double shd[4];
+                                                   int64_t cap_stride, double* __restrict__ stats,
+                                                   int calib) {
+  __shared__ double shd[8];
   __shared__ float shf[4];
   const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
   const int n = cand.n(b, h);
@@ -55,7 +134,21 @@ __global__ __launch_bounds__(256) void k_calibrate(Cand cand, const int8_t* __re
   const float* x = logit + bh * cap_stride;
   const bool is_l2 = aux_metric(metric, h);  // second score array
   double shift = 0.0, scale = 1.0;
-  if (is_l2) {
+  if (is_l2 && calib == HARDKV_CALIB_ENTROPY) {
+    const float* s = l2 + bh * cap_stride;
+    shift = 0.0;
+    scale = 0.0;
+    if (n > 0)  // uniform over the workgroup
+      entropy_temperature<4>(
+          [&](auto f) {
+            for (int t = tid; t < n; t += 256) f(x[t]);
+          },
+          [&](auto f) {
+            for (int t = tid; t < n; t += 256) f(s[t]);
+          },
+          shd, shf, shift, scale);
+    x = s;
+  } else if (is_l2) {
     const float* s = l2 + bh * cap_stride;
     double sx = 0.0, sy = 0.0;
     for (int t = tid; t < n; t += 256) {
@@ -310,9 +403,9 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
                                                         int64_t cap_stride,
                                                         double* __restrict__ stats, float top_p,
                                                         uint8_t* __restrict__ mask,
-                                                        CountOut co) {
+                                                        CountOut co, int calib) {
   __shared__ SelShared S;
-  __shared__ double shd[kSelWaves];
+  __shared__ double shd[2 * kSelWaves];
   __shared__ float shf[kSelWaves];
   const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
   const int n = cand.n(b, h);
@@ -338,7 +431,29 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
     c[i] = t < n ? xs[t] : 0.f;
   }
   double shift = 0.0, scale = 1.0;
-  if (is_l2) {
+  if (is_l2 && calib == HARDKV_CALIB_ENTROPY) {
+    const float* ss = l2 + bh * cap_stride;
+    float sv[NPT];
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int t = tid + kSelThreads * i;
+      sv[i] = t < n ? ss[t] : 0.f;
+    }
+    entropy_temperature<kSelWaves>(
+        [&](auto f) {
+#pragma unroll
+          for (int i = 0; i < NPT; ++i)
+            if (tid + kSelThreads * i < n) f(c[i]);
+        },
+        [&](auto f) {
+#pragma unroll
+          for (int i = 0; i < NPT; ++i)
+            if (tid + kSelThreads * i < n) f(sv[i]);
+        },
+        shd, shf, shift, scale);
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) c[i] = cval(sv[i], shift, scale);
+  } else if (is_l2) {
     const float* ss = l2 + bh * cap_stride;
     float sv[NPT];
     double sx = 0.0, sy = 0.0;
@@ -561,16 +676,16 @@ void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st) {
   const dim3 grid(a.hkv, a.B), blk(kSelThreads);
   if (max_cand <= 4 * kSelThreads)
     hipLaunchKernelGGL(k_calsel<4>, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2,
-                       a.cap_stride, a.stats, a.top_p, a.mask, count_out(a));
+                       a.cap_stride, a.stats, a.top_p, a.mask, count_out(a), a.calib);
   else
     hipLaunchKernelGGL(k_calsel<16>, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2,
-                       a.cap_stride, a.stats, a.top_p, a.mask, count_out(a));
+                       a.cap_stride, a.stats, a.top_p, a.mask, count_out(a), a.calib);
 }
 
 void launch_calibrate(const SelectArgs& a, hipStream_t st) {
   observe("k_calibrate", st);
   hipLaunchKernelGGL(k_calibrate, dim3(a.hkv, a.B), dim3(256), 0, st, a.cand, a.metric, a.logit,
-                     a.l2, a.cap_stride, a.stats);
+                     a.l2, a.cap_stride, a.stats, a.calib);
 }
 
 void launch_select(const SelectArgs& a, hipStream_t st) {

@@ -22,6 +22,7 @@ F32, BF16 = 0, 1
 METRIC_QK, METRIC_L2, METRIC_WINDOW = 0, 1, 2
 MODE_REWRITE, MODE_SPARSE = 0, 1
 MERGE_MEAN, MERGE_WEIGHTED = 0, 1
+CALIB_SPREAD, CALIB_ENTROPY = 0, 1
 POLICY_REWRITE, POLICY_SPARSE, POLICY_MTI = 0, 1, 2
 INT32_MAX = 2 ** 31 - 1
 
@@ -44,7 +45,7 @@ class Desc(ctypes.Structure):
                 ("sparse_cap", ctypes.c_int32), ("chunk_cap", ctypes.c_int32),
                 ("top_p", ctypes.c_float), ("sinks", ctypes.c_int32), ("merge", ctypes.c_int32),
                 ("packed_rows", ctypes.c_int32), ("obs_window", ctypes.c_int32),
-                ("pool_radius", ctypes.c_int32)]
+                ("pool_radius", ctypes.c_int32), ("calibration", ctypes.c_int32)]
 
 
 class Cache(ctypes.Structure):
@@ -137,14 +138,15 @@ def _check(rc, fn):
 
 def make_desc(B, Hq, Hkv, d, dtype, W, C, top_p, ctx_cap, block_size=0, max_blocks=0,
               sparse_cap=None, chunk_cap=None, sinks=0, merge=MERGE_MEAN,
-              packed_rows=0, obs_window=1, pool_radius=0) -> Desc:
+              packed_rows=0, obs_window=1, pool_radius=0, calibration=CALIB_SPREAD) -> Desc:
     A = max(ctx_cap - W - sinks, 0)
     if sparse_cap is None:
         sparse_cap = A
     if chunk_cap is None:
         chunk_cap = -(-A // C) if C > 0 else 0
     return Desc(B, Hq, Hkv, d, dtype, W, C, block_size, ctx_cap, max_blocks, sparse_cap,
-                chunk_cap, float(top_p), sinks, merge, packed_rows, obs_window, pool_radius)
+                chunk_cap, float(top_p), sinks, merge, packed_rows, obs_window, pool_radius,
+                calibration)
 
 
 def validate(desc: Desc) -> int:

@@ -50,6 +50,7 @@ class Workload:
     merge: int = 0       # 0 mean, 1 attention-weighted merging of evicted tokens
     obs_window: int = 1  # queries in the observation window (window-metric heads)
     pool_radius: int = 0  # max-pooling radius of the window metric
+    calibration: int = 0  # temperature rule of non-logit heads: 0 spread, 1 entropy
 
     @property
     def G(self):

@@ -73,6 +73,14 @@ typedef struct ihipStream_t* hardkv_stream_t; /* same type as hipStream_t */
                                   [t - pool_radius, t + pool_radius]; calibrated like L2
                                   (section 2.B: SnapKV-style strategies) */
 
+/* How L2 and window heads are calibrated (hardkv_desc.calibration); QK heads
+ * always keep temperature 1 (section 2.B, Mechanism: a temperature maps a
+ * metric onto the raw attention distribution). */
+#define HARDKV_CALIB_SPREAD 0  /* c = (x - mean x) * std(logit) / std(x) */
+#define HARDKV_CALIB_ENTROPY 1 /* c = (x - max x) * beta, softmax(beta x) with the entropy of
+                                  softmax(logit) (section 2.A Tier 2: budgets from attention
+                                  entropy); beta from a fixed 32-step float64 bisection */
+
 /* How evicted tokens are merged into a condensed chunk (hardkv_desc.merge). */
 #define HARDKV_MERGE_MEAN 0     /* plain mean of the chunk's evicted tokens */
 #define HARDKV_MERGE_WEIGHTED 1 /* mean weighted by each token's calibrated attention weight */
@@ -132,6 +140,7 @@ typedef struct hardkv_desc {
   int32_t obs_window;   /* HARDKV_METRIC_WINDOW heads: queries in the observation window,
                            0..64 (0 or 1 = this step's query only; > 1 needs cache->q_hist) */
   int32_t pool_radius;  /* HARDKV_METRIC_WINDOW heads: max-pooling radius, 0..512 */
+  int32_t calibration;  /* HARDKV_CALIB_*: the temperature rule of L2 and window heads */
 } hardkv_desc;
 
 /* The KV cache of one layer.
@@ -231,8 +240,16 @@ int hardkv_score(const hardkv_desc* desc, const void* q, const hardkv_cache* cac
  * For each (b, h) maps the aged tokens' metric x into calibrated values
  *   c_t = fl32((x_t - shift) * scale)
  * QK heads: x = logit, shift 0, scale 1 (the raw attention distribution).
- * L2 and window heads: x = l2, shift = mean(l2), scale = std(logit) / std(l2)
- * (population moments over the aged tokens; 0 if either spread is 0).
+ * L2 and window heads, x = l2:
+ *   HARDKV_CALIB_SPREAD:  shift = mean(l2), scale = std(logit) / std(l2)
+ *                         (population moments over the aged tokens; 0 if either
+ *                         spread is 0)
+ *   HARDKV_CALIB_ENTROPY: shift = max(l2), scale = beta with
+ *                         H(softmax(beta l2)) = H(softmax(logit)), H the entropy:
+ *                         the bracket [0, 1024 / (max l2 - min l2)] is halved 32
+ *                         times (midpoint entropy above the target raises the lower
+ *                         end) and beta is the final midpoint; 0 if l2 is constant.
+ *                         Costs 32 float64 passes over the head's values.
  *   stats: [B][Hkv][4] float64 {shift, scale, m = max c, Z = sum exp(c - m)}. */
 int hardkv_calibrate(const hardkv_desc* desc, const int32_t* ctx_len, const int8_t* metric,
                      const float* logit, const float* l2, double* stats, void* ws,
@@ -340,7 +357,7 @@ int hardkv_step_policy(const hardkv_desc* desc, const hardkv_policy* policy, con
  *   4. every dropped resident is added to the running sums of chunk pos / C;
  *   5. attention over the ring, the pool and the chunks -> out [B][Hq][d] f32;
  *   6. seq_len[b] += 1.
- * desc->block_size, sinks, merge, packed_rows and pool_radius must be 0 and obs_window
+ * desc->block_size, sinks, merge, packed_rows, pool_radius and calibration must be 0 and obs_window
  * at most 1 (the pool has no position-ordered neighbours to pool or old queries to keep); ctx_cap bounds P + 1 and sizes the pool
  * (sparse_cap >= ctx_cap - W) and the chunks (chunk_cap >= ceil((ctx_cap - W) / C)). */
 int hardkv_step_inplace(const hardkv_desc* desc, const void* q, const void* k_new,

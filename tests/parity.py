@@ -35,7 +35,8 @@ def desc_for(case: S.Case, top_p=None, sparse_cap=None, chunk_cap=None) -> H.Des
     return H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.W, w.C,
                        w.p if top_p is None else top_p, case.ctx_cap, w.block_size,
                        case.max_blocks, sparse_cap, chunk_cap, w.sinks, w.merge,
-                       obs_window=w.obs_window, pool_radius=w.pool_radius)
+                       obs_window=w.obs_window, pool_radius=w.pool_radius,
+                       calibration=w.calibration)
 
 
 def cache_of(case: S.Case) -> H.Cache:
@@ -86,7 +87,7 @@ def oracle_head(case: S.Case, b: int, h: int, p: float):
     if case.q_hist is not None:
         hist = case.q_hist[b, :, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
     ref = O.step_head(q, K, V, w.T[b], w.W, w.C, p, int(w.metrics[h]), w.sinks, w.merge,
-                      q_hist=hist, radius=w.pool_radius)
+                      q_hist=hist, radius=w.pool_radius, calib=w.calibration)
     return q, K, V, ref
 
 

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = H.load()
-    assert lib.hardkv_version() == 10400
+    assert lib.hardkv_version() == 10500
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.hardkv_strerror(code)
     assert lib.hardkv_strerror(99) == b"unknown error"
@@ -42,7 +42,7 @@ def base_desc(**kw):
                        d["ctx_cap"], d.get("block_size", 0), d.get("max_blocks", 0),
                        d.get("sparse_cap"), d.get("chunk_cap"), d.get("sinks", 0),
                        d.get("merge", 0), d.get("packed_rows", 0), d.get("obs_window", 1),
-                       d.get("pool_radius", 0))
+                       d.get("pool_radius", 0), d.get("calibration", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -82,6 +82,9 @@ def base_desc(**kw):
     (dict(obs_window=65), H.ERR_INVALID_ARG),
     (dict(pool_radius=513), H.ERR_INVALID_ARG),
     (dict(pool_radius=-1), H.ERR_INVALID_ARG),
+    (dict(calibration=H.CALIB_ENTROPY), H.OK),
+    (dict(calibration=2), H.ERR_INVALID_ARG),
+    (dict(calibration=-1), H.ERR_INVALID_ARG),
 ])
 def test_validate_codes(kw, code):
     assert H.validate(base_desc(**kw)) == code
@@ -274,3 +277,16 @@ def test_window_metric_needs_the_query_history():
     state = H.StateC(fake, fake, tiers, fake)
     assert lib.hardkv_step_inplace(d, fake, fake, fake, None, ctypes.byref(state), fake, fake,
                                    need, st) == H.ERR_INVALID_ARG
+
+
+def test_lifecycle_keeps_the_spread_rule():
+    # the running chunk sums of the lifecycle are built under one rule
+    lib = H.load()
+    fake = ctypes.c_void_p(0x1000)
+    st = ctypes.c_void_p(0)
+    ent = base_desc(calibration=H.CALIB_ENTROPY)
+    need = H.workspace_size(ent)
+    assert need == H.workspace_size(base_desc())  # no extra workspace
+    state = H.StateC(fake, fake, H.TiersC(*([fake] * 7)), fake)
+    assert lib.hardkv_step_inplace(ctypes.byref(ent), fake, fake, fake, None, ctypes.byref(state),
+                                   fake, fake, need, st) == H.ERR_INVALID_ARG

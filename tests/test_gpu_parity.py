@@ -77,6 +77,15 @@ GRID = [
     dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=1, C=64, p=0.7, obs_window=8, pool_radius=64, merge=1,
          sinks=3, metric=(S.METRIC_WINDOW,)),
     dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.9, metric=(S.METRIC_WINDOW, S.METRIC_QK)),
+    # entropy-matched calibration of key-norm and window heads
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.9, metric=(S.METRIC_L2, S.METRIC_QK),
+         calibration=1),
+    dict(dtype=S.DT_F32, d=64, Hq=8, Hkv=4, C=7, p=0.8, obs_window=2, calibration=1,
+         metric=(S.METRIC_WINDOW, S.METRIC_L2, S.METRIC_WINDOW, S.METRIC_QK)),
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.95, T=(9000, 5000, 300),
+         metric=(S.METRIC_L2, S.METRIC_L2), calibration=1),
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.9, block_size=16, sinks=4, merge=1,
+         metric=(S.METRIC_WINDOW, S.METRIC_L2), obs_window=4, pool_radius=3, calibration=1),
 ]
 
 
@@ -227,6 +236,36 @@ def test_headline_with_window_metric(gpu):
     check_all_heads_invariants(case, desc, g)
     rep = check_case(case, g, w.p, heads=_sample_heads(w, 4, 3), stages=False)
     say(rep)
+
+
+def test_headline_with_entropy_calibration(gpu):
+    """The headline shape with every other KV head on the key norm,
+    calibrated by the entropy-matched temperature: sampled heads against the
+    oracle, invariants on every head."""
+    w = S.workload("qwen8b_b32_16k_paged", metric=(S.METRIC_L2, S.METRIC_QK) * 4, calibration=1)
+    say(w.name, "entropy calibration")
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_step(case, desc)
+    check_all_heads_invariants(case, desc, g)
+    rep = check_case(case, g, w.p, heads=_sample_heads(w, 6, 4), stages=False)
+    say(rep)
+
+
+def test_mixed_metric_64k_entropy_calibration(gpu):
+    """65280 candidates per head: the standalone calibrate kernel's entropy
+    bisection on flat and peaked key-norm heads."""
+    w = S.workload("qwen8b_b8_64k_mixed", calibration=1)
+    say(w.name, "entropy calibration")
+    case = S.make_case(w, gpu)
+    desc = desc_for(case, top_p=0.9)
+    g = run_stages(case, desc)
+    check_all_heads_invariants(case, desc, g)
+    rep = check_case(case, g, 0.9, heads=[(0, 4), (2, 5), (7, 6), (1, 0)])
+    say(rep)
+    # the peaked key-norm head keeps far fewer tokens than the flat ones
+    cnt = g["tiers"].count.float()
+    assert cnt[:, 4].max() < 0.5 * cnt[:, [5, 6, 7]].min()
 
 
 def test_ragged_b32_paged(gpu):
