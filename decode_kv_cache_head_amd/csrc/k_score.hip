@@ -30,7 +30,12 @@ __global__ __launch_bounds__(256) void k_q_to_f64(const T* __restrict__ q,
   q64[i] = (double)Elt<T>::load1(src);
 }
 
-constexpr int kScoreTile = 128;  // tokens per workgroup
+constexpr int kScoreTile = 128;  // tokens per tile
+// consecutive tiles per workgroup, the next one loaded while the current one
+// is scored; at G = 8 the float64 work dominates and single tiles in more
+// workgroups are faster
+template <int G>
+constexpr int score_group() { return G >= 8 ? 1 : 4; }
 
 // Partial q.k over one split of the row: `row` points at the split's first
 // byte, `qg` at the split's first query element; float64 from exact inputs.
@@ -56,15 +61,16 @@ __device__ __forceinline__ void split_dot(const unsigned char* row, const double
   }
 }
 
-// One 128-token tile of one (b, h) per 256-thread workgroup.  The tile is
-// staged into LDS with coalesced 16-byte loads; then every token is scored
-// by two lanes in different waves, one per half of the head dimension:
-// waves 0-1 take the first half of tokens 0-63 / 64-127, waves 2-3 the
-// second half.  The half index is wave-uniform, so the float64 query
-// elements stay scalar loads (SGPR operands of v_fma_f64); the second half's
-// partial sums reach the first through LDS.  Small register and LDS
-// footprints (four workgroups per CU) let the waves of other workgroups
-// cover the loads, instead of a register prefetch inside one workgroup.
+// Consecutive 128-token tiles of one (b, h) per 256-thread workgroup (four,
+// or one at G = 8).  A tile is staged into LDS with coalesced 16-byte loads,
+// and the next tile's loads are issued into registers before the current one
+// is scored, so each workgroup keeps its loads in flight while its float64
+// arithmetic runs.  Every token is scored by two lanes in different waves,
+// one per half of the head dimension: waves 0-1 take the first half of
+// tokens 0-63 / 64-127, waves 2-3 the second half.  The half index is
+// wave-uniform, so the float64 query elements stay scalar loads (SGPR
+// operands of v_fma_f64); the second half's partial sums reach the first
+// through LDS.
 template <typename T, int D, int G, bool P, bool WIN>
 __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, int hq, Rows rows,
                                                Cand cand, const int8_t* __restrict__ metric,
@@ -78,80 +84,104 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
   constexpr int LOADS = kScoreTile * CPR / 256;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kScoreTile * PAD];
   __shared__ double s_part[G + 1][kScoreTile];  // second half's dots and squared norm
-  // logical (tile, h, b), tile fastest, spread XCD-contiguously
+  // logical (tile group, h, b), tile group fastest, spread XCD-contiguously
   const int hkv = gridDim.y, tid = threadIdx.x;
   const int nwg = gridDim.x * gridDim.y * gridDim.z;
   const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const int id = xcd_contiguous(L, nwg);
-  const int tile = id % gridDim.x, h = (id / gridDim.x) % hkv, b = id / (gridDim.x * hkv);
+  const int grp = id % gridDim.x, h = (id / gridDim.x) % hkv, b = id / (gridDim.x * hkv);
   const int n = cand.n(b, h);
-  const int t0 = tile * kScoreTile;
-  if (t0 >= n) return;
+  constexpr int kScoreGroup = score_group<G>();
+  const int g0 = grp * kScoreGroup * kScoreTile;
+  if (g0 >= n) return;
   const int w = tid >> 6, lane = tid & 63;
   const int half = __builtin_amdgcn_readfirstlane(w >> 1);
   const int tok = (w & 1) * 64 + lane;
-  {
-    v4u buf[LOADS];
+  const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
+  const bool is_win = metric != nullptr && metric[h] == HARDKV_METRIC_WINDOW;
+  const int64_t qoff = ((int64_t)b * window * hq + (int64_t)h * G) * D + half * (D / 2);
+  const unsigned char* row = lds + tok * PAD + half * (RB / 2);
+  const int64_t obase = ((int64_t)b * hkv + h) * cap_stride;
+  v4u buf[LOADS];
+  auto fetch = [&](int t0) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int idx = j * 256 + tid, r = idx / CPR, c = idx % CPR;
       buf[j] = *(const v4u*)(rows.template row<P>(b, h, min(t0 + r, n - 1)) + c * 16);
     }
+  };
+  // scores of the staged tile starting at t0 (uniform over the workgroup)
+  auto score_staged = [&](int t0) {
+    const int t = t0 + tok;
+    const double* __restrict__ qg = q64 + qoff;
+    double acc[G], ss;
+    if (is_l2)
+      split_dot<T, D, G, PCS, true>(row, qg, acc, ss);
+    else
+      split_dot<T, D, G, PCS, false>(row, qg, acc, ss);
+    if (half) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) s_part[g][tok] = acc[g];
+      s_part[G][tok] = ss;
+    }
+    __syncthreads();
+    double mx = -INFINITY;
+    if (!half) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) mx = fmax(mx, acc[g] + s_part[g][tok]);
+      if (t < n) {
+        logit[obase + t] = (float)(mx * scale);
+        if (is_l2) l2[obase + t] = (float)sqrt(ss + s_part[G][tok]);
+      }
+    }
+    if (is_win) {
+      // observation window: the earlier queries of the window, one partial
+      // exchange each (a wave-uniform branch: the whole workgroup takes it)
+      double mw = mx;
+      if constexpr (WIN) {
+#pragma unroll 1
+        for (int i = 1; i < window; ++i) {
+          split_dot<T, D, G, PCS, false>(row, qg + (int64_t)i * hq * D, acc, ss);
+          __syncthreads();  // the previous exchange has been read
+          if (half) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) s_part[g][tok] = acc[g];
+          }
+          __syncthreads();
+          if (!half) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) mw = fmax(mw, acc[g] + s_part[g][tok]);
+          }
+        }
+      }
+      if (!half && t < n) wdst[obase + t] = (float)(mw * scale);
+    }
+  };
+  fetch(g0);
+  if constexpr (kScoreGroup == 1) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int idx = j * 256 + tid, r = idx / CPR, c = idx % CPR;
       *(v4u*)(lds + r * PAD + c * 16) = buf[j];
     }
-  }
-  __syncthreads();
-  const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
-  const bool is_win = metric != nullptr && metric[h] == HARDKV_METRIC_WINDOW;
-  const double* __restrict__ qg =
-      q64 + ((int64_t)b * window * hq + (int64_t)h * G) * D + half * (D / 2);
-  const unsigned char* row = lds + tok * PAD + half * (RB / 2);
-  const int t = t0 + tok;
-  const int64_t obase = ((int64_t)b * hkv + h) * cap_stride;
-  double acc[G], ss;
-  if (is_l2)
-    split_dot<T, D, G, PCS, true>(row, qg, acc, ss);
-  else
-    split_dot<T, D, G, PCS, false>(row, qg, acc, ss);
-  if (half) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) s_part[g][tok] = acc[g];
-    s_part[G][tok] = ss;
-  }
-  __syncthreads();
-  double mx = -INFINITY;
-  if (!half) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) mx = fmax(mx, acc[g] + s_part[g][tok]);
-    if (t < n) {
-      logit[obase + t] = (float)(mx * scale);
-      if (is_l2) l2[obase + t] = (float)sqrt(ss + s_part[G][tok]);
-    }
-  }
-  if (is_win) {
-    // observation window: the earlier queries of the window, one partial
-    // exchange each (a wave-uniform branch: the whole workgroup takes it)
-    double mw = mx;
-    if constexpr (WIN) {
+    __syncthreads();
+    score_staged(g0);
+  } else {
 #pragma unroll 1
-      for (int i = 1; i < window; ++i) {
-        split_dot<T, D, G, PCS, false>(row, qg + (int64_t)i * hq * D, acc, ss);
-        __syncthreads();  // the previous exchange has been read
-        if (half) {
+    for (int k = 0; k < kScoreGroup; ++k) {
+      const int t0 = g0 + k * kScoreTile;  // uniform over the workgroup
+      if (t0 >= n) break;
+      if (k) __syncthreads();  // the previous tile's LDS and exchange reads are done
 #pragma unroll
-          for (int g = 0; g < G; ++g) s_part[g][tok] = acc[g];
-        }
-        __syncthreads();
-        if (!half) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) mw = fmax(mw, acc[g] + s_part[g][tok]);
-        }
+      for (int j = 0; j < LOADS; ++j) {
+        const int idx = j * 256 + tid, r = idx / CPR, c = idx % CPR;
+        *(v4u*)(lds + r * PAD + c * 16) = buf[j];
       }
+      __syncthreads();
+      // the next tile's rows are in flight while this one is scored
+      if (k + 1 < kScoreGroup && t0 + kScoreTile < n) fetch(t0 + kScoreTile);
+      score_staged(t0);
     }
-    if (!half && t < n) wdst[obase + t] = (float)(mw * scale);
   }
 }
 
@@ -205,7 +235,7 @@ static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   observe("k_q_to_f64", st);
   hipLaunchKernelGGL(k_q_to_f64<T>, dim3(ceil_div(nq, 256)), dim3(256), 0, st, (const T*)a.q,
                      (const T*)a.q_hist, a.window, per_q, a.q64, nq);
-  dim3 grid(ceil_div(a.max_cand, kScoreTile), a.rows.hkv, a.B);
+  dim3 grid(ceil_div(a.max_cand, kScoreTile * score_group<G>()), a.rows.hkv, a.B);
   if (grid.x == 0) return;
   // window heads: the metric goes straight to l2 unless it is pooled
   float* wdst = a.radius > 0 ? a.wx : a.l2;
