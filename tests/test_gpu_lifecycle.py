@@ -131,6 +131,9 @@ def check_step(run, states, s, rep):
     dict(B=2, Hq=16, Hkv=2, d=128, T0=1500, W=512, C=64, p=0.95, steps=12),
     dict(B=3, Hq=8, Hkv=4, d=64, T0=700, W=100, C=7, p=0.8, steps=9),
     dict(B=1, Hq=4, Hkv=4, d=128, T0=300, W=64, C=1, p=0.5, steps=6, dtype=torch.float32),
+    # chunks wider than a compaction sub-tile (128 bf16 rows): running sums
+    # carried across sub-tiles
+    dict(B=2, Hq=8, Hkv=2, d=128, T0=1400, W=64, C=300, p=0.9, steps=5),
 ])
 def test_lifecycle_matches_oracle(gpu, cfg):
     steps = cfg.pop("steps")
