@@ -64,3 +64,69 @@ def test_step_graph_replay_matches_eager(gpu, name, kw):
         if rep == 3:   # and the replayed step is right, not only repeatable
             rep_ = check_case(case, dict(tiers=tiers, out=out), w.p, stages=False)
             print(rep_, file=sys.stderr, flush=True)
+
+
+def _lifecycle(dev, seed, B, Hq, Hkv, d, T0, W, C, p, steps):
+    g = torch.Generator(device=dev).manual_seed(seed)
+    desc = H.make_desc(B, Hq, Hkv, d, H.BF16, W, C, p, T0 + steps)
+    A = T0 - W
+    K = torch.randn((B, Hkv, T0, d), generator=g, device=dev).to(torch.bfloat16)
+    V = torch.randn((B, Hkv, T0, d), generator=g, device=dev).to(torch.bfloat16)
+    tiers = H.alloc_tiers(desc, dev, zero=True)
+    tiers.k[:, :, :A] = K[:, :, :A]
+    tiers.v[:, :, :A] = V[:, :, :A]
+    tiers.pos[:, :, :A] = torch.arange(A, dtype=torch.int32, device=dev)
+    tiers.count.fill_(A)
+    ring_k = torch.empty((B, Hkv, W, d), dtype=torch.bfloat16, device=dev)
+    ring_v = torch.empty_like(ring_k)
+    for t in range(T0 - W, T0):
+        ring_k[:, :, t % W] = K[:, :, t]
+        ring_v[:, :, t % W] = V[:, :, t]
+    state = H.State(ring_k, ring_v, tiers, torch.full((B,), T0, dtype=torch.int32, device=dev))
+    return desc, state
+
+
+def test_lifecycle_graph_replayed_300_steps(gpu):
+    """hardkv_step_inplace captured once and replayed for 300 consecutive
+    decode steps (new query, key and value copied into the captured buffers
+    before each replay) equals the same 300 steps run eagerly: every step's
+    attention output and the final ring, pool, chunk sums and lengths bit
+    for bit."""
+    B, Hq, Hkv, d, T0, W, C, p, steps = 2, 16, 2, 128, 1200, 64, 32, 0.9, 300
+    desc, st_g = _lifecycle(gpu, 21, B, Hq, Hkv, d, T0, W, C, p, steps)
+    _, st_e = _lifecycle(gpu, 21, B, Hq, Hkv, d, T0, W, C, p, steps)
+    ws_g, ws_e = H.alloc_workspace(desc, gpu), H.alloc_workspace(desc, gpu)
+    q = torch.zeros((B, Hq, d), dtype=torch.bfloat16, device=gpu)
+    kn = torch.zeros((B, Hkv, d), dtype=torch.bfloat16, device=gpu)
+    vn = torch.zeros_like(kn)
+    out_g = torch.empty((B, Hq, d), device=gpu)
+    out_e = torch.empty_like(out_g)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):  # recorded only: the state is not advanced here
+        H.step_inplace(desc, q, kn, vn, None, st_g, out_g, ws_g)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device=gpu).manual_seed(22)
+    for s in range(steps):
+        q.copy_((torch.randn(q.shape, generator=gen, device=gpu) * 1.5).to(q.dtype))
+        kn.copy_(torch.randn(kn.shape, generator=gen, device=gpu).to(kn.dtype))
+        vn.copy_(torch.randn(vn.shape, generator=gen, device=gpu).to(vn.dtype))
+        g.replay()
+        H.step_inplace(desc, q, kn, vn, None, st_e, out_e, ws_e)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), s
+    assert torch.equal(st_g.seq_len, st_e.seq_len)
+    assert int(st_g.seq_len[0]) == T0 + steps
+    assert torch.equal(st_g.ring_k, st_e.ring_k) and torch.equal(st_g.ring_v, st_e.ring_v)
+    tg, te = st_g.tiers, st_e.tiers
+    assert torch.equal(tg.count, te.count)
+    for b in range(B):
+        for h in range(Hkv):
+            n = int(te.count[b, h])
+            assert torch.equal(tg.pos[b, h, :n], te.pos[b, h, :n])
+            assert torch.equal(tg.k[b, h, :n], te.k[b, h, :n])
+            assert torch.equal(tg.v[b, h, :n], te.v[b, h, :n])
+    assert torch.equal(tg.ccount, te.ccount)
+    assert torch.equal(tg.ksum, te.ksum) and torch.equal(tg.vsum, te.vsum)
+    # tokens kept flowing into the condensed tier over the replays
+    assert int(tg.ccount.sum()) > B * Hkv * (T0 - W) // 4
+    print("pool after", steps, "steps:", te.count.tolist(), file=sys.stderr, flush=True)
