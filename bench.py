@@ -264,7 +264,7 @@ def lifecycle(dev, reps=5, steady_steps=48):
     import torch
     from decode_kv_cache_head_amd import hardkv as H
     B, Hq, Hkv, d, T0, W, C, p = 64, 64, 8, 128, 12288, 512, 64, 0.95
-    steps_cap = 1 + steady_steps + 8
+    steps_cap = 1 + steady_steps + 8 + 8  # step 1, steady steps, graph replays
     desc = H.make_desc(B, Hq, Hkv, d, H.BF16, W, C, p, T0 + steps_cap)
     A = T0 - W
     ws = H.alloc_workspace(desc, dev)
@@ -319,10 +319,25 @@ def lifecycle(dev, reps=5, steady_steps=48):
     e1.record()
     torch.cuda.synchronize()
     steady = e0.elapsed_time(e1) / 8
+    # the same steady step captured once in a HIP graph and replayed
+    qg = qs[0].clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        H.step_inplace(desc, qg, kn, vn, None, st, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(8):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    steady_graph = e0.elapsed_time(e1) / 8
+    del graph
     step1 = sum(s1) / len(s1)
     res = {"shape": "qwen3-32b attention, B=64, T0=12288, W=512, C=64, p=0.95, one layer",
            "step1_ms": round(step1, 4), "step1_pool_median_after": pool1,
            "aged_pool_before_step1": A, "steady_ms": round(steady, 4),
+           "steady_graph_replay_ms": round(steady_graph, 4),
            "steady_after_steps": steady_steps,
            "steady_pool_median": int(t.count.float().median().item()),
            "step1_tokens_per_s": round(B / (step1 * 1e-3), 1),
