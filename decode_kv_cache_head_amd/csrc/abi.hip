@@ -150,6 +150,7 @@ void do_score(const hardkv_desc* d, const Layout& L, char* ws, const void* q, co
   a.G = d->num_q_heads / d->num_kv_heads;
   a.B = d->batch;
   a.hq = d->num_q_heads;
+  a.hkv = d->num_kv_heads;
   a.q = q;
   a.q_hist = q_hist;
   a.window = window_of(d);
@@ -518,6 +519,23 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   if (!q || !k_new || !v_new || !s || !s->ring_k || !s->ring_v || !s->seq_len ||
       !tiers_ok(&s->tiers) || s->tiers.mode || !out)
     return HARDKV_ERR_INVALID_ARG;
+  // head-wise block manager of the pool
+  PoolPaging pg{};
+  if (s->pool_block != 0) {
+    const int bs = s->pool_block;
+    if (bs < 1 || bs > 4096 || (bs & (bs - 1)) || s->pool_blocks < 1 || !s->pool_table ||
+        !s->free_ids || !s->free_top)
+      return HARDKV_ERR_INVALID_ARG;
+    pg.lbs = log2i(bs);
+    pg.maxb = ceil_div(d->sparse_cap, bs);
+    pg.nblocks = s->pool_blocks;
+    if ((int64_t)d->batch * d->num_kv_heads * pg.maxb >= ((int64_t)1 << 31) ||
+        (int64_t)s->pool_blocks * bs >= ((int64_t)1 << 31))
+      return HARDKV_ERR_INVALID_ARG;
+    pg.table = s->pool_table;
+    pg.free_ids = s->free_ids;
+    pg.free_top = s->free_top;
+  }
   const Layout L = layout(d);
   char* w = (char*)ws;
   hipStream_t st = (hipStream_t)stream;
@@ -541,12 +559,29 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   ap.pool_pos = t->pos;
   ap.pool_count = t->count;
   ap.seq_len = s->seq_len;
+  ap.pg = pg;
+  ap.ksum = t->ksum;
+  ap.vsum = t->vsum;
+  ap.ccount = t->ccount;
+  ap.C = d->chunk;
+  ap.chunk_cap = d->chunk_cap;
+  if (pg.table) launch_pool_grow(ap, st);
   launch_append(ap, st);
 
   const Cand cand{nullptr, t->count, d->dense_window, d->ctx_cap, d->sparse_cap,
                   d->num_kv_heads};
-  const Rows pk = region_rows(d, t->k, d->sparse_cap);
-  const Rows pv = region_rows(d, t->v, d->sparse_cap);
+  Rows pk = region_rows(d, t->k, d->sparse_cap);
+  Rows pv = region_rows(d, t->v, d->sparse_cap);
+  if (pg.table) {
+    // pool rows through per-head block tables (one head per block)
+    for (Rows* r : {&pk, &pv}) {
+      r->table = pg.table;
+      r->hkv = 1;
+      r->lbs = pg.lbs;
+      r->max_blocks = pg.maxb;
+      r->headtab = d->num_kv_heads;
+    }
+  }
   float* logit = (float*)(w + L.logit);
   float* l2 = (float*)(w + L.l2);
   double* stats = (double*)(w + L.stats);
@@ -556,8 +591,15 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
   launch_calibrate(sa, st);
   launch_select(sa, st);
-  launch_compact_inplace(compact_args(d, L, w, pk, pv, cand, d->sparse_cap, mask, t), st);
+  CompactArgs ca = compact_args(d, L, w, pk, pv, cand, d->sparse_cap, mask, t);
+  ca.pg = pg;
+  launch_compact_inplace(ca, st);
+  if (pg.table) launch_pool_shrink(pg, t->count, d->batch * d->num_kv_heads, st);
   AttnArgs a = attn_args(d, L, w, q, t, out);
+  if (pg.table) {
+    a.sk = pk;
+    a.sv = pv;
+  }
   a.dk = region_rows(d, s->ring_k, d->dense_window);
   a.dv = region_rows(d, s->ring_v, d->dense_window);
   a.ctx_len = s->seq_len;

@@ -62,6 +62,12 @@ struct Rows {
   int32_t max_blocks;
   int32_t row_bytes;
   int32_t off;  // added to every position (the first candidate position)
+  // > 0: per-head block tables (the lifecycle pool's block manager): blocks
+  // hold one head's rows and sequence b's head h uses table row b * headtab + h;
+  // row() is then called with tb(b, h), th(h) (hkv = 1 in that case)
+  int32_t headtab;
+  __device__ inline int tb(int b, int h) const { return headtab ? b * headtab + h : b; }
+  __device__ inline int th(int h) const { return headtab ? 0 : h; }
   // PAGED is a compile-time property of the launch, so the unrolled loads of
   // a tile stay in one basic block.
   template <bool PAGED>

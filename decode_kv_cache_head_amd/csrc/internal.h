@@ -57,7 +57,7 @@ namespace hk {
 void observe(const char* kernel, hipStream_t st);
 
 struct ScoreArgs {
-  int dtype, D, G, B, hq;
+  int dtype, D, G, B, hq, hkv;
   const void* q;
   const void* q_hist;  // [B][window - 1][Hq][D] previous queries (window metric)
   int window;          // queries in the observation window (>= 1)
@@ -108,6 +108,17 @@ inline int compact_tile(int C) { return C >= 1024 ? C : C * (1024 / C); }
 // which can also fold attention over the kept rows into the same pass.
 inline bool compact_fusable(int C) { return C % 64 == 0 && compact_tile(C) <= 1024; }
 
+// Head-wise block manager of the lifecycle pool: table == nullptr means
+// per-head regions of sparse_cap rows.
+struct PoolPaging {
+  int32_t* table;     // [B * Hkv][maxb] block ids or -1
+  int32_t* free_ids;  // [nblocks] stack
+  int32_t* free_top;  // [1]
+  int lbs;            // log2(rows per block)
+  int maxb;           // table entries per head
+  int nblocks;
+};
+
 struct CompactArgs {
   int dtype, D, B, hkv, C;
   Rows krows, vrows;    // candidate rows
@@ -133,6 +144,7 @@ struct CompactArgs {
   const float* logit;
   const float* l2;
   const double* stats;  // [B][Hkv][4] {shift, scale, max, Z}
+  PoolPaging pg;         // in place: pool rows through per-head block tables
   // fused attention over the kept rows (launch_compact_attn only)
   int G, hq;
   const void* q;        // [B][Hq][D]
@@ -189,8 +201,18 @@ struct AppendArgs {
   int32_t* pool_pos;
   int32_t* pool_count;
   const int32_t* seq_len;
+  PoolPaging pg;
+  // condensed tier, for a token that finds no free block
+  float* ksum;
+  float* vsum;
+  int32_t* ccount;
+  int C, chunk_cap;
 };
 void launch_append(const AppendArgs& a, hipStream_t st);
 void launch_advance(int32_t* seq_len, int B, hipStream_t st);
+// block manager: blocks for the rows the append is about to write, and the
+// return of blocks past each head's count after the compaction
+void launch_pool_grow(const AppendArgs& a, hipStream_t st);
+void launch_pool_shrink(const PoolPaging& pg, const int32_t* count, int n_heads, hipStream_t st);
 
 }  // namespace hk

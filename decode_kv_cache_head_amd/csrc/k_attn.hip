@@ -226,7 +226,9 @@ __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr
   }
 }
 
-template <typename T, int D, int G, bool P>
+// PS: the sparse tier is the lifecycle pool under the block manager (rows
+// through per-head block tables; the dense tier is then the ring, P false).
+template <typename T, int D, int G, bool P, bool PS>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   __shared__ float s_m[4 * G], s_l[4 * G];
   __shared__ float s_o[4 * G * D];
@@ -257,6 +259,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       sk.region = sv.region = 0;
       tile_attn<T, D, G, T, false, false>(a, qg, sk, sv, b, h, r0, min(kAttnTile, tc.ns - r0),
                                           nullptr, s_m, s_l, s_o, part_out);
+    } else if constexpr (PS) {
+      tile_attn<T, D, G, T, false, true>(a, qg, a.sk, a.sv, a.sk.tb(b, h), a.sk.th(h), r0,
+                                         min(kAttnTile, tc.ns - r0), nullptr, s_m, s_l, s_o,
+                                         part_out);
     } else {
       tile_attn<T, D, G, T, false, false>(a, qg, a.sk, a.sv, b, h, r0,
                                           min(kAttnTile, tc.ns - r0), nullptr, s_m, s_l, s_o,
@@ -326,7 +332,12 @@ static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
                      : a.max_tiles;
   if (gx > 0) {
     observe("k_attn", st);
-    hipLaunchKernelGGL((k_attn<T, D, G, P>), dim3(gx, a.hkv, a.B), dim3(256), 0, st, a);
+    bool pool_paged = false;
+    if constexpr (!P) pool_paged = a.sk.table != nullptr;
+    if (pool_paged)
+      hipLaunchKernelGGL((k_attn<T, D, G, false, true>), dim3(gx, a.hkv, a.B), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_attn<T, D, G, P, false>), dim3(gx, a.hkv, a.B), dim3(256), 0, st, a);
   }
   observe("k_attn_merge", st);
   hipLaunchKernelGGL((k_attn_merge<T, D, G>), dim3(ceil_div((int64_t)a.B * a.hq, 4)), dim3(256),

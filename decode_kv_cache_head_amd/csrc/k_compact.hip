@@ -581,9 +581,17 @@ __global__ __launch_bounds__(512) void k_compact_inplace(CompactArgs a) {
   const int n = a.cand.n(b, h);
   const int64_t bh = (int64_t)b * a.hkv + h;
   const uint8_t* mk = a.mask + bh * a.cap_stride;
-  char* pk = a.out_k + bh * a.cap_stride * RB;   // pool rows (read and written)
-  char* pv = a.out_v + bh * a.cap_stride * RB;
   int32_t* pos = a.out_pos + bh * a.cap_stride;
+  // pool row r (read and written): the head's region, or row r % bs of block
+  // table[r / bs] under the block manager (a missing block reads as block 0:
+  // the tables always cover [0, count))
+  const int32_t* ptab = a.pg.table ? a.pg.table + bh * a.pg.maxb : nullptr;
+  auto prow = [&](char* base, int r) -> char* {
+    if (!ptab) return base + (bh * a.cap_stride + r) * RB;
+    int blk = ptab[r >> a.pg.lbs];
+    blk = blk < 0 || blk >= a.pg.nblocks ? 0 : blk;
+    return base + (((int64_t)blk << a.pg.lbs) + (r & ((1 << a.pg.lbs) - 1))) * RB;
+  };
 
   v4u buf[PER];
   bool sel = false;
@@ -593,7 +601,7 @@ __global__ __launch_bounds__(512) void k_compact_inplace(CompactArgs a) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int idx = (k % (PER / 2)) * NT + tid, r = idx / CPR, c = idx % CPR;
-      buf[k] = *(const v4u*)((k < PER / 2 ? pk : pv) + (int64_t)(s0 + min(r, nr - 1)) * RB + c * 16);
+      buf[k] = *(const v4u*)(prow(k < PER / 2 ? a.out_k : a.out_v, s0 + min(r, nr - 1)) + c * 16);
     }
     if (tid < SUB) {
       sel = tid < nr && mk[s0 + tid] != 0;
@@ -647,7 +655,7 @@ __global__ __launch_bounds__(512) void k_compact_inplace(CompactArgs a) {
       if (r < nr && kept(r)) {
         const int rk = rank(r);
         if (rk != s0 + r)
-          *(v4u*)((k < PER / 2 ? pk : pv) + (int64_t)rk * RB + c * 16) =
+          *(v4u*)(prow(k < PER / 2 ? a.out_k : a.out_v, rk) + c * 16) =
               *(const v4u*)((k < PER / 2 ? sk : sv) + r * RB + c * 16);
       }
     }

@@ -103,11 +103,12 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
   const unsigned char* row = lds + tok * PAD + half * (RB / 2);
   const int64_t obase = ((int64_t)b * hkv + h) * cap_stride;
   v4u buf[LOADS];
+  const int rb = rows.tb(b, h), rh = rows.th(h);  // (b, h) as the row tables index them
   auto fetch = [&](int t0) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int idx = j * 256 + tid, r = idx / CPR, c = idx % CPR;
-      buf[j] = *(const v4u*)(rows.template row<P>(b, h, min(t0 + r, n - 1)) + c * 16);
+      buf[j] = *(const v4u*)(rows.template row<P>(rb, rh, min(t0 + r, n - 1)) + c * 16);
     }
   };
   // scores of the staged tile starting at t0 (uniform over the workgroup)
@@ -235,7 +236,7 @@ static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   observe("k_q_to_f64", st);
   hipLaunchKernelGGL(k_q_to_f64<T>, dim3(ceil_div(nq, 256)), dim3(256), 0, st, (const T*)a.q,
                      (const T*)a.q_hist, a.window, per_q, a.q64, nq);
-  dim3 grid(ceil_div(a.max_cand, kScoreTile * score_group<G>()), a.rows.hkv, a.B);
+  dim3 grid(ceil_div(a.max_cand, kScoreTile * score_group<G>()), a.hkv, a.B);
   if (grid.x == 0) return;
   // window heads: the metric goes straight to l2 unless it is pooled
   float* wdst = a.radius > 0 ? a.wx : a.l2;
@@ -248,7 +249,7 @@ static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
                        a.cand, a.metric, a.logit, a.l2, wdst, a.window, a.cap_stride, a.scale);
   if (a.radius > 0 && a.metric != nullptr) {
     observe("k_pool", st);
-    hipLaunchKernelGGL(k_pool, dim3(ceil_div(a.max_cand, kPoolTile), a.rows.hkv, a.B), dim3(256),
+    hipLaunchKernelGGL(k_pool, dim3(ceil_div(a.max_cand, kPoolTile), a.hkv, a.B), dim3(256),
                        0, st, a.cand, a.metric, (const float*)a.wx, a.l2, a.cap_stride, a.radius);
   }
 }

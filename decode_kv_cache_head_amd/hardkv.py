@@ -68,7 +68,10 @@ class Policy(ctypes.Structure):
 
 class StateC(ctypes.Structure):
     _fields_ = [("ring_k", ctypes.c_void_p), ("ring_v", ctypes.c_void_p),
-                ("tiers", TiersC), ("seq_len", ctypes.c_void_p)]
+                ("tiers", TiersC), ("seq_len", ctypes.c_void_p),
+                ("pool_table", ctypes.c_void_p), ("free_ids", ctypes.c_void_p),
+                ("free_top", ctypes.c_void_p), ("pool_block", ctypes.c_int32),
+                ("pool_blocks", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -295,9 +298,63 @@ class State:
     ring_v: torch.Tensor
     tiers: Tiers
     seq_len: torch.Tensor
+    # head-wise block manager of the pool (None: per-head regions)
+    pool_table: torch.Tensor | None = None  # [B][Hkv][ceil(sparse_cap / pool_block)] int32
+    free_ids: torch.Tensor | None = None    # [pool_blocks] int32 stack
+    free_top: torch.Tensor | None = None    # [1] int32
+    pool_block: int = 0
 
     def c(self) -> StateC:
-        return StateC(_p(self.ring_k), _p(self.ring_v), self.tiers.c(), _p(self.seq_len))
+        nblk = self.free_ids.numel() if self.free_ids is not None else 0
+        return StateC(_p(self.ring_k), _p(self.ring_v), self.tiers.c(), _p(self.seq_len),
+                      _p(self.pool_table), _p(self.free_ids), _p(self.free_top),
+                      self.pool_block, nblk)
+
+    def pool_rows(self, b, h, which="k"):
+        """Head (b, h)'s pool rows 0..count-1 in order (either layout)."""
+        src = self.tiers.k if which == "k" else self.tiers.v
+        n = int(self.tiers.count[b, h])
+        if self.pool_block == 0:
+            return src[b, h, :n]
+        nb = -(-n // self.pool_block)
+        ids = self.pool_table[b, h, :nb].long()
+        return src[ids].reshape(-1, src.shape[-1])[:n]
+
+    def blocks_held(self) -> int:
+        return int((self.pool_table >= 0).sum()) if self.pool_table is not None else 0
+
+
+def paged_state(desc: Desc, K_aged, V_aged, ring_k, ring_v, seq_len, pool_block: int,
+                pool_blocks: int) -> State:
+    """Lifecycle state with the pool under the block manager, holding the
+    aged rows K_aged / V_aged ([B][Hkv][A][d], position order 0..A-1): head
+    (b, h) gets blocks (b * Hkv + h) * nb .. + nb - 1, nb = ceil(A / pool_block);
+    the other blocks go on the free stack, lowest id on top."""
+    B, Hkv, A, d = K_aged.shape
+    dev = K_aged.device
+    bs = pool_block
+    nb = -(-A // bs)
+    maxb = -(-desc.sparse_cap // bs)
+    used = B * Hkv * nb
+    if used > pool_blocks or nb > maxb:
+        raise ValueError("the prefill does not fit the block pool")
+    tiers = alloc_tiers(desc, dev, zero=True)
+    tiers.k = torch.zeros((pool_blocks, bs, d), dtype=K_aged.dtype, device=dev)
+    tiers.v = torch.zeros_like(tiers.k)
+    pad = nb * bs - A
+    kk = torch.nn.functional.pad(K_aged, (0, 0, 0, pad)) if pad else K_aged
+    vv = torch.nn.functional.pad(V_aged, (0, 0, 0, pad)) if pad else V_aged
+    tiers.k[:used] = kk.reshape(used, bs, d)
+    tiers.v[:used] = vv.reshape(used, bs, d)
+    tiers.pos[:, :, :A] = torch.arange(A, dtype=torch.int32, device=dev)
+    tiers.count.fill_(A)
+    table = torch.full((B, Hkv, maxb), -1, dtype=torch.int32, device=dev)
+    table[:, :, :nb] = torch.arange(used, dtype=torch.int32, device=dev).reshape(B, Hkv, nb)
+    free = torch.arange(pool_blocks - 1, used - 1, -1, dtype=torch.int32, device=dev)
+    free_ids = torch.full((pool_blocks,), -1, dtype=torch.int32, device=dev)
+    free_ids[:free.numel()] = free
+    top = torch.tensor([free.numel()], dtype=torch.int32, device=dev)
+    return State(ring_k, ring_v, tiers, seq_len, table, free_ids, top, bs)
 
 
 def step_inplace(desc, q, k_new, v_new, metric, state: State, out, ws, stream=None):

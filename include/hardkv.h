@@ -188,12 +188,33 @@ typedef struct hardkv_tiers {
  *   ring_k, ring_v: [B][Hkv][W][d] dense window; position t lives in slot t % W
  *   tiers: sparse pool (positions ascending, `count` residents) and running chunk sums;
  *          tiers.mode must be NULL (the pool is always compacted in place)
- *   seq_len: [B] int32 tokens seen so far; must be >= W; advanced by one per step */
+ *   seq_len: [B] int32 tokens seen so far; must be >= W; advanced by one per step
+ *
+ * Head-wise block manager (section 2.C: a head-wise block manager allocates
+ * head-adaptive budgets under static shapes).  pool_block = 0: every (b, h)
+ * owns a region of sparse_cap pool rows (tiers.k / tiers.v = [B][Hkv][sparse_cap][d]).
+ * pool_block > 0 (a power of two, at most 4096): pool row r of (b, h) lives in
+ * row r % pool_block of block pool_table[b][h][r / pool_block] of a shared pool,
+ * tiers.k / tiers.v = [pool_blocks][pool_block][d] (one head per block); tiers.pos
+ * stays [B][Hkv][sparse_cap].  A head holds exactly ceil(count / pool_block)
+ * blocks (table entries beyond are -1).  Every step, before the append, each
+ * head whose next row starts a block takes one from the free stack
+ * free_ids[0 .. *free_top) (top first, heads served in (b, h) order); after the
+ * compaction every head returns the blocks it no longer needs (pushed in (b, h)
+ * order, each head's in ascending table index).  Deterministic.  When the stack
+ * is empty, the token leaving the window goes straight into its condensed
+ * chunk instead of the pool.  The caller sets up the tables, the stack and the
+ * pool rows (e.g. after prefill) so that these invariants hold. */
 typedef struct hardkv_state {
   void* ring_k;
   void* ring_v;
   hardkv_tiers tiers;
   int32_t* seq_len;
+  int32_t* pool_table;  /* [B][Hkv][ceil(sparse_cap / pool_block)] block ids or -1 */
+  int32_t* free_ids;    /* [pool_blocks] stack of free block ids */
+  int32_t* free_top;    /* [1] free ids on the stack */
+  int32_t pool_block;   /* rows per block; 0 = per-head regions (the fields above unused) */
+  int32_t pool_blocks;  /* blocks in the shared pool */
 } hardkv_state;
 
 /* Library version (major * 10000 + minor * 100 + patch). */
@@ -350,16 +371,21 @@ int hardkv_step_policy(const hardkv_desc* desc, const hardkv_policy* policy, con
 /* One decode step of the multi-step token lifecycle on persistent tiers
  * (section 2.A: tokens move dense -> sparse -> condensed as they age; the
  * sparse tier is re-selected every step).  For every (b, h), with P = seq_len[b]:
+ *   0. (block manager) heads whose next pool row starts a block take one;
  *   1. append: the token in ring slot P % W (position P - W) moves to the end of
- *      the sparse pool; k_new / v_new ([B][Hkv][d]) take its ring slot;
+ *      the sparse pool (or, with the block manager out of blocks, into its
+ *      chunk); k_new / v_new ([B][Hkv][d]) take its ring slot;
  *   2. score, calibrate and top-p over the pool residents;
  *   3. the kept residents are compacted in place (stable, positions ascending);
- *   4. every dropped resident is added to the running sums of chunk pos / C;
+ *   4. every dropped resident is added to the running sums of chunk pos / C
+ *      (block manager: blocks past the new count go back to the free stack);
  *   5. attention over the ring, the pool and the chunks -> out [B][Hq][d] f32;
  *   6. seq_len[b] += 1.
  * desc->block_size, sinks, merge, packed_rows, pool_radius and calibration must be 0 and obs_window
  * at most 1 (the pool has no position-ordered neighbours to pool or old queries to keep); ctx_cap bounds P + 1 and sizes the pool
- * (sparse_cap >= ctx_cap - W) and the chunks (chunk_cap >= ceil((ctx_cap - W) / C)). */
+ * (sparse_cap >= ctx_cap - W) and the chunks (chunk_cap >= ceil((ctx_cap - W) / C)).
+ * With state->pool_block > 0: pool_table, free_ids and free_top non-NULL, pool_blocks >= 1,
+ * B * Hkv * ceil(sparse_cap / pool_block) < 2^31 and pool_blocks * pool_block < 2^31. */
 int hardkv_step_inplace(const hardkv_desc* desc, const void* q, const void* k_new,
                         const void* v_new, const int8_t* metric, const hardkv_state* state,
                         float* out, void* ws, size_t ws_bytes, hardkv_stream_t stream);

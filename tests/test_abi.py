@@ -290,3 +290,20 @@ def test_lifecycle_keeps_the_spread_rule():
     state = H.StateC(fake, fake, H.TiersC(*([fake] * 7)), fake)
     assert lib.hardkv_step_inplace(ctypes.byref(ent), fake, fake, fake, None, ctypes.byref(state),
                                    fake, fake, need, st) == H.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(pool_block=48), dict(pool_block=8192), dict(pool_block=-16),
+                                dict(pool_block=16, pool_blocks=0),
+                                dict(pool_block=16, table=False), dict(pool_block=16, stack=False)])
+def test_block_manager_arguments(kw):
+    lib = H.load()
+    fake = ctypes.c_void_p(0x1000)
+    st = ctypes.c_void_p(0)
+    d = base_desc()
+    need = H.workspace_size(d)
+    state = H.StateC(fake, fake, H.TiersC(*([fake] * 7)), fake,
+                     None if kw.get("table") is False else fake,
+                     None if kw.get("stack") is False else fake, fake,
+                     kw.get("pool_block", 0), kw.get("pool_blocks", 64))
+    assert lib.hardkv_step_inplace(ctypes.byref(d), fake, fake, fake, None, ctypes.byref(state),
+                                   fake, fake, need, st) == H.ERR_INVALID_ARG

@@ -28,7 +28,8 @@ def say(*a):
 class Run:
     """Seeded lifecycle inputs and the GPU state for one layer."""
 
-    def __init__(self, dev, seed, B, Hq, Hkv, d, T0, W, C, p, steps, dtype=torch.bfloat16):
+    def __init__(self, dev, seed, B, Hq, Hkv, d, T0, W, C, p, steps, dtype=torch.bfloat16,
+                 pool_block=0, pool_blocks=None):
         g = torch.Generator(device=dev).manual_seed(seed)
         self.B, self.Hq, self.Hkv, self.d, self.T0, self.W, self.C, self.p = B, Hq, Hkv, d, T0, W, C, p
         self.G = Hq // Hkv
@@ -52,8 +53,14 @@ class Run:
         for t in range(T0 - W, T0):
             ring_k[:, :, t % W] = self.K[:, :, t]
             ring_v[:, :, t % W] = self.V[:, :, t]
-        self.state = H.State(ring_k, ring_v, tiers,
-                             torch.full((B,), T0, dtype=torch.int32, device=dev))
+        seq = torch.full((B,), T0, dtype=torch.int32, device=dev)
+        if pool_block:
+            maxb = -(-self.desc.sparse_cap // pool_block)
+            nblk = pool_blocks if pool_blocks is not None else B * Hkv * maxb
+            self.state = H.paged_state(self.desc, self.K[:, :, :A], self.V[:, :, :A], ring_k,
+                                       ring_v, seq, pool_block, nblk)
+        else:
+            self.state = H.State(ring_k, ring_v, tiers, seq)
         self.ws = H.alloc_workspace(self.desc, dev)
         self.out = torch.empty((B, Hq, d), device=dev)
 
@@ -72,12 +79,36 @@ def resync(st, run, b, h):
     """Oracle state of (b, h) from the GPU tiers (staged comparison)."""
     t = run.state.tiers
     n = int(t.count[b, h])
-    st.pool_K = t.k[b, h, :n].float().cpu().numpy()
-    st.pool_V = t.v[b, h, :n].float().cpu().numpy()
+    st.pool_K = run.state.pool_rows(b, h, "k").float().cpu().numpy()
+    st.pool_V = run.state.pool_rows(b, h, "v").float().cpu().numpy()
     st.pool_pos = t.pos[b, h, :n].cpu().numpy().astype(np.int64)
     st.ksum = t.ksum[b, h].double().cpu().numpy()
     st.vsum = t.vsum[b, h].double().cpu().numpy()
     st.cnt = t.ccount[b, h].cpu().numpy().astype(np.int64)
+
+
+def check_blocks(state):
+    """Block manager invariants: each head holds exactly ceil(count / bs)
+    blocks (its first table entries), ids are distinct, and the held and the
+    free blocks together are the whole pool."""
+    if not state.pool_block:
+        return
+    bs = state.pool_block
+    tab = state.pool_table.cpu().numpy()
+    cnt = state.tiers.count.cpu().numpy()
+    held = []
+    for b in range(tab.shape[0]):
+        for h in range(tab.shape[1]):
+            need = -(-int(cnt[b, h]) // bs)
+            assert (tab[b, h, :need] >= 0).all() and (tab[b, h, need:] == -1).all(), (b, h)
+            held += tab[b, h, :need].tolist()
+    top = int(state.free_top.item())
+    free = state.free_ids[:top].cpu().numpy().tolist()
+    nblk = state.free_ids.numel()
+    assert len(set(held)) == len(held) and len(set(free)) == len(free)
+    assert not set(held) & set(free)
+    assert len(held) + top == nblk
+    assert all(0 <= x < nblk for x in held + free)
 
 
 def check_step(run, states, s, rep):
@@ -109,7 +140,7 @@ def check_step(run, states, s, rep):
         # pool rows are bit copies of the tokens at their positions
         src_k = np.concatenate([run.K[b, h].float().cpu().numpy(),
                                 run.knew[:s + 1, b, h].float().cpu().numpy()])
-        assert np.array_equal(t.k[b, h, :n].float().cpu().numpy(), src_k[pos])
+        assert np.array_equal(run.state.pool_rows(b, h, "k").float().cpu().numpy(), src_k[pos])
         assert np.array_equal(t.pos[b, h, :n].cpu().numpy(), st.pool_pos)
         cc = t.ccount[b, h].cpu().numpy()
         assert np.array_equal(cc, st.cnt)
@@ -125,6 +156,7 @@ def check_step(run, states, s, rep):
         err = np.abs(o - out_ref).max(axis=1) / np.abs(out_ref).max(axis=1)
         assert np.all(err <= ATTN_TOL), (s, b, h, err.max())
         rep["max_attn_err"] = max(rep["max_attn_err"], float(err.max()))
+    check_blocks(run.state)
 
 
 @pytest.mark.parametrize("cfg", [
@@ -134,6 +166,12 @@ def check_step(run, states, s, rep):
     # chunks wider than a compaction sub-tile (128 bf16 rows): running sums
     # carried across sub-tiles
     dict(B=2, Hq=8, Hkv=2, d=128, T0=1400, W=64, C=300, p=0.9, steps=5),
+    # the pool under the head-wise block manager
+    dict(B=2, Hq=16, Hkv=2, d=128, T0=1500, W=512, C=64, p=0.95, steps=12, pool_block=64),
+    dict(B=3, Hq=8, Hkv=4, d=64, T0=700, W=100, C=7, p=0.8, steps=9, pool_block=16),
+    dict(B=1, Hq=4, Hkv=4, d=128, T0=300, W=64, C=1, p=0.5, steps=6, dtype=torch.float32,
+         pool_block=32),
+    dict(B=2, Hq=8, Hkv=2, d=128, T0=1400, W=64, C=300, p=0.9, steps=5, pool_block=128),
 ])
 def test_lifecycle_matches_oracle(gpu, cfg):
     steps = cfg.pop("steps")
@@ -147,6 +185,39 @@ def test_lifecycle_matches_oracle(gpu, cfg):
     say(rep)
     # tokens keep flowing dense -> sparse -> condensed
     assert int(run.state.tiers.ccount.sum()) > 0
+
+
+def test_block_manager_returns_blocks_and_runs_out_gracefully(gpu):
+    """p = 1 keeps every token, so the pools only grow; with one spare block
+    the first requester in (b, h) order takes it and the other heads' aged
+    tokens go straight into their chunks.  Nothing is lost, the run is
+    deterministic, and with fresh random queries (p = 0.9) the blocks the
+    compaction empties return to the stack."""
+    cfg = dict(B=2, Hq=8, Hkv=2, d=128, T0=700, W=64, C=32, steps=12, pool_block=16)
+    A = 700 - 64                      # 636 rows: 40 blocks per head, 4 rows free in the last
+    runs = [Run(gpu, 31, p=1.0, pool_blocks=4 * 40 + 1, **cfg) for _ in range(2)]
+    for s in range(12):
+        for r in runs:
+            r.gpu_step(s)
+        a, b_ = runs[0].state, runs[1].state
+        assert torch.equal(a.tiers.count, b_.tiers.count) and torch.equal(a.pool_table, b_.pool_table)
+        assert torch.equal(a.tiers.ccount, b_.tiers.ccount) and torch.equal(a.tiers.ksum, b_.tiers.ksum)
+        aged = 700 + s + 1 - 64
+        total = a.tiers.count + a.tiers.ccount.sum(-1)
+        assert torch.all(total == aged), (s, total.tolist())
+        check_blocks(a)
+    cnt = runs[0].state.tiers.count.cpu().tolist()
+    # head (0, 0) got the spare block at step 5 (row 640) and keeps growing
+    assert cnt[0][0] == A + 12 and cnt[0][1] == cnt[1][0] == cnt[1][1] == 640
+    assert int(runs[0].state.free_top.item()) == 0
+    # compaction under fresh random queries empties blocks, which return
+    run = Run(gpu, 32, p=0.9, **cfg)
+    before = run.state.blocks_held()
+    for s in range(12):
+        run.gpu_step(s)
+        check_blocks(run.state)
+    assert run.state.blocks_held() < before // 2
+    assert int(run.state.free_top.item()) == run.state.free_ids.numel() - run.state.blocks_held()
 
 
 def test_lifecycle_p_one_keeps_everything(gpu):
