@@ -66,7 +66,7 @@ def test_step_graph_replay_matches_eager(gpu, name, kw):
             print(rep_, file=sys.stderr, flush=True)
 
 
-def _lifecycle(dev, seed, B, Hq, Hkv, d, T0, W, C, p, steps):
+def _lifecycle(dev, seed, B, Hq, Hkv, d, T0, W, C, p, steps, pool_block=0):
     g = torch.Generator(device=dev).manual_seed(seed)
     desc = H.make_desc(B, Hq, Hkv, d, H.BF16, W, C, p, T0 + steps)
     A = T0 - W
@@ -82,19 +82,24 @@ def _lifecycle(dev, seed, B, Hq, Hkv, d, T0, W, C, p, steps):
     for t in range(T0 - W, T0):
         ring_k[:, :, t % W] = K[:, :, t]
         ring_v[:, :, t % W] = V[:, :, t]
-    state = H.State(ring_k, ring_v, tiers, torch.full((B,), T0, dtype=torch.int32, device=dev))
-    return desc, state
+    seq = torch.full((B,), T0, dtype=torch.int32, device=dev)
+    if pool_block:
+        maxb = -(-desc.sparse_cap // pool_block)
+        return desc, H.paged_state(desc, K[:, :, :A], V[:, :, :A], ring_k, ring_v, seq, pool_block,
+                                   B * Hkv * maxb)
+    return desc, H.State(ring_k, ring_v, tiers, seq)
 
 
-def test_lifecycle_graph_replayed_300_steps(gpu):
+@pytest.mark.parametrize("pool_block", [0, 64])
+def test_lifecycle_graph_replayed_300_steps(gpu, pool_block):
     """hardkv_step_inplace captured once and replayed for 300 consecutive
     decode steps (new query, key and value copied into the captured buffers
     before each replay) equals the same 300 steps run eagerly: every step's
     attention output and the final ring, pool, chunk sums and lengths bit
-    for bit."""
+    for bit; with the block manager also its tables and free stack."""
     B, Hq, Hkv, d, T0, W, C, p, steps = 2, 16, 2, 128, 1200, 64, 32, 0.9, 300
-    desc, st_g = _lifecycle(gpu, 21, B, Hq, Hkv, d, T0, W, C, p, steps)
-    _, st_e = _lifecycle(gpu, 21, B, Hq, Hkv, d, T0, W, C, p, steps)
+    desc, st_g = _lifecycle(gpu, 21, B, Hq, Hkv, d, T0, W, C, p, steps, pool_block)
+    _, st_e = _lifecycle(gpu, 21, B, Hq, Hkv, d, T0, W, C, p, steps, pool_block)
     ws_g, ws_e = H.alloc_workspace(desc, gpu), H.alloc_workspace(desc, gpu)
     q = torch.zeros((B, Hq, d), dtype=torch.bfloat16, device=gpu)
     kn = torch.zeros((B, Hkv, d), dtype=torch.bfloat16, device=gpu)
@@ -123,8 +128,14 @@ def test_lifecycle_graph_replayed_300_steps(gpu):
         for h in range(Hkv):
             n = int(te.count[b, h])
             assert torch.equal(tg.pos[b, h, :n], te.pos[b, h, :n])
-            assert torch.equal(tg.k[b, h, :n], te.k[b, h, :n])
-            assert torch.equal(tg.v[b, h, :n], te.v[b, h, :n])
+            assert torch.equal(st_g.pool_rows(b, h, "k"), st_e.pool_rows(b, h, "k"))
+            assert torch.equal(st_g.pool_rows(b, h, "v"), st_e.pool_rows(b, h, "v"))
+    if pool_block:
+        assert torch.equal(st_g.pool_table, st_e.pool_table)
+        assert torch.equal(st_g.free_top, st_e.free_top)
+        top = int(st_e.free_top.item())
+        assert torch.equal(st_g.free_ids[:top], st_e.free_ids[:top])
+        assert st_e.blocks_held() + top == st_e.free_ids.numel()
     assert torch.equal(tg.ccount, te.ccount)
     assert torch.equal(tg.ksum, te.ksum) and torch.equal(tg.vsum, te.vsum)
     # tokens kept flowing into the condensed tier over the replays
