@@ -254,13 +254,15 @@ def amortization(w, case, steps, horizons=(1, 2, 4, 8, 16, 32)):
     }
 
 
-def lifecycle(dev, reps=5, steady_steps=48):
+def lifecycle(dev, reps=5, steady_steps=48, pool_block=0):
     """The multi-step lifecycle (hardkv_step_inplace) of one layer at the
     Qwen3-32B attention shape: 64 sequences, 64 query / 8 KV heads, d = 128,
     12288-token prefill, window 512, chunk 64, p = 0.95, fresh N(0, 1) query,
     key and value every step.  Step 1 re-selects over the whole aged pool
     (restored from a copy before each timed repetition); later steps run on
-    the pool that the selections left."""
+    the pool that the selections left.  pool_block > 0: the pool under the
+    head-wise block manager (blocks of that many rows, as many blocks as the
+    per-head regions would hold)."""
     import torch
     from decode_kv_cache_head_amd import hardkv as H
     B, Hq, Hkv, d, T0, W, C, p = 64, 64, 8, 128, 12288, 512, 64, 0.95
@@ -270,24 +272,40 @@ def lifecycle(dev, reps=5, steady_steps=48):
     ws = H.alloc_workspace(desc, dev)
     out = torch.empty((B, Hq, d), device=dev)
     g = torch.Generator(device=dev).manual_seed(4242)
-    t = H.alloc_tiers(desc, dev)
+    k0 = torch.empty((B, Hkv, A, d), dtype=torch.bfloat16, device=dev)
+    v0 = torch.empty_like(k0)
     for i in range(0, B, 8):
-        t.k[i:i + 8, :, :A] = torch.randn((8, Hkv, A, d), generator=g, device=dev).to(torch.bfloat16)
-        t.v[i:i + 8, :, :A] = torch.randn((8, Hkv, A, d), generator=g, device=dev).to(torch.bfloat16)
-    t.pos[:, :, :A] = torch.arange(A, dtype=torch.int32, device=dev)
+        k0[i:i + 8] = torch.randn((8, Hkv, A, d), generator=g, device=dev).to(torch.bfloat16)
+        v0[i:i + 8] = torch.randn((8, Hkv, A, d), generator=g, device=dev).to(torch.bfloat16)
     ring_k = torch.randn((B, Hkv, W, d), generator=g, device=dev).to(torch.bfloat16)
     ring_v = torch.randn((B, Hkv, W, d), generator=g, device=dev).to(torch.bfloat16)
-    k0, v0 = t.k[:, :, :A].clone(), t.v[:, :, :A].clone()
     r0k, r0v = ring_k.clone(), ring_v.clone()
     seq = torch.full((B,), T0, dtype=torch.int32, device=dev)
-    st = H.State(ring_k, ring_v, t, seq)
+    if pool_block:
+        maxb = -(-desc.sparse_cap // pool_block)
+        st = H.paged_state(desc, k0, v0, ring_k, ring_v, seq, pool_block, B * Hkv * maxb)
+        saved = [x.clone() for x in (st.pool_table, st.free_ids, st.free_top)]
+        used = B * Hkv * (-(-A // pool_block))
+        pk0, pv0 = st.tiers.k[:used].clone(), st.tiers.v[:used].clone()
+    else:
+        t = H.alloc_tiers(desc, dev)
+        t.k[:, :, :A] = k0
+        t.v[:, :, :A] = v0
+        st = H.State(ring_k, ring_v, t, seq)
+    t = st.tiers
     qs = [torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(4)]
     kn = torch.randn((B, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
     vn = torch.randn((B, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
 
     def reset():
-        t.k[:, :, :A].copy_(k0)
-        t.v[:, :, :A].copy_(v0)
+        if pool_block:
+            t.k[:used].copy_(pk0)
+            t.v[:used].copy_(pv0)
+            for x, x0 in zip((st.pool_table, st.free_ids, st.free_top), saved):
+                x.copy_(x0)
+        else:
+            t.k[:, :, :A].copy_(k0)
+            t.v[:, :, :A].copy_(v0)
         t.pos[:, :, :A] = torch.arange(A, dtype=torch.int32, device=dev)
         t.count.fill_(A)
         t.ksum.zero_()
@@ -297,6 +315,11 @@ def lifecycle(dev, reps=5, steady_steps=48):
         ring_v.copy_(r0v)
         seq.fill_(T0)
 
+    def pool_mb():
+        rows = st.blocks_held() * pool_block if pool_block else B * Hkv * desc.sparse_cap
+        return round(rows * d * 2 * 2 / 2**20, 1)
+
+    mb0 = pool_mb()
     s1 = []
     for r in range(reps + 1):
         reset()
@@ -309,6 +332,7 @@ def lifecycle(dev, reps=5, steady_steps=48):
         if r:
             s1.append(e0.elapsed_time(e1))
     pool1 = int(t.count.float().median().item())
+    mb1 = pool_mb()
     for i in range(steady_steps - 8):
         H.step_inplace(desc, qs[i % 4], kn, vn, None, st, out, ws)
     torch.cuda.synchronize()
@@ -319,6 +343,8 @@ def lifecycle(dev, reps=5, steady_steps=48):
     e1.record()
     torch.cuda.synchronize()
     steady = e0.elapsed_time(e1) / 8
+    pool_steady = int(t.count.float().median().item())
+    mb_steady = pool_mb()
     # the same steady step captured once in a HIP graph and replayed
     qg = qs[0].clone()
     graph = torch.cuda.CUDAGraph()
@@ -335,14 +361,16 @@ def lifecycle(dev, reps=5, steady_steps=48):
     del graph
     step1 = sum(s1) / len(s1)
     res = {"shape": "qwen3-32b attention, B=64, T0=12288, W=512, C=64, p=0.95, one layer",
+           "pool_block": pool_block,
            "step1_ms": round(step1, 4), "step1_pool_median_after": pool1,
            "aged_pool_before_step1": A, "steady_ms": round(steady, 4),
            "steady_graph_replay_ms": round(steady_graph, 4),
            "steady_after_steps": steady_steps,
-           "steady_pool_median": int(t.count.float().median().item()),
+           "steady_pool_median": pool_steady,
+           "pool_kv_mb": {"before": mb0, "after_step1": mb1, "steady": mb_steady},
            "step1_tokens_per_s": round(B / (step1 * 1e-3), 1),
            "steady_tokens_per_s": round(B / (steady * 1e-3), 1)}
-    del t, k0, v0, ws
+    del t, st, k0, v0, ws
     torch.cuda.empty_cache()
     return res
 
@@ -529,6 +557,7 @@ def main():
         res["amortization"] = am
         print("[bench] lifecycle", file=sys.stderr, flush=True)
         res["lifecycle"] = lifecycle(dev)
+        res["lifecycle_block_manager"] = lifecycle(dev, pool_block=64)
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(case, w, args.cpu_seconds)

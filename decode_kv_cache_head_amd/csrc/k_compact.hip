@@ -564,6 +564,8 @@ void launch_compact_attn(const CompactArgs& a, hipStream_t st) {
 // sums of chunk pos / C in ascending position order, one thread per (tensor,
 // dimension); a chunk's old sums are loaded when its first evicted row is
 // met and stored back when the next chunk starts.
+constexpr int kInplaceTab = 2048;  // block-table entries a workgroup keeps in LDS
+
 template <typename T, int D>
 __global__ __launch_bounds__(512) void k_compact_inplace(CompactArgs a) {
   constexpr int NT = 512;
@@ -577,18 +579,25 @@ __global__ __launch_bounds__(512) void k_compact_inplace(CompactArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char sv[SUB * RB];
   __shared__ unsigned long long s_bal[NW];
   __shared__ int s_pos[SUB];
+  __shared__ int32_t s_tab[kInplaceTab];  // the head's block table row (block manager)
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, w = tid >> 6;
   const int n = a.cand.n(b, h);
   const int64_t bh = (int64_t)b * a.hkv + h;
   const uint8_t* mk = a.mask + bh * a.cap_stride;
   int32_t* pos = a.out_pos + bh * a.cap_stride;
   // pool row r (read and written): the head's region, or row r % bs of block
-  // table[r / bs] under the block manager (a missing block reads as block 0:
-  // the tables always cover [0, count))
+  // table[r / bs] under the block manager, with the head's table row copied
+  // into LDS when it is short (a missing block reads as block 0: the tables
+  // always cover [0, count))
   const int32_t* ptab = a.pg.table ? a.pg.table + bh * a.pg.maxb : nullptr;
+  const bool tab_lds = ptab && a.pg.maxb <= kInplaceTab;
+  if (tab_lds) {
+    for (int i = tid; i < a.pg.maxb; i += NT) s_tab[i] = ptab[i];
+    __syncthreads();
+  }
   auto prow = [&](char* base, int r) -> char* {
     if (!ptab) return base + (bh * a.cap_stride + r) * RB;
-    int blk = ptab[r >> a.pg.lbs];
+    int blk = tab_lds ? s_tab[r >> a.pg.lbs] : ptab[r >> a.pg.lbs];
     blk = blk < 0 || blk >= a.pg.nblocks ? 0 : blk;
     return base + (((int64_t)blk << a.pg.lbs) + (r & ((1 << a.pg.lbs) - 1))) * RB;
   };

@@ -148,14 +148,33 @@ __global__ __launch_bounds__(1024) void k_pool_shrink(PoolPaging pg, const int32
       int c = count[bh];
       c = c < 0 ? 0 : c;
       keep = (int)(((int64_t)c + (1 << pg.lbs) - 1) >> pg.lbs);
-      for (int i = keep; i < pg.maxb && tab[i] >= 0; ++i) ++nrel;
+      // held blocks past `keep`: eight independent loads per round
+      for (int i = keep; i < pg.maxb; i += 8) {
+        int e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = i + j < pg.maxb ? tab[i + j] : -1;
+        int run = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (run == j && e[j] >= 0) ++run;
+        nrel += run;
+        if (run < 8) break;
+      }
     }
     int total;
     const int rank = scan_1024(nrel, sh, total);
-    for (int j = 0; j < nrel; ++j) {
-      const int at = s_top + s_pushed + rank + j;
-      if (at < pg.nblocks) pg.free_ids[at] = tab[keep + j];
-      tab[keep + j] = -1;
+    // eight independent loads per round, then their stores
+    for (int j0 = 0; j0 < nrel; j0 += 8) {
+      int e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = j0 + j < nrel ? tab[keep + j0 + j] : -1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j0 + j >= nrel) break;
+        const int at = s_top + s_pushed + rank + j0 + j;
+        if (at < pg.nblocks) pg.free_ids[at] = e[j];
+        tab[keep + j0 + j] = -1;
+      }
     }
     __syncthreads();
     if (tid == 0) s_pushed += total;
