@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
       // rows past the sub-tile re-read its last row (in bounds, never stored)
       const int t = s0 + min(r, nr - 1);
       const char* src = tsr ? a.vrows.template row<P>(b, h, t) : a.krows.template row<P>(b, h, t);
-      buf[k] = *(const v4u*)(src + c * 16);
+      buf[k] = __builtin_nontemporal_load((const v4u*)(src + c * 16));
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -157,8 +157,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
     for (int k = 0; k < PER; ++k) {
       const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
       if (copy_rows && r < nr && s_sel[r])
-        *(v4u*)((tsr ? ov : ok) + (int64_t)s_rank[r] * RB + c * 16) =
-            *(const v4u*)((tsr ? sv : sk) + r * RB + c * 16);
+        __builtin_nontemporal_store(*(const v4u*)((tsr ? sv : sk) + r * RB + c * 16),
+                                    (v4u*)((tsr ? ov : ok) + (int64_t)s_rank[r] * RB + c * 16));
     }
     if (summer) {
       const T* src = (const T*)(tensor ? sv : sk);
@@ -324,8 +324,11 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = min(r0 + RGW * i, nrows - 1);
-      buf[i] = *(const v4u*)(a.krows.template row<P>(b, h, t0 + r) + c * 16);
-      buf[RPT + i] = *(const v4u*)(a.vrows.template row<P>(b, h, t0 + r) + c * 16);
+      // streamed once: non-temporal, so the pass does not flush what the
+      // following kernels read (chunk sums, dense rows) out of the caches
+      buf[i] = __builtin_nontemporal_load((const v4u*)(a.krows.template row<P>(b, h, t0 + r) + c * 16));
+      buf[RPT + i] =
+          __builtin_nontemporal_load((const v4u*)(a.vrows.template row<P>(b, h, t0 + r) + c * 16));
     }
   };
   auto process = [&](const v4u (&buf)[NB], int k, auto skip) {
@@ -376,8 +379,8 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
         const int rk = s_rank[r];
         if (rk >= 0) {
           if (copy_rows) {
-            *(v4u*)(ok + (int64_t)rk * RB + c * 16) = buf[i];
-            *(v4u*)(ov + (int64_t)rk * RB + c * 16) = buf[RPT + i];
+            __builtin_nontemporal_store(buf[i], (v4u*)(ok + (int64_t)rk * RB + c * 16));
+            __builtin_nontemporal_store(buf[RPT + i], (v4u*)(ov + (int64_t)rk * RB + c * 16));
           }
         } else if (WMERGE) {
           const float wt = mw.at(t0 + r);
