@@ -566,7 +566,8 @@ void launch_compact_attn(const CompactArgs& a, hipStream_t st) {
 // below the rows of sub-tile s + 1.  Evicted rows are added to the running
 // sums of chunk pos / C in ascending position order, one thread per (tensor,
 // dimension); a chunk's old sums are loaded when its first evicted row is
-// met and stored back when the next chunk starts.
+// met and stored back when the next chunk starts.  Pool rows are streamed
+// with non-temporal loads and stores.
 constexpr int kInplaceTab = 2048;  // block-table entries a workgroup keeps in LDS
 
 template <typename T, int D>
@@ -613,7 +614,8 @@ __global__ __launch_bounds__(512) void k_compact_inplace(CompactArgs a) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int idx = (k % (PER / 2)) * NT + tid, r = idx / CPR, c = idx % CPR;
-      buf[k] = *(const v4u*)(prow(k < PER / 2 ? a.out_k : a.out_v, s0 + min(r, nr - 1)) + c * 16);
+      buf[k] = __builtin_nontemporal_load(
+          (const v4u*)(prow(k < PER / 2 ? a.out_k : a.out_v, s0 + min(r, nr - 1)) + c * 16));
     }
     if (tid < SUB) {
       sel = tid < nr && mk[s0 + tid] != 0;
@@ -667,8 +669,8 @@ __global__ __launch_bounds__(512) void k_compact_inplace(CompactArgs a) {
       if (r < nr && kept(r)) {
         const int rk = rank(r);
         if (rk != s0 + r)
-          *(v4u*)(prow(k < PER / 2 ? a.out_k : a.out_v, rk) + c * 16) =
-              *(const v4u*)((k < PER / 2 ? sk : sv) + r * RB + c * 16);
+          __builtin_nontemporal_store(*(const v4u*)((k < PER / 2 ? sk : sv) + r * RB + c * 16),
+                                      (v4u*)(prow(k < PER / 2 ? a.out_k : a.out_v, rk) + c * 16));
       }
     }
     if (tid < nr && kept(tid)) pos[rank(tid)] = s_pos[tid];
