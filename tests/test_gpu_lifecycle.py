@@ -29,11 +29,14 @@ class Run:
     """Seeded lifecycle inputs and the GPU state for one layer."""
 
     def __init__(self, dev, seed, B, Hq, Hkv, d, T0, W, C, p, steps, dtype=torch.bfloat16,
-                 pool_block=0, pool_blocks=None):
+                 pool_block=0, pool_blocks=None, metric=None):
         g = torch.Generator(device=dev).manual_seed(seed)
         self.B, self.Hq, self.Hkv, self.d, self.T0, self.W, self.C, self.p = B, Hq, Hkv, d, T0, W, C, p
         self.G = Hq // Hkv
         self.dt = dtype
+        self.metrics = tuple(metric) if metric else (O.METRIC_QK,) * Hkv
+        self.metric = (torch.tensor(self.metrics, dtype=torch.int8, device=dev)
+                       if metric else None)
         Tmax = T0 + steps
         self.K = torch.randn((B, Hkv, T0, d), generator=g, device=dev).to(dtype)
         self.V = torch.randn((B, Hkv, T0, d), generator=g, device=dev).to(dtype)
@@ -70,7 +73,7 @@ class Run:
         return O.init_state(K, V, self.T0, self.W, self.C, self.desc.chunk_cap)
 
     def gpu_step(self, s):
-        H.step_inplace(self.desc, self.q[s], self.knew[s], self.vnew[s], None, self.state,
+        H.step_inplace(self.desc, self.q[s], self.knew[s], self.vnew[s], self.metric, self.state,
                        self.out, self.ws)
         torch.cuda.synchronize()
 
@@ -121,7 +124,7 @@ def check_step(run, states, s, rep):
         q = run.q[s, b, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
         kn = run.knew[s, b, h].float().cpu().numpy()
         vn = run.vnew[s, b, h].float().cpu().numpy()
-        out_ref, info = O.lifecycle_step(st, q, kn, vn, run.p, O.METRIC_QK)
+        out_ref, info = O.lifecycle_step(st, q, kn, vn, run.p, run.metrics[h])
         n = int(t.count[b, h])
         pos = t.pos[b, h, :n].cpu().numpy().astype(np.int64)
         diff = np.setxor1d(pos, st.pool_pos)
@@ -172,6 +175,11 @@ def check_step(run, states, s, rep):
     dict(B=1, Hq=4, Hkv=4, d=128, T0=300, W=64, C=1, p=0.5, steps=6, dtype=torch.float32,
          pool_block=32),
     dict(B=2, Hq=8, Hkv=2, d=128, T0=1400, W=64, C=300, p=0.9, steps=5, pool_block=128),
+    # key-norm heads beside QK heads, calibrated onto the logit spread
+    dict(B=2, Hq=16, Hkv=4, d=128, T0=1200, W=128, C=64, p=0.9, steps=8,
+         metric=(O.METRIC_QK, O.METRIC_L2, O.METRIC_L2, O.METRIC_QK)),
+    dict(B=3, Hq=8, Hkv=2, d=64, T0=600, W=64, C=16, p=0.85, steps=8, pool_block=32,
+         metric=(O.METRIC_L2, O.METRIC_QK)),
 ])
 def test_lifecycle_matches_oracle(gpu, cfg):
     steps = cfg.pop("steps")
