@@ -18,6 +18,11 @@
 //
 // Condensed entries hold float32 sums and a count n: their logit is
 // q.(ksum / n) / sqrt(d) + ln n and their value vsum / n.
+//
+// bf16 rows with d = 128 and G >= 4 take the matrix-core path (wave_attn_mx):
+// scores and the weighted value sum are 16x16x32 bf16 MFMA products with
+// float32 accumulation; the weights enter the second product as a bf16
+// high part plus a bf16 remainder, so each weight carries 16 significant bits.
 #include "internal.h"
 
 namespace hk {
@@ -173,32 +178,155 @@ __device__ inline void wave_attn(const QT* __restrict__ qg, const Rows& kr, cons
   }
 }
 
-template <typename E, int D, int G, typename QT, bool CHUNK, bool P, bool IDX = false>
-__device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr, const Rows& vr,
-                                 int b, int h, int r0, int nrows, const int32_t* cc, float* s_m,
-                                 float* s_l, float* s_o, float* part_out,
-                                 const int32_t* idx = nullptr, int idx_max = 0,
-                                 int gap_at = 0, int gap_len = 0) {
-  using L = Lay<E, D>;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int wn = nrows - w * 64;
-  wn = wn < 0 ? 0 : (wn > 64 ? 64 : wn);
-  float m[G], l[G], o[G][L::EPL];
-  wave_attn<E, D, G, QT, CHUNK, P, IDX>(qg, kr, vr, b, h, r0 + w * 64, wn, cc, idx, idx_max,
-                                        gap_at, gap_len, (float)a.scale, m, l, o);
-  if (lane < L::LPR) {
+// ------------------------------------------------ matrix-core row tiles --
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// D(16x16) += A(16x32) B(32x16): lane l holds A[l % 16][8 (l / 16) + j] and
+// B[8 (l / 16) + j][l % 16] (j = 0..7, bf16) and D[4 (l / 16) + i][l % 16]
+// (i = 0..3, float32).
+__device__ __forceinline__ f32x4_t mfma16(const v4u& a, const v4u& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Word j of the bf16 pairs (x.half, y.half): the same element of two rows.
+template <int HI>
+__device__ __forceinline__ uint32_t pair_of(uint32_t x, uint32_t y) {
+  return HI ? __builtin_amdgcn_perm(y, x, 0x07060302u) : __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t word_of(const v4u& v) {
+  return B == 0 ? v.x : (B == 1 ? v.y : (B == 2 ? v.z : v.w));
+}
+
+// Column blk of the 8x8 bf16 block held as 8 rows of 8: 8 values (rows 0..7)
+// packed in pairs, the A operand of the value product.
+template <int BLK>
+__device__ __forceinline__ v4u column_of(const v4u (&r)[8]) {
+  v4u c;
+  c.x = pair_of<BLK & 1>(word_of<BLK / 2>(r[0]), word_of<BLK / 2>(r[1]));
+  c.y = pair_of<BLK & 1>(word_of<BLK / 2>(r[2]), word_of<BLK / 2>(r[3]));
+  c.z = pair_of<BLK & 1>(word_of<BLK / 2>(r[4]), word_of<BLK / 2>(r[5]));
+  c.w = pair_of<BLK & 1>(word_of<BLK / 2>(r[6]), word_of<BLK / 2>(r[7]));
+  return c;
+}
+
+template <int BLK>
+__device__ __forceinline__ void pv_block(const v4u (&vb)[8], const v4u& ph, const v4u& pl,
+                                         f32x4_t (&acc)[8]) {
+  const v4u va = column_of<BLK>(vb);
+  acc[BLK] = mfma16(va, ph, acc[BLK]);
+  acc[BLK] = mfma16(va, pl, acc[BLK]);
+}
+
+// One wave, up to 64 bf16 rows (d = 128) starting at entry r0, G <= 16 query
+// heads, in steps of 32 entries.  Lane l = 16 g + i (i = l % 16, g = l / 16).
+//   scores  S^T = K Q^T: two 16-row products whose row r is entry
+//           8 (r / 4) + r % 4 (+4 for the second), so lane l receives the
+//           scores of entries 8 g .. 8 g + 7 for query head i; the d order of
+//           the contraction is d = 32 s + 8 g + j in both operands;
+//   values  O^T = V^T P^T with d permuted as d = 8 r + blk for row r of
+//           product blk: lane l loads 16 bytes (d = 8 i .. 8 i + 7) of each
+//           of its 8 entries and transposes them in registers.
+// On return lane l holds, for query head i, the running max m (common to the
+// 4 lanes of i), its own part of the sum l, and acc[blk][c] = the numerator
+// at d = 8 (4 g + c) + blk.  Rows are addressed as in wave_attn.
+template <int G, bool P, bool IDX>
+__device__ inline void wave_attn_mx(const bf16_t* __restrict__ qg, const Rows& kr,
+                                    const Rows& vr, int b, int h, int r0, int wn,
+                                    const int32_t* __restrict__ idx, int idx_max, int gap_at,
+                                    int gap_len, float scale, float& m_run, float& l_run,
+                                    f32x4_t (&acc)[8]) {
+  constexpr int D = 128;
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+  v4u qb[4];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+  for (int s = 0; s < 4; ++s)
+    qb[s] = i < G ? *(const v4u*)(qg + i * D + 32 * s + 8 * g) : v4u{0u, 0u, 0u, 0u};
+  m_run = -INFINITY;
+  l_run = 0.f;
 #pragma unroll
-      for (int e = 0; e < L::EPL; ++e) s_o[(w * G + g) * D + lane * L::EPL + e] = o[g][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      s_m[w * G + g] = m[g];
-      s_l[w * G + g] = l[g];
+  for (int k = 0; k < 8; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto row_of = [&](int r) -> int {
+    r = r < wn ? r : wn - 1;  // in bounds; weight 0 below
+    if (IDX) {
+      const int t = idx[r0 + r];
+      return t < 0 ? 0 : (t > idx_max ? idx_max : t);
     }
+    const int t = r0 + r;
+    return t >= gap_at ? t + gap_len : t;
+  };
+  for (int base = 0; base < wn; base += 32) {
+    const int ek = base + 8 * (i >> 2) + (i & 3);
+    const char* k0 = kr.template row<P>(b, h, row_of(ek)) + 16 * g;
+    const char* k1 = kr.template row<P>(b, h, row_of(ek + 4)) + 16 * g;
+    v4u kb0[4], kb1[4], vb[8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kb0[s] = *(const v4u*)(k0 + 64 * s);
+      kb1[s] = *(const v4u*)(k1 + 64 * s);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      vb[j] = *(const v4u*)(vr.template row<P>(b, h, row_of(base + 8 * g + j)) + 16 * i);
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      s0 = mfma16(kb0[s], qb[s], s0);
+      s1 = mfma16(kb1[s], qb[s], s1);
+    }
+    float sc[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      sc[c] = base + 8 * g + c < wn ? s0[c] * scale : -INFINITY;
+      sc[4 + c] = base + 8 * g + 4 + c < wn ? s1[c] * scale : -INFINITY;
+      mx = fmaxf(mx, fmaxf(sc[c], sc[4 + c]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m_run, mx);
+    const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - mn);
+    l_run *= alpha;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] *= alpha;
+    m_run = mn;
+    bf16x8_t hi, lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = sc[j] == -INFINITY ? 0.f : __expf(sc[j] - mn);
+      l_run += p;
+      hi[j] = (__bf16)p;
+      lo[j] = (__bf16)(p - (float)hi[j]);
+    }
+    const v4u ph = __builtin_bit_cast(v4u, hi), pl = __builtin_bit_cast(v4u, lo);
+    pv_block<0>(vb, ph, pl, acc);
+    pv_block<1>(vb, ph, pl, acc);
+    pv_block<2>(vb, ph, pl, acc);
+    pv_block<3>(vb, ph, pl, acc);
+    pv_block<4>(vb, ph, pl, acc);
+    pv_block<5>(vb, ph, pl, acc);
+    pv_block<6>(vb, ph, pl, acc);
+    pv_block<7>(vb, ph, pl, acc);
   }
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+}
+
+// LDS row stride of the per-wave numerators (padded against bank conflicts
+// of the matrix-core path's stores, where lanes of one store hold different
+// query heads).
+template <int D>
+constexpr int kSO = D + 4;
+
+// The four waves' (m, l, o) in LDS -> one partial (max, sum, numerator) per
+// query head of the tile.
+template <int G, int D>
+__device__ inline void combine_waves(const float* s_m, const float* s_l, const float* s_o,
+                                     float* part_out) {
   __syncthreads();
   for (int i = threadIdx.x; i < G * D; i += 256) {
     const int g = i / D, e = i % D;
@@ -212,7 +340,7 @@ __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr
         const float mv = s_m[v * G + g];
         if (mv != -INFINITY) {
           const float f = __expf(mv - M);
-          O = fmaf(f, s_o[(v * G + g) * D + e], O);
+          O = fmaf(f, s_o[(v * G + g) * kSO<D> + e], O);
           S = fmaf(f, s_l[v * G + g], S);
         }
       }
@@ -226,25 +354,85 @@ __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr
   }
 }
 
+// bf16 rows, d = 128, G >= 4: the matrix-core path.
+template <typename E, int D, int G, bool CHUNK>
+constexpr bool kUseMx = !CHUNK && D == 128 && G >= 4 && sizeof(E) == 2;
+
+// One tile of up to 256 entries: wave w takes entries [64 w, 64 w + 64).
+template <typename E, int D, int G, typename QT, bool CHUNK, bool P, bool IDX = false>
+__device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr, const Rows& vr,
+                                 int b, int h, int r0, int nrows, const int32_t* cc, float* s_m,
+                                 float* s_l, float* s_o, float* part_out,
+                                 const int32_t* idx = nullptr, int idx_max = 0,
+                                 int gap_at = 0, int gap_len = 0) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int wn = nrows - w * 64;
+  wn = wn < 0 ? 0 : (wn > 64 ? 64 : wn);
+  if constexpr (kUseMx<E, D, G, CHUNK>) {
+    float m, l;
+    f32x4_t acc[8];
+    wave_attn_mx<G, P, IDX>((const bf16_t*)qg, kr, vr, b, h, r0 + w * 64, wn, idx, idx_max,
+                            gap_at, gap_len, (float)a.scale, m, l, acc);
+    const int i = lane & 15, g = lane >> 4;
+    if (i < G) {
+      float* so = s_o + (w * G + i) * kSO<D>;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d0 = 8 * (4 * g + c);
+        *(float4*)(so + d0) = float4{acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
+        *(float4*)(so + d0 + 4) = float4{acc[4][c], acc[5][c], acc[6][c], acc[7][c]};
+      }
+      if (g == 0) {
+        s_m[w * G + i] = wn > 0 ? m : -INFINITY;
+        s_l[w * G + i] = l;
+      }
+    }
+  } else {
+    using L = Lay<E, D>;
+    float m[G], l[G], o[G][L::EPL];
+    wave_attn<E, D, G, QT, CHUNK, P, IDX>(qg, kr, vr, b, h, r0 + w * 64, wn, cc, idx, idx_max,
+                                          gap_at, gap_len, (float)a.scale, m, l, o);
+    if (lane < L::LPR) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < L::EPL; ++e) s_o[(w * G + g) * kSO<D> + lane * L::EPL + e] = o[g][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        s_m[w * G + g] = m[g];
+        s_l[w * G + g] = l[g];
+      }
+    }
+  }
+  combine_waves<G, D>(s_m, s_l, s_o, part_out);
+}
+
 // PS: the sparse tier is the lifecycle pool under the block manager (rows
 // through per-head block tables; the dense tier is then the ring, P false).
-template <typename T, int D, int G, bool P, bool PS>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+// PART 0: every tile of the head; 1: the dense and sparse tiles; 2: the
+// condensed tiles (grid x counts from the first condensed tile).  Launches
+// whose row tiles take the matrix-core path split the two kinds, so the
+// float32 chunk tiles do not set the register budget of the row tiles.
+template <typename T, int D, int G, bool P, bool PS, int PART>
+__device__ inline void attn_tiles(const AttnArgs& a) {
   __shared__ float s_m[4 * G], s_l[4 * G];
-  __shared__ float s_o[4 * G * D];
-  const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  __shared__ __align__(16) float s_o[4 * G * kSO<D>];
+  const int h = blockIdx.y, b = blockIdx.z;
   const TileCounts tc = tile_counts(a, b, h);
-  if (x >= tc.ntd + tc.nts + tc.ntc) return;
+  const int x = PART == 2 ? tc.ntd + tc.nts + (int)blockIdx.x : (int)blockIdx.x;
+  if (x >= tc.ntd + tc.nts + (PART == 1 ? 0 : tc.ntc)) return;
   const int64_t bh = (int64_t)b * a.hkv + h;
   const T* qg = (const T*)a.q + ((int64_t)b * a.hq + (int64_t)h * G) * D;
   float* part_out = a.part + (bh * a.max_tiles + tc.first + x) * G * (D + 2);
-  if (x < tc.ntd) {
+  if (PART != 2 && x < tc.ntd) {
     // dense entries: sinks [0, S), then the window from S + A (ring: slots)
     const int r0 = x * kAttnTile;
     tile_attn<T, D, G, T, false, P>(a, qg, a.dk, a.dv, b, h, r0, min(kAttnTile, tc.nd - r0),
                                     nullptr, s_m, s_l, s_o, part_out, nullptr, 0, tc.gap_at,
                                     tc.gap_len);
-  } else if (x < tc.ntd + tc.nts) {
+  } else if (PART != 2 && x < tc.ntd + tc.nts) {
     const int r0 = (x - tc.ntd) * kAttnTile;
     if (a.mode && a.mode[bh] == HARDKV_MODE_SPARSE) {
       // sparse loading: the kept rows stay in the cache, found through pos
@@ -268,13 +456,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
                                           min(kAttnTile, tc.ns - r0), nullptr, s_m, s_l, s_o,
                                           part_out);
     }
-  } else {
+  } else if constexpr (PART != 1) {
     const int r0 = (x - tc.ntd - tc.nts) * kAttnTile;
     Rows ck{(const char*)a.ksum, nullptr, a.chunk_cap, a.hkv, 0, 0, D * 4};
     Rows cv{(const char*)a.vsum, nullptr, a.chunk_cap, a.hkv, 0, 0, D * 4};
     tile_attn<float, D, G, T, true, false>(a, qg, ck, cv, b, h, r0, min(kAttnTile, tc.nc - r0),
-                                    a.ccount + bh * a.chunk_cap, s_m, s_l, s_o, part_out);
+                                           a.ccount + bh * a.chunk_cap, s_m, s_l, s_o, part_out);
   }
+}
+
+template <typename T, int D, int G, bool P, bool PS, int PART>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+  attn_tiles<T, D, G, P, PS, PART>(a);
 }
 
 // One wave per (b, query head): joins the partials of every tile.
@@ -327,17 +520,24 @@ int attn_max_tiles(int W, int sparse_cap, int chunk_cap) {
 
 template <typename T, int D, int G, bool P>
 static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
-  const int gx = a.fused_tt > 0
-                     ? ceil_div(a.W + a.sinks, kAttnTile) + ceil_div(a.chunk_cap, kAttnTile)
-                     : a.max_tiles;
-  if (gx > 0) {
+  constexpr bool split = kUseMx<T, D, G, false> && G >= 8;
+  const int gd = ceil_div(a.W + a.sinks, kAttnTile), gc = ceil_div(a.chunk_cap, kAttnTile);
+  const int gx = a.fused_tt > 0 ? gd + gc : a.max_tiles;
+  const int grows = split ? gx - gc : gx;
+  bool pool_paged = false;
+  if constexpr (!P) pool_paged = a.sk.table != nullptr;
+  if (grows > 0) {
     observe("k_attn", st);
-    bool pool_paged = false;
-    if constexpr (!P) pool_paged = a.sk.table != nullptr;
+    const dim3 grid(grows, a.hkv, a.B);
     if (pool_paged)
-      hipLaunchKernelGGL((k_attn<T, D, G, false, true>), dim3(gx, a.hkv, a.B), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_attn<T, D, G, false, true, split ? 1 : 0>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((k_attn<T, D, G, P, false>), dim3(gx, a.hkv, a.B), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_attn<T, D, G, P, false, split ? 1 : 0>), grid, dim3(256), 0, st, a);
+  }
+  if (split && gc > 0) {
+    observe("k_attn_chunks", st);
+    hipLaunchKernelGGL((k_attn<T, D, G, false, false, 2>), dim3(gc, a.hkv, a.B), dim3(256), 0, st,
+                       a);
   }
   observe("k_attn_merge", st);
   hipLaunchKernelGGL((k_attn_merge<T, D, G>), dim3(ceil_div((int64_t)a.B * a.hq, 4)), dim3(256),

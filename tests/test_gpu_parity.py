@@ -127,6 +127,48 @@ def test_p_one_is_full_attention(gpu):
             assert err <= 2e-3, err
 
 
+ROW_TILE_CASES = [
+    dict(Hq=16, Hkv=2),                                   # G = 8
+    dict(Hq=8, Hkv=2, block_size=16),                     # G = 4, paged rows
+    dict(Hq=16, Hkv=2, peaked_heads=(0,), temp_range=(0.3, 0.5)),
+    dict(Hq=8, Hkv=2, peaked_heads=(1,), block_size=16),
+]
+
+
+@pytest.mark.parametrize("i", range(len(ROW_TILE_CASES)))
+def test_row_tiles_ragged_and_peaked_full_attention(gpu, i):
+    """bf16 rows with d = 128 and G >= 4 (the matrix-core attention): tier
+    lengths that end at every offset of a 32-entry step, a 64-entry wave and a
+    256-entry tile, flat and peaked heads (Zipf-planted keys with logits up to
+    24 above the rest).  p = 1 keeps every token, so the output is full
+    attention (float64 SDPA).  Bound 1e-4 of max|o|: each weight enters the
+    value product as a bf16 pair whose sum is within 2^-18 of it, products of
+    bf16 values are exact in float32 and the float32 sums run over at most
+    1300 terms."""
+    W = 64
+    T = (40,) + tuple(W + n for n in (1, 31, 32, 33, 63, 65, 255, 257, 1000, 1240))
+    w = small(f"rowtiles{i}", B=len(T), T=T, W=W, p=1.0, **ROW_TILE_CASES[i])
+    say("row tiles", w)
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_step(case, desc)
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            G = w.G
+            q = case.q[b, h * G:(h + 1) * G].double().cpu()
+            K = S.head_rows(case, b, h, "k").double().cpu()
+            V = S.head_rows(case, b, h, "v").double().cpu()
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[None, :, None], K[None, None].expand(1, G, -1, -1).contiguous(),
+                V[None, None].expand(1, G, -1, -1).contiguous())[0, :, 0]
+            o = g["out"][b, h * G:(h + 1) * G].double().cpu()
+            err = ((o - ref).abs().amax(1) / ref.abs().amax(1)).max().item()
+            worst = max(worst, err)
+            assert err <= 1e-4, (b, h, err)
+    say("worst relative error", worst)
+
+
 def test_edge_cases(gpu):
     # every sequence shorter than the window, a single-token context, and a
     # context exactly one token past the window
