@@ -210,13 +210,23 @@ __device__ inline uint64_t ceil_mul(float p, uint64_t Z) {
   return (uint64_t)((prod + ((one << sh) - 1)) >> sh);
 }
 
+// Histogram slot of bin b when NB bins are searched: one pad slot after
+// every NB / 64 bins, so the 64 lanes of find_bin, each summing its own run
+// of consecutive bins, read different LDS banks.
+template <int NB>
+__device__ __forceinline__ int hslot(uint32_t b) {
+  return (int)(b + b / (NB / 64));
+}
+constexpr int kHistSlots = 2048 + 64;
+
 struct SelShared {
-  unsigned long long hist[2048];
+  unsigned long long hist[kHistSlots];
   unsigned long long target;
   unsigned long long above;
   uint32_t bin;
   int wc[kSelWaves];
   int red[kSelWaves];
+  int tpre[16 * kSelWaves];  // k_calsel: ties before (slot, wave), position order
 };
 
 // Run by wave 0: the largest bin whose suffix mass (bins at or above it)
@@ -228,7 +238,7 @@ __device__ inline void find_bin(SelShared& S, bool from_total, float p) {
   constexpr int PER = NB / 64;
   unsigned long long s = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) s += S.hist[lane * PER + i];
+  for (int i = 0; i < PER; ++i) s += S.hist[lane * (PER + 1) + i];
   unsigned long long suf = s;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -244,18 +254,23 @@ __device__ inline void find_bin(SelShared& S, bool from_total, float p) {
     target = S.target;
   }
   const unsigned long long ok = __ballot(suf >= target);
-  const int L = __popcll(ok) - 1;
-  if (lane == L) {
-    unsigned long long run = suf - s;
-    for (int i = PER - 1; i >= 0; --i) {
-      const unsigned long long hv = S.hist[lane * PER + i];
-      if (run + hv >= target) {
-        S.bin = lane * PER + i;
-        S.above = run;
-        break;
-      }
-      run += hv;
-    }
+  int L = __popcll(ok) - 1;  // suf falls with the lane: lanes 0..L reach the target
+  L = L < 0 ? 0 : L;
+  // inside lane L's PER bins: suffix sums over PER lanes, the same rule
+  const unsigned long long base = __shfl(suf - s, L, 64);  // mass above the chunk
+  const unsigned long long hv = lane < PER ? S.hist[L * (PER + 1) + lane] : 0ull;
+  unsigned long long suf2 = hv;
+#pragma unroll
+  for (int o = 1; o < PER; o <<= 1) {
+    const unsigned long long v = __shfl_down(suf2, o, 64);
+    if (lane + o < PER) suf2 += v;
+  }
+  const unsigned long long ok2 = __ballot(lane < PER && base + suf2 >= target);
+  int J = __popcll(ok2) - 1;
+  J = J < 0 ? 0 : J;
+  if (lane == J) {
+    S.bin = L * PER + J;
+    S.above = base + suf2 - hv;
   }
   if (from_total && lane == 0) S.target = target;
 }
@@ -300,12 +315,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   auto cv = [&](int t) -> float { return is_l2 ? cval(x[t], shift, scale) : x[t]; };
 
   // pass 1: top 11 bits of the key
-  for (int i = tid; i < 2048; i += kSelThreads) S.hist[i] = 0;
+  for (int i = tid; i < kHistSlots; i += kSelThreads) S.hist[i] = 0;
   __syncthreads();
   for (int t = tid; t < n; t += kSelThreads) {
     const float c = cv(t);
     const uint64_t w = wfix(c, m);
-    if (w) atomicAdd(&S.hist[okey(c) >> 21], (unsigned long long)w);
+    if (w) atomicAdd(&S.hist[hslot<2048>(okey(c) >> 21)], (unsigned long long)w);
   }
   __syncthreads();
   if (tid < 64) find_bin<2048>(S, true, top_p);
@@ -316,13 +331,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   __syncthreads();
 
   // pass 2: next 11 bits inside bin b1
-  for (int i = tid; i < 2048; i += kSelThreads) S.hist[i] = 0;
+  for (int i = tid; i < kHistSlots; i += kSelThreads) S.hist[i] = 0;
   if (tid == 0) S.target = target - above;
   __syncthreads();
   for (int t = tid; t < n; t += kSelThreads) {
     const float c = cv(t);
     const uint32_t k = okey(c);
-    if ((k >> 21) == b1) atomicAdd(&S.hist[(k >> 10) & 2047u], (unsigned long long)wfix(c, m));
+    if ((k >> 21) == b1)
+      atomicAdd(&S.hist[hslot<2048>((k >> 10) & 2047u)], (unsigned long long)wfix(c, m));
   }
   __syncthreads();
   if (tid < 64) find_bin<2048>(S, false, top_p);
@@ -333,14 +349,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   __syncthreads();
 
   // pass 3: last 10 bits inside (b1, b2)
-  for (int i = tid; i < 1024; i += kSelThreads) S.hist[i] = 0;
+  for (int i = tid; i < kHistSlots; i += kSelThreads) S.hist[i] = 0;
   if (tid == 0) S.target = t2 - S.above;
   __syncthreads();
   const uint32_t pre = (b1 << 11) | b2;
   for (int t = tid; t < n; t += kSelThreads) {
     const float c = cv(t);
     const uint32_t k = okey(c);
-    if ((k >> 10) == pre) atomicAdd(&S.hist[k & 1023u], (unsigned long long)wfix(c, m));
+    if ((k >> 10) == pre) atomicAdd(&S.hist[hslot<1024>(k & 1023u)], (unsigned long long)wfix(c, m));
   }
   __syncthreads();
   if (tid < 64) find_bin<1024>(S, false, top_p);
@@ -405,6 +421,8 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
                                                         uint8_t* __restrict__ mask,
                                                         CountOut co, int calib) {
   __shared__ SelShared S;
+  // fixed-point weight of token tid + 1024 i at [i][tid], from pass 1 on
+  __shared__ unsigned long long s_w[NPT * kSelThreads];
   __shared__ double shd[2 * kSelWaves];
   __shared__ float shf[kSelWaves];
   const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
@@ -496,17 +514,19 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   const double m = (double)block_max_f32<kSelWaves>(mloc, shf);
 
   // pass 1: weights, Z, and the histogram of the top 11 key bits
-  for (int i = tid; i < 2048; i += kSelThreads) S.hist[i] = 0;
+  for (int i = tid; i < kHistSlots; i += kSelThreads) S.hist[i] = 0;
   __syncthreads();
   double Z = 0.0;
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
+    uint64_t w = 0;
     if (tid + kSelThreads * i < n) {
       const double wd = exp((double)c[i] - m);
       Z += wd;
-      const uint64_t w = (uint64_t)__double2ull_rn(wd * 140737488355328.0);
-      if (w) atomicAdd(&S.hist[okey(c[i]) >> 21], (unsigned long long)w);
+      w = (uint64_t)__double2ull_rn(wd * 140737488355328.0);  // = wfix(c, m)
+      if (w) atomicAdd(&S.hist[hslot<2048>(okey(c[i]) >> 21)], (unsigned long long)w);
     }
+    s_w[i * kSelThreads + tid] = w;
   }
   Z = block_sum_f64<kSelWaves>(Z, shd);  // contains the barrier before find_bin
   if (tid == 0) {
@@ -530,14 +550,14 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   unsigned long long above = S.above;
   __syncthreads();
 
-  for (int i = tid; i < 2048; i += kSelThreads) S.hist[i] = 0;
+  for (int i = tid; i < kHistSlots; i += kSelThreads) S.hist[i] = 0;
   if (tid == 0) S.target = target - above;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
     const uint32_t k = okey(c[i]);
     if (tid + kSelThreads * i < n && (k >> 21) == b1)
-      atomicAdd(&S.hist[(k >> 10) & 2047u], (unsigned long long)wfix(c[i], m));
+      atomicAdd(&S.hist[hslot<2048>((k >> 10) & 2047u)], s_w[i * kSelThreads + tid]);
   }
   __syncthreads();
   if (tid < 64) find_bin<2048>(S, false, top_p);
@@ -547,7 +567,7 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   const unsigned long long t2 = S.target;
   __syncthreads();
 
-  for (int i = tid; i < 1024; i += kSelThreads) S.hist[i] = 0;
+  for (int i = tid; i < kHistSlots; i += kSelThreads) S.hist[i] = 0;
   if (tid == 0) S.target = t2 - S.above;
   __syncthreads();
   const uint32_t pre = (b1 << 11) | b2;
@@ -555,7 +575,7 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   for (int i = 0; i < NPT; ++i) {
     const uint32_t k = okey(c[i]);
     if (tid + kSelThreads * i < n && (k >> 10) == pre)
-      atomicAdd(&S.hist[k & 1023u], (unsigned long long)wfix(c[i], m));
+      atomicAdd(&S.hist[hslot<1024>(k & 1023u)], s_w[i * kSelThreads + tid]);
   }
   __syncthreads();
   if (tid < 64) find_bin<1024>(S, false, top_p);
@@ -565,30 +585,65 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   const unsigned long long wstar = wfix(okey_inv(kstar), m);
   const unsigned long long need = target - above;
   const unsigned long long r = (need + wstar - 1) / wstar;
+  // every token tied at K* has weight wstar, so the bin holds mass / wstar of
+  // them; when r reaches that count all are taken and no ranking is needed
+  const unsigned long long ntie = S.hist[hslot<1024>(S.bin)] / wstar;
 
+  // Tokens tied at K* are taken in position order t = tid + 1024 i, i.e.
+  // ordered by (slot i, wave, lane): count the ties of every (slot, wave),
+  // scan them once (wave 0), then each tie's rank is its entry plus the tied
+  // lanes below it in its wave's ballot.
   const int wv = tid >> 6, ln = tid & 63;
-  unsigned long long carried = 0;
+  const bool rank_ties = r < ntie;  // uniform
+  uint32_t tmask = 0;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i)
+    if (tid + kSelThreads * i < n && okey(c[i]) == kstar) tmask |= 1u << i;
+  if (rank_ties) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const unsigned long long bal = __ballot((tmask >> i) & 1u);
+      if (ln == 0) S.tpre[i * kSelWaves + wv] = __popcll(bal);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      constexpr int PER = NPT * kSelWaves / 64;  // entries per lane, in order
+      int e[PER], sum = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        e[j] = S.tpre[tid * PER + j];
+        sum += e[j];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (tid >= o) incl += u;
+      }
+      int run = incl - sum;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        S.tpre[tid * PER + j] = run;
+        run += e[j];
+      }
+    }
+    __syncthreads();
+  }
   int nsel = 0;
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
     if (kSelThreads * i >= n) break;  // uniform
     const int t = tid + kSelThreads * i;
     const bool valid = t < n;
-    const uint32_t k = valid ? okey(c[i]) : 0u;
-    const bool tie = valid && k == kstar;
-    const int ntie = __syncthreads_count(tie);
-    unsigned long long rank = 0;
-    if (ntie) {
+    const bool tie = (tmask >> i) & 1u;
+    bool take_tie = tie;
+    if (rank_ties) {
       const unsigned long long bal = __ballot(tie);
-      if (ln == 0) S.wc[wv] = __popcll(bal);
-      __syncthreads();
-      int off = 0;
-      for (int j = 0; j < wv; ++j) off += S.wc[j];
-      __syncthreads();
-      rank = carried + off + __popcll(bal & ((1ull << ln) - 1ull));
-      carried += ntie;
+      const unsigned long long rank = (unsigned long long)S.tpre[i * kSelWaves + wv] +
+                                      __popcll(bal & ((1ull << ln) - 1ull));
+      take_tie = tie && rank < r;
     }
-    const bool sel = valid && (k > kstar || (tie && rank < r));
+    const bool sel = valid && (okey(c[i]) > kstar || take_tie);
     if (valid) mk[t] = sel ? 1 : 0;
     nsel += sel;
   }
