@@ -316,6 +316,142 @@ __device__ inline void wave_attn_mx(const bf16_t* __restrict__ qg, const Rows& k
   l_run += __shfl_xor(l_run, 32, 64);
 }
 
+// x ~= hi + lo with hi = bf16(x) and lo = bf16(x - hi): 16 significant bits
+// of each float32, packed as the pairs (x0, x1) an MFMA operand word holds.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
+  hi = __builtin_bit_cast(uint32_t, bf16x2_t{h0, h1});
+  lo = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)(x0 - (float)h0), (__bf16)(x1 - (float)h1)});
+}
+
+__device__ __forceinline__ float comp(const v4u& v, int c) {
+  return __uint_as_float(c == 0 ? v.x : (c == 1 ? v.y : (c == 2 ? v.z : v.w)));
+}
+
+// Value product of one block for float32 rows held as vf[j][0..1] (8 floats
+// of d = 8 i .. 8 i + 7 of entry j): A = V^T split into two bf16 terms,
+// B = the weights' two terms; the lo x lo product (below 2^-18) is dropped.
+template <int BLK>
+__device__ __forceinline__ void pv_block_f32(const v4u (&vf)[8][2], const v4u& ph, const v4u& pl,
+                                             f32x4_t (&acc)[8]) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+    split2(comp(vf[2 * jj][BLK / 4], BLK % 4), comp(vf[2 * jj + 1][BLK / 4], BLK % 4), h[jj],
+           l[jj]);
+  const v4u vh = {h[0], h[1], h[2], h[3]}, vl = {l[0], l[1], l[2], l[3]};
+  acc[BLK] = mfma16(vh, ph, acc[BLK]);
+  acc[BLK] = mfma16(vh, pl, acc[BLK]);
+  acc[BLK] = mfma16(vl, ph, acc[BLK]);
+}
+
+// The condensed tier on the matrix cores: like wave_attn_mx, with float32
+// sums (ksum, vsum) and counts n.  Entry e's logit is q.ksum_e / n_e *
+// scale + ln n_e and its value vsum_e / n_e (the weight enters divided by
+// n_e).  Key and value sums enter as two bf16 terms each (relative error
+// below 2^-17 per element), the weights as two terms as well.
+template <int G>
+__device__ inline void wave_attn_mx_chunk(const bf16_t* __restrict__ qg, const Rows& kr,
+                                          const Rows& vr, int b, int h, int r0, int wn,
+                                          const int32_t* __restrict__ cc, float scale,
+                                          float& m_run, float& l_run, f32x4_t (&acc)[8]) {
+  constexpr int D = 128;
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+  v4u qb[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    qb[s] = i < G ? *(const v4u*)(qg + i * D + 32 * s + 8 * g) : v4u{0u, 0u, 0u, 0u};
+  m_run = -INFINITY;
+  l_run = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < wn; base += 32) {
+    const int ek = base + 8 * (i >> 2) + (i & 3);
+    const char* k0 = kr.template row<false>(b, h, r0 + min(ek, wn - 1)) + 32 * g;
+    const char* k1 = kr.template row<false>(b, h, r0 + min(ek + 4, wn - 1)) + 32 * g;
+    v4u kf[2][4][2], vf[8][2];
+    int cn[8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kf[0][s][0] = *(const v4u*)(k0 + 128 * s);
+      kf[0][s][1] = *(const v4u*)(k0 + 128 * s + 16);
+      kf[1][s][0] = *(const v4u*)(k1 + 128 * s);
+      kf[1][s][1] = *(const v4u*)(k1 + 128 * s + 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = base + 8 * g + j;
+      cn[j] = e < wn ? cc[r0 + e] : 0;
+    }
+    // scores: each k-step's 8 floats as two bf16 terms against the bf16 query
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const v4u& a0 = kf[c][s][0];
+        const v4u& a1 = kf[c][s][1];
+        uint32_t hh[4], ll[4];
+        split2(__uint_as_float(a0.x), __uint_as_float(a0.y), hh[0], ll[0]);
+        split2(__uint_as_float(a0.z), __uint_as_float(a0.w), hh[1], ll[1]);
+        split2(__uint_as_float(a1.x), __uint_as_float(a1.y), hh[2], ll[2]);
+        split2(__uint_as_float(a1.z), __uint_as_float(a1.w), hh[3], ll[3]);
+        const v4u kh = {hh[0], hh[1], hh[2], hh[3]}, kl = {ll[0], ll[1], ll[2], ll[3]};
+        f32x4_t& sc = c ? s1 : s0;
+        sc = mfma16(kh, qb[s], sc);
+        sc = mfma16(kl, qb[s], sc);
+      }
+    }
+    // the value rows, loaded once the key sums have been consumed
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const char* vrow = vr.template row<false>(b, h, r0 + min(base + 8 * g + j, wn - 1)) + 32 * i;
+      vf[j][0] = *(const v4u*)vrow;
+      vf[j][1] = *(const v4u*)(vrow + 16);
+    }
+    float lg[8], inv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float dot = j < 4 ? s0[j] : s1[j - 4];
+      const bool valid = cn[j] > 0;
+      inv[j] = valid ? 1.f / (float)cn[j] : 0.f;
+      lg[j] = valid ? dot * inv[j] * scale + __logf((float)cn[j]) : -INFINITY;
+      mx = fmaxf(mx, lg[j]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m_run, mx);
+    const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - mn);
+    l_run *= alpha;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] *= alpha;
+    m_run = mn;
+    float pw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = lg[j] == -INFINITY ? 0.f : __expf(lg[j] - mn);
+      l_run += p;
+      pw[j] = p * inv[j];
+    }
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) split2(pw[2 * jj], pw[2 * jj + 1], ph[jj], pl[jj]);
+    const v4u phv = {ph[0], ph[1], ph[2], ph[3]}, plv = {pl[0], pl[1], pl[2], pl[3]};
+    pv_block_f32<0>(vf, phv, plv, acc);
+    pv_block_f32<1>(vf, phv, plv, acc);
+    pv_block_f32<2>(vf, phv, plv, acc);
+    pv_block_f32<3>(vf, phv, plv, acc);
+    pv_block_f32<4>(vf, phv, plv, acc);
+    pv_block_f32<5>(vf, phv, plv, acc);
+    pv_block_f32<6>(vf, phv, plv, acc);
+    pv_block_f32<7>(vf, phv, plv, acc);
+  }
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+}
+
 // LDS row stride of the per-wave numerators (padded against bank conflicts
 // of the matrix-core path's stores, where lanes of one store hold different
 // query heads).
@@ -357,6 +493,10 @@ __device__ inline void combine_waves(const float* s_m, const float* s_l, const f
 // bf16 rows, d = 128, G >= 4: the matrix-core path.
 template <typename E, int D, int G, bool CHUNK>
 constexpr bool kUseMx = !CHUNK && D == 128 && G >= 4 && sizeof(E) == 2;
+// float32 chunk sums with bf16 queries, d = 128, G >= 4: the matrix-core
+// condensed path.
+template <int D, int G, bool CHUNK, typename QT>
+constexpr bool kUseMxChunk = CHUNK && D == 128 && G >= 4 && sizeof(QT) == 2;
 
 // One tile of up to 256 entries: wave w takes entries [64 w, 64 w + 64).
 template <typename E, int D, int G, typename QT, bool CHUNK, bool P, bool IDX = false>
@@ -368,11 +508,15 @@ __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int wn = nrows - w * 64;
   wn = wn < 0 ? 0 : (wn > 64 ? 64 : wn);
-  if constexpr (kUseMx<E, D, G, CHUNK>) {
+  if constexpr (kUseMx<E, D, G, CHUNK> || kUseMxChunk<D, G, CHUNK, QT>) {
     float m, l;
     f32x4_t acc[8];
-    wave_attn_mx<G, P, IDX>((const bf16_t*)qg, kr, vr, b, h, r0 + w * 64, wn, idx, idx_max,
-                            gap_at, gap_len, (float)a.scale, m, l, acc);
+    if constexpr (CHUNK)
+      wave_attn_mx_chunk<G>((const bf16_t*)qg, kr, vr, b, h, r0 + w * 64, wn, cc,
+                            (float)a.scale, m, l, acc);
+    else
+      wave_attn_mx<G, P, IDX>((const bf16_t*)qg, kr, vr, b, h, r0 + w * 64, wn, idx, idx_max,
+                              gap_at, gap_len, (float)a.scale, m, l, acc);
     const int i = lane & 15, g = lane >> 4;
     if (i < G) {
       float* so = s_o + (w * G + i) * kSO<D>;

@@ -170,6 +170,43 @@ def test_row_tiles_ragged_and_peaked_full_attention(gpu, i):
     say("worst relative error", worst)
 
 
+@pytest.mark.parametrize("Hq", [8, 16])
+def test_condensed_tier_attention_precision(gpu, Hq):
+    """Most of the mass in the condensed tier (p = 0.3, C = 16, G = 4 and 8):
+    the GPU's attention against the oracle's float64 attention over the
+    GPU's own tiers, so only the attention arithmetic is compared.  Bound
+    1e-4 of max|o|: chunk sums and weights enter the matrix products as two
+    bf16 terms each (relative error below 2^-17 per element), which moves a
+    chunk logit by about 1e-5."""
+    w = small(f"chunkprec{Hq}", Hq=Hq, Hkv=2, C=16, p=0.3, T=(4000, 1500, 300))
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_step(case, desc)
+    tiers = g["tiers"]
+    G = w.G
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            T = w.T[b]
+            A = max(T - w.W, 0)
+            nch = -(-A // w.C)
+            q = case.q[b, h * G:(h + 1) * G].double().cpu().numpy()
+            K = S.head_rows(case, b, h, "k").double().cpu().numpy()
+            V = S.head_rows(case, b, h, "v").double().cpu().numpy()
+            k = int(tiers.count[b, h])
+            pos = tiers.pos[b, h, :k].long().cpu().numpy()
+            ks = tiers.ksum[b, h, :nch].double().cpu().numpy()
+            vs = tiers.vsum[b, h, :nch].double().cpu().numpy()
+            cc = tiers.ccount[b, h, :nch].cpu().numpy()
+            dense = O.dense_positions(T, 0, A)
+            ref = O.attend_head(q, K[dense], V[dense], K[pos], V[pos], ks, vs, cc)
+            o = g["out"][b, h * G:(h + 1) * G].double().cpu().numpy()
+            err = float((np.abs(o - ref).max(1) / np.abs(ref).max(1)).max())
+            worst = max(worst, err)
+            assert err <= 1e-4, (b, h, err)
+    say("worst relative error", worst)
+
+
 def test_edge_cases(gpu):
     # every sequence shorter than the window, a single-token context, and a
     # context exactly one token past the window
