@@ -56,6 +56,12 @@ and 2.B: a temperature, the raw attention distribution, budgets from
 attention entropy) is pinned in tests/test_oracle_entropy.py by the
 proportional-logit closed form, an independent root of the same equation
 (scipy's brentq), exact power-of-two rescaling and the bisection's limits.
+
+The key-dissimilarity metric (``keydiff_head``; section 2.B: similarity
+scores) is pinned in tests/test_oracle_keydiff.py by scipy's cosine distance,
+closed forms (antipodal key groups, an orthonormal key set), exact
+power-of-two scale invariance, the zero-vector convention and reductions of
+the whole step to full softmax attention.
 """
 from __future__ import annotations
 
@@ -67,6 +73,8 @@ import numpy as np
 METRIC_QK = 0      # max-over-GQA-group q.k logit
 METRIC_L2 = 1      # key L2 norm
 METRIC_WINDOW = 2  # observation-window, position-pooled max logit
+METRIC_KEYDIFF = 3  # key dissimilarity: minus the cosine to the candidates' key sum
+AUX_METRICS = (METRIC_L2, METRIC_WINDOW, METRIC_KEYDIFF)  # calibrated by a temperature
 
 # Calibration rule for heads whose metric is not the raw logit
 CALIB_SPREAD = 0   # temperature that matches the raw-logit spread (moments)
@@ -244,7 +252,7 @@ def calibrate_head(ell, s, metric: int, calib: int = CALIB_SPREAD) -> Calibratio
     if metric == METRIC_QK:
         shift, scale = 0.0, 1.0
         c = ell.copy()
-    elif metric in (METRIC_L2, METRIC_WINDOW) and calib == CALIB_ENTROPY:
+    elif metric in AUX_METRICS and calib == CALIB_ENTROPY:
         s64 = _f64(s)
         if n == 0 or s64.max() == s64.min():
             shift, scale = 0.0, 0.0
@@ -252,7 +260,7 @@ def calibrate_head(ell, s, metric: int, calib: int = CALIB_SPREAD) -> Calibratio
         else:
             shift, scale = float(s64.max()), entropy_temperature(ell, s)
             c = ((s64 - shift) * scale).astype(np.float32)
-    elif metric in (METRIC_L2, METRIC_WINDOW):
+    elif metric in AUX_METRICS:
         if calib != CALIB_SPREAD:
             raise ValueError(f"unknown calibration rule {calib}")
         if n == 0:
@@ -469,6 +477,33 @@ def dense_positions(T: int, S: int, A: int) -> np.ndarray:
     return np.concatenate([np.arange(0, S if A else T), np.arange(S + A, T) if A else []]).astype(np.int64)
 
 
+def keydiff_head(K):
+    """Key-dissimilarity metric of one head's candidate keys.
+
+    Section 2.B ("Goal") names similarity scores among the importance metrics
+    the calibration brings into one probability space, and the pages list
+    key-similarity-based eviction (KeyDiff) among related work.  Reading:
+    s_t = -cos(k_t, mu) with mu = the sum of the candidate keys (the mean
+    key's direction); a key whose direction differs most from the head's
+    typical key ranks highest.  cos is taken as 0 when k_t or mu is the zero
+    vector.  float64 from the exact inputs (the sum of bf16 or float32 keys),
+    s = -(k_t . mu) / (||k_t|| ||mu||), rounded once to float32.
+    """
+    k = _f64(K)
+    _check_finite(k)
+    n = k.shape[0]
+    if n == 0:
+        return np.zeros(0, np.float32)
+    mu = k.sum(axis=0)
+    nm = float(np.sqrt(mu @ mu))
+    nk = np.sqrt(np.einsum("nd,nd->n", k, k))
+    dots = k @ mu
+    s = np.zeros(n)
+    ok = (nk > 0) & (nm > 0)
+    s[ok] = -dots[ok] / (nk[ok] * nm)
+    return s.astype(np.float32)
+
+
 def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
               sinks: int = 0, merge: int = MERGE_MEAN, q_hist=None,
               radius: int = 0, calib: int = CALIB_SPREAD) -> HeadResult:
@@ -487,6 +522,8 @@ def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
     S, A = candidate_range(T, W, sinks)
     cand_K = K[S:S + A]
     ell, s = score_head(q_group, cand_K)
+    if metric == METRIC_KEYDIFF:
+        s = keydiff_head(cand_K)
     if metric == METRIC_WINDOW:
         # the window: this step's query, then the previous ones (q_hist [w-1, G, d])
         qw = [np.asarray(q_group)[None]]
@@ -600,6 +637,8 @@ def lifecycle_step(st: HeadState, q_group, k_new, v_new, p: float, metric: int):
     st.ring_V[slot] = v_new
     st.T = P + 1
     ell, s = score_head(q_group, st.pool_K)
+    if metric == METRIC_KEYDIFF:
+        s = keydiff_head(st.pool_K)
     cal = calibrate_head(ell, s, metric)
     sel = topp_head(cal.c, cal.w, cal.Z, p, positions=st.pool_pos)
     keep = np.zeros(len(st.pool_pos), bool)
