@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s + HBM GB/s (% of peak), Qwen3-8B shape, 16k ctx, batch 32"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = {"k_q_to_f64": "k_score.hip", "k_score": "k_score.hip",
+KERNEL_SOURCES = {"k_prep": "k_score.hip", "k_score": "k_score.hip",
                   "k_calibrate": "k_select.hip", "k_select": "k_select.hip",
                   "k_calsel": "k_select.hip",
                   "k_compact_attn": "k_compact.hip", "k_compact_fast": "k_compact.hip",
@@ -59,7 +59,8 @@ def kernel_bytes(w, A, k, kernel, fused):
 
     A[b, h]: aged candidates, k[b, h]: kept tokens (numpy int arrays);
     row = d * element size, nch = ceil(A / C), W' = dense rows.  Per (b, h):
-      k_score        A*row (keys) + 4A (logits)         [+ 4A norms, L2 heads]
+      k_prep         q widened to float64                [+ A*row, key-dissimilarity heads]
+      k_score        A*row (keys) + 4A (logits)         [+ 4A second metric, other heads]
       k_calibrate    4A (scores)                         [+ 4A]
       k_select       4A (scores) + A (mask)              [+ 4A]
       k_calsel       4A (scores) + A (mask)              [+ 4A] (both in one)
@@ -72,14 +73,15 @@ def kernel_bytes(w, A, k, kernel, fused):
     d = w.d
     es = 4 if w.dtype == 0 else 2
     row = d * es
-    l2 = np.array([m == 1 for m in w.metrics])[None, :]
+    l2 = np.array([m != 0 for m in w.metrics])[None, :]
+    kd = np.array([m == 3 for m in w.metrics])[None, :]
     T = np.array(w.T)[:, None]
     nch = -(-A // w.C)
     dense = np.minimum(T, w.W) + 0 * A
     q_bytes = w.B * w.Hq * d * es
     o_bytes = w.B * w.Hq * d * 4
-    if kernel == "k_q_to_f64":
-        return q_bytes + w.B * w.Hq * d * 8
+    if kernel == "k_prep":
+        return int(q_bytes + w.B * w.Hq * d * 8 + (A * row * kd).sum())
     if kernel == "k_score":
         return int((A * row + 4 * A + 4 * A * l2).sum() + w.B * w.Hq * d * 8)
     if kernel == "k_calibrate":
@@ -546,6 +548,10 @@ def main():
             wsv = H.alloc_workspace(dv, dev)
             var[tag] = round(time_ms(lambda: H.step(dv, case.q, cache, metric_n, tiers, out, wsv),
                                      args.steps), 4)
+        # every head on the key-dissimilarity metric (one more pass for the key sums)
+        metric_k = torch.full((w.Hkv,), H.METRIC_KEYDIFF, dtype=torch.int8, device=dev)
+        var["keydiff_spread"] = round(time_ms(lambda: H.step(desc, case.q, cache, metric_k, tiers,
+                                                             out, ws), args.steps), 4)
         res["variant_step_ms"] = var
     if not args.no_amortization:
         print("[bench] selection reuse", file=sys.stderr, flush=True)

@@ -71,7 +71,7 @@ int validate(const hardkv_desc* d) {
 }
 
 struct Layout {
-  size_t q64, logit, l2, wx, stats, mask, count, part, total;
+  size_t q64, kmu, logit, l2, wx, stats, mask, count, part, total;
   int max_tiles;
 };
 
@@ -89,6 +89,7 @@ Layout layout(const hardkv_desc* d) {
   const size_t B = d->batch, Hq = d->num_q_heads, Hkv = d->num_kv_heads, D = d->head_dim;
   const size_t G = Hq / Hkv, cap = d->sparse_cap;
   L.q64 = take(B * (size_t)window_of(d) * Hq * D * 8);
+  L.kmu = take(B * Hkv * (D + 1) * 8);
   L.logit = take(B * Hkv * cap * 4);
   L.l2 = take(B * Hkv * cap * 4);
   L.wx = take(d->pool_radius > 0 ? B * Hkv * cap * 4 : 0);
@@ -157,6 +158,7 @@ void do_score(const hardkv_desc* d, const Layout& L, char* ws, const void* q, co
   a.radius = d->pool_radius;
   a.wx = (float*)(ws + L.wx);
   a.q64 = (double*)(ws + L.q64);
+  a.kmu = (double*)(ws + L.kmu);
   a.rows = rows;
   a.cand = cand;
   a.max_cand = max_cand;

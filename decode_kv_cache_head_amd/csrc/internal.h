@@ -64,6 +64,7 @@ struct ScoreArgs {
   int radius;          // max-pooling radius of the window metric
   float* wx;           // workspace [B][Hkv][cap_stride]: window metric before pooling
   double* q64;        // workspace [B][window][Hq][D]
+  double* kmu;        // workspace [B][Hkv][D + 1]: key sum and its norm (key-dissimilarity heads)
   Rows rows;          // candidate key rows
   Cand cand;
   int max_cand;       // upper bound of any (b, h)'s candidate count

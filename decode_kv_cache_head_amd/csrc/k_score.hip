@@ -5,6 +5,10 @@
 // the max over the earlier queries of the window, then a max-pooling pass
 // over neighbouring positions (k_pool).
 //
+// Key-dissimilarity heads (section 2.B: similarity scores) score
+// s_t = -(k_t . mu) / (||k_t|| ||mu||) with mu the sum of the head's candidate
+// keys, which k_prep forms in float64 first.
+//
 // HBM-bound stream over the aged keys.  Each workgroup stages one 128-token
 // tile of one (b, h) in LDS; two lanes score each token, one per half of the
 // head dimension, with the G query rows of the head's GQA group read as
@@ -16,18 +20,79 @@
 
 namespace hk {
 
-// q64[b][i][:] = this step's query (i = 0) or the i-th previous one (q_hist)
-template <typename T>
-__global__ __launch_bounds__(256) void k_q_to_f64(const T* __restrict__ q,
-                                                   const T* __restrict__ q_hist, int window,
-                                                   int64_t per_q, double* __restrict__ q64,
-                                                   int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const int64_t b = i / (window * per_q), rest = i % (window * per_q);
-  const int64_t wi = rest / per_q, e = rest % per_q;
-  const T* src = wi == 0 ? q + b * per_q + e : q_hist + (b * (window - 1) + wi - 1) * per_q + e;
-  q64[i] = (double)Elt<T>::load1(src);
+// Before the score, one launch:
+//   blocks [0, nqb): q64[b][i][:] = this step's query (i = 0) or the i-th
+//     previous one (q_hist), widened to float64;
+//   blocks [nqb, nqb + B Hkv): one per (b, h); key-dissimilarity heads sum
+//     their candidate keys in float64 (each thread a fixed 16-byte piece of a
+//     fixed set of rows, the row groups then added in order in LDS) into
+//     kmu[b][h][0..D) and ||mu|| into kmu[b][h][D]; other heads return.
+template <typename T, int D, bool P>
+__global__ __launch_bounds__(256) void k_prep(const T* __restrict__ q, const T* __restrict__ q_hist,
+                                              int window, int64_t per_q, double* __restrict__ q64,
+                                              int64_t nq, int nqb, int hkv, Rows rows, Cand cand,
+                                              const int8_t* __restrict__ metric,
+                                              double* __restrict__ kmu) {
+  constexpr int EPC = Elt<T>::kPer16;
+  constexpr int CPR = D * (int)sizeof(T) / 16;  // pieces per row
+  constexpr int RG = 256 / CPR;                  // row groups
+  constexpr int U = 16;                          // rows in flight per thread
+  __shared__ double red[256][EPC];
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < nqb) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + tid;
+    if (i >= nq) return;
+    const int64_t b = i / (window * per_q), rest = i % (window * per_q);
+    const int64_t wi = rest / per_q, e = rest % per_q;
+    const T* src = wi == 0 ? q + b * per_q + e : q_hist + (b * (window - 1) + wi - 1) * per_q + e;
+    q64[i] = (double)Elt<T>::load1(src);
+    return;
+  }
+  const int hb = blockIdx.x - nqb;
+  const int b = hb / hkv, h = hb % hkv;
+  if (metric[h] != HARDKV_METRIC_KEYDIFF) return;
+  const int n = cand.n(b, h);
+  const int c = tid % CPR, r0 = tid / CPR;
+  const int rb = rows.tb(b, h), rh = rows.th(h);
+  double acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+  for (int r = r0; r < n; r += U * RG) {
+    v4u raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int rr = r + u * RG;
+      raw[u] = rr < n ? *(const v4u*)(rows.template row<P>(rb, rh, rr) + c * 16)
+                      : v4u{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float f[EPC];
+      Elt<T>::unpack(raw[u], f);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += (double)f[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) red[tid][e] = acc[e];
+  __syncthreads();
+  double* mu = kmu + ((int64_t)b * hkv + h) * (D + 1);
+  double sq = 0.0;
+  if (tid < D) {
+    const int pc = tid / EPC, e = tid % EPC;
+    double sum = 0.0;
+    for (int g = 0; g < RG; ++g) sum += red[g * CPR + pc][e];
+    mu[tid] = sum;
+    sq = sum * sum;
+  }
+  __syncthreads();
+  if (tid < D) red[tid][0] = sq;
+  __syncthreads();
+  if (tid == 0) {
+    double ss = 0.0;
+    for (int i = 0; i < D; ++i) ss += red[i][0];
+    mu[D] = sqrt(ss);
+  }
 }
 
 constexpr int kScoreTile = 128;  // tokens per tile
@@ -39,13 +104,17 @@ constexpr int score_group() { return G >= 8 ? 1 : 4; }
 
 // Partial q.k over one split of the row: `row` points at the split's first
 // byte, `qg` at the split's first query element; float64 from exact inputs.
-template <typename T, int D, int G, int PCS, bool L2>
+// KD: also the partial dot with the key sum mu (same split, float64).
+template <typename T, int D, int G, int PCS, bool L2, bool KD = false>
 __device__ __forceinline__ void split_dot(const unsigned char* row, const double* __restrict__ qg,
-                                          double (&acc)[G], double& ss) {
+                                          double (&acc)[G], double& ss,
+                                          const double* __restrict__ mu = nullptr,
+                                          double* mdot = nullptr) {
   constexpr int EPC = Elt<T>::kPer16;
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g] = 0.0;
   ss = 0.0;
+  if (KD) *mdot = 0.0;
 #pragma unroll
   for (int c = 0; c < PCS; ++c) {
     const v4u raw = *(const v4u*)(row + c * 16);
@@ -57,6 +126,7 @@ __device__ __forceinline__ void split_dot(const unsigned char* row, const double
 #pragma unroll
       for (int g = 0; g < G; ++g) acc[g] = fma(qg[g * D + c * EPC + e], kd, acc[g]);
       if (L2) ss = fma(kd, kd, ss);
+      if (KD) *mdot = fma(mu[c * EPC + e], kd, *mdot);
     }
   }
 }
@@ -76,14 +146,15 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
                                                Cand cand, const int8_t* __restrict__ metric,
                                                float* __restrict__ logit, float* __restrict__ l2,
                                                float* __restrict__ wdst, int window,
-                                               int64_t cap_stride, double scale) {
+                                               int64_t cap_stride, double scale,
+                                               const double* __restrict__ kmu) {
   constexpr int RB = D * (int)sizeof(T);
   constexpr int CPR = RB / 16;             // 16-byte pieces per row
   constexpr int PCS = CPR / 2;             // pieces per half row
   constexpr int PAD = RB + 16;             // conflict-free per-lane row reads
   constexpr int LOADS = kScoreTile * CPR / 256;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kScoreTile * PAD];
-  __shared__ double s_part[G + 1][kScoreTile];  // second half's dots and squared norm
+  __shared__ double s_part[G + 2][kScoreTile];  // second half's dots, squared norm, key-sum dot
   // logical (tile group, h, b), tile group fastest, spread XCD-contiguously
   const int hkv = gridDim.y, tid = threadIdx.x;
   const int nwg = gridDim.x * gridDim.y * gridDim.z;
@@ -99,6 +170,9 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
   const int tok = (w & 1) * 64 + lane;
   const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
   const bool is_win = metric != nullptr && metric[h] == HARDKV_METRIC_WINDOW;
+  const bool is_kd = metric != nullptr && metric[h] == HARDKV_METRIC_KEYDIFF;
+  // key-dissimilarity heads: the candidates' key sum (this half) and its norm
+  const double* kmu_h = kmu + ((int64_t)b * hkv + h) * (D + 1);
   const int64_t qoff = ((int64_t)b * window * hq + (int64_t)h * G) * D + half * (D / 2);
   const unsigned char* row = lds + tok * PAD + half * (RB / 2);
   const int64_t obase = ((int64_t)b * hkv + h) * cap_stride;
@@ -115,8 +189,10 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
   auto score_staged = [&](int t0) {
     const int t = t0 + tok;
     const double* __restrict__ qg = q64 + qoff;
-    double acc[G], ss;
-    if (is_l2)
+    double acc[G], ss, md = 0.0;
+    if (is_kd)
+      split_dot<T, D, G, PCS, true, true>(row, qg, acc, ss, kmu_h + half * (D / 2), &md);
+    else if (is_l2)
       split_dot<T, D, G, PCS, true>(row, qg, acc, ss);
     else
       split_dot<T, D, G, PCS, false>(row, qg, acc, ss);
@@ -124,6 +200,7 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
 #pragma unroll
       for (int g = 0; g < G; ++g) s_part[g][tok] = acc[g];
       s_part[G][tok] = ss;
+      s_part[G + 1][tok] = md;
     }
     __syncthreads();
     double mx = -INFINITY;
@@ -133,6 +210,11 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
       if (t < n) {
         logit[obase + t] = (float)(mx * scale);
         if (is_l2) l2[obase + t] = (float)sqrt(ss + s_part[G][tok]);
+        if (is_kd) {
+          const double nk = sqrt(ss + s_part[G][tok]), nm = kmu_h[D];
+          const double v = nk > 0.0 && nm > 0.0 ? -(md + s_part[G + 1][tok]) / (nk * nm) : 0.0;
+          l2[obase + t] = (float)v;
+        }
       }
     }
     if (is_win) {
@@ -233,9 +315,13 @@ template <typename T, int D, int G, bool P>
 static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   const int64_t per_q = (int64_t)a.hq * D;
   const int64_t nq = (int64_t)a.B * a.window * per_q;
-  observe("k_q_to_f64", st);
-  hipLaunchKernelGGL(k_q_to_f64<T>, dim3(ceil_div(nq, 256)), dim3(256), 0, st, (const T*)a.q,
-                     (const T*)a.q_hist, a.window, per_q, a.q64, nq);
+  const int nqb = ceil_div(nq, 256);
+  // with a metric array, one more block per (b, h) for the key sums
+  const int nkb = a.metric != nullptr ? a.B * a.hkv : 0;
+  observe("k_prep", st);
+  hipLaunchKernelGGL((k_prep<T, D, P>), dim3(nqb + nkb), dim3(256), 0, st, (const T*)a.q,
+                     (const T*)a.q_hist, a.window, per_q, a.q64, nq, nqb, a.hkv, a.rows, a.cand,
+                     a.metric, a.kmu);
   dim3 grid(ceil_div(a.max_cand, kScoreTile * score_group<G>()), a.hkv, a.B);
   if (grid.x == 0) return;
   // window heads: the metric goes straight to l2 unless it is pooled
@@ -243,10 +329,12 @@ static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   observe("k_score", st);
   if (a.window > 1)
     hipLaunchKernelGGL((k_score<T, D, G, P, true>), grid, dim3(256), 0, st, a.q64, a.hq, a.rows,
-                       a.cand, a.metric, a.logit, a.l2, wdst, a.window, a.cap_stride, a.scale);
+                       a.cand, a.metric, a.logit, a.l2, wdst, a.window, a.cap_stride, a.scale,
+                       a.kmu);
   else
     hipLaunchKernelGGL((k_score<T, D, G, P, false>), grid, dim3(256), 0, st, a.q64, a.hq, a.rows,
-                       a.cand, a.metric, a.logit, a.l2, wdst, a.window, a.cap_stride, a.scale);
+                       a.cand, a.metric, a.logit, a.l2, wdst, a.window, a.cap_stride, a.scale,
+                       a.kmu);
   if (a.radius > 0 && a.metric != nullptr) {
     observe("k_pool", st);
     hipLaunchKernelGGL(k_pool, dim3(ceil_div(a.max_cand, kPoolTile), a.hkv, a.B), dim3(256),

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libhardkv.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
-METRIC_QK, METRIC_L2, METRIC_WINDOW = 0, 1, 2
+METRIC_QK, METRIC_L2, METRIC_WINDOW, METRIC_KEYDIFF = 0, 1, 2, 3
 MODE_REWRITE, MODE_SPARSE = 0, 1
 MERGE_MEAN, MERGE_WEIGHTED = 0, 1
 CALIB_SPREAD, CALIB_ENTROPY = 0, 1

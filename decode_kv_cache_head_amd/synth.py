@@ -23,6 +23,7 @@ DT_BF16 = 1
 METRIC_QK = 0
 METRIC_L2 = 1
 METRIC_WINDOW = 2
+METRIC_KEYDIFF = 3
 
 
 @dataclass(frozen=True)

@@ -72,6 +72,10 @@ typedef struct ihipStream_t* hardkv_stream_t; /* same type as hipStream_t */
                                   the GQA group of q.k / sqrt(d), max-pooled over positions
                                   [t - pool_radius, t + pool_radius]; calibrated like L2
                                   (section 2.B: SnapKV-style strategies) */
+#define HARDKV_METRIC_KEYDIFF 3 /* key dissimilarity: -(k_t . mu) / (||k_t|| ||mu||), mu the
+                                   sum of the head's candidate keys (0 for a zero vector),
+                                   float64, one rounding; calibrated like L2 (section 2.B:
+                                   similarity scores among the importance metrics) */
 
 /* How L2 and window heads are calibrated (hardkv_desc.calibration); QK heads
  * always keep temperature 1 (section 2.B, Mechanism: a temperature maps a
@@ -250,7 +254,9 @@ size_t hardkv_workspace_size(const hardkv_desc* desc);
  *           the dot product accumulated in float64
  *   l2:     [B][Hkv][sparse_cap] float32 second metric: key norms for HARDKV_METRIC_L2
  *           heads, the pooled window metric for HARDKV_METRIC_WINDOW heads (float64
- *           dots, one rounding, exact max-pooling); must be non-NULL whenever metric is
+ *           dots, one rounding, exact max-pooling), the key dissimilarity for
+ *           HARDKV_METRIC_KEYDIFF heads (the key sum is formed first, in float64 and
+ *           in a fixed order, in the workspace); must be non-NULL whenever metric is
  *           non-NULL
  * Entries at t >= A_b are unspecified. */
 int hardkv_score(const hardkv_desc* desc, const void* q, const hardkv_cache* cache,

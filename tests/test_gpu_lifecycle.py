@@ -180,6 +180,11 @@ def check_step(run, states, s, rep):
          metric=(O.METRIC_QK, O.METRIC_L2, O.METRIC_L2, O.METRIC_QK)),
     dict(B=3, Hq=8, Hkv=2, d=64, T0=600, W=64, C=16, p=0.85, steps=8, pool_block=32,
          metric=(O.METRIC_L2, O.METRIC_QK)),
+    # key-dissimilarity heads: the key sum of each step's pool formed first
+    dict(B=2, Hq=16, Hkv=4, d=128, T0=2600, W=128, C=64, p=0.9, steps=6,
+         metric=(O.METRIC_KEYDIFF, O.METRIC_QK, O.METRIC_L2, O.METRIC_KEYDIFF)),
+    dict(B=2, Hq=8, Hkv=2, d=64, T0=900, W=64, C=16, p=0.85, steps=6, pool_block=32,
+         metric=(O.METRIC_QK, O.METRIC_KEYDIFF)),
 ])
 def test_lifecycle_matches_oracle(gpu, cfg):
     steps = cfg.pop("steps")

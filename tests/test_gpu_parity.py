@@ -87,6 +87,14 @@ GRID = [
          metric=(S.METRIC_L2, S.METRIC_L2), calibration=1),
     dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.9, block_size=16, sinks=4, merge=1,
          metric=(S.METRIC_WINDOW, S.METRIC_L2), obs_window=4, pool_radius=3, calibration=1),
+    # key-dissimilarity heads (the candidates' key sum formed before the score)
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.9, metric=(S.METRIC_KEYDIFF, S.METRIC_QK)),
+    dict(dtype=S.DT_F32, d=64, Hq=8, Hkv=4, C=7, p=0.8, obs_window=2, calibration=1,
+         metric=(S.METRIC_KEYDIFF, S.METRIC_L2, S.METRIC_WINDOW, S.METRIC_KEYDIFF)),
+    dict(dtype=S.DT_BF16, d=128, Hq=16, Hkv=2, C=64, p=0.95, block_size=16, sinks=4, merge=1,
+         T=(9000, 2100, 300), metric=(S.METRIC_KEYDIFF, S.METRIC_KEYDIFF)),
+    dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=2, C=32, p=0.7, calibration=1,
+         metric=(S.METRIC_QK, S.METRIC_KEYDIFF)),
 ]
 
 
@@ -366,6 +374,20 @@ def test_headline_with_entropy_calibration(gpu):
     g = run_step(case, desc)
     check_all_heads_invariants(case, desc, g)
     rep = check_case(case, g, w.p, heads=_sample_heads(w, 6, 4), stages=False)
+    say(rep)
+
+
+def test_headline_with_key_dissimilarity(gpu):
+    """The headline shape with half the KV heads on the key-dissimilarity
+    metric (spread rule) and the stage-by-stage path: sampled heads against
+    the oracle, invariants on every head."""
+    w = S.workload("qwen8b_b32_16k_paged", metric=(S.METRIC_QK, S.METRIC_KEYDIFF) * 4)
+    say(w.name, "key dissimilarity")
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_stages(case, desc)
+    check_all_heads_invariants(case, desc, g)
+    rep = check_case(case, g, w.p, heads=_sample_heads(w, 6, 4))
     say(rep)
 
 
