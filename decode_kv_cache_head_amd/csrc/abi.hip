@@ -18,7 +18,7 @@ void hk::observe(const char* kernel, hipStream_t st) {
 
 namespace {
 
-constexpr int kVersion = 10500;  // 1.5.0
+constexpr int kVersion = 10600;  // 1.6.0
 
 int log2i(int v) {
   int l = 0;

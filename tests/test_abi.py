@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = H.load()
-    assert lib.hardkv_version() == 10500
+    assert lib.hardkv_version() == 10600
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.hardkv_strerror(code)
     assert lib.hardkv_strerror(99) == b"unknown error"
