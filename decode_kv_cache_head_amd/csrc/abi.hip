@@ -591,12 +591,11 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   int32_t* count = (int32_t*)(w + L.count);
   do_score(d, L, w, q, nullptr, pk, cand, d->sparse_cap, metric, logit, l2, st);
   const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
-  if (calsel_fits(d->sparse_cap)) {
-    launch_calsel(sa, d->sparse_cap, st);
-  } else {
-    launch_calibrate(sa, st);
-    launch_select(sa, st);
-  }
+  // separate launches: after the first steps the pools are a few hundred
+  // tokens, where the fused kernel's one-workgroup-per-CU footprint (scores
+  // in registers, weights in LDS) costs more than the two light kernels
+  launch_calibrate(sa, st);
+  launch_select(sa, st);
   CompactArgs ca = compact_args(d, L, w, pk, pv, cand, d->sparse_cap, mask, t);
   ca.pg = pg;
   launch_compact_inplace(ca, st);

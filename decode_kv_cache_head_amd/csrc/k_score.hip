@@ -20,27 +20,32 @@
 
 namespace hk {
 
-// Before the score, one launch:
+// Before the score, one launch of 1024-thread blocks:
 //   blocks [0, nqb): q64[b][i][:] = this step's query (i = 0) or the i-th
 //     previous one (q_hist), widened to float64;
 //   blocks [nqb, nqb + B Hkv): one per (b, h); key-dissimilarity heads sum
-//     their candidate keys in float64 (each thread a fixed 16-byte piece of a
-//     fixed set of rows, the row groups then added in order in LDS) into
-//     kmu[b][h][0..D) and ||mu|| into kmu[b][h][D]; other heads return.
+//     their candidate keys in float64 into kmu[b][h][0..D) and ||mu|| into
+//     kmu[b][h][D]; other heads return.  Each thread adds a fixed 16-byte
+//     piece of a fixed set of rows, the next batch of rows in flight while
+//     the current one is added; the row groups are then combined in a fixed
+//     order (lane pairs inside each wave, then the waves in LDS).
+constexpr int kPrepThreads = 1024;
+
 template <typename T, int D, bool P>
-__global__ __launch_bounds__(256) void k_prep(const T* __restrict__ q, const T* __restrict__ q_hist,
-                                              int window, int64_t per_q, double* __restrict__ q64,
-                                              int64_t nq, int nqb, int hkv, Rows rows, Cand cand,
-                                              const int8_t* __restrict__ metric,
-                                              double* __restrict__ kmu) {
+__global__ __launch_bounds__(kPrepThreads) void k_prep(
+    const T* __restrict__ q, const T* __restrict__ q_hist, int window, int64_t per_q,
+    double* __restrict__ q64, int64_t nq, int nqb, int hkv, Rows rows, Cand cand,
+    const int8_t* __restrict__ metric, double* __restrict__ kmu) {
   constexpr int EPC = Elt<T>::kPer16;
-  constexpr int CPR = D * (int)sizeof(T) / 16;  // pieces per row
-  constexpr int RG = 256 / CPR;                  // row groups
-  constexpr int U = 16;                          // rows in flight per thread
-  __shared__ double red[256][EPC];
+  constexpr int CPR = D * (int)sizeof(T) / 16;  // pieces per row (<= 64)
+  constexpr int RG = kPrepThreads / CPR;         // row groups
+  constexpr int U = 8;                           // rows per batch per thread
+  constexpr int NW = kPrepThreads / 64;
+  __shared__ double red[NW][CPR][EPC];
+  __shared__ double sq[D];
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < nqb) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + tid;
+    const int64_t i = (int64_t)blockIdx.x * kPrepThreads + tid;
     if (i >= nq) return;
     const int64_t b = i / (window * per_q), rest = i % (window * per_q);
     const int64_t wi = rest / per_q, e = rest % per_q;
@@ -54,43 +59,55 @@ __global__ __launch_bounds__(256) void k_prep(const T* __restrict__ q, const T* 
   const int n = cand.n(b, h);
   const int c = tid % CPR, r0 = tid / CPR;
   const int rb = rows.tb(b, h), rh = rows.th(h);
-  double acc[EPC];
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
-  for (int r = r0; r < n; r += U * RG) {
-    v4u raw[U];
+  auto fetch = [&](v4u (&raw)[U], int r) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rr = r + u * RG;
       raw[u] = rr < n ? *(const v4u*)(rows.template row<P>(rb, rh, rr) + c * 16)
                       : v4u{0u, 0u, 0u, 0u};
     }
+  };
+  double acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+  v4u cur[U], nxt[U];
+  fetch(cur, r0);
+  for (int r = r0; r < n; r += U * RG) {
+    if (r + U * RG < n) fetch(nxt, r + U * RG);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float f[EPC];
-      Elt<T>::unpack(raw[u], f);
+      Elt<T>::unpack(cur[u], f);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[e] += (double)f[e];
     }
-  }
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) red[tid][e] = acc[e];
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+  }
+  // lanes l and l + CPR of a wave hold the same piece: pair them up to one
+  // value per piece per wave (fixed pairing), then add the waves in order
+  const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  if (lane < CPR) {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) red[w][lane][e] = acc[e];
+  }
   __syncthreads();
   double* mu = kmu + ((int64_t)b * hkv + h) * (D + 1);
-  double sq = 0.0;
   if (tid < D) {
     const int pc = tid / EPC, e = tid % EPC;
     double sum = 0.0;
-    for (int g = 0; g < RG; ++g) sum += red[g * CPR + pc][e];
+    for (int v = 0; v < NW; ++v) sum += red[v][pc][e];
     mu[tid] = sum;
-    sq = sum * sum;
+    sq[tid] = sum * sum;
   }
-  __syncthreads();
-  if (tid < D) red[tid][0] = sq;
   __syncthreads();
   if (tid == 0) {
     double ss = 0.0;
-    for (int i = 0; i < D; ++i) ss += red[i][0];
+    for (int i = 0; i < D; ++i) ss += sq[i];
     mu[D] = sqrt(ss);
   }
 }
@@ -315,11 +332,11 @@ template <typename T, int D, int G, bool P>
 static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   const int64_t per_q = (int64_t)a.hq * D;
   const int64_t nq = (int64_t)a.B * a.window * per_q;
-  const int nqb = ceil_div(nq, 256);
+  const int nqb = ceil_div(nq, kPrepThreads);
   // with a metric array, one more block per (b, h) for the key sums
   const int nkb = a.metric != nullptr ? a.B * a.hkv : 0;
   observe("k_prep", st);
-  hipLaunchKernelGGL((k_prep<T, D, P>), dim3(nqb + nkb), dim3(256), 0, st, (const T*)a.q,
+  hipLaunchKernelGGL((k_prep<T, D, P>), dim3(nqb + nkb), dim3(kPrepThreads), 0, st, (const T*)a.q,
                      (const T*)a.q_hist, a.window, per_q, a.q64, nq, nqb, a.hkv, a.rows, a.cand,
                      a.metric, a.kmu);
   dim3 grid(ceil_div(a.max_cand, kScoreTile * score_group<G>()), a.hkv, a.B);
