@@ -136,6 +136,10 @@ Cand aged_cand(const hardkv_desc* d, const int32_t* ctx_len) {
               d->sinks};
 }
 
+// Drops an error left by an earlier, unrelated launch on this thread, so
+// launched() reports only this call's launches.
+void clear_launch_error() { (void)hipGetLastError(); }
+
 int launched() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? HARDKV_OK : HARDKV_ERR_HIP;
@@ -305,7 +309,7 @@ void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
   double* stats = (double*)(w + L.stats);
   uint8_t* mask = (uint8_t*)(w + L.mask);
   int32_t* count = (int32_t*)(w + L.count);
-  hipGetLastError();
+  clear_launch_error();
   do_score(d, L, w, q, cache->q_hist, kr, cand, max_aged(d), metric, logit, l2, st);
   SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
   sa.mode = t.mode;
@@ -378,7 +382,7 @@ int hardkv_score(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
   if (rc) return rc;
   if (!q || !scored_cache_ok(d, cache) || !logit || (metric && !l2)) return HARDKV_ERR_INVALID_ARG;
   const Layout L = layout(d);
-  hipGetLastError();
+  clear_launch_error();
   do_score(d, L, (char*)ws, q, cache->q_hist, cand_rows(d, cache->k, cache->block_table),
            aged_cand(d, cache->ctx_len), max_aged(d), metric, logit, l2, (hipStream_t)stream);
   return launched();
@@ -390,7 +394,7 @@ int hardkv_calibrate(const hardkv_desc* d, const int32_t* ctx_len, const int8_t*
   int rc = common_checks(d, ws, ws_bytes);
   if (rc) return rc;
   if (!ctx_len || !logit || !stats || (metric && !l2)) return HARDKV_ERR_INVALID_ARG;
-  hipGetLastError();
+  clear_launch_error();
   launch_calibrate(select_args(d, aged_cand(d, ctx_len), metric, logit, l2, stats, nullptr, nullptr),
                    (hipStream_t)stream);
   return launched();
@@ -403,7 +407,7 @@ int hardkv_topp_select(const hardkv_desc* d, const int32_t* ctx_len, const int8_
   if (rc) return rc;
   if (!ctx_len || !logit || !stats || !mask || !count || (metric && !l2))
     return HARDKV_ERR_INVALID_ARG;
-  hipGetLastError();
+  clear_launch_error();
   launch_select(select_args(d, aged_cand(d, ctx_len), metric, logit, l2, (double*)stats, mask,
                             count),
                 (hipStream_t)stream);
@@ -427,7 +431,7 @@ int hardkv_compact_scored(const hardkv_desc* d, const hardkv_cache* cache,
   a.logit = logit;
   a.l2 = l2;
   a.stats = stats;
-  hipGetLastError();
+  clear_launch_error();
   launch_compact(a, (hipStream_t)stream);
   return launched();
 }
@@ -453,7 +457,7 @@ int hardkv_decode_attn(const hardkv_desc* d, const void* q, const hardkv_cache* 
   a.dv = cache_rows(d, cache->v, cache->block_table);
   a.ctx_len = cache->ctx_len;
   a.ring = false;
-  hipGetLastError();
+  clear_launch_error();
   launch_attn(a, (hipStream_t)stream);
   return launched();
 }
@@ -467,7 +471,7 @@ int hardkv_plan(const hardkv_desc* d, const hardkv_policy* policy, const int32_t
                              nullptr, (int32_t*)count);
   a.mode = mode;
   a.policy = *policy;
-  hipGetLastError();
+  clear_launch_error();
   launch_plan(a, (hipStream_t)stream);
   return launched();
 }
@@ -478,7 +482,7 @@ int hardkv_pack(const hardkv_desc* d, const int32_t* count, const hardkv_tiers* 
   if (rc) return rc;
   if (d->packed_rows == 0 || !count || !tiers || !tiers->mode || !tiers->offset)
     return HARDKV_ERR_INVALID_ARG;
-  hipGetLastError();
+  clear_launch_error();
   launch_pack(d->batch * d->num_kv_heads, count, max_aged(d), tiers->mode, tiers->offset,
               d->packed_rows, (hipStream_t)stream);
   return launched();
@@ -542,7 +546,7 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   char* w = (char*)ws;
   hipStream_t st = (hipStream_t)stream;
   const hardkv_tiers* t = &s->tiers;
-  hipGetLastError();
+  clear_launch_error();
 
   AppendArgs ap{};
   ap.dtype = d->dtype;
