@@ -29,6 +29,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s + HBM GB/s (% of peak), Qwen3-8B shape, 16k ctx, batch 32"
 HBM_PEAK_GBS = 8000.0
+QWEN3_8B_LAYERS = 36   # decoder layers of the public Qwen3-8B / Qwen3-32B models
+QWEN3_32B_LAYERS = 64
 KERNEL_SOURCES = {"k_prep": "k_score.hip", "k_score": "k_score.hip",
                   "k_calibrate": "k_select.hip", "k_select": "k_select.hip",
                   "k_calsel": "k_select.hip",
@@ -371,7 +373,11 @@ def lifecycle(dev, reps=5, steady_steps=48, pool_block=0):
            "steady_pool_median": pool_steady,
            "pool_kv_mb": {"before": mb0, "after_step1": mb1, "steady": mb_steady},
            "step1_tokens_per_s": round(B / (step1 * 1e-3), 1),
-           "steady_tokens_per_s": round(B / (steady * 1e-3), 1)}
+           "steady_tokens_per_s": round(B / (steady * 1e-3), 1),
+           # attention + compression only, every layer of the model, steady state
+           "steady_model_tokens_per_s_attention_only": {
+               "layers": QWEN3_32B_LAYERS,
+               "value": round(B / (steady * 1e-3) / QWEN3_32B_LAYERS, 1)}}
     del t, st, k0, v0, ws
     torch.cuda.empty_cache()
     return res
@@ -515,6 +521,9 @@ def main():
         "graph_replay_ms_per_step": round(graph_ms, 4),
         "device_copy_gbs": round(copy_gbs, 1),
         "kept_fraction": round(float(k.sum() / max(A.sum(), 1)), 4),
+        # attention + compression only, every layer of the model at this shape
+        "model_tokens_per_s_attention_only": {
+            "layers": QWEN3_8B_LAYERS, "value": round(tok_s / QWEN3_8B_LAYERS, 1)},
         "dtype_note": "bf16 q/K/V in HBM; float64 score accumulation, 2^-47 fixed-point "
                       "top-p masses, float32 attention",
     }
