@@ -611,10 +611,10 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   }
   a.dk = region_rows(d, s->ring_k, d->dense_window);
   a.dv = region_rows(d, s->ring_v, d->dense_window);
-  a.ctx_len = s->seq_len;
+  a.ctx_len = nullptr;  // the ring's tiers do not depend on the length
   a.ring = true;
+  a.advance = s->seq_len;  // the merge, the step's last kernel, moves every sequence on
   launch_attn(a, st);
-  launch_advance(s->seq_len, d->batch, st);
   return launched();
 }
 

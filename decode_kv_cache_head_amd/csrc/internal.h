@@ -187,6 +187,9 @@ struct AttnArgs {
   // > 0: the sparse tier was attended by the fused compaction (its tiles of
   // fused_tt candidates own partial slots 0..); only dense and chunk tiles here
   int fused_tt;
+  // lifecycle: advance[b] += 1 for every sequence once the outputs are
+  // written (by the merge); null elsewhere
+  int32_t* advance;
 };
 int attn_max_tiles(int W, int sparse_cap, int chunk_cap);
 void launch_attn(const AttnArgs& a, hipStream_t st);
@@ -210,7 +213,6 @@ struct AppendArgs {
   int C, chunk_cap;
 };
 void launch_append(const AppendArgs& a, hipStream_t st);
-void launch_advance(int32_t* seq_len, int B, hipStream_t st);
 // block manager: blocks for the rows the append is about to write, and the
 // return of blocks past each head's count after the compaction
 void launch_pool_grow(const AppendArgs& a, hipStream_t st);

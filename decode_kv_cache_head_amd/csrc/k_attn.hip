@@ -614,9 +614,15 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   attn_tiles<T, D, G, P, PS, PART>(a);
 }
 
-// One wave per (b, query head): joins the partials of every tile.
+// One wave per (b, query head): joins the partials of every tile.  With
+// a.advance (the lifecycle), thread i < B also moves sequence i on by one
+// token; nothing in this launch reads those lengths.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  if (a.advance) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < a.B) a.advance[i] += 1;
+  }
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (wid >= a.B * a.hq) return;
   const int b = wid / a.hq, qh = wid % a.hq, h = qh / G, g = qh % G;

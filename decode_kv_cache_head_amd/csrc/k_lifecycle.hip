@@ -186,11 +186,6 @@ __global__ __launch_bounds__(1024) void k_pool_shrink(PoolPaging pg, const int32
   }
 }
 
-__global__ void k_advance(int32_t* seq_len, int B) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < B) seq_len[i] += 1;
-}
-
 template <typename T, int D, int G_unused>
 static void launch_append_t(const AppendArgs& a, hipStream_t st) {
   observe("k_append", st);
@@ -209,11 +204,6 @@ void launch_pool_grow(const AppendArgs& a, hipStream_t st) {
 void launch_pool_shrink(const PoolPaging& pg, const int32_t* count, int n_heads, hipStream_t st) {
   observe("k_pool_shrink", st);
   hipLaunchKernelGGL(k_pool_shrink, dim3(1), dim3(1024), 0, st, pg, count, n_heads);
-}
-
-void launch_advance(int32_t* seq_len, int B, hipStream_t st) {
-  observe("k_advance", st);
-  hipLaunchKernelGGL(k_advance, dim3(ceil_div(B, 256)), dim3(256), 0, st, seq_len, B);
 }
 
 }  // namespace hk
