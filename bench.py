@@ -214,6 +214,9 @@ def amortization(w, case, steps, horizons=(1, 2, 4, 8, 16, 32)):
     dense = time_ms(lambda: H.decode_attn(d_dense, case.q, cache, t_none, out, ws_dense), steps)
     A = np.maximum(np.array(w.T) - w.W, 0)
     k = t_rw.count.cpu().numpy()
+    # the reuse step is the attention launch alone (plus its merge): its
+    # algorithmic bytes (rewritten rows, dense rows, chunks, q) per second
+    reuse_bytes = kernel_bytes(w, np.repeat(A[:, None], w.Hkv, axis=1), k, "k_attn", False)
 
     def avg(sel, reuse, n):
         return (sel + (n - 1) * reuse) / n
@@ -245,6 +248,10 @@ def amortization(w, case, steps, horizons=(1, 2, 4, 8, 16, 32)):
         "select_ms": {"rewrite": round(sel_rw, 4), "sparse": round(sel_sp, 4)},
         "reuse_ms": {"rewrite": round(reuse_rw, 4), "sparse": round(reuse_sp, 4)},
         "dense_attention_ms": round(dense, 4),
+        "reuse_attention_hbm": {"algorithmic_gb": round(reuse_bytes / 1e9, 4),
+                                "gbs": round(reuse_bytes / (reuse_rw * 1e-3) / 1e9, 1),
+                                "frac_of_peak": round(reuse_bytes / (reuse_rw * 1e-3) / 1e9
+                                                      / HBM_PEAK_GBS, 4)},
         "avg_step_ms": {str(n): {"rewrite": round(avg(sel_rw, reuse_rw, n), 4),
                                  "sparse": round(avg(sel_sp, reuse_sp, n), 4)}
                         for n in horizons},

@@ -199,7 +199,11 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int idx = j * 256 + tid, r = idx / CPR, c = idx % CPR;
-      buf[j] = *(const v4u*)(rows.template row<P>(rb, rh, min(t0 + r, n - 1)) + c * 16);
+      // non-temporal: the keys are read once here and once more by the
+      // compaction, far apart in time; streaming them keeps the caches for
+      // the score arrays the selection reads next
+      buf[j] = __builtin_nontemporal_load(
+          (const v4u*)(rows.template row<P>(rb, rh, min(t0 + r, n - 1)) + c * 16));
     }
   };
   // scores of the staged tile starting at t0 (uniform over the workgroup)
