@@ -21,6 +21,12 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("name,kw", [
     ("qwen8b_b1_16k", dict(B=2, T=(5000, 3333))),
     ("qwen8b_b32_16k_paged", dict(B=4, T=(4000, 2500, 300, 1024))),
+    # every non-logit metric (key sums formed in the first launch) and both
+    # calibration rules
+    ("qwen8b_b32_16k_paged", dict(B=3, T=(4000, 2500, 1024), metric=(
+        S.METRIC_KEYDIFF, S.METRIC_QK, S.METRIC_L2, S.METRIC_KEYDIFF) * 2)),
+    ("qwen8b_b1_16k", dict(B=2, T=(5000, 3333), calibration=1, metric=(
+        S.METRIC_L2, S.METRIC_KEYDIFF, S.METRIC_QK, S.METRIC_L2) * 2)),
 ])
 def test_step_graph_replay_matches_eager(gpu, name, kw):
     w = S.workload(name, **kw)
