@@ -146,10 +146,12 @@ int launched() {
 }
 
 // ---------------------------------------------------------- launch steps --
+// q_ready: an earlier launch of the same step has widened q into q64.
 void do_score(const hardkv_desc* d, const Layout& L, char* ws, const void* q, const void* q_hist,
               const Rows& rows, const Cand& cand, int max_cand, const int8_t* metric,
-              float* logit, float* l2, hipStream_t st) {
+              float* logit, float* l2, hipStream_t st, bool q_ready = false) {
   ScoreArgs a{};
+  a.q_ready = q_ready;
   a.dtype = d->dtype;
   a.D = d->head_dim;
   a.G = d->num_q_heads / d->num_kv_heads;
@@ -571,6 +573,9 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   ap.ccount = t->ccount;
   ap.C = d->chunk;
   ap.chunk_cap = d->chunk_cap;
+  ap.q = q;  // the append also widens this step's queries for the score
+  ap.q64 = (double*)(w + L.q64);
+  ap.hq = d->num_q_heads;
   if (pg.table) launch_pool_grow(ap, st);
   launch_append(ap, st);
 
@@ -593,7 +598,7 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   double* stats = (double*)(w + L.stats);
   uint8_t* mask = (uint8_t*)(w + L.mask);
   int32_t* count = (int32_t*)(w + L.count);
-  do_score(d, L, w, q, nullptr, pk, cand, d->sparse_cap, metric, logit, l2, st);
+  do_score(d, L, w, q, nullptr, pk, cand, d->sparse_cap, metric, logit, l2, st, true);
   const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
   // separate launches: after the first steps the pools are a few hundred
   // tokens, where the fused kernel's one-workgroup-per-CU footprint (scores

@@ -65,6 +65,7 @@ struct ScoreArgs {
   float* wx;           // workspace [B][Hkv][cap_stride]: window metric before pooling
   double* q64;        // workspace [B][window][Hq][D]
   double* kmu;        // workspace [B][Hkv][D + 1]: key sum and its norm (key-dissimilarity heads)
+  bool q_ready;       // q64 already holds this step's queries (the lifecycle's append widens them)
   Rows rows;          // candidate key rows
   Cand cand;
   int max_cand;       // upper bound of any (b, h)'s candidate count
@@ -211,6 +212,11 @@ struct AppendArgs {
   float* vsum;
   int32_t* ccount;
   int C, chunk_cap;
+  // this step's queries widened to float64 for the score: head h's block
+  // writes q64[b][hG .. hG + G)[:] from q (hq query heads)
+  const void* q;
+  double* q64;
+  int hq;
 };
 void launch_append(const AppendArgs& a, hipStream_t st);
 // block manager: blocks for the rows the append is about to write, and the

@@ -30,6 +30,12 @@ __global__ __launch_bounds__(64) void k_append(AppendArgs a) {
   static_assert(2 * CPR <= 64, "one 16-byte piece per thread");
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t bh = (int64_t)b * a.hkv + h;
+  if (a.q64) {
+    // the score's float64 queries: this head's GQA group
+    const int G = a.hq / a.hkv;
+    const int64_t q0 = ((int64_t)b * a.hq + (int64_t)h * G) * D;
+    for (int i = tid; i < G * D; i += 64) a.q64[q0 + i] = (double)Elt<T>::load1((const T*)a.q + q0 + i);
+  }
   const int P = a.seq_len[b];
   if (P < a.W || a.W <= 0) return;
   const int cnt = a.pool_count[bh];

@@ -336,13 +336,15 @@ template <typename T, int D, int G, bool P>
 static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   const int64_t per_q = (int64_t)a.hq * D;
   const int64_t nq = (int64_t)a.B * a.window * per_q;
-  const int nqb = ceil_div(nq, kPrepThreads);
+  const int nqb = a.q_ready ? 0 : ceil_div(nq, kPrepThreads);
   // with a metric array, one more block per (b, h) for the key sums
   const int nkb = a.metric != nullptr ? a.B * a.hkv : 0;
-  observe("k_prep", st);
-  hipLaunchKernelGGL((k_prep<T, D, P>), dim3(nqb + nkb), dim3(kPrepThreads), 0, st, (const T*)a.q,
-                     (const T*)a.q_hist, a.window, per_q, a.q64, nq, nqb, a.hkv, a.rows, a.cand,
-                     a.metric, a.kmu);
+  if (nqb + nkb > 0) {
+    observe("k_prep", st);
+    hipLaunchKernelGGL((k_prep<T, D, P>), dim3(nqb + nkb), dim3(kPrepThreads), 0, st,
+                       (const T*)a.q, (const T*)a.q_hist, a.window, per_q, a.q64, nq, nqb,
+                       a.hkv, a.rows, a.cand, a.metric, a.kmu);
+  }
   dim3 grid(ceil_div(a.max_cand, kScoreTile * score_group<G>()), a.hkv, a.B);
   if (grid.x == 0) return;
   // window heads: the metric goes straight to l2 unless it is pooled
