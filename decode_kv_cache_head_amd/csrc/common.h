@@ -199,6 +199,26 @@ __device__ inline float across_groups_sum(float v) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 16x16x32 bf16 matrix product, float32 accumulation: D(16x16) += A(16x32)
+// B(32x16), where lane l holds A[l % 16][8 (l / 16) + j] and
+// B[8 (l / 16) + j][l % 16] (j = 0..7) and D[4 (l / 16) + i][l % 16]
+// (i = 0..3).  Products of bf16 values are exact in float32.
+__device__ __forceinline__ f32x4_t mfma16(const v4u& a, const v4u& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Max over the 16 lanes of a DPP row; every lane of the row receives it.
+__device__ inline float row_max16(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  return v;
+}
 
 // Takes the word by value: bit-casting an ext-vector element in place
 // (__builtin_bit_cast(T, v.y)) is compiled as a cast of element 0.

@@ -179,17 +179,6 @@ __device__ inline void wave_attn(const QT* __restrict__ qg, const Rows& kr, cons
 }
 
 // ------------------------------------------------ matrix-core row tiles --
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-// D(16x16) += A(16x32) B(32x16): lane l holds A[l % 16][8 (l / 16) + j] and
-// B[8 (l / 16) + j][l % 16] (j = 0..7, bf16) and D[4 (l / 16) + i][l % 16]
-// (i = 0..3, float32).
-__device__ __forceinline__ f32x4_t mfma16(const v4u& a, const v4u& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
 // Word j of the bf16 pairs (x.half, y.half): the same element of two rows.
 template <int HI>
 __device__ __forceinline__ uint32_t pair_of(uint32_t x, uint32_t y) {

@@ -289,6 +289,126 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
   }
 }
 
+// Logit-only launches with bf16 keys, d = 128 and G >= 4: the matrix cores
+// find each token's winning query heads, float64 decides among them.
+//   1. S = K Q^T and A = |K| |Q|^T as 16x16x32 bf16 MFMA products; the
+//      products are exact in float32, so each float32 dot is within
+//      127 * 2^-24 * A of the true one (recursive summation of 128 terms;
+//      the kernel allows four times that, 2^-15 A).
+//   2. Per token, every query head whose float32 dot is within 2 * 2^-15 *
+//      max A of the largest is a candidate (usually one head).
+//   3. Two lanes per token (one per half of d, as in k_score) take the
+//      float64 dot of each candidate from the exact inputs, in k_score's
+//      order, and keep the maximum.
+// The logit fl32(max_g q_g . k_t / sqrt(d)) is the one k_score computes: the
+// true maximum is always a candidate.  Float64 work falls from G to about one
+// dot per token.
+constexpr int kScoreMxQS = 128 + 2;  // float64 query row stride in LDS (rows on different banks)
+constexpr int kScoreMxGroup = 8;     // consecutive tiles per workgroup, the next one in flight
+
+template <int G, bool P>
+__global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q,
+                                                  const double* __restrict__ q64, int hq,
+                                                  Rows rows, Cand cand,
+                                                  float* __restrict__ logit, int64_t cap_stride,
+                                                  double scale) {
+  constexpr int D = 128, RB = 256, CPR = 16, PAD = RB + 16;
+  constexpr int LOADS = kScoreTile * CPR / 256;
+  constexpr float kErr = 1.0f / 32768.0f;  // 2^-15: four times the float32 summation bound
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kScoreTile * PAD];
+  __shared__ __attribute__((aligned(16))) double s_q[G][kScoreMxQS];
+  __shared__ uint32_t s_cand[kScoreTile];
+  const int hkv = gridDim.y, tid = threadIdx.x;
+  const int nwg = gridDim.x * gridDim.y * gridDim.z;
+  const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int id = xcd_contiguous(L, nwg);
+  const int grp = id % gridDim.x, h = (id / gridDim.x) % hkv, b = id / (gridDim.x * hkv);
+  const int n = cand.n(b, h);
+  const int g0 = grp * kScoreMxGroup * kScoreTile;
+  if (g0 >= n) return;
+  const int rb = rows.tb(b, h), rh = rows.th(h);
+  v4u buf[LOADS];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int idx = j * 256 + tid, r = idx / CPR, c = idx % CPR;
+      buf[j] = __builtin_nontemporal_load(
+          (const v4u*)(rows.template row<P>(rb, rh, min(t0 + r, n - 1)) + c * 16));
+    }
+  };
+  fetch(g0);
+  const int64_t qrow = (int64_t)b * hq + (int64_t)h * G;
+  for (int i = tid; i < G * D; i += 256) s_q[i / D][i % D] = q64[qrow * D + i];
+  const int w = tid >> 6, lane = tid & 63;
+  const int qi = lane & 15, g4 = lane >> 4;
+  v4u qb[4], qa[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    qb[s] = qi < G ? *(const v4u*)(q + (qrow + qi) * D + 32 * s + 8 * g4) : v4u{0u, 0u, 0u, 0u};
+    qa[s] = qb[s] & 0x7fff7fffu;
+  }
+  const int tok = 32 * w + (lane & 31), half = lane >> 5;
+  float* out = logit + ((int64_t)b * hkv + h) * cap_stride;
+#pragma unroll 1
+  for (int k = 0; k < kScoreMxGroup; ++k) {
+    const int t0 = g0 + k * kScoreTile;  // uniform over the workgroup
+    if (t0 >= n) break;
+    if (k) __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int idx = j * 256 + tid, r = idx / CPR, c = idx % CPR;
+      *(v4u*)(lds + r * PAD + c * 16) = buf[j];
+    }
+    __syncthreads();
+    // the next tile's rows are in flight while this one is scored
+    if (k + 1 < kScoreMxGroup && t0 + kScoreTile < n) fetch(t0 + kScoreTile);
+    // 1-2: wave w filters tokens [32 w, 32 w + 32), two 16-row products
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r = 32 * w + 16 * c + qi;
+      f32x4_t sd = {0.f, 0.f, 0.f, 0.f}, sa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const v4u ka = *(const v4u*)(lds + r * PAD + (32 * s + 8 * g4) * 2);
+        sd = mfma16(ka, qb[s], sd);
+        sa = mfma16(ka & 0x7fff7fffu, qa[s], sa);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        // token 32 w + 16 c + 4 g4 + cc, query head qi
+        const float v = qi < G ? sd[cc] : -INFINITY;
+        const float m = row_max16(v);
+        const float e = row_max16(qi < G ? kErr * sa[cc] : 0.f);
+        const unsigned long long bal = __ballot(qi < G && v >= m - 2.f * e);
+        if (qi == 0) s_cand[32 * w + 16 * c + 4 * g4 + cc] = (uint32_t)(bal >> (16 * g4)) & 0xffffu;
+      }
+    }
+    // 3: float64 dots of the candidates, lanes l and l + 32 on the two halves
+    // (s_cand of these tokens was written by this wave)
+    uint32_t mask = s_cand[tok];
+    const unsigned char* row = lds + tok * PAD + half * (RB / 2);
+    double best = -INFINITY;
+    while (mask) {
+      const int i = __builtin_ctz(mask);
+      mask &= mask - 1u;
+      const double* qh = &s_q[i][half * (D / 2)];
+      double acc = 0.0;
+#pragma unroll 1
+      for (int c = 0; c < 8; ++c) {
+        const v4u raw = *(const v4u*)(row + c * 16);
+        float f[8];
+        Elt<bf16_t>::unpack(raw, f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fma(qh[c * 8 + e], (double)f[e], acc);
+      }
+      const double other = __shfl_xor(acc, 32, 64);
+      best = fmax(best, half ? other + acc : acc + other);
+    }
+    const int t = t0 + tok;
+    if (half == 0 && t < n) out[t] = (float)(best * scale);
+  }
+}
+
 // Max-pooling of the window metric over positions [t - r, t + r] inside the
 // candidates, for window heads: a 1024-token tile plus r on each side in
 // LDS, then doubling passes (M_{2p}[i] = max(M_p[i], M_p[i + p])) and one
@@ -349,6 +469,16 @@ static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   if (grid.x == 0) return;
   // window heads: the metric goes straight to l2 unless it is pooled
   float* wdst = a.radius > 0 ? a.wx : a.l2;
+  if constexpr (sizeof(T) == 2 && D == 128 && G >= 4) {
+    if (a.metric == nullptr && a.window == 1) {
+      observe("k_score", st);
+      hipLaunchKernelGGL((k_score_mx<G, P>),
+                         dim3(ceil_div(a.max_cand, kScoreMxGroup * kScoreTile), a.hkv, a.B),
+                         dim3(256), 0, st, (const bf16_t*)a.q, a.q64, a.hq, a.rows, a.cand,
+                         a.logit, a.cap_stride, a.scale);
+      return;
+    }
+  }
   observe("k_score", st);
   if (a.window > 1)
     hipLaunchKernelGGL((k_score<T, D, G, P, true>), grid, dim3(256), 0, st, a.q64, a.hq, a.rows,
