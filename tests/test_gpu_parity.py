@@ -215,6 +215,32 @@ def test_condensed_tier_attention_precision(gpu, Hq):
     say("worst relative error", worst)
 
 
+def test_score_filter_with_tied_and_near_tied_query_heads(gpu):
+    """The matrix-core score filter (bf16, d = 128, G = 8, no metric array):
+    KV head 0's query heads come in identical pairs, so every token has at
+    least two candidate heads; head 1's pairs differ in one element by one
+    bf16 step, so their float32 dots sit within the filter's band and the
+    float64 dots decide.  Logits must equal the oracle's float64 maximum
+    under the usual rule (at most 1 ulp, on a tiny fraction)."""
+    w = small("scorefilter", Hq=16, Hkv=2, T=(6000, 2500, 700), p=0.9)
+    case = S.make_case(w, gpu)
+    q = case.q.clone()
+    G = w.G
+    for b in range(w.B):
+        for j in range(0, G, 2):
+            q[b, j + 1] = q[b, j]                      # head 0: exact ties
+            q[b, G + j + 1] = q[b, G + j]              # head 1: one element one bf16 step up
+            e = (7 * j) % w.d
+            bits = q[b, G + j + 1, e].view(torch.int16) + 1
+            q[b, G + j + 1, e] = bits.view(torch.bfloat16)
+    case.q.copy_(q)
+    desc = desc_for(case)
+    g = run_stages(case, desc)
+    rep = check_case(case, g, w.p)
+    say(rep)
+    assert rep["logit_1ulp"] <= 0.001 * rep["candidates"]
+
+
 def test_edge_cases(gpu):
     # every sequence shorter than the window, a single-token context, and a
     # context exactly one token past the window
