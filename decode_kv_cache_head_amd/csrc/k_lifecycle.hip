@@ -31,10 +31,16 @@ __global__ __launch_bounds__(64) void k_append(AppendArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t bh = (int64_t)b * a.hkv + h;
   if (a.q64) {
-    // the score's float64 queries: this head's GQA group
+    // the score's float64 queries: this head's GQA group, 16-byte pieces
+    constexpr int EPC = Elt<T>::kPer16;
     const int G = a.hq / a.hkv;
     const int64_t q0 = ((int64_t)b * a.hq + (int64_t)h * G) * D;
-    for (int i = tid; i < G * D; i += 64) a.q64[q0 + i] = (double)Elt<T>::load1((const T*)a.q + q0 + i);
+    for (int p = tid; p < G * D / EPC; p += 64) {
+      float f[EPC];
+      Elt<T>::unpack(*(const v4u*)((const T*)a.q + q0 + p * EPC), f);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) a.q64[q0 + p * EPC + e] = (double)f[e];
+    }
   }
   const int P = a.seq_len[b];
   if (P < a.W || a.W <= 0) return;

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
   }
 }
 
-// Logit-only launches with bf16 keys, d = 128 and G >= 4: the matrix cores
+// Logit-only launches with bf16 keys, d = 128 and G >= 8: the matrix cores
 // find each token's winning query heads, float64 decides among them.
 //   1. S = K Q^T and A = |K| |Q|^T as 16x16x32 bf16 MFMA products; the
 //      products are exact in float32, so each float32 dot is within
@@ -469,7 +469,9 @@ static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   if (grid.x == 0) return;
   // window heads: the metric goes straight to l2 unless it is pooled
   float* wdst = a.radius > 0 ? a.wx : a.l2;
-  if constexpr (sizeof(T) == 2 && D == 128 && G >= 4) {
+  // the filter pays at G >= 8; at G = 4 the float64 dots of k_score already
+  // hide behind its loads (0.195 vs 0.236 ms on the 16k headline shape)
+  if constexpr (sizeof(T) == 2 && D == 128 && G >= 8) {
     if (a.metric == nullptr && a.window == 1) {
       observe("k_score", st);
       hipLaunchKernelGGL((k_score_mx<G, P>),

@@ -127,7 +127,7 @@ class Case:
     v: torch.Tensor
     ctx_len: torch.Tensor      # [B] int32
     block_table: torch.Tensor | None  # [B][max_blocks] int32
-    metric: torch.Tensor       # [Hkv] int8
+    metric: torch.Tensor | None  # [Hkv] int8, or None when every head is QK
     ctx_cap: int
     max_blocks: int
     extra: dict = field(default_factory=dict)
@@ -201,7 +201,8 @@ def make_case(w: Workload, device="cpu") -> Case:
             k[b] = kb
             v[b] = vb
     ctx_len = torch.tensor(w.T, dtype=torch.int32, device=device)
-    metric = torch.tensor(w.metrics, dtype=torch.int8, device=device)
+    # no metric array when every head scores with the logit (NULL = all QK)
+    metric = torch.tensor(w.metric, dtype=torch.int8, device=device) if w.metric else None
     if table is not None:
         table = table.to(device)
     q_hist = None
