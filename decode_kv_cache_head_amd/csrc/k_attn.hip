@@ -23,6 +23,10 @@
 // scores and the weighted value sum are 16x16x32 bf16 MFMA products with
 // float32 accumulation; the weights enter the second product as a bf16
 // high part plus a bf16 remainder, so each weight carries 16 significant bits.
+// With bf16 queries the condensed tiles do the same with their float32 sums
+// split into two bf16 terms (wave_attn_mx_chunk).  At G >= 8 the condensed
+// tiles run as a second launch so they do not set the row tiles' register
+// budget.
 #include "internal.h"
 
 namespace hk {

@@ -15,7 +15,9 @@
 // float64 from wave-uniform addresses (scalar loads, SGPR operands).  The
 // token's key is widened exactly to float64 and the dot products are
 // accumulated in float64, so the only rounding the ranking key sees is the
-// final fl32().
+// final fl32().  At G >= 8 (bf16, d = 128, no metric array) k_score_mx
+// first picks each token's candidate heads on the matrix cores and takes the
+// float64 dot of those only; the logit is the same.
 #include "internal.h"
 
 namespace hk {
