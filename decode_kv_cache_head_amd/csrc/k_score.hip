@@ -300,17 +300,17 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
 //   2. Per token, every query head whose float32 dot is within 2 * 2^-15 *
 //      max A of the largest is a candidate (usually one head).
 //   3. Two lanes per token (one per half of d, as in k_score) take the
-//      float64 dot of each candidate from the exact inputs, in k_score's
-//      order, and keep the maximum.
+//      float64 dot of each candidate from the exact inputs (bf16 queries and
+//      keys from LDS, widened in registers), in k_score's order, and keep
+//      the maximum.
 // The logit fl32(max_g q_g . k_t / sqrt(d)) is the one k_score computes: the
 // true maximum is always a candidate.  Float64 work falls from G to about one
 // dot per token.
-constexpr int kScoreMxQS = 128 + 2;  // float64 query row stride in LDS (rows on different banks)
+constexpr int kScoreMxQS = 128 + 8;  // bf16 query row stride in LDS (rows on different banks)
 constexpr int kScoreMxGroup = 8;     // consecutive tiles per workgroup, the next one in flight
 
 template <int G, bool P>
-__global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q,
-                                                  const double* __restrict__ q64, int hq,
+__global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, int hq,
                                                   Rows rows, Cand cand,
                                                   float* __restrict__ logit, int64_t cap_stride,
                                                   double scale) {
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q,
   constexpr int LOADS = kScoreTile * CPR / 256;
   constexpr float kErr = 1.0f / 32768.0f;  // 2^-15: four times the float32 summation bound
   __shared__ __attribute__((aligned(16))) unsigned char lds[kScoreTile * PAD];
-  __shared__ __attribute__((aligned(16))) double s_q[G][kScoreMxQS];
+  __shared__ __attribute__((aligned(16))) bf16_t s_q[G][kScoreMxQS];  // exact: widened per use
   __shared__ uint32_t s_cand[kScoreTile];
   const int hkv = gridDim.y, tid = threadIdx.x;
   const int nwg = gridDim.x * gridDim.y * gridDim.z;
@@ -340,7 +340,8 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q,
   };
   fetch(g0);
   const int64_t qrow = (int64_t)b * hq + (int64_t)h * G;
-  for (int i = tid; i < G * D; i += 256) s_q[i / D][i % D] = q64[qrow * D + i];
+  for (int i = tid; i < G * D / 8; i += 256)  // 16-byte pieces
+    *(v4u*)&s_q[i / (D / 8)][(i % (D / 8)) * 8] = *(const v4u*)(q + qrow * D + i * 8);
   const int w = tid >> 6, lane = tid & 63;
   const int qi = lane & 15, g4 = lane >> 4;
   v4u qb[4], qa[4];
@@ -393,15 +394,17 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q,
     while (mask) {
       const int i = __builtin_ctz(mask);
       mask &= mask - 1u;
-      const double* qh = &s_q[i][half * (D / 2)];
+      const bf16_t* qh = &s_q[i][half * (D / 2)];
       double acc = 0.0;
 #pragma unroll 1
       for (int c = 0; c < 8; ++c) {
         const v4u raw = *(const v4u*)(row + c * 16);
-        float f[8];
+        const v4u qr = *(const v4u*)(qh + c * 8);
+        float f[8], g[8];
         Elt<bf16_t>::unpack(raw, f);
+        Elt<bf16_t>::unpack(qr, g);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fma(qh[c * 8 + e], (double)f[e], acc);
+        for (int e = 0; e < 8; ++e) acc = fma((double)g[e], (double)f[e], acc);
       }
       const double other = __shfl_xor(acc, 32, 64);
       best = fmax(best, half ? other + acc : acc + other);
@@ -458,7 +461,10 @@ template <typename T, int D, int G, bool P>
 static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   const int64_t per_q = (int64_t)a.hq * D;
   const int64_t nq = (int64_t)a.B * a.window * per_q;
-  const int nqb = a.q_ready ? 0 : ceil_div(nq, kPrepThreads);
+  // the filter (G >= 8, bf16, d = 128, no metric array) reads the bf16 queries
+  constexpr bool kMx = sizeof(T) == 2 && D == 128 && G >= 8;
+  const bool mx = kMx && a.metric == nullptr && a.window == 1;
+  const int nqb = a.q_ready || mx ? 0 : ceil_div(nq, kPrepThreads);
   // with a metric array, one more block per (b, h) for the key sums
   const int nkb = a.metric != nullptr ? a.B * a.hkv : 0;
   if (nqb + nkb > 0) {
@@ -473,12 +479,12 @@ static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
   float* wdst = a.radius > 0 ? a.wx : a.l2;
   // the filter pays at G >= 8; at G = 4 the float64 dots of k_score already
   // hide behind its loads (0.195 vs 0.236 ms on the 16k headline shape)
-  if constexpr (sizeof(T) == 2 && D == 128 && G >= 8) {
-    if (a.metric == nullptr && a.window == 1) {
+  if constexpr (kMx) {
+    if (mx) {
       observe("k_score", st);
       hipLaunchKernelGGL((k_score_mx<G, P>),
                          dim3(ceil_div(a.max_cand, kScoreMxGroup * kScoreTile), a.hkv, a.B),
-                         dim3(256), 0, st, (const bf16_t*)a.q, a.q64, a.hq, a.rows, a.cand,
+                         dim3(256), 0, st, (const bf16_t*)a.q, a.hq, a.rows, a.cand,
                          a.logit, a.cap_stride, a.scale);
       return;
     }
