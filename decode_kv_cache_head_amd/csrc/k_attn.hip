@@ -31,7 +31,11 @@
 
 namespace hk {
 
+// Entries per workgroup tile: 256 for the dense and condensed tiers, 512
+// for the sparse tier (the large one, where longer per-wave runs keep more
+// loads in flight per workgroup start-up).  The four waves split a tile evenly.
 constexpr int kAttnTile = 256;
+constexpr int kSparseTile = 512;
 
 template <typename E, int D>
 struct Lay {
@@ -67,7 +71,7 @@ __device__ inline TileCounts tile_counts(const AttnArgs& a, int b, int h) {
   int ns = a.count[b * a.hkv + h];
   t.ns = ns < 0 ? 0 : (ns > a.sparse_cap ? a.sparse_cap : ns);
   t.ntd = (t.nd + kAttnTile - 1) / kAttnTile;
-  t.nts = (t.ns + kAttnTile - 1) / kAttnTile;
+  t.nts = (t.ns + kSparseTile - 1) / kSparseTile;
   t.ntc = (t.nc + kAttnTile - 1) / kAttnTile;
   t.first = 0;
   if (a.fused_tt > 0) {
@@ -78,7 +82,7 @@ __device__ inline TileCounts tile_counts(const AttnArgs& a, int b, int h) {
   return t;
 }
 
-// One wave, up to 64 entries starting at row r0 of `kr`/`vr`, in rounds of
+// One wave, wn entries starting at row r0 of `kr`/`vr`, in rounds of
 // 8 iterations x RPI rows.  Each round issues the K and the V loads of all
 // its rows first, then scores, then rescales the running (m, l, o) to the
 // new maximum and accumulates p * v.  CHUNK: float32 sums with counts.
@@ -491,24 +495,28 @@ constexpr bool kUseMx = !CHUNK && D == 128 && G >= 4 && sizeof(E) == 2;
 template <int D, int G, bool CHUNK, typename QT>
 constexpr bool kUseMxChunk = CHUNK && D == 128 && G >= 4 && sizeof(QT) == 2;
 
-// One tile of up to 256 entries: wave w takes entries [64 w, 64 w + 64).
-template <typename E, int D, int G, typename QT, bool CHUNK, bool P, bool IDX = false>
+// One tile of up to TILE entries: wave w takes entries [w RW, (w + 1) RW).
+template <typename E, int D, int G, typename QT, bool CHUNK, bool P, bool IDX = false,
+          int TILE = kAttnTile>
 __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr, const Rows& vr,
                                  int b, int h, int r0, int nrows, const int32_t* cc, float* s_m,
                                  float* s_l, float* s_o, float* part_out,
                                  const int32_t* idx = nullptr, int idx_max = 0,
                                  int gap_at = 0, int gap_len = 0) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int wn = nrows - w * 64;
-  wn = wn < 0 ? 0 : (wn > 64 ? 64 : wn);
+  // entries per wave: the tile's rows spread evenly over the four waves in
+  // whole 32-entry steps, so a short tier does not fall on one wave
+  const int RW = min(TILE / 4, ((nrows + 127) >> 7) << 5);
+  int wn = nrows - w * RW;
+  wn = wn < 0 ? 0 : (wn > RW ? RW : wn);
   if constexpr (kUseMx<E, D, G, CHUNK> || kUseMxChunk<D, G, CHUNK, QT>) {
     float m, l;
     f32x4_t acc[8];
     if constexpr (CHUNK)
-      wave_attn_mx_chunk<G>((const bf16_t*)qg, kr, vr, b, h, r0 + w * 64, wn, cc,
+      wave_attn_mx_chunk<G>((const bf16_t*)qg, kr, vr, b, h, r0 + w * RW, wn, cc,
                             (float)a.scale, m, l, acc);
     else
-      wave_attn_mx<G, P, IDX>((const bf16_t*)qg, kr, vr, b, h, r0 + w * 64, wn, idx, idx_max,
+      wave_attn_mx<G, P, IDX>((const bf16_t*)qg, kr, vr, b, h, r0 + w * RW, wn, idx, idx_max,
                               gap_at, gap_len, (float)a.scale, m, l, acc);
     const int i = lane & 15, g = lane >> 4;
     if (i < G) {
@@ -527,7 +535,7 @@ __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr
   } else {
     using L = Lay<E, D>;
     float m[G], l[G], o[G][L::EPL];
-    wave_attn<E, D, G, QT, CHUNK, P, IDX>(qg, kr, vr, b, h, r0 + w * 64, wn, cc, idx, idx_max,
+    wave_attn<E, D, G, QT, CHUNK, P, IDX>(qg, kr, vr, b, h, r0 + w * RW, wn, cc, idx, idx_max,
                                           gap_at, gap_len, (float)a.scale, m, l, o);
     if (lane < L::LPR) {
 #pragma unroll
@@ -570,28 +578,28 @@ __device__ inline void attn_tiles(const AttnArgs& a) {
                                     nullptr, s_m, s_l, s_o, part_out, nullptr, 0, tc.gap_at,
                                     tc.gap_len);
   } else if (PART != 2 && x < tc.ntd + tc.nts) {
-    const int r0 = (x - tc.ntd) * kAttnTile;
+    const int r0 = (x - tc.ntd) * kSparseTile;
+    const int ns = min(kSparseTile, tc.ns - r0);
     if (a.mode && a.mode[bh] == HARDKV_MODE_SPARSE) {
       // sparse loading: the kept rows stay in the cache, found through pos
-      tile_attn<T, D, G, T, false, P, true>(a, qg, a.dk, a.dv, b, h, r0,
-                                            min(kAttnTile, tc.ns - r0), nullptr, s_m, s_l, s_o,
-                                            part_out, a.pos + bh * a.sparse_cap, a.ctx_cap - 1);
+      tile_attn<T, D, G, T, false, P, true, kSparseTile>(a, qg, a.dk, a.dv, b, h, r0, ns, nullptr,
+                                                         s_m, s_l, s_o, part_out,
+                                                         a.pos + bh * a.sparse_cap, a.ctx_cap - 1);
     } else if (a.offset) {
       // packed tier: this head's slots start at row offset[b][h]
       Rows sk = a.sk, sv = a.sv;
       sk.base += (int64_t)a.offset[bh] * sk.row_bytes;
       sv.base += (int64_t)a.offset[bh] * sv.row_bytes;
       sk.region = sv.region = 0;
-      tile_attn<T, D, G, T, false, false>(a, qg, sk, sv, b, h, r0, min(kAttnTile, tc.ns - r0),
-                                          nullptr, s_m, s_l, s_o, part_out);
+      tile_attn<T, D, G, T, false, false, false, kSparseTile>(a, qg, sk, sv, b, h, r0, ns, nullptr,
+                                                              s_m, s_l, s_o, part_out);
     } else if constexpr (PS) {
-      tile_attn<T, D, G, T, false, true>(a, qg, a.sk, a.sv, a.sk.tb(b, h), a.sk.th(h), r0,
-                                         min(kAttnTile, tc.ns - r0), nullptr, s_m, s_l, s_o,
-                                         part_out);
+      tile_attn<T, D, G, T, false, true, false, kSparseTile>(a, qg, a.sk, a.sv, a.sk.tb(b, h),
+                                                             a.sk.th(h), r0, ns, nullptr, s_m,
+                                                             s_l, s_o, part_out);
     } else {
-      tile_attn<T, D, G, T, false, false>(a, qg, a.sk, a.sv, b, h, r0,
-                                          min(kAttnTile, tc.ns - r0), nullptr, s_m, s_l, s_o,
-                                          part_out);
+      tile_attn<T, D, G, T, false, false, false, kSparseTile>(a, qg, a.sk, a.sv, b, h, r0, ns,
+                                                              nullptr, s_m, s_l, s_o, part_out);
     }
   } else if constexpr (PART != 1) {
     const int r0 = (x - tc.ntd - tc.nts) * kAttnTile;
@@ -657,8 +665,11 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 }
 
 // W: dense rows at most (window plus sinks)
+// (the fused compaction's tiles hold at least 576 candidates, so they fit in
+// the sparse tier's slots too)
 int attn_max_tiles(int W, int sparse_cap, int chunk_cap) {
-  return ceil_div(W, kAttnTile) + ceil_div(sparse_cap, kAttnTile) + ceil_div(chunk_cap, kAttnTile);
+  return ceil_div(W, kAttnTile) + ceil_div(sparse_cap, kSparseTile) +
+         ceil_div(chunk_cap, kAttnTile);
 }
 
 template <typename T, int D, int G, bool P>

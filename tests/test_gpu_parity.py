@@ -15,8 +15,8 @@ import oracle as O
 from decode_kv_cache_head_amd import hardkv as H
 from decode_kv_cache_head_amd import synth as S
 
-from parity import (check_all_heads_invariants, check_case, desc_for, oracle_head, run_stages,
-                    run_step)
+from parity import (cache_of, check_all_heads_invariants, check_case, desc_for, oracle_head,
+                    run_stages, run_step)
 
 pytestmark = pytest.mark.gpu
 
@@ -147,20 +147,27 @@ ROW_TILE_CASES = [
 @pytest.mark.parametrize("i", range(len(ROW_TILE_CASES)))
 def test_row_tiles_ragged_and_peaked_full_attention(gpu, i):
     """bf16 rows with d = 128 and G >= 4 (the matrix-core attention): tier
-    lengths that end at every offset of a 32-entry step, a 64-entry wave and a
-    256-entry tile, flat and peaked heads (Zipf-planted keys with logits up to
-    24 above the rest).  p = 1 keeps every token, so the output is full
-    attention (float64 SDPA).  Bound 1e-4 of max|o|: each weight enters the
-    value product as a bf16 pair whose sum is within 2^-18 of it, products of
-    bf16 values are exact in float32 and the float32 sums run over at most
-    1300 terms."""
+    lengths that end at every offset of a 32-entry step, a 64- and 128-entry
+    wave and a 256- and 512-entry tile, flat and peaked heads (Zipf-planted
+    keys with logits up to 24 above the rest).  p = 1 keeps every token, so
+    the output is full attention (float64 SDPA), both from the step (the
+    kept rows attended inside the compaction pass) and from a standalone
+    attention call over the step's tiers (the kept rows in 512-entry tiles).
+    Bound 1e-4 of max|o|: each weight enters the value product as a bf16 pair
+    whose sum is within 2^-18 of it, products of bf16 values are exact in
+    float32 and the float32 sums run over at most 1300 terms."""
     W = 64
-    T = (40,) + tuple(W + n for n in (1, 31, 32, 33, 63, 65, 255, 257, 1000, 1240))
+    T = (40,) + tuple(W + n for n in (1, 31, 32, 33, 63, 65, 127, 129, 255, 257, 511, 513, 1000,
+                                      1240))
     w = small(f"rowtiles{i}", B=len(T), T=T, W=W, p=1.0, **ROW_TILE_CASES[i])
     say("row tiles", w)
     case = S.make_case(w, gpu)
     desc = desc_for(case)
-    g = run_step(case, desc)
+    ws = H.alloc_workspace(desc, gpu)
+    g = run_step(case, desc, ws=ws)
+    alone = torch.full_like(g["out"], float("nan"))
+    H.decode_attn(desc, case.q, cache_of(case), g["tiers"], alone, ws)
+    torch.cuda.synchronize()
     worst = 0.0
     for b in range(w.B):
         for h in range(w.Hkv):
@@ -171,10 +178,11 @@ def test_row_tiles_ragged_and_peaked_full_attention(gpu, i):
             ref = torch.nn.functional.scaled_dot_product_attention(
                 q[None, :, None], K[None, None].expand(1, G, -1, -1).contiguous(),
                 V[None, None].expand(1, G, -1, -1).contiguous())[0, :, 0]
-            o = g["out"][b, h * G:(h + 1) * G].double().cpu()
-            err = ((o - ref).abs().amax(1) / ref.abs().amax(1)).max().item()
-            worst = max(worst, err)
-            assert err <= 1e-4, (b, h, err)
+            for name, res in (("step", g["out"]), ("decode_attn", alone)):
+                o = res[b, h * G:(h + 1) * G].double().cpu()
+                err = ((o - ref).abs().amax(1) / ref.abs().amax(1)).max().item()
+                worst = max(worst, err)
+                assert err <= 1e-4, (name, b, h, err)
     say("worst relative error", worst)
 
 
