@@ -31,11 +31,10 @@
 
 namespace hk {
 
-// Entries per workgroup tile: 256 for the dense and condensed tiers, 512
-// for the sparse tier (the large one, where longer per-wave runs keep more
-// loads in flight per workgroup start-up).  The four waves split a tile evenly.
-constexpr int kAttnTile = 256;
-constexpr int kSparseTile = 512;
+// Entries per workgroup tile of any tier.  The four waves split a tile
+// evenly, so on a long tier each wave runs four 32-entry steps per
+// workgroup start-up.
+constexpr int kAttnTile = 512;
 
 template <typename E, int D>
 struct Lay {
@@ -71,7 +70,7 @@ __device__ inline TileCounts tile_counts(const AttnArgs& a, int b, int h) {
   int ns = a.count[b * a.hkv + h];
   t.ns = ns < 0 ? 0 : (ns > a.sparse_cap ? a.sparse_cap : ns);
   t.ntd = (t.nd + kAttnTile - 1) / kAttnTile;
-  t.nts = (t.ns + kSparseTile - 1) / kSparseTile;
+  t.nts = (t.ns + kAttnTile - 1) / kAttnTile;
   t.ntc = (t.nc + kAttnTile - 1) / kAttnTile;
   t.first = 0;
   if (a.fused_tt > 0) {
@@ -495,9 +494,8 @@ constexpr bool kUseMx = !CHUNK && D == 128 && G >= 4 && sizeof(E) == 2;
 template <int D, int G, bool CHUNK, typename QT>
 constexpr bool kUseMxChunk = CHUNK && D == 128 && G >= 4 && sizeof(QT) == 2;
 
-// One tile of up to TILE entries: wave w takes entries [w RW, (w + 1) RW).
-template <typename E, int D, int G, typename QT, bool CHUNK, bool P, bool IDX = false,
-          int TILE = kAttnTile>
+// One tile of up to kAttnTile entries: wave w takes entries [w RW, (w + 1) RW).
+template <typename E, int D, int G, typename QT, bool CHUNK, bool P, bool IDX = false>
 __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr, const Rows& vr,
                                  int b, int h, int r0, int nrows, const int32_t* cc, float* s_m,
                                  float* s_l, float* s_o, float* part_out,
@@ -506,7 +504,7 @@ __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // entries per wave: the tile's rows spread evenly over the four waves in
   // whole 32-entry steps, so a short tier does not fall on one wave
-  const int RW = min(TILE / 4, ((nrows + 127) >> 7) << 5);
+  const int RW = min(kAttnTile / 4, ((nrows + 127) >> 7) << 5);
   int wn = nrows - w * RW;
   wn = wn < 0 ? 0 : (wn > RW ? RW : wn);
   if constexpr (kUseMx<E, D, G, CHUNK> || kUseMxChunk<D, G, CHUNK, QT>) {
@@ -578,28 +576,27 @@ __device__ inline void attn_tiles(const AttnArgs& a) {
                                     nullptr, s_m, s_l, s_o, part_out, nullptr, 0, tc.gap_at,
                                     tc.gap_len);
   } else if (PART != 2 && x < tc.ntd + tc.nts) {
-    const int r0 = (x - tc.ntd) * kSparseTile;
-    const int ns = min(kSparseTile, tc.ns - r0);
+    const int r0 = (x - tc.ntd) * kAttnTile;
+    const int ns = min(kAttnTile, tc.ns - r0);
     if (a.mode && a.mode[bh] == HARDKV_MODE_SPARSE) {
       // sparse loading: the kept rows stay in the cache, found through pos
-      tile_attn<T, D, G, T, false, P, true, kSparseTile>(a, qg, a.dk, a.dv, b, h, r0, ns, nullptr,
-                                                         s_m, s_l, s_o, part_out,
-                                                         a.pos + bh * a.sparse_cap, a.ctx_cap - 1);
+      tile_attn<T, D, G, T, false, P, true>(a, qg, a.dk, a.dv, b, h, r0, ns, nullptr, s_m, s_l,
+                                            s_o, part_out, a.pos + bh * a.sparse_cap,
+                                            a.ctx_cap - 1);
     } else if (a.offset) {
       // packed tier: this head's slots start at row offset[b][h]
       Rows sk = a.sk, sv = a.sv;
       sk.base += (int64_t)a.offset[bh] * sk.row_bytes;
       sv.base += (int64_t)a.offset[bh] * sv.row_bytes;
       sk.region = sv.region = 0;
-      tile_attn<T, D, G, T, false, false, false, kSparseTile>(a, qg, sk, sv, b, h, r0, ns, nullptr,
-                                                              s_m, s_l, s_o, part_out);
+      tile_attn<T, D, G, T, false, false>(a, qg, sk, sv, b, h, r0, ns, nullptr, s_m, s_l, s_o,
+                                          part_out);
     } else if constexpr (PS) {
-      tile_attn<T, D, G, T, false, true, false, kSparseTile>(a, qg, a.sk, a.sv, a.sk.tb(b, h),
-                                                             a.sk.th(h), r0, ns, nullptr, s_m,
-                                                             s_l, s_o, part_out);
+      tile_attn<T, D, G, T, false, true>(a, qg, a.sk, a.sv, a.sk.tb(b, h), a.sk.th(h), r0, ns,
+                                         nullptr, s_m, s_l, s_o, part_out);
     } else {
-      tile_attn<T, D, G, T, false, false, false, kSparseTile>(a, qg, a.sk, a.sv, b, h, r0, ns,
-                                                              nullptr, s_m, s_l, s_o, part_out);
+      tile_attn<T, D, G, T, false, false>(a, qg, a.sk, a.sv, b, h, r0, ns, nullptr, s_m, s_l,
+                                          s_o, part_out);
     }
   } else if constexpr (PART != 1) {
     const int r0 = (x - tc.ntd - tc.nts) * kAttnTile;
@@ -668,8 +665,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // (the fused compaction's tiles hold at least 576 candidates, so they fit in
 // the sparse tier's slots too)
 int attn_max_tiles(int W, int sparse_cap, int chunk_cap) {
-  return ceil_div(W, kAttnTile) + ceil_div(sparse_cap, kSparseTile) +
-         ceil_div(chunk_cap, kAttnTile);
+  return ceil_div(W, kAttnTile) + ceil_div(sparse_cap, kAttnTile) + ceil_div(chunk_cap, kAttnTile);
 }
 
 template <typename T, int D, int G, bool P>
