@@ -294,11 +294,13 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
 // Logit-only launches with bf16 keys, d = 128 and G >= 8: the matrix cores
 // find each token's winning query heads, float64 decides among them.
 //   1. S = K Q^T and A = |K| |Q|^T as 16x16x32 bf16 MFMA products; the
-//      products are exact in float32, so each float32 dot is within
-//      127 * 2^-24 * A of the true one (recursive summation of 128 terms;
-//      the kernel allows four times that, 2^-15 A).
+//      products are exact in float32 (inside its range), so each float32
+//      dot is within 127 * 2^-24 * A of the true one (recursive summation
+//      of 128 terms; the kernel allows four times that, 2^-15 A).
 //   2. Per token, every query head whose float32 dot is within 2 * 2^-15 *
-//      max A of the largest is a candidate (usually one head).
+//      max A of the largest is a candidate (usually one head).  Where that
+//      bound does not hold (a product beyond float32's range, or dots so
+//      small that subnormal products matter) every head is a candidate.
 //   3. Two lanes per token (one per half of d, as in k_score) take the
 //      float64 dot of each candidate from the exact inputs (bf16 queries and
 //      keys from LDS, widened in registers), in k_score's order, and keep
@@ -382,7 +384,12 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
         const float v = qi < G ? sd[cc] : -INFINITY;
         const float m = row_max16(v);
         const float e = row_max16(qi < G ? kErr * sa[cc] : 0.f);
-        const unsigned long long bal = __ballot(qi < G && v >= m - 2.f * e);
+        // the band is a bound only inside float32's range: no sum of |q k|
+        // overflows (e finite), and subnormal products, at most 2^-126 off
+        // each when flushed, stay far inside it (e >= 2^-115); otherwise
+        // every head is a candidate and the float64 dots decide
+        const bool all = !(e < INFINITY) || e < 0x1p-115f;
+        const unsigned long long bal = __ballot(qi < G && (all || v >= m - 2.f * e));
         if (qi == 0) s_cand[32 * w + 16 * c + 4 * g4 + cc] = (uint32_t)(bal >> (16 * g4)) & 0xffffu;
       }
     }

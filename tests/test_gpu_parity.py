@@ -249,6 +249,49 @@ def test_score_filter_with_tied_and_near_tied_query_heads(gpu):
     assert rep["logit_1ulp"] <= 0.001 * rep["candidates"]
 
 
+@pytest.mark.parametrize("e", [63, -60])
+def test_score_filter_outside_float32_range(gpu, e):
+    """The matrix-core score filter with queries and keys scaled by 2^e
+    (exact in bf16).  At e = 63 the products reach 2^126 and their float32
+    sums overflow; at e = -60 the products are float32 subnormals (2^-120).
+    Either way the filter's float32 band is no bound, every head must stay a
+    candidate, and the logits must equal the oracle's float64 maximum (at
+    most 1 ulp, on a tiny fraction; equal infinities where the maximum
+    leaves float32's range)."""
+    w = small(f"scorerange{e}", Hq=16, Hkv=2, B=2, T=(3000, 700), p=0.9)
+    case = S.make_case(w, gpu)
+    f = 2.0 ** e
+    case.q.mul_(f)
+    case.k.mul_(f)
+    desc = desc_for(case)
+    shape = (w.B, w.Hkv, desc.sparse_cap)
+    logit = torch.full(shape, float("nan"), device=gpu)
+    l2 = torch.full(shape, float("nan"), device=gpu)
+    ws = H.alloc_workspace(desc, gpu)
+    H.score(desc, case.q, cache_of(case), case.metric, logit, l2, ws)
+    torch.cuda.synchronize()
+    G, n_ulp, n_all = w.G, 0, 0
+    for b in range(w.B):
+        A = max(w.T[b] - w.W, 0)
+        for h in range(w.Hkv):
+            q = case.q[b, h * G:(h + 1) * G].float().cpu().numpy()
+            K = S.head_rows(case, b, h, "k").float().cpu().numpy()[:A]
+            with np.errstate(over="ignore"):
+                ref, _ = O.score_head(q, K)
+            got = logit[b, h, :A].cpu().numpy()
+            inf = np.isinf(ref)
+            assert np.array_equal(np.isinf(got), inf), (b, h)
+            assert np.array_equal(got[inf], ref[inf]), (b, h)
+            ia = got[~inf].view(np.int32).astype(np.int64)
+            ib = ref[~inf].view(np.int32).astype(np.int64)
+            diff = np.abs(ia - ib)
+            assert diff.max(initial=0) <= 1, (b, h, diff.max())
+            n_ulp += int((diff == 1).sum())
+            n_all += A
+    say("1-ulp logits", n_ulp, "of", n_all)
+    assert n_ulp <= 0.001 * n_all
+
+
 def test_edge_cases(gpu):
     # every sequence shorter than the window, a single-token context, and a
     # context exactly one token past the window
