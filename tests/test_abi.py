@@ -221,8 +221,9 @@ def test_sinks_and_merge_errors_before_launch():
         assert lib.hardkv_step_inplace(ctypes.byref(desc), fake, fake, fake, None,
                                        ctypes.byref(state), fake, fake, H.workspace_size(desc),
                                        st) == H.ERR_INVALID_ARG
-    # sinks add dense tiles: at equal capacities the workspace grows with them
-    assert H.workspace_size(base_desc(sinks=300, sparse_cap=936, chunk_cap=30)) > \
+    # sinks add dense tiles (64 + 500 rows: two 512-entry tiles instead of
+    # one): at equal capacities the workspace grows with them
+    assert H.workspace_size(base_desc(sinks=500, sparse_cap=936, chunk_cap=30)) > \
         H.workspace_size(base_desc())
 
 
