@@ -249,16 +249,18 @@ def test_score_filter_with_tied_and_near_tied_query_heads(gpu):
     assert rep["logit_1ulp"] <= 0.001 * rep["candidates"]
 
 
+@pytest.mark.parametrize("Hq", [8, 16])
 @pytest.mark.parametrize("e", [63, -60])
-def test_score_filter_outside_float32_range(gpu, e):
-    """The matrix-core score filter with queries and keys scaled by 2^e
-    (exact in bf16).  At e = 63 the products reach 2^126 and their float32
-    sums overflow; at e = -60 the products are float32 subnormals (2^-120).
-    Either way the filter's float32 band is no bound, every head must stay a
-    candidate, and the logits must equal the oracle's float64 maximum (at
-    most 1 ulp, on a tiny fraction; equal infinities where the maximum
-    leaves float32's range)."""
-    w = small(f"scorerange{e}", Hq=16, Hkv=2, B=2, T=(3000, 700), p=0.9)
+def test_score_filter_outside_float32_range(gpu, e, Hq):
+    """Queries and keys scaled by 2^e (exact in bf16).  At e = 63 the
+    products reach 2^126 and their float32 sums overflow; at e = -60 the
+    products are float32 subnormals (2^-120).  At G = 8 (the matrix-core
+    filter) the filter's float32 band is then no bound and every head must
+    stay a candidate; at G = 4 the score is float64 throughout.  Either way
+    the logits must equal the oracle's float64 maximum (at most 1 ulp, on a
+    tiny fraction; equal infinities where the maximum leaves float32's
+    range)."""
+    w = small(f"scorerange{e}_{Hq}", Hq=Hq, Hkv=2, B=2, T=(3000, 700), p=0.9)
     case = S.make_case(w, gpu)
     f = 2.0 ** e
     case.q.mul_(f)
