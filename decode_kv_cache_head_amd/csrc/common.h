@@ -132,9 +132,19 @@ __device__ inline float cval(float x, double shift, double scale) {
 }
 
 // Fixed-point weight round(exp(c - m) * 2^47); exp(c - m) <= 1.
-__device__ inline uint64_t wfix(float c, double m) {
+__device__ inline uint64_t wfix(float c, double m, double scale) {
   const double w = exp((double)c - m);
-  return (uint64_t)__double2ull_rn(w * 140737488355328.0);
+  return (uint64_t)__double2ull_rn(w * scale);
+}
+
+// Fixed-point scale of the selection masses for heads of up to n_max
+// candidates: each weight exp(c - m) <= 1 becomes round(w * 2^s) with
+// s = min(47, 63 - ceil(log2 n_max)), so a head's total stays within 2^63
+// (2^-47 units up to 65536 candidates).
+inline double mass_scale(int n_max) {
+  int l = 0;
+  while (l < 31 && (1 << l) < n_max) ++l;
+  return ldexp(1.0, 63 - l < 47 ? 63 - l : 47);
 }
 
 // ------------------------------------------------------ XCD placement ----

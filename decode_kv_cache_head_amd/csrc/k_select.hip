@@ -7,7 +7,8 @@
 //   heads, then m = max c and Z = sum exp(c - m).
 // select: one 1024-thread workgroup per (b, h).  Radix select by MASS on the
 //   order-preserving 32-bit key of the float32 calibrated value: 11/11/10-bit
-//   passes, each accumulating per-bin mass in LDS as 2^-47 fixed point
+//   passes, each accumulating per-bin mass in LDS in fixed point (2^-47
+//   units up to 65536 candidates per head, coarser beyond: mass_scale)
 //   (integer atomics, so the result does not depend on the order of the
 //   additions).  The cutoff key K* is the bin where the mass accumulated from
 //   the top first reaches ceil(p * Z); the tokens tied at K* are taken lowest
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(256) void k_calibrate(Cand cand, const int8_t* __re
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 
-// ceil(p * Z) exactly, p a float in (0, 1), Z < 2^63.
+// ceil(p * Z) exactly, p a float in (0, 1), Z <= 2^63.
 __device__ inline uint64_t ceil_mul(float p, uint64_t Z) {
   int ex;
   const float f = frexpf(p, &ex);                      // p = f * 2^ex, f in [0.5, 1)
@@ -293,8 +294,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
                                                         const float* __restrict__ l2,
                                                         int64_t cap_stride,
                                                         const double* __restrict__ stats,
-                                                        float top_p, uint8_t* __restrict__ mask,
-                                                        CountOut co) {
+                                                        float top_p, double wscale,
+                                                        uint8_t* __restrict__ mask, CountOut co) {
   __shared__ SelShared S;
   const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
   const int n = cand.n(b, h);
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   __syncthreads();
   for (int t = tid; t < n; t += kSelThreads) {
     const float c = cv(t);
-    const uint64_t w = wfix(c, m);
+    const uint64_t w = wfix(c, m, wscale);
     if (w) atomicAdd(&S.hist[hslot<2048>(okey(c) >> 21)], (unsigned long long)w);
   }
   __syncthreads();
@@ -338,7 +339,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
     const float c = cv(t);
     const uint32_t k = okey(c);
     if ((k >> 21) == b1)
-      atomicAdd(&S.hist[hslot<2048>((k >> 10) & 2047u)], (unsigned long long)wfix(c, m));
+      atomicAdd(&S.hist[hslot<2048>((k >> 10) & 2047u)],
+                (unsigned long long)wfix(c, m, wscale));
   }
   __syncthreads();
   if (tid < 64) find_bin<2048>(S, false, top_p);
@@ -356,7 +358,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   for (int t = tid; t < n; t += kSelThreads) {
     const float c = cv(t);
     const uint32_t k = okey(c);
-    if ((k >> 10) == pre) atomicAdd(&S.hist[hslot<1024>(k & 1023u)], (unsigned long long)wfix(c, m));
+    if ((k >> 10) == pre)
+      atomicAdd(&S.hist[hslot<1024>(k & 1023u)], (unsigned long long)wfix(c, m, wscale));
   }
   __syncthreads();
   if (tid < 64) find_bin<1024>(S, false, top_p);
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   const uint32_t kstar = (pre << 10) | S.bin;
   above += S.above;
   // all tokens tied at K* carry the same weight; take r of them
-  const unsigned long long wstar = wfix(okey_inv(kstar), m);
+  const unsigned long long wstar = wfix(okey_inv(kstar), m, wscale);
   const unsigned long long need = target - above;
   const unsigned long long r = (need + wstar - 1) / wstar;
 
@@ -418,7 +421,7 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
                                                         const float* __restrict__ l2,
                                                         int64_t cap_stride,
                                                         double* __restrict__ stats, float top_p,
-                                                        uint8_t* __restrict__ mask,
+                                                        double wscale, uint8_t* __restrict__ mask,
                                                         CountOut co, int calib) {
   __shared__ SelShared S;
   // fixed-point weight of token tid + 1024 i at [i][tid], from pass 1 on
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
     if (tid + kSelThreads * i < n) {
       const double wd = exp((double)c[i] - m);
       Z += wd;
-      w = (uint64_t)__double2ull_rn(wd * 140737488355328.0);  // = wfix(c, m)
+      w = (uint64_t)__double2ull_rn(wd * wscale);  // = wfix(c, m, wscale)
       if (w) atomicAdd(&S.hist[hslot<2048>(okey(c[i]) >> 21)], (unsigned long long)w);
     }
     s_w[i * kSelThreads + tid] = w;
@@ -582,7 +585,7 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   __syncthreads();
   const uint32_t kstar = (pre << 10) | S.bin;
   above += S.above;
-  const unsigned long long wstar = wfix(okey_inv(kstar), m);
+  const unsigned long long wstar = wfix(okey_inv(kstar), m, wscale);
   const unsigned long long need = target - above;
   const unsigned long long r = (need + wstar - 1) / wstar;
   // every token tied at K* has weight wstar, so the bin holds mass / wstar of
@@ -731,10 +734,12 @@ void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st) {
   const dim3 grid(a.hkv, a.B), blk(kSelThreads);
   if (max_cand <= 4 * kSelThreads)
     hipLaunchKernelGGL(k_calsel<4>, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2,
-                       a.cap_stride, a.stats, a.top_p, a.mask, count_out(a), a.calib);
+                       a.cap_stride, a.stats, a.top_p, mass_scale(a.cand.cap), a.mask,
+                       count_out(a), a.calib);
   else
     hipLaunchKernelGGL(k_calsel<16>, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2,
-                       a.cap_stride, a.stats, a.top_p, a.mask, count_out(a), a.calib);
+                       a.cap_stride, a.stats, a.top_p, mass_scale(a.cand.cap), a.mask,
+                       count_out(a), a.calib);
 }
 
 void launch_calibrate(const SelectArgs& a, hipStream_t st) {
@@ -746,7 +751,8 @@ void launch_calibrate(const SelectArgs& a, hipStream_t st) {
 void launch_select(const SelectArgs& a, hipStream_t st) {
   observe("k_select", st);
   hipLaunchKernelGGL(k_select, dim3(a.hkv, a.B), dim3(kSelThreads), 0, st, a.cand, a.metric,
-                     a.logit, a.l2, a.cap_stride, (const double*)a.stats, a.top_p, a.mask, count_out(a));
+                     a.logit, a.l2, a.cap_stride, (const double*)a.stats, a.top_p,
+                     mass_scale(a.cand.cap), a.mask, count_out(a));
 }
 
 }  // namespace hk

@@ -285,7 +285,8 @@ int hardkv_calibrate(const hardkv_desc* desc, const int32_t* ctx_len, const int8
 /* Calibrated Top-p selection (section 2.A, Tier 2; section 2.B, Outcome).
  * Ranks the aged tokens by c (highest first, equal values lower position first)
  * and keeps the smallest prefix whose mass sum exp(c - m) reaches top_p * Z.
- * Masses are accumulated exactly in 2^-47 fixed point.
+ * Masses are accumulated exactly in fixed point: 2^-47 units for heads of up to
+ * 65536 candidates, 2^-(63 - ceil(log2 n)) for a larger candidate capacity n.
  *   mask:  [B][Hkv][sparse_cap] uint8, 1 = kept, for t < A_b (later bytes unspecified)
  *   count: [B][Hkv] int32 kept tokens. */
 int hardkv_topp_select(const hardkv_desc* desc, const int32_t* ctx_len, const int8_t* metric,

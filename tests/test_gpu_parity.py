@@ -294,6 +294,28 @@ def test_score_filter_outside_float32_range(gpu, e, Hq):
     assert n_ulp <= 0.001 * n_all
 
 
+def test_selection_beyond_65536_candidates(gpu):
+    """Heads of 139936 candidates (more than 2^17): the selection's
+    fixed-point masses take 2^-45 units there, so a head's total stays within
+    2^63.  Sequence 0's keys are one row repeated: every weight is 1 (in
+    2^-47 units the total would pass 2^64) and the kept set is the first
+    ceil(p n) positions.  Sequence 1 is N(0, 1).  Both against the oracle."""
+    w = small("longheads", B=2, T=(140000, 140000), p=0.9)
+    case = S.make_case(w, gpu)
+    for h in range(w.Hkv):
+        case.k[0, h, :w.T[0]] = case.k[0, h, :1].clone()
+    desc = desc_for(case)
+    g = run_stages(case, desc)
+    rep = check_case(case, g, w.p)
+    say(rep)
+    n = w.T[0] - w.W
+    k = math.ceil(float(np.float32(w.p)) * n)
+    for h in range(w.Hkv):
+        assert int(g["tiers"].count[0, h]) == k
+        pos = g["tiers"].pos[0, h, :k].cpu().numpy()
+        assert np.array_equal(pos, np.arange(k)), h
+
+
 def test_edge_cases(gpu):
     # every sequence shorter than the window, a single-token context, and a
     # context exactly one token past the window
