@@ -150,7 +150,9 @@ typedef struct hardkv_desc {
 /* The KV cache of one layer.
  *   contiguous: k, v = [B][Hkv][ctx_cap][d]
  *   paged:      k, v = [num_blocks][Hkv][block_size][d]; token t of sequence b,
- *               head h is row (t % block_size) of block block_table[b][t / block_size]
+ *               head h is row (t % block_size) of block block_table[b][t / block_size];
+ *               the entries covering t < T_b must be block ids of k and v (they are
+ *               read on the device and not checked: the pool's size is not passed)
  *   ctx_len:    [B] int32, 1 <= T_b <= ctx_cap (clamped on the device). */
 typedef struct hardkv_cache {
   const void* k;
