@@ -309,7 +309,12 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
 // true maximum is always a candidate.  Float64 work falls from G to about one
 // dot per token.
 constexpr int kScoreMxQS = 128 + 8;  // bf16 query row stride in LDS (rows on different banks)
-constexpr int kScoreMxGroup = 8;     // consecutive tiles per workgroup, the next one in flight
+// Workgroups per (b, h): each takes one contiguous run of the head's tiles,
+// split by the head's actual candidate count (read on the device), with the
+// next tile in flight.  A pool far below its capacity then dispatches few
+// idle workgroups (fixed groups of the capacity would leave most of the
+// grid idle).
+constexpr int kScoreMxSplit = 8;
 
 template <int G, bool P>
 __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, int hq,
@@ -328,8 +333,11 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
   const int id = xcd_contiguous(L, nwg);
   const int grp = id % gridDim.x, h = (id / gridDim.x) % hkv, b = id / (gridDim.x * hkv);
   const int n = cand.n(b, h);
-  const int g0 = grp * kScoreMxGroup * kScoreTile;
-  if (g0 >= n) return;
+  const int ntiles = (n + kScoreTile - 1) / kScoreTile;
+  const int per = (ntiles + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int tbeg = grp * per, tcnt = min(per, ntiles - tbeg);
+  if (tcnt <= 0) return;
+  const int g0 = tbeg * kScoreTile;
   const int rb = rows.tb(b, h), rh = rows.th(h);
   v4u buf[LOADS];
   auto fetch = [&](int t0) {
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
   const int tok = 32 * w + (lane & 31), half = lane >> 5;
   float* out = logit + ((int64_t)b * hkv + h) * cap_stride;
 #pragma unroll 1
-  for (int k = 0; k < kScoreMxGroup; ++k) {
+  for (int k = 0; k < tcnt; ++k) {
     const int t0 = g0 + k * kScoreTile;  // uniform over the workgroup
     if (t0 >= n) break;
     if (k) __syncthreads();  // the previous tile's LDS reads are done
@@ -366,7 +374,7 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
     }
     __syncthreads();
     // the next tile's rows are in flight while this one is scored
-    if (k + 1 < kScoreMxGroup && t0 + kScoreTile < n) fetch(t0 + kScoreTile);
+    if (k + 1 < tcnt) fetch(t0 + kScoreTile);
     // 1-2: wave w filters tokens [32 w, 32 w + 32), two 16-row products
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -490,7 +498,7 @@ static void launch_score_t(const ScoreArgs& a, hipStream_t st) {
     if (mx) {
       observe("k_score", st);
       hipLaunchKernelGGL((k_score_mx<G, P>),
-                         dim3(ceil_div(a.max_cand, kScoreMxGroup * kScoreTile), a.hkv, a.B),
+                         dim3(min(kScoreMxSplit, ceil_div(a.max_cand, kScoreTile)), a.hkv, a.B),
                          dim3(256), 0, st, (const bf16_t*)a.q, a.hq, a.rows, a.cand,
                          a.logit, a.cap_stride, a.scale);
       return;
