@@ -2,10 +2,11 @@
 // arXiv abstract; gist.science technical summary, sections 2.A and 3).
 //
 // Split-K: the entries of one (b, h) -- dense rows, sparse (rewritten) rows
-// and non-empty condensed chunks -- are cut into 256-entry tiles; one
+// and non-empty condensed chunks -- are cut into 512-entry tiles; one
 // workgroup handles one tile for all G query heads of the KV head, so each
-// K/V row is read from HBM once per step (GQA packing).  Every wave takes 64
-// entries: a row is spread over LPR lanes that each load one 16-byte piece
+// K/V row is read from HBM once per step (GQA packing).  The four waves
+// share a tile evenly (up to 128 entries each).  On the vector path a row
+// is spread over LPR lanes that each load one 16-byte piece
 // (coalesced), the G dot products are reduced across those lanes with DPP,
 // scores go to LDS, then the V rows are streamed and accumulated with the
 // wave's max subtracted.  The four waves combine in LDS and write one
