@@ -99,9 +99,18 @@ def test_workspace_size():
     assert H.workspace_size(big) > n
 
 
-def _call_all(desc, ws_bytes, null_q=False):
-    """Calls every entry point with fake (never dereferenced) device
-    pointers; each must fail validation before any launch."""
+ENTRY_POINTS = ("score", "calibrate", "topp_select", "compact", "decode_attn", "step",
+                "step_inplace", "step_policy")
+# the entry points that take a query pointer
+TAKES_Q = ("score", "decode_attn", "step", "step_inplace", "step_policy")
+
+
+def _call_all(desc, ws_bytes, null_q=False, only=ENTRY_POINTS):
+    """Calls the named entry points with fake (never dereferenced) device
+    pointers and returns their codes in ENTRY_POINTS order.  Every call made
+    here must fail validation: a call whose arguments all pass would enqueue
+    kernels on the fake pointers, so callers pass only the entry points that
+    the argument under test makes invalid (with null_q, those taking q)."""
     lib = H.load()
     fake = ctypes.c_void_p(0x1000)
     cache = H.Cache(fake, fake, None, fake)
@@ -111,20 +120,30 @@ def _call_all(desc, ws_bytes, null_q=False):
     q = None if null_q else fake
     d = ctypes.byref(desc)
     st = ctypes.c_void_p(0)
-    return [
-        lib.hardkv_score(d, q, ctypes.byref(cache), None, fake, None, fake, ws_bytes, st),
-        lib.hardkv_calibrate(d, fake, None, fake, None, fake, fake, ws_bytes, st),
-        lib.hardkv_topp_select(d, fake, None, fake, None, fake, fake, fake, fake, ws_bytes, st),
-        lib.hardkv_compact(d, ctypes.byref(cache), fake, ctypes.byref(tiers), fake, ws_bytes, st),
-        lib.hardkv_decode_attn(d, q, ctypes.byref(cache), ctypes.byref(tiers), fake, fake,
-                               ws_bytes, st),
-        lib.hardkv_step(d, q, ctypes.byref(cache), None, ctypes.byref(tiers), fake, fake,
-                        ws_bytes, st),
-        lib.hardkv_step_inplace(d, q, fake, fake, None, ctypes.byref(state), fake, fake,
-                                ws_bytes, st),
-        lib.hardkv_step_policy(d, ctypes.byref(pol), q, ctypes.byref(cache), None,
-                               ctypes.byref(tiers), fake, fake, ws_bytes, st),
-    ]
+    calls = {
+        "score": lambda: lib.hardkv_score(d, q, ctypes.byref(cache), None, fake, None, fake,
+                                          ws_bytes, st),
+        "calibrate": lambda: lib.hardkv_calibrate(d, fake, None, fake, None, fake, fake,
+                                                  ws_bytes, st),
+        "topp_select": lambda: lib.hardkv_topp_select(d, fake, None, fake, None, fake, fake,
+                                                      fake, fake, ws_bytes, st),
+        "compact": lambda: lib.hardkv_compact(d, ctypes.byref(cache), fake, ctypes.byref(tiers),
+                                              fake, ws_bytes, st),
+        "decode_attn": lambda: lib.hardkv_decode_attn(d, q, ctypes.byref(cache),
+                                                      ctypes.byref(tiers), fake, fake, ws_bytes,
+                                                      st),
+        "step": lambda: lib.hardkv_step(d, q, ctypes.byref(cache), None, ctypes.byref(tiers),
+                                        fake, fake, ws_bytes, st),
+        "step_inplace": lambda: lib.hardkv_step_inplace(d, q, fake, fake, None,
+                                                        ctypes.byref(state), fake, fake,
+                                                        ws_bytes, st),
+        "step_policy": lambda: lib.hardkv_step_policy(d, ctypes.byref(pol), q,
+                                                      ctypes.byref(cache), None,
+                                                      ctypes.byref(tiers), fake, fake, ws_bytes,
+                                                      st),
+    }
+    assert set(only) <= set(ENTRY_POINTS)
+    return [calls[n]() for n in ENTRY_POINTS if n in only]
 
 
 def test_errors_before_launch():
@@ -134,11 +153,14 @@ def test_errors_before_launch():
     assert _call_all(base_desc(d=96), need) == [H.ERR_UNSUPPORTED] * 8
     assert _call_all(base_desc(top_p=2.0), need) == [H.ERR_INVALID_ARG] * 8
     assert _call_all(base_desc(sparse_cap=10), need) == [H.ERR_CAPACITY] * 8
-    rc = _call_all(desc, need, null_q=True)
-    assert rc[0] == rc[4] == rc[5] == rc[6] == rc[7] == H.ERR_INVALID_ARG
-    # the lifecycle needs a contiguous layout and a window
+    # a null query: only the entry points that take one are called, and every
+    # one of them must refuse
+    assert _call_all(desc, need, null_q=True, only=TAKES_Q) == [H.ERR_INVALID_ARG] * len(TAKES_Q)
+    # the lifecycle needs a contiguous layout and a window (the single-step
+    # calls accept a paged descriptor, so they are not called here)
     paged = base_desc(block_size=16, max_blocks=63)
-    assert _call_all(paged, H.workspace_size(paged))[6] == H.ERR_INVALID_ARG
+    assert _call_all(paged, H.workspace_size(paged), only=("step_inplace",)) == \
+        [H.ERR_INVALID_ARG]
     lib = H.load()
     assert lib.hardkv_validate(None) == H.ERR_INVALID_ARG
     assert lib.hardkv_workspace_size(None) == 0
