@@ -187,7 +187,15 @@ def make_case(w: Workload, device="cpu") -> Case:
             qh = qb[g0]
             r = torch.arange(1, w.peaked_m + 1, dtype=torch.float32, device=device)
             L_r = w.peaked_top - w.peaked_zipf * torch.log(r)
-            keys = (L_r * math.sqrt(d) / qh.norm())[:, None] * (qh / qh.norm())[None, :]
+            if w.metrics[h] == METRIC_L2:
+                # a key-norm head ranks by |k|: the planted keys' norms stand
+                # L_r standard deviations of a flat key's norm (1/sqrt(2) for
+                # N(0, 1) entries) above the typical norm sqrt(d)
+                norm = math.sqrt(d) + L_r / math.sqrt(2.0)
+            else:
+                # a logit head: the planted keys' logit with q_g0 is L_r
+                norm = L_r * math.sqrt(d) / qh.norm()
+            keys = norm[:, None] * (qh / qh.norm())[None, :]
             pos = torch.randperm(A, generator=_gen(w, "cpu", "peak", b, h))[:w.peaked_m]
             kb[h, pos.to(device)] = keys[:len(pos)]
             extra[("peaked", b, h)] = [int(x) for x in pos]

@@ -594,6 +594,12 @@ class HeadState:
     vsum: np.ndarray
     cnt: np.ndarray
     T: int                 # tokens seen so far (positions 0..T-1)
+    # per chunk, the sums of |k| and |v| over the tokens merged so far: not
+    # part of the method, the scale against which a float32 sum of the same
+    # tokens is judged (relative error of a sum is bounded by that of
+    # sum |x|)
+    kabs: np.ndarray | None = None
+    vabs: np.ndarray | None = None
 
 
 def init_state(K, V, T0: int, W: int, C: int, nchunks: int) -> HeadState:
@@ -610,7 +616,8 @@ def init_state(K, V, T0: int, W: int, C: int, nchunks: int) -> HeadState:
     A = T0 - W
     return HeadState(W, C, ring_K, ring_V, np.array(K[:A]), np.array(V[:A]),
                      np.arange(A), np.zeros((nchunks, d)), np.zeros((nchunks, d)),
-                     np.zeros(nchunks, np.int64), T0)
+                     np.zeros(nchunks, np.int64), T0, np.zeros((nchunks, d)),
+                     np.zeros((nchunks, d)))
 
 
 def lifecycle_step(st: HeadState, q_group, k_new, v_new, p: float, metric: int):
@@ -648,6 +655,11 @@ def lifecycle_step(st: HeadState, q_group, k_new, v_new, p: float, metric: int):
     st.ksum += ks
     st.vsum += vs
     st.cnt += cn
+    if st.kabs is not None:
+        ka, va, _ = condense(np.abs(st.pool_K), np.abs(st.pool_V), evicted, st.pool_pos, C,
+                             len(st.cnt))
+        st.kabs += ka
+        st.vabs += va
     n_before = len(st.pool_pos)
     st.pool_K = st.pool_K[keep]
     st.pool_V = st.pool_V[keep]

@@ -1,7 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Small cases check every (b, h) and every stage; the full-size workloads
-check sampled heads against the oracle and cheap invariants on all heads.
+Small cases check every (b, h) and every stage.  At full size the product
+call hardkv_step is compared with the oracle on every head of the headline,
+ragged and 64k workloads; the stage-by-stage calls and the option variants
+on sampled heads, with cheap invariants on every head.
 Comparison rules: tests/parity.py.
 """
 import math
@@ -424,16 +426,17 @@ def _sample_heads(w, n, seed):
 
 
 def test_headline_b32_16k_paged(gpu):
-    """The headline workload at full size: sampled heads against the oracle
-    through hardkv_step, invariants on every head."""
+    """The headline workload at full size through hardkv_step: every one of
+    the 256 (sequence, KV head) pairs against the oracle."""
     w = S.workload("qwen8b_b32_16k_paged")
     say(w.name)
     case = S.make_case(w, gpu)
     desc = desc_for(case)
     g = run_step(case, desc)
     check_all_heads_invariants(case, desc, g)
-    rep = check_case(case, g, w.p, heads=_sample_heads(w, 10, 1), stages=False)
+    rep = check_case(case, g, w.p, stages=False)
     say(rep)
+    assert rep["heads"] == w.B * w.Hkv
 
 
 def test_headline_with_sinks_and_weighted_merging(gpu):
@@ -509,14 +512,44 @@ def test_mixed_metric_64k_entropy_calibration(gpu):
 
 
 def test_ragged_b32_paged(gpu):
+    """Ragged contexts of 8192..32768 tokens in a paged cache.  The product
+    call hardkv_step (more than 16384 candidates per head: separate
+    calibrate and select launches, up to 32 fused compaction tiles per head)
+    is compared with the oracle on all 256 heads; the stage-by-stage calls on
+    sampled heads."""
     w = S.workload("qwen8b_b32_ragged_paged")
     say(w.name, w.T[:4])
+    assert max(w.T) - w.W > 16384
     case = S.make_case(w, gpu)
     desc = desc_for(case)
+    g = run_step(case, desc)
+    check_all_heads_invariants(case, desc, g)
+    rep = check_case(case, g, w.p, stages=False)
+    say("step", rep)
+    assert rep["heads"] == w.B * w.Hkv
+    del g
     g = run_stages(case, desc)
     check_all_heads_invariants(case, desc, g)
     rep = check_case(case, g, w.p, heads=_sample_heads(w, 8, 2))
+    say("stages", rep)
+
+
+@pytest.mark.parametrize("p", [0.8, 0.9, 0.99])
+def test_mixed_metric_64k_step(gpu, p):
+    """65280 candidates per head, logit and key-norm heads, peaked and flat:
+    the product call hardkv_step (separate calibrate and select launches, 64
+    fused compaction tiles per head) against the oracle on all 64 heads."""
+    w = S.workload("qwen8b_b8_64k_mixed")
+    say(w.name, "p", p)
+    case = S.make_case(w, gpu)
+    desc = desc_for(case, top_p=p)
+    g = run_step(case, desc)
+    check_all_heads_invariants(case, desc, g)
+    rep = check_case(case, g, p, stages=False)
     say(rep)
+    assert rep["heads"] == w.B * w.Hkv
+    cnt = g["tiers"].count.float() / (w.T[0] - w.W)
+    assert cnt[:, 0].max() < 0.01 and cnt[:, 4].max() < 0.01
 
 
 def test_mixed_metric_64k_p_sweep(gpu):
@@ -538,7 +571,6 @@ def test_mixed_metric_64k_p_sweep(gpu):
         prev = m
         cnt = g["tiers"].count.float() / A
         # peaked heads keep far fewer tokens than flat heads
-        if p < 0.95:
-            assert cnt[:, 0].max() < 0.01 and cnt[:, 4].max() < 0.01
+        assert cnt[:, 0].max() < 0.01 and cnt[:, 4].max() < 0.01
         assert cnt[:, [0, 4]].max() < 0.5 * cnt[:, [1, 2, 3, 5, 6, 7]].min()
         del g

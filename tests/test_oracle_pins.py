@@ -372,6 +372,17 @@ def test_lifecycle_invariants():
         for t in range(P - W + 1, P + 1):
             assert np.array_equal(st.ring_K[t % W], K[t])
         pool_prev = pool
+    # the running chunk scale sum|x| is, chunk by chunk, the brute-force sum
+    # of |k| and |v| over the positions merged into it (every aged position
+    # outside the pool)
+    merged = sorted(set(range(T0 + steps - W)) - set(st.pool_pos.tolist()))
+    ka = np.zeros_like(st.kabs)
+    va = np.zeros_like(st.vabs)
+    for t in merged:
+        ka[t // C] += np.abs(K[t].astype(np.float64))
+        va[t // C] += np.abs(V[t].astype(np.float64))
+    assert np.allclose(st.kabs, ka, rtol=1e-13, atol=0) and np.allclose(st.vabs, va, rtol=1e-13, atol=0)
+    assert np.all(np.abs(st.ksum) <= st.kabs * (1 + 1e-12))
 
 
 @pytest.mark.parametrize("p,C", [(1.0, 8), (0.7, 1)])
