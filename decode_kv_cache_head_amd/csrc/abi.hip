@@ -3,9 +3,16 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 using namespace hk;
+
+// Workspace of hardkv_step_noalloc.  Host code never names this array past
+// set-up: its host-side symbol is a stand-in, not a device address; the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[HARDKV_SCRATCH_BYTES];
 
 namespace {
 hardkv_launch_observer g_observer = nullptr;
@@ -18,7 +25,27 @@ void hk::observe(const char* kernel, hipStream_t st) {
 
 namespace {
 
-constexpr int kVersion = 10600;  // 1.6.0
+constexpr int kVersion = 10700;  // 1.7.0
+
+// Device address of `scratch` on each device, looked up on the first
+// hardkv_step_noalloc call with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HARDKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+      return HARDKV_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HARDKV_OK;
+}
 
 int log2i(int v) {
   int l = 0;
@@ -500,6 +527,20 @@ int hardkv_step(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
   const hardkv_policy rewrite_all{HARDKV_POLICY_REWRITE, 1, 0, 0};
   run_step(d, &rewrite_all, q, cache, metric, tiers, out, ws, (hipStream_t)stream);
   return launched();
+}
+
+int hardkv_step_noalloc(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
+                        const int8_t* metric, const hardkv_tiers* tiers, float* out,
+                        hardkv_stream_t stream) {
+  const int rc = validate(d);
+  if (rc) return rc;
+  if (!q || !scored_cache_ok(d, cache) || !tiers_ok(d, tiers) || !out)
+    return HARDKV_ERR_INVALID_ARG;
+  if (layout(d).total > HARDKV_SCRATCH_BYTES) return HARDKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int src = scratch_of_current_device(&ws);
+  if (src) return src;
+  return hardkv_step(d, q, cache, metric, tiers, out, ws, HARDKV_SCRATCH_BYTES, stream);
 }
 
 int hardkv_step_policy(const hardkv_desc* d, const hardkv_policy* policy, const void* q,

@@ -96,6 +96,8 @@ _SIGS = {
                             ctypes.POINTER(TiersC), _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "hardkv_step": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(Cache), _P,
                      ctypes.POINTER(TiersC), _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hardkv_step_noalloc": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(Cache), _P,
+                             ctypes.POINTER(TiersC), _P, _P], ctypes.c_int),
     "hardkv_plan": ([ctypes.POINTER(Desc), ctypes.POINTER(Policy), _P, _P, _P, _P],
                     ctypes.c_int),
     "hardkv_pack": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(TiersC), _P], ctypes.c_int),
@@ -270,6 +272,17 @@ def step(desc, q, cache: Cache, metric, tiers: Tiers, out, ws, stream=None):
     rc = load().hardkv_step(ctypes.byref(desc), _p(q), ctypes.byref(cache), _p(metric),
                             ctypes.byref(tc), _p(out), _p(ws), ws.numel(), _stream(stream))
     _check(rc, "hardkv_step")
+
+
+SCRATCH_BYTES = 64 << 20  # HARDKV_SCRATCH_BYTES
+
+
+def step_noalloc(desc, q, cache: Cache, metric, tiers: Tiers, out, stream=None):
+    """hardkv_step with the library-held workspace of the current device."""
+    tc = tiers.c()
+    rc = load().hardkv_step_noalloc(ctypes.byref(desc), _p(q), ctypes.byref(cache), _p(metric),
+                                    ctypes.byref(tc), _p(out), _stream(stream))
+    _check(rc, "hardkv_step_noalloc")
 
 
 def plan(desc, pol: Policy, ctx_len, count, mode, stream=None):

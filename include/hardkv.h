@@ -399,6 +399,31 @@ int hardkv_step_inplace(const hardkv_desc* desc, const void* q, const void* k_ne
                         const void* v_new, const int8_t* metric, const hardkv_state* state,
                         float* out, void* ws, size_t ws_bytes, hardkv_stream_t stream);
 
+/* Bytes of the library-held workspace of hardkv_step_noalloc, per device. */
+#define HARDKV_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* hardkv_step for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same launches as hardkv_step, with the workspace taken from a library-held
+ * array of HARDKV_SCRATCH_BYTES on the current device (hipGetDevice; the
+ * stream must belong to that device).  Each device's copy is set up on the
+ * first call with that device current and lives until the process ends;
+ * nothing is allocated or freed by any call.
+ *   Arguments, layouts and results: as hardkv_step (the caller still owns q,
+ *   the cache, the tiers and out).
+ *   Errors: as hardkv_step, and HARDKV_ERR_WORKSPACE when
+ *   hardkv_workspace_size(desc) exceeds HARDKV_SCRATCH_BYTES (the headline
+ *   shape, 32 sequences x 8 KV heads x 16k tokens, needs 54 MiB);
+ *   HARDKV_ERR_HIP when the device or the array's address cannot be queried.
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents (the step needs none of them: each kernel writes what it
+ * reads later in the same call).  Calls that overlap on one device (two
+ * streams, two threads) race on the array and must be serialised by the
+ * caller. */
+int hardkv_step_noalloc(const hardkv_desc* desc, const void* q, const hardkv_cache* cache,
+                        const int8_t* metric, const hardkv_tiers* tiers, float* out,
+                        hardkv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = H.load()
-    assert lib.hardkv_version() == 10600
+    assert lib.hardkv_version() == 10700
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.hardkv_strerror(code)
     assert lib.hardkv_strerror(99) == b"unknown error"
@@ -164,6 +164,35 @@ def test_errors_before_launch():
     lib = H.load()
     assert lib.hardkv_validate(None) == H.ERR_INVALID_ARG
     assert lib.hardkv_workspace_size(None) == 0
+
+
+def test_noalloc_step_errors_before_launch():
+    """hardkv_step_noalloc refuses, before touching any device, a descriptor
+    whose workspace exceeds the library-held array and every missing
+    argument."""
+    lib = H.load()
+    fake = ctypes.c_void_p(0x1000)
+    cache = H.Cache(fake, fake, None, fake)
+    tiers = H.TiersC(*([fake] * 9))
+    st = ctypes.c_void_p(0)
+    # 32 sequences x 8 heads x 32k tokens: 106 MiB of workspace
+    big = base_desc(B=32, Hq=32, Hkv=8, W=256, C=64, ctx_cap=32768)
+    assert H.workspace_size(big) > H.SCRATCH_BYTES
+    assert lib.hardkv_step_noalloc(ctypes.byref(big), fake, ctypes.byref(cache), None,
+                                   ctypes.byref(tiers), fake, st) == H.ERR_WORKSPACE
+    # the headline shape fits
+    head = base_desc(B=32, Hq=32, Hkv=8, W=256, C=64, ctx_cap=16384, block_size=16,
+                     max_blocks=1024)
+    assert H.workspace_size(head) <= H.SCRATCH_BYTES
+    d = ctypes.byref(base_desc())
+    no_ccount = H.TiersC(*([fake] * 6), None)
+    for args in ((None, cache, tiers, fake), (fake, H.Cache(fake, None, None, fake), tiers, fake),
+                 (fake, cache, no_ccount, fake), (fake, cache, tiers, None)):
+        q, c, t, out = args
+        assert lib.hardkv_step_noalloc(d, q, ctypes.byref(c), None, ctypes.byref(t), out,
+                                       st) == H.ERR_INVALID_ARG
+    assert lib.hardkv_step_noalloc(ctypes.byref(base_desc(d=96)), fake, ctypes.byref(cache), None,
+                                   ctypes.byref(tiers), fake, st) == H.ERR_UNSUPPORTED
 
 
 def test_l2_buffer_required_with_metric():
