@@ -131,10 +131,41 @@ __device__ inline float cval(float x, double shift, double scale) {
   return (float)(((double)x - shift) * scale);
 }
 
-// Fixed-point weight round(exp(c - m) * 2^47); exp(c - m) <= 1.
-__device__ inline uint64_t wfix(float c, double m, double scale) {
-  const double w = exp((double)c - m);
-  return (uint64_t)__double2ull_rn(w * scale);
+// exp(x) for x <= 0 in float64, table-driven (P. T. P. Tang, "Table-driven
+// implementation of the exponential function in IEEE floating-point
+// arithmetic", ACM TOMS 15(2), 1989): x = k ln2/64 + r with |r| <= ln2/128
+// (ln2/64 split in a 39-bit high part, so k times it is exact for the k
+// here, and a low part), k = 64 q + j, exp(x) = 2^q 2^(j/64) e^r, e^r - 1
+// from its Taylor series to degree 5 (truncation below 4e-17 relative).
+// tab[j] = 2^(j/64) (exp_table_init).  x below -100 is taken as -100: the
+// result, < 4e-44, rounds to 0 in every fixed-point use here.
+__device__ inline double exp_nonpos(double x, const double* tab) {
+  x = fmax(x, -100.0);
+  const double kd = rint(x * 0x1.71547652b82fep+6);  // x * 64 / ln 2
+  double r = fma(-kd, 0x1.62e42fefa4000p-7, x);
+  r = fma(-kd, -0x1.8432a1b0e2634p-49, r);
+  const double p =
+      r * (1.0 + r * (0.5 + r * (1.0 / 6.0 + r * (1.0 / 24.0 + r * (1.0 / 120.0)))));
+  const int k = (int)kd;
+  const double t = tab[k & 63];
+  return ldexp(fma(t, p, t), k >> 6);
+}
+// Fills tab[0..63] with 2^(j/64); threads 0..63 of the calling workgroup
+// each write one entry (a barrier must follow before exp_nonpos reads it).
+__device__ inline void exp_table_init(double* tab) {
+  if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 64.0));
+}
+
+// round(v) for 0 <= v < 2^52, ties to even: adding 2^52 leaves the nearest
+// integer in the low mantissa bits.
+__device__ inline uint64_t fix_round(double v) {
+  return (uint64_t)__double_as_longlong(v + 0x1p52) - 0x4330000000000000ull;
+}
+
+// Fixed-point weight round(exp(c - m) * scale); exp(c - m) <= 1 and scale a
+// power of two <= 2^47, so the product is exact and below 2^52.
+__device__ inline uint64_t wfix(float c, double m, double scale, const double* tab) {
+  return fix_round(exp_nonpos((double)c - m, tab) * scale);
 }
 
 // Fixed-point scale of the selection masses for heads of up to n_max

@@ -185,8 +185,9 @@ struct AttnArgs {
   int max_tiles;
   float* out;
   double scale;
-  // > 0: the sparse tier was attended by the fused compaction (its tiles of
-  // fused_tt candidates own partial slots 0..); only dense and chunk tiles here
+  // > 0: the sparse and condensed tiers were attended by the fused
+  // compaction (its tiles of fused_tt candidates own partial slots 0..);
+  // only dense tiles here
   int fused_tt;
   // lifecycle: advance[b] += 1 for every sequence once the outputs are
   // written (by the merge); null elsewhere

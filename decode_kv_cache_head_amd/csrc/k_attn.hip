@@ -75,9 +75,11 @@ __device__ inline TileCounts tile_counts(const AttnArgs& a, int b, int h) {
   t.ntc = (t.nc + kAttnTile - 1) / kAttnTile;
   t.first = 0;
   if (a.fused_tt > 0) {
+    // the compaction's tiles attended the sparse and condensed tiers
     int n = A > a.sparse_cap ? a.sparse_cap : A;
     t.first = (n + a.fused_tt - 1) / a.fused_tt;
     t.nts = 0;
+    t.ntc = 0;
   }
   return t;
 }
@@ -673,8 +675,8 @@ template <typename T, int D, int G, bool P>
 static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
   constexpr bool split = kUseMx<T, D, G, false> && G >= 8;
   const int gd = ceil_div(a.W + a.sinks, kAttnTile), gc = ceil_div(a.chunk_cap, kAttnTile);
-  const int gx = a.fused_tt > 0 ? gd + gc : a.max_tiles;
-  const int grows = split ? gx - gc : gx;
+  const int gx = a.fused_tt > 0 ? gd : a.max_tiles;
+  const int grows = split && a.fused_tt == 0 ? gx - gc : gx;
   bool pool_paged = false;
   if constexpr (!P) pool_paged = a.sk.table != nullptr;
   if (grows > 0) {
@@ -685,7 +687,7 @@ static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
     else
       hipLaunchKernelGGL((k_attn<T, D, G, P, false, split ? 1 : 0>), grid, dim3(256), 0, st, a);
   }
-  if (split && gc > 0) {
+  if (split && gc > 0 && a.fused_tt == 0) {
     observe("k_attn_chunks", st);
     hipLaunchKernelGGL((k_attn<T, D, G, false, false, 2>), dim3(gc, a.hkv, a.B), dim3(256), 0, st,
                        a);

@@ -205,7 +205,12 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
 // per 64 rows.  In the fused step, tiles that keep under 1/8 of their rows
 // run a copy of the streaming loop that skips the attention arithmetic of
 // units without a kept row; denser tiles run the copy without that branch
-// (it costs them more than it saves).
+// (it costs them more than it saves).  The fused step's tile also attends
+// the condensed chunks it has just formed (a tile holds whole chunks, so
+// every chunk's sum is final inside its tile): each non-empty chunk enters
+// the tile's partial with key ksum / n, value vsum / n and logit
+// q.(ksum / n) / sqrt(d) + ln n, from the float32 sums as stored, so the
+// sums are never read back from memory.
 template <typename T, int D, int G, bool P, bool ATTN, bool WMERGE>
 __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   constexpr int RB = D * (int)sizeof(T);
@@ -227,6 +232,11 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   __shared__ int s_kept_tile;           // kept rows in the tile
   __shared__ float s_am[4][GA], s_al[4][GA];
   __shared__ float s_ao[ATTN ? 4 * G * D : 1];
+  __shared__ float s_q[ATTN ? G * D : 1];          // the group's queries, float32
+  __shared__ float s_cl[ATTN ? MAXU * G : 1];      // chunk logits (-inf: empty chunk)
+  __shared__ float s_cf[ATTN ? MAXU * G : 1];      // chunk weights against the tile max
+  __shared__ float s_cv[ATTN ? MAXU * G : 1];      // ... divided by the chunk's count
+  __shared__ float s_M[GA];                         // tile max per query head
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int n = a.cand.n(b, h);
   const int t0 = j * TT;
@@ -307,6 +317,7 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   float am[GA], al[GA], ao[GA][EPC];
   if constexpr (ATTN) {
     const T* qg = (const T*)a.q + ((int64_t)b * a.hq + (int64_t)h * G) * D;
+    for (int i = tid; i < G * D; i += 256) s_q[i] = Elt<T>::load1(qg + i);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       qp[g].load(qg + g * D + c * EPC);
@@ -486,16 +497,55 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
         v = ne > 0 ? v * ((float)ne / wt) : 0.f;
       }
       (q ? a.vsum : a.ksum)[(bh * a.chunk_stride + ch0 + cl) * D + dim] = v;
+      // the stored chunk sum, kept for the attention below in the slot of
+      // the chunk's first unit (read above by this thread only)
+      if (ATTN) s_unit[cl * upc][q][dim] = v;
     }
     if (tid < nch) a.ccount[bh * a.chunk_stride + ch0 + tid] = s_evc[tid];
   }
   if constexpr (ATTN) {
-    float* part_out = a.part + (bh * a.max_tiles + j) * G * (D + 2);
-    for (int i = tid; i < G * D; i += 256) {
-      const int g = i / D, e = i % D;
+    const int upc = a.C / 64;
+    const int nch = (nrows + a.C - 1) / a.C;
+    __syncthreads();
+    // chunk logits: wave w takes chunks w, w + 4, ...; each lane holds D / 64
+    // dimensions of the chunk's key sum, the dot products are wave sums
+    for (int cl = w; cl < MAXU; cl += 4) {
+      const int ne = cl < nch ? s_evc[cl] : 0;  // uniform over the wave
+      if (ne > 0) {
+        const float* ks = s_unit[cl * upc][0];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float dot = 0.f;
+#pragma unroll
+          for (int e = lane; e < D; e += 64) dot = fmaf(s_q[g * D + e], ks[e], dot);
+          dot = group_sum<64>(dot);
+          if (lane == 0) s_cl[cl * G + g] = dot / (float)ne * a.scale + __logf((float)ne);
+        }
+      } else if (lane < G) {
+        s_cl[cl * G + lane] = -INFINITY;
+      }
+    }
+    __syncthreads();
+    // per (chunk, query head): its weight against the head's maximum over the
+    // tile (kept rows of the four waves and the chunks), and the value weight
+    // (the chunk's value is vsum / n)
+    if (tid < MAXU * G) {
+      const int cl = tid / G, g = tid % G;
       float M = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 4; ++v) M = fmaxf(M, s_am[v][g]);
+      for (int x = 0; x < nch; ++x) M = fmaxf(M, s_cl[x * G + g]);
+      const float lg = s_cl[cl * G + g];
+      const float f = cl < nch && lg != -INFINITY ? __expf(lg - M) : 0.f;
+      s_cf[cl * G + g] = f;
+      s_cv[cl * G + g] = f > 0.f ? f / (float)s_evc[cl] : 0.f;
+      if (cl == 0) s_M[g] = M;
+    }
+    __syncthreads();
+    float* part_out = a.part + (bh * a.max_tiles + j) * G * (D + 2);
+    for (int i = tid; i < G * D; i += 256) {
+      const int g = i / D, e = i % D;
+      const float M = s_M[g];
       float O = 0.f, S = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
@@ -505,6 +555,10 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
             O = fmaf(f, s_ao[(v * G + g) * D + e], O);
             S = fmaf(f, s_al[v][g], S);
           }
+        }
+        for (int cl = 0; cl < nch; ++cl) {
+          O = fmaf(s_cv[cl * G + g], s_unit[cl * upc][1][e], O);
+          S += s_cf[cl * G + g];
         }
       }
       float* pp = part_out + g * (D + 2);

@@ -13,6 +13,8 @@
 //   additions).  The cutoff key K* is the bin where the mass accumulated from
 //   the top first reaches ceil(p * Z); the tokens tied at K* are taken lowest
 //   position first, as many as needed.  A final ordered pass writes the mask.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace hk {
@@ -224,15 +226,44 @@ struct SelShared {
   unsigned long long hist[kHistSlots];
   unsigned long long target;
   unsigned long long above;
+  unsigned long long total;   // fixed-point mass of the head (pass 1)
+  unsigned long long tally;   // k_calsel: selected count << 32 | waves done
   uint32_t bin;
   int wc[kSelWaves];
   int red[kSelWaves];
   int tpre[16 * kSelWaves];  // k_calsel: ties before (slot, wave), position order
 };
 
+// Lane l's value moved from lane l - K of its 16-lane row (0 for the first
+// K lanes of the row), both 32-bit halves through DPP row shifts.
+template <int K>
+__device__ __forceinline__ uint64_t row_shr_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x110 + K, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x110 + K, 0xF, 0xF, true);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Inclusive prefix sum over the 64 lanes of the wave: Hillis-Steele steps
+// inside each 16-lane row, then the totals of the rows below added from
+// lanes 15, 31 and 47.
+__device__ __forceinline__ uint64_t wave_prefix_u64(uint64_t v) {
+  v += row_shr_u64<1>(v);
+  v += row_shr_u64<2>(v);
+  v += row_shr_u64<4>(v);
+  v += row_shr_u64<8>(v);
+  const uint64_t r0 = readlane_u64(v, 15), r1 = readlane_u64(v, 31), r2 = readlane_u64(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0ull) + (row >= 2 ? r1 : 0ull) + (row >= 3 ? r2 : 0ull);
+}
+
 // Run by wave 0: the largest bin whose suffix mass (bins at or above it)
 // reaches `target`; records the bin and the mass strictly above it.  With
-// from_total, the target is first set to max(ceil(p * total), 1).
+// from_total, the target is first set to max(ceil(p * total), 1) and the
+// total is recorded.
 template <int NB>
 __device__ inline void find_bin(SelShared& S, bool from_total, float p) {
   const int lane = threadIdx.x;
@@ -240,15 +271,12 @@ __device__ inline void find_bin(SelShared& S, bool from_total, float p) {
   unsigned long long s = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) s += S.hist[lane * (PER + 1) + i];
-  unsigned long long suf = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long v = __shfl_down(suf, o, 64);
-    if (lane + o < 64) suf += v;
-  }
+  // suffix sums over the lanes: total minus the exclusive prefix
+  const unsigned long long pre = wave_prefix_u64(s);
+  const unsigned long long total = readlane_u64(pre, 63);
+  const unsigned long long suf = total - pre + s;
   unsigned long long target;
   if (from_total) {
-    const unsigned long long total = __shfl(suf, 0, 64);
     target = ceil_mul(p, total);
     if (target < 1) target = 1;
   } else {
@@ -258,14 +286,10 @@ __device__ inline void find_bin(SelShared& S, bool from_total, float p) {
   int L = __popcll(ok) - 1;  // suf falls with the lane: lanes 0..L reach the target
   L = L < 0 ? 0 : L;
   // inside lane L's PER bins: suffix sums over PER lanes, the same rule
-  const unsigned long long base = __shfl(suf - s, L, 64);  // mass above the chunk
+  const unsigned long long base = readlane_u64(suf - s, L);  // mass above the chunk
   const unsigned long long hv = lane < PER ? S.hist[L * (PER + 1) + lane] : 0ull;
-  unsigned long long suf2 = hv;
-#pragma unroll
-  for (int o = 1; o < PER; o <<= 1) {
-    const unsigned long long v = __shfl_down(suf2, o, 64);
-    if (lane + o < PER) suf2 += v;
-  }
+  const unsigned long long pre2 = wave_prefix_u64(hv);
+  const unsigned long long suf2 = readlane_u64(pre2, 63) - pre2 + hv;
   const unsigned long long ok2 = __ballot(lane < PER && base + suf2 >= target);
   int J = __popcll(ok2) - 1;
   J = J < 0 ? 0 : J;
@@ -273,7 +297,10 @@ __device__ inline void find_bin(SelShared& S, bool from_total, float p) {
     S.bin = L * PER + J;
     S.above = base + suf2 - hv;
   }
-  if (from_total && lane == 0) S.target = target;
+  if (from_total && lane == 0) {
+    S.target = target;
+    S.total = total;
+  }
 }
 
 // Where a selection's size goes: count[bh] = k and, when a mode array is
@@ -297,6 +324,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
                                                         float top_p, double wscale,
                                                         uint8_t* __restrict__ mask, CountOut co) {
   __shared__ SelShared S;
+  __shared__ double s_et[64];
   const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
   const int n = cand.n(b, h);
   const int64_t bh = (int64_t)b * hkv + h;
@@ -305,6 +333,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
     if (tid == 0) co.put(bh, n, 0);
     return;
   }
+  exp_table_init(s_et);
   if (!(top_p < 1.0f)) {
     for (int t = tid; t < n; t += kSelThreads) mk[t] = 1;
     if (tid == 0) co.put(bh, n, n);
@@ -320,7 +349,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   __syncthreads();
   for (int t = tid; t < n; t += kSelThreads) {
     const float c = cv(t);
-    const uint64_t w = wfix(c, m, wscale);
+    const uint64_t w = wfix(c, m, wscale, s_et);
     if (w) atomicAdd(&S.hist[hslot<2048>(okey(c) >> 21)], (unsigned long long)w);
   }
   __syncthreads();
@@ -340,7 +369,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
     const uint32_t k = okey(c);
     if ((k >> 21) == b1)
       atomicAdd(&S.hist[hslot<2048>((k >> 10) & 2047u)],
-                (unsigned long long)wfix(c, m, wscale));
+                (unsigned long long)wfix(c, m, wscale, s_et));
   }
   __syncthreads();
   if (tid < 64) find_bin<2048>(S, false, top_p);
@@ -359,7 +388,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
     const float c = cv(t);
     const uint32_t k = okey(c);
     if ((k >> 10) == pre)
-      atomicAdd(&S.hist[hslot<1024>(k & 1023u)], (unsigned long long)wfix(c, m, wscale));
+      atomicAdd(&S.hist[hslot<1024>(k & 1023u)], (unsigned long long)wfix(c, m, wscale, s_et));
   }
   __syncthreads();
   if (tid < 64) find_bin<1024>(S, false, top_p);
@@ -367,7 +396,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   const uint32_t kstar = (pre << 10) | S.bin;
   above += S.above;
   // all tokens tied at K* carry the same weight; take r of them
-  const unsigned long long wstar = wfix(okey_inv(kstar), m, wscale);
+  const unsigned long long wstar = wfix(okey_inv(kstar), m, wscale, s_et);
   const unsigned long long need = target - above;
   const unsigned long long r = (need + wstar - 1) / wstar;
 
@@ -414,8 +443,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
 // scores held in registers (NPT per thread, token t = tid + 1024 i), so every
 // pass after the first load runs from registers.  Same rules as k_calibrate
 // and k_select; the float64 reductions run over 1024 threads instead of 256,
-// so the diagnostic statistics may differ in their last bits.
-template <int NPT>
+// so the diagnostic statistics may differ in their last bits.  AUX false:
+// launched without a metric array, every head ranks by its logit, and the
+// second-metric paths (moments, entropy bisection) are compiled out, which
+// keeps the 16-slot form inside the 128 registers a 1024-thread workgroup
+// allows (with them it spilled to scratch).
+template <int NPT, bool AUX>
 __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t* __restrict__ metric,
                                                         const float* __restrict__ logit,
                                                         const float* __restrict__ l2,
@@ -428,11 +461,12 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   __shared__ unsigned long long s_w[NPT * kSelThreads];
   __shared__ double shd[2 * kSelWaves];
   __shared__ float shf[kSelWaves];
+  __shared__ double s_et[64];
   const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
   const int n = cand.n(b, h);
   const int64_t bh = (int64_t)b * hkv + h;
   uint8_t* mk = mask + bh * cap_stride;
-  const bool is_l2 = aux_metric(metric, h);  // second score array
+  const bool is_l2 = AUX && aux_metric(metric, h);  // second score array
   if (n == 0) {
     if (tid == 0) {
       double* o = stats + bh * 4;
@@ -446,108 +480,115 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   }
   const float* xs = logit + bh * cap_stride;
   float c[NPT];
-#pragma unroll
-  for (int i = 0; i < NPT; ++i) {
-    const int t = tid + kSelThreads * i;
-    c[i] = t < n ? xs[t] : 0.f;
-  }
   double shift = 0.0, scale = 1.0;
-  if (is_l2 && calib == HARDKV_CALIB_ENTROPY) {
-    const float* ss = l2 + bh * cap_stride;
-    float sv[NPT];
+  if (!is_l2) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int t = tid + kSelThreads * i;
-      sv[i] = t < n ? ss[t] : 0.f;
+      c[i] = t < n ? xs[t] : 0.f;
     }
-    entropy_temperature<kSelWaves>(
-        [&](auto f) {
-#pragma unroll
-          for (int i = 0; i < NPT; ++i)
-            if (tid + kSelThreads * i < n) f(c[i]);
-        },
-        [&](auto f) {
-#pragma unroll
-          for (int i = 0; i < NPT; ++i)
-            if (tid + kSelThreads * i < n) f(sv[i]);
-        },
-        shd, shf, shift, scale);
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) c[i] = cval(sv[i], shift, scale);
-  } else if (is_l2) {
+  } else {
+    // a second-metric head: its logits and metric values wait in this
+    // thread's own weight slots (free until pass 1 writes the weights there;
+    // slot i holds the logit in its low and the metric in its high half),
+    // not in registers, while the temperature is worked out
+    float* sl = reinterpret_cast<float*>(s_w) + 2 * tid;
+    constexpr int SV = 2 * kSelThreads;  // floats per row of weight slots
     const float* ss = l2 + bh * cap_stride;
-    float sv[NPT];
-    double sx = 0.0, sy = 0.0;
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int t = tid + kSelThreads * i;
-      sv[i] = t < n ? ss[t] : 0.f;
-      sx += (double)c[i];
-      sy += (double)sv[i];
+      sl[i * SV] = t < n ? xs[t] : 0.f;
+      sl[i * SV + 1] = t < n ? ss[t] : 0.f;
     }
-    sx = block_sum_f64<kSelWaves>(sx, shd);
-    sy = block_sum_f64<kSelWaves>(sy, shd);
-    const double mux = sx / n, mus = sy / n;
-    double vx = 0.0, vy = 0.0;
+    if (calib == HARDKV_CALIB_ENTROPY) {
+      entropy_temperature<kSelWaves>(
+          [&](auto f) {
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      if (tid + kSelThreads * i < n) {
-        const double dx = (double)c[i] - mux, dy = (double)sv[i] - mus;
-        vx += dx * dx;
-        vy += dy * dy;
+            for (int i = 0; i < NPT; ++i)
+              if (tid + kSelThreads * i < n) f(sl[i * SV]);
+          },
+          [&](auto f) {
+#pragma unroll
+            for (int i = 0; i < NPT; ++i)
+              if (tid + kSelThreads * i < n) f(sl[i * SV + 1]);
+          },
+          shd, shf, shift, scale);
+    } else {
+      double sx = 0.0, sy = 0.0;
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        sx += (double)sl[i * SV];
+        sy += (double)sl[i * SV + 1];
+      }
+      sx = block_sum_f64<kSelWaves>(sx, shd);
+      sy = block_sum_f64<kSelWaves>(sy, shd);
+      const double mux = sx / n, mus = sy / n;
+      double vx = 0.0, vy = 0.0;
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        if (tid + kSelThreads * i < n) {
+          const double dx = (double)sl[i * SV] - mux, dy = (double)sl[i * SV + 1] - mus;
+          vx += dx * dx;
+          vy += dy * dy;
+        }
+      }
+      vx = block_sum_f64<kSelWaves>(vx, shd);
+      vy = block_sum_f64<kSelWaves>(vy, shd);
+      const double sdx = sqrt(vx / n), sds = sqrt(vy / n);
+      if (sdx == 0.0 || sds == 0.0) {
+        shift = 0.0;
+        scale = 0.0;
+      } else {
+        shift = mus;
+        scale = sdx / sds;
       }
     }
-    vx = block_sum_f64<kSelWaves>(vx, shd);
-    vy = block_sum_f64<kSelWaves>(vy, shd);
-    const double sdx = sqrt(vx / n), sds = sqrt(vy / n);
-    if (sdx == 0.0 || sds == 0.0) {
-      shift = 0.0;
-      scale = 0.0;
-    } else {
-      shift = mus;
-      scale = sdx / sds;
-    }
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) c[i] = cval(sv[i], shift, scale);
+    for (int i = 0; i < NPT; ++i) c[i] = cval(sl[i * SV + 1], shift, scale);
   }
   float mloc = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NPT; ++i)
     if (tid + kSelThreads * i < n) mloc = fmaxf(mloc, c[i]);
+  exp_table_init(s_et);  // read after the barriers of the block maximum
   const double m = (double)block_max_f32<kSelWaves>(mloc, shf);
 
-  // pass 1: weights, Z, and the histogram of the top 11 key bits
+  // pass 1: weights, Z, and the histogram of the top 11 key bits; from here
+  // on the tokens are known by their order-preserving keys
   for (int i = tid; i < kHistSlots; i += kSelThreads) S.hist[i] = 0;
+  if (tid == 0) S.tally = 0ull;
   __syncthreads();
-  double Z = 0.0;
+  uint32_t key[NPT];
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
+    key[i] = okey(c[i]);
     uint64_t w = 0;
     if (tid + kSelThreads * i < n) {
-      const double wd = exp((double)c[i] - m);
-      Z += wd;
-      w = (uint64_t)__double2ull_rn(wd * wscale);  // = wfix(c, m, wscale)
-      if (w) atomicAdd(&S.hist[hslot<2048>(okey(c[i]) >> 21)], (unsigned long long)w);
+      w = fix_round(exp_nonpos((double)c[i] - m, s_et) * wscale);  // = wfix(c, m, wscale, s_et)
+      if (w) atomicAdd(&S.hist[hslot<2048>(key[i] >> 21)], (unsigned long long)w);
     }
     s_w[i * kSelThreads + tid] = w;
   }
-  Z = block_sum_f64<kSelWaves>(Z, shd);  // contains the barrier before find_bin
-  if (tid == 0) {
-    double* o = stats + bh * 4;
-    o[0] = shift;
-    o[1] = scale;
-    o[2] = m;
-    o[3] = Z;
-  }
+  __syncthreads();
   if (!(top_p < 1.0f)) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i)
       if (tid + kSelThreads * i < n) mk[tid + kSelThreads * i] = 1;
     if (tid == 0) co.put(bh, n, n);
-    return;
   }
   if (tid < 64) find_bin<2048>(S, true, top_p);
   __syncthreads();
+  if (tid == 0) {
+    // Z as the fixed-point total (within n 2^-48 of the float64 sum; the
+    // step reads only shift, scale and m downstream)
+    double* o = stats + bh * 4;
+    o[0] = shift;
+    o[1] = scale;
+    o[2] = m;
+    o[3] = (double)S.total / wscale;
+  }
+  if (!(top_p < 1.0f)) return;  // uniform
   const unsigned long long target = S.target;
   const uint32_t b1 = S.bin;
   unsigned long long above = S.above;
@@ -558,9 +599,8 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
-    const uint32_t k = okey(c[i]);
-    if (tid + kSelThreads * i < n && (k >> 21) == b1)
-      atomicAdd(&S.hist[hslot<2048>((k >> 10) & 2047u)], s_w[i * kSelThreads + tid]);
+    if (tid + kSelThreads * i < n && (key[i] >> 21) == b1)
+      atomicAdd(&S.hist[hslot<2048>((key[i] >> 10) & 2047u)], s_w[i * kSelThreads + tid]);
   }
   __syncthreads();
   if (tid < 64) find_bin<2048>(S, false, top_p);
@@ -576,16 +616,15 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   const uint32_t pre = (b1 << 11) | b2;
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
-    const uint32_t k = okey(c[i]);
-    if (tid + kSelThreads * i < n && (k >> 10) == pre)
-      atomicAdd(&S.hist[hslot<1024>(k & 1023u)], s_w[i * kSelThreads + tid]);
+    if (tid + kSelThreads * i < n && (key[i] >> 10) == pre)
+      atomicAdd(&S.hist[hslot<1024>(key[i] & 1023u)], s_w[i * kSelThreads + tid]);
   }
   __syncthreads();
   if (tid < 64) find_bin<1024>(S, false, top_p);
   __syncthreads();
   const uint32_t kstar = (pre << 10) | S.bin;
   above += S.above;
-  const unsigned long long wstar = wfix(okey_inv(kstar), m, wscale);
+  const unsigned long long wstar = wfix(okey_inv(kstar), m, wscale, s_et);
   const unsigned long long need = target - above;
   const unsigned long long r = (need + wstar - 1) / wstar;
   // every token tied at K* has weight wstar, so the bin holds mass / wstar of
@@ -601,7 +640,7 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   uint32_t tmask = 0;
 #pragma unroll
   for (int i = 0; i < NPT; ++i)
-    if (tid + kSelThreads * i < n && okey(c[i]) == kstar) tmask |= 1u << i;
+    if (tid + kSelThreads * i < n && key[i] == kstar) tmask |= 1u << i;
   if (rank_ties) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
@@ -632,6 +671,8 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
     }
     __syncthreads();
   }
+  // mask: for each slot the wave's 64 decisions (tokens 1024 i + 64 wv ..)
+  // come from one ballot; lanes 0..3 each store 16 of them as bytes
   int nsel = 0;
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
@@ -646,19 +687,31 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
                                       __popcll(bal & ((1ull << ln) - 1ull));
       take_tie = tie && rank < r;
     }
-    const bool sel = valid && (okey(c[i]) > kstar || take_tie);
-    if (valid) mk[t] = sel ? 1 : 0;
-    nsel += sel;
+    const bool sel = valid && (key[i] > kstar || take_tie);
+    const unsigned long long bal = __ballot(sel);
+    nsel += __popcll(bal);
+    if (ln < 4) {
+      const int t0 = kSelThreads * i + 64 * wv + 16 * ln;
+      const uint32_t bits = (uint32_t)(bal >> (16 * ln)) & 0xffffu;
+      if (t0 + 16 <= n && ((uintptr_t)(mk + t0) & 15) == 0) {
+        // each nibble of bits becomes four 0/1 bytes
+        uint4 v;
+        v.x = ((bits & 15u) * 0x00204081u) & 0x01010101u;
+        v.y = (((bits >> 4) & 15u) * 0x00204081u) & 0x01010101u;
+        v.z = (((bits >> 8) & 15u) * 0x00204081u) & 0x01010101u;
+        v.w = (((bits >> 12) & 15u) * 0x00204081u) & 0x01010101u;
+        *(uint4*)(mk + t0) = v;
+      } else {
+        for (int q = 0; q < 16 && t0 + q < n; ++q) mk[t0 + q] = (uint8_t)((bits >> q) & 1u);
+      }
+    }
   }
-  int v = nsel;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  if (ln == 0) S.red[wv] = v;
-  __syncthreads();
-  if (tid == 0) {
-    int tot = 0;
-    for (int j = 0; j < kSelWaves; ++j) tot += S.red[j];
-    co.put(bh, n, tot);
+  // count: the waves add (selected << 32 | 1) to one LDS word; the wave that
+  // finds the other fifteen already there writes the total
+  if (ln == 0) {
+    const unsigned long long old =
+        atomicAdd(&S.tally, ((unsigned long long)nsel << 32) | 1ull);
+    if ((old & 0xffffffffull) == kSelWaves - 1) co.put(bh, n, (int)(old >> 32) + nsel);
   }
 }
 
@@ -732,14 +785,12 @@ bool calsel_fits(int max_cand) { return max_cand <= 16 * kSelThreads; }
 void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st) {
   observe("k_calsel", st);
   const dim3 grid(a.hkv, a.B), blk(kSelThreads);
-  if (max_cand <= 4 * kSelThreads)
-    hipLaunchKernelGGL(k_calsel<4>, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2,
-                       a.cap_stride, a.stats, a.top_p, mass_scale(a.cand.cap), a.mask,
-                       count_out(a), a.calib);
-  else
-    hipLaunchKernelGGL(k_calsel<16>, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2,
-                       a.cap_stride, a.stats, a.top_p, mass_scale(a.cand.cap), a.mask,
-                       count_out(a), a.calib);
+  const bool aux = a.metric != nullptr;
+  const bool small = max_cand <= 4 * kSelThreads;
+  auto kern = small ? (aux ? k_calsel<4, true> : k_calsel<4, false>)
+                    : (aux ? k_calsel<16, true> : k_calsel<16, false>);
+  hipLaunchKernelGGL(kern, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2, a.cap_stride,
+                     a.stats, a.top_p, mass_scale(a.cand.cap), a.mask, count_out(a), a.calib);
 }
 
 void launch_calibrate(const SelectArgs& a, hipStream_t st) {
