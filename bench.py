@@ -9,10 +9,15 @@ Qwen3-8B attention shape (32 query heads, 8 KV heads, head_dim 128), batch
 window 256, chunk 64, top-p 0.95.  Inputs are synthetic N(0, 1) and resident
 in HBM before timing.
 
-Prints one JSON line.  In the timed region the library's launch observer
-records a HIP event on the launch stream before every kernel, so each
-kernel's average duration is measured live; the same loop without the
-observer is timed as a cross-check.
+Prints one JSON line.  `value` and `ms_per_step` come from a plain loop of
+the step; a second loop with the library's launch observer records a HIP
+event on the launch stream before every kernel, so each kernel's average
+duration is measured live.  The line also carries, under "configs", the
+other workloads of the same path: a tiny fp32 step, one 16k sequence with
+per-head query temperatures, 32 ragged paged sequences of 8k-32k tokens,
+8 sequences of 64k tokens with logit and key-norm heads at p = 0.8 / 0.9 /
+0.99 (inputs rotated over seeded copies when one copy is under 512 MB), and
+the 64-layer x 256-step lifecycle at the Qwen3-32B attention shape.
 """
 from __future__ import annotations
 
@@ -53,6 +58,10 @@ def parse():
                     help="override the cache layout (0 = contiguous)")
     ap.add_argument("--no-amortization", action="store_true",
                     help="skip the selection-reuse timings")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config results (tiny, 16k batch 1, ragged, 64k mixed)")
+    ap.add_argument("--no-lifecycle-full", action="store_true",
+                    help="skip the 64-layer x 256-step lifecycle run")
     return ap.parse_args()
 
 
@@ -67,8 +76,9 @@ def kernel_bytes(w, A, k, kernel, fused):
       k_select       4A (scores) + A (mask)              [+ 4A]
       k_calsel       4A (scores) + A (mask)              [+ 4A] (both in one)
       k_compact*     2A*row (K, V) + A (mask) + 2k*row + 4k (rows, positions)
-                     + nch*(8d + 4) (chunk sums, counts)
-      k_attn         fused: 2W'*row + nch*(8d + 4); unfused: + 2k*row
+                     + nch*(8d + 4) (chunk sums, counts written)
+      k_attn         fused (the compaction attended the sparse and condensed
+                     tiers): 2W'*row; unfused: + 2k*row + nch*(8d + 4)
     plus q once per query head (score, attention) and o (attention).
     """
     import numpy as np
@@ -96,8 +106,8 @@ def kernel_bytes(w, A, k, kernel, fused):
         extra = q_bytes if kernel == "k_compact_attn" else 0
         return int((2 * A * row + A + 2 * k * row + 4 * k + nch * (8 * d + 4)).sum() + extra)
     if kernel == "k_attn":
-        sparse = 0 if fused else 2 * k * row
-        return int((2 * dense * row + sparse + nch * (8 * d + 4)).sum() + q_bytes)
+        rest = 0 if fused else 2 * k * row + nch * (8 * d + 4)
+        return int((2 * dense * row + rest).sum() + q_bytes)
     if kernel == "k_attn_merge":
         return o_bytes
     return 0
@@ -122,9 +132,10 @@ def traffic_from_profile(kernel, workload):
     return int(t["fetch_bytes"] * t["fetch_scale"] + t["write_bytes"] * t["write_scale"])
 
 
-def cpu_baseline(case, w, seconds):
-    """The CPU oracle (one BLAS thread) on the same workload: whole passes
-    over every (sequence, KV head) until about `seconds` of oracle time."""
+def cpu_baseline(case, w, seconds, threads):
+    """The CPU oracle on the same workload, NumPy/BLAS limited to `threads`
+    threads: whole passes over every (sequence, KV head) until about
+    `seconds` of oracle time."""
     import numpy as np
     import oracle as O
     from decode_kv_cache_head_amd import synth as S
@@ -137,7 +148,7 @@ def cpu_baseline(case, w, seconds):
             q = case.q[b, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
             heads.append((b, h, q))
     spent, passes, done = 0.0, 0, 0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         while True:
             for b, h, q in heads:
                 K = S.head_rows(case, b, h, "k").float().cpu().numpy()
@@ -155,10 +166,12 @@ def cpu_baseline(case, w, seconds):
                 continue
             break
     step_s = spent / done * len(heads)
-    return {"value": round(w.B / step_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": round(w.B / step_s, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
             "sample": f"{done} (sequence, KV head) oracle steps = {done / len(heads):.2f} passes "
                       f"over all {len(heads)} heads of the same workload, {spent:.1f} s of "
-                      f"single-thread oracle time; input copies to host not timed",
+                      f"oracle time with NumPy/BLAS limited to {threads} thread(s); input copies "
+                      f"to host not timed",
             "ms_per_step": round(step_s * 1e3, 1)}
 
 
@@ -174,6 +187,174 @@ def time_ms(fn, steps, warmup=2):
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def run_config(w, dev, steps, warmup, top_p=None, rotate_bytes=512 << 20, max_copies=64):
+    """One workload through hardkv_step.  When one copy of the inputs (q, K,
+    V) is smaller than rotate_bytes, up to max_copies seeded copies are drawn
+    and the timed steps cycle through them, so the 256 MB Infinity Cache
+    cannot serve the reads.  Returns the step time (plain loop), live
+    per-kernel times (launch observer), algorithmic bytes and bandwidth per
+    kernel."""
+    import numpy as np
+    import torch
+    from dataclasses import replace
+    from decode_kv_cache_head_amd import hardkv as H
+    from decode_kv_cache_head_amd import synth as S
+    if top_p is not None:
+        w = replace(w, p=top_p)
+    first = S.make_case(w, dev)
+    one = sum(t.numel() * t.element_size() for t in (first.q, first.k, first.v))
+    n_copies = 1 if one >= rotate_bytes else min(max_copies, -(-rotate_bytes // one))
+    cases = [first] + [S.make_case(replace(w, seed=w.seed + 1 + i), dev)
+                       for i in range(n_copies - 1)]
+    desc = H.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, w.W, w.C, w.p, first.ctx_cap,
+                       w.block_size, first.max_blocks)
+    ws = H.alloc_workspace(desc, dev)
+    caches = [H.cache_struct(c.k, c.v, c.ctx_len, c.block_table) for c in cases]
+    tiers = H.alloc_tiers(desc, dev)
+    out = torch.empty((w.B, w.Hq, w.d), device=dev)
+    stream = torch.cuda.current_stream()
+    nsteps = max(steps, n_copies)
+
+    def step(i):
+        H.step(desc, cases[i % n_copies].q, caches[i % n_copies], first.metric, tiers, out, ws)
+
+    for i in range(max(warmup, 2)):
+        step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(nsteps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / nsteps
+    with H.KernelTimer() as kt:
+        for i in range(nsteps):
+            kt.mark(stream)
+            step(i)
+        kt.mark(stream)
+    torch.cuda.synchronize()
+    per = {}
+    for name, ms in kt.durations():
+        per.setdefault(name, []).append(ms)
+    kernel_ms = {n: float(np.mean(v)) for n, v in per.items()}
+    # algorithmic bytes of the first copy's selection (the copies are draws of
+    # the same distribution)
+    step(0)
+    torch.cuda.synchronize()
+    A = np.maximum(np.array(w.T)[:, None] - w.W, 0) * np.ones((1, w.Hkv), np.int64)
+    k = tiers.count.cpu().numpy().astype(np.int64)
+    fused = "k_compact_attn" in kernel_ms
+    alg = {n: kernel_bytes(w, A, k, n, fused) for n in kernel_ms}
+    gbs = {n: alg[n] / (kernel_ms[n] * 1e-3) / 1e9 for n in kernel_ms}
+    total = sum(alg.values())
+    res = {"workload": w.name, "batch": w.B, "ctx": list(w.T) if len(set(w.T)) > 1 else w.T[0],
+           "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+           "dtype": "f32" if w.dtype == S.DT_F32 else "bf16",
+           "layout": f"paged{w.block_size}" if w.block_size else "contiguous",
+           "metrics": [int(x) for x in w.metrics] if w.metric else "all QK",
+           "top_p": w.p, "dense_window": w.W, "chunk": w.C,
+           "input_copies": n_copies, "inputs_mb_per_copy": round(one / 2**20, 2),
+           "step_ms": round(step_ms, 4), "tokens_per_s": round(w.B / (step_ms * 1e-3), 1),
+           "kept_fraction": round(float(k.sum() / max(A.sum(), 1)), 4),
+           "kernel_ms": {n: round(v, 4) for n, v in kernel_ms.items()},
+           "kernel_algorithmic_gb": {n: round(v / 1e9, 5) for n, v in alg.items()},
+           "kernel_hbm_gbs": {n: round(v, 1) for n, v in gbs.items()},
+           "kernel_peak_frac": {n: round(v / HBM_PEAK_GBS, 4) for n, v in gbs.items()},
+           "step_algorithmic_gb": round(total / 1e9, 4),
+           "step_hbm_gbs": round(total / (step_ms * 1e-3) / 1e9, 1)}
+    del cases, caches, tiers, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def lifecycle_full(dev, layers=64, steps=256):
+    """The multi-step lifecycle as specified for the Qwen3-32B attention shape:
+    64 layers with their own tiers, 64 sequences starting at 12288 tokens of
+    N(0, 1) bf16 keys and values, 256 decode steps of fresh N(0, 1) q/k/v per
+    layer (drawn on the device into per-step buffers before timing), window
+    512, chunk 64, p = 0.95, compaction in place.  One step = all 64 layers;
+    its time comes from events between steps."""
+    import numpy as np
+    import torch
+    from decode_kv_cache_head_amd import hardkv as H
+    B, Hq, Hkv, d, T0, W, C, p = 64, 64, 8, 128, 12288, 512, 64, 0.95
+    A = T0 - W
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    desc = H.make_desc(B, Hq, Hkv, d, H.BF16, W, C, p, T0 + steps)
+    per_layer = (2 * B * Hkv * desc.sparse_cap * d * 2 + 2 * B * Hkv * W * d * 2 +
+                 2 * B * Hkv * desc.chunk_cap * d * 4)
+    need = layers * per_layer * 1.02 + H.workspace_size(desc)
+    if free < need:
+        return {"skipped": f"needs {need / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} free"}
+    ws = H.alloc_workspace(desc, dev)
+    out = torch.empty((B, Hq, d), device=dev)
+    states = []
+    t_gen = time.perf_counter()
+    for layer in range(layers):
+        g = torch.Generator(device=dev).manual_seed(5000 + layer)
+        t = H.alloc_tiers(desc, dev)
+        for i in range(0, B, 8):
+            t.k[i:i + 8, :, :A] = torch.randn((8, Hkv, A, d), generator=g,
+                                              device=dev).to(torch.bfloat16)
+            t.v[i:i + 8, :, :A] = torch.randn((8, Hkv, A, d), generator=g,
+                                              device=dev).to(torch.bfloat16)
+        t.pos[:, :, :A] = torch.arange(A, dtype=torch.int32, device=dev)
+        t.count.fill_(A)
+        t.ksum.zero_()
+        t.vsum.zero_()
+        t.ccount.zero_()
+        rk = torch.randn((B, Hkv, W, d), generator=g, device=dev).to(torch.bfloat16)
+        rv = torch.randn((B, Hkv, W, d), generator=g, device=dev).to(torch.bfloat16)
+        states.append(H.State(rk, rv, t, torch.full((B,), T0, dtype=torch.int32, device=dev)))
+        if layer % 16 == 15:
+            print(f"[bench] lifecycle: {layer + 1} layers drawn", file=sys.stderr, flush=True)
+    # per-step inputs: a small bank of q / k / v draws per layer, cycled, so
+    # no random generation sits inside the timed steps
+    gq = torch.Generator(device=dev).manual_seed(77)
+    bank = 8
+    qs = torch.randn((bank, B, Hq, d), generator=gq, device=dev).to(torch.bfloat16)
+    ks = torch.randn((bank, B, Hkv, d), generator=gq, device=dev).to(torch.bfloat16)
+    vs = torch.randn((bank, B, Hkv, d), generator=gq, device=dev).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    pools = {}
+    ev[0].record(stream)
+    for s in range(steps):
+        for layer in range(layers):
+            j = (s * layers + layer) % bank
+            H.step_inplace(desc, qs[j], ks[(j + 3) % bank], vs[(j + 5) % bank], None, states[layer],
+                           out, ws)
+        ev[s + 1].record(stream)
+        if s in (0, 1, 9, 19, 49, 99, steps - 1):
+            # mean pool of layer 0, kept on the device (no host sync mid-run)
+            pools[str(s + 1)] = states[0].tiers.count.float().mean()
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    # pool sizes after the run, and the invariant that every token is in one tier
+    cnt = states[0].tiers.count.float()
+    tot = states[0].tiers.count.long() + states[0].tiers.ccount.long().sum(-1) + W
+    assert bool(torch.all(tot == T0 + steps)), "token count invariant"
+    res = {"shape": "qwen3-32b attention (64 q / 8 KV heads, d = 128), 64 layers, B = 64, "
+                    "T0 = 12288, 256 steps, W = 512, C = 64, p = 0.95",
+           "layers": layers, "steps": steps, "generation_s_untimed": round(gen_s, 1),
+           "total_s": round(sum(ms) * 1e-3, 4),
+           "step1_ms": round(ms[0], 3),
+           "step2_ms": round(ms[1], 3),
+           "steps_2_to_256_mean_ms": round(float(np.mean(ms[1:])), 4),
+           "steps_50_to_256_mean_ms": round(float(np.mean(ms[49:])), 4),
+           "step_ms_at": {str(i + 1): round(ms[i], 4) for i in (0, 1, 9, 19, 49, 99, steps - 1)},
+           "pool_median_after_run": int(cnt.median().item()),
+           "mean_pool_after_step": {k: round(float(v.item()), 1) for k, v in pools.items()},
+           "tokens_per_s_all_layers": round(B * steps / (sum(ms) * 1e-3), 1),
+           "steady_tokens_per_s_all_layers": round(B / (float(np.mean(ms[49:])) * 1e-3), 1)}
+    del states, ws, qs, ks, vs
+    torch.cuda.empty_cache()
+    return res
 
 
 def amortization(w, case, steps, horizons=(1, 2, 4, 8, 16, 32)):
@@ -507,11 +688,13 @@ def main():
             "traffic": traffic, "algorithmic_bytes": alg[dom],
             "avg_launch_ms": round(kernel_ms[dom], 4)}
     step_bytes = sum(alg.values())
-    tok_s = w.B / (ms_per_step * 1e-3)
+    # the headline figure is the plain loop (no per-kernel events in it)
+    tok_s = w.B / (plain_ms * 1e-3)
     res = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(plain_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == S.DT_BF16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "ctx": max(w.T), "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.d, "kv_dtype": "bf16" if w.dtype else "f32",
@@ -523,8 +706,8 @@ def main():
         "kernel_hbm_gbs": {n: round(v, 1) for n, v in gbs.items()},
         "kernel_peak_frac": {n: round(v / HBM_PEAK_GBS, 4) for n, v in gbs.items()},
         "step_algorithmic_gb": round(step_bytes / 1e9, 4),
-        "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "step_ms_without_observer": round(plain_ms, 4),
+        "step_hbm_gbs": round(step_bytes / (plain_ms * 1e-3) / 1e9, 1),
+        "step_ms_with_kernel_events": round(ms_per_step, 4),
         "graph_replay_ms_per_step": round(graph_ms, 4),
         "device_copy_gbs": round(copy_gbs, 1),
         "kept_fraction": round(float(k.sum() / max(A.sum(), 1)), 4),
@@ -533,6 +716,9 @@ def main():
             "layers": QWEN3_8B_LAYERS, "value": round(tok_s / QWEN3_8B_LAYERS, 1)},
         "dtype_note": "bf16 q/K/V in HBM; float64 score accumulation, 2^-47 fixed-point "
                       "top-p masses, float32 attention",
+        "roofline_note": "achieved = algorithmic bytes of one launch / its live average "
+                         "duration; traffic = counter bytes (FETCH_SIZE, WRITE_SIZE) of the "
+                         "committed profile when it was taken on the current kernel source",
     }
     if not args.no_amortization and args.block_size is None:
         # the step with attention sinks and / or attention-weighted merging
@@ -582,7 +768,25 @@ def main():
         res["lifecycle_block_manager"] = lifecycle(dev, pool_block=64)
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(case, w, args.cpu_seconds)
+        cores = len(os.sched_getaffinity(0))
+        res["cpu_baseline"] = cpu_baseline(case, w, args.cpu_seconds, cores)
+        res["cpu_baseline"]["single_thread"] = cpu_baseline(case, w, args.cpu_seconds / 2, 1)
+        res["cpu_baseline"]["host_cores_available"] = cores
+    del case, cache, tiers, ws, out
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        cfg = {}
+        for tag, name, p in (("1", "tiny", None), ("2", "qwen8b_b1_16k", None),
+                             ("3", "qwen8b_b32_ragged_paged", None),
+                             ("4_p0.8", "qwen8b_b8_64k_mixed", 0.8),
+                             ("4_p0.9", "qwen8b_b8_64k_mixed", 0.9),
+                             ("4_p0.99", "qwen8b_b8_64k_mixed", 0.99)):
+            print(f"[bench] config {tag}: {name}", file=sys.stderr, flush=True)
+            cfg[tag] = run_config(S.workload(name), dev, args.steps, args.warmup, top_p=p)
+        res["configs"] = cfg
+    if not args.no_lifecycle_full:
+        print("[bench] lifecycle: 64 layers x 256 steps", file=sys.stderr, flush=True)
+        res.setdefault("configs", {})["5"] = lifecycle_full(dev)
     print(json.dumps(res), flush=True)
 
 

@@ -348,9 +348,15 @@ def merge_weights(c, m):
 
     Reading of "weighted merging" (section 2.A, Tier 3): a token enters its
     chunk with its calibrated attention weight exp(c - m), the quantity the
-    top-p selection ranked it by.  A weight below e^-60 of the head's largest
-    counts as e^-60, so a chunk never has zero total weight, and float32
-    products of such weights with the cache's values stay normal numbers.
+    top-p selection ranked it by.  The pages give no formula, and the weight
+    needs a floor: exp(c - m) of a token far below the head's maximum is 0
+    in any finite precision, which leaves the weighted mean of a chunk made
+    only of such tokens undefined (0 / 0).  A weight below e^-60 counts as
+    e^-60: such a chunk becomes the plain mean of its tokens (equal weights),
+    and a chunk whose heaviest token has weight w_max moves by at most a
+    relative n e^-60 / w_max (n tokens), nothing for any chunk holding a
+    token within a few dozen nats of the maximum.  The value 60 is this
+    reading's choice (about 26 decades below the heaviest token).
     """
     return np.exp(np.maximum(_f64(c) - float(m), MERGE_FLOOR))
 

@@ -147,3 +147,58 @@ def test_lifecycle_graph_replayed_300_steps(gpu, pool_block):
     # tokens kept flowing into the condensed tier over the replays
     assert int(tg.ccount.sum()) > B * Hkv * (T0 - W) // 4
     print("pool after", steps, "steps:", te.count.tolist(), file=sys.stderr, flush=True)
+
+
+def test_lifecycle_graph_replayed_10000_steps(gpu):
+    """One capture of hardkv_step_inplace replayed for 10000 consecutive
+    decode steps (the pages stress graph compatibility over tens of
+    thousands of decoding steps) against the same steps run eagerly: every
+    step's attention output and the final state bit for bit.  The inputs of
+    all steps are drawn up front and copied into the captured buffers before
+    each replay; outputs are kept per step and compared at the end."""
+    B, Hq, Hkv, d, T0, W, C, p, steps = 2, 16, 2, 128, 700, 64, 32, 0.9, 10000
+    desc, st_g = _lifecycle(gpu, 31, B, Hq, Hkv, d, T0, W, C, p, steps)
+    _, st_e = _lifecycle(gpu, 31, B, Hq, Hkv, d, T0, W, C, p, steps)
+    ws_g, ws_e = H.alloc_workspace(desc, gpu), H.alloc_workspace(desc, gpu)
+    gen = torch.Generator(device=gpu).manual_seed(32)
+    Q = (torch.randn((steps, B, Hq, d), generator=gen, device=gpu) * 1.5).to(torch.bfloat16)
+    KN = torch.randn((steps, B, Hkv, d), generator=gen, device=gpu).to(torch.bfloat16)
+    VN = torch.randn((steps, B, Hkv, d), generator=gen, device=gpu).to(torch.bfloat16)
+    q = torch.zeros_like(Q[0])
+    kn = torch.zeros_like(KN[0])
+    vn = torch.zeros_like(VN[0])
+    out_g = torch.empty((B, Hq, d), device=gpu)
+    outs_g = torch.empty((steps, B, Hq, d), device=gpu)
+    outs_e = torch.empty_like(outs_g)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):  # recorded only: the state is not advanced here
+        H.step_inplace(desc, q, kn, vn, None, st_g, out_g, ws_g)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        q.copy_(Q[s])
+        kn.copy_(KN[s])
+        vn.copy_(VN[s])
+        g.replay()
+        outs_g[s].copy_(out_g)
+        H.step_inplace(desc, Q[s], KN[s], VN[s], None, st_e, outs_e[s], ws_e)
+        if s % 2000 == 1999:
+            torch.cuda.synchronize()
+            print(f"replayed {s + 1} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    same = (outs_g.view(steps, -1).view(torch.int32) == outs_e.view(steps, -1).view(torch.int32)).all(1)
+    assert bool(same.all()), f"first differing step {int((~same).nonzero()[0])}"
+    assert int(st_g.seq_len[0]) == T0 + steps and torch.equal(st_g.seq_len, st_e.seq_len)
+    assert torch.equal(st_g.ring_k, st_e.ring_k) and torch.equal(st_g.ring_v, st_e.ring_v)
+    tg, te = st_g.tiers, st_e.tiers
+    assert torch.equal(tg.count, te.count)
+    assert torch.equal(tg.ccount, te.ccount)
+    assert torch.equal(tg.ksum, te.ksum) and torch.equal(tg.vsum, te.vsum)
+    for b in range(B):
+        for h in range(Hkv):
+            n = int(te.count[b, h])
+            assert torch.equal(tg.pos[b, h, :n], te.pos[b, h, :n])
+            assert torch.equal(tg.k[b, h, :n], te.k[b, h, :n])
+    # every token is in exactly one tier after 10000 steps
+    tot = te.count.long() + te.ccount.long().sum(-1) + W
+    assert torch.all(tot == T0 + steps)
+    print("pool after", steps, "steps:", te.count.tolist(), file=sys.stderr, flush=True)

@@ -108,7 +108,11 @@ def test_step_reduces_to_full_attention():
     q = bf(rng.standard_normal((G, d)))
     K = bf(rng.standard_normal((T, d)))
     V = bf(rng.standard_normal((T, d)))
-    ref = O.full_attention(q, K, V)
+    # full softmax attention from torch's library routine (float64, CPU)
+    qt = torch.tensor(np.asarray(q, np.float64))[None, :, None, :]
+    kt = torch.tensor(np.asarray(K, np.float64))[None, None].expand(1, G, -1, -1).contiguous()
+    vt = torch.tensor(np.asarray(V, np.float64))[None, None].expand(1, G, -1, -1).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, :, 0].numpy()
     for calib in (O.CALIB_SPREAD, O.CALIB_ENTROPY):
         for C, p in ((32, 1.0), (1, 0.4)):
             r = O.step_head(q, K, V, T, 50, C, p, O.METRIC_KEYDIFF, calib=calib)
