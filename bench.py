@@ -189,6 +189,16 @@ def time_ms(fn, steps, warmup=2):
     return e0.elapsed_time(e1) / steps
 
 
+def hold(stream, cycles=120_000_000):
+    """Keeps the GPU busy for ~50 ms with torch's bounded spin kernel so the
+    host can enqueue ahead of it (no-op where torch lacks it)."""
+    import torch
+    spin = getattr(torch.cuda, "_sleep", None)
+    if spin is not None:
+        with torch.cuda.stream(stream):
+            spin(cycles)
+
+
 def run_config(w, dev, steps, warmup, top_p=None, rotate_bytes=512 << 20, max_copies=64):
     """One workload through hardkv_step.  When one copy of the inputs (q, K,
     V) is smaller than rotate_bytes, up to max_copies seeded copies are drawn
@@ -222,6 +232,11 @@ def run_config(w, dev, steps, warmup, top_p=None, rotate_bytes=512 << 20, max_co
 
     for i in range(max(warmup, 2)):
         step(i)
+    torch.cuda.synchronize()
+    # the stream is first held by a bounded spin kernel, so the host enqueues
+    # every timed launch (and the observer's events) before the GPU reaches
+    # them: steps of ~0.1 ms would otherwise time the host's launch rate
+    hold(stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(nsteps):
@@ -229,6 +244,7 @@ def run_config(w, dev, steps, warmup, top_p=None, rotate_bytes=512 << 20, max_co
     e1.record(stream)
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / nsteps
+    hold(stream)
     with H.KernelTimer() as kt:
         for i in range(nsteps):
             kt.mark(stream)
@@ -323,6 +339,7 @@ def lifecycle_full(dev, layers=64, steps=256):
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     pools = {}
+    hold(stream)
     ev[0].record(stream)
     for s in range(steps):
         for layer in range(layers):
@@ -528,6 +545,9 @@ def lifecycle(dev, reps=5, steady_steps=48, pool_block=0):
     for i in range(steady_steps - 8):
         H.step_inplace(desc, qs[i % 4], kn, vn, None, st, out, ws)
     torch.cuda.synchronize()
+    # steady steps take ~0.1 ms of GPU time, about what the host needs to
+    # launch one: the stream is held first so the timed steps run back to back
+    hold(torch.cuda.current_stream())
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(8):
@@ -543,6 +563,7 @@ def lifecycle(dev, reps=5, steady_steps=48, pool_block=0):
     with torch.cuda.graph(graph):
         H.step_inplace(desc, qg, kn, vn, None, st, out, ws)
     torch.cuda.synchronize()
+    hold(torch.cuda.current_stream())
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(8):

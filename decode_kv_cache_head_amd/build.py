@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhardkv.so")
 SOURCES = ["abi.hip", "k_score.hip", "k_select.hip", "k_compact.hip", "k_attn.hip",
-           "k_lifecycle.hip"]
+           "k_lifecycle.hip", "k_life.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -617,39 +617,56 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   ap.q = q;  // the append also widens this step's queries for the score
   ap.q64 = (double*)(w + L.q64);
   ap.hq = d->num_q_heads;
-  if (pg.table) launch_pool_grow(ap, st);
-  launch_append(ap, st);
-
   const Cand cand{nullptr, t->count, d->dense_window, d->ctx_cap, d->sparse_cap,
                   d->num_kv_heads};
-  Rows pk = region_rows(d, t->k, d->sparse_cap);
-  Rows pv = region_rows(d, t->v, d->sparse_cap);
-  if (pg.table) {
-    // pool rows through per-head block tables (one head per block)
-    for (Rows* r : {&pk, &pv}) {
-      r->table = pg.table;
-      r->hkv = 1;
-      r->lbs = pg.lbs;
-      r->max_blocks = pg.maxb;
-      r->headtab = d->num_kv_heads;
-    }
-  }
   float* logit = (float*)(w + L.logit);
   float* l2 = (float*)(w + L.l2);
   double* stats = (double*)(w + L.stats);
   uint8_t* mask = (uint8_t*)(w + L.mask);
   int32_t* count = (int32_t*)(w + L.count);
-  do_score(d, L, w, q, nullptr, pk, cand, d->sparse_cap, metric, logit, l2, st, true);
-  const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
-  // separate launches: after the first steps the pools are a few hundred
-  // tokens, where the fused kernel's one-workgroup-per-CU footprint (scores
-  // in registers, weights in LDS) costs more than the two light kernels
-  launch_calibrate(sa, st);
-  launch_select(sa, st);
-  CompactArgs ca = compact_args(d, L, w, pk, pv, cand, d->sparse_cap, mask, t);
-  ca.pg = pg;
-  launch_compact_inplace(ca, st);
-  if (pg.table) launch_pool_shrink(pg, t->count, d->batch * d->num_kv_heads, st);
+  Rows pk = region_rows(d, t->k, d->sparse_cap);
+  Rows pv = region_rows(d, t->v, d->sparse_cap);
+  if (!metric && !pg.table) {
+    // every head on the logit, per-head regions: append, score, select and
+    // compaction of each head in one workgroup
+    LifeArgs la{};
+    la.ap = ap;
+    la.ap.q64 = nullptr;
+    la.ca = compact_args(d, L, w, pk, pv, cand, d->sparse_cap, mask, t);
+    la.q = q;
+    la.logit = logit;
+    la.mask = mask;
+    la.cap_stride = d->sparse_cap;
+    la.stats = stats;
+    la.top_p = d->top_p;
+    la.wscale = mass_scale(d->sparse_cap);
+    la.scale = 1.0 / sqrt((double)d->head_dim);
+    launch_life(la, st);
+  } else {
+    if (pg.table) launch_pool_grow(ap, st);
+    launch_append(ap, st);
+    if (pg.table) {
+      // pool rows through per-head block tables (one head per block)
+      for (Rows* r : {&pk, &pv}) {
+        r->table = pg.table;
+        r->hkv = 1;
+        r->lbs = pg.lbs;
+        r->max_blocks = pg.maxb;
+        r->headtab = d->num_kv_heads;
+      }
+    }
+    do_score(d, L, w, q, nullptr, pk, cand, d->sparse_cap, metric, logit, l2, st, true);
+    const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
+    // separate launches: after the first steps the pools are a few hundred
+    // tokens, where the fused kernel's one-workgroup-per-CU footprint (scores
+    // in registers, weights in LDS) costs more than the two light kernels
+    launch_calibrate(sa, st);
+    launch_select(sa, st);
+    CompactArgs ca = compact_args(d, L, w, pk, pv, cand, d->sparse_cap, mask, t);
+    ca.pg = pg;
+    launch_compact_inplace(ca, st);
+    if (pg.table) launch_pool_shrink(pg, t->count, d->batch * d->num_kv_heads, st);
+  }
   AttnArgs a = attn_args(d, L, w, q, t, out);
   if (pg.table) {
     a.sk = pk;

@@ -192,6 +192,9 @@ struct AttnArgs {
   // lifecycle: advance[b] += 1 for every sequence once the outputs are
   // written (by the merge); null elsewhere
   int32_t* advance;
+  // set by the launcher: the chunk launch holds one tile per head, which
+  // joins the head's partials itself (no merge launch follows)
+  bool merge_chunks;
 };
 int attn_max_tiles(int W, int sparse_cap, int chunk_cap);
 void launch_attn(const AttnArgs& a, hipStream_t st);
@@ -220,6 +223,23 @@ struct AppendArgs {
   int hq;
 };
 void launch_append(const AppendArgs& a, hipStream_t st);
+
+// The lifecycle step's append, score, calibrate + select and in-place
+// compaction in one workgroup per (b, h) (launches with every head on the
+// logit and per-head pool regions).
+struct LifeArgs {
+  AppendArgs ap;        // ring, pool, lengths, the new token (q64 unused)
+  CompactArgs ca;       // in-place compaction of the pool (mask in the workspace)
+  const void* q;        // [B][Hq][D]
+  float* logit;         // workspace [B][Hkv][cap_stride]
+  uint8_t* mask;        // workspace [B][Hkv][cap_stride] (ca.mask, written here)
+  int64_t cap_stride;
+  double* stats;        // workspace [B][Hkv][4]
+  float top_p;
+  double wscale;        // fixed-point scale of the selection masses
+  double scale;         // 1 / sqrt(D)
+};
+void launch_life(const LifeArgs& a, hipStream_t st);
 // block manager: blocks for the rows the append is about to write, and the
 // return of blocks past each head's count after the compaction
 void launch_pool_grow(const AppendArgs& a, hipStream_t st);

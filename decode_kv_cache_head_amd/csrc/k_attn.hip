@@ -610,23 +610,11 @@ __device__ inline void attn_tiles(const AttnArgs& a) {
   }
 }
 
-template <typename T, int D, int G, bool P, bool PS, int PART>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-  attn_tiles<T, D, G, P, PS, PART>(a);
-}
-
-// One wave per (b, query head): joins the partials of every tile.  With
-// a.advance (the lifecycle), thread i < B also moves sequence i on by one
-// token; nothing in this launch reads those lengths.
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
-  if (a.advance) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < a.B) a.advance[i] += 1;
-  }
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (wid >= a.B * a.hq) return;
-  const int b = wid / a.hq, qh = wid % a.hq, h = qh / G, g = qh % G;
+// Joins the partials of every tile of query head qh of sequence b into its
+// output row; one wave (lane = this thread's lane).
+template <int D, int G>
+__device__ inline void merge_row(const AttnArgs& a, int b, int qh, int lane) {
+  const int h = qh / G, g = qh % G;
   const TileCounts tc = tile_counts(a, b, h);
   const int nt = tc.first + tc.ntd + tc.nts + tc.ntc;
   const int64_t bh = (int64_t)b * a.hkv + h;
@@ -664,6 +652,39 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   for (int e = 0; e < PE; ++e) out[lane * PE + e] = S > 0.f ? O[e] / S : 0.f;
 }
 
+template <typename T, int D, int G, bool P, bool PS, int PART>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+  attn_tiles<T, D, G, P, PS, PART>(a);
+  if constexpr (PART == 2) {
+    // the step's last launch: with merge_chunks (the ring's tiers, one chunk
+    // tile per head) this workgroup holds the head's only chunk tile, and
+    // the row tiles' partials came from the launch before, so it joins them
+    // all itself and, for head 0, advances the sequence
+    if (a.merge_chunks) {
+      const int h = blockIdx.y, b = blockIdx.z;
+      if (blockIdx.x != 0) return;
+      __syncthreads();  // this tile's partial is written
+      const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+      for (int g = w; g < G; g += 4) merge_row<D, G>(a, b, h * G + g, lane);
+      if (h == 0 && threadIdx.x == 0) a.advance[b] += 1;
+    }
+  }
+}
+
+// One wave per (b, query head): joins the partials of every tile.  With
+// a.advance (the lifecycle), thread i < B also moves sequence i on by one
+// token; nothing in this launch reads those lengths.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  if (a.advance) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < a.B) a.advance[i] += 1;
+  }
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wid >= a.B * a.hq) return;
+  merge_row<D, G>(a, wid / a.hq, wid % a.hq, lane);
+}
+
 // W: dense rows at most (window plus sinks)
 // (the fused compaction's tiles hold at least 576 candidates, so they fit in
 // the sparse tier's slots too)
@@ -688,9 +709,14 @@ static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((k_attn<T, D, G, P, false, split ? 1 : 0>), grid, dim3(256), 0, st, a);
   }
   if (split && gc > 0 && a.fused_tt == 0) {
+    // the ring's tiers give every head exactly ceil(chunk_cap / tile) chunk
+    // tiles; with one, that tile joins the head's partials (no merge launch)
+    AttnArgs c = a;
+    c.merge_chunks = a.ring && gc == 1;
     observe("k_attn_chunks", st);
     hipLaunchKernelGGL((k_attn<T, D, G, false, false, 2>), dim3(gc, a.hkv, a.B), dim3(256), 0, st,
-                       a);
+                       c);
+    if (c.merge_chunks) return;
   }
   observe("k_attn_merge", st);
   hipLaunchKernelGGL((k_attn_merge<T, D, G>), dim3(ceil_div((int64_t)a.B * a.hq, 4)), dim3(256),

@@ -15,55 +15,9 @@
 //   position first, as many as needed.  A final ordered pass writes the mask.
 #include <type_traits>
 
-#include "internal.h"
+#include "select_core.h"
 
 namespace hk {
-
-template <int NW>
-__device__ inline double block_sum_f64(double v, double* sh) {
-  v = wave_sum_f64(v);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  __syncthreads();
-  if (l == 0) sh[w] = v;
-  __syncthreads();
-  double r = sh[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) r += sh[i];
-  return r;
-}
-
-template <int NW>
-__device__ inline float block_max_f32(float v, float* sh) {
-  v = wave_max_f32(v);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  __syncthreads();
-  if (l == 0) sh[w] = v;
-  __syncthreads();
-  float r = sh[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) r = fmaxf(r, sh[i]);
-  return r;
-}
-
-template <int NW>
-__device__ inline void block_sum2_f64(double& a, double& b, double* sh) {
-  a = wave_sum_f64(a);
-  b = wave_sum_f64(b);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  __syncthreads();
-  if (l == 0) {
-    sh[2 * w] = a;
-    sh[2 * w + 1] = b;
-  }
-  __syncthreads();
-  a = sh[0];
-  b = sh[1];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) {
-    a += sh[2 * i];
-    b += sh[2 * i + 1];
-  }
-}
 
 // Entropy-matched temperature (HARDKV_CALIB_ENTROPY) of one head, run by the
 // whole workgroup.  each_logit(f) / each_metric(f) call f on every logit /
@@ -197,125 +151,6 @@ __global__ __launch_bounds__(256) void k_calibrate(Cand cand, const int8_t* __re
   }
 }
 
-// --------------------------------------------------------------- select ---
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
-
-// ceil(p * Z) exactly, p a float in (0, 1), Z <= 2^63.
-__device__ inline uint64_t ceil_mul(float p, uint64_t Z) {
-  int ex;
-  const float f = frexpf(p, &ex);                      // p = f * 2^ex, f in [0.5, 1)
-  const uint64_t mant = (uint64_t)(f * 16777216.0f);   // exact 24-bit significand
-  const int sh = 24 - ex;                              // p = mant * 2^-sh, sh >= 24
-  const unsigned __int128 prod = (unsigned __int128)mant * Z;
-  if (sh >= 120) return prod ? 1 : 0;
-  const unsigned __int128 one = 1;
-  return (uint64_t)((prod + ((one << sh) - 1)) >> sh);
-}
-
-// Histogram slot of bin b when NB bins are searched: one pad slot after
-// every NB / 64 bins, so the 64 lanes of find_bin, each summing its own run
-// of consecutive bins, read different LDS banks.
-template <int NB>
-__device__ __forceinline__ int hslot(uint32_t b) {
-  return (int)(b + b / (NB / 64));
-}
-constexpr int kHistSlots = 2048 + 64;
-
-struct SelShared {
-  unsigned long long hist[kHistSlots];
-  unsigned long long target;
-  unsigned long long above;
-  unsigned long long total;   // fixed-point mass of the head (pass 1)
-  unsigned long long tally;   // k_calsel: selected count << 32 | waves done
-  uint32_t bin;
-  int wc[kSelWaves];
-  int red[kSelWaves];
-  int tpre[16 * kSelWaves];  // k_calsel: ties before (slot, wave), position order
-};
-
-// Lane l's value moved from lane l - K of its 16-lane row (0 for the first
-// K lanes of the row), both 32-bit halves through DPP row shifts.
-template <int K>
-__device__ __forceinline__ uint64_t row_shr_u64(uint64_t v) {
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x110 + K, 0xF, 0xF, true);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x110 + K, 0xF, 0xF, true);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-// Inclusive prefix sum over the 64 lanes of the wave: Hillis-Steele steps
-// inside each 16-lane row, then the totals of the rows below added from
-// lanes 15, 31 and 47.
-__device__ __forceinline__ uint64_t wave_prefix_u64(uint64_t v) {
-  v += row_shr_u64<1>(v);
-  v += row_shr_u64<2>(v);
-  v += row_shr_u64<4>(v);
-  v += row_shr_u64<8>(v);
-  const uint64_t r0 = readlane_u64(v, 15), r1 = readlane_u64(v, 31), r2 = readlane_u64(v, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  return v + (row >= 1 ? r0 : 0ull) + (row >= 2 ? r1 : 0ull) + (row >= 3 ? r2 : 0ull);
-}
-
-// Run by wave 0: the largest bin whose suffix mass (bins at or above it)
-// reaches `target`; records the bin and the mass strictly above it.  With
-// from_total, the target is first set to max(ceil(p * total), 1) and the
-// total is recorded.
-template <int NB>
-__device__ inline void find_bin(SelShared& S, bool from_total, float p) {
-  const int lane = threadIdx.x;
-  constexpr int PER = NB / 64;
-  unsigned long long s = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) s += S.hist[lane * (PER + 1) + i];
-  // suffix sums over the lanes: total minus the exclusive prefix
-  const unsigned long long pre = wave_prefix_u64(s);
-  const unsigned long long total = readlane_u64(pre, 63);
-  const unsigned long long suf = total - pre + s;
-  unsigned long long target;
-  if (from_total) {
-    target = ceil_mul(p, total);
-    if (target < 1) target = 1;
-  } else {
-    target = S.target;
-  }
-  const unsigned long long ok = __ballot(suf >= target);
-  int L = __popcll(ok) - 1;  // suf falls with the lane: lanes 0..L reach the target
-  L = L < 0 ? 0 : L;
-  // inside lane L's PER bins: suffix sums over PER lanes, the same rule
-  const unsigned long long base = readlane_u64(suf - s, L);  // mass above the chunk
-  const unsigned long long hv = lane < PER ? S.hist[L * (PER + 1) + lane] : 0ull;
-  const unsigned long long pre2 = wave_prefix_u64(hv);
-  const unsigned long long suf2 = readlane_u64(pre2, 63) - pre2 + hv;
-  const unsigned long long ok2 = __ballot(lane < PER && base + suf2 >= target);
-  int J = __popcll(ok2) - 1;
-  J = J < 0 ? 0 : J;
-  if (lane == J) {
-    S.bin = L * PER + J;
-    S.above = base + suf2 - hv;
-  }
-  if (from_total && lane == 0) {
-    S.target = target;
-    S.total = total;
-  }
-}
-
-// Where a selection's size goes: count[bh] = k and, when a mode array is
-// given, the head's rewrite / sparse-loading choice for (A = n, k).
-struct CountOut {
-  int32_t* count;
-  uint8_t* mode;
-  hardkv_policy pol;
-  int W;
-  __device__ inline void put(int64_t bh, int n, int k) const {
-    count[bh] = k;
-    if (mode) mode[bh] = plan_mode(pol, n, k, W);
-  }
-};
-
 __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t* __restrict__ metric,
                                                         const float* __restrict__ logit,
                                                         const float* __restrict__ l2,
@@ -344,88 +179,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   const double shift = stats[bh * 4 + 0], scale = stats[bh * 4 + 1], m = stats[bh * 4 + 2];
   auto cv = [&](int t) -> float { return is_l2 ? cval(x[t], shift, scale) : x[t]; };
 
-  // pass 1: top 11 bits of the key
-  for (int i = tid; i < kHistSlots; i += kSelThreads) S.hist[i] = 0;
-  __syncthreads();
-  for (int t = tid; t < n; t += kSelThreads) {
-    const float c = cv(t);
-    const uint64_t w = wfix(c, m, wscale, s_et);
-    if (w) atomicAdd(&S.hist[hslot<2048>(okey(c) >> 21)], (unsigned long long)w);
-  }
-  __syncthreads();
-  if (tid < 64) find_bin<2048>(S, true, top_p);
-  __syncthreads();
-  const unsigned long long target = S.target;
-  const uint32_t b1 = S.bin;
-  unsigned long long above = S.above;
-  __syncthreads();
-
-  // pass 2: next 11 bits inside bin b1
-  for (int i = tid; i < kHistSlots; i += kSelThreads) S.hist[i] = 0;
-  if (tid == 0) S.target = target - above;
-  __syncthreads();
-  for (int t = tid; t < n; t += kSelThreads) {
-    const float c = cv(t);
-    const uint32_t k = okey(c);
-    if ((k >> 21) == b1)
-      atomicAdd(&S.hist[hslot<2048>((k >> 10) & 2047u)],
-                (unsigned long long)wfix(c, m, wscale, s_et));
-  }
-  __syncthreads();
-  if (tid < 64) find_bin<2048>(S, false, top_p);
-  __syncthreads();
-  const uint32_t b2 = S.bin;
-  above += S.above;
-  const unsigned long long t2 = S.target;
-  __syncthreads();
-
-  // pass 3: last 10 bits inside (b1, b2)
-  for (int i = tid; i < kHistSlots; i += kSelThreads) S.hist[i] = 0;
-  if (tid == 0) S.target = t2 - S.above;
-  __syncthreads();
-  const uint32_t pre = (b1 << 11) | b2;
-  for (int t = tid; t < n; t += kSelThreads) {
-    const float c = cv(t);
-    const uint32_t k = okey(c);
-    if ((k >> 10) == pre)
-      atomicAdd(&S.hist[hslot<1024>(k & 1023u)], (unsigned long long)wfix(c, m, wscale, s_et));
-  }
-  __syncthreads();
-  if (tid < 64) find_bin<1024>(S, false, top_p);
-  __syncthreads();
-  const uint32_t kstar = (pre << 10) | S.bin;
-  above += S.above;
-  // all tokens tied at K* carry the same weight; take r of them
-  const unsigned long long wstar = wfix(okey_inv(kstar), m, wscale, s_et);
-  const unsigned long long need = target - above;
-  const unsigned long long r = (need + wstar - 1) / wstar;
-
-  // pass 4: mask, ties by ascending position
-  const int wv = tid >> 6, ln = tid & 63;
-  unsigned long long carried = 0;
-  int nsel = 0;
-  for (int t0 = 0; t0 < n; t0 += kSelThreads) {
-    const int t = t0 + tid;
-    const bool valid = t < n;
-    const uint32_t k = valid ? okey(cv(t)) : 0u;
-    const bool tie = valid && k == kstar;
-    const int ntie = __syncthreads_count(tie);
-    unsigned long long rank = 0;
-    if (ntie) {
-      const unsigned long long bal = __ballot(tie);
-      if (ln == 0) S.wc[wv] = __popcll(bal);
-      __syncthreads();
-      int off = 0;
-      for (int i = 0; i < wv; ++i) off += S.wc[i];
-      __syncthreads();
-      rank = carried + off + __popcll(bal & ((1ull << ln) - 1ull));
-      carried += ntie;
-    }
-    const bool sel = valid && (k > kstar || (tie && rank < r));
-    if (valid) mk[t] = sel ? 1 : 0;
-    nsel += sel;
-  }
+  const int nsel = select_head<kSelThreads>(S, n, cv, m, top_p, wscale, s_et, mk);
   // block sum of nsel
+  const int wv = tid >> 6, ln = tid & 63;
   int v = nsel;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
