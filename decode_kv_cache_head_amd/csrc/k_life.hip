@@ -171,8 +171,8 @@ __global__ __launch_bounds__(kLifeThreads) void k_life(LifeArgs A) {
     if (!(A.top_p < 1.0f)) {
       for (int t = tid; t < n; t += NT) mk[t] = 1;
     } else {
-      select_head<NT>(U.sel, n, [&](int t) -> float { return logit[t]; }, (double)m, A.top_p,
-                      A.wscale, s_et, mk);
+      select_head<NT>(U.sel, n, logit, [](float raw) -> float { return raw; }, (double)m,
+                      A.top_p, A.wscale, s_et, mk);
     }
   }
   if (tid == 0) {

@@ -78,51 +78,89 @@ __device__ inline void entropy_temperature(EachLogit each_logit, EachMetric each
 }
 
 // ------------------------------------------------------------ calibrate ---
-__global__ __launch_bounds__(256) void k_calibrate(Cand cand, const int8_t* __restrict__ metric,
-                                                   const float* __restrict__ logit,
-                                                   const float* __restrict__ l2,
-                                                   int64_t cap_stride, double* __restrict__ stats,
-                                                   int calib) {
-  __shared__ double shd[8];
-  __shared__ float shf[4];
+// One 1024-thread workgroup per (b, h); every pass reads the head's scores
+// with eight loads in flight per thread (each thread adds its values in
+// position order, so the float64 sums do not depend on the batching).
+//   logit heads:   m = max x; Z = sum exp(x - m)
+//   spread rule:   sums of x and s and max s; then the two squared
+//                  deviations; shift = mean s, scale = sd(x) / sd(s); the
+//                  calibration is non-decreasing in s, so m = cval(max s)
+//   entropy rule:  the bisection of entropy_temperature, then m and Z
+// exp of non-positive arguments through exp_nonpos.
+constexpr int kCalThreads = 1024;
+constexpr int kCalWaves = kCalThreads / 64;
+
+__global__ __launch_bounds__(kCalThreads) void k_calibrate(Cand cand, const int8_t* __restrict__ metric,
+                                                           const float* __restrict__ logit,
+                                                           const float* __restrict__ l2,
+                                                           int64_t cap_stride,
+                                                           double* __restrict__ stats, int calib) {
+  constexpr int U = 8;
+  __shared__ double shd[2 * kCalWaves];
+  __shared__ float shf[kCalWaves];
+  __shared__ double s_et[64];
   const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
   const int n = cand.n(b, h);
   const int64_t bh = (int64_t)b * hkv + h;
   const float* x = logit + bh * cap_stride;
+  const float* sv = l2 + bh * cap_stride;
   const bool is_l2 = aux_metric(metric, h);  // second score array
+  exp_table_init(s_et);
   double shift = 0.0, scale = 1.0;
+  float m = -INFINITY;
   if (is_l2 && calib == HARDKV_CALIB_ENTROPY) {
-    const float* s = l2 + bh * cap_stride;
     shift = 0.0;
     scale = 0.0;
     if (n > 0)  // uniform over the workgroup
-      entropy_temperature<4>(
-          [&](auto f) {
-            for (int t = tid; t < n; t += 256) f(x[t]);
-          },
-          [&](auto f) {
-            for (int t = tid; t < n; t += 256) f(s[t]);
-          },
+      entropy_temperature<kCalWaves>(
+          [&](auto f) { each_value<kCalThreads, U>(x, n, [&](int, float v) { f(v); }); },
+          [&](auto f) { each_value<kCalThreads, U>(sv, n, [&](int, float v) { f(v); }); },
           shd, shf, shift, scale);
-    x = s;
+    float ml = -INFINITY;
+    each_value<kCalThreads, U>(sv, n, [&](int, float v) { ml = fmaxf(ml, cval(v, shift, scale)); });
+    m = block_max_f32<kCalWaves>(ml, shf);
   } else if (is_l2) {
-    const float* s = l2 + bh * cap_stride;
     double sx = 0.0, sy = 0.0;
-    for (int t = tid; t < n; t += 256) {
-      sx += (double)x[t];
-      sy += (double)s[t];
+    float smax = -INFINITY;
+    for (int t0 = tid; t0 < n; t0 += kCalThreads * U) {
+      float a[U], c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * kCalThreads;
+        a[u] = t < n ? x[t] : 0.f;
+        c[u] = t < n ? sv[t] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (t0 + u * kCalThreads < n) {
+          sx += (double)a[u];
+          sy += (double)c[u];
+          smax = fmaxf(smax, c[u]);
+        }
+      }
     }
-    sx = block_sum_f64<4>(sx, shd);
-    sy = block_sum_f64<4>(sy, shd);
+    block_sum2_f64<kCalWaves>(sx, sy, shd);
+    smax = block_max_f32<kCalWaves>(smax, shf);
     const double mux = n ? sx / n : 0.0, mus = n ? sy / n : 0.0;
     double vx = 0.0, vy = 0.0;
-    for (int t = tid; t < n; t += 256) {
-      const double dx = (double)x[t] - mux, dy = (double)s[t] - mus;
-      vx += dx * dx;
-      vy += dy * dy;
+    for (int t0 = tid; t0 < n; t0 += kCalThreads * U) {
+      float a[U], c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * kCalThreads;
+        a[u] = t < n ? x[t] : 0.f;
+        c[u] = t < n ? sv[t] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (t0 + u * kCalThreads < n) {
+          const double dx = (double)a[u] - mux, dy = (double)c[u] - mus;
+          vx += dx * dx;
+          vy += dy * dy;
+        }
+      }
     }
-    vx = block_sum_f64<4>(vx, shd);
-    vy = block_sum_f64<4>(vy, shd);
+    block_sum2_f64<kCalWaves>(vx, vy, shd);
     const double sdx = n ? sqrt(vx / n) : 0.0, sds = n ? sqrt(vy / n) : 0.0;
     if (sdx == 0.0 || sds == 0.0) {
       shift = 0.0;
@@ -131,17 +169,19 @@ __global__ __launch_bounds__(256) void k_calibrate(Cand cand, const int8_t* __re
       shift = mus;
       scale = sdx / sds;
     }
-    x = s;
+    m = n ? cval(smax, shift, scale) : -INFINITY;
+  } else {
+    float ml = -INFINITY;
+    each_value<kCalThreads, U>(x, n, [&](int, float v) { ml = fmaxf(ml, v); });
+    m = block_max_f32<kCalWaves>(ml, shf);
   }
-  float m = -INFINITY;
-  for (int t = tid; t < n; t += 256) m = fmaxf(m, is_l2 ? cval(x[t], shift, scale) : x[t]);
-  m = block_max_f32<4>(m, shf);
+  const float* src = is_l2 ? sv : x;
   double Z = 0.0;
-  for (int t = tid; t < n; t += 256) {
-    const float c = is_l2 ? cval(x[t], shift, scale) : x[t];
-    Z += exp((double)c - (double)m);
-  }
-  Z = block_sum_f64<4>(Z, shd);
+  each_value<kCalThreads, U>(src, n, [&](int, float v) {
+    const float c = is_l2 ? cval(v, shift, scale) : v;
+    Z += exp_nonpos((double)c - (double)m, s_et);
+  });
+  Z = block_sum_f64<kCalWaves>(Z, shd);
   if (tid == 0) {
     double* o = stats + bh * 4;
     o[0] = shift;
@@ -151,6 +191,7 @@ __global__ __launch_bounds__(256) void k_calibrate(Cand cand, const int8_t* __re
   }
 }
 
+// --------------------------------------------------------------- select ---
 __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t* __restrict__ metric,
                                                         const float* __restrict__ logit,
                                                         const float* __restrict__ l2,
@@ -177,9 +218,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   const bool is_l2 = aux_metric(metric, h);  // second score array
   const float* x = (is_l2 ? l2 : logit) + bh * cap_stride;
   const double shift = stats[bh * 4 + 0], scale = stats[bh * 4 + 1], m = stats[bh * 4 + 2];
-  auto cv = [&](int t) -> float { return is_l2 ? cval(x[t], shift, scale) : x[t]; };
+  auto cv = [&](float raw) -> float { return is_l2 ? cval(raw, shift, scale) : raw; };
 
-  const int nsel = select_head<kSelThreads>(S, n, cv, m, top_p, wscale, s_et, mk);
+  const int nsel = select_head<kSelThreads>(S, n, x, cv, m, top_p, wscale, s_et, mk);
   // block sum of nsel
   const int wv = tid >> 6, ln = tid & 63;
   int v = nsel;
@@ -551,8 +592,8 @@ void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st) {
 
 void launch_calibrate(const SelectArgs& a, hipStream_t st) {
   observe("k_calibrate", st);
-  hipLaunchKernelGGL(k_calibrate, dim3(a.hkv, a.B), dim3(256), 0, st, a.cand, a.metric, a.logit,
-                     a.l2, a.cap_stride, a.stats, a.calib);
+  hipLaunchKernelGGL(k_calibrate, dim3(a.hkv, a.B), dim3(kCalThreads), 0, st, a.cand, a.metric,
+                     a.logit, a.l2, a.cap_stride, a.stats, a.calib);
 }
 
 void launch_select(const SelectArgs& a, hipStream_t st) {

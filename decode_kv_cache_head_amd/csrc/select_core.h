@@ -173,26 +173,48 @@ struct CountOut {
   }
 };
 
+// f(t, x[t]) for t = tid, tid + NT, tid + 2 NT, ... below n, in that order,
+// with the loads issued U at a time (each thread's sequence of values is the
+// same as one load per step; only the latency is hidden).
+template <int NT, int U, typename F>
+__device__ __forceinline__ void each_value(const float* x, int n, F f) {
+  for (int t0 = (int)threadIdx.x; t0 < n; t0 += NT * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * NT;
+      v[u] = t < n ? x[t] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * NT;
+      if (t < n) f(t, v[u]);
+    }
+  }
+}
+
 // Calibrated top-p selection of one head by a workgroup of NT threads
 // (shared by the standalone select and the fused lifecycle step).  Radix
-// select by MASS on the order-preserving key of the calibrated value cv(t),
-// t in [0, n): 11/11/10-bit passes over the tokens, each weight
-// wfix(c, m, wscale) recomputed where a pass needs it; the tokens tied at the
-// cutoff key are taken lowest position first.  Writes mk[0, n) and returns
-// this thread's count of selected tokens (the caller adds them up).
+// select by MASS on the order-preserving key of the calibrated value
+// c_t = cv(x[t]), t in [0, n): 11/11/10-bit passes over the tokens, each
+// weight wfix(c, m, wscale) recomputed where a pass needs it; the tokens tied
+// at the cutoff key are taken lowest position first.  Writes mk[0, n) and
+// returns this thread's count of selected tokens (the caller adds them up).
 // Requires 0 < n and top_p < 1; tab: the exp_nonpos table.
 template <int NT, typename CV>
-__device__ inline int select_head(SelShared& S, int n, CV cv, double m, float top_p,
-                                  double wscale, const double* tab, uint8_t* __restrict__ mk) {
+__device__ inline int select_head(SelShared& S, int n, const float* x, CV cv, double m,
+                                  float top_p, double wscale, const double* tab,
+                                  uint8_t* __restrict__ mk) {
+  constexpr int U = 8;
   const int tid = threadIdx.x;
   // pass 1: top 11 bits of the key
   for (int i = tid; i < kHistSlots; i += NT) S.hist[i] = 0;
   __syncthreads();
-  for (int t = tid; t < n; t += NT) {
-    const float c = cv(t);
+  each_value<NT, U>(x, n, [&](int, float raw) {
+    const float c = cv(raw);
     const uint64_t w = wfix(c, m, wscale, tab);
     if (w) atomicAdd(&S.hist[hslot<2048>(okey(c) >> 21)], (unsigned long long)w);
-  }
+  });
   __syncthreads();
   if (tid < 64) find_bin<2048>(S, true, top_p);
   __syncthreads();
@@ -205,13 +227,13 @@ __device__ inline int select_head(SelShared& S, int n, CV cv, double m, float to
   for (int i = tid; i < kHistSlots; i += NT) S.hist[i] = 0;
   if (tid == 0) S.target = target - above;
   __syncthreads();
-  for (int t = tid; t < n; t += NT) {
-    const float c = cv(t);
+  each_value<NT, U>(x, n, [&](int, float raw) {
+    const float c = cv(raw);
     const uint32_t k = okey(c);
     if ((k >> 21) == b1)
       atomicAdd(&S.hist[hslot<2048>((k >> 10) & 2047u)],
                 (unsigned long long)wfix(c, m, wscale, tab));
-  }
+  });
   __syncthreads();
   if (tid < 64) find_bin<2048>(S, false, top_p);
   __syncthreads();
@@ -225,12 +247,12 @@ __device__ inline int select_head(SelShared& S, int n, CV cv, double m, float to
   if (tid == 0) S.target = t2 - S.above;
   __syncthreads();
   const uint32_t pre = (b1 << 11) | b2;
-  for (int t = tid; t < n; t += NT) {
-    const float c = cv(t);
+  each_value<NT, U>(x, n, [&](int, float raw) {
+    const float c = cv(raw);
     const uint32_t k = okey(c);
     if ((k >> 10) == pre)
       atomicAdd(&S.hist[hslot<1024>(k & 1023u)], (unsigned long long)wfix(c, m, wscale, tab));
-  }
+  });
   __syncthreads();
   if (tid < 64) find_bin<1024>(S, false, top_p);
   __syncthreads();
@@ -241,14 +263,18 @@ __device__ inline int select_head(SelShared& S, int n, CV cv, double m, float to
   const unsigned long long need = target - above;
   const unsigned long long r = (need + wstar - 1) / wstar;
 
-  // pass 4: mask, ties by ascending position
+  // pass 4: mask, ties by ascending position; the next block's value is
+  // loaded while the current one is ranked
   const int wv = tid >> 6, ln = tid & 63;
   unsigned long long carried = 0;
   int nsel = 0;
+  float nxt = tid < n ? x[tid] : 0.f;
   for (int t0 = 0; t0 < n; t0 += NT) {
     const int t = t0 + tid;
     const bool valid = t < n;
-    const uint32_t k = valid ? okey(cv(t)) : 0u;
+    const float raw = nxt;
+    nxt = t + NT < n ? x[t + NT] : 0.f;
+    const uint32_t k = valid ? okey(cv(raw)) : 0u;
     const bool tie = valid && k == kstar;
     const int ntie = __syncthreads_count(tie);
     unsigned long long rank = 0;
