@@ -57,6 +57,14 @@ attention entropy) is pinned in tests/test_oracle_entropy.py by the
 proportional-logit closed form, an independent root of the same equation
 (scipy's brentq), exact power-of-two rescaling and the bisection's limits.
 
+The R-KV redundancy metric (``redundancy_head``; section 2.B, "Mechanism":
+strategies such as R-KV) is pinned in tests/test_oracle_redundancy.py by a
+brute-force mean over all pairs of scipy's cosine distance, closed forms
+(identical directions, an orthonormal set, two antipodal groups), exact
+invariance under positive power-of-two scaling of single keys and under
+permutation, the zero-key and single-candidate conventions, and reductions
+of the whole step to full softmax attention.
+
 The key-dissimilarity metric (``keydiff_head``; section 2.B: similarity
 scores) is pinned in tests/test_oracle_keydiff.py by scipy's cosine distance,
 closed forms (antipodal key groups, an orthonormal key set), exact
@@ -74,7 +82,8 @@ METRIC_QK = 0      # max-over-GQA-group q.k logit
 METRIC_L2 = 1      # key L2 norm
 METRIC_WINDOW = 2  # observation-window, position-pooled max logit
 METRIC_KEYDIFF = 3  # key dissimilarity: minus the cosine to the candidates' key sum
-AUX_METRICS = (METRIC_L2, METRIC_WINDOW, METRIC_KEYDIFF)  # calibrated by a temperature
+METRIC_RKV = 4      # R-KV redundancy: minus the mean cosine to the other candidates
+AUX_METRICS = (METRIC_L2, METRIC_WINDOW, METRIC_KEYDIFF, METRIC_RKV)  # calibrated by a temperature
 
 # Calibration rule for heads whose metric is not the raw logit
 CALIB_SPREAD = 0   # temperature that matches the raw-logit spread (moments)
@@ -510,6 +519,36 @@ def keydiff_head(K):
     return s.astype(np.float32)
 
 
+def redundancy_head(K):
+    """R-KV redundancy metric of one head's candidate keys.
+
+    Section 2.B ("Mechanism") names R-KV, a redundancy-aware strategy, among
+    the selection strategies the calibration maps onto one softmax; the pages
+    give no formula.  Reading: a candidate's redundancy is its mean cosine
+    similarity to the other candidates, r_t = mean_{j != t} cos(k_t, k_j),
+    and the metric is s_t = -r_t (the less a key repeats the others, the more
+    it is worth keeping).  cos with a zero key is 0.  With unit keys
+    u_j = k_j / ||k_j|| (u = 0 for a zero key) and nu = sum_j u_j, the sum over
+    j != t is u_t . nu - [k_t != 0], so r_t = (u_t . nu - [k_t != 0]) / (A - 1),
+    linear in the candidate count A; A = 1 gives r = 0.  float64 from the exact
+    inputs, rounded once to float32.
+    """
+    k = _f64(K)
+    _check_finite(k)
+    n = k.shape[0]
+    if n == 0:
+        return np.zeros(0, np.float32)
+    if n == 1:
+        return np.zeros(1, np.float32)
+    nk = np.sqrt(np.einsum("nd,nd->n", k, k))
+    nz = nk > 0
+    u = np.zeros_like(k)
+    u[nz] = k[nz] / nk[nz, None]
+    nu = u.sum(axis=0)
+    r = (u @ nu - nz.astype(np.float64)) / (n - 1)
+    return (-r).astype(np.float32)
+
+
 def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
               sinks: int = 0, merge: int = MERGE_MEAN, q_hist=None,
               radius: int = 0, calib: int = CALIB_SPREAD) -> HeadResult:
@@ -530,6 +569,8 @@ def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
     ell, s = score_head(q_group, cand_K)
     if metric == METRIC_KEYDIFF:
         s = keydiff_head(cand_K)
+    if metric == METRIC_RKV:
+        s = redundancy_head(cand_K)
     if metric == METRIC_WINDOW:
         # the window: this step's query, then the previous ones (q_hist [w-1, G, d])
         qw = [np.asarray(q_group)[None]]
@@ -652,6 +693,8 @@ def lifecycle_step(st: HeadState, q_group, k_new, v_new, p: float, metric: int):
     ell, s = score_head(q_group, st.pool_K)
     if metric == METRIC_KEYDIFF:
         s = keydiff_head(st.pool_K)
+    if metric == METRIC_RKV:
+        s = redundancy_head(st.pool_K)
     cal = calibrate_head(ell, s, metric)
     sel = topp_head(cal.c, cal.w, cal.Z, p, positions=st.pool_pos)
     keep = np.zeros(len(st.pool_pos), bool)
