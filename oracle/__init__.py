@@ -12,5 +12,5 @@ from .hardkv_oracle import (  # noqa: F401
     MERGE_WEIGHTED, MERGE_FLOOR, merge_weights, candidate_range, dense_positions,
     pack_heads, CALIB_SPREAD, CALIB_ENTROPY, ENTROPY_STEPS, ENTROPY_SPAN, softmax_entropy,
     entropy_temperature, HeadResult, METRIC_KEYDIFF, AUX_METRICS, keydiff_head,
-    METRIC_RKV, redundancy_head,
+    METRIC_RKV, redundancy_head, block_topp_head, BlockSelection, Selection,
 )

@@ -343,6 +343,57 @@ def topp_head(c, w, Z, p, positions=None) -> Selection:
     return Selection(order, k, selected, prefix_excl, ws)
 
 
+@dataclass
+class BlockSelection:
+    blocks: np.ndarray     # block ids (position // bs) of the candidates' blocks, ascending
+    mass: np.ndarray       # calibrated mass of each block (float64)
+    order: np.ndarray      # indices into `blocks` in rank order (mass desc, block id asc)
+    k: int                 # number of kept blocks
+    selected: np.ndarray   # kept candidate indices, ascending
+    prefix_excl: np.ndarray  # exclusive prefix mass / Z in block rank order
+
+
+def block_topp_head(w, Z, p, positions, bs: int) -> BlockSelection:
+    """Smallest set of whole blocks whose calibrated mass reaches p.
+
+    Reading of section 2.C ("Rewrite Cache": selected blocks are moved into
+    contiguous ranges) and section 2.A (Tier 3 merges the oldest blocks):
+    selection at the granularity of the paged cache's blocks.  Block j holds
+    the candidates with position in [j bs, (j + 1) bs) (aligned to absolute
+    positions, as the cache's pages are); its score is its calibrated mass,
+    the sum of its candidates' weights w_t = exp(c_t - m).  Blocks are ranked
+    by mass, highest first, equal masses by lower block id first; the kept
+    blocks are the shortest rank prefix whose mass reaches p * Z (p taken as
+    float32 and widened exactly); p >= 1 keeps every block.  Every candidate
+    of a kept block is kept.  bs = 1 is token-level top-p.
+    """
+    pos = np.asarray(positions, np.int64)
+    n = pos.shape[0]
+    p32 = float(np.float32(p))
+    if p32 <= 0.0 or bs < 1:
+        raise ValueError("top_p must be > 0 and the block size >= 1")
+    if n == 0:
+        e = np.zeros(0, np.int64)
+        return BlockSelection(e, np.zeros(0), e, 0, e, np.zeros(0))
+    bid = pos // bs
+    blocks, inv = np.unique(bid, return_inverse=True)
+    mass = np.zeros(len(blocks))
+    for t in range(n):                     # each candidate's weight into its block
+        mass[inv[t]] += float(w[t])
+    order = np.lexsort((blocks, -mass))    # primary: mass desc, then block id asc
+    prefix = np.cumsum(mass[order])
+    prefix_excl = np.concatenate(([0.0], prefix[:-1])) / Z
+    if p32 >= 1.0:
+        k = len(blocks)
+    else:
+        hits = np.nonzero(prefix >= p32 * Z)[0]
+        k = int(hits[0]) + 1 if hits.size else len(blocks)
+    kept = np.zeros(len(blocks), bool)
+    kept[order[:k]] = True
+    selected = np.nonzero(kept[inv])[0]
+    return BlockSelection(blocks, mass, order, k, selected, prefix_excl)
+
+
 # ---------------------------------------------------------------------------
 # Condensed tier (section 2.A, Tier 3: oldest blocks compressed into
 # constant-size storage by eviction or weighted merging).
@@ -551,7 +602,7 @@ def redundancy_head(K):
 
 def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
               sinks: int = 0, merge: int = MERGE_MEAN, q_hist=None,
-              radius: int = 0, calib: int = CALIB_SPREAD) -> HeadResult:
+              radius: int = 0, calib: int = CALIB_SPREAD, select_block: int = 0) -> HeadResult:
     """Single-step compression + attention of one KV head.
 
     K, V: [>=T, d] rows of this head's cache in position order (exact
@@ -562,7 +613,8 @@ def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
     Rewrite: the selected rows are copied, in ascending position order, into
     contiguous slots 0..k-1 (Rewrite Cache + Flatten Index to the maximum
     length, section 2.C).  Evicted candidates go to the condensed tier, mean-
-    or attention-weighted-merged (``condense``).
+    or attention-weighted-merged (``condense``).  select_block > 0 keeps whole
+    blocks of that many positions (``block_topp_head``) instead of tokens.
     """
     S, A = candidate_range(T, W, sinks)
     cand_K = K[S:S + A]
@@ -579,6 +631,13 @@ def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
         s = window_score_head(np.concatenate(qw, axis=0), cand_K, radius)
     cal = calibrate_head(ell, s, metric, calib)
     sel = topp_head(cal.c, cal.w, cal.Z, p)
+    extra = {}
+    if select_block > 0:
+        bsel = block_topp_head(cal.w, cal.Z, p, S + np.arange(A), select_block)
+        extra["blocks"] = bsel
+        # the kept set is the blocks'; the token ranking stays for reference
+        sel = Selection(sel.order, len(bsel.selected), bsel.selected, sel.prefix_excl,
+                        sel.w_sorted)
     mask = np.zeros(A, np.uint8)
     mask[sel.selected] = 1
     evicted = np.nonzero(mask == 0)[0]
@@ -595,7 +654,7 @@ def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
     Vc = np.asarray(V)[pos]
     dense = dense_positions(T, S, A)
     out = attend_head(q_group, np.asarray(K)[dense], np.asarray(V)[dense], Kc, Vc, ksum, vsum, cnt)
-    return HeadResult(A, ell, s, cal, sel, mask, pos, Kc, Vc, ksum, vsum, cnt, out, sinks=S)
+    return HeadResult(A, ell, s, cal, sel, mask, pos, Kc, Vc, ksum, vsum, cnt, out, extra, sinks=S)
 
 
 def step(q, k_rows, v_rows, ctx_len, W, C, p, metric, sinks=0, merge=MERGE_MEAN):
