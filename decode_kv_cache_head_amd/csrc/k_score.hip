@@ -27,7 +27,9 @@ namespace hk {
 //     previous one (q_hist), widened to float64;
 //   blocks [nqb, nqb + B Hkv): one per (b, h); key-dissimilarity heads sum
 //     their candidate keys in float64 into kmu[b][h][0..D) and ||mu|| into
-//     kmu[b][h][D]; other heads return.  Each thread adds a fixed 16-byte
+//     kmu[b][h][D]; R-KV heads sum their unit keys k / ||k|| instead (each
+//     row's norm from its pieces, reduced over the lanes that hold them);
+//     other heads return.  Each thread adds a fixed 16-byte
 //     piece of a fixed set of rows, the next batch of rows in flight while
 //     the current one is added; the row groups are then combined in a fixed
 //     order (lane pairs inside each wave, then the waves in LDS).
@@ -57,7 +59,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
   }
   const int hb = blockIdx.x - nqb;
   const int b = hb / hkv, h = hb % hkv;
-  if (metric[h] != HARDKV_METRIC_KEYDIFF) return;
+  const bool unit = metric[h] == HARDKV_METRIC_RKV;
+  if (metric[h] != HARDKV_METRIC_KEYDIFF && !unit) return;
   const int n = cand.n(b, h);
   const int c = tid % CPR, r0 = tid / CPR;
   const int rb = rows.tb(b, h), rh = rows.th(h);
@@ -80,8 +83,21 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     for (int u = 0; u < U; ++u) {
       float f[EPC];
       Elt<T>::unpack(cur[u], f);
+      if (unit) {
+        // the row's squared norm: this piece's part, then the CPR lanes of
+        // the row (aligned groups of CPR consecutive lanes) in a fixed order
+        double ss = 0.0;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[e] += (double)f[e];
+        for (int e = 0; e < EPC; ++e) ss = fma((double)f[e], (double)f[e], ss);
+#pragma unroll
+        for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
+        const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] += (double)f[e] * inv;
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] += (double)f[e];
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) cur[u] = nxt[u];
@@ -189,7 +205,8 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
   const int tok = (w & 1) * 64 + lane;
   const bool is_l2 = metric != nullptr && metric[h] == HARDKV_METRIC_L2;
   const bool is_win = metric != nullptr && metric[h] == HARDKV_METRIC_WINDOW;
-  const bool is_kd = metric != nullptr && metric[h] == HARDKV_METRIC_KEYDIFF;
+  const bool is_rkv = metric != nullptr && metric[h] == HARDKV_METRIC_RKV;
+  const bool is_kd = is_rkv || (metric != nullptr && metric[h] == HARDKV_METRIC_KEYDIFF);
   // key-dissimilarity heads: the candidates' key sum (this half) and its norm
   const double* kmu_h = kmu + ((int64_t)b * hkv + h) * (D + 1);
   const int64_t qoff = ((int64_t)b * window * hq + (int64_t)h * G) * D + half * (D / 2);
@@ -233,7 +250,13 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
       if (t < n) {
         logit[obase + t] = (float)(mx * scale);
         if (is_l2) l2[obase + t] = (float)sqrt(ss + s_part[G][tok]);
-        if (is_kd) {
+        if (is_rkv) {
+          // minus the mean cosine to the other candidates: (u_t . nu - 1) / (n - 1)
+          const double nk = sqrt(ss + s_part[G][tok]);
+          const double v = nk > 0.0 && n > 1 ? -((md + s_part[G + 1][tok]) / nk - 1.0) / (n - 1)
+                                             : 0.0;
+          l2[obase + t] = (float)v;
+        } else if (is_kd) {
           const double nk = sqrt(ss + s_part[G][tok]), nm = kmu_h[D];
           const double v = nk > 0.0 && nm > 0.0 ? -(md + s_part[G + 1][tok]) / (nk * nm) : 0.0;
           l2[obase + t] = (float)v;

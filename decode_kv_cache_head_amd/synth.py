@@ -24,6 +24,7 @@ METRIC_QK = 0
 METRIC_L2 = 1
 METRIC_WINDOW = 2
 METRIC_KEYDIFF = 3
+METRIC_RKV = 4
 
 
 @dataclass(frozen=True)

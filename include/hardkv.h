@@ -76,6 +76,11 @@ typedef struct ihipStream_t* hardkv_stream_t; /* same type as hipStream_t */
                                    sum of the head's candidate keys (0 for a zero vector),
                                    float64, one rounding; calibrated like L2 (section 2.B:
                                    similarity scores among the importance metrics) */
+#define HARDKV_METRIC_RKV 4 /* R-KV redundancy: -(u_t . nu - [k_t != 0]) / (A - 1), the minus
+                               mean cosine similarity to the other candidates, u the unit keys
+                               (0 for a zero key), nu their sum over the head's candidates; 0
+                               when A = 1; float64, one rounding; calibrated like L2
+                               (section 2.B, "Mechanism": strategies such as R-KV) */
 
 /* How L2 and window heads are calibrated (hardkv_desc.calibration); QK heads
  * always keep temperature 1 (section 2.B, Mechanism: a temperature maps a
@@ -257,7 +262,8 @@ size_t hardkv_workspace_size(const hardkv_desc* desc);
  *   l2:     [B][Hkv][sparse_cap] float32 second metric: key norms for HARDKV_METRIC_L2
  *           heads, the pooled window metric for HARDKV_METRIC_WINDOW heads (float64
  *           dots, one rounding, exact max-pooling), the key dissimilarity for
- *           HARDKV_METRIC_KEYDIFF heads (the key sum is formed first, in float64 and
+ *           HARDKV_METRIC_KEYDIFF heads and the redundancy for HARDKV_METRIC_RKV heads
+ *           (the sum of the keys, or of the unit keys, is formed first, in float64 and
  *           in a fixed order, in the workspace); must be non-NULL whenever metric is
  *           non-NULL
  * Entries at t >= A_b are unspecified. */

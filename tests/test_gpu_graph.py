@@ -27,6 +27,8 @@ pytestmark = pytest.mark.gpu
         S.METRIC_KEYDIFF, S.METRIC_QK, S.METRIC_L2, S.METRIC_KEYDIFF) * 2)),
     ("qwen8b_b1_16k", dict(B=2, T=(5000, 3333), calibration=1, metric=(
         S.METRIC_L2, S.METRIC_KEYDIFF, S.METRIC_QK, S.METRIC_L2) * 2)),
+    ("qwen8b_b32_16k_paged", dict(B=3, T=(4000, 2500, 1024), metric=(
+        S.METRIC_RKV, S.METRIC_QK, S.METRIC_KEYDIFF, S.METRIC_RKV) * 2)),
 ])
 def test_step_graph_replay_matches_eager(gpu, name, kw):
     w = S.workload(name, **kw)

@@ -97,6 +97,14 @@ GRID = [
          T=(9000, 2100, 300), metric=(S.METRIC_KEYDIFF, S.METRIC_KEYDIFF)),
     dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=2, C=32, p=0.7, calibration=1,
          metric=(S.METRIC_QK, S.METRIC_KEYDIFF)),
+    # R-KV redundancy heads (the candidates' unit-key sum formed before the score)
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.9, metric=(S.METRIC_RKV, S.METRIC_QK)),
+    dict(dtype=S.DT_F32, d=64, Hq=8, Hkv=4, C=7, p=0.8, calibration=1,
+         metric=(S.METRIC_RKV, S.METRIC_KEYDIFF, S.METRIC_L2, S.METRIC_RKV)),
+    dict(dtype=S.DT_BF16, d=128, Hq=16, Hkv=2, C=64, p=0.95, block_size=16, sinks=4, merge=1,
+         T=(9000, 2100, 300), metric=(S.METRIC_RKV, S.METRIC_RKV)),
+    dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=2, C=32, p=0.7, T=(2100, 777, 2),
+         metric=(S.METRIC_QK, S.METRIC_RKV)),
 ]
 
 
@@ -493,6 +501,25 @@ def test_headline_with_key_dissimilarity(gpu):
     check_all_heads_invariants(case, desc, g)
     rep = check_case(case, g, w.p, heads=_sample_heads(w, 6, 4))
     say(rep)
+
+
+def test_headline_with_redundancy(gpu):
+    """The headline shape with half the KV heads on the R-KV redundancy
+    metric: the product call on every head and the stage-by-stage calls on
+    sampled heads against the oracle."""
+    w = S.workload("qwen8b_b32_16k_paged", metric=(S.METRIC_RKV, S.METRIC_QK) * 4)
+    say(w.name, "redundancy")
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_step(case, desc)
+    check_all_heads_invariants(case, desc, g)
+    rep = check_case(case, g, w.p, stages=False)
+    say("step", rep)
+    assert rep["heads"] == w.B * w.Hkv
+    del g
+    g = run_stages(case, desc)
+    rep = check_case(case, g, w.p, heads=_sample_heads(w, 6, 5))
+    say("stages", rep)
 
 
 def test_mixed_metric_64k_entropy_calibration(gpu):
