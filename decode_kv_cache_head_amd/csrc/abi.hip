@@ -25,7 +25,7 @@ void hk::observe(const char* kernel, hipStream_t st) {
 
 namespace {
 
-constexpr int kVersion = 10700;  // 1.7.0
+constexpr int kVersion = 10800;  // 1.8.0
 
 // Device address of `scratch` on each device, looked up on the first
 // hardkv_step_noalloc call with that device current.
@@ -83,11 +83,16 @@ int validate(const hardkv_desc* d) {
     return HARDKV_ERR_INVALID_ARG;
   if (d->calibration != HARDKV_CALIB_SPREAD && d->calibration != HARDKV_CALIB_ENTROPY)
     return HARDKV_ERR_INVALID_ARG;
+  if (d->select_block < 0 || d->select_block > 1024 ||
+      (d->select_block & (d->select_block - 1)))
+    return HARDKV_ERR_INVALID_ARG;
   if (d->packed_rows > 0 &&
       (int64_t)d->batch * d->num_kv_heads * (int64_t)d->sparse_cap >= ((int64_t)1 << 31))
     return HARDKV_ERR_INVALID_ARG;
   if (d->sparse_cap < 0 || d->chunk_cap < 0) return HARDKV_ERR_INVALID_ARG;
   const int A = max_aged(d);
+  if (d->select_block > 0 && ceil_div(A, d->select_block) + 1 > kBlockSelMax)
+    return HARDKV_ERR_UNSUPPORTED;
   if (d->sparse_cap < A) return HARDKV_ERR_CAPACITY;
   if ((int64_t)d->chunk_cap * d->chunk < A) return HARDKV_ERR_CAPACITY;
   // every element offset must fit comfortably in 63 bits
@@ -221,6 +226,7 @@ SelectArgs select_args(const hardkv_desc* d, const Cand& cand, const int8_t* met
   a.mode = nullptr;
   a.policy = hardkv_policy{HARDKV_POLICY_REWRITE, 1, 0, 0};
   a.calib = d->calibration;
+  a.block = d->select_block;
   return a;
 }
 
@@ -343,7 +349,10 @@ void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
   SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
   sa.mode = t.mode;
   sa.policy = *policy;
-  if (calsel_fits(max_aged(d))) {
+  if (d->select_block > 0) {
+    launch_calibrate(sa, st);
+    launch_blocksel(sa, st);
+  } else if (calsel_fits(max_aged(d))) {
     launch_calsel(sa, max_aged(d), st);
   } else {
     launch_calibrate(sa, st);
@@ -437,9 +446,12 @@ int hardkv_topp_select(const hardkv_desc* d, const int32_t* ctx_len, const int8_
   if (!ctx_len || !logit || !stats || !mask || !count || (metric && !l2))
     return HARDKV_ERR_INVALID_ARG;
   clear_launch_error();
-  launch_select(select_args(d, aged_cand(d, ctx_len), metric, logit, l2, (double*)stats, mask,
-                            count),
-                (hipStream_t)stream);
+  const SelectArgs sa = select_args(d, aged_cand(d, ctx_len), metric, logit, l2, (double*)stats,
+                                    mask, count);
+  if (d->select_block > 0)
+    launch_blocksel(sa, (hipStream_t)stream);
+  else
+    launch_select(sa, (hipStream_t)stream);
   return launched();
 }
 
@@ -563,7 +575,7 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   if (rc) return rc;
   if (d->block_size != 0 || d->dense_window < 1 || d->sinks != 0 ||
       d->merge != HARDKV_MERGE_MEAN || d->packed_rows != 0 || window_of(d) != 1 ||
-      d->pool_radius != 0 || d->calibration != HARDKV_CALIB_SPREAD)
+      d->pool_radius != 0 || d->calibration != HARDKV_CALIB_SPREAD || d->select_block != 0)
     return HARDKV_ERR_INVALID_ARG;
   if (!q || !k_new || !v_new || !s || !s->ring_k || !s->ring_v || !s->seq_len ||
       !tiers_ok(&s->tiers) || s->tiers.mode || !out)

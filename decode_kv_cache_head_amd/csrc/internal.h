@@ -91,8 +91,12 @@ struct SelectArgs {
   uint8_t* mode;        // [B][Hkv] rewrite / sparse choice, written with count; may be null
   hardkv_policy policy;
   int calib;            // HARDKV_CALIB_* for heads on the second score array
+  int block;            // > 0: block-granular selection, blocks of this many positions
 };
 void launch_calibrate(const SelectArgs& a, hipStream_t st);
+// top-p over position-aligned blocks ranked by calibrated mass (after calibrate)
+constexpr int kBlockSelMax = 4096;  // blocks per head
+void launch_blocksel(const SelectArgs& a, hipStream_t st);
 void launch_select(const SelectArgs& a, hipStream_t st);
 // calibrate + select in one launch, scores in registers (max_cand <= 16384)
 bool calsel_fits(int max_cand);

@@ -512,7 +512,144 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   }
 }
 
+// ------------------------------------------------------ block selection ---
+// Top-p over whole blocks (section 2.C: selected blocks are moved into
+// contiguous ranges).  One 1024-thread workgroup per (b, h), after
+// calibrate: block j holds the candidates at positions [j bs, (j + 1) bs);
+// its mass is the integer sum of its candidates' fixed-point weights
+// wfix(c, m) (LDS atomics: deterministic).  The blocks are sorted by (mass
+// desc, block id asc) with a bitonic network in LDS, a block-wide scan of the
+// sorted masses finds the shortest prefix reaching ceil(p * total), and every
+// candidate of a kept block is kept.
+__global__ __launch_bounds__(kSelThreads) void k_blocksel(Cand cand, const int8_t* __restrict__ metric,
+                                                          const float* __restrict__ logit,
+                                                          const float* __restrict__ l2,
+                                                          int64_t cap_stride,
+                                                          const double* __restrict__ stats,
+                                                          float top_p, double wscale,
+                                                          uint8_t* __restrict__ mask, CountOut co,
+                                                          int bs) {
+  constexpr int NT = kSelThreads;
+  __shared__ unsigned long long s_mass[kBlockSelMax];
+  __shared__ uint16_t s_idx[kBlockSelMax];
+  __shared__ uint8_t s_kept[kBlockSelMax];
+  __shared__ unsigned long long s_wsum[kSelWaves];
+  __shared__ double s_et[64];
+  __shared__ int s_k;
+  __shared__ int s_red[kSelWaves];
+  const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
+  const int wv = tid >> 6, ln = tid & 63;
+  const int n = cand.n(b, h);
+  const int64_t bh = (int64_t)b * hkv + h;
+  uint8_t* mk = mask + bh * cap_stride;
+  if (n == 0) {
+    if (tid == 0) co.put(bh, n, 0);
+    return;
+  }
+  if (!(top_p < 1.0f)) {
+    for (int t = tid; t < n; t += NT) mk[t] = 1;
+    if (tid == 0) co.put(bh, n, n);
+    return;
+  }
+  exp_table_init(s_et);
+  const int S = cand.sinks;                 // position of candidate 0
+  const int jb0 = S / bs;
+  const int nb = (S + n - 1) / bs - jb0 + 1;  // <= kBlockSelMax (validated)
+  int np = 64;
+  while (np < nb) np <<= 1;
+  for (int i = tid; i < np; i += NT) {
+    s_mass[i] = 0ull;
+    s_idx[i] = (uint16_t)i;  // entries past nb: mass 0, ids above every block's
+    s_kept[i] = 0;
+  }
+  if (tid == 0) s_k = np;
+  __syncthreads();
+  const bool is_l2 = aux_metric(metric, h);
+  const float* x = (is_l2 ? l2 : logit) + bh * cap_stride;
+  const double shift = stats[bh * 4 + 0], scale = stats[bh * 4 + 1], m = stats[bh * 4 + 2];
+  each_value<NT, 8>(x, n, [&](int t, float raw) {
+    const float c = is_l2 ? cval(raw, shift, scale) : raw;
+    const uint64_t w = wfix(c, m, wscale, s_et);
+    if (w) atomicAdd(&s_mass[(S + t) / bs - jb0], (unsigned long long)w);
+  });
+  __syncthreads();
+  // bitonic sort: entry i precedes entry j when its mass is larger, or equal
+  // with a lower block id
+  for (int k = 2; k <= np; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < np; i += NT) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long ma = s_mass[i], mb = s_mass[ixj];
+          const uint16_t ia = s_idx[i], ib = s_idx[ixj];
+          const bool a_first = ma > mb || (ma == mb && ia < ib);
+          const bool forward = (i & k) == 0;
+          if (forward != a_first) {
+            s_mass[i] = mb;
+            s_mass[ixj] = ma;
+            s_idx[i] = ib;
+            s_idx[ixj] = ia;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // inclusive prefix of the sorted masses: thread tid takes entries
+  // [tid E, tid E + E), a wave scan, then the waves below in order
+  const int E = np > NT ? np / NT : 1;
+  unsigned long long run = 0;
+  if (tid * E < np)
+    for (int e = 0; e < E; ++e) run += s_mass[tid * E + e];
+  const unsigned long long incl = wave_prefix_u64(run);
+  if (ln == 63) s_wsum[wv] = incl;
+  __syncthreads();
+  unsigned long long before = 0, total = 0;
+  for (int i = 0; i < kSelWaves; ++i) {
+    if (i < wv) before += s_wsum[i];
+    total += s_wsum[i];
+  }
+  unsigned long long target = ceil_mul(top_p, total);
+  if (target < 1) target = 1;
+  unsigned long long acc = before + incl - run;
+  if (tid * E < np) {
+    for (int e = 0; e < E; ++e) {
+      acc += s_mass[tid * E + e];
+      if (acc >= target) {
+        atomicMin(&s_k, tid * E + e + 1);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const int kb = min(s_k, nb);
+  for (int r = tid; r < kb; r += NT) s_kept[s_idx[r]] = 1;
+  __syncthreads();
+  int nsel = 0;
+  for (int t = tid; t < n; t += NT) {
+    const uint8_t kept = s_kept[(S + t) / bs - jb0];
+    mk[t] = kept;
+    nsel += kept;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) nsel += __shfl_xor(nsel, o, 64);
+  if (ln == 0) s_red[wv] = nsel;
+  __syncthreads();
+  if (tid == 0) {
+    int tot = 0;
+    for (int i = 0; i < kSelWaves; ++i) tot += s_red[i];
+    co.put(bh, n, tot);
+  }
+}
+
 static CountOut count_out(const SelectArgs& a) { return CountOut{a.count, a.mode, a.policy, a.cand.W}; }
+
+void launch_blocksel(const SelectArgs& a, hipStream_t st) {
+  observe("k_blocksel", st);
+  hipLaunchKernelGGL(k_blocksel, dim3(a.hkv, a.B), dim3(kSelThreads), 0, st, a.cand, a.metric,
+                     a.logit, a.l2, a.cap_stride, (const double*)a.stats, a.top_p,
+                     mass_scale(a.cand.cap), a.mask, count_out(a), a.block);
+}
 
 __global__ __launch_bounds__(256) void k_plan(Cand cand, int B, const int32_t* __restrict__ count,
                                               uint8_t* __restrict__ mode, hardkv_policy pol) {

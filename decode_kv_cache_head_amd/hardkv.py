@@ -45,7 +45,8 @@ class Desc(ctypes.Structure):
                 ("sparse_cap", ctypes.c_int32), ("chunk_cap", ctypes.c_int32),
                 ("top_p", ctypes.c_float), ("sinks", ctypes.c_int32), ("merge", ctypes.c_int32),
                 ("packed_rows", ctypes.c_int32), ("obs_window", ctypes.c_int32),
-                ("pool_radius", ctypes.c_int32), ("calibration", ctypes.c_int32)]
+                ("pool_radius", ctypes.c_int32), ("calibration", ctypes.c_int32),
+                ("select_block", ctypes.c_int32)]
 
 
 class Cache(ctypes.Structure):
@@ -143,7 +144,8 @@ def _check(rc, fn):
 
 def make_desc(B, Hq, Hkv, d, dtype, W, C, top_p, ctx_cap, block_size=0, max_blocks=0,
               sparse_cap=None, chunk_cap=None, sinks=0, merge=MERGE_MEAN,
-              packed_rows=0, obs_window=1, pool_radius=0, calibration=CALIB_SPREAD) -> Desc:
+              packed_rows=0, obs_window=1, pool_radius=0, calibration=CALIB_SPREAD,
+              select_block=0) -> Desc:
     A = max(ctx_cap - W - sinks, 0)
     if sparse_cap is None:
         sparse_cap = A
@@ -151,7 +153,7 @@ def make_desc(B, Hq, Hkv, d, dtype, W, C, top_p, ctx_cap, block_size=0, max_bloc
         chunk_cap = -(-A // C) if C > 0 else 0
     return Desc(B, Hq, Hkv, d, dtype, W, C, block_size, ctx_cap, max_blocks, sparse_cap,
                 chunk_cap, float(top_p), sinks, merge, packed_rows, obs_window, pool_radius,
-                calibration)
+                calibration, select_block)
 
 
 def validate(desc: Desc) -> int:

@@ -53,6 +53,7 @@ class Workload:
     obs_window: int = 1  # queries in the observation window (window-metric heads)
     pool_radius: int = 0  # max-pooling radius of the window metric
     calibration: int = 0  # temperature rule of non-logit heads: 0 spread, 1 entropy
+    select_block: int = 0  # 0 token-level top-p; > 0 whole blocks of this many positions
 
     @property
     def G(self):

@@ -150,6 +150,11 @@ typedef struct hardkv_desc {
                            0..64 (0 or 1 = this step's query only; > 1 needs cache->q_hist) */
   int32_t pool_radius;  /* HARDKV_METRIC_WINDOW heads: max-pooling radius, 0..512 */
   int32_t calibration;  /* HARDKV_CALIB_*: the temperature rule of L2 and window heads */
+  int32_t select_block; /* 0: top-p over tokens; a power of two bs in 1..1024: top-p over
+                           whole blocks of positions [j bs, (j + 1) bs), each ranked by its
+                           calibrated mass (section 2.C: selected blocks moved into contiguous
+                           ranges); at most 4096 blocks per head (ceil(max aged / bs) + 1);
+                           single-step calls only */
 } hardkv_desc;
 
 /* The KV cache of one layer.

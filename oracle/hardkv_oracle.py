@@ -635,6 +635,7 @@ def step_head(q_group, K, V, T: int, W: int, C: int, p: float, metric: int,
     if select_block > 0:
         bsel = block_topp_head(cal.w, cal.Z, p, S + np.arange(A), select_block)
         extra["blocks"] = bsel
+        extra["block_size"] = select_block
         # the kept set is the blocks'; the token ranking stays for reference
         sel = Selection(sel.order, len(bsel.selected), bsel.selected, sel.prefix_excl,
                         sel.w_sorted)

@@ -36,7 +36,7 @@ def desc_for(case: S.Case, top_p=None, sparse_cap=None, chunk_cap=None) -> H.Des
                        w.p if top_p is None else top_p, case.ctx_cap, w.block_size,
                        case.max_blocks, sparse_cap, chunk_cap, w.sinks, w.merge,
                        obs_window=w.obs_window, pool_radius=w.pool_radius,
-                       calibration=w.calibration)
+                       calibration=w.calibration, select_block=w.select_block)
 
 
 def cache_of(case: S.Case) -> H.Cache:
@@ -87,7 +87,8 @@ def oracle_head(case: S.Case, b: int, h: int, p: float):
     if case.q_hist is not None:
         hist = case.q_hist[b, :, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
     ref = O.step_head(q, K, V, w.T[b], w.W, w.C, p, int(w.metrics[h]), w.sinks, w.merge,
-                      q_hist=hist, radius=w.pool_radius, calib=w.calibration)
+                      q_hist=hist, radius=w.pool_radius, calib=w.calibration,
+                      select_block=w.select_block)
     return q, K, V, ref
 
 
@@ -113,6 +114,31 @@ def borderline_tokens(ref: O.HeadResult, p: float, tokens) -> np.ndarray:
         i = rank[t]
         mass = abs(sel.prefix_excl[i] - p32) <= BORDER * p32
         order = any(abs(w[t] - c) <= BORDER * c for c in cuts)
+        ok.append(mass or order)
+    return np.array(ok, bool)
+
+
+def borderline_blocks(ref: O.HeadResult, p: float, tokens) -> np.ndarray:
+    """Block-granular selection: tokens (candidate indices) whose block is
+    borderline for the cutoff: its exclusive prefix mass in block rank order
+    within 1e-6 relative of p, or its mass within 1e-6 relative of the last
+    kept or first dropped block's."""
+    bsel = ref.extra["blocks"]
+    p32 = float(np.float32(p))
+    bs_ids = ref.sinks + np.asarray(tokens, np.int64)
+    rank = np.empty(len(bsel.blocks), np.int64)
+    rank[bsel.order] = np.arange(len(bsel.blocks))
+    cuts = []
+    if bsel.k >= 1:
+        cuts.append(bsel.mass[bsel.order[bsel.k - 1]])
+    if bsel.k < len(bsel.blocks):
+        cuts.append(bsel.mass[bsel.order[bsel.k]])
+    ok = []
+    for pos in bs_ids:
+        j = int(np.searchsorted(bsel.blocks, pos // ref.extra["block_size"]))
+        i = rank[j]
+        mass = abs(bsel.prefix_excl[i] - p32) <= BORDER * p32
+        order = any(abs(bsel.mass[j] - c) <= BORDER * c for c in cuts)
         ok.append(mass or order)
     return np.array(ok, bool)
 
@@ -151,8 +177,14 @@ def check_head(case, b, h, gpu, p, report, stages=True, desc=None, skip_slots=Fa
     if stages:
         assert np.array_equal(pos_gpu, s0 + np.nonzero(gm)[0])
     diff = np.setxor1d(pos_gpu, ref.pos)
+    if w.select_block:
+        # whole blocks on the GPU too
+        kept_blocks = np.unique(pos_gpu // w.select_block)
+        cand = s0 + np.arange(A)
+        assert np.array_equal(pos_gpu, cand[np.isin(cand // w.select_block, kept_blocks)])
     if diff.size:
-        bl = borderline_tokens(ref, p, diff - s0)
+        bl = (borderline_blocks(ref, p, diff - s0) if w.select_block else
+              borderline_tokens(ref, p, diff - s0))
         assert bl.all(), f"non-borderline set mismatch at ({b},{h}): {diff[~bl][:10]}"
         report["borderline"] += int(diff.size)
     else:

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = H.load()
-    assert lib.hardkv_version() == 10700
+    assert lib.hardkv_version() == 10800
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.hardkv_strerror(code)
     assert lib.hardkv_strerror(99) == b"unknown error"
@@ -42,7 +42,8 @@ def base_desc(**kw):
                        d["ctx_cap"], d.get("block_size", 0), d.get("max_blocks", 0),
                        d.get("sparse_cap"), d.get("chunk_cap"), d.get("sinks", 0),
                        d.get("merge", 0), d.get("packed_rows", 0), d.get("obs_window", 1),
-                       d.get("pool_radius", 0), d.get("calibration", 0))
+                       d.get("pool_radius", 0), d.get("calibration", 0),
+                       d.get("select_block", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -85,6 +86,17 @@ def base_desc(**kw):
     (dict(calibration=H.CALIB_ENTROPY), H.OK),
     (dict(calibration=2), H.ERR_INVALID_ARG),
     (dict(calibration=-1), H.ERR_INVALID_ARG),
+    (dict(select_block=16), H.OK),
+    (dict(select_block=1), H.OK),
+    (dict(select_block=1024), H.OK),
+    (dict(select_block=12), H.ERR_INVALID_ARG),
+    (dict(select_block=-16), H.ERR_INVALID_ARG),
+    (dict(select_block=2048), H.ERR_INVALID_ARG),
+    # at most 4096 blocks per head: ceil(A / bs) + 1
+    (dict(ctx_cap=4095 + 64, select_block=1), H.OK),
+    (dict(ctx_cap=4096 + 64, select_block=1), H.ERR_UNSUPPORTED),
+    (dict(ctx_cap=65520 + 256, W=256, select_block=16), H.OK),
+    (dict(ctx_cap=65536 + 256, W=256, select_block=16), H.ERR_UNSUPPORTED),
 ])
 def test_validate_codes(kw, code):
     assert H.validate(base_desc(**kw)) == code
@@ -329,6 +341,16 @@ def test_window_metric_needs_the_query_history():
     state = H.StateC(fake, fake, tiers, fake)
     assert lib.hardkv_step_inplace(d, fake, fake, fake, None, ctypes.byref(state), fake, fake,
                                    need, st) == H.ERR_INVALID_ARG
+
+
+def test_lifecycle_has_no_block_selection():
+    lib = H.load()
+    fake = ctypes.c_void_p(0x1000)
+    st = ctypes.c_void_p(0)
+    d = base_desc(select_block=16)
+    state = H.StateC(fake, fake, H.TiersC(*([fake] * 7)), fake)
+    assert lib.hardkv_step_inplace(ctypes.byref(d), fake, fake, fake, None, ctypes.byref(state),
+                                   fake, fake, H.workspace_size(d), st) == H.ERR_INVALID_ARG
 
 
 def test_lifecycle_keeps_the_spread_rule():

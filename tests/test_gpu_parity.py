@@ -105,6 +105,14 @@ GRID = [
          T=(9000, 2100, 300), metric=(S.METRIC_RKV, S.METRIC_RKV)),
     dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=2, C=32, p=0.7, T=(2100, 777, 2),
          metric=(S.METRIC_QK, S.METRIC_RKV)),
+    # block-granular selection: whole position-aligned blocks ranked by mass
+    dict(dtype=S.DT_BF16, d=128, Hq=8, Hkv=2, C=64, p=0.9, block_size=16, select_block=16),
+    dict(dtype=S.DT_F32, d=64, Hq=8, Hkv=4, C=7, p=0.8, select_block=8, sinks=5,
+         metric=(S.METRIC_L2, S.METRIC_QK, S.METRIC_RKV, S.METRIC_QK)),
+    dict(dtype=S.DT_BF16, d=128, Hq=16, Hkv=2, C=64, p=0.95, block_size=16, select_block=64,
+         merge=1, T=(9000, 2100, 300)),
+    dict(dtype=S.DT_BF16, d=64, Hq=8, Hkv=2, C=32, p=0.6, select_block=1, calibration=1,
+         metric=(S.METRIC_QK, S.METRIC_L2)),
 ]
 
 
@@ -520,6 +528,37 @@ def test_headline_with_redundancy(gpu):
     g = run_stages(case, desc)
     rep = check_case(case, g, w.p, heads=_sample_heads(w, 6, 5))
     say("stages", rep)
+
+
+def test_block_size_one_equals_token_selection(gpu):
+    """Blocks of one position select exactly the token-level set."""
+    w = small("blk1", T=(3000, 1500, 700), metric=(S.METRIC_QK, S.METRIC_L2))
+    case = S.make_case(w, gpu)
+    tok = run_step(case, desc_for(case))
+    from dataclasses import replace
+    case_b = S.Case(replace(w, select_block=1), case.q, case.k, case.v, case.ctx_len,
+                    case.block_table, case.metric, case.ctx_cap, case.max_blocks)
+    blk = run_step(case_b, desc_for(case_b))
+    assert torch.equal(tok["tiers"].count, blk["tiers"].count)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            n = int(tok["tiers"].count[b, h])
+            assert torch.equal(tok["tiers"].pos[b, h, :n], blk["tiers"].pos[b, h, :n])
+
+
+@pytest.mark.parametrize("name,bs", [("qwen8b_b32_16k_paged", 16), ("qwen8b_b8_64k_mixed", 16)])
+def test_block_selection_full_size(gpu, name, bs):
+    """Block-granular selection at full size through hardkv_step, every head
+    against the oracle (the 64k heads hold 4081 blocks, near the 4096 cap)."""
+    w = S.workload(name, select_block=bs)
+    say(w.name, "select_block", bs)
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    g = run_step(case, desc)
+    check_all_heads_invariants(case, desc, g)
+    rep = check_case(case, g, w.p, stages=False)
+    say(rep)
+    assert rep["heads"] == w.B * w.Hkv
 
 
 def test_mixed_metric_64k_entropy_calibration(gpu):
