@@ -60,6 +60,8 @@ def parse():
                     help="skip the selection-reuse timings")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-config results (tiny, 16k batch 1, ragged, 64k mixed)")
+    ap.add_argument("--no-lifecycle", action="store_true",
+                    help="skip the one-layer lifecycle timings (step 1 and steady state)")
     ap.add_argument("--no-lifecycle-full", action="store_true",
                     help="skip the 64-layer x 256-step lifecycle run")
     return ap.parse_args()
@@ -114,9 +116,12 @@ def kernel_bytes(w, A, k, kernel, fused):
 
 
 def source_hash(kernel):
+    """Hash of the kernel's source file and every header of the library."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "common.h", "internal.h"):
-        h.update(open(os.path.join(ROOT, "decode_kv_cache_head_amd", "csrc", f), "rb").read())
+    csrc = os.path.join(ROOT, "decode_kv_cache_head_amd", "csrc")
+    headers = sorted(f for f in os.listdir(csrc) if f.endswith(".h"))
+    for f in [KERNEL_SOURCES[kernel]] + headers:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -784,6 +789,7 @@ def main():
             am[wp.name] = amortization(wp, S.make_case(wp, dev), args.steps)
             torch.cuda.empty_cache()
         res["amortization"] = am
+    if not args.no_lifecycle:
         print("[bench] lifecycle", file=sys.stderr, flush=True)
         res["lifecycle"] = lifecycle(dev)
         res["lifecycle_block_manager"] = lifecycle(dev, pool_block=64)

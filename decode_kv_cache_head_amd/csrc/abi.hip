@@ -25,7 +25,7 @@ void hk::observe(const char* kernel, hipStream_t st) {
 
 namespace {
 
-constexpr int kVersion = 10800;  // 1.8.0
+constexpr int kVersion = 10900;  // 1.9.0
 
 // Device address of `scratch` on each device, looked up on the first
 // hardkv_step_noalloc call with that device current.
@@ -89,6 +89,13 @@ int validate(const hardkv_desc* d) {
   if (d->packed_rows > 0 &&
       (int64_t)d->batch * d->num_kv_heads * (int64_t)d->sparse_cap >= ((int64_t)1 << 31))
     return HARDKV_ERR_INVALID_ARG;
+  if (d->tier_block != 0) {
+    if (d->tier_block < 16 || d->tier_block > 1024 || (d->tier_block & (d->tier_block - 1)) ||
+        d->tier_blocks < 1 || (int64_t)d->tier_blocks * d->tier_block >= ((int64_t)1 << 31) ||
+        d->packed_rows != 0)
+      return HARDKV_ERR_INVALID_ARG;
+    if ((int64_t)d->batch * d->num_kv_heads > kTierMaxHeads) return HARDKV_ERR_UNSUPPORTED;
+  }
   if (d->sparse_cap < 0 || d->chunk_cap < 0) return HARDKV_ERR_INVALID_ARG;
   const int A = max_aged(d);
   if (d->select_block > 0 && ceil_div(A, d->select_block) + 1 > kBlockSelMax)
@@ -160,6 +167,34 @@ Rows region_rows(const hardkv_desc* d, const void* base, int64_t region) {
   r.region = region;
   r.hkv = d->num_kv_heads;
   r.row_bytes = d->head_dim * (d->dtype == HARDKV_F32 ? 4 : 2);
+  return r;
+}
+
+// block manager of the rewritten tier
+int tier_maxb(const hardkv_desc* d) { return ceil_div(d->sparse_cap, d->tier_block); }
+TierBlocks tier_blocks(const hardkv_desc* d, const hardkv_tiers* t) {
+  TierBlocks b{};
+  b.table = t->table;
+  b.held = t->held;
+  b.free_ids = t->free_ids;
+  b.free_top = t->free_top;
+  b.lbs = log2i(d->tier_block);
+  b.maxb = tier_maxb(d);
+  b.nblocks = d->tier_blocks;
+  return b;
+}
+// rows of the rewritten tier under its block manager: head (b, h) uses
+// table row b * Hkv + h, blocks of tier_block rows of one head each
+Rows tier_rows(const hardkv_desc* d, const void* base, const int32_t* table) {
+  Rows r{};
+  r.base = (const char*)base;
+  r.table = table;
+  r.region = 0;
+  r.hkv = 1;
+  r.lbs = log2i(d->tier_block);
+  r.max_blocks = tier_maxb(d);
+  r.row_bytes = d->head_dim * (d->dtype == HARDKV_F32 ? 4 : 2);
+  r.headtab = d->num_kv_heads;
   return r;
 }
 
@@ -255,6 +290,12 @@ CompactArgs compact_args(const hardkv_desc* d, const Layout& L, char* ws, const 
   a.chunk_stride = d->chunk_cap;
   a.mode = t->mode;
   a.offset = d->packed_rows > 0 ? t->offset : nullptr;
+  if (d->tier_block > 0) {
+    a.tier_table = t->table;
+    a.tier_lbs = log2i(d->tier_block);
+    a.tier_maxb = tier_maxb(d);
+    a.tier_nblocks = d->tier_blocks;
+  }
   a.pos_off = d->sinks;
   a.merge = d->merge;
   a.G = d->num_q_heads / d->num_kv_heads;
@@ -279,8 +320,13 @@ AttnArgs attn_args(const hardkv_desc* d, const Layout& L, char* ws, const void* 
   a.ctx_cap = d->ctx_cap;
   a.W = d->dense_window;
   a.sinks = d->sinks;
-  a.sk = region_rows(d, t->k, d->sparse_cap);
-  a.sv = region_rows(d, t->v, d->sparse_cap);
+  if (d->tier_block > 0) {
+    a.sk = tier_rows(d, t->k, t->table);
+    a.sv = tier_rows(d, t->v, t->table);
+  } else {
+    a.sk = region_rows(d, t->k, d->sparse_cap);
+    a.sv = region_rows(d, t->v, d->sparse_cap);
+  }
   a.count = t->count;
   a.sparse_cap = d->sparse_cap;
   a.mode = t->mode;
@@ -302,9 +348,12 @@ AttnArgs attn_args(const hardkv_desc* d, const Layout& L, char* ws, const void* 
 bool tiers_ok(const hardkv_tiers* t) {
   return t && t->k && t->v && t->pos && t->count && t->ksum && t->vsum && t->ccount;
 }
-// ... and, for a packed rewritten tier, the offsets and the per-head modes
+// ... and, for a packed rewritten tier, the offsets and the per-head modes;
+// under the tier's block manager, its state and the per-head modes
 bool tiers_ok(const hardkv_desc* d, const hardkv_tiers* t) {
-  return tiers_ok(t) && (d->packed_rows == 0 || (t->mode && t->offset));
+  return tiers_ok(t) && (d->packed_rows == 0 || (t->mode && t->offset)) &&
+         (d->tier_block == 0 ||
+          (t->mode && t->table && t->held && t->free_ids && t->free_top));
 }
 bool cache_ok(const hardkv_desc* d, const hardkv_cache* c) {
   return c && c->k && c->v && c->ctx_len && (d->block_size == 0 || c->block_table);
@@ -361,6 +410,9 @@ void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
   if (d->packed_rows > 0)
     launch_pack(d->batch * d->num_kv_heads, count, max_aged(d), t.mode, t.offset,
                 d->packed_rows, st);
+  if (d->tier_block > 0)
+    launch_tier_alloc(tier_blocks(d, &t), d->batch * d->num_kv_heads, count, max_aged(d), t.mode,
+                      st);
   CompactArgs ca = compact_args(d, L, w, kr, vr, cand, max_aged(d), mask, &t);
   ca.metric = metric;
   ca.logit = logit;
@@ -529,6 +581,30 @@ int hardkv_pack(const hardkv_desc* d, const int32_t* count, const hardkv_tiers* 
   return launched();
 }
 
+int hardkv_tier_init(const hardkv_desc* d, const hardkv_tiers* tiers, hardkv_stream_t stream) {
+  const int rc = validate(d);
+  if (rc) return rc;
+  if (d->tier_block == 0 || !tiers || !tiers->table || !tiers->held || !tiers->free_ids ||
+      !tiers->free_top)
+    return HARDKV_ERR_INVALID_ARG;
+  clear_launch_error();
+  launch_tier_init(tier_blocks(d, tiers), d->batch * d->num_kv_heads, (hipStream_t)stream);
+  return launched();
+}
+
+int hardkv_tier_alloc(const hardkv_desc* d, const int32_t* count, const hardkv_tiers* tiers,
+                      hardkv_stream_t stream) {
+  const int rc = validate(d);
+  if (rc) return rc;
+  if (d->tier_block == 0 || !count || !tiers || !tiers->mode || !tiers->table || !tiers->held ||
+      !tiers->free_ids || !tiers->free_top)
+    return HARDKV_ERR_INVALID_ARG;
+  clear_launch_error();
+  launch_tier_alloc(tier_blocks(d, tiers), d->batch * d->num_kv_heads, count, max_aged(d),
+                    tiers->mode, (hipStream_t)stream);
+  return launched();
+}
+
 int hardkv_step(const hardkv_desc* d, const void* q, const hardkv_cache* cache,
                 const int8_t* metric, const hardkv_tiers* tiers, float* out, void* ws,
                 size_t ws_bytes, hardkv_stream_t stream) {
@@ -575,7 +651,8 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
   if (rc) return rc;
   if (d->block_size != 0 || d->dense_window < 1 || d->sinks != 0 ||
       d->merge != HARDKV_MERGE_MEAN || d->packed_rows != 0 || window_of(d) != 1 ||
-      d->pool_radius != 0 || d->calibration != HARDKV_CALIB_SPREAD || d->select_block != 0)
+      d->pool_radius != 0 || d->calibration != HARDKV_CALIB_SPREAD || d->select_block != 0 ||
+      d->tier_block != 0)
     return HARDKV_ERR_INVALID_ARG;
   if (!q || !k_new || !v_new || !s || !s->ring_k || !s->ring_v || !s->seq_len ||
       !tiers_ok(&s->tiers) || s->tiers.mode || !out)

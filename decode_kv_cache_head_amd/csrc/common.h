@@ -192,6 +192,16 @@ __device__ inline int xcd_contiguous(int L, int N) {
   return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
 }
 
+// (b, h) of a one-workgroup-per-head launch over grid (Hkv, B), numbered as
+// the tiled score launch numbers its heads: each XCD takes one contiguous
+// range of heads in (b, h) order, the range whose scores its L2 received.
+__device__ inline void head_of_block(int& b, int& h) {
+  const int n = gridDim.x * gridDim.y;
+  const int id = xcd_contiguous(blockIdx.x + gridDim.x * blockIdx.y, n);
+  h = id % gridDim.x;
+  b = id / gridDim.x;
+}
+
 // ------------------------------------------------------- wave reductions --
 __device__ inline double wave_sum_f64(double v) {
 #pragma unroll

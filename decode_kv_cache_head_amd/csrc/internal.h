@@ -104,6 +104,20 @@ void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st);
 // mode[b][h] from count[b][h] and the candidate count
 void launch_plan(const SelectArgs& a, hipStream_t st);
 // offsets of the packed rewritten tier (and overflow -> sparse loading)
+// Block manager of the rewritten tier (tier_block rows per block).
+struct TierBlocks {
+  int32_t* table;     // [n_heads][maxb]
+  int32_t* held;      // [n_heads]
+  int32_t* free_ids;  // [nblocks]
+  int32_t* free_top;  // [1]
+  int lbs;            // log2(rows per block)
+  int maxb;           // table entries per head
+  int nblocks;
+};
+constexpr int kTierMaxHeads = 16384;  // heads one allocation handles (its scans live in LDS)
+void launch_tier_init(const TierBlocks& tb, int n_heads, hipStream_t st);
+void launch_tier_alloc(const TierBlocks& tb, int n_heads, const int32_t* count, int cap,
+                       uint8_t* mode, hipStream_t st);
 void launch_pack(int n_heads, const int32_t* count, int cap, uint8_t* mode, int32_t* offset,
                  int packed_rows, hipStream_t st);
 
@@ -142,6 +156,16 @@ struct CompactArgs {
   int chunk_stride;
   const uint8_t* mode;  // [B][Hkv]; HARDKV_MODE_SPARSE heads skip the row copies; may be null
   const int32_t* offset;  // packed tier: head (b, h)'s slot 0 is row offset[b][h]; may be null
+  // block manager of the rewritten tier: slot j of head i is row
+  // (tier_table[i][j >> tier_lbs] << tier_lbs) + (j & mask) of out_k / out_v; may be null
+  const int32_t* tier_table;
+  int tier_lbs, tier_maxb, tier_nblocks;
+  // -1: the slot's block id lies outside the pool (nothing is stored)
+  __device__ inline int64_t tier_slot(int64_t bh, int j) const {
+    const int id = tier_table[bh * tier_maxb + (j >> tier_lbs)];
+    if (id < 0 || id >= tier_nblocks) return -1;
+    return ((int64_t)id << tier_lbs) + (j & ((1 << tier_lbs) - 1));
+  }
   int pos_off;          // position of candidate 0 (the sink count)
   // weighted merging (merge == HARDKV_MERGE_WEIGHTED): per-token weights from
   // the selection's scores and statistics

@@ -555,8 +555,9 @@ __device__ inline void tile_attn(const AttnArgs& a, const QT* qg, const Rows& kr
   combine_waves<G, D>(s_m, s_l, s_o, part_out);
 }
 
-// PS: the sparse tier is the lifecycle pool under the block manager (rows
-// through per-head block tables; the dense tier is then the ring, P false).
+// PS: the sparse tier's rows go through per-head block tables (the lifecycle
+// pool under its block manager, with the ring as the dense tier, or the
+// rewritten tier under its block manager, beside a cache of either layout).
 // PART 0: every tile of the head; 1: the dense and sparse tiles; 2: the
 // condensed tiles (grid x counts from the first condensed tile).  Launches
 // whose row tiles take the matrix-core path split the two kinds, so the
@@ -698,13 +699,14 @@ static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
   const int gd = ceil_div(a.W + a.sinks, kAttnTile), gc = ceil_div(a.chunk_cap, kAttnTile);
   const int gx = a.fused_tt > 0 ? gd : a.max_tiles;
   const int grows = split && a.fused_tt == 0 ? gx - gc : gx;
-  bool pool_paged = false;
-  if constexpr (!P) pool_paged = a.sk.table != nullptr;
+  // sparse tier through per-head block tables: the lifecycle's pool, or the
+  // rewritten tier under its block manager
+  const bool pool_paged = a.sk.table != nullptr;
   if (grows > 0) {
     observe("k_attn", st);
     const dim3 grid(grows, a.hkv, a.B);
     if (pool_paged)
-      hipLaunchKernelGGL((k_attn<T, D, G, false, true, split ? 1 : 0>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_attn<T, D, G, P, true, split ? 1 : 0>), grid, dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((k_attn<T, D, G, P, false, split ? 1 : 0>), grid, dim3(256), 0, st, a);
   }

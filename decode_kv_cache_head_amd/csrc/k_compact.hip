@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
   const int tend = min(t0 + TT, n);
   const bool copy_rows = a.mode == nullptr || a.mode[bh] == HARDKV_MODE_REWRITE;
   const uint8_t* mk = a.mask + bh * a.cap_stride;
-  const int64_t slot0 = a.offset ? (int64_t)a.offset[bh] : bh * a.cap_stride;
+  const int64_t slot0 = a.offset ? (int64_t)a.offset[bh] : a.tier_table ? 0 : bh * a.cap_stride;
   char* ok = a.out_k + slot0 * RB;
   char* ov = a.out_v + slot0 * RB;
   int32_t* pos = a.out_pos + bh * a.cap_stride;
@@ -156,9 +156,12 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int tsr = k / (PER / 2), rem = (k % (PER / 2)) * 256 + tid, r = rem / CPR, c = rem % CPR;
-      if (copy_rows && r < nr && s_sel[r])
-        __builtin_nontemporal_store(*(const v4u*)((tsr ? sv : sk) + r * RB + c * 16),
-                                    (v4u*)((tsr ? ov : ok) + (int64_t)s_rank[r] * RB + c * 16));
+      if (copy_rows && r < nr && s_sel[r]) {
+        const int64_t drow = a.tier_table ? a.tier_slot(bh, s_rank[r]) : (int64_t)s_rank[r];
+        if (drow >= 0)
+          __builtin_nontemporal_store(*(const v4u*)((tsr ? sv : sk) + r * RB + c * 16),
+                                      (v4u*)((tsr ? ov : ok) + drow * RB + c * 16));
+      }
     }
     if (summer) {
       const T* src = (const T*)(tensor ? sv : sk);
@@ -237,6 +240,7 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   __shared__ float s_cf[ATTN ? MAXU * G : 1];      // chunk weights against the tile max
   __shared__ float s_cv[ATTN ? MAXU * G : 1];      // ... divided by the chunk's count
   __shared__ float s_M[GA];                         // tile max per query head
+  __shared__ int s_tab[1024 / 16 + 2];              // block ids of the tile's kept slots
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int n = a.cand.n(b, h);
   const int t0 = j * TT;
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   const int nrows = min(TT, n - t0);
   const bool copy_rows = a.mode == nullptr || a.mode[bh] == HARDKV_MODE_REWRITE;
   const uint8_t* mk = a.mask + bh * a.cap_stride;
-  const int64_t slot0 = a.offset ? (int64_t)a.offset[bh] : bh * a.cap_stride;
+  const int64_t slot0 = a.offset ? (int64_t)a.offset[bh] : a.tier_table ? 0 : bh * a.cap_stride;
   char* ok = a.out_k + slot0 * RB;
   char* ov = a.out_v + slot0 * RB;
   int32_t* pos = a.out_pos + bh * a.cap_stride;
@@ -297,6 +301,24 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
     if (t0 + nrows == n && tid == 255) a.out_count[bh] = rk;
   }
   __syncthreads();
+  // block manager: the block ids of the tile's kept slots [base, base + kept)
+  int tab0 = 0;
+  if (a.tier_table && copy_rows) {
+    tab0 = base >> a.tier_lbs;
+    const int nt = s_kept_tile > 0 ? ((base + s_kept_tile - 1) >> a.tier_lbs) - tab0 + 1 : 0;
+    if (tid < nt) {
+      // a block id outside the pool (a tier never allocated) stores nothing
+      const int id = tab0 + tid < a.tier_maxb ? a.tier_table[bh * a.tier_maxb + tab0 + tid] : -1;
+      s_tab[tid] = id >= 0 && id < a.tier_nblocks ? id : -1;
+    }
+    __syncthreads();
+  }
+  // destination row of kept slot rk, -1: none
+  auto dest_row = [&](int rk) -> int64_t {
+    if (!a.tier_table) return rk;
+    const int id = s_tab[(rk >> a.tier_lbs) - tab0];
+    return id < 0 ? -1 : ((int64_t)id << a.tier_lbs) + (rk & ((1 << a.tier_lbs) - 1));
+  };
 
   const int w = tid >> 6, lane = tid & 63;
   const int c = lane % CPR, rg = lane / CPR;
@@ -389,9 +411,10 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
       if (r < nrows) {
         const int rk = s_rank[r];
         if (rk >= 0) {
-          if (copy_rows) {
-            __builtin_nontemporal_store(buf[i], (v4u*)(ok + (int64_t)rk * RB + c * 16));
-            __builtin_nontemporal_store(buf[RPT + i], (v4u*)(ov + (int64_t)rk * RB + c * 16));
+          const int64_t dr = copy_rows ? dest_row(rk) : -1;
+          if (dr >= 0) {
+            __builtin_nontemporal_store(buf[i], (v4u*)(ok + dr * RB + c * 16));
+            __builtin_nontemporal_store(buf[RPT + i], (v4u*)(ov + dr * RB + c * 16));
           }
         } else if (WMERGE) {
           const float wt = mw.at(t0 + r);

@@ -13,6 +13,7 @@
 //   additions).  The cutoff key K* is the bin where the mass accumulated from
 //   the top first reaches ceil(p * Z); the tokens tied at K* are taken lowest
 //   position first, as many as needed.  A final ordered pass writes the mask.
+#include <algorithm>
 #include <type_traits>
 
 #include "select_core.h"
@@ -99,7 +100,9 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(Cand cand, const int8
   __shared__ double shd[2 * kCalWaves];
   __shared__ float shf[kCalWaves];
   __shared__ double s_et[64];
-  const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
+  const int hkv = gridDim.x, tid = threadIdx.x;
+  int b, h;
+  head_of_block(b, h);
   const int n = cand.n(b, h);
   const int64_t bh = (int64_t)b * hkv + h;
   const float* x = logit + bh * cap_stride;
@@ -201,7 +204,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
                                                         uint8_t* __restrict__ mask, CountOut co) {
   __shared__ SelShared S;
   __shared__ double s_et[64];
-  const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
+  const int hkv = gridDim.x, tid = threadIdx.x;
+  int b, h;
+  head_of_block(b, h);
   const int n = cand.n(b, h);
   const int64_t bh = (int64_t)b * hkv + h;
   uint8_t* mk = mask + bh * cap_stride;
@@ -259,7 +264,9 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   __shared__ double shd[2 * kSelWaves];
   __shared__ float shf[kSelWaves];
   __shared__ double s_et[64];
-  const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
+  const int hkv = gridDim.x, tid = threadIdx.x;
+  int b, h;
+  head_of_block(b, h);
   const int n = cand.n(b, h);
   const int64_t bh = (int64_t)b * hkv + h;
   uint8_t* mk = mask + bh * cap_stride;
@@ -469,7 +476,12 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
     __syncthreads();
   }
   // mask: for each slot the wave's 64 decisions (tokens 1024 i + 64 wv ..)
-  // come from one ballot; lanes 0..3 each store 16 of them as bytes
+  // come from one ballot; lanes 0..3 each put 16 of them as bytes into LDS
+  // (the histogram's space, free now), then every thread stores 16
+  // consecutive bytes: whole-line stores instead of 64-byte pieces
+  static_assert(NPT * kSelThreads <= (int)sizeof(S.hist), "mask staging");
+  uint8_t* sm = reinterpret_cast<uint8_t*>(S.hist);
+  __syncthreads();  // every read of the histogram is done
   int nsel = 0;
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
@@ -488,19 +500,22 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
     const unsigned long long bal = __ballot(sel);
     nsel += __popcll(bal);
     if (ln < 4) {
-      const int t0 = kSelThreads * i + 64 * wv + 16 * ln;
       const uint32_t bits = (uint32_t)(bal >> (16 * ln)) & 0xffffu;
-      if (t0 + 16 <= n && ((uintptr_t)(mk + t0) & 15) == 0) {
-        // each nibble of bits becomes four 0/1 bytes
-        uint4 v;
-        v.x = ((bits & 15u) * 0x00204081u) & 0x01010101u;
-        v.y = (((bits >> 4) & 15u) * 0x00204081u) & 0x01010101u;
-        v.z = (((bits >> 8) & 15u) * 0x00204081u) & 0x01010101u;
-        v.w = (((bits >> 12) & 15u) * 0x00204081u) & 0x01010101u;
-        *(uint4*)(mk + t0) = v;
-      } else {
-        for (int q = 0; q < 16 && t0 + q < n; ++q) mk[t0 + q] = (uint8_t)((bits >> q) & 1u);
-      }
+      // each nibble of bits becomes four 0/1 bytes
+      uint4 v;
+      v.x = ((bits & 15u) * 0x00204081u) & 0x01010101u;
+      v.y = (((bits >> 4) & 15u) * 0x00204081u) & 0x01010101u;
+      v.z = (((bits >> 8) & 15u) * 0x00204081u) & 0x01010101u;
+      v.w = (((bits >> 12) & 15u) * 0x00204081u) & 0x01010101u;
+      *(uint4*)(sm + kSelThreads * i + 64 * wv + 16 * ln) = v;
+    }
+  }
+  __syncthreads();
+  for (int t0 = 16 * tid; t0 < n; t0 += 16 * kSelThreads) {
+    if (t0 + 16 <= n && ((uintptr_t)(mk + t0) & 15) == 0) {
+      *(uint4*)(mk + t0) = *(const uint4*)(sm + t0);
+    } else {
+      for (int q = 0; q < 16 && t0 + q < n; ++q) mk[t0 + q] = sm[t0 + q];
     }
   }
   // count: the waves add (selected << 32 | 1) to one LDS word; the wave that
@@ -537,7 +552,9 @@ __global__ __launch_bounds__(kSelThreads) void k_blocksel(Cand cand, const int8_
   __shared__ double s_et[64];
   __shared__ int s_k;
   __shared__ int s_red[kSelWaves];
-  const int h = blockIdx.x, b = blockIdx.y, hkv = gridDim.x, tid = threadIdx.x;
+  const int hkv = gridDim.x, tid = threadIdx.x;
+  int b, h;
+  head_of_block(b, h);
   const int wv = tid >> 6, ln = tid & 63;
   const int n = cand.n(b, h);
   const int64_t bh = (int64_t)b * hkv + h;
@@ -705,6 +722,129 @@ __global__ __launch_bounds__(kSelThreads) void k_pack(int n_heads, const int32_t
     run = total;
     __syncthreads();
   }
+}
+
+// ------------------------------------------- rewritten tier's block manager --
+// (section 2.C "Metadata": a head-wise block manager for head-adaptive
+// budgets under static shapes.)
+__global__ __launch_bounds__(256) void k_tier_init(TierBlocks tb, int n_heads) {
+  const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x, stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = i0; i < tb.nblocks; i += stride) tb.free_ids[i] = (int32_t)i;
+  for (int64_t i = i0; i < n_heads; i += stride) tb.held[i] = 0;
+  for (int64_t i = i0; i < (int64_t)n_heads * tb.maxb; i += stride) tb.table[i] = -1;
+  if (i0 == 0) tb.free_top[0] = tb.nblocks;
+}
+
+void launch_tier_init(const TierBlocks& tb, int n_heads, hipStream_t st) {
+  observe("k_tier_init", st);
+  const int64_t work = std::max<int64_t>((int64_t)n_heads * tb.maxb, tb.nblocks);
+  const int grid = (int)std::min<int64_t>(std::max<int64_t>(ceil_div(work, 256), 1), 1024);
+  hipLaunchKernelGGL(k_tier_init, dim3(grid), dim3(256), 0, st, tb, n_heads);
+}
+
+// Exclusive scan of v over the heads in (b, h) order into s[0 .. n] (s[n] =
+// total), 1024 heads per round with the running total carried; returns the
+// total.  Every thread returns with the scan visible in LDS.
+template <typename F>
+__device__ inline int tier_scan(int n, F val, int* s, int* s_w) {
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+  int run = 0;
+  for (int base = 0; base < n; base += kSelThreads) {
+    const int i = base + tid;
+    const int v = i < n ? val(i) : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (ln >= o) incl += u;
+    }
+    if (ln == 63) s_w[wv] = incl;
+    __syncthreads();
+    int before = run, total = run;
+    for (int j = 0; j < kSelWaves; ++j) {
+      if (j < wv) before += s_w[j];
+      total += s_w[j];
+    }
+    if (i < n) s[i] = before + incl - v;
+    run = total;
+    __syncthreads();
+  }
+  if (tid == 0) s[n] = run;
+  __syncthreads();
+  return run;
+}
+
+// The head whose scan range [s[i], s[i + 1]) holds entry e (s ascending,
+// e < s[n]): the last i with s[i] <= e.
+__device__ inline int tier_head_of(const int* s, int n, int e) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s[mid] <= e) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One workgroup: every head returns its blocks to the free stack, then the
+// rewritten heads take ceil(k / tb) blocks each from the top, in (b, h)
+// order; a head that does not fit (nor any after it) is sparse-loaded.
+__global__ __launch_bounds__(kSelThreads) void k_tier_alloc(TierBlocks tb, int n_heads,
+                                                            const int32_t* __restrict__ count,
+                                                            int cap, uint8_t* __restrict__ mode) {
+  __shared__ int s_scan[kTierMaxHeads + 1];
+  __shared__ int s_w[kSelWaves];
+  const int tid = threadIdx.x;
+  // device-resident sizes are clamped to the pool, so a state that was never
+  // set up cannot send a store past it
+  int top0 = tb.free_top[0];
+  top0 = top0 < 0 ? 0 : (top0 > tb.nblocks ? tb.nblocks : top0);
+  // 1. push the held blocks: head i's go to stack entries top0 + s[i] + j
+  const int held_all = tier_scan(
+      n_heads,
+      [&](int i) -> int {
+        const int h = tb.held[i];
+        return h < 0 ? 0 : (h > tb.maxb ? tb.maxb : h);
+      },
+      s_scan, s_w);
+  const int pushed = min(held_all, tb.nblocks - top0);
+  for (int e = tid; e < pushed; e += kSelThreads) {
+    const int i = tier_head_of(s_scan, n_heads, e);
+    tb.free_ids[top0 + e] = tb.table[(int64_t)i * tb.maxb + (e - s_scan[i])];
+  }
+  __syncthreads();  // the pushes are done before any head's table changes
+  const int top1 = top0 + pushed;
+  // 2. pop the needs of the rewritten heads
+  const int needed = tier_scan(
+      n_heads,
+      [&](int i) -> int {
+        if (mode[i] != HARDKV_MODE_REWRITE) return 0;
+        int k = count[i];
+        k = k < 0 ? 0 : (k > cap ? cap : k);
+        return (k + (1 << tb.lbs) - 1) >> tb.lbs;
+      },
+      s_scan, s_w);
+  // heads whose range ends at or below top1 fit; they form a prefix
+  for (int i = tid; i < n_heads; i += kSelThreads) {
+    const int need = s_scan[i + 1] - s_scan[i];
+    const bool fits = s_scan[i + 1] <= top1;
+    tb.held[i] = fits ? need : 0;
+    if (mode[i] == HARDKV_MODE_REWRITE && !fits) mode[i] = HARDKV_MODE_SPARSE;
+  }
+  // the fitting prefix's total: all of it, or the start of the last head
+  // that starts at or below top1 (that head ends past it)
+  const int fit_total = needed <= top1 ? needed : s_scan[tier_head_of(s_scan, n_heads, top1)];
+  for (int e = tid; e < fit_total; e += kSelThreads) {
+    const int i = tier_head_of(s_scan, n_heads, e);
+    tb.table[(int64_t)i * tb.maxb + (e - s_scan[i])] = tb.free_ids[top1 - 1 - e];
+  }
+  if (tid == 0) tb.free_top[0] = top1 - fit_total;
+}
+
+void launch_tier_alloc(const TierBlocks& tb, int n_heads, const int32_t* count, int cap,
+                       uint8_t* mode, hipStream_t st) {
+  observe("k_tier_alloc", st);
+  hipLaunchKernelGGL(k_tier_alloc, dim3(1), dim3(kSelThreads), 0, st, tb, n_heads, count, cap,
+                     mode);
 }
 
 void launch_pack(int n_heads, const int32_t* count, int cap, uint8_t* mode, int32_t* offset,

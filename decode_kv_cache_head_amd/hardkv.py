@@ -46,7 +46,8 @@ class Desc(ctypes.Structure):
                 ("top_p", ctypes.c_float), ("sinks", ctypes.c_int32), ("merge", ctypes.c_int32),
                 ("packed_rows", ctypes.c_int32), ("obs_window", ctypes.c_int32),
                 ("pool_radius", ctypes.c_int32), ("calibration", ctypes.c_int32),
-                ("select_block", ctypes.c_int32)]
+                ("select_block", ctypes.c_int32), ("tier_block", ctypes.c_int32),
+                ("tier_blocks", ctypes.c_int32)]
 
 
 class Cache(ctypes.Structure):
@@ -59,7 +60,9 @@ class TiersC(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
                 ("count", ctypes.c_void_p), ("ksum", ctypes.c_void_p),
                 ("vsum", ctypes.c_void_p), ("ccount", ctypes.c_void_p),
-                ("mode", ctypes.c_void_p), ("offset", ctypes.c_void_p)]
+                ("mode", ctypes.c_void_p), ("offset", ctypes.c_void_p),
+                ("table", ctypes.c_void_p), ("held", ctypes.c_void_p),
+                ("free_ids", ctypes.c_void_p), ("free_top", ctypes.c_void_p)]
 
 
 class Policy(ctypes.Structure):
@@ -102,6 +105,8 @@ _SIGS = {
     "hardkv_plan": ([ctypes.POINTER(Desc), ctypes.POINTER(Policy), _P, _P, _P, _P],
                     ctypes.c_int),
     "hardkv_pack": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(TiersC), _P], ctypes.c_int),
+    "hardkv_tier_init": ([ctypes.POINTER(Desc), ctypes.POINTER(TiersC), _P], ctypes.c_int),
+    "hardkv_tier_alloc": ([ctypes.POINTER(Desc), _P, ctypes.POINTER(TiersC), _P], ctypes.c_int),
     "hardkv_step_policy": ([ctypes.POINTER(Desc), ctypes.POINTER(Policy), _P,
                             ctypes.POINTER(Cache), _P, ctypes.POINTER(TiersC), _P, _P,
                             ctypes.c_size_t, _P], ctypes.c_int),
@@ -145,7 +150,7 @@ def _check(rc, fn):
 def make_desc(B, Hq, Hkv, d, dtype, W, C, top_p, ctx_cap, block_size=0, max_blocks=0,
               sparse_cap=None, chunk_cap=None, sinks=0, merge=MERGE_MEAN,
               packed_rows=0, obs_window=1, pool_radius=0, calibration=CALIB_SPREAD,
-              select_block=0) -> Desc:
+              select_block=0, tier_block=0, tier_blocks=0) -> Desc:
     A = max(ctx_cap - W - sinks, 0)
     if sparse_cap is None:
         sparse_cap = A
@@ -153,7 +158,7 @@ def make_desc(B, Hq, Hkv, d, dtype, W, C, top_p, ctx_cap, block_size=0, max_bloc
         chunk_cap = -(-A // C) if C > 0 else 0
     return Desc(B, Hq, Hkv, d, dtype, W, C, block_size, ctx_cap, max_blocks, sparse_cap,
                 chunk_cap, float(top_p), sinks, merge, packed_rows, obs_window, pool_radius,
-                calibration, select_block)
+                calibration, select_block, tier_block, tier_blocks)
 
 
 def validate(desc: Desc) -> int:
@@ -182,30 +187,61 @@ class Tiers:
     ccount: torch.Tensor
     mode: torch.Tensor | None = None   # [B][Hkv] uint8, None = every head rewritten
     offset: torch.Tensor | None = None  # [B][Hkv] int32, packed tier only
+    # block manager of the rewritten tier (tier_block > 0): k, v = [blocks][tb][d]
+    table: torch.Tensor | None = None     # [B][Hkv][ceil(sparse_cap / tb)] int32
+    held: torch.Tensor | None = None      # [B][Hkv] int32
+    free_ids: torch.Tensor | None = None  # [blocks] int32
+    free_top: torch.Tensor | None = None  # [1] int32
 
     def c(self) -> TiersC:
         return TiersC(*(ctypes.c_void_p(t.data_ptr()) for t in
                         (self.k, self.v, self.pos, self.count, self.ksum, self.vsum, self.ccount)),
-                      _p(self.mode), _p(self.offset))
+                      _p(self.mode), _p(self.offset), _p(self.table), _p(self.held),
+                      _p(self.free_ids), _p(self.free_top))
 
     def slots(self, b, h, which="k"):
-        """Head (b, h)'s rewritten slots 0..count-1 (either layout)."""
+        """Head (b, h)'s rewritten slots 0..count-1 (any layout)."""
         src = self.k if which == "k" else self.v
         n = int(self.count[b, h])
+        if self.table is not None:
+            tb = src.shape[1]
+            ids = self.table[b, h, :-(-n // tb)].long()
+            return src[ids].reshape(-1, src.shape[-1])[:n]
         if self.offset is None:
             return src[b, h, :n]
         o = int(self.offset[b, h])
         return src[o:o + n]
 
 
-def alloc_tiers(desc: Desc, device="cuda", zero=False, mode=False) -> Tiers:
+def alloc_tiers(desc: Desc, device="cuda", zero=False, mode=False, blocks=None) -> Tiers:
     """Tiers for `desc`; a packed desc (packed_rows > 0) gets one [packed_rows][d]
-    region for K and for V plus the offsets and modes it needs."""
+    region for K and for V plus the offsets and modes it needs; a block-managed
+    desc (tier_block > 0) a pool of [tier_blocks][tier_block][d] and the
+    manager's state (set up with tier_init before the first selection), or
+    the given `blocks` = (k, v, free_ids, free_top) of a pool shared with
+    other tiers."""
     B, Hkv, d = desc.batch, desc.num_kv_heads, desc.head_dim
     dt = torch.float32 if desc.dtype == F32 else torch.bfloat16
     mk = torch.zeros if zero else torch.empty
     cap, ccap = desc.sparse_cap, desc.chunk_cap
     packed = desc.packed_rows > 0
+    if desc.tier_block > 0:
+        tb = desc.tier_block
+        if blocks is None:
+            blocks = (mk((desc.tier_blocks, tb, d), dtype=dt, device=device),
+                      mk((desc.tier_blocks, tb, d), dtype=dt, device=device),
+                      torch.empty(desc.tier_blocks, dtype=torch.int32, device=device),
+                      torch.empty(1, dtype=torch.int32, device=device))
+        return Tiers(blocks[0], blocks[1],
+                     mk((B, Hkv, cap), dtype=torch.int32, device=device),
+                     mk((B, Hkv), dtype=torch.int32, device=device),
+                     mk((B, Hkv, ccap, d), dtype=torch.float32, device=device),
+                     mk((B, Hkv, ccap, d), dtype=torch.float32, device=device),
+                     mk((B, Hkv, ccap), dtype=torch.int32, device=device),
+                     torch.zeros((B, Hkv), dtype=torch.uint8, device=device), None,
+                     torch.empty((B, Hkv, -(-cap // tb)), dtype=torch.int32, device=device),
+                     torch.empty((B, Hkv), dtype=torch.int32, device=device),
+                     blocks[2], blocks[3])
     rows = (desc.packed_rows, d) if packed else (B, Hkv, cap, d)
     return Tiers(mk(rows, dtype=dt, device=device),
                  mk(rows, dtype=dt, device=device),
@@ -297,6 +333,19 @@ def pack(desc, count, tiers: Tiers, stream=None):
     tc = tiers.c()
     rc = load().hardkv_pack(ctypes.byref(desc), _p(count), ctypes.byref(tc), _stream(stream))
     _check(rc, "hardkv_pack")
+
+
+def tier_init(desc, tiers: Tiers, stream=None):
+    tc = tiers.c()
+    rc = load().hardkv_tier_init(ctypes.byref(desc), ctypes.byref(tc), _stream(stream))
+    _check(rc, "hardkv_tier_init")
+
+
+def tier_alloc(desc, count, tiers: Tiers, stream=None):
+    tc = tiers.c()
+    rc = load().hardkv_tier_alloc(ctypes.byref(desc), _p(count), ctypes.byref(tc),
+                                  _stream(stream))
+    _check(rc, "hardkv_tier_alloc")
 
 
 def step_policy(desc, pol: Policy, q, cache: Cache, metric, tiers: Tiers, out, ws, stream=None):

@@ -155,6 +155,14 @@ typedef struct hardkv_desc {
                            calibrated mass (section 2.C: selected blocks moved into contiguous
                            ranges); at most 4096 blocks per head (ceil(max aged / bs) + 1);
                            single-step calls only */
+  int32_t tier_block;   /* 0: no block manager.  A power of two tb in 16..1024: the rewritten
+                           tier lives in a shared pool of tier_blocks blocks of tb rows
+                           (tiers->k, v = [tier_blocks][tb][d]); slot j of (b, h) is row
+                           j % tb of block tiers->table[b][h][j / tb] (section 2.C, a
+                           head-wise block manager for head-adaptive budgets under static
+                           shapes); needs tiers->table, held, free_ids, free_top and mode;
+                           excludes packed_rows; single-step calls only */
+  int32_t tier_blocks;  /* blocks in that pool, 1 .. 2^31 / tb (tier_block > 0) */
 } hardkv_desc;
 
 /* The KV cache of one layer.
@@ -198,6 +206,19 @@ typedef struct hardkv_tiers {
   int32_t* ccount;
   uint8_t* mode;
   int32_t* offset;
+  /* block manager of the rewritten tier (desc->tier_block > 0; else may be NULL):
+   *   table:    [B][Hkv][ceil(sparse_cap / tier_block)] int32 block ids, entries
+   *             0 .. held - 1 valid
+   *   held:     [B][Hkv] int32 blocks the head holds
+   *   free_ids: [tier_blocks] int32 stack of free block ids, entries 0 .. *free_top - 1
+   *   free_top: [1] int32
+   * Set up once with hardkv_tier_init; every selection then returns each head's
+   * blocks and hands out new ones (hardkv_tier_alloc).  The pool and this state
+   * may be shared by several layers' tiers (one table and held array each). */
+  int32_t* table;
+  int32_t* held;
+  int32_t* free_ids;
+  int32_t* free_top;
 } hardkv_tiers;
 
 /* Persistent state of the multi-step lifecycle (one layer).
@@ -376,6 +397,31 @@ int hardkv_plan(const hardkv_desc* desc, const hardkv_policy* policy, const int3
  * after hardkv_plan and before hardkv_compact; the steps run it themselves. */
 int hardkv_pack(const hardkv_desc* desc, const int32_t* count, const hardkv_tiers* tiers,
                 hardkv_stream_t stream);
+
+/* Set-up of the rewritten tier's block manager (desc->tier_block > 0): every
+ * block free (free_ids[i] = i, *free_top = tier_blocks), every head holding
+ * none (held = 0, table = -1).  A kernel launch (no memset), so it can be
+ * captured.  Run it once before the first selection on a fresh pool; with a
+ * pool shared by several tiers, once per tier before any of them selects
+ * (each call also refills the shared stack). */
+int hardkv_tier_init(const hardkv_desc* desc, const hardkv_tiers* tiers, hardkv_stream_t stream);
+
+/* Head-wise block allocation of the rewritten tier (desc->tier_block > 0;
+ * section 2.C, "Metadata": a head-wise block manager for head-adaptive
+ * budgets under static shapes).  One workgroup, deterministic:
+ *   1. every head, in (b, h) order, pushes its held blocks (table order) onto
+ *      the free stack and then holds none;
+ *   2. every HARDKV_MODE_REWRITE head, in (b, h) order, needs ceil(k / tier_block)
+ *      blocks for its k = count kept rows (clamped to [0, max aged]) and pops them
+ *      from the top of the stack into table entries 0, 1, ...; a head whose need
+ *      exceeds what the heads before it left on the stack takes none and is
+ *      switched to HARDKV_MODE_SPARSE (its rows stay in the cache; its attention
+ *      is unchanged), and so is every head after it.
+ * Reads count and tiers->mode; writes tiers->table, held, free_ids, free_top and
+ * mode.  Run it after the selection (and hardkv_plan) and before hardkv_compact;
+ * the steps run it themselves. */
+int hardkv_tier_alloc(const hardkv_desc* desc, const int32_t* count, const hardkv_tiers* tiers,
+                      hardkv_stream_t stream);
 
 /* hardkv_step with a per-head choice between rewriting the selection and
  * loading it in place: the policy is evaluated right after the top-p

@@ -10,7 +10,7 @@ from .hardkv_oracle import (  # noqa: F401
     init_state, lifecycle_step, POLICY_REWRITE, POLICY_SPARSE, POLICY_MTI,
     MODE_REWRITE, MODE_SPARSE, mti_head, plan_head, reuse_head, MERGE_MEAN,
     MERGE_WEIGHTED, MERGE_FLOOR, merge_weights, candidate_range, dense_positions,
-    pack_heads, CALIB_SPREAD, CALIB_ENTROPY, ENTROPY_STEPS, ENTROPY_SPAN, softmax_entropy,
+    pack_heads, tier_alloc, CALIB_SPREAD, CALIB_ENTROPY, ENTROPY_STEPS, ENTROPY_SPAN, softmax_entropy,
     entropy_temperature, HeadResult, METRIC_KEYDIFF, AUX_METRICS, keydiff_head,
     METRIC_RKV, redundancy_head, block_topp_head, BlockSelection, Selection,
 )

@@ -875,6 +875,58 @@ def reuse_head(q_group, K, V, T_now: int, sel: HeadResult):
 # head-wise block manager for head-adaptive allocation under static shapes;
 # "Techniques": Flatten Index to the maximum length or to the sum).
 # ---------------------------------------------------------------------------
+def tier_alloc(table, held, free_ids, free_top: int, counts, modes, tier_block: int, cap: int):
+    """One selection's block allocation for a block-managed rewritten tier.
+
+    Reading of section 2.C ("Metadata": a head-wise block manager allocates
+    head-adaptive budgets under static shapes; the pages give no allocation
+    rule).  The rewritten tier is a pool of blocks of `tier_block` rows with a
+    stack of free block ids; head i = (b, h) lists its blocks in table[i].
+    Every selection re-lays the tier:
+      1. every head, in (b, h) order, pushes its held blocks (table order)
+         onto the free stack and holds none;
+      2. every rewritten head, in (b, h) order, needs ceil(k / tier_block)
+         blocks (k = its kept count clamped to [0, cap]) and pops them, one
+         after another from the top of the stack, into table entries 0, 1, ...;
+         a head whose need exceeds what the heads before it left is
+         sparse-loaded instead and takes none (as pack_heads does for rows).
+    table: [B][Hkv][maxb]; held, counts, modes: [B][Hkv]; free_ids: [blocks].
+    Returns (table, held, free_ids, free_top, modes), new arrays; table
+    entries at or past a head's held count are left as they were.
+    """
+    table = np.array(table, np.int64, copy=True)
+    held = np.array(held, np.int64, copy=True)
+    free = [int(x) for x in np.asarray(free_ids)[:free_top]]
+    modes = np.array(modes, np.uint8, copy=True)
+    counts = np.asarray(counts, np.int64)
+    B, Hkv = counts.shape
+    for b in range(B):
+        for h in range(Hkv):
+            for j in range(int(held[b, h])):
+                free.append(int(table[b, h, j]))
+            held[b, h] = 0
+    avail = len(free)
+    run = 0
+    for b in range(B):
+        for h in range(Hkv):
+            need = 0
+            if modes[b, h] == MODE_REWRITE:
+                k = min(max(int(counts[b, h]), 0), cap)
+                need = -(-k // tier_block)
+            if run + need > avail:
+                if modes[b, h] == MODE_REWRITE:
+                    modes[b, h] = MODE_SPARSE
+            else:
+                for j in range(need):
+                    table[b, h, j] = free.pop()
+                held[b, h] = need
+            run += need
+    top = len(free)
+    ids = np.asarray(free_ids, np.int64).copy()
+    ids[:top] = free                      # the stack's live entries; the rest unspecified
+    return table, held, ids, top, modes
+
+
 def pack_heads(counts, modes, packed_rows: int):
     """Offsets of every head's rewritten rows in one shared region.
 

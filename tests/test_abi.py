@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = H.load()
-    assert lib.hardkv_version() == 10800
+    assert lib.hardkv_version() == 10900
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.hardkv_strerror(code)
     assert lib.hardkv_strerror(99) == b"unknown error"
@@ -43,7 +43,8 @@ def base_desc(**kw):
                        d.get("sparse_cap"), d.get("chunk_cap"), d.get("sinks", 0),
                        d.get("merge", 0), d.get("packed_rows", 0), d.get("obs_window", 1),
                        d.get("pool_radius", 0), d.get("calibration", 0),
-                       d.get("select_block", 0))
+                       d.get("select_block", 0), d.get("tier_block", 0),
+                       d.get("tier_blocks", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -97,6 +98,17 @@ def base_desc(**kw):
     (dict(ctx_cap=4096 + 64, select_block=1), H.ERR_UNSUPPORTED),
     (dict(ctx_cap=65520 + 256, W=256, select_block=16), H.OK),
     (dict(ctx_cap=65536 + 256, W=256, select_block=16), H.ERR_UNSUPPORTED),
+    (dict(tier_block=16, tier_blocks=100), H.OK),
+    (dict(tier_block=1024, tier_blocks=1), H.OK),
+    (dict(tier_block=8, tier_blocks=100), H.ERR_INVALID_ARG),
+    (dict(tier_block=48, tier_blocks=100), H.ERR_INVALID_ARG),
+    (dict(tier_block=2048, tier_blocks=100), H.ERR_INVALID_ARG),
+    (dict(tier_block=16, tier_blocks=0), H.ERR_INVALID_ARG),
+    (dict(tier_block=16, tier_blocks=1 << 27), H.ERR_INVALID_ARG),
+    (dict(tier_block=16, tier_blocks=100, packed_rows=500), H.ERR_INVALID_ARG),
+    (dict(B=2049, Hkv=8, Hq=8, tier_block=16, tier_blocks=100), H.ERR_UNSUPPORTED),
+    (dict(B=2048, Hkv=8, Hq=8, tier_block=16, tier_blocks=100), H.OK),
+    (dict(B=2048, Hkv=8, Hq=8), H.OK),
 ])
 def test_validate_codes(kw, code):
     assert H.validate(base_desc(**kw)) == code
@@ -315,6 +327,51 @@ def test_packed_tier_errors_before_launch():
     assert lib.hardkv_pack(ctypes.byref(base_desc()), fake, ctypes.byref(full), st) == \
         H.ERR_INVALID_ARG
     # the lifecycle keeps per-head pools
+    state = H.StateC(fake, fake, H.TiersC(*([fake] * 7)), fake)
+    assert lib.hardkv_step_inplace(d, fake, fake, fake, None, ctypes.byref(state), fake, fake,
+                                   need, st) == H.ERR_INVALID_ARG
+
+
+def test_tier_block_manager_errors_before_launch():
+    """Every call with a block-managed rewritten tier needs the manager's
+    state and the per-head modes; init and alloc need a block-managed
+    descriptor.  No call here passes validation."""
+    lib = H.load()
+    fake = ctypes.c_void_p(0x1000)
+    cache = H.Cache(fake, fake, None, fake)
+    st = ctypes.c_void_p(0)
+    bm = base_desc(tier_block=16, tier_blocks=200)
+    need = H.workspace_size(bm)
+    d = ctypes.byref(bm)
+    full = H.TiersC(*([fake] * 8), None, *([fake] * 4))
+    partial = [H.TiersC(*([fake] * 7), None, None, *([fake] * 4)),     # no mode
+               H.TiersC(*([fake] * 8), None, None, *([fake] * 3)),     # no table
+               H.TiersC(*([fake] * 8), None, fake, None, fake, fake),  # no held
+               H.TiersC(*([fake] * 8), None, fake, fake, None, fake),  # no free ids
+               H.TiersC(*([fake] * 8), None, fake, fake, fake, None)]  # no top
+    pol = H.policy()
+    for t in partial:
+        tb = ctypes.byref(t)
+        assert lib.hardkv_step(d, fake, ctypes.byref(cache), None, tb, fake, fake, need, st) == \
+            H.ERR_INVALID_ARG
+        assert lib.hardkv_step_policy(d, ctypes.byref(pol), fake, ctypes.byref(cache), None, tb,
+                                      fake, fake, need, st) == H.ERR_INVALID_ARG
+        assert lib.hardkv_compact(d, ctypes.byref(cache), fake, tb, fake, need, st) == \
+            H.ERR_INVALID_ARG
+        assert lib.hardkv_decode_attn(d, fake, ctypes.byref(cache), tb, fake, fake, need, st) == \
+            H.ERR_INVALID_ARG
+        assert lib.hardkv_tier_alloc(d, fake, tb, st) == H.ERR_INVALID_ARG
+    for t in partial[1:]:
+        assert lib.hardkv_tier_init(d, ctypes.byref(t), st) == H.ERR_INVALID_ARG
+    assert lib.hardkv_tier_alloc(d, None, ctypes.byref(full), st) == H.ERR_INVALID_ARG
+    assert lib.hardkv_tier_init(d, None, st) == H.ERR_INVALID_ARG
+    # both need a block-managed descriptor
+    plain = ctypes.byref(base_desc())
+    assert lib.hardkv_tier_init(plain, ctypes.byref(full), st) == H.ERR_INVALID_ARG
+    assert lib.hardkv_tier_alloc(plain, fake, ctypes.byref(full), st) == H.ERR_INVALID_ARG
+    assert lib.hardkv_tier_init(ctypes.byref(base_desc(tier_block=12, tier_blocks=9)),
+                                ctypes.byref(full), st) == H.ERR_INVALID_ARG
+    # the lifecycle keeps its own pool manager
     state = H.StateC(fake, fake, H.TiersC(*([fake] * 7)), fake)
     assert lib.hardkv_step_inplace(d, fake, fake, fake, None, ctypes.byref(state), fake, fake,
                                    need, st) == H.ERR_INVALID_ARG

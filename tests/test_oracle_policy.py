@@ -198,3 +198,65 @@ def test_pack_heads_brute_force():
             assert o + n <= cap
             for o2, n2 in used[a + 1:]:
                 assert o + n <= o2 or o2 + n2 <= o
+
+
+# ------------------------------------------- rewritten tier's block manager --
+def test_tier_alloc_worked_example():
+    # four heads (B=2, Hkv=2), blocks of 4 rows, a pool of 6 blocks, all free
+    table = np.full((2, 2, 3), -1)
+    held = np.zeros((2, 2), np.int64)
+    ids = np.arange(6)
+    counts = np.array([[5, 3], [9, 0]])      # needs 2, 1, 3, 0 blocks
+    modes = np.zeros((2, 2), np.uint8)
+    t, hd, ids2, top, m = O.tier_alloc(table, held, ids, 6, counts, modes, 4, 100)
+    # pops from the top: head 0 takes 5, 4; head 1 takes 3; head 2 takes 2, 1, 0
+    assert t[0, 0, :2].tolist() == [5, 4] and t[0, 1, :1].tolist() == [3]
+    assert t[1, 0, :3].tolist() == [2, 1, 0]
+    assert hd.tolist() == [[2, 1], [3, 0]] and top == 0 and m.tolist() == modes.tolist()
+    # next selection: budgets 1, 8, 2, 4 (needs 1, 2, 1, 1); everything is
+    # pushed back in head order (5 4 | 3 | 2 1 0), then popped from the top
+    t3, hd3, ids3, top3, m3 = O.tier_alloc(t, hd, ids2, top, np.array([[1, 8], [2, 4]]),
+                                           modes, 4, 100)
+    assert t3[0, 0, 0] == 0 and t3[0, 1, :2].tolist() == [1, 2] and t3[1, 0, 0] == 3
+    assert t3[1, 1, 0] == 4 and top3 == 1 and ids3[0] == 5
+    assert hd3.tolist() == [[1, 2], [1, 1]]
+    # a pool that runs out: needs 2, 1, 3 with 4 free blocks -> head 2 and
+    # every rewritten head after it is sparse-loaded
+    t4, hd4, _, top4, m4 = O.tier_alloc(table, held, np.arange(6), 4, counts, modes, 4, 100)
+    assert m4.tolist() == [[0, 0], [1, 1]] and hd4.tolist() == [[2, 1], [0, 0]] and top4 == 1
+    # sparse-loaded heads by policy need nothing; counts clamp to the cap
+    m_in = np.array([[1, 0], [0, 0]], np.uint8)
+    _, hd5, _, top5, m5 = O.tier_alloc(table, held, np.arange(6), 6, counts, m_in, 4, 6)
+    assert hd5.tolist() == [[0, 1], [2, 0]] and top5 == 3 and m5.tolist() == m_in.tolist()
+
+
+def test_tier_alloc_invariants_and_pack_rule():
+    """Over random histories: blocks are conserved and never shared, each
+    head holds ceil(k / tb) blocks when rewritten, and which heads fit is
+    pack_heads' rule applied to block needs over the blocks free after the
+    pushes."""
+    rng = np.random.default_rng(12)
+    for trial in range(60):
+        B, Hkv, tb = int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.choice([4, 8]))
+        cap, nblk = 40, int(rng.integers(1, 30))
+        maxb = -(-cap // tb)
+        table = np.full((B, Hkv, maxb), -1)
+        held = np.zeros((B, Hkv), np.int64)
+        ids, top = np.arange(nblk), nblk
+        for step in range(5):
+            counts = rng.integers(-3, cap + 10, (B, Hkv))
+            modes = (rng.random((B, Hkv)) < 0.25).astype(np.uint8)
+            table, held2, ids, top2, m = O.tier_alloc(table, held, ids, top, counts, modes, tb,
+                                                      cap)
+            need = -(-np.clip(counts, 0, cap) // tb)
+            _, want = O.pack_heads(need, modes, top + int(held.sum()))
+            assert np.array_equal(m, want)
+            live = [int(table[b, h, j]) for b in range(B) for h in range(Hkv)
+                    for j in range(int(held2[b, h]))]
+            stack = ids[:top2].tolist()
+            assert sorted(live + stack) == list(range(nblk))       # conserved, distinct
+            for b in range(B):
+                for h in range(Hkv):
+                    want_h = need[b, h] if m[b, h] == O.MODE_REWRITE else 0
+                    assert held2[b, h] == want_h
+            held, top = held2, top2
