@@ -39,6 +39,7 @@ template <typename T, int D, int G>
 union LifeLds {
   LifeScoreLds<T, D, G> sc;
   SelShared sel;
+  SelSmall small;
   InplaceLds<T, D, false> cp;
 };
 
@@ -72,34 +73,9 @@ __global__ __launch_bounds__(kLifeThreads) void k_life(LifeArgs A) {
   const int cnt0 = ap.pool_count[bh];
   const bool append = P >= ap.W && ap.W > 0;
   const bool room = append && cnt0 >= 0 && cnt0 < ap.sparse_cap && P < ap.ctx_cap;
-  {
-    const int slot = append ? P % ap.W : 0;
-    char* rk = ap.ring_k + (bh * ap.W + slot) * RB;
-    char* rv = ap.ring_v + (bh * ap.W + slot) * RB;
-    const int tsr = tid / CPR, c = tid % CPR;
-    const bool mine = append && tid < 2 * CPR;
-    v4u old{};
-    if (mine) old = *(const v4u*)((tsr ? rv : rk) + c * 16);
-    __syncthreads();  // every read of the old ring row is done
-    if (mine) {
-      if (room) *(v4u*)((tsr ? ap.pool_v : ap.pool_k) + ((bh * ap.sparse_cap + cnt0) * RB) + c * 16) = old;
-      *(v4u*)((tsr ? rv : rk) + c * 16) =
-          *(const v4u*)((const char*)(tsr ? ap.v_new : ap.k_new) + bh * RB + c * 16);
-    }
-    if (tid == 0 && room) ap.pool_pos[bh * ap.sparse_cap + cnt0] = P - ap.W;
-  }
   int n = cnt0 + (room ? 1 : 0);
   n = n < 0 ? 0 : (n > ap.sparse_cap ? ap.sparse_cap : n);
-  __syncthreads();  // the appended row is visible to the whole workgroup
-
-  // ---- 2. score: thread (token, half, head group)
-  const int tok = tid % kLifeTile;
-  const int half = __builtin_amdgcn_readfirstlane((tid / kLifeTile) & 1);
-  const int hg = __builtin_amdgcn_readfirstlane(tid / (2 * kLifeTile));
-  const bool scorer = hg < HG;
   const char* pool_k = (const char*)ap.pool_k + bh * ap.sparse_cap * RB;
-  float* logit = A.logit + bh * A.cap_stride;
-  float lmax = -INFINITY;
   v4u buf[LOADS];
   auto fetch = [&](int t0) {
 #pragma unroll
@@ -108,20 +84,54 @@ __global__ __launch_bounds__(kLifeThreads) void k_life(LifeArgs A) {
       buf[j] = __builtin_nontemporal_load((const v4u*)(pool_k + (int64_t)min(t0 + r, n - 1) * RB + c * 16));
     }
   };
+  // the first tile's rows are read while the append is under way: rows below
+  // cnt0 are not written by it, and the appended row (pool row cnt0, whose
+  // load here returns an unused value) enters the tile from the registers
+  // that carry it from the ring
   if (n > 0) fetch(0);
+  const int tsr = tid / CPR, cpc = tid % CPR;
+  const bool mine = append && tid < 2 * CPR;
+  v4u old{};
+  {
+    const int slot = append ? P % ap.W : 0;
+    char* rk = ap.ring_k + (bh * ap.W + slot) * RB;
+    char* rv = ap.ring_v + (bh * ap.W + slot) * RB;
+    if (mine) old = *(const v4u*)((tsr ? rv : rk) + cpc * 16);
+    __syncthreads();  // every read of the old ring row is done
+    if (mine) {
+      if (room) *(v4u*)((tsr ? ap.pool_v : ap.pool_k) + ((bh * ap.sparse_cap + cnt0) * RB) + cpc * 16) = old;
+      *(v4u*)((tsr ? rv : rk) + cpc * 16) =
+          *(const v4u*)((const char*)(tsr ? ap.v_new : ap.k_new) + bh * RB + cpc * 16);
+    }
+    if (tid == 0 && room) ap.pool_pos[bh * ap.sparse_cap + cnt0] = P - ap.W;
+  }
+  __syncthreads();  // the appended row is visible to the whole workgroup
+
+  // ---- 2. score: thread (token, half, head group)
+  const int tok = tid % kLifeTile;
+  const int half = __builtin_amdgcn_readfirstlane((tid / kLifeTile) & 1);
+  const int hg = __builtin_amdgcn_readfirstlane(tid / (2 * kLifeTile));
+  const bool scorer = hg < HG;
+  float* logit = A.logit + bh * A.cap_stride;
+  float lmax = -INFINITY;
+  float my_lg = 0.f;  // this thread's logit of the last tile (token tid when n <= one tile)
+  const bool app_in_tile0 = room && cnt0 < kLifeTile;
   for (int t0 = 0; t0 < n; t0 += kLifeTile) {
     if (t0) __syncthreads();  // the previous round's LDS reads are done
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int idx = j * NT + tid, r = idx / CPR, c = idx % CPR;
-      *(v4u*)(U.sc.rows + r * PAD + c * 16) = buf[j];
+      if (!(t0 == 0 && app_in_tile0 && r == cnt0)) *(v4u*)(U.sc.rows + r * PAD + c * 16) = buf[j];
     }
+    if (t0 == 0 && app_in_tile0 && mine && tsr == 0)
+      *(v4u*)(U.sc.rows + cnt0 * PAD + cpc * 16) = old;
     __syncthreads();
     if (t0 + kLifeTile < n) fetch(t0 + kLifeTile);  // in flight while this tile is scored
     double acc[GH];
 #pragma unroll
     for (int g = 0; g < GH; ++g) acc[g] = 0.0;
-    if (scorer) {
+    // waves whose 64 tokens all lie past the pool skip the dot products
+    if (scorer && t0 + (tok & ~63) < n) {
       const unsigned char* row = U.sc.rows + tok * PAD + half * (RB / 2);
       const double* qh = s_q + (hg * GH) * D + half * (D / 2);
 #pragma unroll
@@ -153,6 +163,7 @@ __global__ __launch_bounds__(kLifeThreads) void k_life(LifeArgs A) {
       const float lg = (float)(mx * A.scale);
       logit[t0 + tok] = lg;
       lmax = fmaxf(lmax, lg);
+      my_lg = lg;
     }
   }
   // head maximum m (the calibrated values are the logits)
@@ -170,6 +181,10 @@ __global__ __launch_bounds__(kLifeThreads) void k_life(LifeArgs A) {
   if (n > 0) {
     if (!(A.top_p < 1.0f)) {
       for (int t = tid; t < n; t += NT) mk[t] = 1;
+    } else if (n <= kSmallSel) {
+      // one tile: thread t < n holds token t's logit
+      static_assert(kSmallSel <= kLifeTile, "small pools fit one score tile");
+      select_small(U.small, n, my_lg, (double)m, A.top_p, A.wscale, s_et, mk);
     } else {
       select_head<NT>(U.sel, n, logit, [](float raw) -> float { return raw; }, (double)m,
                       A.top_p, A.wscale, s_et, mk);

@@ -295,4 +295,55 @@ __device__ inline int select_head(SelShared& S, int n, const float* x, CV cv, do
   return nsel;
 }
 
+// ------------------------------------------------------- small selection --
+constexpr int kSmallSel = 128;  // tokens select_small takes (two waves)
+
+struct SelSmall {
+  uint32_t key[kSmallSel];
+  unsigned long long w[kSmallSel];  // fixed-point weights in rank order
+  unsigned long long wtot[2];       // the two waves' totals
+};
+
+// The same selection as select_head for n <= kSmallSel tokens whose
+// calibrated values thread t < n holds in c: each token's rank in (key
+// descending, position ascending) order is counted against every key, the
+// weights wfix(c, m, wscale) are laid out in rank order and summed (integer
+// prefix sums), and the shortest rank prefix reaching max(ceil(p * Z), 1) is
+// kept.  No pass over memory: for the short pools of a steady lifecycle,
+// where the radix passes' histogram clears, barriers and re-reads dominate.
+// Requires 0 < n <= kSmallSel and top_p < 1; called by every thread of the
+// workgroup.  Writes mk[0, n).
+__device__ inline void select_small(SelSmall& S, int n, float c, double m, float top_p,
+                                    double wscale, const double* tab, uint8_t* __restrict__ mk) {
+  const int tid = threadIdx.x;
+  const bool mine = tid < n;
+  const uint32_t key = mine ? okey(c) : 0u;
+  const unsigned long long w = mine ? (unsigned long long)wfix(c, m, wscale, tab) : 0ull;
+  if (mine) S.key[tid] = key;
+  __syncthreads();
+  int rank = 0;
+  if ((tid & ~63) < n) {  // waves holding tokens
+    for (int j = 0; j < n; ++j) {
+      const uint32_t kj = S.key[j];
+      rank += (kj > key) | ((kj == key) & (j < tid));
+    }
+  }
+  if (mine) S.w[rank] = w;
+  __syncthreads();
+  unsigned long long incl = 0;
+  if (tid < kSmallSel) {  // waves 0 and 1, whole
+    incl = wave_prefix_u64(tid < n ? S.w[tid] : 0ull);
+    if ((tid & 63) == 63) S.wtot[tid >> 6] = incl;
+  }
+  __syncthreads();
+  const unsigned long long total = S.wtot[0] + S.wtot[1];
+  if (tid >= 64 && tid < kSmallSel) incl += S.wtot[0];
+  unsigned long long target = ceil_mul(top_p, total);
+  if (target < 1) target = 1;
+  // k = 1 + the ranks whose inclusive prefix is still below the target
+  const int below = __syncthreads_count(tid < n && incl < target);
+  const int k = below + 1 < n ? below + 1 : n;
+  if (mine) mk[tid] = rank < k ? 1 : 0;
+}
+
 }  // namespace hk
