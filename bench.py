@@ -468,7 +468,7 @@ def amortization(w, case, steps, horizons=(1, 2, 4, 8, 16, 32)):
     }
 
 
-def lifecycle(dev, reps=5, steady_steps=48, pool_block=0):
+def lifecycle(dev, reps=5, transition_steps=48, steady_steps=100, pool_block=0):
     """The multi-step lifecycle (hardkv_step_inplace) of one layer at the
     Qwen3-32B attention shape: 64 sequences, 64 query / 8 KV heads, d = 128,
     12288-token prefill, window 512, chunk 64, p = 0.95, fresh N(0, 1) query,
@@ -476,11 +476,14 @@ def lifecycle(dev, reps=5, steady_steps=48, pool_block=0):
     (restored from a copy before each timed repetition); later steps run on
     the pool that the selections left.  pool_block > 0: the pool under the
     head-wise block manager (blocks of that many rows, as many blocks as the
-    per-head regions would hold)."""
+    per-head regions would hold).  Steps are timed twice: after
+    transition_steps, while some heads still hold hundreds of pool rows (the
+    slowest head sets a fused step's time), and after steady_steps, once the
+    pools have converged to a few dozen rows."""
     import torch
     from decode_kv_cache_head_amd import hardkv as H
     B, Hq, Hkv, d, T0, W, C, p = 64, 64, 8, 128, 12288, 512, 64, 0.95
-    steps_cap = 1 + steady_steps + 8 + 8  # step 1, steady steps, graph replays
+    steps_cap = 1 + steady_steps + 8 + 8  # step 1, timed and untimed steps, graph replays
     desc = H.make_desc(B, Hq, Hkv, d, H.BF16, W, C, p, T0 + steps_cap)
     A = T0 - W
     ws = H.alloc_workspace(desc, dev)
@@ -547,20 +550,39 @@ def lifecycle(dev, reps=5, steady_steps=48, pool_block=0):
             s1.append(e0.elapsed_time(e1))
     pool1 = int(t.count.float().median().item())
     mb1 = pool_mb()
-    for i in range(steady_steps - 8):
+
+    def pools():
+        c = t.count.float()
+        return {"median": int(c.median().item()), "mean": round(float(c.mean().item()), 1),
+                "max": int(c.max().item())}
+
+    def timed8(done):
+        # these steps take ~0.1 ms of GPU time, about what the host needs to
+        # launch one: the stream is held first so the timed steps run back to back
+        hold(torch.cuda.current_stream())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(8):
+            H.step_inplace(desc, qs[(done + i) % 4], kn, vn, None, st, out, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 8
+
+    done = 1
+    for i in range(transition_steps - 8 - done):
         H.step_inplace(desc, qs[i % 4], kn, vn, None, st, out, ws)
+    done = transition_steps - 8
     torch.cuda.synchronize()
-    # steady steps take ~0.1 ms of GPU time, about what the host needs to
-    # launch one: the stream is held first so the timed steps run back to back
-    hold(torch.cuda.current_stream())
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(8):
-        H.step_inplace(desc, qs[i % 4], kn, vn, None, st, out, ws)
-    e1.record()
+    pool_tr = pools()
+    transition = timed8(done)
+    done += 8
+    for i in range(steady_steps - 8 - done):
+        H.step_inplace(desc, qs[(done + i) % 4], kn, vn, None, st, out, ws)
+    done = steady_steps - 8
     torch.cuda.synchronize()
-    steady = e0.elapsed_time(e1) / 8
-    pool_steady = int(t.count.float().median().item())
+    pool_st = pools()
+    steady = timed8(done)
+    pool_steady = pool_st["median"]
     mb_steady = pool_mb()
     # the same steady step captured once in a HIP graph and replayed
     qg = qs[0].clone()
@@ -581,9 +603,14 @@ def lifecycle(dev, reps=5, steady_steps=48, pool_block=0):
     res = {"shape": "qwen3-32b attention, B=64, T0=12288, W=512, C=64, p=0.95, one layer",
            "pool_block": pool_block,
            "step1_ms": round(step1, 4), "step1_pool_median_after": pool1,
-           "aged_pool_before_step1": A, "steady_ms": round(steady, 4),
+           "aged_pool_before_step1": A,
+           "transition_ms": round(transition, 4),
+           "transition_steps": [transition_steps - 8, transition_steps],
+           "transition_pools": pool_tr,
+           "steady_ms": round(steady, 4),
            "steady_graph_replay_ms": round(steady_graph, 4),
-           "steady_after_steps": steady_steps,
+           "steady_steps": [steady_steps - 8, steady_steps],
+           "steady_pools": pool_st,
            "steady_pool_median": pool_steady,
            "pool_kv_mb": {"before": mb0, "after_step1": mb1, "steady": mb_steady},
            "step1_tokens_per_s": round(B / (step1 * 1e-3), 1),

@@ -102,6 +102,8 @@ int validate(const hardkv_desc* d) {
     return HARDKV_ERR_UNSUPPORTED;
   if (d->sparse_cap < A) return HARDKV_ERR_CAPACITY;
   if ((int64_t)d->chunk_cap * d->chunk < A) return HARDKV_ERR_CAPACITY;
+  // launch grids: the batch and the KV heads are grid dimensions of their own
+  if (d->batch > 65535 || d->num_kv_heads > 65535) return HARDKV_ERR_UNSUPPORTED;
   // every element offset must fit comfortably in 63 bits
   const double elems = (double)d->batch * d->num_kv_heads *
                        ((double)d->sparse_cap + d->ctx_cap + d->chunk_cap) * d->head_dim * 8.0;

@@ -181,6 +181,9 @@ __global__ __launch_bounds__(kLifeThreads) void k_life(LifeArgs A) {
   if (n > 0) {
     if (!(A.top_p < 1.0f)) {
       for (int t = tid; t < n; t += NT) mk[t] = 1;
+    } else if (n <= 64) {
+      // one wave: lane t holds token t's logit
+      if (tid < 64) select_wave(n, my_lg, (double)m, A.top_p, A.wscale, s_et, mk);
     } else if (n <= kSmallSel) {
       // one tile: thread t < n holds token t's logit
       static_assert(kSmallSel <= kLifeTile, "small pools fit one score tile");

@@ -346,4 +346,33 @@ __device__ inline void select_small(SelSmall& S, int n, float c, double m, float
   if (mine) mk[tid] = rank < k ? 1 : 0;
 }
 
+// select_small for n <= 64 tokens held by the lanes of one wave (lane t:
+// token t), run by that wave alone: ranks from the keys broadcast lane by
+// lane, the weights moved to their rank's lane (forward permute), an integer
+// prefix over the lanes and a ballot for the cutoff.  No LDS and no
+// workgroup barrier; the caller's next barrier publishes the mask.
+__device__ inline void select_wave(int n, float c, double m, float top_p, double wscale,
+                                   const double* tab, uint8_t* __restrict__ mk) {
+  const int lane = threadIdx.x & 63;
+  const bool mine = lane < n;
+  const uint32_t key = mine ? okey(c) : 0u;
+  const unsigned long long w = mine ? (unsigned long long)wfix(c, m, wscale, tab) : 0ull;
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
+    rank += (kj > key) | ((kj == key) & (j < lane));
+  }
+  // lanes past the tokens keep their own index: the targets stay a permutation
+  const int dst = mine ? rank : lane;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_permute(dst * 4, (int)(uint32_t)w);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_permute(dst * 4, (int)(uint32_t)(w >> 32));
+  const unsigned long long incl = wave_prefix_u64(((unsigned long long)hi << 32) | lo);
+  const unsigned long long total = readlane_u64(incl, 63);
+  unsigned long long target = ceil_mul(top_p, total);
+  if (target < 1) target = 1;
+  const int below = __popcll(__ballot(lane < n && incl < target));
+  const int k = below + 1 < n ? below + 1 : n;
+  if (mine) mk[lane] = rank < k ? 1 : 0;
+}
+
 }  // namespace hk
