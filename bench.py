@@ -116,12 +116,27 @@ def kernel_bytes(w, A, k, kernel, fused):
 
 
 def source_hash(kernel):
-    """Hash of the kernel's source file and every header of the library."""
-    h = hashlib.sha256()
+    """Hash of the kernel's source file and of every library header it
+    includes, directly or through other headers."""
     csrc = os.path.join(ROOT, "decode_kv_cache_head_amd", "csrc")
-    headers = sorted(f for f in os.listdir(csrc) if f.endswith(".h"))
-    for f in [KERNEL_SOURCES[kernel]] + headers:
-        h.update(open(os.path.join(csrc, f), "rb").read())
+    inc = os.path.join(ROOT, "include")
+    seen, todo = [], [KERNEL_SOURCES[kernel]]
+    while todo:
+        f = todo.pop(0)
+        if f in seen:
+            continue
+        path = os.path.join(csrc, f) if os.path.exists(os.path.join(csrc, f)) else os.path.join(inc, f)
+        if not os.path.exists(path):
+            continue
+        seen.append(f)
+        for line in open(path):
+            line = line.strip()
+            if line.startswith('#include "'):
+                todo.append(line.split('"')[1])
+    h = hashlib.sha256()
+    for f in sorted(seen):
+        path = os.path.join(csrc, f) if os.path.exists(os.path.join(csrc, f)) else os.path.join(inc, f)
+        h.update(open(path, "rb").read())
     return h.hexdigest()[:16]
 
 
