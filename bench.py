@@ -60,6 +60,8 @@ def parse():
                     help="skip the selection-reuse timings")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-config results (tiny, 16k batch 1, ragged, 64k mixed)")
+    ap.add_argument("--no-score-g8", action="store_true",
+                    help="skip the score-only timing at the Qwen3-32B shape (G = 8)")
     ap.add_argument("--no-lifecycle", action="store_true",
                     help="skip the one-layer lifecycle timings (step 1 and steady state)")
     ap.add_argument("--no-lifecycle-full", action="store_true",
@@ -483,6 +485,48 @@ def amortization(w, case, steps, horizons=(1, 2, 4, 8, 16, 32)):
     }
 
 
+def score_g8(dev, steps):
+    """hardkv_score alone at the Qwen3-32B attention shape of the lifecycle's
+    first step (64 sequences, 64 query / 8 KV heads, d = 128, 11776 aged
+    tokens of N(0, 1) bf16 keys, contiguous): the matrix-core filtered score
+    (k_score_mx), timed with HIP events; algorithmic bytes A·row + 4A per
+    head plus the queries."""
+    import torch
+    from decode_kv_cache_head_amd import hardkv as H
+    B, Hq, Hkv, d, T, W = 64, 64, 8, 128, 12288, 512
+    desc = H.make_desc(B, Hq, Hkv, d, H.BF16, W, 64, 0.95, T)
+    A = T - W
+    g = torch.Generator(device=dev).manual_seed(321)
+    k = torch.empty((B, Hkv, T, d), dtype=torch.bfloat16, device=dev)
+    for i in range(0, B, 8):
+        k[i:i + 8] = torch.randn((8, Hkv, T, d), generator=g, device=dev).to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    ctx = torch.full((B,), T, dtype=torch.int32, device=dev)
+    cache = H.cache_struct(k, k, ctx)
+    ws = H.alloc_workspace(desc, dev)
+    logit = torch.empty((B, Hkv, desc.sparse_cap), device=dev)
+    st = torch.cuda.current_stream()
+    with H.KernelTimer() as kt:
+        for _ in range(steps + 2):
+            kt.mark(st)
+            H.score(desc, q, cache, None, logit, None, ws)
+        kt.mark(st)
+    torch.cuda.synchronize()
+    per = {}
+    for name, ms in kt.durations()[2 * 1:]:
+        per.setdefault(name, []).append(ms)
+    ms = {n: sum(v) / len(v) for n, v in per.items()}
+    name = max(ms, key=ms.get)
+    alg = B * Hkv * (A * d * 2 + 4 * A) + B * Hq * d * 2
+    gbs = alg / (ms[name] * 1e-3) / 1e9
+    del k, ws, logit
+    torch.cuda.empty_cache()
+    return {"shape": "qwen3-32b attention, B=64, 64/8 heads, d=128, 11776 aged tokens, contiguous bf16",
+            "kernel": name, "ms": round(ms[name], 4), "algorithmic_gb": round(alg / 1e9, 4),
+            "gbs": round(gbs, 1), "frac_of_peak": round(gbs / 8000.0, 4),
+            "other_kernels_ms": {n: round(v, 4) for n, v in ms.items() if n != name}}
+
+
 def lifecycle(dev, reps=5, transition_steps=48, steady_steps=100, pool_block=0):
     """The multi-step lifecycle (hardkv_step_inplace) of one layer at the
     Qwen3-32B attention shape: 64 sequences, 64 query / 8 KV heads, d = 128,
@@ -831,6 +875,9 @@ def main():
             am[wp.name] = amortization(wp, S.make_case(wp, dev), args.steps)
             torch.cuda.empty_cache()
         res["amortization"] = am
+    if not args.no_score_g8:
+        print("[bench] score at G = 8", file=sys.stderr, flush=True)
+        res["score_g8"] = score_g8(dev, args.steps)
     if not args.no_lifecycle:
         print("[bench] lifecycle", file=sys.stderr, flush=True)
         res["lifecycle"] = lifecycle(dev)

@@ -263,11 +263,19 @@ __device__ __forceinline__ f32x4_t mfma16(const v4u& a, const v4u& b, f32x4_t c)
 }
 
 // Max over the 16 lanes of a DPP row; every lane of the row receives it.
+// Each step keeps the larger of two values by compare and select: for the
+// finite or -inf values it serves this equals fmaxf, without the NaN
+// canonicalisations fmaxf adds around every DPP move.
 __device__ inline float row_max16(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  float o;
+  o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v = o > v ? o : v;
+  o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v = o > v ? o : v;
+  o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true));
+  v = o > v ? o : v;
+  o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true));
+  v = o > v ? o : v;
   return v;
 }
 

@@ -320,18 +320,19 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
 //      products are exact in float32 (inside its range), so each float32
 //      dot is within 127 * 2^-24 * A of the true one (recursive summation
 //      of 128 terms; the kernel allows four times that, 2^-15 A).
-//   2. Per token, every query head whose float32 dot is within 2 * 2^-15 *
-//      max A of the largest is a candidate (usually one head).  Where that
-//      bound does not hold (a product beyond float32's range, or dots so
-//      small that subnormal products matter) every head is a candidate.
+//   2. Per token, head i with float32 dot v_i and bound e_i = 2^-15 A_i +
+//      2^-117 (the second term covers subnormal products flushed to zero) is
+//      a candidate when v_i + e_i reaches max_j (v_j - e_j): the head with
+//      the true maximum always does (usually it is the only one).  A head
+//      whose A_i overflows float32 has no bound and is always a candidate.
 //   3. Two lanes per token (one per half of d, as in k_score) take the
-//      float64 dot of each candidate from the exact inputs (bf16 queries and
-//      keys from LDS, widened in registers), in k_score's order, and keep
-//      the maximum.
+//      float64 dot of each candidate from the exact inputs (the queries
+//      widened exactly to float32 in LDS, the bf16 keys widened in
+//      registers), in k_score's order, and keep the maximum.
 // The logit fl32(max_g q_g . k_t / sqrt(d)) is the one k_score computes: the
 // true maximum is always a candidate.  Float64 work falls from G to about one
 // dot per token.
-constexpr int kScoreMxQS = 128 + 8;  // bf16 query row stride in LDS (rows on different banks)
+constexpr int kScoreMxQS = 128 + 4;  // float32 query row stride in LDS (rows on different banks)
 // Workgroups per (b, h): each takes one contiguous run of the head's tiles,
 // split by the head's actual candidate count (read on the device), with the
 // next tile in flight.  A pool far below its capacity then dispatches few
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
   constexpr int LOADS = kScoreTile * CPR / 256;
   constexpr float kErr = 1.0f / 32768.0f;  // 2^-15: four times the float32 summation bound
   __shared__ __attribute__((aligned(16))) unsigned char lds[kScoreTile * PAD];
-  __shared__ __attribute__((aligned(16))) bf16_t s_q[G][kScoreMxQS];  // exact: widened per use
+  __shared__ __attribute__((aligned(16))) float s_q[G][kScoreMxQS];  // bf16 widened exactly
   __shared__ uint32_t s_cand[kScoreTile];
   const int hkv = gridDim.y, tid = threadIdx.x;
   const int nwg = gridDim.x * gridDim.y * gridDim.z;
@@ -373,8 +374,13 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
   };
   fetch(g0);
   const int64_t qrow = (int64_t)b * hq + (int64_t)h * G;
-  for (int i = tid; i < G * D / 8; i += 256)  // 16-byte pieces
-    *(v4u*)&s_q[i / (D / 8)][(i % (D / 8)) * 8] = *(const v4u*)(q + qrow * D + i * 8);
+  for (int i = tid; i < G * D / 8; i += 256) {  // 16-byte pieces, 8 values each
+    float f[8];
+    Elt<bf16_t>::unpack(*(const v4u*)(q + qrow * D + i * 8), f);
+    float* dst = &s_q[i / (D / 8)][(i % (D / 8)) * 8];
+    *(float4*)dst = float4{f[0], f[1], f[2], f[3]};
+    *(float4*)(dst + 4) = float4{f[4], f[5], f[6], f[7]};
+  }
   const int w = tid >> 6, lane = tid & 63;
   const int qi = lane & 15, g4 = lane >> 4;
   v4u qb[4], qa[4];
@@ -411,16 +417,18 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
       }
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        // token 32 w + 16 c + 4 g4 + cc, query head qi
+        // token 32 w + 16 c + 4 g4 + cc, query head qi: its float32 dot v
+        // lies within e of the true one (the summation bound 2^-15 A plus
+        // 2^-117 for subnormal products, at most 2^-126 off each when
+        // flushed), so the head may hold the maximum only if v + e reaches
+        // the largest lower bound v' - e' of the token's heads.  A head whose
+        // sum of |q k| overflows float32 has no bound: it is a candidate and
+        // sets no lower bound.
         const float v = qi < G ? sd[cc] : -INFINITY;
-        const float m = row_max16(v);
-        const float e = row_max16(qi < G ? kErr * sa[cc] : 0.f);
-        // the band is a bound only inside float32's range: no sum of |q k|
-        // overflows (e finite), and subnormal products, at most 2^-126 off
-        // each when flushed, stay far inside it (e >= 2^-115); otherwise
-        // every head is a candidate and the float64 dots decide
-        const bool all = !(e < INFINITY) || e < 0x1p-115f;
-        const unsigned long long bal = __ballot(qi < G && (all || v >= m - 2.f * e));
+        const float e = qi < G ? fmaf(kErr, sa[cc], 0x1p-117f) : 0.f;
+        const bool bounded = e < INFINITY;
+        const float lo = row_max16(bounded ? v - e : -INFINITY);
+        const unsigned long long bal = __ballot(qi < G && (!bounded || v + e >= lo));
         if (qi == 0) s_cand[32 * w + 16 * c + 4 * g4 + cc] = (uint32_t)(bal >> (16 * g4)) & 0xffffu;
       }
     }
@@ -432,15 +440,15 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
     while (mask) {
       const int i = __builtin_ctz(mask);
       mask &= mask - 1u;
-      const bf16_t* qh = &s_q[i][half * (D / 2)];
+      const float* qh = &s_q[i][half * (D / 2)];
       double acc = 0.0;
 #pragma unroll 1
       for (int c = 0; c < 8; ++c) {
         const v4u raw = *(const v4u*)(row + c * 16);
-        const v4u qr = *(const v4u*)(qh + c * 8);
-        float f[8], g[8];
+        const float4 g0 = *(const float4*)(qh + c * 8), g1 = *(const float4*)(qh + c * 8 + 4);
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        float f[8];
         Elt<bf16_t>::unpack(raw, f);
-        Elt<bf16_t>::unpack(qr, g);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fma((double)g[e], (double)f[e], acc);
       }
