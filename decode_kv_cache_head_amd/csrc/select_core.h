@@ -262,6 +262,19 @@ __device__ inline int select_head(SelShared& S, int n, const float* x, CV cv, do
   const unsigned long long wstar = wfix(okey_inv(kstar), m, wscale, tab);
   const unsigned long long need = target - above;
   const unsigned long long r = (need + wstar - 1) / wstar;
+  // every token tied at K* carries wstar, so its bin holds mass / wstar of
+  // them; when r reaches that count every tie is taken and the mask needs no
+  // ranking (no barrier per block of tokens)
+  const unsigned long long ntie_all = S.hist[hslot<1024>(S.bin)] / wstar;
+  if (r >= ntie_all) {
+    int nsel = 0;
+    each_value<NT, U>(x, n, [&](int t, float raw) {
+      const bool sel = okey(cv(raw)) >= kstar;
+      mk[t] = sel ? 1 : 0;
+      nsel += sel;
+    });
+    return nsel;
+  }
 
   // pass 4: mask, ties by ascending position; the next block's value is
   // loaded while the current one is ranked
