@@ -406,6 +406,7 @@ void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
   } else if (calsel_fits(max_aged(d))) {
     launch_calsel(sa, max_aged(d), st);
   } else {
+    sa.z_from_select = true;
     launch_calibrate(sa, st);
     launch_select(sa, st);
   }
@@ -747,7 +748,8 @@ int hardkv_step_inplace(const hardkv_desc* d, const void* q, const void* k_new,
       }
     }
     do_score(d, L, w, q, nullptr, pk, cand, d->sparse_cap, metric, logit, l2, st, true);
-    const SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
+    SelectArgs sa = select_args(d, cand, metric, logit, l2, stats, mask, count);
+    sa.z_from_select = true;
     // separate launches: after the first steps the pools are a few hundred
     // tokens, where the fused kernel's one-workgroup-per-CU footprint (scores
     // in registers, weights in LDS) costs more than the two light kernels

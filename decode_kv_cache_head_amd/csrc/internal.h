@@ -92,6 +92,9 @@ struct SelectArgs {
   hardkv_policy policy;
   int calib;            // HARDKV_CALIB_* for heads on the second score array
   int block;            // > 0: block-granular selection, blocks of this many positions
+  // the steps' own statistics: calibrate leaves Z out and the select records
+  // it as its fixed-point total (nothing downstream reads Z)
+  bool z_from_select;
 };
 void launch_calibrate(const SelectArgs& a, hipStream_t st);
 // top-p over position-aligned blocks ranked by calibrated mass (after calibrate)

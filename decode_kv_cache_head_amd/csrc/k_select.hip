@@ -95,7 +95,8 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(Cand cand, const int8
                                                            const float* __restrict__ logit,
                                                            const float* __restrict__ l2,
                                                            int64_t cap_stride,
-                                                           double* __restrict__ stats, int calib) {
+                                                           double* __restrict__ stats, int calib,
+                                                           bool with_z) {
   constexpr int U = 8;
   __shared__ double shd[2 * kCalWaves];
   __shared__ float shf[kCalWaves];
@@ -180,17 +181,19 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(Cand cand, const int8
   }
   const float* src = is_l2 ? sv : x;
   double Z = 0.0;
-  each_value<kCalThreads, U>(src, n, [&](int, float v) {
-    const float c = is_l2 ? cval(v, shift, scale) : v;
-    Z += exp_nonpos((double)c - (double)m, s_et);
-  });
-  Z = block_sum_f64<kCalWaves>(Z, shd);
+  if (with_z) {  // uniform
+    each_value<kCalThreads, U>(src, n, [&](int, float v) {
+      const float c = is_l2 ? cval(v, shift, scale) : v;
+      Z += exp_nonpos((double)c - (double)m, s_et);
+    });
+    Z = block_sum_f64<kCalWaves>(Z, shd);
+  }
   if (tid == 0) {
     double* o = stats + bh * 4;
     o[0] = shift;
     o[1] = scale;
     o[2] = n ? (double)m : 0.0;
-    o[3] = n ? Z : 0.0;
+    if (with_z) o[3] = n ? Z : 0.0;
   }
 }
 
@@ -199,9 +202,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
                                                         const float* __restrict__ logit,
                                                         const float* __restrict__ l2,
                                                         int64_t cap_stride,
-                                                        const double* __restrict__ stats,
+                                                        double* __restrict__ stats,
                                                         float top_p, double wscale,
-                                                        uint8_t* __restrict__ mask, CountOut co) {
+                                                        uint8_t* __restrict__ mask, CountOut co,
+                                                        bool write_z) {
   __shared__ SelShared S;
   __shared__ double s_et[64];
   const int hkv = gridDim.x, tid = threadIdx.x;
@@ -226,6 +230,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   auto cv = [&](float raw) -> float { return is_l2 ? cval(raw, shift, scale) : raw; };
 
   const int nsel = select_head<kSelThreads>(S, n, x, cv, m, top_p, wscale, s_et, mk);
+  // Z as the fixed-point total of pass 1 (within n 2^-48 of the float64 sum)
+  if (write_z && tid == 0) stats[bh * 4 + 3] = (double)S.total / wscale;
   // block sum of nsel
   const int wv = tid >> 6, ln = tid & 63;
   int v = nsel;
@@ -870,14 +876,14 @@ void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st) {
 void launch_calibrate(const SelectArgs& a, hipStream_t st) {
   observe("k_calibrate", st);
   hipLaunchKernelGGL(k_calibrate, dim3(a.hkv, a.B), dim3(kCalThreads), 0, st, a.cand, a.metric,
-                     a.logit, a.l2, a.cap_stride, a.stats, a.calib);
+                     a.logit, a.l2, a.cap_stride, a.stats, a.calib, !a.z_from_select);
 }
 
 void launch_select(const SelectArgs& a, hipStream_t st) {
   observe("k_select", st);
   hipLaunchKernelGGL(k_select, dim3(a.hkv, a.B), dim3(kSelThreads), 0, st, a.cand, a.metric,
-                     a.logit, a.l2, a.cap_stride, (const double*)a.stats, a.top_p,
-                     mass_scale(a.cand.cap), a.mask, count_out(a));
+                     a.logit, a.l2, a.cap_stride, a.stats, a.top_p, mass_scale(a.cand.cap),
+                     a.mask, count_out(a), a.z_from_select);
 }
 
 }  // namespace hk
