@@ -74,7 +74,8 @@ struct Rows {
   __device__ inline const char* row(int b, int h, int t) const {
     t += off;
     if constexpr (PAGED) {
-      const int blk = table[(int64_t)b * max_blocks + (t >> lbs)];
+      int blk = table[(int64_t)b * max_blocks + (t >> lbs)];
+      blk = blk < 0 ? 0 : blk;  // an unset entry (-1) reads block 0, never before the pool
       return base + ((((int64_t)blk * hkv + h) << lbs) + (t & ((1 << lbs) - 1))) * row_bytes;
     } else {
       return base + (((int64_t)b * hkv + h) * region + t) * row_bytes;

@@ -74,6 +74,64 @@ def test_step_graph_replay_matches_eager(gpu, name, kw):
             print(rep_, file=sys.stderr, flush=True)
 
 
+
+def test_step_graph_replay_with_tier_block_manager(gpu):
+    """The step with the rewritten tier under its block manager, captured
+    once and replayed: the allocation (blocks returned and handed out again
+    on the device every replay), the tiers read through the tables and the
+    output equal eager steps on an identical pool, replay after replay, with
+    the pool small enough that some heads are sparse-loaded."""
+    w = S.workload("qwen8b_b32_16k_paged", B=4, T=(4000, 2500, 3000, 1024))
+    case = S.make_case(w, gpu)
+    desc = desc_for(case)
+    desc.tier_block = 32
+    desc.tier_blocks = 600
+    ws = H.alloc_workspace(desc, gpu)
+    out = torch.empty((w.B, w.Hq, w.d), device=gpu)
+    cache = cache_of(case)
+    tiers = H.alloc_tiers(desc, gpu)
+    ref_tiers = H.alloc_tiers(desc, gpu)
+    H.tier_init(desc, tiers)
+    H.tier_init(desc, ref_tiers)
+    ref_out = torch.empty_like(out)
+    ref_ws = H.alloc_workspace(desc, gpu)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        H.step(desc, case.q, cache, case.metric, tiers, out, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    H.step(desc, case.q, cache, case.metric, ref_tiers, ref_out, ref_ws)  # same history
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        H.step(desc, case.q, cache, case.metric, tiers, out, ws)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device=gpu).manual_seed(6)
+    sparse_seen = 0
+    for rep in range(5):
+        case.q.copy_((torch.randn(case.q.shape, generator=gen, device=gpu) * (1 + rep)).to(case.q.dtype))
+        case.k.copy_(torch.randn(case.k.shape, generator=gen, device=gpu).to(case.k.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        H.step(desc, case.q, cache, case.metric, ref_tiers, ref_out, ref_ws)
+        torch.cuda.synchronize()
+        for f in ("count", "mode", "held", "free_top"):
+            assert torch.equal(getattr(tiers, f), getattr(ref_tiers, f)), (rep, f)
+        top = int(tiers.free_top.item())
+        assert torch.equal(tiers.free_ids[:top], ref_tiers.free_ids[:top]), rep
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                n = int(ref_tiers.count[b, h])
+                nb = int(ref_tiers.held[b, h])
+                assert torch.equal(tiers.table[b, h, :nb], ref_tiers.table[b, h, :nb])
+                assert torch.equal(tiers.pos[b, h, :n], ref_tiers.pos[b, h, :n])
+                if nb:
+                    assert torch.equal(tiers.slots(b, h, "k"), ref_tiers.slots(b, h, "k"))
+        assert torch.equal(out, ref_out), rep
+        sparse_seen += int(tiers.mode.sum())
+    assert sparse_seen > 0  # the pool ran out on some replays
+
 def _lifecycle(dev, seed, B, Hq, Hkv, d, T0, W, C, p, steps, pool_block=0):
     g = torch.Generator(device=dev).manual_seed(seed)
     desc = H.make_desc(B, Hq, Hkv, d, H.BF16, W, C, p, T0 + steps)
