@@ -112,7 +112,7 @@ int validate(const hardkv_desc* d) {
 }
 
 struct Layout {
-  size_t q64, kmu, logit, l2, wx, stats, mask, count, part, total;
+  size_t q64, kmu, logit, l2, wx, stats, mask, count, kept, part, total;
   int max_tiles;
 };
 
@@ -137,6 +137,7 @@ Layout layout(const hardkv_desc* d) {
   L.stats = take(B * Hkv * 4 * 8);
   L.mask = take(B * Hkv * cap);
   L.count = take(B * Hkv * 4);
+  L.kept = take(B * Hkv * (size_t)kept_stride(d->sparse_cap) * 4);
   L.max_tiles = attn_max_tiles(d->dense_window + d->sinks, d->sparse_cap, d->chunk_cap);
   L.part = take(B * Hkv * (size_t)L.max_tiles * G * (D + 2) * 4);
   L.total = off;
@@ -403,12 +404,22 @@ void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
   if (d->select_block > 0) {
     launch_calibrate(sa, st);
     launch_blocksel(sa, st);
-  } else if (calsel_fits(max_aged(d))) {
-    launch_calsel(sa, max_aged(d), st);
   } else {
-    sa.z_from_select = true;
-    launch_calibrate(sa, st);
-    launch_select(sa, st);
+    // the select kernels count the kept tokens of every block of candidates
+    // for the compaction tiles' offsets (whole blocks per tile)
+    if (compact_fusable(d->chunk) &&
+        compact_tile(d->chunk, max_aged(d)) % kKeptBlk == 0 &&
+        kept_stride(max_aged(d)) <= kKeptMaxBlks) {
+      sa.kept_blk = (int32_t*)(w + L.kept);
+      sa.kept_stride = kept_stride(max_aged(d));
+    }
+    if (calsel_fits(max_aged(d))) {
+      launch_calsel(sa, max_aged(d), st);
+    } else {
+      sa.z_from_select = true;
+      launch_calibrate(sa, st);
+      launch_select(sa, st);
+    }
   }
   if (d->packed_rows > 0)
     launch_pack(d->batch * d->num_kv_heads, count, max_aged(d), t.mode, t.offset,
@@ -417,6 +428,8 @@ void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
     launch_tier_alloc(tier_blocks(d, &t), d->batch * d->num_kv_heads, count, max_aged(d), t.mode,
                       st);
   CompactArgs ca = compact_args(d, L, w, kr, vr, cand, max_aged(d), mask, &t);
+  ca.kept_blk = sa.kept_blk;
+  ca.kept_stride = sa.kept_stride;
   ca.metric = metric;
   ca.logit = logit;
   ca.l2 = l2;
@@ -431,7 +444,7 @@ void run_step(const hardkv_desc* d, const hardkv_policy* policy, const void* q,
     // attention launch then covers the dense and condensed tiers only
     ca.q = q;
     launch_compact_attn(ca, st);
-    a.fused_tt = compact_tile(d->chunk);
+    a.fused_tt = compact_tile(d->chunk, max_aged(d));
   } else {
     launch_compact(ca, st);
   }

@@ -95,6 +95,10 @@ struct SelectArgs {
   // the steps' own statistics: calibrate leaves Z out and the select records
   // it as its fixed-point total (nothing downstream reads Z)
   bool z_from_select;
+  // kept tokens per kKeptBlk-token block of each head, [B][Hkv][kept_stride]
+  // (for the compaction's tile offsets); null = not emitted
+  int32_t* kept_blk;
+  int kept_stride;
 };
 void launch_calibrate(const SelectArgs& a, hipStream_t st);
 // top-p over position-aligned blocks ranked by calibrated mass (after calibrate)
@@ -126,10 +130,18 @@ void launch_pack(int n_heads, const int32_t* count, int cap, uint8_t* mode, int3
 
 // Tile of the single-step compaction: whole chunks, about 1024 tokens
 // (one chunk when a chunk is longer), processed in 64-row sub-tiles.
-inline int compact_tile(int C) { return C >= 1024 ? C : C * (1024 / C); }
+// Candidate rows per compaction tile: whole chunks, ~1024 rows.  Capacities
+// of 16385 to 32768 candidates take 512-row tiles when C divides 512: on a
+// batch of uneven heads of that length the shorter tiles end with a shorter
+// tail (measured: 8k-32k ragged batch -4 %, uniform 64k heads +2 %, so
+// longer capacities keep 1024).
+inline int compact_tile(int C, int max_cand) {
+  if (max_cand > 16384 && max_cand <= 32768 && 512 % C == 0) return 512;
+  return C >= 1024 ? C : C * (1024 / C);
+}
 // Chunks of whole 64-row sub-tiles take the register-streaming compaction,
 // which can also fold attention over the kept rows into the same pass.
-inline bool compact_fusable(int C) { return C % 64 == 0 && compact_tile(C) <= 1024; }
+inline bool compact_fusable(int C) { return C % 64 == 0 && compact_tile(C, 0) <= 1024; }
 
 // Head-wise block manager of the lifecycle pool: table == nullptr means
 // per-head regions of sparse_cap rows.
@@ -141,6 +153,13 @@ struct PoolPaging {
   int maxb;           // table entries per head
   int nblocks;
 };
+
+// Kept-token counts per block of candidates, from the select kernels: a
+// compaction tile starts at the sum of the counts before it instead of
+// counting the mask bytes before it.
+constexpr int kKeptBlk = 512;
+constexpr int kKeptMaxBlks = 256;  // blocks a select kernel counts in LDS (131072 candidates)
+inline int kept_stride(int max_cand) { return ceil_div(max_cand, kKeptBlk); }
 
 struct CompactArgs {
   int dtype, D, B, hkv, C;
@@ -159,6 +178,8 @@ struct CompactArgs {
   int chunk_stride;
   const uint8_t* mode;  // [B][Hkv]; HARDKV_MODE_SPARSE heads skip the row copies; may be null
   const int32_t* offset;  // packed tier: head (b, h)'s slot 0 is row offset[b][h]; may be null
+  const int32_t* kept_blk;  // kept tokens per kKeptBlk block ([B][Hkv][kept_stride]); may be null
+  int kept_stride;
   // block manager of the rewritten tier: slot j of head i is row
   // (tier_table[i][j >> tier_lbs] << tier_lbs) + (j & mask) of out_k / out_v; may be null
   const int32_t* tier_table;

@@ -687,7 +687,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 }
 
 // W: dense rows at most (window plus sinks)
-// (the fused compaction's tiles hold at least 576 candidates, so they fit in
+// (the fused compaction's tiles hold at least 512 candidates, so they fit in
 // the sparse tier's slots too)
 int attn_max_tiles(int W, int sparse_cap, int chunk_cap) {
   return ceil_div(W, kAttnTile) + ceil_div(sparse_cap, kAttnTile) + ceil_div(chunk_cap, kAttnTile);

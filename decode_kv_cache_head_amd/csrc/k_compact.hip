@@ -259,12 +259,18 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   if (tid < MAXU) s_evc[tid] = 0;
   if (tid == 0) s_kept_sub = 0u;
 
-  // kept tokens before the tile
+  // kept tokens before the tile: the select's per-block counts when given
+  // (tiles start on block boundaries), else the mask bytes before it
   int base;
   {
     int c = 0;
+    if (a.kept_blk) {
+      const int nb = t0 / kKeptBlk;
+      for (int i = tid; i < nb; i += 256) c += a.kept_blk[bh * a.kept_stride + i];
+    } else {
 #pragma unroll 8
-    for (int t = tid; t < t0; t += 256) c += mk[t] != 0;
+      for (int t = tid; t < t0; t += 256) c += mk[t] != 0;
+    }
     int total;
     block_excl_scan_256(c, s_scan, total);
     base = total;
@@ -596,7 +602,7 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
 
 template <typename T, int D, int G_unused, bool P>
 static void launch_compact_t(const CompactArgs& a, hipStream_t st) {
-  const int TT = compact_tile(a.C);
+  const int TT = compact_tile(a.C, a.max_cand);
   const int nt = max(1, ceil_div(a.max_cand, TT));  // tile 0 also writes count = 0
   if (compact_fusable(a.C)) {
     observe("k_compact_fast", st);
@@ -618,7 +624,7 @@ void launch_compact(const CompactArgs& a, hipStream_t st) {
 
 template <typename T, int D, int G, bool P>
 static void launch_compact_attn_t(const CompactArgs& a, hipStream_t st) {
-  const int TT = compact_tile(a.C);
+  const int TT = compact_tile(a.C, a.max_cand);
   const int nt = max(1, ceil_div(a.max_cand, TT));
   observe("k_compact_attn", st);
   if (a.merge == HARDKV_MERGE_WEIGHTED)

@@ -205,7 +205,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
                                                         double* __restrict__ stats,
                                                         float top_p, double wscale,
                                                         uint8_t* __restrict__ mask, CountOut co,
-                                                        bool write_z) {
+                                                        bool write_z, int32_t* __restrict__ kept,
+                                                        int kept_stride) {
   __shared__ SelShared S;
   __shared__ double s_et[64];
   const int hkv = gridDim.x, tid = threadIdx.x;
@@ -219,9 +220,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
     return;
   }
   exp_table_init(s_et);
+  const int nblk = (n + kKeptBlk - 1) / kKeptBlk;
+  const bool count = kept != nullptr && nblk <= kKeptMaxBlks;
   if (!(top_p < 1.0f)) {
     for (int t = tid; t < n; t += kSelThreads) mk[t] = 1;
     if (tid == 0) co.put(bh, n, n);
+    if (count)
+      for (int i = tid; i < nblk; i += kSelThreads) kept[bh * kept_stride + i] = min(kKeptBlk, n - i * kKeptBlk);
     return;
   }
   const bool is_l2 = aux_metric(metric, h);  // second score array
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
   const double shift = stats[bh * 4 + 0], scale = stats[bh * 4 + 1], m = stats[bh * 4 + 2];
   auto cv = [&](float raw) -> float { return is_l2 ? cval(raw, shift, scale) : raw; };
 
-  const int nsel = select_head<kSelThreads>(S, n, x, cv, m, top_p, wscale, s_et, mk);
+  const int nsel = select_head<kSelThreads>(S, n, x, cv, m, top_p, wscale, s_et, mk, count);
   // Z as the fixed-point total of pass 1 (within n 2^-48 of the float64 sum)
   if (write_z && tid == 0) stats[bh * 4 + 3] = (double)S.total / wscale;
   // block sum of nsel
@@ -244,6 +249,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(Cand cand, const int8_t*
     for (int i = 0; i < kSelWaves; ++i) tot += S.red[i];
     co.put(bh, n, tot);
   }
+  if (count)
+    for (int i = tid; i < nblk; i += kSelThreads) kept[bh * kept_stride + i] = S.blkcnt[i];
 }
 
 // ------------------------------------------------ calibrate + select -----
@@ -263,7 +270,9 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
                                                         int64_t cap_stride,
                                                         double* __restrict__ stats, float top_p,
                                                         double wscale, uint8_t* __restrict__ mask,
-                                                        CountOut co, int calib) {
+                                                        CountOut co, int calib,
+                                                        int32_t* __restrict__ kept,
+                                                        int kept_stride) {
   __shared__ SelShared S;
   // fixed-point weight of token tid + 1024 i at [i][tid], from pass 1 on
   __shared__ unsigned long long s_w[NPT * kSelThreads];
@@ -367,6 +376,7 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
   // pass 1: weights, Z, and the histogram of the top 11 key bits; from here
   // on the tokens are known by their order-preserving keys
   for (int i = tid; i < kHistSlots; i += kSelThreads) S.hist[i] = 0;
+  for (int i = tid; i < 2 * NPT; i += kSelThreads) S.blkcnt[i] = 0;
   if (tid == 0) S.tally = 0ull;
   __syncthreads();
   uint32_t key[NPT];
@@ -386,6 +396,9 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
     for (int i = 0; i < NPT; ++i)
       if (tid + kSelThreads * i < n) mk[tid + kSelThreads * i] = 1;
     if (tid == 0) co.put(bh, n, n);
+    if (kept)
+      for (int i = tid; i < (n + kKeptBlk - 1) / kKeptBlk; i += kSelThreads)
+        kept[bh * kept_stride + i] = min(kKeptBlk, n - i * kKeptBlk);
   }
   if (tid < 64) find_bin<2048>(S, true, top_p);
   __syncthreads();
@@ -505,6 +518,8 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
     const bool sel = valid && (key[i] > kstar || take_tie);
     const unsigned long long bal = __ballot(sel);
     nsel += __popcll(bal);
+    // slot i is tokens [1024 i, 1024 i + 1024): waves 0-7 the first 512
+    if (kept && ln == 0 && bal) atomicAdd(&S.blkcnt[2 * i + (wv >= 8)], (int)__popcll(bal));
     if (ln < 4) {
       const uint32_t bits = (uint32_t)(bal >> (16 * ln)) & 0xffffu;
       // each nibble of bits becomes four 0/1 bytes
@@ -517,6 +532,9 @@ __global__ __launch_bounds__(kSelThreads) void k_calsel(Cand cand, const int8_t*
     }
   }
   __syncthreads();
+  if (kept)
+    for (int i = tid; i < (n + kKeptBlk - 1) / kKeptBlk; i += kSelThreads)
+      kept[bh * kept_stride + i] = S.blkcnt[i];
   for (int t0 = 16 * tid; t0 < n; t0 += 16 * kSelThreads) {
     if (t0 + 16 <= n && ((uintptr_t)(mk + t0) & 15) == 0) {
       *(uint4*)(mk + t0) = *(const uint4*)(sm + t0);
@@ -870,7 +888,8 @@ void launch_calsel(const SelectArgs& a, int max_cand, hipStream_t st) {
   auto kern = small ? (aux ? k_calsel<4, true> : k_calsel<4, false>)
                     : (aux ? k_calsel<16, true> : k_calsel<16, false>);
   hipLaunchKernelGGL(kern, grid, blk, 0, st, a.cand, a.metric, a.logit, a.l2, a.cap_stride,
-                     a.stats, a.top_p, mass_scale(a.cand.cap), a.mask, count_out(a), a.calib);
+                     a.stats, a.top_p, mass_scale(a.cand.cap), a.mask, count_out(a), a.calib,
+                     a.kept_blk, a.kept_stride);
 }
 
 void launch_calibrate(const SelectArgs& a, hipStream_t st) {
@@ -883,7 +902,7 @@ void launch_select(const SelectArgs& a, hipStream_t st) {
   observe("k_select", st);
   hipLaunchKernelGGL(k_select, dim3(a.hkv, a.B), dim3(kSelThreads), 0, st, a.cand, a.metric,
                      a.logit, a.l2, a.cap_stride, a.stats, a.top_p, mass_scale(a.cand.cap),
-                     a.mask, count_out(a), a.z_from_select);
+                     a.mask, count_out(a), a.z_from_select, a.kept_blk, a.kept_stride);
 }
 
 }  // namespace hk

@@ -89,6 +89,7 @@ struct SelShared {
   int wc[kSelWaves];
   int red[kSelWaves];
   int tpre[16 * kSelWaves];  // k_calsel: ties before (slot, wave), position order
+  int blkcnt[kKeptMaxBlks];  // kept tokens per kKeptBlk block
 };
 
 // Lane l's value moved from lane l - K of its 16-lane row (0 for the first
@@ -201,12 +202,18 @@ __device__ __forceinline__ void each_value(const float* x, int n, F f) {
 // at the cutoff key are taken lowest position first.  Writes mk[0, n) and
 // returns this thread's count of selected tokens (the caller adds them up).
 // Requires 0 < n and top_p < 1; tab: the exp_nonpos table.
+// count: also add each wave's kept tokens of every block of kKeptBlk
+// positions into S.blkcnt (cleared here; complete after the caller's next
+// barrier; requires ceil(n / kKeptBlk) <= kKeptMaxBlks).
 template <int NT, typename CV>
 __device__ inline int select_head(SelShared& S, int n, const float* x, CV cv, double m,
                                   float top_p, double wscale, const double* tab,
-                                  uint8_t* __restrict__ mk) {
+                                  uint8_t* __restrict__ mk, bool count = false) {
   constexpr int U = 8;
+  static_assert(NT % kKeptBlk == 0 || kKeptBlk % NT == 0, "waves map to blocks");
   const int tid = threadIdx.x;
+  if (count)
+    for (int i = tid; i < kKeptMaxBlks; i += NT) S.blkcnt[i] = 0;
   // pass 1: top 11 bits of the key
   for (int i = tid; i < kHistSlots; i += NT) S.hist[i] = 0;
   __syncthreads();
@@ -266,19 +273,34 @@ __device__ inline int select_head(SelShared& S, int n, const float* x, CV cv, do
   // them; when r reaches that count every tie is taken and the mask needs no
   // ranking (no barrier per block of tokens)
   const unsigned long long ntie_all = S.hist[hslot<1024>(S.bin)] / wstar;
+  const int wv = tid >> 6, ln = tid & 63;
   if (r >= ntie_all) {
     int nsel = 0;
-    each_value<NT, U>(x, n, [&](int t, float raw) {
-      const bool sel = okey(cv(raw)) >= kstar;
-      mk[t] = sel ? 1 : 0;
-      nsel += sel;
-    });
+    for (int t0 = 0; t0 < n; t0 += NT * U) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * NT + tid;
+        v[u] = t < n ? x[t] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * NT + tid;
+        const bool sel = t < n && okey(cv(v[u])) >= kstar;
+        if (t < n) mk[t] = sel ? 1 : 0;
+        nsel += sel;
+        if (count) {
+          const unsigned long long bal = __ballot(sel);
+          if (ln == 0 && bal)
+            atomicAdd(&S.blkcnt[(t0 + u * NT + 64 * wv) / kKeptBlk], (int)__popcll(bal));
+        }
+      }
+    }
     return nsel;
   }
 
   // pass 4: mask, ties by ascending position; the next block's value is
   // loaded while the current one is ranked
-  const int wv = tid >> 6, ln = tid & 63;
   unsigned long long carried = 0;
   int nsel = 0;
   float nxt = tid < n ? x[tid] : 0.f;
@@ -304,6 +326,10 @@ __device__ inline int select_head(SelShared& S, int n, const float* x, CV cv, do
     const bool sel = valid && (k > kstar || (tie && rank < r));
     if (valid) mk[t] = sel ? 1 : 0;
     nsel += sel;
+    if (count) {
+      const unsigned long long bal = __ballot(sel);
+      if (ln == 0 && bal) atomicAdd(&S.blkcnt[(t0 + 64 * wv) / kKeptBlk], (int)__popcll(bal));
+    }
   }
   return nsel;
 }
