@@ -327,12 +327,12 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
 //      whose A_i overflows float32 has no bound and is always a candidate.
 //   3. Two lanes per token (one per half of d, as in k_score) take the
 //      float64 dot of each candidate from the exact inputs (the queries
-//      widened exactly to float32 in LDS, the bf16 keys widened in
+//      widened exactly to float64 in LDS, the bf16 keys widened in
 //      registers), in k_score's order, and keep the maximum.
 // The logit fl32(max_g q_g . k_t / sqrt(d)) is the one k_score computes: the
 // true maximum is always a candidate.  Float64 work falls from G to about one
 // dot per token.
-constexpr int kScoreMxQS = 128 + 4;  // float32 query row stride in LDS (rows on different banks)
+constexpr int kScoreMxQS = 128 + 2;  // float64 query row stride in LDS (rows on different banks)
 // Workgroups per (b, h): each takes one contiguous run of the head's tiles,
 // split by the head's actual candidate count (read on the device), with the
 // next tile in flight.  A pool far below its capacity then dispatches few
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
   constexpr int LOADS = kScoreTile * CPR / 256;
   constexpr float kErr = 1.0f / 32768.0f;  // 2^-15: four times the float32 summation bound
   __shared__ __attribute__((aligned(16))) unsigned char lds[kScoreTile * PAD];
-  __shared__ __attribute__((aligned(16))) float s_q[G][kScoreMxQS];  // bf16 widened exactly
+  __shared__ __attribute__((aligned(16))) double s_q[G][kScoreMxQS];  // bf16 widened exactly
   __shared__ uint32_t s_cand[kScoreTile];
   const int hkv = gridDim.y, tid = threadIdx.x;
   const int nwg = gridDim.x * gridDim.y * gridDim.z;
@@ -377,9 +377,9 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
   for (int i = tid; i < G * D / 8; i += 256) {  // 16-byte pieces, 8 values each
     float f[8];
     Elt<bf16_t>::unpack(*(const v4u*)(q + qrow * D + i * 8), f);
-    float* dst = &s_q[i / (D / 8)][(i % (D / 8)) * 8];
-    *(float4*)dst = float4{f[0], f[1], f[2], f[3]};
-    *(float4*)(dst + 4) = float4{f[4], f[5], f[6], f[7]};
+    double* dst = &s_q[i / (D / 8)][(i % (D / 8)) * 8];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) *(double2*)(dst + e) = double2{(double)f[e], (double)f[e + 1]};
   }
   const int w = tid >> 6, lane = tid & 63;
   const int qi = lane & 15, g4 = lane >> 4;
@@ -440,17 +440,22 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
     while (mask) {
       const int i = __builtin_ctz(mask);
       mask &= mask - 1u;
-      const float* qh = &s_q[i][half * (D / 2)];
+      const double* qh = &s_q[i][half * (D / 2)];
       double acc = 0.0;
 #pragma unroll 1
       for (int c = 0; c < 8; ++c) {
         const v4u raw = *(const v4u*)(row + c * 16);
-        const float4 g0 = *(const float4*)(qh + c * 8), g1 = *(const float4*)(qh + c * 8 + 4);
-        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        double g[8];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const double2 gg = *(const double2*)(qh + c * 8 + e);
+          g[e] = gg.x;
+          g[e + 1] = gg.y;
+        }
         float f[8];
         Elt<bf16_t>::unpack(raw, f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fma((double)g[e], (double)f[e], acc);
+        for (int e = 0; e < 8; ++e) acc = fma(g[e], (double)f[e], acc);
       }
       const double other = __shfl_xor(acc, 32, 64);
       best = fmax(best, half ? other + acc : acc + other);
