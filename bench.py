@@ -506,19 +506,26 @@ def score_g8(dev, steps):
     ws = H.alloc_workspace(desc, dev)
     logit = torch.empty((B, Hkv, desc.sparse_cap), device=dev)
     st = torch.cuda.current_stream()
-    for _ in range(2):  # warm-up
-        H.score(desc, q, cache, None, logit, None, ws)
+    # warm-up, with the launch observer naming the kernels of one call
     with H.KernelTimer() as kt:
-        for _ in range(steps):
+        for _ in range(2):
             kt.mark(st)
             H.score(desc, q, cache, None, logit, None, ws)
         kt.mark(st)
     torch.cuda.synchronize()
-    per = {}
-    for name, ms in kt.durations():
-        per.setdefault(name, []).append(ms)
-    ms = {n: sum(v) / len(v) for n, v in per.items()}
-    name = max(ms, key=ms.get)
+    names = sorted({n for n, _ in kt.durations()})
+    # the call is one launch: its average duration is the time of `steps`
+    # back-to-back calls between two events (no per-launch events, whose
+    # host-side recording would sit between the launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        H.score(desc, q, cache, None, logit, None, ws)
+    e1.record(st)
+    torch.cuda.synchronize()
+    assert len(names) == 1, names
+    name = names[0]
+    ms = {name: e0.elapsed_time(e1) / steps}
     alg = B * Hkv * (A * d * 2 + 4 * A) + B * Hq * d * 2
     gbs = alg / (ms[name] * 1e-3) / 1e9
     del k, ws, logit
