@@ -75,6 +75,43 @@ __device__ inline int block_excl_scan_256(int v, int* sh, int& total) {
   return off + incl - v;
 }
 
+// Two exclusive prefix sums over the 256 threads in one pass (the same two
+// barriers as one): returns v1's prefix, v0's goes to ex0, the totals to
+// t0 / t1.  sh holds 8 ints.
+__device__ inline int block_excl_scan2_256(int v0, int v1, int* sh, int& ex0, int& t0,
+                                           int& t1) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  int i0 = v0, i1 = v1;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u0 = __shfl_up(i0, o, 64), u1 = __shfl_up(i1, o, 64);
+    if (l >= o) {
+      i0 += u0;
+      i1 += u1;
+    }
+  }
+  __syncthreads();
+  if (l == 63) {
+    sh[w] = i0;
+    sh[4 + w] = i1;
+  }
+  __syncthreads();
+  int o0 = 0, o1 = 0;
+  t0 = 0;
+  t1 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < w) {
+      o0 += sh[i];
+      o1 += sh[4 + i];
+    }
+    t0 += sh[i];
+    t1 += sh[4 + i];
+  }
+  ex0 = o0 + i0 - v0;
+  return o1 + i1 - v1;
+}
+
 template <typename T, int D, bool P>
 __global__ __launch_bounds__(256) void k_compact(CompactArgs a, int TT) {
   constexpr int RB = D * (int)sizeof(T);
@@ -230,7 +267,7 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   __shared__ float s_unit[MAXU][2][D];  // per-unit sums of the evicted rows
   __shared__ float s_unitw[WMERGE ? MAXU : 1];
   __shared__ int s_evc[MAXU];           // evicted rows per chunk of the tile
-  __shared__ int s_scan[4];
+  __shared__ int s_scan[8];
   __shared__ unsigned s_kept_sub;       // bit u: unit u holds a kept row
   __shared__ int s_kept_tile;           // kept rows in the tile
   __shared__ float s_am[4][GA], s_al[4][GA];
@@ -259,24 +296,21 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
   if (tid < MAXU) s_evc[tid] = 0;
   if (tid == 0) s_kept_sub = 0u;
 
-  // kept tokens before the tile: the select's per-block counts when given
-  // (tiles start on block boundaries), else the mask bytes before it
+  // kept tokens before the tile (the select's per-block counts when given,
+  // tiles starting on block boundaries; else the mask bytes before it) and
+  // the ranks of the tile's rows (rows 4 tid .. 4 tid + 3, one unit; -1 =
+  // evicted): both counts are read together and scanned in one pass
   int base;
   {
     int c = 0;
     if (a.kept_blk) {
-      const int nb = t0 / kKeptBlk;
-      for (int i = tid; i < nb; i += 256) c += a.kept_blk[bh * a.kept_stride + i];
+      // fewer blocks than kept_stride <= kKeptMaxBlks: one count per thread
+      static_assert(kKeptMaxBlks <= 256, "one block count per thread");
+      if (tid < t0 / kKeptBlk) c = a.kept_blk[bh * a.kept_stride + tid];
     } else {
 #pragma unroll 8
       for (int t = tid; t < t0; t += 256) c += mk[t] != 0;
     }
-    int total;
-    block_excl_scan_256(c, s_scan, total);
-    base = total;
-  }
-  // ranks of the tile's rows (rows 4 tid .. 4 tid + 3, one unit); -1 = evicted
-  {
     int c4 = 0, ev4 = 0, flags = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -286,8 +320,9 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a, int TT) {
       c4 += sel;
       ev4 += r < nrows && !sel;
     }
-    int total;
-    int rk = base + block_excl_scan_256(c4, s_scan, total);
+    int ex_unused, total;
+    const int pre = block_excl_scan2_256(c, c4, s_scan, ex_unused, base, total);
+    int rk = base + pre;
     if (tid == 0) s_kept_tile = total;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
