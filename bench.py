@@ -841,6 +841,18 @@ def main():
                          "duration; traffic = counter bytes (FETCH_SIZE, WRITE_SIZE) of the "
                          "committed profile when it was taken on the current kernel source",
     }
+    # the per-kernel goal (score, select, attention each at >= 60 % of the
+    # HBM peak, or under 15 us for the small launches), stated as measured
+    goal = {}
+    for role, names in (("score", ("k_score",)), ("select", ("k_calsel", "k_calibrate", "k_select")),
+                        ("attention", ("k_compact_attn", "k_attn"))):
+        for n in names:
+            if n in kernel_ms:
+                frac = gbs[n] / HBM_PEAK_GBS
+                us = kernel_ms[n] * 1e3
+                goal[n] = {"role": role, "frac": round(frac, 4), "us": round(us, 1),
+                           "met": bool(frac >= 0.60 or us < 15.0)}
+    res["per_kernel_goal"] = {"rule": ">= 0.60 of 8 TB/s or < 15 us per launch", **goal}
     if not args.no_amortization and args.block_size is None:
         # the step with attention sinks and / or attention-weighted merging
         var = {}
