@@ -279,6 +279,18 @@ __device__ inline float row_max16(float v) {
   v = o > v ? o : v;
   return v;
 }
+// The same over each group of 8 lanes (lanes 0-7 and 8-15 of every row):
+// the quad maxima, then each lane against its mirror in the half row.
+__device__ inline float row_max8(float v) {
+  float o;
+  o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v = o > v ? o : v;
+  o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v = o > v ? o : v;
+  o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+  v = o > v ? o : v;
+  return v;
+}
 
 // Takes the word by value: bit-casting an ext-vector element in place
 // (__builtin_bit_cast(T, v.y)) is compiled as a cast of element 0.

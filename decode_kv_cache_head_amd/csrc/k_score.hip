@@ -427,7 +427,9 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
         const float v = qi < G ? sd[cc] : -INFINITY;
         const float e = qi < G ? fmaf(kErr, sa[cc], 0x1p-117f) : 0.f;
         const bool bounded = e < INFINITY;
-        const float lo = row_max16(bounded ? v - e : -INFINITY);
+        // (at G <= 8 the heads sit in lanes 0-7 of the row: their own maximum)
+        const float lb = bounded ? v - e : -INFINITY;
+        const float lo = G <= 8 ? row_max8(lb) : row_max16(lb);
         const unsigned long long bal = __ballot(qi < G && (!bounded || v + e >= lo));
         if (qi == 0) s_cand[32 * w + 16 * c + 4 * g4 + cc] = (uint32_t)(bal >> (16 * g4)) & 0xffffu;
       }
