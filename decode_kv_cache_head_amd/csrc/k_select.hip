@@ -80,7 +80,7 @@ __device__ inline void entropy_temperature(EachLogit each_logit, EachMetric each
 
 // ------------------------------------------------------------ calibrate ---
 // One 1024-thread workgroup per (b, h); every pass reads the head's scores
-// with eight loads in flight per thread (each thread adds its values in
+// with sixteen loads in flight per thread (each thread adds its values in
 // position order, so the float64 sums do not depend on the batching).
 //   logit heads:   m = max x; Z = sum exp(x - m)
 //   spread rule:   sums of x and s and max s; then the two squared
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(Cand cand, const int8
                                                            int64_t cap_stride,
                                                            double* __restrict__ stats, int calib,
                                                            bool with_z) {
-  constexpr int U = 8;
+  constexpr int U = 16;
   __shared__ double shd[2 * kCalWaves];
   __shared__ float shf[kCalWaves];
   __shared__ double s_et[64];
