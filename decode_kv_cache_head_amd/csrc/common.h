@@ -193,12 +193,31 @@ __device__ inline int xcd_contiguous(int L, int N) {
   return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
 }
 
+// Logical id grp + ngrp * hb of a launch that gives each of nh heads (hb =
+// b * Hkv + h) ngrp workgroups, all on one XCD: each XCD takes its heads in
+// order, one head's workgroups after the other.  The heads are dealt to the
+// XCDs in rows of 8: row r (heads 8r .. 8r + 7) gives XCD x head
+// 8r + (x + r) mod 8, a rotation that changes from row to row.  With 8 KV
+// heads a row is one sequence, so every XCD holds one head of each sequence
+// (a batch of unequal lengths still gives the XCDs equal work, which
+// contiguous ranges of heads would not) and, over 8 sequences, each KV head
+// once (heads that score with different metrics, and so write different
+// amounts, are spread as well).  When nh is not a multiple of 8 the XCDs
+// cannot take equal head counts: then contiguous ranges (a bijection on
+// [0, ngrp * nh) either way).
+__device__ inline int xcd_by_head(int L, int ngrp, int nh) {
+  constexpr int X = 8;
+  if (nh % X) return xcd_contiguous(L, ngrp * nh);
+  const int xcd = L % X, local = L / X;
+  const int r = local / ngrp;
+  return (r * X + (xcd + r) % X) * ngrp + local % ngrp;
+}
+
 // (b, h) of a one-workgroup-per-head launch over grid (Hkv, B), numbered as
-// the tiled score launch numbers its heads: each XCD takes one contiguous
-// range of heads in (b, h) order, the range whose scores its L2 received.
+// the tiled score launch numbers its heads (ngrp = 1), so that each head is
+// selected on the XCD whose L2 received its scores.
 __device__ inline void head_of_block(int& b, int& h) {
-  const int n = gridDim.x * gridDim.y;
-  const int id = xcd_contiguous(blockIdx.x + gridDim.x * blockIdx.y, n);
+  const int id = xcd_by_head(blockIdx.x + gridDim.x * blockIdx.y, 1, gridDim.x * gridDim.y);
   h = id % gridDim.x;
   b = id / gridDim.x;
 }

@@ -190,11 +190,10 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ q64, i
   constexpr int LOADS = kScoreTile * CPR / 256;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kScoreTile * PAD];
   __shared__ double s_part[G + 2][kScoreTile];  // second half's dots, squared norm, key-sum dot
-  // logical (tile group, h, b), tile group fastest, spread XCD-contiguously
+  // logical (tile group, h, b), tile group fastest; each head on one XCD
   const int hkv = gridDim.y, tid = threadIdx.x;
-  const int nwg = gridDim.x * gridDim.y * gridDim.z;
   const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const int id = xcd_contiguous(L, nwg);
+  const int id = xcd_by_head(L, gridDim.x, gridDim.y * gridDim.z);
   const int grp = id % gridDim.x, h = (id / gridDim.x) % hkv, b = id / (gridDim.x * hkv);
   const int n = cand.n(b, h);
   constexpr int kScoreGroup = score_group<G>();
@@ -352,9 +351,8 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
   __shared__ __attribute__((aligned(16))) double s_q[G][kScoreMxQS];  // bf16 widened exactly
   __shared__ uint32_t s_cand[kScoreTile];
   const int hkv = gridDim.y, tid = threadIdx.x;
-  const int nwg = gridDim.x * gridDim.y * gridDim.z;
   const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const int id = xcd_contiguous(L, nwg);
+  const int id = xcd_by_head(L, gridDim.x, gridDim.y * gridDim.z);
   const int grp = id % gridDim.x, h = (id / gridDim.x) % hkv, b = id / (gridDim.x * hkv);
   const int n = cand.n(b, h);
   const int ntiles = (n + kScoreTile - 1) / kScoreTile;
