@@ -66,6 +66,10 @@ def parse():
                     help="skip the one-layer lifecycle timings (step 1 and steady state)")
     ap.add_argument("--no-lifecycle-full", action="store_true",
                     help="skip the 64-layer x 256-step lifecycle run")
+    # worker mode of the CPU baseline (started by the bench itself)
+    ap.add_argument("--cpu-worker", default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-worker-index", type=int, default=0, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-worker-count", type=int, default=1, help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -154,46 +158,90 @@ def traffic_from_profile(kernel, workload):
     return int(t["fetch_bytes"] * t["fetch_scale"] + t["write_bytes"] * t["write_scale"])
 
 
-def cpu_baseline(case, w, seconds, threads):
-    """The CPU oracle on the same workload, NumPy/BLAS limited to `threads`
-    threads: whole passes over every (sequence, KV head) until about
-    `seconds` of oracle time."""
+def cpu_worker(folder, index, count, seconds):
+    """One process of the CPU baseline: the oracle steps of heads index,
+    index + count, ... of the sample in `folder`, repeated until `seconds` of
+    wall-clock time; prints {"done": heads stepped, "wall": seconds}."""
     import numpy as np
     import oracle as O
+
+    meta = json.load(open(os.path.join(folder, "meta.json")))
+    mine = []
+    for j in range(index, len(meta["heads"]), count):
+        b, h, T, metric = meta["heads"][j]
+        arr = [np.array(np.load(os.path.join(folder, f"{x}{j}.npy"), mmap_mode="r"))
+               for x in ("q", "k", "v")]
+        mine.append((arr, T, metric))
+    done, t0 = 0, time.perf_counter()
+    while True:
+        for (q, K, V), T, metric in mine:
+            O.step_head(q, K, V, T, meta["W"], meta["C"], meta["p"], metric)
+            done += 1
+        wall = time.perf_counter() - t0
+        if wall >= seconds or not mine:
+            break
+    print(json.dumps({"done": done, "wall": wall}), flush=True)
+
+
+def cpu_baseline(case, w, seconds, procs, every=4):
+    """The CPU oracle on the same workload, timed on the host's cores: the
+    inputs of every `every`-th (sequence, KV head) are written to a scratch
+    folder (not timed), then `procs` child processes (this file in its
+    worker mode, NumPy/BLAS at one thread each, no GPU) each step their share
+    of those heads through the oracle, repeatedly, for about `seconds` of
+    wall-clock time.  Heads per second, summed over the processes, give the
+    oracle's time for one whole step of every head."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    import numpy as np
     from decode_kv_cache_head_amd import synth as S
-    from threadpoolctl import threadpool_limits
 
     G = w.G
-    heads = []
-    for b in range(w.B):
-        for h in range(w.Hkv):
-            q = case.q[b, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
-            heads.append((b, h, q))
-    spent, passes, done = 0.0, 0, 0
-    with threadpool_limits(limits=threads):
-        while True:
-            for b, h, q in heads:
-                K = S.head_rows(case, b, h, "k").float().cpu().numpy()
-                V = S.head_rows(case, b, h, "v").float().cpu().numpy()
-                t0 = time.perf_counter()
-                O.step_head(q, K, V, w.T[b], w.W, w.C, w.p, int(w.metrics[h]))
-                spent += time.perf_counter() - t0
-                done += 1
-                if passes and spent >= seconds:
-                    break
-            else:
-                passes += 1
-                if spent >= seconds:
-                    break
-                continue
-            break
-    step_s = spent / done * len(heads)
-    return {"value": round(w.B / step_s, 3), "unit": "tokens/s", "cores": threads,
+    folder = tempfile.mkdtemp(prefix="hardkv_cpu_")
+    try:
+        heads = []
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                j = len(heads)
+                if (b * w.Hkv + h) % every:
+                    continue
+                q = case.q[b, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
+                np.save(os.path.join(folder, f"q{j}.npy"), q)
+                np.save(os.path.join(folder, f"k{j}.npy"),
+                        S.head_rows(case, b, h, "k").float().cpu().numpy())
+                np.save(os.path.join(folder, f"v{j}.npy"),
+                        S.head_rows(case, b, h, "v").float().cpu().numpy())
+                heads.append((b, h, int(w.T[b]), int(w.metrics[h])))
+        json.dump({"heads": heads, "W": w.W, "C": w.C, "p": w.p},
+                  open(os.path.join(folder, "meta.json"), "w"))
+        env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1",
+                   MKL_NUM_THREADS="1")
+        ps = [subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-worker", folder,
+                                "--cpu-worker-index", str(i), "--cpu-worker-count", str(procs),
+                                "--cpu-seconds", str(seconds)],
+                               stdout=subprocess.PIPE, env=env, text=True)
+              for i in range(procs)]
+        res = []
+        for pr in ps:
+            out, _ = pr.communicate()
+            if pr.returncode != 0:
+                raise RuntimeError(f"CPU oracle worker failed ({pr.returncode})")
+            res.append(json.loads(out.strip().splitlines()[-1]))
+    finally:
+        shutil.rmtree(folder, ignore_errors=True)
+    done = sum(r["done"] for r in res)
+    rate = sum(r["done"] / r["wall"] for r in res if r["done"])   # heads per second
+    step_s = w.B * w.Hkv / rate
+    wall = max(r["wall"] for r in res)
+    return {"value": round(w.B / step_s, 3), "unit": "tokens/s", "cores": procs,
             "kind": "oracle",
-            "sample": f"{done} (sequence, KV head) oracle steps = {done / len(heads):.2f} passes "
-                      f"over all {len(heads)} heads of the same workload, {spent:.1f} s of "
-                      f"oracle time with NumPy/BLAS limited to {threads} thread(s); input copies "
-                      f"to host not timed",
+            "sample": f"{len(heads)} of the {w.B * w.Hkv} (sequence, KV head) heads of the same "
+                      f"workload (one head in {every}), {done} oracle head steps in {wall:.1f} s of "
+                      f"wall time over {procs} process(es) on {procs} core(s), NumPy/BLAS at one "
+                      f"thread each; the whole step's time is the sample's rate scaled to all "
+                      f"heads; input copies to host not timed",
             "ms_per_step": round(step_s * 1e3, 1)}
 
 
@@ -694,6 +742,10 @@ def lifecycle(dev, reps=5, transition_steps=48, steady_steps=100, pool_block=0):
 
 def main():
     args = parse()
+    if args.cpu_worker:
+        cpu_worker(args.cpu_worker, args.cpu_worker_index, args.cpu_worker_count,
+                   args.cpu_seconds)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path shards by "
               "(sequence, KV head) with no exchange, which is described but not run here.",

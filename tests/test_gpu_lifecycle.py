@@ -292,16 +292,87 @@ def test_first_lifecycle_step_equals_single_step(gpu):
     assert err < 1e-5
 
 
+def snapshot(state):
+    """Device copies of everything a lifecycle step reads from one layer."""
+    t = state.tiers
+    return dict(rk=state.ring_k.clone(), rv=state.ring_v.clone(), k=t.k.clone(), v=t.v.clone(),
+                pos=t.pos.clone(), count=t.count.clone(), ksum=t.ksum.clone(),
+                vsum=t.vsum.clone(), ccount=t.ccount.clone(), T=state.seq_len.clone())
+
+
+def check_every_head(snap, state, q, kn, vn, out, W, C, p, rep):
+    """Every (b, h) of one layer after one step, against the oracle's step
+    from the state the GPU started from (snap): the kept positions (borderline
+    tokens counted), the pool rows as bit copies, the chunk counts, the chunk
+    sums within 1e-5 * (|old sum| + sum|x| of the tokens merged this step), the
+    ring, and attention within the bf16 tolerance."""
+    t = state.tiers
+    B, Hkv = snap["count"].shape
+    G = q.shape[1] // Hkv
+    cnt0, cnt1 = snap["count"].cpu().numpy(), t.count.cpu().numpy()
+    T = snap["T"].cpu().numpy()
+    ks0, vs0 = snap["ksum"].double().cpu().numpy(), snap["vsum"].double().cpu().numpy()
+    cc0 = snap["ccount"].cpu().numpy().astype(np.int64)
+    ks1, vs1 = t.ksum.double().cpu().numpy(), t.vsum.double().cpu().numpy()
+    cc1 = t.ccount.cpu().numpy().astype(np.int64)
+    pos0, pos1 = snap["pos"].cpu().numpy(), t.pos.cpu().numpy()
+    rk0, rv0 = snap["rk"].float().cpu().numpy(), snap["rv"].float().cpu().numpy()
+    rk1 = state.ring_k.float().cpu().numpy()
+    qa = q.float().cpu().numpy().astype(np.float64)
+    kna, vna = kn.float().cpu().numpy(), vn.float().cpu().numpy()
+    oa = out.double().cpu().numpy()
+    for b in range(B):
+        m0, m1 = int(cnt0[b].max()), int(cnt1[b].max())
+        k0 = snap["k"][b, :, :m0].float().cpu().numpy()
+        v0 = snap["v"][b, :, :m0].float().cpu().numpy()
+        k1 = t.k[b, :, :m1].float().cpu().numpy()
+        v1 = t.v[b, :, :m1].float().cpu().numpy()
+        for h in range(Hkv):
+            n0, n1 = int(cnt0[b, h]), int(cnt1[b, h])
+            st = O.HeadState(W, C, rk0[b, h].copy(), rv0[b, h].copy(), k0[h, :n0], v0[h, :n0],
+                             pos0[b, h, :n0].astype(np.int64), ks0[b, h].copy(),
+                             vs0[b, h].copy(), cc0[b, h].copy(), int(T[b]),
+                             np.abs(ks0[b, h]), np.abs(vs0[b, h]))
+            pool_before = st.pool_pos.copy()
+            qh = qa[b, h * G:(h + 1) * G]
+            out_ref, info = O.lifecycle_step(st, qh, kna[b, h], vna[b, h], p, O.METRIC_QK)
+            pos = pos1[b, h, :n1].astype(np.int64)
+            diff = np.setxor1d(pos, st.pool_pos)
+            rep["heads"] += 1
+            assert np.array_equal(rk1[b, h], st.ring_K), (b, h)
+            if diff.size:
+                cand = np.concatenate([pool_before, [int(T[b]) - W]])
+                ref = O.HeadResult(len(cand), None, None, info["cal"], info["sel"], None, None,
+                                   None, None, None, None, None, None)
+                assert borderline_tokens(ref, p, np.searchsorted(cand, diff)).all(), (b, h)
+                rep["borderline"] += int(diff.size)
+                # attention over the GPU's own tiers (the oracle's attention)
+                out_ref = O.attend_head(qh, st.ring_K, st.ring_V, k1[h, :n1], v1[h, :n1],
+                                        ks1[b, h], vs1[b, h], cc1[b, h])
+            else:
+                assert np.array_equal(k1[h, :n1], st.pool_K), (b, h)
+                assert np.array_equal(v1[h, :n1], st.pool_V), (b, h)
+                assert np.array_equal(cc1[b, h], st.cnt), (b, h)
+                assert np.all(np.abs(ks1[b, h] - st.ksum) <= 1e-5 * st.kabs + 1e-30), (b, h)
+                assert np.all(np.abs(vs1[b, h] - st.vsum) <= 1e-5 * st.vabs + 1e-30), (b, h)
+            o = oa[b, h * G:(h + 1) * G]
+            err = np.abs(o - out_ref).max(axis=1) / np.abs(out_ref).max(axis=1)
+            assert np.all(err <= ATTN_TOL), (b, h, err.max())
+            rep["max_attn_err"] = max(rep["max_attn_err"], float(err.max()))
+
+
 def test_lifecycle_qwen32b_64_layers_256_steps(gpu):
     """Full-size lifecycle: Qwen3-32B attention shape (64 query heads, 8 KV
     heads, d=128), 64 layers with their own caches, 64 sequences starting at
     12288 tokens, 256 decode steps, window 512, chunk 64, p = 0.95.  Sampled
-    (layer, sequence, head) triples follow the oracle step by step; every
-    head is checked for the token-count invariant at several steps."""
+    (layer, sequence, head) triples follow the oracle step by step; at steps
+    1, 50 and 256 every head of layers 0, 31 and 63 is checked against the
+    oracle's step from the state the GPU started that step with; every head
+    is checked for the token-count invariant at several steps."""
     L, B, Hq, Hkv, d, T0, W, C, p, steps = 64, 64, 64, 8, 128, 12288, 512, 64, 0.95, 256
     torch.cuda.empty_cache()
     free, _ = torch.cuda.mem_get_info()
-    need = L * B * Hkv * ((T0 + steps - W) * d * 4 + W * d * 4 + 188 * d * 8) * 1.02
+    need = (L + 1) * B * Hkv * ((T0 + steps - W) * d * 4 + W * d * 4 + 188 * d * 8) * 1.02
     if free < need:
         pytest.skip(f"needs {need / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} free")
     desc = H.make_desc(B, Hq, Hkv, d, H.BF16, W, C, p, T0 + steps)
@@ -343,7 +414,17 @@ def test_lifecycle_qwen32b_64_layers_256_steps(gpu):
             q = (torch.randn((B, Hq, d), generator=gq, device=gpu)).to(torch.bfloat16)
             kn = torch.randn((B, Hkv, d), generator=gq, device=gpu).to(torch.bfloat16)
             vn = torch.randn((B, Hkv, d), generator=gq, device=gpu).to(torch.bfloat16)
+            full = layer in (0, 31, 63) and s in (0, 49, steps - 1)
+            snap = snapshot(layers[layer]) if full else None
             H.step_inplace(desc, q, kn, vn, None, layers[layer], out, ws)
+            if snap is not None:
+                torch.cuda.synchronize()
+                every = dict(heads=0, borderline=0, max_attn_err=0.0)
+                check_every_head(snap, layers[layer], q, kn, vn, out, W, C, p, every)
+                say(f"step {s + 1}: every head of layer {layer}", every)
+                rep["borderline"] += every["borderline"]
+                rep["max_attn_err"] = max(rep["max_attn_err"], every["max_attn_err"])
+                del snap
             for (ly, b, h), st in states.items():
                 if ly != layer:
                     continue
