@@ -214,6 +214,7 @@ def cpu_baseline(case, w, seconds, procs, every=4):
                 np.save(os.path.join(folder, f"v{j}.npy"),
                         S.head_rows(case, b, h, "v").float().cpu().numpy())
                 heads.append((b, h, int(w.T[b]), int(w.metrics[h])))
+        procs = max(1, min(procs, len(heads)))   # no process without a head
         json.dump({"heads": heads, "W": w.W, "C": w.C, "p": w.p},
                   open(os.path.join(folder, "meta.json"), "w"))
         env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1",
@@ -269,13 +270,15 @@ def hold(stream, cycles=120_000_000):
             spin(cycles)
 
 
-def run_config(w, dev, steps, warmup, top_p=None, rotate_bytes=512 << 20, max_copies=64):
+def run_config(w, dev, steps, warmup, top_p=None, rotate_bytes=512 << 20, max_copies=64,
+               cpu_seconds=None, cpu_every=1):
     """One workload through hardkv_step.  When one copy of the inputs (q, K,
     V) is smaller than rotate_bytes, up to max_copies seeded copies are drawn
     and the timed steps cycle through them, so the 256 MB Infinity Cache
     cannot serve the reads.  Returns the step time (plain loop), live
     per-kernel times (launch observer), algorithmic bytes and bandwidth per
-    kernel."""
+    kernel; with cpu_seconds, also the CPU oracle on one head in cpu_every of
+    the first copy, over the host's cores (cpu_baseline)."""
     import numpy as np
     import torch
     from dataclasses import replace
@@ -350,6 +353,9 @@ def run_config(w, dev, steps, warmup, top_p=None, rotate_bytes=512 << 20, max_co
            "kernel_peak_frac": {n: round(v / HBM_PEAK_GBS, 4) for n, v in gbs.items()},
            "step_algorithmic_gb": round(total / 1e9, 4),
            "step_hbm_gbs": round(total / (step_ms * 1e-3) / 1e9, 1)}
+    if cpu_seconds:
+        res["cpu_oracle"] = cpu_baseline(first, w, cpu_seconds, len(os.sched_getaffinity(0)),
+                                         every=cpu_every)
     del cases, caches, tiers, ws
     torch.cuda.empty_cache()
     return res
@@ -965,13 +971,15 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_configs:
         cfg = {}
-        for tag, name, p in (("1", "tiny", None), ("2", "qwen8b_b1_16k", None),
-                             ("3", "qwen8b_b32_ragged_paged", None),
-                             ("4_p0.8", "qwen8b_b8_64k_mixed", 0.8),
-                             ("4_p0.9", "qwen8b_b8_64k_mixed", 0.9),
-                             ("4_p0.99", "qwen8b_b8_64k_mixed", 0.99)):
+        # (tag, workload, p, one head in `every` for the CPU oracle)
+        for tag, name, p, every in (("1", "tiny", None, 1), ("2", "qwen8b_b1_16k", None, 1),
+                                    ("3", "qwen8b_b32_ragged_paged", None, 4),
+                                    ("4_p0.8", "qwen8b_b8_64k_mixed", 0.8, 2),
+                                    ("4_p0.9", "qwen8b_b8_64k_mixed", 0.9, 2),
+                                    ("4_p0.99", "qwen8b_b8_64k_mixed", 0.99, 2)):
             print(f"[bench] config {tag}: {name}", file=sys.stderr, flush=True)
-            cfg[tag] = run_config(S.workload(name), dev, args.steps, args.warmup, top_p=p)
+            cfg[tag] = run_config(S.workload(name), dev, args.steps, args.warmup, top_p=p,
+                                  cpu_seconds=None if args.no_cpu else 3.0, cpu_every=every)
         res["configs"] = cfg
     if not args.no_lifecycle_full:
         print("[bench] lifecycle: 64 layers x 256 steps", file=sys.stderr, flush=True)
