@@ -611,50 +611,75 @@ __device__ inline void attn_tiles(const AttnArgs& a) {
   }
 }
 
-// Joins the partials of every tile of query head qh of sequence b into its
-// output row; one wave (lane = this thread's lane).
-template <int D, int G>
-__device__ inline void merge_row(const AttnArgs& a, int b, int qh, int lane) {
-  const int h = qh / G, g = qh % G;
+// Joins the partials of every tile of R query heads of sequence b, heads
+// qh0, qh0 + 4, ... (those below qh_end), each into its output row; one wave
+// (lane = this thread's lane), the loads of all R rows issued together.
+template <int D, int G, int R = 1>
+__device__ inline void merge_rows(const AttnArgs& a, int b, int qh0, int qh_end, int lane) {
+  const int h = qh0 / G;
   const TileCounts tc = tile_counts(a, b, h);
   const int nt = tc.first + tc.ntd + tc.nts + tc.ntc;
   const int64_t bh = (int64_t)b * a.hkv + h;
   constexpr int PE = D / 64;  // elements per lane
-  float M = -INFINITY, S = 0.f, O[PE];
+  float M[R], S[R], O[R][PE];
 #pragma unroll
-  for (int e = 0; e < PE; ++e) O[e] = 0.f;
-  constexpr int U = 8;  // partials fetched per round, loads issued together
+  for (int r = 0; r < R; ++r) {
+    M[r] = -INFINITY;
+    S[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < PE; ++e) O[r][e] = 0.f;
+  }
+  constexpr int U = 8;  // partials fetched per round and row, loads issued together
   for (int x0 = 0; x0 < nt; x0 += U) {
-    float pm[U], pl[U], po[U][PE];
+    float pm[R][U], pl[R][U], po[R][U][PE];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int x = min(x0 + u, nt - 1);
-      const float* p = a.part + ((bh * a.max_tiles + x) * G + g) * (D + 2);
-      pm[u] = x0 + u < nt ? p[0] : -INFINITY;
-      pl[u] = p[1];
+    for (int r = 0; r < R; ++r) {
+      const int g = min(qh0 + 4 * r, qh_end - 1) % G;
 #pragma unroll
-      for (int e = 0; e < PE; ++e) po[u][e] = p[2 + lane * PE + e];
+      for (int u = 0; u < U; ++u) {
+        const int x = min(x0 + u, nt - 1);
+        const float* p = a.part + ((bh * a.max_tiles + x) * G + g) * (D + 2);
+        pm[r][u] = x0 + u < nt ? p[0] : -INFINITY;
+        pl[r][u] = p[1];
+#pragma unroll
+        for (int e = 0; e < PE; ++e) po[r][u][e] = p[2 + lane * PE + e];
+      }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float mx = pm[u];
-      if (mx == -INFINITY) continue;
-      const float nm = fmaxf(M, mx);
-      const float fa = M == -INFINITY ? 0.f : __expf(M - nm);
-      const float fb = __expf(mx - nm);
-      S = S * fa + pl[u] * fb;
+    for (int r = 0; r < R; ++r) {
 #pragma unroll
-      for (int e = 0; e < PE; ++e) O[e] = O[e] * fa + po[u][e] * fb;
-      M = nm;
+      for (int u = 0; u < U; ++u) {
+        const float mx = pm[r][u];
+        if (mx == -INFINITY) continue;
+        const float nm = fmaxf(M[r], mx);
+        const float fa = M[r] == -INFINITY ? 0.f : __expf(M[r] - nm);
+        const float fb = __expf(mx - nm);
+        S[r] = S[r] * fa + pl[r][u] * fb;
+#pragma unroll
+        for (int e = 0; e < PE; ++e) O[r][e] = O[r][e] * fa + po[r][u][e] * fb;
+        M[r] = nm;
+      }
     }
   }
-  float* out = a.out + ((int64_t)b * a.hq + qh) * D;
 #pragma unroll
-  for (int e = 0; e < PE; ++e) out[lane * PE + e] = S > 0.f ? O[e] / S : 0.f;
+  for (int r = 0; r < R; ++r) {
+    const int qh = qh0 + 4 * r;
+    if (qh >= qh_end) break;
+    float* out = a.out + ((int64_t)b * a.hq + qh) * D;
+#pragma unroll
+    for (int e = 0; e < PE; ++e) out[lane * PE + e] = S[r] > 0.f ? O[r][e] / S[r] : 0.f;
+  }
 }
 
+// Minimum waves per SIMD the compiler must leave room for: the G = 8 dense
+// and sparse row tiles fit three (about 140 registers, no spills) instead of
+// the two their default allocation allows; the float32 chunk tiles and the
+// G = 4 tiles would spill, so they keep the default.
+template <int G, int PART>
+constexpr int attn_min_waves() { return G == 8 && PART == 1 ? 3 : 1; }
+
 template <typename T, int D, int G, bool P, bool PS, int PART>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(256, (attn_min_waves<G, PART>())) void k_attn(AttnArgs a) {
   attn_tiles<T, D, G, P, PS, PART>(a);
   if constexpr (PART == 2) {
     // the step's last launch: with merge_chunks (the ring's tiers, one chunk
@@ -666,7 +691,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       if (blockIdx.x != 0) return;
       __syncthreads();  // this tile's partial is written
       const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-      for (int g = w; g < G; g += 4) merge_row<D, G>(a, b, h * G + g, lane);
+      // wave w joins query heads w, w + 4, ... of this KV head
+      if (w < G) merge_rows<D, G, (G + 3) / 4>(a, b, h * G + w, (h + 1) * G, lane);
       if (h == 0 && threadIdx.x == 0) a.advance[b] += 1;
     }
   }
@@ -683,7 +709,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   }
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (wid >= a.B * a.hq) return;
-  merge_row<D, G>(a, wid / a.hq, wid % a.hq, lane);
+  merge_rows<D, G>(a, wid / a.hq, wid % a.hq, wid % a.hq + 1, lane);
 }
 
 // W: dense rows at most (window plus sinks)
