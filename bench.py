@@ -183,6 +183,16 @@ def cpu_worker(folder, index, count, seconds):
     print(json.dumps({"done": done, "wall": wall}), flush=True)
 
 
+def cpu_baseline_or_error(*args, **kw):
+    """cpu_baseline, or {"error": ...} when the host side fails (scratch space,
+    a worker process): the GPU figures of the line do not depend on it."""
+    try:
+        return cpu_baseline(*args, **kw)
+    except Exception as e:  # noqa: BLE001 -- reported in the JSON line instead
+        print(f"[bench] CPU oracle baseline failed: {e!r}", file=sys.stderr, flush=True)
+        return {"error": repr(e), "kind": "oracle"}
+
+
 def cpu_baseline(case, w, seconds, procs, every=4):
     """The CPU oracle on the same workload, timed on the host's cores: the
     inputs of every `every`-th (sequence, KV head) are written to a scratch
@@ -354,7 +364,8 @@ def run_config(w, dev, steps, warmup, top_p=None, rotate_bytes=512 << 20, max_co
            "step_algorithmic_gb": round(total / 1e9, 4),
            "step_hbm_gbs": round(total / (step_ms * 1e-3) / 1e9, 1)}
     if cpu_seconds:
-        res["cpu_oracle"] = cpu_baseline(first, w, cpu_seconds, len(os.sched_getaffinity(0)),
+        res["cpu_oracle"] = cpu_baseline_or_error(first, w, cpu_seconds,
+                                                  len(os.sched_getaffinity(0)),
                                          every=cpu_every)
     del cases, caches, tiers, ws
     torch.cuda.empty_cache()
@@ -964,8 +975,9 @@ def main():
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         cores = len(os.sched_getaffinity(0))
-        res["cpu_baseline"] = cpu_baseline(case, w, args.cpu_seconds, cores)
-        res["cpu_baseline"]["single_thread"] = cpu_baseline(case, w, args.cpu_seconds / 2, 1)
+        res["cpu_baseline"] = cpu_baseline_or_error(case, w, args.cpu_seconds, cores)
+        res["cpu_baseline"]["single_thread"] = cpu_baseline_or_error(case, w,
+                                                                     args.cpu_seconds / 2, 1)
         res["cpu_baseline"]["host_cores_available"] = cores
     del case, cache, tiers, ws, out
     torch.cuda.empty_cache()
