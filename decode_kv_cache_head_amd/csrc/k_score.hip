@@ -442,7 +442,7 @@ __global__ __launch_bounds__(256) void k_score_mx(const bf16_t* __restrict__ q, 
       mask &= mask - 1u;
       const double* qh = &s_q[i][half * (D / 2)];
       double acc = 0.0;
-#pragma unroll 1
+#pragma unroll 4
       for (int c = 0; c < 8; ++c) {
         const v4u raw = *(const v4u*)(row + c * 16);
         double g[8];
