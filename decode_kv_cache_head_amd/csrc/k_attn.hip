@@ -36,10 +36,6 @@ namespace hk {
 // evenly, so on a long tier each wave runs four 32-entry steps per
 // workgroup start-up.
 constexpr int kAttnTile = 512;
-// The single step's dense tier, when the compaction attended the other two
-// (a short window beside hundreds of heads): 128-entry tiles, one 32-entry
-// step per wave, so each head's window is spread over several workgroups.
-constexpr int kDenseTileStep = 128;
 
 template <typename E, int D>
 struct Lay {
@@ -52,7 +48,6 @@ struct Lay {
 
 struct TileCounts {
   int nd, ns, nc, ntd, nts, ntc;
-  int dt;        // entries per dense tile
   int first;     // partial slots taken by the fused compaction's tiles
   int gap_at;    // dense entry r is position r, or r + gap_len from gap_at on
   int gap_len;
@@ -75,9 +70,7 @@ __device__ inline TileCounts tile_counts(const AttnArgs& a, int b, int h) {
   }
   int ns = a.count[b * a.hkv + h];
   t.ns = ns < 0 ? 0 : (ns > a.sparse_cap ? a.sparse_cap : ns);
-  const int dt = a.fused_tt > 0 && !a.ring ? kDenseTileStep : kAttnTile;
-  t.dt = dt;
-  t.ntd = (t.nd + dt - 1) / dt;
+  t.ntd = (t.nd + kAttnTile - 1) / kAttnTile;
   t.nts = (t.ns + kAttnTile - 1) / kAttnTile;
   t.ntc = (t.nc + kAttnTile - 1) / kAttnTile;
   t.first = 0;
@@ -582,8 +575,8 @@ __device__ inline void attn_tiles(const AttnArgs& a) {
   float* part_out = a.part + (bh * a.max_tiles + tc.first + x) * G * (D + 2);
   if (PART != 2 && x < tc.ntd) {
     // dense entries: sinks [0, S), then the window from S + A (ring: slots)
-    const int r0 = x * tc.dt;
-    tile_attn<T, D, G, T, false, P>(a, qg, a.dk, a.dv, b, h, r0, min(tc.dt, tc.nd - r0),
+    const int r0 = x * kAttnTile;
+    tile_attn<T, D, G, T, false, P>(a, qg, a.dk, a.dv, b, h, r0, min(kAttnTile, tc.nd - r0),
                                     nullptr, s_m, s_l, s_o, part_out, nullptr, 0, tc.gap_at,
                                     tc.gap_len);
   } else if (PART != 2 && x < tc.ntd + tc.nts) {
@@ -723,17 +716,19 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // (the fused compaction's tiles hold at least 512 candidates, so they fit in
 // the sparse tier's slots too)
 int attn_max_tiles(int W, int sparse_cap, int chunk_cap) {
-  return ceil_div(W, kDenseTileStep) + ceil_div(sparse_cap, kAttnTile) +
-         ceil_div(chunk_cap, kAttnTile);
+  return ceil_div(W, kAttnTile) + ceil_div(sparse_cap, kAttnTile) + ceil_div(chunk_cap, kAttnTile);
 }
 
 template <typename T, int D, int G, bool P>
 static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
   constexpr bool split = kUseMx<T, D, G, false> && G >= 8;
-  const int dt = a.fused_tt > 0 && !a.ring ? kDenseTileStep : kAttnTile;
-  const int gd = ceil_div(a.W + a.sinks, dt), gc = ceil_div(a.chunk_cap, kAttnTile);
+  const int gd = ceil_div(a.W + a.sinks, kAttnTile), gc = ceil_div(a.chunk_cap, kAttnTile);
   const int gx = a.fused_tt > 0 ? gd : a.max_tiles;
-  const int grows = split && a.fused_tt == 0 ? gx - gc : gx;
+  int grows = split && a.fused_tt == 0 ? gx - gc : gx;
+  // an odd row grid: workgroups go to the XCDs round-robin by linear id, so
+  // with an even one the first (ring or dense) tile of every head would fall
+  // on half the XCDs or fewer; the extra workgroup finds no tile and returns
+  if (grows > 1 && (grows & 1) == 0) ++grows;
   // sparse tier through per-head block tables: the lifecycle's pool, or the
   // rewritten tier under its block manager
   const bool pool_paged = a.sk.table != nullptr;
