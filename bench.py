@@ -682,7 +682,24 @@ def lifecycle(dev, reps=5, transition_steps=48, steady_steps=100, pool_block=0):
         if r:
             s1.append(e0.elapsed_time(e1))
     pool1 = int(t.count.float().median().item())
+    kept1 = float(t.count.float().mean().item())
     mb1 = pool_mb()
+
+    def step_bytes(n, k):
+        """Algorithmic bytes of one lifecycle step over every (b, h): n
+        candidates (the pool plus the appended token), k kept, per head on
+        average.  Append: the displaced ring row and the new row, each read
+        and written once (8 rows); score: the n keys; in-place compaction: the
+        n rows of K and V read, the k kept ones written, and the chunk sums
+        that evicted tokens enter read and written; attention: the ring, the
+        k pool rows, every chunk sum and count, the queries and the outputs."""
+        row = d * 2
+        G = Hq // Hkv
+        nch = desc.chunk_cap
+        touched = min(max(n - k, 0.0), nch)
+        per_head = (8 * row + n * row + 2 * n * row + 2 * k * row + 2 * touched * (8 * d + 4)
+                    + 2 * W * row + 2 * k * row + nch * (8 * d + 4) + G * d * 6)
+        return B * Hkv * per_head
 
     def pools():
         c = t.count.float()
@@ -708,6 +725,7 @@ def lifecycle(dev, reps=5, transition_steps=48, steady_steps=100, pool_block=0):
     torch.cuda.synchronize()
     pool_tr = pools()
     transition = timed8(done)
+    kept_tr = float(t.count.float().mean().item())
     done += 8
     for i in range(steady_steps - 8 - done):
         H.step_inplace(desc, qs[(done + i) % 4], kn, vn, None, st, out, ws)
@@ -715,6 +733,7 @@ def lifecycle(dev, reps=5, transition_steps=48, steady_steps=100, pool_block=0):
     torch.cuda.synchronize()
     pool_st = pools()
     steady = timed8(done)
+    kept_st = float(t.count.float().mean().item())
     pool_steady = pool_st["median"]
     mb_steady = pool_mb()
     # the same steady step captured once in a HIP graph and replayed
@@ -733,6 +752,13 @@ def lifecycle(dev, reps=5, transition_steps=48, steady_steps=100, pool_block=0):
     steady_graph = e0.elapsed_time(e1) / 8
     del graph
     step1 = sum(s1) / len(s1)
+    # mean pool before and after: step 1 starts from the A-row prefill (plus
+    # the appended token); the timed 8-step windows from the pools measured
+    # before them, ending at the pools after them
+    alg = {"step1": step_bytes(A + 1, kept1),
+           "transition": step_bytes(pool_tr["mean"] + 1, kept_tr),
+           "steady": step_bytes(pool_st["mean"] + 1, kept_st)}
+    ms = {"step1": step1, "transition": transition, "steady": steady}
     res = {"shape": "qwen3-32b attention, B=64, T0=12288, W=512, C=64, p=0.95, one layer",
            "pool_block": pool_block,
            "step1_ms": round(step1, 4), "step1_pool_median_after": pool1,
@@ -748,6 +774,10 @@ def lifecycle(dev, reps=5, transition_steps=48, steady_steps=100, pool_block=0):
            "pool_kv_mb": {"before": mb0, "after_step1": mb1, "steady": mb_steady},
            "step1_tokens_per_s": round(B / (step1 * 1e-3), 1),
            "steady_tokens_per_s": round(B / (steady * 1e-3), 1),
+           "algorithmic_gb": {k: round(v / 1e9, 4) for k, v in alg.items()},
+           "hbm_gbs": {k: round(alg[k] / (ms[k] * 1e-3) / 1e9, 1) for k in alg},
+           "frac_of_peak": {k: round(alg[k] / (ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                            for k in alg},
            # attention + compression only, every layer of the model, steady state
            "steady_model_tokens_per_s_attention_only": {
                "layers": QWEN3_32B_LAYERS,
